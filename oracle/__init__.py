@@ -1,0 +1,168 @@
+"""fp64 CPU oracle for paged decode attention (ctypes wrapper over paged_attention_ref.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may use this package; the GPU library never does.  It imports
+nothing from the library.  Inputs are host arrays (numpy, or CPU torch tensors
+whose raw storage is read): q as bf16, K/V caches as bf16 or FP8 E4M3FN codes.
+
+Every function computes the plain definition written out in
+paged_attention_ref.c (scaled dot-product attention of one query token per
+sequence over the K/V rows its block table points to; natural-log LSE).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+_c_int = ctypes.c_int
+_c_double = ctypes.c_double
+_p = ctypes.c_void_p
+
+_STATUS = {0: "ok", -1: "bad argument", -2: "block-table entry outside the page pool",
+           -3: "sequence length outside [0, max_pages * page_size]", -4: "out of memory"}
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        common = [_c_int] * 8 + [_p] * 7 + [_c_double]
+        L.pkd_oracle_paged_decode.argtypes = common + [_p, _p, _c_int]
+        L.pkd_oracle_paged_decode.restype = _c_int
+        L.pkd_oracle_paged_decode_split.argtypes = common + [_c_int, _p, _p, _c_int]
+        L.pkd_oracle_paged_decode_split.restype = _c_int
+        L.pkd_oracle_paged_decode_rows.argtypes = common + [_c_int, _p, _p, _p]
+        L.pkd_oracle_paged_decode_rows.restype = _c_int
+        L.pkd_oracle_lse_merge.argtypes = [ctypes.c_int64, _c_int, _c_int, _p, _p, _p, _p]
+        L.pkd_oracle_lse_merge.restype = None
+        L.pkd_oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.pkd_oracle_bf16_value.restype = _c_double
+        L.pkd_oracle_fp8e4m3_value.argtypes = [ctypes.c_uint8]
+        L.pkd_oracle_fp8e4m3_value.restype = _c_double
+        _lib = L
+    return _lib
+
+
+def _raw(x, dtype):
+    """Contiguous numpy view of x's raw storage, reinterpreted as `dtype`."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor on the CPU
+        x = x.detach().contiguous()
+        import torch
+        if x.dtype in (torch.bfloat16, torch.float16):
+            x = x.view(torch.int16)
+        elif x.dtype == torch.float8_e4m3fn:
+            x = x.view(torch.uint8)
+        x = x.numpy()
+    x = np.ascontiguousarray(x)
+    if x.dtype.itemsize != np.dtype(dtype).itemsize:
+        raise TypeError(f"expected {np.dtype(dtype)} storage, got {x.dtype}")
+    return x.view(dtype)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_p)
+
+
+def _check(st):
+    if st != 0:
+        raise ValueError(f"oracle: {_STATUS.get(st, st)}")
+
+
+class _Args:
+    def __init__(self, q, k_cache, v_cache, block_table, seq_lens, scale, k_scale=None, v_scale=None,
+                 kv_fp8=None):
+        self.q = _raw(q, np.uint16)
+        B, hq, d = self.q.shape
+        kv_fp8 = (np.asarray(k_cache).dtype.itemsize == 1 if not hasattr(k_cache, "element_size")
+                  else k_cache.element_size() == 1) if kv_fp8 is None else kv_fp8
+        self.fp8 = bool(kv_fp8)
+        self.k = _raw(k_cache, np.uint8 if self.fp8 else np.uint16)
+        self.v = _raw(v_cache, np.uint8 if self.fp8 else np.uint16)
+        num_pages, ps, hkv, d2 = self.k.shape
+        assert d2 == d and self.v.shape == self.k.shape
+        self.bt = _raw(block_table, np.int32)
+        self.lens = _raw(seq_lens, np.int32)
+        assert self.bt.shape[0] == B and self.lens.shape == (B,)
+        self.ks = _raw(k_scale, np.float32)
+        self.vs = _raw(v_scale, np.float32)
+        self.dims = (B, hq, hkv, d, ps, num_pages, self.bt.shape[1], 1 if self.fp8 else 0)
+        self.scale = float(scale)
+
+    def head(self):
+        return list(self.dims) + [_ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.bt),
+                                  _ptr(self.lens), _ptr(self.ks), _ptr(self.vs), self.scale]
+
+
+def paged_decode(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale=None, v_scale=None,
+                 nthreads: int = 1):
+    """Plain definition.  Returns (out [B,Hq,D] float64, lse [B,Hq] float64)."""
+    a = _Args(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale, v_scale)
+    B, hq, _, d = a.dims[:4]
+    out = np.empty((B, hq, d), np.float64)
+    lse = np.empty((B, hq), np.float64)
+    _check(lib().pkd_oracle_paged_decode(*a.head(), _ptr(out), _ptr(lse), int(nthreads)))
+    return out, lse
+
+
+def paged_decode_split(q, k_cache, v_cache, block_table, seq_lens, scale, num_splits,
+                       k_scale=None, v_scale=None, nthreads: int = 1):
+    """Split form: ceil(L/S)-token ranges recombined by the LSE merge."""
+    a = _Args(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale, v_scale)
+    B, hq, _, d = a.dims[:4]
+    out = np.empty((B, hq, d), np.float64)
+    lse = np.empty((B, hq), np.float64)
+    _check(lib().pkd_oracle_paged_decode_split(*a.head(), int(num_splits), _ptr(out), _ptr(lse),
+                                               int(nthreads)))
+    return out, lse
+
+
+def paged_decode_rows(q, k_cache, v_cache, block_table, seq_lens, scale, rows,
+                      k_scale=None, v_scale=None):
+    """Plain definition for rows = b * Hq + h only.  Returns (out [n, D], lse [n])."""
+    a = _Args(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale, v_scale)
+    d = a.dims[3]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.empty((rows.size, d), np.float64)
+    lse = np.empty((rows.size,), np.float64)
+    _check(lib().pkd_oracle_paged_decode_rows(*a.head(), int(rows.size), _ptr(rows), _ptr(out),
+                                              _ptr(lse)))
+    return out, lse
+
+
+def lse_merge(o_part, lse_part):
+    """o_part [R, S, D], lse_part [R, S] (float64) -> (out [R, D], lse [R])."""
+    o = np.ascontiguousarray(o_part, dtype=np.float64)
+    l = np.ascontiguousarray(lse_part, dtype=np.float64)
+    R, S, D = o.shape
+    assert l.shape == (R, S)
+    out = np.empty((R, D), np.float64)
+    lse = np.empty((R,), np.float64)
+    lib().pkd_oracle_lse_merge(R, S, D, _ptr(o), _ptr(l), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def bf16_value(bits: int) -> float:
+    return lib().pkd_oracle_bf16_value(int(bits) & 0xFFFF)
+
+
+def fp8e4m3_value(code: int) -> float:
+    return lib().pkd_oracle_fp8e4m3_value(int(code) & 0xFF)
+
+
+def run_workload(w, nthreads: int = 1, num_splits: int = 0):
+    """Oracle over a drawn workload object (q, k_cache, v_cache, block_table,
+    seq_lens, scale, k_scale, v_scale attributes)."""
+    args = (w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale)
+    if num_splits:
+        return paged_decode_split(*args, num_splits, w.k_scale, w.v_scale, nthreads)
+    return paged_decode(*args, w.k_scale, w.v_scale, nthreads)

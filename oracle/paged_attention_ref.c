@@ -1,0 +1,343 @@
+/*
+ * Reference ("oracle") for single-query paged decode attention with GQA.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct CPU
+ * definition that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it.  It shares
+ * no code, header, table or helper with the HIP library under
+ * paged_kv_decode_amd/, and the library never calls it.
+ *
+ * What is computed (the operation the AstrAI commit log for
+ * csrc/kernels/attn_paged_decode_split_kv_mma.cuh builds kernels for, and the
+ * "Paged attention" row of the b12x 0.30.0 kernel inventory lists as
+ * decode over BF16 or FP8-E4M3 paged KV caches with GQA):
+ *
+ *   for every sequence b and query head h, with G = Hq / Hkv query heads per
+ *   KV head, kv(h) = floor(h / G) and L = seq_lens[b]:
+ *     token t in [0, L) lives in physical page p = block_table[b][t / ps],
+ *     slot t % ps; its key/value rows are K[p][slot][kv(h)][:] and V[...].
+ *     s_t   = scale * sum_d q[b][h][d] * k_t[d]
+ *     m     = max_t s_t,  Z = sum_t exp(s_t - m)
+ *     lse   = m + ln Z                       (natural log)
+ *     out[d]= sum_t exp(s_t - m) * v_t[d] / Z
+ *   L = 0 gives out = 0 and lse = -inf (no page is read).
+ *
+ * Everything is fp64, two-pass (max first, then sums), in token order, with no
+ * tiling, blocking or fusion.  BF16 values are decoded from their bit patterns
+ * (the upper half of an IEEE binary32), FP8 values from the OCP E4M3FN
+ * definition (bias 7, no infinities, S.1111.111 is NaN) and multiplied by the
+ * per-KV-head fp32 scale.
+ *
+ * The split form (pkd_oracle_paged_decode_split) cuts each sequence into
+ * num_splits contiguous ranges, computes each range by the same definition and
+ * recombines the ranges with the log-sum-exp merge (pkd_oracle_lse_merge).  It
+ * exists to pin the merge algebra that split-KV decoding relies on (the AstrAI
+ * log's split partials; the b12x "split-KV or direct output" variants and its
+ * PagedPersistentMergeKernel; the merge_attn_states row of the sglang
+ * fuse/overlap catalogue, vLLM section).
+ *
+ * Work is spread over an optional pthread pool by (sequence, KV head) items.
+ * The items are independent and each is computed in a fixed order, so the
+ * result is bitwise identical for any thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Status codes returned by the oracle entry points. */
+#define PKD_ORACLE_OK 0
+#define PKD_ORACLE_BAD_ARG (-1)
+#define PKD_ORACLE_BAD_PAGE (-2)   /* a used block-table entry is outside [0, num_pages) */
+#define PKD_ORACLE_BAD_LEN (-3)    /* seq_len < 0 or > max_pages_per_seq * page_size */
+#define PKD_ORACLE_NO_MEM (-4)
+
+/* ---- scalar decoders ---------------------------------------------------- */
+
+/* bfloat16: the 16 high-order bits of an IEEE-754 binary32. */
+double pkd_oracle_bf16_value(uint16_t bits) {
+  uint32_t u = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* OCP 8-bit floating point, E4M3FN variant: 1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits.  Exponent field 0 encodes subnormals
+ * (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN; there is no infinity. */
+double pkd_oracle_fp8e4m3_value(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 3) & 0xF;
+  int m = code & 0x7;
+  double mag;
+  if (e == 0xF && m == 0x7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, 1 - 7);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* ---- problem description ------------------------------------------------ */
+
+typedef struct {
+  int batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8;
+  const uint16_t* q;          /* [B][Hq][D] bf16 bits */
+  const void* k_cache;        /* [num_pages][ps][Hkv][D], bf16 bits or fp8 codes */
+  const void* v_cache;
+  const int32_t* block_table; /* [B][max_pages] */
+  const int32_t* seq_lens;    /* [B] */
+  const float* k_scale;       /* [Hkv], fp8 only */
+  const float* v_scale;
+  double scale;
+  int num_splits;             /* 0: plain definition; >= 1: split form */
+  double* out;                /* [B][Hq][D] */
+  double* lse;                /* [B][Hq] */
+} problem;
+
+/* Value of element d of token t's key (is_v = 0) or value (is_v = 1) row for
+ * KV head g of sequence b; the page lookup is the per-token one described
+ * above.  Page validity is checked by the caller. */
+static double kv_elem(const problem* P, int is_v, int b, int t, int g, int d) {
+  int32_t page = P->block_table[(int64_t)b * P->max_pages + t / P->page_size];
+  int slot = t % P->page_size;
+  int64_t idx = (((int64_t)page * P->page_size + slot) * P->hkv + g) * P->head_dim + d;
+  if (P->kv_fp8) {
+    const uint8_t* c = (const uint8_t*)(is_v ? P->v_cache : P->k_cache);
+    const float* sc = is_v ? P->v_scale : P->k_scale;
+    return pkd_oracle_fp8e4m3_value(c[idx]) * (double)sc[g];
+  }
+  const uint16_t* c = (const uint16_t*)(is_v ? P->v_cache : P->k_cache);
+  return pkd_oracle_bf16_value(c[idx]);
+}
+
+/* Attention of query head h of sequence b over tokens [t0, t1), by the plain
+ * two-pass definition.  Writes D values to o and returns the natural-log LSE;
+ * an empty range gives o = 0 and lse = -inf.  `s` is caller scratch of at
+ * least t1 - t0 doubles. */
+static double attend_range(const problem* P, int b, int h, int t0, int t1, double* o, double* s) {
+  const int D = P->head_dim;
+  const int G = P->hq / P->hkv;
+  const int g = h / G;
+  const uint16_t* qrow = P->q + ((int64_t)b * P->hq + h) * D;
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  if (t1 <= t0) return -INFINITY;
+
+  double m = -INFINITY;
+  for (int t = t0; t < t1; ++t) {
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d) acc += pkd_oracle_bf16_value(qrow[d]) * kv_elem(P, 0, b, t, g, d);
+    s[t - t0] = P->scale * acc;
+    if (s[t - t0] > m) m = s[t - t0];
+  }
+  double z = 0.0;
+  for (int t = t0; t < t1; ++t) {
+    double w = exp(s[t - t0] - m);
+    z += w;
+    for (int d = 0; d < D; ++d) o[d] += w * kv_elem(P, 1, b, t, g, d);
+  }
+  for (int d = 0; d < D; ++d) o[d] /= z;
+  return m + log(z);
+}
+
+/* Log-sum-exp merge of S partial results of one row: each partial j is a
+ * normalised output o_j (D values) with its log-sum-exp lse_j.  The merged
+ * row is the attention over the union of the partials' token ranges:
+ *   M = max_j lse_j;  lse = M + ln sum_j exp(lse_j - M);
+ *   out = sum_j exp(lse_j - lse) * o_j.
+ * A partial with lse_j = -inf (an empty range) has weight 0; if every partial
+ * is empty the row is out = 0, lse = -inf. */
+static double merge_row(int S, int D, const double* o_part, const double* lse_part, double* out) {
+  double M = -INFINITY;
+  for (int j = 0; j < S; ++j)
+    if (lse_part[j] > M) M = lse_part[j];
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  if (M == -INFINITY) return -INFINITY;
+  double z = 0.0;
+  for (int j = 0; j < S; ++j) z += exp(lse_part[j] - M);
+  double lse = M + log(z);
+  for (int j = 0; j < S; ++j) {
+    double w = exp(lse_part[j] - lse);
+    for (int d = 0; d < D; ++d) out[d] += w * o_part[(int64_t)j * D + d];
+  }
+  return lse;
+}
+
+void pkd_oracle_lse_merge(int64_t rows, int num_splits, int head_dim, const double* o_part,
+                          const double* lse_part, double* out, double* lse) {
+  for (int64_t r = 0; r < rows; ++r)
+    lse[r] = merge_row(num_splits, head_dim, o_part + r * num_splits * head_dim,
+                       lse_part + r * num_splits, out + r * head_dim);
+}
+
+/* ---- work items ---------------------------------------------------------- */
+
+typedef struct {
+  const problem* P;
+  int next;           /* shared item counter, guarded by mu */
+  int status;
+  pthread_mutex_t mu;
+} pool;
+
+static int check_sequence(const problem* P, int b) {
+  int L = P->seq_lens[b];
+  if (L < 0 || (int64_t)L > (int64_t)P->max_pages * P->page_size) return PKD_ORACLE_BAD_LEN;
+  int used = (L + P->page_size - 1) / P->page_size;
+  for (int i = 0; i < used; ++i) {
+    int32_t p = P->block_table[(int64_t)b * P->max_pages + i];
+    if (p < 0 || p >= P->num_pages) return PKD_ORACLE_BAD_PAGE;
+  }
+  return PKD_ORACLE_OK;
+}
+
+/* One item = one (sequence, KV head): all G query heads of that KV head. */
+static int run_item(const problem* P, int item) {
+  const int G = P->hq / P->hkv;
+  const int D = P->head_dim;
+  const int b = item / P->hkv;
+  const int g = item % P->hkv;
+  const int L = P->seq_lens[b];
+  double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  if (!s) return PKD_ORACLE_NO_MEM;
+  int S = P->num_splits;
+  double* op = NULL;
+  double* lp = NULL;
+  if (S >= 1) {
+    op = (double*)malloc(sizeof(double) * (size_t)S * D);
+    lp = (double*)malloc(sizeof(double) * (size_t)S);
+    if (!op || !lp) {
+      free(s); free(op); free(lp);
+      return PKD_ORACLE_NO_MEM;
+    }
+  }
+  for (int h = g * G; h < (g + 1) * G; ++h) {
+    double* o = P->out + ((int64_t)b * P->hq + h) * D;
+    double* l = P->lse + (int64_t)b * P->hq + h;
+    if (S < 1) {
+      *l = attend_range(P, b, h, 0, L, o, s);
+    } else {
+      /* split j covers [j*c, min((j+1)*c, L)) with c = ceil(L / S) */
+      int c = (L + S - 1) / S;
+      for (int j = 0; j < S; ++j) {
+        int t0 = j * c, t1 = (j + 1) * c;
+        if (t0 > L) t0 = L;
+        if (t1 > L) t1 = L;
+        lp[j] = attend_range(P, b, h, t0, t1, op + (int64_t)j * D, s);
+      }
+      *l = merge_row(S, D, op, lp, o);
+    }
+  }
+  free(s); free(op); free(lp);
+  return PKD_ORACLE_OK;
+}
+
+static void* worker(void* arg) {
+  pool* W = (pool*)arg;
+  const int n_items = W->P->batch * W->P->hkv;
+  for (;;) {
+    pthread_mutex_lock(&W->mu);
+    int item = W->next++;
+    pthread_mutex_unlock(&W->mu);
+    if (item >= n_items) break;
+    int st = run_item(W->P, item);
+    if (st != PKD_ORACLE_OK) {
+      pthread_mutex_lock(&W->mu);
+      W->status = st;
+      pthread_mutex_unlock(&W->mu);
+    }
+  }
+  return NULL;
+}
+
+static int run(problem* P, int nthreads) {
+  if (P->batch < 0 || P->hq < 1 || P->hkv < 1 || P->hq % P->hkv != 0 || P->head_dim < 1 ||
+      P->page_size < 1 || P->max_pages < 0 || P->num_pages < 0 || !P->out || !P->lse)
+    return PKD_ORACLE_BAD_ARG;
+  if (P->kv_fp8 && (!P->k_scale || !P->v_scale)) return PKD_ORACLE_BAD_ARG;
+  for (int b = 0; b < P->batch; ++b) {
+    int st = check_sequence(P, b);
+    if (st != PKD_ORACLE_OK) return st;
+  }
+  pool W;
+  W.P = P;
+  W.next = 0;
+  W.status = PKD_ORACLE_OK;
+  pthread_mutex_init(&W.mu, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads == 1) {
+    worker(&W);
+  } else {
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!th) return PKD_ORACLE_NO_MEM;
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i)
+      if (pthread_create(&th[i], NULL, worker, &W) == 0) ++started;
+    if (started == 0) worker(&W);
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    free(th);
+  }
+  pthread_mutex_destroy(&W.mu);
+  return W.status;
+}
+
+/* Plain definition.  q: bf16 bits [B][Hq][D]; k_cache/v_cache: bf16 bits or
+ * (kv_fp8 != 0) fp8 E4M3FN codes, [num_pages][page_size][Hkv][D];
+ * block_table [B][max_pages]; seq_lens [B]; k_scale/v_scale [Hkv] for fp8.
+ * out [B][Hq][D] and lse [B][Hq] are fp64.  Returns 0 or a negative status. */
+int pkd_oracle_paged_decode(int batch, int hq, int hkv, int head_dim, int page_size, int num_pages,
+                            int max_pages, int kv_fp8, const uint16_t* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, const float* k_scale, const float* v_scale,
+                            double scale, double* out, double* lse, int nthreads) {
+  problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
+               q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+               0, out, lse};
+  return run(&P, nthreads);
+}
+
+/* Split form: same arguments plus num_splits >= 1. */
+int pkd_oracle_paged_decode_split(int batch, int hq, int hkv, int head_dim, int page_size,
+                                  int num_pages, int max_pages, int kv_fp8, const uint16_t* q,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  const float* k_scale, const float* v_scale, double scale,
+                                  int num_splits, double* out, double* lse, int nthreads) {
+  if (num_splits < 1) return PKD_ORACLE_BAD_ARG;
+  problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
+               q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+               num_splits, out, lse};
+  return run(&P, nthreads);
+}
+
+/* Plain definition for a chosen list of (sequence, query head) rows only:
+ * rows[i] = b * Hq + h.  out is [n_rows][D] and lse [n_rows], fp64.  Used to
+ * spot-check full-size problems without computing every row.  Single thread,
+ * rows in the given order. */
+int pkd_oracle_paged_decode_rows(int batch, int hq, int hkv, int head_dim, int page_size,
+                                 int num_pages, int max_pages, int kv_fp8, const uint16_t* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const float* k_scale, const float* v_scale, double scale,
+                                 int n_rows, const int64_t* rows, double* out, double* lse) {
+  problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
+               q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+               0, out, lse};
+  if (batch < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || head_dim < 1 || page_size < 1 ||
+      n_rows < 0 || !rows || !out || !lse)
+    return PKD_ORACLE_BAD_ARG;
+  if (kv_fp8 && (!k_scale || !v_scale)) return PKD_ORACLE_BAD_ARG;
+  for (int i = 0; i < n_rows; ++i) {
+    int64_t r = rows[i];
+    if (r < 0 || r >= (int64_t)batch * hq) return PKD_ORACLE_BAD_ARG;
+    int b = (int)(r / hq), h = (int)(r % hq);
+    int st = check_sequence(&P, b);
+    if (st != PKD_ORACLE_OK) return st;
+    int L = seq_lens[b];
+    double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    if (!s) return PKD_ORACLE_NO_MEM;
+    lse[i] = attend_range(&P, b, h, 0, L, out + (int64_t)i * head_dim, s);
+    free(s);
+  }
+  return PKD_ORACLE_OK;
+}

@@ -1,0 +1,260 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module only draws and lays out inputs; it holds none of the attention
+arithmetic.  Both the GPU library's tests and the CPU oracle's tests take their
+inputs from here, and nothing here imports either of them.
+
+A workload is drawn on the CPU with one ``torch.Generator`` in a fixed order:
+sequence lengths, then the physical page permutation, then q, then the logical
+(per-token) K rows, then the logical V rows.  Values are N(0, 1) in float32,
+rounded to bfloat16 (round-to-nearest-even).  For an FP8 cache every KV head
+gets its own fp32 scale, amax / 448 over that head's values, and the values are
+divided by the scale, clamped to +-448 and rounded to OCP FP8 E4M3FN
+(``torch.float8_e4m3fn``).
+
+The logical rows are then scattered into a page pool ``[num_pages, page_size,
+Hkv, D]``: sequence b's i-th logical page goes to physical page
+``perm[first_page_of_b + i]``.  The pool holds exactly the pages the sequences
+use (sum of ceil(L_b / page_size)); slots past a sequence's length in its last
+page are filled with NaN (``tail="nan"``, used by parity runs so that any read
+of them shows) or zeros (``tail="zero"``).  Block-table entries past a
+sequence's last page are -1.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+FP8_E4M3_MAX = 448.0
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadSpec:
+    """Shape and draw recipe of one synthetic decode step."""
+    name: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    kv_dtype: str                      # "bf16" or "fp8_e4m3"
+    seed: int
+    seq_lens: Optional[tuple] = None   # fixed lengths, or
+    len_range: Optional[tuple] = None  # inclusive uniform integer range (lo, hi)
+    max_len: int = 0                   # longest length the block table must allow
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return -(-self.max_len // self.page_size)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def _spec(name, B, hq, hkv, d, ps, dtype, seed, seq_lens=None, len_range=None):
+    max_len = max(seq_lens) if seq_lens is not None else len_range[1]
+    return WorkloadSpec(name, B, hq, hkv, d, ps, dtype, seed,
+                        tuple(seq_lens) if seq_lens is not None else None,
+                        tuple(len_range) if len_range is not None else None, max_len)
+
+
+# The decode shapes the method is exercised on: a tiny case, a Llama-style
+# B=32 step, a B=128 step, long-context head-dim sweeps and an FP8 cache.
+WORKLOADS = {w.name: w for w in [
+    _spec("tiny_b2_d64_ps16", 2, 4, 1, 64, 16, "bf16", 1, seq_lens=(37, 100)),
+    _spec("llama_b32_d128_ps64", 32, 32, 8, 128, 64, "bf16", 2, len_range=(1024, 4096)),
+    _spec("batch128_d128_ps128", 128, 32, 8, 128, 128, "bf16", 3, seq_lens=(2048,) * 128),
+    _spec("longctx_b1_d32", 1, 16, 2, 32, 64, "bf16", 41, seq_lens=(131072,)),
+    _spec("longctx_b1_d64", 1, 16, 2, 64, 64, "bf16", 42, seq_lens=(131072,)),
+    _spec("longctx_b1_d256", 1, 16, 2, 256, 64, "bf16", 43, seq_lens=(131072,)),
+    _spec("longctx_b16_d32", 16, 16, 2, 32, 64, "bf16", 44, len_range=(8192, 32768)),
+    _spec("longctx_b16_d64", 16, 16, 2, 64, 64, "bf16", 45, len_range=(8192, 32768)),
+    _spec("longctx_b16_d256", 16, 16, 2, 256, 64, "bf16", 46, len_range=(8192, 32768)),
+    _spec("fp8kv_b64_d128_ps64", 64, 64, 8, 128, 64, "fp8_e4m3", 5, len_range=(512, 8192)),
+]}
+
+
+@dataclasses.dataclass
+class Workload:
+    """Host (CPU) tensors of one decode step plus the logical rows they came from."""
+    spec: WorkloadSpec
+    seq_lens: torch.Tensor       # [B] int32
+    block_table: torch.Tensor    # [B, max_pages] int32, -1 past the used pages
+    num_pages: int
+    q: torch.Tensor              # [B, Hq, D] bfloat16
+    k_cache: torch.Tensor        # [num_pages, ps, Hkv, D] bfloat16 or float8_e4m3fn
+    v_cache: torch.Tensor
+    k_scale: Optional[torch.Tensor]  # [Hkv] float32 (fp8 only)
+    v_scale: Optional[torch.Tensor]
+    k_logical: torch.Tensor      # [sum L, Hkv, D] in the cache dtype, sequence-major
+    v_logical: torch.Tensor
+    token_offsets: torch.Tensor  # [B + 1] int64 prefix sums of seq_lens
+    perm: torch.Tensor           # [num_pages] int64 physical page of each logical page
+
+    @property
+    def scale(self) -> float:
+        return self.spec.scale
+
+    def kv_bytes(self) -> int:
+        """Bytes of the K and V rows the step reads: sum_b L_b * Hkv * D * 2 * elem."""
+        e = self.k_cache.element_size()
+        return int(self.seq_lens.to(torch.int64).sum()) * self.spec.num_kv_heads * self.spec.head_dim * 2 * e
+
+
+def _quantize_fp8_per_head(x: torch.Tensor):
+    """x: [T, Hkv, D] float32 -> (codes float8_e4m3fn, scale [Hkv] float32)."""
+    amax = x.abs().amax(dim=(0, 2)).to(torch.float32)
+    scale = torch.where(amax > 0, amax / FP8_E4M3_MAX, torch.ones_like(amax))
+    codes = (x / scale.view(1, -1, 1)).clamp(-FP8_E4M3_MAX, FP8_E4M3_MAX).to(torch.float8_e4m3fn)
+    return codes, scale
+
+
+def _nan_fill(dtype):
+    if dtype == torch.float8_e4m3fn:
+        return torch.tensor([0x7F], dtype=torch.uint8).view(torch.float8_e4m3fn)[0]
+    return torch.tensor(float("nan"), dtype=dtype)
+
+
+def scatter_to_pages(k_logical: torch.Tensor, v_logical: torch.Tensor, seq_lens: Sequence[int],
+                     page_size: int, perm: torch.Tensor, max_pages: int, tail: str = "nan"):
+    """Lay logical rows out in a page pool.
+
+    k_logical, v_logical: [sum L, Hkv, D] rows of all sequences, sequence-major.
+    perm: physical page of each logical page (a permutation of range(num_pages)).
+    Returns (k_cache, v_cache, block_table).
+    """
+    lens = [int(x) for x in seq_lens]
+    B = len(lens)
+    npages = [-(-L // page_size) for L in lens]
+    num_pages = sum(npages)
+    assert perm.numel() == num_pages
+    hkv, d = k_logical.shape[1], k_logical.shape[2]
+    dtype = k_logical.dtype
+    shape = (num_pages, page_size, hkv, d)
+    if tail == "nan":
+        fill = _nan_fill(dtype)
+        k_cache = torch.empty(shape, dtype=dtype)
+        v_cache = torch.empty(shape, dtype=dtype)
+        if dtype == torch.float8_e4m3fn:
+            k_cache.view(torch.uint8).fill_(0x7F)
+            v_cache.view(torch.uint8).fill_(0x7F)
+        else:
+            k_cache.fill_(fill)
+            v_cache.fill_(fill)
+    elif tail == "zero":
+        k_cache = torch.zeros(shape, dtype=dtype) if dtype != torch.float8_e4m3fn else \
+            torch.zeros(shape, dtype=torch.uint8).view(torch.float8_e4m3fn)
+        v_cache = k_cache.clone()
+    else:
+        raise ValueError(f"tail must be 'nan' or 'zero', got {tail!r}")
+
+    block_table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    rows = []
+    first = 0
+    for b, L in enumerate(lens):
+        assert npages[b] <= max_pages, "sequence longer than the block table allows"
+        phys = perm[first:first + npages[b]]
+        block_table[b, :npages[b]] = phys.to(torch.int32)
+        t = torch.arange(L, dtype=torch.int64)
+        rows.append(phys[t // page_size] * page_size + t % page_size)
+        first += npages[b]
+    if rows:
+        rows = torch.cat(rows)
+        if dtype == torch.float8_e4m3fn:
+            k_cache.view(torch.uint8).view(-1, hkv, d)[rows] = k_logical.view(torch.uint8)
+            v_cache.view(torch.uint8).view(-1, hkv, d)[rows] = v_logical.view(torch.uint8)
+        else:
+            k_cache.view(-1, hkv, d)[rows] = k_logical
+            v_cache.view(-1, hkv, d)[rows] = v_logical
+    return k_cache, v_cache, block_table
+
+
+def draw_seq_lens(spec: WorkloadSpec, g: torch.Generator) -> torch.Tensor:
+    if spec.seq_lens is not None:
+        return torch.tensor(spec.seq_lens, dtype=torch.int32)
+    lo, hi = spec.len_range
+    lens = torch.randint(lo, hi + 1, (spec.batch,), generator=g, dtype=torch.int64)
+    if spec.kv_dtype == "fp8_e4m3" and spec.batch >= 2:
+        # The FP8 case must hold lengths that are and are not page multiples.
+        mult = (lens % spec.page_size) == 0
+        if not bool(mult.any()):
+            lens[0] = max(spec.page_size, min(hi - hi % spec.page_size,
+                                              int(lens[0]) - int(lens[0]) % spec.page_size))
+        if bool(((lens % spec.page_size) == 0).all()):
+            lens[1] = lens[1] - 1 if int(lens[1]) > lo else lens[1] + 1
+    return lens.to(torch.int32)
+
+
+def make_workload(spec: WorkloadSpec, tail: str = "nan",
+                  seq_lens: Optional[Sequence[int]] = None) -> Workload:
+    """Draw one decode step from `spec` (optionally overriding its lengths)."""
+    g = torch.Generator().manual_seed(spec.seed)
+    lens = torch.tensor(list(seq_lens), dtype=torch.int32) if seq_lens is not None \
+        else draw_seq_lens(spec, g)
+    B, hq, hkv, d, ps = spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size
+    assert lens.numel() == B
+    max_pages = max(spec.max_pages_per_seq, max((-(-int(L) // ps) for L in lens), default=0), 1)
+    num_pages = sum(-(-int(L) // ps) for L in lens)
+    perm = torch.randperm(num_pages, generator=g)
+    q = torch.randn(B, hq, d, generator=g).to(torch.bfloat16)
+    total = int(lens.to(torch.int64).sum())
+    k32 = torch.randn(total, hkv, d, generator=g)
+    v32 = torch.randn(total, hkv, d, generator=g)
+    k_scale = v_scale = None
+    if spec.kv_dtype == "bf16":
+        k_log, v_log = k32.to(torch.bfloat16), v32.to(torch.bfloat16)
+    elif spec.kv_dtype == "fp8_e4m3":
+        k_log, k_scale = _quantize_fp8_per_head(k32)
+        v_log, v_scale = _quantize_fp8_per_head(v32)
+    else:
+        raise ValueError(spec.kv_dtype)
+    del k32, v32
+    k_cache, v_cache, bt = scatter_to_pages(k_log, v_log, lens.tolist(), ps, perm, max_pages, tail)
+    offs = torch.zeros(B + 1, dtype=torch.int64)
+    offs[1:] = torch.cumsum(lens.to(torch.int64), 0)
+    return Workload(spec, lens, bt, num_pages, q, k_cache, v_cache, k_scale, v_scale,
+                    k_log, v_log, offs, perm)
+
+
+def custom_workload(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+                    seq_lens: Sequence[int], kv_dtype: str = "bf16", seed: int = 0,
+                    tail: str = "nan", max_pages: Optional[int] = None, name: str = "custom") -> Workload:
+    """A one-off workload with explicit lengths (edge cases, small parity cases)."""
+    lens = [int(x) for x in seq_lens]
+    max_len = max(lens + [1])
+    if max_pages is not None:
+        max_len = max(max_len, max_pages * page_size)
+    spec = WorkloadSpec(name, batch, num_q_heads, num_kv_heads, head_dim, page_size, kv_dtype, seed,
+                        tuple(lens), None, max_len)
+    return make_workload(spec, tail=tail)
+
+
+def rebuild_with_rows(w: Workload, q: Optional[torch.Tensor] = None,
+                      k_logical: Optional[torch.Tensor] = None,
+                      v_logical: Optional[torch.Tensor] = None,
+                      perm: Optional[torch.Tensor] = None, tail: str = "nan") -> Workload:
+    """Same pages and lengths as `w`, with some of q / logical K / logical V / the
+    page permutation replaced (values are used as given; the dtypes must match)."""
+    q = w.q if q is None else q
+    k_log = w.k_logical if k_logical is None else k_logical
+    v_log = w.v_logical if v_logical is None else v_logical
+    perm = w.perm if perm is None else perm
+    k_cache, v_cache, bt = scatter_to_pages(k_log, v_log, w.seq_lens.tolist(), w.spec.page_size,
+                                            perm, w.block_table.shape[1], tail)
+    return dataclasses.replace(w, q=q, k_cache=k_cache, v_cache=v_cache, block_table=bt,
+                               k_logical=k_log, v_logical=v_log, perm=perm)
+
+
+def as_numpy_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw storage of a bf16 / fp8 tensor as a contiguous numpy integer array."""
+    t = t.contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()

@@ -1,0 +1,280 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+The pages print no worked example, so every pin is a brute-force library
+computation, a closed form, an invariant or a special case that the definition
+of paged decode attention fixes.  Each is chosen so that a plausible slip in the
+oracle (a dropped term, a wrong sign, a wrong page/slot index, a transposed
+operand, the wrong KV head for a query head, a base-2 LSE) fails one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from paged_kv_decode_amd import workloads as wl
+
+
+def _f64(t):
+    return t.to(torch.float64).numpy() if t.dtype != torch.float8_e4m3fn else t.to(torch.float32).to(torch.float64).numpy()
+
+
+def brute_force(w):
+    """Dense attention over the logical (pre-scatter) rows with scipy's softmax and
+    logsumexp; never sees the page pool or the block table."""
+    B, hq, d = w.q.shape
+    hkv = w.spec.num_kv_heads
+    G = hq // hkv
+    q = _f64(w.q)
+    K = _f64(w.k_logical)
+    V = _f64(w.v_logical)
+    if w.k_scale is not None:
+        K = K * w.k_scale.double().numpy()[None, :, None]
+        V = V * w.v_scale.double().numpy()[None, :, None]
+    out = np.zeros((B, hq, d))
+    lse = np.full((B, hq), -np.inf)
+    for b in range(B):
+        t0, t1 = int(w.token_offsets[b]), int(w.token_offsets[b + 1])
+        if t1 == t0:
+            continue
+        for h in range(hq):
+            g = h // G
+            s = w.scale * (K[t0:t1, g, :] @ q[b, h])
+            out[b, h] = scipy.special.softmax(s) @ V[t0:t1, g, :]
+            lse[b, h] = scipy.special.logsumexp(s)
+    return out, lse
+
+
+def _close(a, b, tol):
+    a, b = np.asarray(a), np.asarray(b)
+    both_inf = np.isneginf(a) & np.isneginf(b)
+    with np.errstate(invalid="ignore"):
+        diff = np.where(both_inf, 0.0, np.abs(a - b))
+    return bool(np.all(diff <= tol * (1.0 + np.abs(np.where(both_inf, 0.0, b)))))
+
+
+SMALL_CASES = [
+    # (B, Hq, Hkv, D, ps, seq_lens, dtype, seed)
+    (1, 1, 1, 8, 1, [5], "bf16", 11),
+    (2, 4, 2, 16, 3, [7, 50], "bf16", 12),
+    (3, 4, 1, 32, 16, [1, 33, 48], "bf16", 13),
+    (3, 8, 4, 16, 3, [49, 2, 17], "bf16", 14),
+    (2, 4, 4, 8, 16, [16, 31], "bf16", 15),
+    (2, 4, 2, 16, 3, [20, 45], "fp8_e4m3", 16),
+    (3, 4, 1, 32, 16, [9, 50, 16], "fp8_e4m3", 17),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES)
+def test_p1_matches_dense_brute_force(case):
+    B, hq, hkv, d, ps, lens, dtype, seed = case
+    w = wl.custom_workload(B, hq, hkv, d, ps, lens, dtype, seed)
+    out, lse = oracle.run_workload(w)
+    ref_out, ref_lse = brute_force(w)
+    assert _close(out, ref_out, 1e-12)
+    assert _close(lse, ref_lse, 1e-12)
+
+
+def test_p1_tiny_named_workload():
+    w = wl.make_workload(wl.WORKLOADS["tiny_b2_d64_ps16"])
+    assert w.num_pages == 10 and w.block_table.shape == (2, 7)
+    assert sorted(w.block_table[w.block_table >= 0].tolist()) == list(range(10))
+    out, lse = oracle.run_workload(w)
+    ref_out, ref_lse = brute_force(w)
+    assert _close(out, ref_out, 1e-12) and _close(lse, ref_lse, 1e-12)
+
+
+def test_closed_form_two_tokens():
+    """q = (1, 0), k0 = (0, 0), k1 = (2, 0), scale 1/2: s = (0, 1); with v0 = (1, 0)
+    and v1 = (0, 1), out = (1, e) / (1 + e) and lse = ln(1 + e)."""
+    w = wl.custom_workload(1, 1, 1, 2, 1, [2], "bf16", 0)
+    bf = torch.bfloat16
+    q = torch.tensor([[[1.0, 0.0]]], dtype=bf)
+    K = torch.tensor([[[0.0, 0.0]], [[2.0, 0.0]]], dtype=bf)
+    V = torch.tensor([[[1.0, 0.0]], [[0.0, 1.0]]], dtype=bf)
+    w = wl.rebuild_with_rows(w, q=q, k_logical=K, v_logical=V)
+    out, lse = oracle.paged_decode(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, 0.5)
+    e = math.e
+    assert abs(out[0, 0, 0] - 1 / (1 + e)) < 1e-15
+    assert abs(out[0, 0, 1] - e / (1 + e)) < 1e-15
+    assert abs(lse[0, 0] - math.log1p(e)) < 1e-15
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_p2_single_token_returns_its_value_row(dtype):
+    w = wl.custom_workload(3, 8, 2, 32, 16, [1, 1, 1], dtype, 21)
+    out, lse = oracle.run_workload(w)
+    V = _f64(w.v_logical)
+    K = _f64(w.k_logical)
+    if w.v_scale is not None:
+        V = V * w.v_scale.double().numpy()[None, :, None]
+        K = K * w.k_scale.double().numpy()[None, :, None]
+    q = _f64(w.q)
+    for b in range(3):
+        for h in range(8):
+            g = h // 4
+            assert np.array_equal(out[b, h], V[b, g])  # exp(0)/1 * v0
+            s = w.scale * float(np.dot(q[b, h], K[b, g]))
+            assert abs(lse[b, h] - s) <= 1e-13 * (1 + abs(s))
+
+
+def test_p3_constant_values_return_the_constant():
+    w = wl.custom_workload(2, 4, 2, 16, 3, [40, 13], "bf16", 31)
+    V = torch.full_like(w.v_logical, 0.7109375)  # exactly representable in bf16
+    w = wl.rebuild_with_rows(w, v_logical=V)
+    out, _ = oracle.run_workload(w)
+    assert np.max(np.abs(out - 0.7109375)) <= 1e-15
+
+
+def test_p4_zero_query_gives_mean_and_log_length():
+    w = wl.custom_workload(2, 4, 1, 16, 16, [37, 100], "bf16", 41)
+    w = wl.rebuild_with_rows(w, q=torch.zeros_like(w.q))
+    out, lse = oracle.run_workload(w)
+    V = _f64(w.v_logical)
+    for b in range(2):
+        t0, t1 = int(w.token_offsets[b]), int(w.token_offsets[b + 1])
+        mean = V[t0:t1, 0, :].mean(axis=0)
+        for h in range(4):
+            assert np.max(np.abs(out[b, h] - mean)) <= 1e-13
+            assert abs(lse[b, h] - math.log(t1 - t0)) <= 1e-13
+
+
+def test_p5_identical_keys_give_dot_plus_log_length():
+    w = wl.custom_workload(2, 4, 2, 16, 3, [25, 8], "bf16", 51)
+    K = w.k_logical.clone()
+    K[:] = K[0:1]
+    w = wl.rebuild_with_rows(w, k_logical=K)
+    out, lse = oracle.run_workload(w)
+    q = _f64(w.q)
+    k = _f64(K[0])
+    for b in range(2):
+        L = int(w.seq_lens[b])
+        for h in range(4):
+            s = w.scale * float(np.dot(q[b, h], k[h // 2]))
+            assert abs(lse[b, h] - (s + math.log(L))) <= 1e-12 * (1 + abs(s))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_p6_page_permutation_invariance_is_bitwise(dtype):
+    w = wl.custom_workload(3, 8, 2, 32, 4, [29, 64, 3], dtype, 61)
+    out1, lse1 = oracle.run_workload(w)
+    g = torch.Generator().manual_seed(999)
+    perm2 = torch.randperm(w.num_pages, generator=g)
+    assert not torch.equal(perm2, w.perm)
+    w2 = wl.rebuild_with_rows(w, perm=perm2)
+    assert not torch.equal(w2.block_table, w.block_table)
+    out2, lse2 = oracle.run_workload(w2)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
+def test_p7_split_count_invariance(splits):
+    w = wl.custom_workload(3, 8, 2, 16, 5, [37, 6, 51], "bf16", 71)
+    out, lse = oracle.run_workload(w)
+    out_s, lse_s = oracle.run_workload(w, num_splits=splits)
+    assert _close(out_s, out, 1e-12) and _close(lse_s, lse, 1e-12)
+
+
+def test_p8_gqa_mapping_consecutive_heads_share_a_kv_head():
+    B, hq, hkv = 2, 8, 4  # G = 2: heads 0,1 -> kv 0; 2,3 -> kv 1; ...
+    w = wl.custom_workload(B, hq, hkv, 16, 4, [10, 19], "bf16", 81)
+    consts = torch.tensor([0.5, -1.25, 2.0, 3.5], dtype=torch.bfloat16)
+    V = consts.view(1, hkv, 1).expand_as(w.v_logical).contiguous()
+    w = wl.rebuild_with_rows(w, v_logical=V)
+    out, _ = oracle.run_workload(w)
+    for h in range(hq):
+        assert np.max(np.abs(out[:, h, :] - float(consts[h // 2]))) <= 1e-15
+
+
+def test_zero_length_sequence_gives_zero_and_minus_inf():
+    w = wl.custom_workload(3, 4, 2, 16, 4, [0, 9, 0], "bf16", 91)
+    out, lse = oracle.run_workload(w)
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+    assert np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2]))
+    assert np.all(np.isfinite(lse[1]))
+    out_s, lse_s = oracle.run_workload(w, num_splits=3)
+    assert _close(out_s, out, 1e-12) and _close(lse_s, lse, 1e-12)
+
+
+def test_thread_count_does_not_change_bits():
+    w = wl.custom_workload(4, 8, 2, 32, 16, [100, 3, 77, 64], "bf16", 95)
+    a = oracle.run_workload(w, nthreads=1)
+    b = oracle.run_workload(w, nthreads=5)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_rows_entry_matches_full_oracle():
+    w = wl.custom_workload(3, 8, 2, 32, 16, [40, 3, 77], "fp8_e4m3", 96)
+    out, lse = oracle.run_workload(w)
+    rows = [0, 5, 9, 23, 17]
+    o_r, l_r = oracle.paged_decode_rows(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens,
+                                        w.scale, rows, w.k_scale, w.v_scale)
+    flat_o, flat_l = out.reshape(-1, 32), lse.reshape(-1)
+    assert np.array_equal(o_r, flat_o[rows]) and np.array_equal(l_r, flat_l[rows])
+
+
+def test_nan_tail_slots_are_never_read():
+    """Parity inputs poison every slot past L; the oracle output stays finite."""
+    w = wl.custom_workload(2, 4, 1, 16, 16, [5, 17], "bf16", 97)
+    assert torch.isnan(w.k_cache.float()).any()
+    out, lse = oracle.run_workload(w)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+def test_bad_block_table_entry_is_reported():
+    w = wl.custom_workload(1, 2, 1, 8, 4, [9], "bf16", 98)
+    bt = w.block_table.clone()
+    bt[0, 2] = w.num_pages  # outside the pool
+    with pytest.raises(ValueError):
+        oracle.paged_decode(w.q, w.k_cache, w.v_cache, bt, w.seq_lens, w.scale)
+
+
+# ---- the log-sum-exp merge ------------------------------------------------
+
+def test_merge_matches_logsumexp_weighting():
+    rng = np.random.default_rng(5)
+    R, S, D = 7, 5, 12
+    o = rng.standard_normal((R, S, D))
+    l = rng.standard_normal((R, S)) * 3
+    l[2, 1] = -np.inf
+    l[4, :] = -np.inf
+    out, lse = oracle.lse_merge(o, l)
+    for r in range(R):
+        if r == 4:
+            assert np.isneginf(lse[r]) and np.all(out[r] == 0)
+            continue
+        ref_lse = scipy.special.logsumexp(l[r])
+        w = scipy.special.softmax(l[r])
+        assert abs(lse[r] - ref_lse) <= 1e-13 * (1 + abs(ref_lse))
+        assert np.max(np.abs(out[r] - w @ o[r])) <= 1e-13
+
+
+def test_merge_of_one_partial_is_identity():
+    rng = np.random.default_rng(6)
+    o = rng.standard_normal((3, 1, 8))
+    l = rng.standard_normal((3, 1))
+    out, lse = oracle.lse_merge(o, l)
+    assert np.allclose(out, o[:, 0], rtol=0, atol=1e-15) and np.allclose(lse, l[:, 0], rtol=0, atol=1e-15)
+
+
+# ---- scalar decoders ------------------------------------------------------
+
+def test_p10_fp8_e4m3fn_decoder_matches_torch_on_all_codes():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32).to(torch.float64).numpy()
+    ours = np.array([oracle.fp8e4m3_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours)) and nan.sum() == 2  # 0x7F and 0xFF
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9  # largest normal, smallest subnormal
+
+
+def test_bf16_decoder_matches_torch_on_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = np.array([oracle.bf16_value(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(ours[~nan], ref[~nan])
