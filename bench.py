@@ -1,0 +1,282 @@
+"""Decode-attention benchmark on one MI355X.
+
+A step is one whole paged decode (split-KV partition kernel, plus the LSE merge
+kernel when more than one split is used) over one batch of synthetic inputs
+already resident in HBM.  Before each timed step a 1 GiB buffer is read and
+written (outside the timed events) so that neither L2 nor the 256 MB Infinity
+Cache holds the KV pages: every step streams them from HBM.  Each step is timed
+with HIP events on the stream the kernels run on; the JSON line reports the
+mean.  The metric is achieved HBM bandwidth, algorithmic bytes / step time,
+where the algorithmic bytes are what the step must move: the K and V rows of
+exactly seq_lens[b] tokens, q, out, lse, the block-table entries used,
+seq_lens and (FP8) the scales.  Split partials and cache effects are not
+counted.
+
+The primary workload is the B=32 Llama-style decode step; the B=128 step is
+reported alongside.  The fp64 CPU oracle is timed on the same host arrays
+(whole workload, all host threads up to 16) as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads NAMES|all]
+                       [--num-splits S] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
+METRIC = "decode-attention achieved HBM GB/s (% of peak) + queries/s at B=32 and B=128"
+PRIMARY = "llama_b32_d128_ps64"
+SECONDARY = "batch128_d128_ps128"
+
+
+def algorithmic_bytes(w, split_kernel_only=False):
+    """Bytes the decode step must move (see the module docstring)."""
+    s = w.spec
+    e = w.k_cache.element_size()
+    lens = [int(x) for x in w.seq_lens]
+    kv = sum(lens) * s.num_kv_heads * s.head_dim * 2 * e
+    q = s.batch * s.num_q_heads * s.head_dim * 2
+    out = s.batch * s.num_q_heads * s.head_dim * 2
+    lse = s.batch * s.num_q_heads * 4
+    bt = sum(-(-L // s.page_size) for L in lens) * 4
+    seq = s.batch * 4
+    scales = 2 * s.num_kv_heads * 4 if w.k_scale is not None else 0
+    if split_kernel_only:
+        return kv + q + bt + seq + scales
+    return kv + q + out + lse + bt + seq + scales
+
+
+class Runner:
+    """Device copies of one workload and the launch sequence of one step."""
+
+    def __init__(self, w, num_splits, device):
+        import torch
+        from paged_kv_decode_amd import binding as B
+        self.B = B
+        self.w = w
+        self.dev = device
+        self.q = w.q.to(device)
+        self.k = w.k_cache.to(device)
+        self.v = w.v_cache.to(device)
+        self.bt = w.block_table.to(device)
+        self.lens = w.seq_lens.to(device)
+        self.ks = None if w.k_scale is None else w.k_scale.to(device)
+        self.vs = None if w.v_scale is None else w.v_scale.to(device)
+        self.dims = B.dims_for(self.q, self.k, self.bt)
+        self.S = num_splits if num_splits > 0 else B.paged_decode_num_splits(self.dims, 0)
+        s = w.spec
+        self.rows = s.batch * s.num_q_heads
+        self.out = torch.empty(self.q.shape, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device=device)
+        if self.S > 1:
+            self.o_part = torch.empty(self.rows * self.S * s.head_dim, dtype=torch.float32, device=device)
+            self.l_part = torch.empty(self.rows * self.S, dtype=torch.float32, device=device)
+        self.stream = torch.cuda.current_stream(device)
+        self.handle = self.stream.cuda_stream
+
+    def kernel1(self):
+        """The partition kernel (direct output when S == 1)."""
+        B = self.B
+        if self.S == 1:
+            st = B.paged_decode(self.dims, self.q, self.k, self.v, self.bt, self.lens, self.ks, self.vs,
+                                self.w.scale, self.out, self.lse, 1, None, 0, self.handle)
+        else:
+            st = B.paged_decode_partials(self.dims, self.q, self.k, self.v, self.bt, self.lens, self.ks,
+                                         self.vs, self.w.scale, self.S, self.o_part, self.l_part,
+                                         self.handle)
+        if st != 0:
+            raise B.PkdError(st)
+
+    def kernel2(self):
+        """The merge kernel (S > 1 only)."""
+        if self.S > 1:
+            st = self.B.paged_decode_merge(self.rows, self.S, self.w.spec.head_dim, self.o_part,
+                                           self.l_part, self.out, self.lse, self.handle)
+            if st != 0:
+                raise self.B.PkdError(st)
+
+    def step(self):
+        self.kernel1()
+        self.kernel2()
+
+
+def bench_one(name, steps, warmup, num_splits, device, scrub):
+    import torch
+    from paged_kv_decode_amd import workloads as wl
+    w = wl.make_workload(wl.WORKLOADS[name], tail="zero")
+    r = Runner(w, num_splits, device)
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        scrub.mul_(-1.0)  # evict L2 / Infinity Cache (outside the events)
+        ev[i][0].record(r.stream)
+        r.kernel1()
+        ev[i][1].record(r.stream)
+        r.kernel2()
+        ev[i][2].record(r.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(steps)]
+    k1_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    # Warm back-to-back timing (KV partly cache-resident when it fits): secondary only.
+    wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wa.record(r.stream)
+    for _ in range(steps):
+        r.step()
+    wb.record(r.stream)
+    torch.cuda.synchronize()
+    warm_ms = wa.elapsed_time(wb) / steps
+
+    step_mean = sum(step_ms) / steps
+    k1_mean = sum(k1_ms) / steps
+    srt = sorted(step_ms)
+    nbytes = algorithmic_bytes(w)
+    k1_bytes = algorithmic_bytes(w, split_kernel_only=r.S > 1)
+    res = dict(
+        workload=name, batch=w.spec.batch, num_q_heads=w.spec.num_q_heads,
+        num_kv_heads=w.spec.num_kv_heads, head_dim=w.spec.head_dim, page_size=w.spec.page_size,
+        kv_dtype=w.spec.kv_dtype, num_splits=r.S, tokens=int(w.seq_lens.sum()),
+        algorithmic_bytes=nbytes, ms_per_step=step_mean,
+        ms_p10=srt[int(0.1 * (steps - 1))], ms_median=srt[(steps - 1) // 2], ms_p90=srt[int(0.9 * (steps - 1))],
+        gbs=nbytes / (step_mean * 1e-3) / 1e9,
+        queries_per_s=w.spec.batch / (step_mean * 1e-3),
+        split_kernel_ms=k1_mean, split_kernel_bytes=k1_bytes,
+        split_kernel_gbs=k1_bytes / (k1_mean * 1e-3) / 1e9,
+        merge_share=(step_mean - k1_mean) / step_mean,
+        warm_ms_per_step=warm_ms, warm_gbs=nbytes / (warm_ms * 1e-3) / 1e9,
+        timed_wall_s=wall,
+    )
+    res["pct_of_peak"] = 100.0 * res["gbs"] / PEAK_HBM_GBS
+    return res, w
+
+
+def cpu_baseline(w, nbytes):
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.run_workload(w, nthreads=threads)
+    dt = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole {w.spec.name} step (all {w.spec.batch} sequences x {w.spec.num_q_heads} "
+                      f"heads), one pass, fp64, {threads} threads on {model}",
+            "seconds": dt, "queries_per_s": w.spec.batch / dt}
+
+
+def traffic_from_profiles(name):
+    """Measured HBM bytes per launch of the partition kernel, if a counter summary
+    for this workload and the current kernel source is committed under profiles/."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    src = os.path.join(ROOT, "paged_kv_decode_amd", "csrc", "split_kv_decode.hip")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != digest:
+            return None
+        return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workloads", default=f"{PRIMARY},{SECONDARY}",
+                    help="comma-separated workload names, or 'all'")
+    ap.add_argument("--num-splits", type=int, default=0, help="0: the library's heuristic")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the decode path runs on a single MI355X and has no "
+              "multi-GPU mode; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_decode_amd import workloads as wl
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    device = torch.device("cuda:0")
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=device).fill_(1.0)  # 1 GiB
+
+    names = list(wl.WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
+    if PRIMARY not in names:
+        names = [PRIMARY] + names
+    results = {}
+    primary_w = None
+    for name in names:
+        res, w = bench_one(name, args.steps, args.warmup, args.num_splits, device, scrub)
+        results[name] = res
+        if name == PRIMARY:
+            primary_w = w
+        else:
+            del w
+        print(f"# {name}: S={res['num_splits']} {res['ms_per_step'] * 1e3:.1f} us/step "
+              f"(p10 {res['ms_p10'] * 1e3:.1f}, p90 {res['ms_p90'] * 1e3:.1f}) "
+              f"{res['gbs']:.0f} GB/s = {res['pct_of_peak']:.1f}% of peak, "
+              f"{res['queries_per_s']:.0f} queries/s; partition kernel {res['split_kernel_gbs']:.0f} GB/s; "
+              f"merge share {100 * res['merge_share']:.1f}%; warm {res['warm_gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+
+    p = results[PRIMARY]
+    roof_achieved = p["split_kernel_gbs"]
+    traffic = traffic_from_profiles(PRIMARY)
+    line = {
+        "metric": METRIC,
+        "value": round(p["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": p["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": PRIMARY, "batch": 32, "num_q_heads": 32, "num_kv_heads": 8,
+                   "head_dim": 128, "page_size": 64, "seq_lens": "uniform integers in [1024, 4096]",
+                   "kv_dtype": "bf16", "num_splits": p["num_splits"], "tokens": p["tokens"],
+                   "algorithmic_bytes": p["algorithmic_bytes"], "timing": "cold HBM (1 GiB scrub before each step), HIP events"},
+        "pct_of_peak": round(p["pct_of_peak"], 2),
+        "queries_per_s": round(p["queries_per_s"], 1),
+        "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(roof_achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "split_kv_kernel<128, bf16>", "kernel_ms": p["split_kernel_ms"],
+                     "kernel_bytes": p["split_kernel_bytes"]},
+        "workloads": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                      for k, v in results.items()},
+    }
+    if SECONDARY in results:
+        s = results[SECONDARY]
+        line["b128"] = {"gbs": round(s["gbs"], 2), "pct_of_peak": round(s["pct_of_peak"], 2),
+                        "queries_per_s": round(s["queries_per_s"], 1), "ms_per_step": s["ms_per_step"],
+                        "num_splits": s["num_splits"]}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(primary_w, p["algorithmic_bytes"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

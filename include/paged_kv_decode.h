@@ -1,0 +1,190 @@
+/*
+ * paged_kv_decode.h -- C ABI of the MI355X (gfx950) paged-KV decode attention library.
+ *
+ * The operation: for each sequence b of a decode batch there is one query
+ * token with Hq heads; its keys and values live in a paged KV cache and are
+ * found through the sequence's block table.  Query head h attends to KV head
+ * floor(h / G), G = Hq / Hkv (grouped-query attention: consecutive query heads
+ * share a KV head):
+ *
+ *   s_t = scale * <q[b,h,:], K[t]>,  out[b,h,:] = sum_t softmax(s)_t * V[t],
+ *   lse[b,h] = ln sum_t exp(s_t)                        (natural log)
+ *
+ * over the tokens t < seq_lens[b], where token t is slot t % page_size of
+ * physical page block_table[b][t / page_size].  This is the paged decode that
+ * the AstrAI commit log for csrc/kernels/attn_paged_decode_split_kv_mma.cuh
+ * builds its split-KV kernels for (per-token page lookup that works for any
+ * page size; one unified paged_decode entry; split partials written without
+ * a memset), and that the b12x 0.30.0 inventory lists in its "Paged attention"
+ * row (BF16 and FP8-E4M3 KV caches, GQA, "split-KV or direct output", a
+ * persistent merge kernel).
+ *
+ * Split-KV: each sequence's tokens are cut into num_splits ranges; each range
+ * produces a normalised partial output and its log-sum-exp, and a merge
+ * combines them (out = sum_j exp(lse_j - lse) * o_j, lse = ln sum_j exp(lse_j)),
+ * the same recombination as the merge_attn_states kernels in the vLLM section
+ * of the sglang fuse/overlap catalogue.  num_splits == 1 writes out and lse
+ * directly with no partials and no second kernel.
+ *
+ * Conventions for every entry point below:
+ *  - Pointers are device pointers unless marked "host".  The caller owns all
+ *    memory; the library allocates and frees nothing and keeps no state other
+ *    than cached device attributes.  Calls are thread-safe.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without synchronising and without any device-to-host
+ *    copy.
+ *  - All arguments are checked on the host before anything is enqueued; on a
+ *    negative status nothing was enqueued and no output was written.
+ *  - Device-side contents are the caller's contract: every block-table entry
+ *    for a page a sequence uses (i < ceil(seq_lens[b] / page_size)) must lie
+ *    in [0, num_pages), and 0 <= seq_lens[b] <= max_pages_per_seq * page_size.
+ *    Entries past a sequence's last page are never read (they may hold -1), nor
+ *    are cache slots past seq_lens[b] in its last page (they may hold
+ *    anything, NaN included).  Violations are undefined behaviour;
+ *    paged_decode_check_tables reports them.
+ *  - Outputs must not alias inputs.  Results are bitwise deterministic for
+ *    fixed inputs and num_splits.
+ */
+#ifndef PAGED_KV_DECODE_H
+#define PAGED_KV_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define PKD_OK 0
+#define PKD_ERR_NULL_POINTER (-1)    /* a required pointer is NULL */
+#define PKD_ERR_BAD_DIMS (-2)        /* a dimension is out of range */
+#define PKD_ERR_GQA (-3)             /* num_q_heads is not a multiple of num_kv_heads */
+#define PKD_ERR_HEAD_DIM (-4)        /* head_dim not in {32, 64, 128, 256} */
+#define PKD_ERR_DTYPE (-5)           /* kv_dtype not a pkd_dtype value */
+#define PKD_ERR_SCALES (-6)          /* FP8 cache without scales, or scales given for BF16 */
+#define PKD_ERR_NUM_SPLITS (-7)      /* num_splits above PKD_MAX_SPLITS */
+#define PKD_ERR_WORKSPACE (-8)       /* workspace NULL or smaller than required */
+#define PKD_ERR_LAUNCH (-9)          /* the HIP runtime refused a launch */
+#define PKD_ERR_DEVICE (-10)         /* no usable gfx950 device is current */
+
+/* Largest num_splits accepted. */
+#define PKD_MAX_SPLITS 512
+
+/* Split boundaries: with S splits, sequence b's split j covers tokens
+ * [j*c, min((j+1)*c, L_b)) where c = PKD_SPLIT_ALIGN * ceil(ceil(L_b / S) / PKD_SPLIT_ALIGN);
+ * trailing splits of a short sequence can be empty. */
+#define PKD_SPLIT_ALIGN 64
+
+/* KV-cache element types.  q and out are always bfloat16. */
+typedef enum {
+  PKD_DTYPE_BF16 = 0,     /* bfloat16 K and V */
+  PKD_DTYPE_FP8_E4M3 = 1  /* OCP FP8 E4M3FN codes with a per-KV-head fp32 scale each for K and V */
+} pkd_dtype;
+
+/* Problem dimensions (passed as a host pointer). */
+typedef struct {
+  int32_t batch;              /* B >= 0 (B == 0 enqueues nothing) */
+  int32_t num_q_heads;        /* Hq >= 1 */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;           /* D in {32, 64, 128, 256} */
+  int32_t page_size;          /* tokens per page, >= 1 (any value) */
+  int32_t num_pages;          /* pages in the pool, >= 1 */
+  int32_t max_pages_per_seq;  /* row length of block_table, >= 1 */
+  int32_t kv_dtype;           /* a pkd_dtype */
+} pkd_dims;
+
+/*
+ * paged_decode -- the whole decode-attention step (split-KV partition + merge).
+ *
+ *   dims         host; see pkd_dims.
+ *   q            [B][Hq][D] bfloat16, contiguous.
+ *   k_cache      [num_pages][page_size][Hkv][D] of kv_dtype, contiguous.
+ *   v_cache      same layout as k_cache.
+ *   block_table  [B][max_pages_per_seq] int32 physical page ids.
+ *   seq_lens     [B] int32 tokens per sequence (0 allowed: out = 0, lse = -inf).
+ *   k_scale      [Hkv] fp32 dequantisation scales for an FP8 cache (K = code * k_scale[kv]);
+ *                must be NULL for BF16.
+ *   v_scale      [Hkv] fp32, as k_scale for V.
+ *   scale        softmax scale applied to q.k (typically 1/sqrt(D)); included in lse.
+ *   out          [B][Hq][D] bfloat16 result (fp32 accumulate, round-to-nearest-even).
+ *   lse          [B][Hq] fp32 natural-log log-sum-exp of the scaled scores, or NULL.
+ *   num_splits   <= 0: chosen by paged_decode_num_splits(dims, max_pages_per_seq * page_size);
+ *                1: direct output (one kernel); 2..PKD_MAX_SPLITS: split-KV + merge (two kernels).
+ *   workspace    device scratch for split partials, at least
+ *                paged_decode_workspace_bytes(dims, S) bytes for the S actually used
+ *                (may be NULL when S == 1).  Its contents on entry do not matter.
+ *   workspace_bytes  size of workspace.
+ *   stream       hipStream_t.
+ * Returns PKD_OK or a negative status.
+ */
+int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                     const float* v_scale, float scale, void* out, float* lse, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_decode_num_splits -- the split count paged_decode uses for num_splits <= 0.
+ * It is sized for the current device's compute units from the number of
+ * (sequence, KV-head) work items and the longest sequence expected,
+ * max_seq_len_hint (<= 0: max_pages_per_seq * page_size).  Host only; returns
+ * a value in [1, PKD_MAX_SPLITS], or a negative status for invalid dims.
+ */
+int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint);
+
+/*
+ * paged_decode_workspace_bytes -- workspace paged_decode needs for num_splits
+ * splits (num_splits <= 0: the heuristic's choice): 0 for one split, otherwise
+ * the fp32 partials [B][Hq][S][D] and [B][Hq][S] plus alignment.  Returns 0 for
+ * invalid dims.
+ */
+size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits);
+
+/*
+ * paged_decode_partials -- the split-KV partition step alone: every split of
+ * every (sequence, query head) writes its normalised partial output and
+ * natural-log LSE.  An empty split writes o = 0 and lse = -inf, so every slot
+ * is written and no clearing is needed.
+ *   o_part    [B][Hq][num_splits][D] fp32.
+ *   lse_part  [B][Hq][num_splits] fp32.
+ *   num_splits 1..PKD_MAX_SPLITS (no heuristic here).
+ * Other arguments as for paged_decode.
+ */
+int32_t paged_decode_partials(const pkd_dims* dims, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, const float* k_scale, const float* v_scale,
+                              float scale, int32_t num_splits, float* o_part, float* lse_part,
+                              void* stream);
+
+/*
+ * paged_decode_merge -- the log-sum-exp merge of split partials alone:
+ * for each of `rows` rows, M = max_j lse_j, lse = M + ln sum_j exp(lse_j - M),
+ * out = sum_j exp(lse_j - lse) * o_j rounded to bfloat16.  Rows whose partials
+ * are all -inf give out = 0, lse = -inf.
+ *   rows       number of rows (B * Hq for paged_decode), >= 0.
+ *   num_splits partials per row, 1..PKD_MAX_SPLITS.
+ *   head_dim   D in {32, 64, 128, 256}.
+ *   o_part     [rows][num_splits][D] fp32;  lse_part [rows][num_splits] fp32.
+ *   out        [rows][D] bfloat16;  lse [rows] fp32 or NULL.
+ */
+int32_t paged_decode_merge(int64_t rows, int32_t num_splits, int32_t head_dim, const float* o_part,
+                           const float* lse_part, void* out, float* lse, void* stream);
+
+/*
+ * paged_decode_check_tables -- optional validation of the device-side
+ * contract (not part of the decode step): counts sequences whose length is
+ * outside [0, max_pages_per_seq * page_size] plus used block-table entries
+ * outside [0, num_pages), and writes the count to *d_error_count (device int32;
+ * written, not accumulated).  Only the used entries are inspected.
+ */
+int32_t paged_decode_check_tables(const pkd_dims* dims, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t* d_error_count, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* paged_decode_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_DECODE_H */

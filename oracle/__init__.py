@@ -41,6 +41,8 @@ def lib():
         L.pkd_oracle_paged_decode_split.restype = _c_int
         L.pkd_oracle_paged_decode_rows.argtypes = common + [_c_int, _p, _p, _p]
         L.pkd_oracle_paged_decode_rows.restype = _c_int
+        L.pkd_oracle_paged_decode_ranges.argtypes = common + [_p, _p, _p, _p]
+        L.pkd_oracle_paged_decode_ranges.restype = _c_int
         L.pkd_oracle_lse_merge.argtypes = [ctypes.c_int64, _c_int, _c_int, _p, _p, _p, _p]
         L.pkd_oracle_lse_merge.restype = None
         L.pkd_oracle_bf16_value.argtypes = [ctypes.c_uint16]
@@ -136,6 +138,20 @@ def paged_decode_rows(q, k_cache, v_cache, block_table, seq_lens, scale, rows,
     lse = np.empty((rows.size,), np.float64)
     _check(lib().pkd_oracle_paged_decode_rows(*a.head(), int(rows.size), _ptr(rows), _ptr(out),
                                               _ptr(lse)))
+    return out, lse
+
+
+def paged_decode_ranges(q, k_cache, v_cache, block_table, seq_lens, scale, t_begin, t_end,
+                        k_scale=None, v_scale=None):
+    """Plain definition over tokens [t_begin[b], t_end[b]) of each sequence."""
+    a = _Args(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale, v_scale)
+    B, hq, _, d = a.dims[:4]
+    tb = np.ascontiguousarray(np.asarray(t_begin, dtype=np.int32))
+    te = np.ascontiguousarray(np.asarray(t_end, dtype=np.int32))
+    assert tb.shape == (B,) and te.shape == (B,)
+    out = np.empty((B, hq, d), np.float64)
+    lse = np.empty((B, hq), np.float64)
+    _check(lib().pkd_oracle_paged_decode_ranges(*a.head(), _ptr(tb), _ptr(te), _ptr(out), _ptr(lse)))
     return out, lse
 
 

@@ -341,3 +341,36 @@ int pkd_oracle_paged_decode_rows(int batch, int hq, int hkv, int head_dim, int p
   }
   return PKD_ORACLE_OK;
 }
+
+/* Plain definition restricted to one token range per sequence: row
+ * (b, h) attends over tokens [t_begin[b], t_end[b]) only (an empty range gives
+ * out = 0, lse = -inf).  Used to check split partials one split at a time.
+ * out [B][Hq][D], lse [B][Hq]; single thread. */
+int pkd_oracle_paged_decode_ranges(int batch, int hq, int hkv, int head_dim, int page_size,
+                                   int num_pages, int max_pages, int kv_fp8, const uint16_t* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const float* k_scale, const float* v_scale, double scale,
+                                   const int32_t* t_begin, const int32_t* t_end, double* out,
+                                   double* lse) {
+  problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
+               q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+               0, out, lse};
+  if (batch < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || head_dim < 1 || page_size < 1 ||
+      !t_begin || !t_end || !out || !lse)
+    return PKD_ORACLE_BAD_ARG;
+  if (kv_fp8 && (!k_scale || !v_scale)) return PKD_ORACLE_BAD_ARG;
+  for (int b = 0; b < batch; ++b) {
+    int st = check_sequence(&P, b);
+    if (st != PKD_ORACLE_OK) return st;
+    int t0 = t_begin[b], t1 = t_end[b];
+    if (t0 < 0 || t1 > seq_lens[b]) return PKD_ORACLE_BAD_ARG;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(t1 > t0 ? t1 - t0 : 1));
+    if (!s) return PKD_ORACLE_NO_MEM;
+    for (int h = 0; h < hq; ++h)
+      lse[(int64_t)b * hq + h] =
+          attend_range(&P, b, h, t0, t1, out + ((int64_t)b * hq + h) * head_dim, s);
+    free(s);
+  }
+  return PKD_ORACLE_OK;
+}

@@ -1,0 +1,221 @@
+"""Thin ctypes binding over libpaged_kv_decode.so, with the C ABI's names.
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels.  Pointer arguments accept a torch tensor (its data_ptr() is passed), a
+plain integer address, or None (NULL).  The raw functions return the library's
+integer status; `decode` is a convenience that infers the dimensions from torch
+tensors, allocates out / lse / workspace with torch.empty on the tensors'
+device and raises PkdError on a negative status.
+
+The library must have been built (paged_kv_decode_amd/build.py); if it is
+missing this module raises on import.  There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpaged_kv_decode.so")
+
+PKD_OK = 0
+PKD_ERR_NULL_POINTER = -1
+PKD_ERR_BAD_DIMS = -2
+PKD_ERR_GQA = -3
+PKD_ERR_HEAD_DIM = -4
+PKD_ERR_DTYPE = -5
+PKD_ERR_SCALES = -6
+PKD_ERR_NUM_SPLITS = -7
+PKD_ERR_WORKSPACE = -8
+PKD_ERR_LAUNCH = -9
+PKD_ERR_DEVICE = -10
+PKD_MAX_SPLITS = 512
+PKD_SPLIT_ALIGN = 64
+PKD_DTYPE_BF16 = 0
+PKD_DTYPE_FP8_E4M3 = 1
+
+EXPORTED = ("paged_decode", "paged_decode_num_splits", "paged_decode_workspace_bytes",
+            "paged_decode_partials", "paged_decode_merge", "paged_decode_check_tables",
+            "paged_decode_status_string")
+
+
+class PkdError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"paged_kv_decode status {status}: {paged_decode_status_string(status)}")
+        self.status = status
+
+
+class pkd_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run paged_kv_decode_amd/build.py "
+                      "(or __graft_entry__.build()) first")
+
+# PyTorch bundles its own HIP runtime (SONAME libamdhip64.so.7).  Loading torch
+# first makes the library's libamdhip64.so.7 dependency resolve to that same
+# runtime, so torch's device pointers and stream handles are valid in the
+# library's calls.  Loading the library first would map a second HIP runtime
+# from /opt/rocm next to torch's, which cannot share streams or devices.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError("two HIP runtimes are mapped in this process "
+                      f"({sorted(_hip_runtimes_mapped())}); import torch before loading "
+                      "libpaged_kv_decode.so")
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_dims_p = ctypes.POINTER(pkd_dims)
+
+_lib.paged_decode.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _i32,
+                              _p, ctypes.c_size_t, _p]
+_lib.paged_decode.restype = _i32
+_lib.paged_decode_num_splits.argtypes = [_dims_p, _i32]
+_lib.paged_decode_num_splits.restype = _i32
+_lib.paged_decode_workspace_bytes.argtypes = [_dims_p, _i32]
+_lib.paged_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.paged_decode_partials.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _i32,
+                                       _p, _p, _p]
+_lib.paged_decode_partials.restype = _i32
+_lib.paged_decode_merge.argtypes = [ctypes.c_int64, _i32, _i32, _p, _p, _p, _p, _p]
+_lib.paged_decode_merge.restype = _i32
+_lib.paged_decode_check_tables.argtypes = [_dims_p, _p, _p, _p, _p]
+_lib.paged_decode_check_tables.restype = _i32
+_lib.paged_decode_status_string.argtypes = [_i32]
+_lib.paged_decode_status_string.restype = ctypes.c_char_p
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _dims_ref(dims):
+    if dims is None:
+        return None
+    return ctypes.byref(dims)
+
+
+def paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, out, lse,
+                 num_splits, workspace, workspace_bytes, stream) -> int:
+    return _lib.paged_decode(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                             _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), float(scale), _ptr(out),
+                             _ptr(lse), int(num_splits), _ptr(workspace), int(workspace_bytes),
+                             _ptr(stream))
+
+
+def paged_decode_num_splits(dims, max_seq_len_hint: int = 0) -> int:
+    return _lib.paged_decode_num_splits(_dims_ref(dims), int(max_seq_len_hint))
+
+
+def paged_decode_workspace_bytes(dims, num_splits: int) -> int:
+    return _lib.paged_decode_workspace_bytes(_dims_ref(dims), int(num_splits))
+
+
+def paged_decode_partials(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+                          num_splits, o_part, lse_part, stream) -> int:
+    return _lib.paged_decode_partials(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(block_table), _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale),
+                                      float(scale), int(num_splits), _ptr(o_part), _ptr(lse_part),
+                                      _ptr(stream))
+
+
+def paged_decode_merge(rows, num_splits, head_dim, o_part, lse_part, out, lse, stream) -> int:
+    return _lib.paged_decode_merge(int(rows), int(num_splits), int(head_dim), _ptr(o_part),
+                                   _ptr(lse_part), _ptr(out), _ptr(lse), _ptr(stream))
+
+
+def paged_decode_check_tables(dims, block_table, seq_lens, d_error_count, stream) -> int:
+    return _lib.paged_decode_check_tables(_dims_ref(dims), _ptr(block_table), _ptr(seq_lens),
+                                          _ptr(d_error_count), _ptr(stream))
+
+
+def paged_decode_status_string(status: int) -> str:
+    return _lib.paged_decode_status_string(int(status)).decode()
+
+
+# ---- torch conveniences (memory and streams only) ---------------------------
+
+def dims_for(q, k_cache, block_table) -> pkd_dims:
+    """pkd_dims from torch tensors q [B,Hq,D], k_cache [P,ps,Hkv,D], block_table [B,MP]."""
+    import torch
+    B, hq, d = q.shape
+    num_pages, ps, hkv, d2 = k_cache.shape
+    if d2 != d:
+        raise ValueError("q and k_cache head_dim differ")
+    if k_cache.dtype == torch.bfloat16:
+        kvd = PKD_DTYPE_BF16
+    elif k_cache.dtype == torch.float8_e4m3fn:
+        kvd = PKD_DTYPE_FP8_E4M3
+    else:
+        raise TypeError(f"unsupported KV-cache dtype {k_cache.dtype}")
+    return pkd_dims(B, hq, hkv, d, ps, num_pages, block_table.shape[1], kvd)
+
+
+def current_stream_handle(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=None, v_scale=None,
+           num_splits: int = 0, out=None, lse=None, workspace=None, stream: Optional[int] = None):
+    """Run paged_decode on torch device tensors; returns (out bf16 [B,Hq,D], lse fp32 [B,Hq])."""
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seq_lens", seq_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must match")
+    dims = dims_for(q, k_cache, block_table)
+    dev = q.device
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    S = num_splits if num_splits > 0 else paged_decode_num_splits(dims, 0)
+    if S < 0:
+        raise PkdError(S)
+    need = paged_decode_workspace_bytes(dims, S)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = current_stream_handle(dev)
+    st = paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, out,
+                      lse, S, workspace, ws_bytes, stream)
+    if st != PKD_OK:
+        raise PkdError(st)
+    return out, lse

@@ -1,0 +1,174 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before anything is enqueued.
+
+No compute call is made here: pointer arguments are fake non-NULL addresses,
+which the library never dereferences on an argument error.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_kv_decode.h")
+
+b = pytest.importorskip("paged_kv_decode_amd.binding",
+                        reason="HIP library not built (run __graft_entry__.build())")
+
+FAKE = 0x1000  # a non-NULL address that is never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def header_defines():
+    vals = {}
+    for name, val in re.findall(r"#define\s+(PKD_\w+)\s+\(?(-?\d+)\)?", open(HEADER).read()):
+        vals[name] = int(val)
+    return vals
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(b.EXPORTED)
+    lib = ctypes.CDLL(b.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_constants_match_header():
+    vals = header_defines()
+    for name, v in vals.items():
+        if hasattr(b, name):
+            assert getattr(b, name) == v, name
+    assert vals["PKD_OK"] == 0 and vals["PKD_MAX_SPLITS"] == b.PKD_MAX_SPLITS
+
+
+def test_dims_struct_layout():
+    assert ctypes.sizeof(b.pkd_dims) == 8 * 4
+
+
+def test_status_strings_are_distinct():
+    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10]
+    texts = [b.paged_decode_status_string(c) for c in codes]
+    assert len(set(texts)) == len(texts)
+    assert b.paged_decode_status_string(-12345) == "unknown status"
+
+
+def dims(**kw):
+    base = dict(batch=2, num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=16, num_pages=10,
+                max_pages_per_seq=7, kv_dtype=b.PKD_DTYPE_BF16)
+    base.update(kw)
+    return b.pkd_dims(*[base[f] for f, _ in b.pkd_dims._fields_])
+
+
+def call(d, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, ks=None, vs=None, scale=0.125, out=FAKE,
+         lse=None, S=1, ws=None, ws_bytes=0):
+    return b.paged_decode(d, q, k, v, bt, lens, ks, vs, scale, out, lse, S, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), b.PKD_ERR_BAD_DIMS),
+    (dict(num_q_heads=0), b.PKD_ERR_BAD_DIMS),
+    (dict(num_kv_heads=0), b.PKD_ERR_BAD_DIMS),
+    (dict(page_size=0), b.PKD_ERR_BAD_DIMS),
+    (dict(num_pages=0), b.PKD_ERR_BAD_DIMS),
+    (dict(max_pages_per_seq=0), b.PKD_ERR_BAD_DIMS),
+    (dict(num_q_heads=6, num_kv_heads=4), b.PKD_ERR_GQA),
+    (dict(head_dim=96), b.PKD_ERR_HEAD_DIM),
+    (dict(head_dim=512), b.PKD_ERR_HEAD_DIM),
+    (dict(kv_dtype=7), b.PKD_ERR_DTYPE),
+    (dict(max_pages_per_seq=2**20, page_size=2**12), b.PKD_ERR_BAD_DIMS),
+])
+def test_bad_dims_are_rejected(kw, status):
+    d = dims(**kw)
+    assert call(d) == status
+    assert b.paged_decode_num_splits(d, 0) == status
+    assert b.paged_decode_workspace_bytes(d, 2) == 0
+
+
+def test_null_pointers_are_rejected():
+    d = dims()
+    assert b.paged_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1, FAKE, None, 1, None, 0,
+                          None) == b.PKD_ERR_NULL_POINTER
+    for kw in ("q", "k", "v", "bt", "lens", "out"):
+        assert call(d, **{kw: None}) == b.PKD_ERR_NULL_POINTER, kw
+
+
+def test_fp8_scales_rules():
+    d8 = dims(kv_dtype=b.PKD_DTYPE_FP8_E4M3)
+    assert call(d8) == b.PKD_ERR_SCALES
+    assert call(d8, ks=FAKE) == b.PKD_ERR_SCALES
+    assert call(d8, vs=FAKE) == b.PKD_ERR_SCALES
+    assert call(dims(), ks=FAKE, vs=FAKE) == b.PKD_ERR_SCALES
+
+
+def test_non_finite_scale_is_rejected():
+    assert call(dims(), scale=float("nan")) == b.PKD_ERR_BAD_DIMS
+    assert call(dims(), scale=float("inf")) == b.PKD_ERR_BAD_DIMS
+
+
+def test_num_splits_and_workspace_rules():
+    d = dims()
+    assert call(d, S=b.PKD_MAX_SPLITS + 1) == b.PKD_ERR_NUM_SPLITS
+    need = b.paged_decode_workspace_bytes(d, 3)
+    # [B][Hq][S][D] fp32 + [B][Hq][S] fp32, each rounded up to 256 bytes
+    assert need == 2 * 4 * 3 * 64 * 4 + 256
+    assert call(d, S=3) == b.PKD_ERR_WORKSPACE
+    assert call(d, S=3, ws=FAKE, ws_bytes=need - 1) == b.PKD_ERR_WORKSPACE
+    assert b.paged_decode_workspace_bytes(d, 1) == 0
+    assert b.paged_decode_workspace_bytes(d, b.PKD_MAX_SPLITS + 1) == 0
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    """With correct arguments and no usable GPU the library reports it instead of
+    computing anything (on a GPU machine this case is covered by the GPU tests)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    d = dims()
+    assert call(d) == b.PKD_ERR_DEVICE
+    need = b.paged_decode_workspace_bytes(d, 3)
+    assert call(d, S=3, ws=FAKE, ws_bytes=need) == b.PKD_ERR_DEVICE
+    assert call(dims(batch=0)) == b.PKD_OK  # an empty batch enqueues nothing
+
+
+def test_partials_and_merge_argument_checks():
+    d = dims()
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1)
+    assert b.paged_decode_partials(d, *args, 0, FAKE, FAKE, None) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_partials(d, *args, 2, None, FAKE, None) == b.PKD_ERR_NULL_POINTER
+    assert b.paged_decode_merge(8, 2, 100, FAKE, FAKE, FAKE, None, None) == b.PKD_ERR_HEAD_DIM
+    assert b.paged_decode_merge(8, 0, 64, FAKE, FAKE, FAKE, None, None) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_merge(-1, 2, 64, FAKE, FAKE, FAKE, None, None) == b.PKD_ERR_BAD_DIMS
+    assert b.paged_decode_merge(8, 2, 64, FAKE, None, FAKE, None, None) == b.PKD_ERR_NULL_POINTER
+    assert b.paged_decode_merge(0, 2, 64, FAKE, FAKE, FAKE, None, None) == b.PKD_OK
+    assert b.paged_decode_check_tables(d, None, FAKE, FAKE, None) == b.PKD_ERR_NULL_POINTER
+
+
+def test_heuristic_is_in_range_and_monotone_in_work():
+    """The split heuristic: one split when (sequence, KV-head) items already fill
+    the device, more when they do not, never above the cap or the length bound."""
+    big = dims(batch=128, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
+               num_pages=2048, max_pages_per_seq=16)
+    assert b.paged_decode_num_splits(big, 0) == 1
+    b32 = dims(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
+               num_pages=1500, max_pages_per_seq=64)
+    s32 = b.paged_decode_num_splits(b32, 0)
+    assert 2 <= s32 <= 16
+    long1 = dims(batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=64,
+                 num_pages=2048, max_pages_per_seq=2048)
+    s1 = b.paged_decode_num_splits(long1, 0)
+    assert s32 < s1 <= b.PKD_MAX_SPLITS
+    assert b.paged_decode_num_splits(long1, 256) == 1  # a short hint caps the split count
+    tiny = dims()
+    assert b.paged_decode_num_splits(tiny, 0) == 1
+
+
+def test_one_hip_runtime_in_process():
+    """The library binds to PyTorch's HIP runtime instead of mapping a second one."""
+    assert len(b._hip_runtimes_mapped()) <= 1
