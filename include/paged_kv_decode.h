@@ -71,9 +71,21 @@ extern "C" {
 /* Largest num_splits accepted. */
 #define PKD_MAX_SPLITS 512
 
+/* Special num_splits values.  PKD_SPLITS_AUTO lets the library choose
+ * (paged_decode_num_splits).  PKD_SPLITS_BALANCED selects the balanced
+ * partition: a persistent grid sized to the device in which every workgroup
+ * gets an equal share of all (sequence, KV head, 16-token group) work and
+ * writes one partial per (workgroup, segment) piece, merged afterwards.  It needs
+ * page_size % 16 == 0 and batch <= PKD_BALANCED_MAX_BATCH. */
+#define PKD_SPLITS_AUTO 0
+#define PKD_SPLITS_BALANCED (-1000)
+#define PKD_BALANCED_MAX_BATCH 1024
+
 /* Split boundaries: with S splits, sequence b's split j covers tokens
- * [j*c, min((j+1)*c, L_b)) where c = PKD_SPLIT_ALIGN * ceil(ceil(L_b / S) / PKD_SPLIT_ALIGN);
- * trailing splits of a short sequence can be empty. */
+ * [min(j*c, L_b), min((j+1)*c, L_b)) where
+ * c = PKD_SPLIT_ALIGN * ceil(ceil(max_pages_per_seq * page_size / S) / PKD_SPLIT_ALIGN),
+ * the same for every sequence of the batch, so that every split carries about
+ * the same work; trailing splits of shorter sequences are empty. */
 #define PKD_SPLIT_ALIGN 64
 
 /* KV-cache element types.  q and out are always bfloat16. */
@@ -109,11 +121,13 @@ typedef struct {
  *   scale        softmax scale applied to q.k (typically 1/sqrt(D)); included in lse.
  *   out          [B][Hq][D] bfloat16 result (fp32 accumulate, round-to-nearest-even).
  *   lse          [B][Hq] fp32 natural-log log-sum-exp of the scaled scores, or NULL.
- *   num_splits   <= 0: chosen by paged_decode_num_splits(dims, max_pages_per_seq * page_size);
- *                1: direct output (one kernel); 2..PKD_MAX_SPLITS: split-KV + merge (two kernels).
- *   workspace    device scratch for split partials, at least
- *                paged_decode_workspace_bytes(dims, S) bytes for the S actually used
- *                (may be NULL when S == 1).  Its contents on entry do not matter.
+ *   num_splits   PKD_SPLITS_AUTO: chosen by paged_decode_num_splits(dims, 0);
+ *                1: direct output (one kernel); 2..PKD_MAX_SPLITS: split-KV + merge (two kernels);
+ *                PKD_SPLITS_BALANCED: balanced partition + merge (two kernels).
+ *                Any other value is an error.
+ *   workspace    device scratch for partials, at least paged_decode_workspace_bytes(dims,
+ *                num_splits) bytes (may be NULL when that is 0).  Its contents on entry do
+ *                not matter.
  *   workspace_bytes  size of workspace.
  *   stream       hipStream_t.
  * Returns PKD_OK or a negative status.
@@ -124,19 +138,40 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * paged_decode_num_splits -- the split count paged_decode uses for num_splits <= 0.
- * It is sized for the current device's compute units from the number of
- * (sequence, KV-head) work items and the longest sequence expected,
+ * paged_decode_partition / paged_decode_finish -- the two phases of paged_decode
+ * for a split mode (num_splits = 2..PKD_MAX_SPLITS or PKD_SPLITS_BALANCED, or
+ * PKD_SPLITS_AUTO when it resolves to one of them; a resolution to direct output
+ * is PKD_ERR_NUM_SPLITS here): the partition kernel writes its partials into
+ * the workspace, then the merge kernel reads them and writes out and lse.
+ * Issued back to back on one stream with the same dims, num_splits and
+ * workspace they are exactly paged_decode; split apart they let a caller
+ * schedule or time the phases.  Arguments as for paged_decode.
+ */
+int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const float* k_scale, const float* v_scale,
+                               float scale, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void* workspace,
+                            size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * paged_decode_num_splits -- what paged_decode does for PKD_SPLITS_AUTO: 1 (direct
+ * output) when the (sequence, KV-head) work items alone fill the current
+ * device's compute units, otherwise PKD_SPLITS_BALANCED where it applies, else
+ * a split count in [2, PKD_MAX_SPLITS] bounded by the longest sequence expected,
  * max_seq_len_hint (<= 0: max_pages_per_seq * page_size).  Host only; returns
- * a value in [1, PKD_MAX_SPLITS], or a negative status for invalid dims.
+ * that value, or a status in [-10, -1] for invalid dims.
  */
 int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint);
 
 /*
  * paged_decode_workspace_bytes -- workspace paged_decode needs for num_splits
- * splits (num_splits <= 0: the heuristic's choice): 0 for one split, otherwise
- * the fp32 partials [B][Hq][S][D] and [B][Hq][S] plus alignment.  Returns 0 for
- * invalid dims.
+ * (PKD_SPLITS_AUTO: the heuristic's choice): 0 for one split; for S splits the
+ * fp32 partials [B][Hq][S][D] and [B][Hq][S]; for PKD_SPLITS_BALANCED the fp32
+ * partials of (W + B*Hkv*ceil(G/16)) slots of min(G,16) heads, W the
+ * workgroups of the device-sized grid, plus B+1 int64 prefix sums; each part rounded up to
+ * 256 bytes.  Returns 0 for invalid dims or an unsupported num_splits.
  */
 size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits);
 

@@ -32,12 +32,15 @@ PKD_ERR_LAUNCH = -9
 PKD_ERR_DEVICE = -10
 PKD_MAX_SPLITS = 512
 PKD_SPLIT_ALIGN = 64
+PKD_SPLITS_AUTO = 0
+PKD_SPLITS_BALANCED = -1000
+PKD_BALANCED_MAX_BATCH = 1024
 PKD_DTYPE_BF16 = 0
 PKD_DTYPE_FP8_E4M3 = 1
 
-EXPORTED = ("paged_decode", "paged_decode_num_splits", "paged_decode_workspace_bytes",
-            "paged_decode_partials", "paged_decode_merge", "paged_decode_check_tables",
-            "paged_decode_status_string")
+EXPORTED = ("paged_decode", "paged_decode_partition", "paged_decode_finish", "paged_decode_num_splits",
+            "paged_decode_workspace_bytes", "paged_decode_partials", "paged_decode_merge",
+            "paged_decode_check_tables", "paged_decode_status_string")
 
 
 class PkdError(RuntimeError):
@@ -91,6 +94,11 @@ _dims_p = ctypes.POINTER(pkd_dims)
 _lib.paged_decode.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _i32,
                               _p, ctypes.c_size_t, _p]
 _lib.paged_decode.restype = _i32
+_lib.paged_decode_partition.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _i32,
+                                        _p, ctypes.c_size_t, _p]
+_lib.paged_decode_partition.restype = _i32
+_lib.paged_decode_finish.argtypes = [_dims_p, _i32, _p, ctypes.c_size_t, _p, _p, _p]
+_lib.paged_decode_finish.restype = _i32
 _lib.paged_decode_num_splits.argtypes = [_dims_p, _i32]
 _lib.paged_decode_num_splits.restype = _i32
 _lib.paged_decode_workspace_bytes.argtypes = [_dims_p, _i32]
@@ -130,6 +138,19 @@ def paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_sc
                              _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), float(scale), _ptr(out),
                              _ptr(lse), int(num_splits), _ptr(workspace), int(workspace_bytes),
                              _ptr(stream))
+
+
+def paged_decode_partition(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+                           num_splits, workspace, workspace_bytes, stream) -> int:
+    return _lib.paged_decode_partition(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(block_table), _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale),
+                                       float(scale), int(num_splits), _ptr(workspace), int(workspace_bytes),
+                                       _ptr(stream))
+
+
+def paged_decode_finish(dims, num_splits, workspace, workspace_bytes, out, lse, stream) -> int:
+    return _lib.paged_decode_finish(_dims_ref(dims), int(num_splits), _ptr(workspace), int(workspace_bytes),
+                                    _ptr(out), _ptr(lse), _ptr(stream))
 
 
 def paged_decode_num_splits(dims, max_seq_len_hint: int = 0) -> int:
@@ -205,8 +226,8 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=Non
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-    S = num_splits if num_splits > 0 else paged_decode_num_splits(dims, 0)
-    if S < 0:
+    S = num_splits if num_splits != PKD_SPLITS_AUTO else paged_decode_num_splits(dims, 0)
+    if -10 <= S < 0:
         raise PkdError(S)
     need = paged_decode_workspace_bytes(dims, S)
     if workspace is None and need > 0:

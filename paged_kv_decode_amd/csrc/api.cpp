@@ -53,6 +53,53 @@ int32_t check_dims(const pkd_dims* d) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workgroups of the balanced grid: as many as the device holds resident
+// at once (compute units x resident workgroups per unit for this kernel
+// instance), so that no workgroup waits for another to finish.  Cached per
+// device and instance.
+std::atomic<int> g_bal_blocks[kMaxDevices][8];  // [device][log2(D/32) * 2 + fp8], 0 = not queried
+
+int balanced_workers(const pkd_dims& d) {
+  const int cus = current_cu_count();
+  int dev = -1;
+  (void)hipGetDevice(&dev);
+  const int fp8 = d.kv_dtype == PKD_DTYPE_FP8_E4M3;
+  const int idx = (d.head_dim == 32 ? 0 : d.head_dim == 64 ? 1 : d.head_dim == 128 ? 2 : 3) * 2 + fp8;
+  int blocks = 0;
+  if (dev >= 0 && dev < kMaxDevices) blocks = g_bal_blocks[dev][idx].load(std::memory_order_relaxed);
+  if (blocks <= 0 && cus > 0) {
+    blocks = pkd::balanced_blocks_per_cu(d.head_dim, fp8 != 0);
+    if (blocks > 0 && dev >= 0 && dev < kMaxDevices) g_bal_blocks[dev][idx].store(blocks, std::memory_order_relaxed);
+  }
+  if (blocks <= 0) blocks = pkd::kBalancedWgsPerCuDefault;
+  return (cus > 0 ? cus : 256) * blocks;
+}
+
+int heads_per_slot(const pkd_dims& d) {
+  const int G = d.num_q_heads / d.num_kv_heads;
+  return G < pkd::kHeadsPerGroup ? G : pkd::kHeadsPerGroup;
+}
+
+// Whether the balanced partition applies: aligned 16-token groups lie in one
+// page, the prefix scan takes the batch, and the work-space arithmetic stays
+// far inside int64 (T * workers < 2^62).
+bool balanced_ok(const pkd_dims& d) {
+  if (d.page_size % 16 != 0 || d.batch > PKD_BALANCED_MAX_BATCH) return false;
+  const int64_t groups = ((int64_t)d.max_pages_per_seq * d.page_size + 15) / 16;
+  const int64_t T = groups * d.batch * d.num_kv_heads * head_groups(d);
+  return T < ((int64_t)1 << 46);
+}
+
+size_t balanced_bytes(const pkd_dims& d, size_t* lse_offset, size_t* prefix_offset) {
+  const size_t slots = (size_t)balanced_workers(d) + (size_t)d.batch * d.num_kv_heads * head_groups(d);
+  const size_t hpg = (size_t)heads_per_slot(d);
+  const size_t o = align256(slots * hpg * d.head_dim * sizeof(float));
+  const size_t l = align256(slots * hpg * sizeof(float));
+  if (lse_offset) *lse_offset = o;
+  if (prefix_offset) *prefix_offset = o + l;
+  return o + l + align256(((size_t)d.batch + 1) * sizeof(int64_t));
+}
+
 size_t partial_bytes(const pkd_dims& d, int S, size_t* lse_offset) {
   const size_t rows = (size_t)d.batch * d.num_q_heads;
   const size_t o = align256(rows * (size_t)S * d.head_dim * sizeof(float));
@@ -60,11 +107,23 @@ size_t partial_bytes(const pkd_dims& d, int S, size_t* lse_offset) {
   return o + align256(rows * (size_t)S * sizeof(float));
 }
 
+// Tokens per split: the longest sequence the block table can hold, cut into S
+// equal pieces rounded up to PKD_SPLIT_ALIGN.  Every split of every sequence
+// then covers the same number of tokens (or is the sequence's shorter last
+// piece, or empty), so workgroups carry equal work whatever the length mix.
+int32_t split_chunk(const pkd_dims& d, int S) {
+  const int64_t cap = (int64_t)d.max_pages_per_seq * d.page_size;
+  const int64_t per = (cap + S - 1) / S;
+  const int64_t c = (per + PKD_SPLIT_ALIGN - 1) / PKD_SPLIT_ALIGN * PKD_SPLIT_ALIGN;
+  return (int32_t)(c < INT32_MAX ? c : INT32_MAX);
+}
+
 int32_t heuristic_splits(const pkd_dims& d, int32_t max_len) {
   const int cus = current_cu_count();
   const int64_t target = 4LL * (cus > 0 ? cus : 256);  // workgroups to keep every CU busy
   const int64_t work = (int64_t)d.batch * d.num_kv_heads * head_groups(d);
   if (work <= 0 || work >= target) return 1;
+  if (balanced_ok(d)) return PKD_SPLITS_BALANCED;
   int64_t s = (target + work - 1) / work;
   const int64_t by_len = (max_len + 255) / 256;  // keep at least ~256 tokens per split
   if (s > by_len) s = by_len;
@@ -92,6 +151,7 @@ pkd::SplitParams make_split_params(const pkd_dims& d, const void* q, const void*
   p.page_size = d.page_size;
   p.max_pages = d.max_pages_per_seq;
   p.num_splits = S;
+  p.chunk = split_chunk(d, S);
   return p;
 }
 
@@ -131,8 +191,9 @@ int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint) 
 size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits) {
   if (check_dims(dims) != PKD_OK) return 0;
   int S = num_splits;
-  if (S <= 0) S = heuristic_splits(*dims, dims->max_pages_per_seq * dims->page_size);
-  if (S > PKD_MAX_SPLITS) return 0;
+  if (S == PKD_SPLITS_AUTO) S = heuristic_splits(*dims, dims->max_pages_per_seq * dims->page_size);
+  if (S == PKD_SPLITS_BALANCED) return balanced_ok(*dims) ? balanced_bytes(*dims, nullptr, nullptr) : 0;
+  if (S < 1 || S > PKD_MAX_SPLITS) return 0;
   if (S == 1) return 0;
   return partial_bytes(*dims, S, nullptr);
 }
@@ -162,10 +223,110 @@ int32_t paged_decode_merge(int64_t rows, int32_t num_splits, int32_t head_dim, c
   if (!o_part || !lse_part || !out) return PKD_ERR_NULL_POINTER;
   if (rows == 0) return PKD_OK;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
-  pkd::MergeParams m{o_part, lse_part, static_cast<uint16_t*>(out), lse, rows, num_splits};
+  pkd::MergeParams m{};
+  m.o_part = o_part;
+  m.lse_part = lse_part;
+  m.out = static_cast<uint16_t*>(out);
+  m.lse = lse;
+  m.rows = rows;
+  m.num_splits = num_splits;
   return pkd::launch_lse_merge(m, head_dim, static_cast<hipStream_t>(stream)) == hipSuccess
              ? PKD_OK : PKD_ERR_LAUNCH;
 }
+
+}  // extern "C"
+
+namespace {
+
+// Resolved split mode of one call.
+struct Plan {
+  int S;           // 1 = direct output, 2.. = grid splits, PKD_SPLITS_BALANCED
+  bool balanced;
+  size_t need;     // workspace bytes
+  size_t lse_off, prefix_off;
+};
+
+int32_t make_plan(const pkd_dims& d, int32_t num_splits, Plan* pl) {
+  int S = num_splits;
+  if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size);
+  pl->S = S;
+  pl->balanced = S == PKD_SPLITS_BALANCED;
+  if (pl->balanced ? !balanced_ok(d) : (S < 1 || S > PKD_MAX_SPLITS)) return PKD_ERR_NUM_SPLITS;
+  pl->lse_off = pl->prefix_off = 0;
+  pl->need = pl->balanced ? balanced_bytes(d, &pl->lse_off, &pl->prefix_off)
+                          : (S > 1 ? partial_bytes(d, S, &pl->lse_off) : 0);
+  return PKD_OK;
+}
+
+pkd::BalancedParams make_balanced_params(const pkd_dims& d, const void* q, const void* k, const void* v,
+                                         const int32_t* bt, const int32_t* lens, const float* ks,
+                                         const float* vs, float scale, void* ws, const Plan& pl) {
+  pkd::BalancedParams b{};
+  b.q = static_cast<const uint16_t*>(q);
+  b.k = static_cast<const uint8_t*>(k);
+  b.v = static_cast<const uint8_t*>(v);
+  b.block_table = bt;
+  b.seq_lens = lens;
+  b.k_scale = ks;
+  b.v_scale = vs;
+  b.o_part = static_cast<float*>(ws);
+  b.lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.lse_off);
+  b.prefix = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(ws) + pl.prefix_off);
+  b.qk_scale_log2 = scale * 1.44269504088896340736f;
+  b.batch = d.batch;
+  b.hq = d.num_q_heads;
+  b.hkv = d.num_kv_heads;
+  b.group = d.num_q_heads / d.num_kv_heads;
+  b.head_groups = head_groups(d);
+  b.hpg = heads_per_slot(d);
+  b.page_size = d.page_size;
+  b.max_pages = d.max_pages_per_seq;
+  b.num_workers = balanced_workers(d);
+  return b;
+}
+
+// Partition phase of a split plan (S > 1 or balanced) into the workspace.
+int32_t run_partition(const pkd_dims& d, const void* q, const void* k, const void* v, const int32_t* bt,
+                      const int32_t* lens, const float* ks, const float* vs, float scale, void* ws,
+                      const Plan& pl, hipStream_t s) {
+  if (pl.balanced) {
+    const pkd::BalancedParams b = make_balanced_params(d, q, k, v, bt, lens, ks, vs, scale, ws, pl);
+    return pkd::launch_balanced(b, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, s) == hipSuccess
+               ? PKD_OK : PKD_ERR_LAUNCH;
+  }
+  pkd::SplitParams p = make_split_params(d, q, k, v, bt, lens, ks, vs, scale, pl.S);
+  p.o_part = static_cast<float*>(ws);
+  p.lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.lse_off);
+  return launch_partition(d, p, false, s);
+}
+
+// Merge phase of a split plan from the workspace.
+int32_t run_finish(const pkd_dims& d, const void* ws, void* out, float* lse, const Plan& pl, hipStream_t s) {
+  pkd::MergeParams m{};
+  m.o_part = static_cast<const float*>(ws);
+  m.lse_part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + pl.lse_off);
+  m.out = static_cast<uint16_t*>(out);
+  m.lse = lse;
+  m.rows = (int64_t)d.batch * d.num_q_heads;
+  if (pl.balanced) {
+    m.balanced = 1;
+    m.prefix = reinterpret_cast<const int64_t*>(static_cast<const uint8_t*>(ws) + pl.prefix_off);
+    m.batch = d.batch;
+    m.hq = d.num_q_heads;
+    m.hkv = d.num_kv_heads;
+    m.group = d.num_q_heads / d.num_kv_heads;
+    m.head_groups = head_groups(d);
+    m.hpg = heads_per_slot(d);
+    m.num_workers = balanced_workers(d);
+  } else {
+    m.num_splits = pl.S;
+  }
+  return pkd::launch_lse_merge(m, d.head_dim, s) == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
 
 int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
@@ -174,31 +335,57 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
   int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
   if (st != PKD_OK) return st;
   if (!out) return PKD_ERR_NULL_POINTER;
-  if (num_splits > PKD_MAX_SPLITS) return PKD_ERR_NUM_SPLITS;
-  const int S = num_splits > 0
-                    ? num_splits
-                    : heuristic_splits(*dims, dims->max_pages_per_seq * dims->page_size);
-  size_t lse_off = 0;
-  if (S > 1) {
-    const size_t need = partial_bytes(*dims, S, &lse_off);
-    if (!workspace || workspace_bytes < need) return PKD_ERR_WORKSPACE;
-  }
+  Plan pl;
+  st = make_plan(*dims, num_splits, &pl);
+  if (st != PKD_OK) return st;
+  if (pl.need > 0 && (!workspace || workspace_bytes < pl.need)) return PKD_ERR_WORKSPACE;
   if (dims->batch == 0) return PKD_OK;
+  if (current_cu_count() < 0) return PKD_ERR_DEVICE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  pkd::SplitParams p = make_split_params(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale,
-                                         v_scale, scale, S);
-  if (S == 1) {
+  if (pl.S == 1) {
+    pkd::SplitParams p = make_split_params(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale,
+                                           v_scale, scale, 1);
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
     return launch_partition(*dims, p, true, s);
   }
-  p.o_part = static_cast<float*>(workspace);
-  p.lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + lse_off);
-  st = launch_partition(*dims, p, false, s);
+  st = run_partition(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, workspace,
+                     pl, s);
   if (st != PKD_OK) return st;
-  pkd::MergeParams m{p.o_part, p.lse_part, static_cast<uint16_t*>(out), lse,
-                     (int64_t)dims->batch * dims->num_q_heads, S};
-  return pkd::launch_lse_merge(m, dims->head_dim, s) == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
+  return run_finish(*dims, workspace, out, lse, pl, s);
+}
+
+int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const float* k_scale, const float* v_scale,
+                               float scale, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
+  if (st != PKD_OK) return st;
+  Plan pl;
+  st = make_plan(*dims, num_splits, &pl);
+  if (st != PKD_OK) return st;
+  if (pl.S == 1) return PKD_ERR_NUM_SPLITS;
+  if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
+  if (dims->batch == 0) return PKD_OK;
+  if (current_cu_count() < 0) return PKD_ERR_DEVICE;
+  return run_partition(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, workspace,
+                       pl, static_cast<hipStream_t>(stream));
+}
+
+int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void* workspace,
+                            size_t workspace_bytes, void* out, float* lse, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != PKD_OK) return st;
+  if (!out) return PKD_ERR_NULL_POINTER;
+  Plan pl;
+  st = make_plan(*dims, num_splits, &pl);
+  if (st != PKD_OK) return st;
+  if (pl.S == 1) return PKD_ERR_NUM_SPLITS;
+  if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
+  if (dims->batch == 0) return PKD_OK;
+  if (current_cu_count() < 0) return PKD_ERR_DEVICE;
+  return run_finish(*dims, workspace, out, lse, pl, static_cast<hipStream_t>(stream));
 }
 
 int32_t paged_decode_check_tables(const pkd_dims* dims, const int32_t* block_table,

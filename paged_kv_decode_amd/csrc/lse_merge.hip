@@ -25,45 +25,151 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-template <int D>
-__global__ void __launch_bounds__(256) lse_merge_kernel(const MergeParams p) {
+// WPR waves per output row (WPR = 1: four rows per workgroup).  Wave `part`
+// of a row takes the row's partials j = part, part + WPR, ...: their LSEs are
+// read one per lane and reduced across the wave to M_w and W_w = sum exp(lse_j
+// - M_w), and their rows are read with lanes along the head dimension, several
+// partials per batch of independent loads, accumulated with weights
+// exp(lse_j - M_w).  With WPR > 1 the waves' (M_w, W_w, o_w) are then combined
+// in LDS by the same rule.
+template <int D, int WPR>
+__global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(const MergeParams p) {
   constexpr int EPL = D >= 64 ? D / 64 : 1;  // elements per lane
+  constexpr int UNROLL = 8;
+  constexpr int WAVES = WPR == 1 ? 4 : WPR;
+  __shared__ float sm_m[WAVES], sm_w[WAVES];
+  __shared__ float sm_o[WPR == 1 ? 1 : WAVES * D];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= p.rows) return;
-  const int S = p.num_splits;
-  const float* lp = p.lse_part + row * S;
-  const float* op = p.o_part + row * S * D;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = WPR == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
+  const int part = WPR == 1 ? 0 : wave;
+  if (row >= p.rows) return;  // with WPR > 1 the whole workgroup shares the row
+
+  // Where this row's partials are: lp[j * ls] and op[j * os + d], j < S.
+  int S;
+  const float* lp;
+  const float* op;
+  int64_t ls, os;
+  if (!p.balanced) {
+    S = p.num_splits;
+    lp = p.lse_part + row * S;
+    op = p.o_part + row * S * D;
+    ls = 1;
+    os = D;
+  } else {
+    // Segment s = (b * Hkv + kvh) * HG + hg starts at group P_s of the work
+    // space; its pieces were written by workgroups w_first .. w_last at slots w + s.
+    const int b = (int)(row / p.hq);
+    const int h = (int)(row - (int64_t)b * p.hq);
+    const int kvh = h / p.group;
+    const int hin = h - kvh * p.group;
+    const int hg = hin / kHeadsPerGroup;
+    const int nh = hin - hg * kHeadsPerGroup;
+    const int spb = p.hkv * p.head_groups;
+    const int seg = kvh * p.head_groups + hg;
+    const int64_t T = p.prefix[p.batch];
+    const int64_t nb = (p.prefix[b + 1] - p.prefix[b]) / spb;
+    S = 0;
+    int64_t slot0 = 0;
+    if (nb > 0) {
+      const int64_t ps_ = p.prefix[b] + seg * nb;
+      const int64_t nwe = min((int64_t)p.num_workers, T);
+      const int64_t w_first = ((ps_ + 1) * nwe - 1) / T;
+      const int64_t w_last = ((ps_ + nb) * nwe - 1) / T;
+      S = (int)(w_last - w_first + 1);
+      slot0 = w_first + (int64_t)b * spb + seg;
+    }
+    lp = p.lse_part + slot0 * p.hpg + nh;
+    op = p.o_part + (slot0 * p.hpg + nh) * D;
+    ls = p.hpg;
+    os = (int64_t)p.hpg * D;
+  }
+  // This wave's partials: j = part + WPR * k, k < mine.
+  const int mine = S > part ? (S - part + WPR - 1) / WPR : 0;
+  lp += (int64_t)part * ls;
+  op += (int64_t)part * os;
+  ls *= WPR;
+  os *= WPR;
 
   float M = -INFINITY;
-  for (int j = lane; j < S; j += 64) M = fmaxf(M, lp[j]);
+  for (int k = lane; k < mine; k += 64) M = fmaxf(M, lp[k * ls]);
   M = wave_max(M);
-
+  float W = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  float W = 0.f;
+  const bool live = lane * EPL < D;
   if (M != -INFINITY) {
-    for (int j = 0; j < S; ++j) {
-      const float w = __builtin_amdgcn_exp2f((lp[j] - M) * kLog2e);
-      W += w;
-      const float* oj = op + (int64_t)j * D;
+    for (int k0 = 0; k0 < mine; k0 += 64) {
+      // weights of partials k0 .. k0+63, one per lane
+      const int kl = k0 + lane;
+      const float wl = kl < mine ? __builtin_amdgcn_exp2f((lp[kl * ls] - M) * kLog2e) : 0.f;
+      W += wl;
+      const int kn = min(64, mine - k0);
+      int k = 0;
+      for (; k + UNROLL <= kn; k += UNROLL) {
+        float v[UNROLL][EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int d = lane * EPL + e;
-        if (d < D) o[e] += w * oj[d];
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            v[u][e] = live ? op[(int64_t)(k0 + k + u) * os + lane * EPL + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const float wgt = __shfl(wl, k + u);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] += wgt * v[u][e];
+        }
+      }
+      for (; k < kn; ++k) {
+        const float wgt = __shfl(wl, k);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          o[e] += wgt * (live ? op[(int64_t)(k0 + k) * os + lane * EPL + e] : 0.f);
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int d = lane * EPL + e;
-    if (d < D) {
+  for (int m = 32; m >= 1; m >>= 1) W += __shfl_xor(W, m);
+
+  if constexpr (WPR > 1) {
+    // Combine the waves: M = max M_w, W = sum e_w W_w, o = sum e_w o_w, e_w = exp(M_w - M).
+    if (lane == 0) {
+      sm_m[wave] = M;
+      sm_w[wave] = W;
+    }
+    if (live)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_o[wave * D + lane * EPL + e] = o[e];
+    __syncthreads();
+    if (wave != 0) return;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) Mx = fmaxf(Mx, sm_m[w]);
+    W = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float ew = __builtin_amdgcn_exp2f((sm_m[w] - Mx) * kLog2e);  // 0 for an empty wave
+        W += ew * sm_w[w];
+        if (live)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] += ew * sm_o[w * D + lane * EPL + e];
+      }
+    }
+    M = Mx;
+  }
+
+  if (live) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
       const float v = M != -INFINITY ? o[e] / W : 0.f;
       const __bf16 h = (__bf16)v;
       uint16_t bits;
       __builtin_memcpy(&bits, &h, 2);
-      p.out[row * D + d] = bits;
+      p.out[row * D + lane * EPL + e] = bits;
     }
   }
   if (lane == 0 && p.lse) p.lse[row] = M != -INFINITY ? M + log2f(W) * kLn2 : -INFINITY;
@@ -99,11 +205,22 @@ check_tables_kernel(const int32_t* bt, const int32_t* lens, int batch, int max_p
   if (threadIdx.x == 0) *d_count = partial[0];
 }
 
-template <int D>
+template <int D, int WPR>
 hipError_t launch_merge_t(const MergeParams& p, hipStream_t stream) {
-  const int64_t blocks = (p.rows + 3) / 4;
-  hipLaunchKernelGGL((lse_merge_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  const int64_t blocks = WPR == 1 ? (p.rows + 3) / 4 : p.rows;
+  hipLaunchKernelGGL((lse_merge_kernel<D, WPR>), dim3((unsigned)blocks), dim3(64 * (WPR == 1 ? 4 : WPR)), 0,
+                     stream, p);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge_d(const MergeParams& p, hipStream_t stream) {
+  // Waves per row from the partials a row is expected to hold.
+  int64_t per_row = p.num_splits;
+  if (p.balanced) per_row = p.num_workers / ((int64_t)p.batch * p.hkv * p.head_groups) + 2;
+  if (per_row >= 64) return launch_merge_t<D, 16>(p, stream);
+  if (per_row >= 12) return launch_merge_t<D, 4>(p, stream);
+  return launch_merge_t<D, 1>(p, stream);
 }
 
 }  // namespace
@@ -111,10 +228,10 @@ hipError_t launch_merge_t(const MergeParams& p, hipStream_t stream) {
 hipError_t launch_lse_merge(const MergeParams& p, int head_dim, hipStream_t stream) {
   if (p.rows == 0) return hipSuccess;
   switch (head_dim) {
-    case 32: return launch_merge_t<32>(p, stream);
-    case 64: return launch_merge_t<64>(p, stream);
-    case 128: return launch_merge_t<128>(p, stream);
-    case 256: return launch_merge_t<256>(p, stream);
+    case 32: return launch_merge_d<32>(p, stream);
+    case 64: return launch_merge_d<64>(p, stream);
+    case 128: return launch_merge_d<128>(p, stream);
+    case 256: return launch_merge_d<256>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

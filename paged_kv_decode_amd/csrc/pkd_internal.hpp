@@ -24,25 +24,55 @@ struct SplitParams {
   int32_t head_groups;         // ceil(G / 16): query heads are packed 16 per workgroup
   int32_t page_size, max_pages;
   int32_t num_splits;
+  int32_t chunk;               // tokens per split (a multiple of kSplitAlign, or >= every length)
 };
 
-// Arguments of the log-sum-exp merge kernel.
+// Arguments of the balanced persistent partition kernel.
+struct BalancedParams {
+  const uint16_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const float* k_scale;
+  const float* v_scale;
+  float* o_part;               // [slots][hpg][D], slots = num_workers + batch * hkv * head_groups
+  float* lse_part;             // [slots][hpg]
+  int64_t* prefix;             // [batch + 1] group prefix sums, written for the merge kernel
+  float qk_scale_log2;
+  int32_t batch, hq, hkv, group, head_groups;
+  int32_t hpg;                 // heads per slot: min(group, 16)
+  int32_t page_size, max_pages;
+  int32_t num_workers;         // workgroups in the grid
+};
+
+// Arguments of the log-sum-exp merge kernel.  Grid-kernel partials sit at
+// [row][j] (j < num_splits); balanced-kernel partials of a row's segment sit at
+// consecutive slots found from the prefix sums.
 struct MergeParams {
-  const float* o_part;         // [rows][S][D]
-  const float* lse_part;       // [rows][S] natural log
+  const float* o_part;
+  const float* lse_part;
   uint16_t* out;               // [rows][D] bf16
   float* lse;                  // [rows] or null
   int64_t rows;
-  int32_t num_splits;
+  int32_t num_splits;          // grid layout
+  int32_t balanced;            // 0: grid layout; 1: balanced layout
+  const int64_t* prefix;       // balanced layout fields
+  int32_t batch, hq, hkv, group, head_groups, hpg, num_workers;
 };
 
 constexpr int kWaves = 4;            // waves per split-kernel workgroup
 constexpr int kSplitAlign = 64;      // tokens; split boundaries are multiples of this
 constexpr int kHeadsPerGroup = 16;   // query heads packed into one MFMA N dimension
+constexpr int kBalancedMaxBatch = 1024;  // largest batch the balanced kernel's prefix scan takes
+constexpr int kBalancedWgsPerCuDefault = 2;  // used when the occupancy cannot be queried
 
 // Launchers (defined in the .hip files).  head_dim in {32, 64, 128, 256}.
 hipError_t launch_split_kv(const SplitParams& p, int batch, int head_dim, bool fp8, bool direct,
                            bool paged16, hipStream_t stream);
+hipError_t launch_balanced(const BalancedParams& p, int head_dim, bool fp8, hipStream_t stream);
+// Resident balanced-kernel workgroups per compute unit for this instance, or -1.
+int balanced_blocks_per_cu(int head_dim, bool fp8);
 hipError_t launch_lse_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* block_table, const int32_t* seq_lens, int batch,
                                int max_pages, int page_size, int num_pages, int32_t* d_count,

@@ -1,30 +1,42 @@
-// Split-KV paged decode attention for gfx950 (CDNA4): the partition kernel.
+// Split-KV paged decode attention for gfx950 (CDNA4): the partition kernels.
 //
-// One workgroup = one (split j, KV head, sequence b) and up to 16 query heads of
-// that KV head (GQA head packing: all query heads that share a KV head are
-// served by each K/V row read from HBM).  Four waves per workgroup; each wave
-// streams its own tiles of the split's token range and keeps its own online
-// softmax state, and the workgroup combines the four wave states at the end.
+// Work is done by waves.  A wave owns a token range of one (sequence b, KV head)
+// pair and up to 16 query heads of that KV head (GQA head packing: every K/V
+// row read from HBM serves all query heads that share the KV head), and keeps
+// its own online-softmax state for them.  Two launch shapes share that wave
+// machinery (WaveAttn below):
+//
+//  * grid kernel: one workgroup of four waves per (split j, KV head, sequence);
+//    the waves interleave the tiles of the split and combine their states in
+//    LDS at the end.  One split writes out/lse directly; several write
+//    partials for the merge kernel.
+//  * balanced kernel: a persistent grid sized to the device; every wave gets an
+//    equal share of the flattened (sequence, KV head, 16-token group) space,
+//    walks it segment by segment and writes one partial per (wave, segment)
+//    piece.  Work per wave is equal whatever the length mix, and the start-up
+//    latency chain (lengths -> block table -> first K/V) is paid once per wave
+//    rather than once per split.
 //
 // Per tile of TT tokens a wave:
 //   1. resolves the page of every row through the block table (per-token
 //      lookup as in the AstrAI commit log's unified paged path; with page_size
-//      a multiple of 16 one scalar lookup per 16-token group suffices),
-//   2. has already issued 16-byte HBM loads for this tile one tile earlier
-//      (register double buffering; the next tile's loads are in flight while
-//      this one computes),
-//   3. writes V transposed into a wave-private LDS tile,
+//      a multiple of 16 one lookup per 16-token group suffices),
+//   2. has issued the tile's 16-byte K/V loads one tile earlier (register
+//      double buffering: the next tile's loads are in flight while this one
+//      computes),
+//   3. writes V row-major into a wave-private LDS tile,
 //   4. QK^T on MFMA (v_mfma_f32_16x16x32_bf16): A = 16 K rows x 32 dims straight
 //      from the load registers, B = the packed query heads (zero-padded to 16),
 //   5. online softmax in base 2 with the running max shared across the four
 //      lane groups by cross-lane xor shuffles,
-//   6. PV on MFMA: A = V^T from LDS, B = P^T taken from the QK accumulator
-//      registers without any shuffle (token order inside each 32-token chunk is
-//      permuted so that the QK output layout is already the PV operand layout).
+//   6. PV on MFMA: A = V^T gathered by transposing LDS reads
+//      (ds_read_b64_tr_b16), B = P^T taken from the QK accumulator registers
+//      without any shuffle (token order inside each 32-token chunk is permuted
+//      so that the QK output layout is already the PV operand layout).
 //
-// Rows past the end of the split are clamped to the last valid row for
+// Rows past the end of a range are clamped to the last valid row for
 // addressing (so no page past the sequence and no tail slot is ever read) and
-// masked to -inf by selection.  An empty split writes o = 0 and lse = -inf.
+// masked to -inf by selection.  An empty range writes o = 0 and lse = -inf.
 #include "pkd_internal.hpp"
 
 namespace pkd {
@@ -63,17 +75,20 @@ struct Cfg {
   static constexpr int CPR = ROWB / VLB;                   // V loads per row
   static constexpr int RPI = 64 / CPR;                     // rows per V load instruction (<= 16)
   static constexpr int NV = TT * ROWB / (64 * VLB);        // V loads per lane per tile
-  static constexpr int RS = TT + 8;                        // V^T LDS row stride (bf16 elements)
+  static constexpr int VS = D + 16;                        // V tile LDS row stride (bf16 elements)
   static constexpr int NB = D / 16;                        // PV output blocks of 16 dims
   static constexpr int NGRP = TT / 16;                     // 16-token groups per tile
-  static constexpr int VT_BYTES = kWaves * D * RS * 2;
+  static constexpr int VT_BYTES = kWaves * TT * VS * 2;
+  static constexpr int BT_OFFSET = VT_BYTES;                // staged block-table entries
+  static constexpr int BT_ENTRIES = 512;
   static constexpr int OW_STRIDE = D + 4;                  // merge staging row stride (floats)
   static constexpr int MERGE_BYTES = kWaves * 16 * (2 + OW_STRIDE) * 4;
-  static constexpr int LDS_BYTES = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
+  static constexpr int LOOP_BYTES = VT_BYTES + BT_ENTRIES * 4;
+  static constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
   static_assert(KK == NPIECE * R, "K pieces must feed whole MFMAs");
   static_assert(RPI <= 16 && 16 % RPI == 0, "a V load instruction must stay in one 16-row group");
   static_assert(NV * 64 * VLB == TT * ROWB, "V loads must tile the rows exactly");
-  static_assert(LDS_BYTES <= 81920, "two workgroups per CU must fit in LDS");
+  static_assert(LDS_BYTES <= 81920 + BT_ENTRIES * 4, "LDS budget");
 };
 
 typedef typename VecT<16>::T Ld16;
@@ -86,17 +101,32 @@ __device__ __forceinline__ To bit_cast_dev(const From& f) {
   return t;
 }
 
+// K/V rows are streamed exactly once: non-temporal loads keep them from
+// displacing reusable lines in L2 and the Infinity Cache.
 template <int BYTES>
 __device__ __forceinline__ typename VecT<BYTES>::T gload(const uint8_t* p) {
-  return *reinterpret_cast<const typename VecT<BYTES>::T*>(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const typename VecT<BYTES>::T*>(p));
 }
 
 // Wave-local LDS ordering: all of this wave's LDS writes have landed before any
 // later LDS read of another lane's data, and the compiler does not move LDS
 // accesses across this point.
 __device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// result lane i, element r is element i % 4 of the 8 bytes that lane 4r + i/4
+// addressed.  So if lane k of a group addresses row r0 + k/4, columns
+// c0 + 4(k%4) .. +3 of a row-major bf16 tile, lane i receives column c0 + i of
+// rows r0 .. r0 + 3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
 // 8 fp8 E4M3FN codes (two dwords) -> 8 bf16 (exact: every E4M3 value is a bf16 value).
@@ -139,66 +169,48 @@ struct TileRegs {
   typename VecT<C::VLB>::T v[C::NV];
 };
 
-template <int D, bool FP8, bool PAGED16, bool DIRECT>
-__global__ void __launch_bounds__(kWaves * 64)
-split_kv_kernel(const SplitParams p) {
+// Block-table entries of one tile, fetched one tile before they are used so
+// that address computation never waits on a block-table read.
+template <int D, bool FP8, bool PAGED16>
+struct TilePages {
   typedef Cfg<D, FP8> C;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
+  int pg[PAGED16 ? C::NGRP : C::NBLK + C::NV];  // PAGED16: per 16-token group; else per K / V row
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15;   // MFMA row/column index of this lane
-  const int g = lane >> 4;   // MFMA k-group of this lane
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y / p.head_groups;
-  const int hg = blockIdx.y - kvh * p.head_groups;
-  const int b = blockIdx.z;
-  const int S = p.num_splits;
+// Per-wave attention state and tile operations, shared by both launch shapes.
+// Lane (n, g) = (lane % 16, lane / 16) in the MFMA operand layouts.
+template <int D, bool FP8>
+struct WaveAttn {
+  typedef Cfg<D, FP8> C;
+  typedef TileRegs<D, FP8> Regs;
 
-  const int L = p.seq_lens[b];
-  const int per = (L + S - 1) / S;
-  const int chunk = ((per + kSplitAlign - 1) / kSplitAlign) * kSplitAlign;
-  const int s0 = split * chunk;
-  const int s1 = min(s0 + chunk, L);
-  const int heads_here = min(kHeadsPerGroup, p.group - hg * kHeadsPerGroup);
-  const int h0 = kvh * p.group + hg * kHeadsPerGroup;
-  const int64_t row0 = (int64_t)b * p.hq + h0;  // first output row of this workgroup
+  int lane, n, g;
+  int k_rig[C::NBLK];  // position of this lane's K row (of each row block) inside its 16-token group
+  int v_rig;           // + (i * RPI) % 16: position of this lane's row of V load i
+  int k_doff, v_doff;  // byte offsets of this lane's K dims / V chunk inside a row
+  bf16x8 qf[C::KK];    // query heads as the B operand of QK^T
+  float qk_scale;      // scale * log2(e) (* k_scale for fp8)
+  float m_run;         // running max (base-2 units) of head n, equal in all lane groups
+  float l_run;         // this lane's partial sum of exp2(s - m_run) for head n
+  f32x4 acc[C::NB];    // O^T: acc[nb][i] = out[head n][16 nb + 4 g + i] (unnormalised)
 
-  if (s0 >= s1) {
-    // Empty split (or an empty sequence): o = 0, lse = -inf.
-    for (int idx = tid; idx < heads_here * D; idx += kWaves * 64) {
-      const int hh = idx / D, d = idx - (idx / D) * D;
-      if constexpr (DIRECT) {
-        p.out[(row0 + hh) * D + d] = 0;
-        if (d == 0 && p.lse) p.lse[row0 + hh] = -INFINITY;
-      } else {
-        p.o_part[((row0 + hh) * S + split) * D + d] = 0.f;
-        if (d == 0) p.lse_part[(row0 + hh) * S + split] = -INFINITY;
-      }
-    }
-    return;
+  __device__ __forceinline__ void init_lane(int lane_) {
+    lane = lane_;
+    n = lane & 15;
+    g = lane >> 4;
+#pragma unroll
+    for (int blk = 0; blk < C::NBLK; ++blk) k_rig[blk] = k_row_token<C::KP>(blk, n) & 15;
+    v_rig = lane / C::CPR;
+    k_doff = g * C::PIECE * C::ELEM;
+    v_doff = (lane % C::CPR) * C::VLB;
   }
 
-  const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
-  const int lim = s1 - 1;
-  const int tok_stride = p.hkv * C::ROWB;  // bytes between consecutive slots of a page
-  const int64_t head_off = (int64_t)kvh * C::ROWB;
-  // The block table is read-only for the whole launch: reading it through the
-  // constant address space makes the uniform lookups scalar loads, which do not
-  // wait behind the vector loads of K/V in flight.
-  const __attribute__((address_space(4))) int32_t* bt =
-      (const __attribute__((address_space(4))) int32_t*)(p.block_table + (int64_t)b * p.max_pages);
-  const int ps = p.page_size;
-
-  // Query heads as the B operand of QK^T: lane (n, g) holds head n's dims for
-  // MFMA kk: (kk / R) * 4 * PIECE + g * PIECE + (kk % R) * 8 + [0, 8).  The K
-  // loads below use the same dim assignment.  Heads past the group are zero.
-  bf16x8 qf[C::KK];
-  {
+  // Lane (n, g) holds head n's dims (kk / R) * 4 * PIECE + g * PIECE + (kk % R) * 8 + [0, 8)
+  // for MFMA kk; the K loads use the same dim assignment.  Heads past the group are zero.
+  __device__ __forceinline__ void load_q(const uint16_t* q, int64_t row0, int heads_here) {
     const bool hv = n < heads_here;
-    const uint16_t* qrow = p.q + (row0 + (hv ? n : 0)) * D;
+    const uint16_t* qrow = q + (row0 + (hv ? n : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       const int d0 = (kk / C::R) * 4 * C::PIECE + g * C::PIECE + (kk % C::R) * 8;
@@ -208,118 +220,99 @@ split_kv_kernel(const SplitParams p) {
     }
   }
 
-  float qk_scale = p.qk_scale_log2;
-  if constexpr (FP8) qk_scale *= p.k_scale[kvh];
+  __device__ __forceinline__ void reset() {
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // Lane-constant parts of the row addressing.  Row tau of a tile (K row block
-  // blk uses tau = k_row_token(blk, n); V load i uses tau = i*RPI + lane/CPR)
-  // sits in 16-token group tau/16 at position tau%16.
-  int k_rig[C::NBLK];   // position inside its 16-group, per K row block
+  // Issue every K and V load of the tile starting at token tb (a multiple of
+  // 16).  pages[q] is the physical page of the tile's 16-token group q (every
+  // aligned group lies in one page when page_size % 16 == 0); a row past lim is
+  // replaced by a valid row of its group (position min(pos, lim - group start))
+  // and masked later.
+  __device__ __forceinline__ void issue_paged16(const uint8_t* kc, const uint8_t* vc, int tb, int lim,
+                                                const int* pages, int ps, int tok_stride,
+                                                int64_t head_off, Regs& R) const {
+    int64_t gbase[C::NGRP];
+    int glim[C::NGRP];
 #pragma unroll
-  for (int blk = 0; blk < C::NBLK; ++blk) k_rig[blk] = k_row_token<C::KP>(blk, n) & 15;
-  const int v_rig = lane / C::CPR;                     // + (i*RPI) % 16 for load i
-  const int k_doff = g * C::PIECE * C::ELEM;           // byte offset of this lane's K dims
-  const int v_doff = (lane % C::CPR) * C::VLB;         // byte offset of this lane's V chunk
-
-  auto issue_loads = [&](int tile, TileRegs<D, FP8>& R) {
-    const int tb = s0 + tile * C::TT;
-    if constexpr (PAGED16) {
-      // Every aligned 16-token group lies in one page: one scalar lookup per
-      // group.  A row past the end is replaced by a valid row of its group
-      // (position min(pos, lim - group start)); it is masked out later.
-      int64_t gbase[C::NGRP];
-      int glim[C::NGRP];
-#pragma unroll
-      for (int q = 0; q < C::NGRP; ++q) {
-        const int gt = min(tb + 16 * q, lim) & ~15;
-        const int pidx = gt / ps;
-        const int page = bt[pidx];
-        gbase[q] = ((int64_t)page * ps + (gt - pidx * ps)) * tok_stride + head_off;
-        glim[q] = lim - gt;
-      }
-#pragma unroll
-      for (int blk = 0; blk < C::NBLK; ++blk) {
-        const int q = k_row_token<C::KP>(blk, n) >> 4;
-        // For KP == 32 the two halves of a row block come from groups 2c, 2c+1.
-        int64_t base;
-        int gl;
-        if constexpr (C::KP == 32) {
-          const int q0 = 2 * (blk >> 1);
-          base = q == q0 ? gbase[q0] : gbase[q0 + 1];
-          gl = q == q0 ? glim[q0] : glim[q0 + 1];
-        } else {
-          base = gbase[blk];
-          gl = glim[blk];
-        }
-        const uint8_t* src = p.k + base + min(k_rig[blk], gl) * tok_stride + k_doff;
-#pragma unroll
-        for (int pc = 0; pc < C::NPIECE; ++pc)
-          R.k[blk][pc] = gload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
-      }
-#pragma unroll
-      for (int i = 0; i < C::NV; ++i) {
-        const int q = (i * C::RPI) >> 4;
-        const int rig = ((i * C::RPI) & 15) + v_rig;
-        R.v[i] = gload<C::VLB>(p.v + gbase[q] + min(rig, glim[q]) * tok_stride + v_doff);
-      }
-    } else {
-      // Any page size: one lookup per row.
-#pragma unroll
-      for (int blk = 0; blk < C::NBLK; ++blk) {
-        const int tok = min(tb + k_row_token<C::KP>(blk, n), lim);
-        const int pidx = tok / ps;
-        const int64_t off = ((int64_t)p.block_table[(int64_t)b * p.max_pages + pidx] * ps + (tok - pidx * ps)) *
-                                tok_stride + head_off;
-        const uint8_t* src = p.k + off + k_doff;
-#pragma unroll
-        for (int pc = 0; pc < C::NPIECE; ++pc)
-          R.k[blk][pc] = gload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
-      }
-#pragma unroll
-      for (int i = 0; i < C::NV; ++i) {
-        const int tok = min(tb + i * C::RPI + v_rig, lim);
-        const int pidx = tok / ps;
-        const int64_t off = ((int64_t)p.block_table[(int64_t)b * p.max_pages + pidx] * ps + (tok - pidx * ps)) *
-                                tok_stride + head_off;
-        R.v[i] = gload<C::VLB>(p.v + off + v_doff);
-      }
+    for (int q = 0; q < C::NGRP; ++q) {
+      const int gt = min(tb + 16 * q, lim) & ~15;
+      const int page = __builtin_amdgcn_readfirstlane(pages[q]);
+      gbase[q] = ((int64_t)page * ps + (gt - (gt / ps) * ps)) * tok_stride + head_off;
+      glim[q] = lim - gt;
     }
-  };
-
-  float m_run = -INFINITY;  // running max (base-2 units) of head n, same in all lane groups
-  float l_run = 0.f;        // this lane's partial sum of exp2(s - m_run) for head n
-  f32x4 acc[C::NB];         // O^T: acc[nb][i] = out[head n][16 nb + 4 g + i] (unnormalised)
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int blk = 0; blk < C::NBLK; ++blk) {
+      int64_t base;
+      int gl;
+      if constexpr (C::KP == 32) {
+        // The two halves of a 32-token row block come from groups 2c and 2c+1.
+        const int q0 = 2 * (blk >> 1);
+        const bool hi = (k_row_token<C::KP>(blk, n) >> 4) != q0;
+        base = hi ? gbase[q0 + 1] : gbase[q0];
+        gl = hi ? glim[q0 + 1] : glim[q0];
+      } else {
+        base = gbase[blk];
+        gl = glim[blk];
+      }
+      const uint8_t* src = kc + base + min(k_rig[blk], gl) * tok_stride + k_doff;
+#pragma unroll
+      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = gload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NV; ++i) {
+      const int q = (i * C::RPI) >> 4;
+      const int rig = ((i * C::RPI) & 15) + v_rig;
+      R.v[i] = gload<C::VLB>(vc + gbase[q] + min(rig, glim[q]) * tok_stride + v_doff);
+    }
+  }
 
-  uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * D * C::RS;  // this wave's V^T[D][RS]
+  // Any page size: pages[blk] is the page of this lane's K row of row block
+  // blk, pages[NBLK + i] that of its row of V load i (rows clamped to lim).
+  __device__ __forceinline__ void issue_generic(const uint8_t* kc, const uint8_t* vc, int tb, int lim,
+                                                const int* pages, int ps, int tok_stride,
+                                                int64_t head_off, Regs& R) const {
+#pragma unroll
+    for (int blk = 0; blk < C::NBLK; ++blk) {
+      const int tok = min(tb + k_row_token<C::KP>(blk, n), lim);
+      const int64_t off = ((int64_t)pages[blk] * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
+      const uint8_t* src = kc + off + k_doff;
+#pragma unroll
+      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = gload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NV; ++i) {
+      const int tok = min(tb + i * C::RPI + v_rig, lim);
+      const int64_t off = ((int64_t)pages[C::NBLK + i] * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
+      R.v[i] = gload<C::VLB>(vc + off + v_doff);
+    }
+  }
 
-  auto process = [&](int tile, const TileRegs<D, FP8>& R) {
-    const int tb = s0 + tile * C::TT;
-    // V -> LDS, transposed to [dim][token] as bf16.
+  // Tokens (relative to tb) whose pages the generic path needs, per lane.
+  __device__ __forceinline__ int generic_row(int idx) const {
+    return idx < C::NBLK ? k_row_token<C::KP>(idx, n) : (idx - C::NBLK) * C::RPI + v_rig;
+  }
+
+  // One tile: V to LDS, QK^T, online softmax, PV.  Rows at or past s1 are masked.
+  __device__ __forceinline__ void process(const Regs& R, int tb, int s1, uint16_t* vs) {
+    // V -> LDS, row-major bf16 (16-byte writes).
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
       const int lin = i * 64 + lane;
-      const int vrow = lin / C::CPR;
-      const int d0 = (lin % C::CPR) * C::VEPL;
+      uint16_t* dst = vs + (lin / C::CPR) * C::VS + (lin % C::CPR) * C::VEPL;
       if constexpr (FP8) {
 #pragma unroll
         for (int h = 0; h < C::VEPL / 8; ++h) {
           u32x2 c8;
           c8[0] = R.v[i][2 * h];
           c8[1] = R.v[i][2 * h + 1];
-          const bf16x8 x = fp8x8_to_bf16(c8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            vt[(d0 + 8 * h + e) * C::RS + vrow] = bit_cast_dev<uint16_t>(x[e]);
+          *reinterpret_cast<bf16x8*>(dst + 8 * h) = fp8x8_to_bf16(c8);
         }
       } else {
-#pragma unroll
-        for (int w = 0; w < C::VEPL / 2; ++w) {
-          const uint32_t two = R.v[i][w];
-          vt[(d0 + 2 * w) * C::RS + vrow] = (uint16_t)(two & 0xffffu);
-          vt[(d0 + 2 * w + 1) * C::RS + vrow] = (uint16_t)(two >> 16);
-        }
+        *reinterpret_cast<u32x4*>(dst) = R.v[i];
       }
     }
 
@@ -374,9 +367,9 @@ split_kv_kernel(const SplitParams p) {
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) acc[nb] *= alpha;
 
-    wave_lds_sync();  // V^T of this tile is complete
+    wave_lds_sync();  // the V tile is complete in LDS
 
-    // O^T += V^T P^T.
+    // O^T += V^T P^T; the V^T operand comes from transposing LDS reads.
     if constexpr (C::KP == 32) {
 #pragma unroll
       for (int c = 0; c < C::NCH; ++c) {
@@ -386,9 +379,14 @@ split_kv_kernel(const SplitParams p) {
           pb[i] = (__bf16)sacc[2 * c][i];
           pb[4 + i] = (__bf16)sacc[2 * c + 1][i];
         }
+        // lane (n, g) needs V[32c + 8g + j][16 nb + n], j = 0..7
+        const uint16_t* rowp = vs + (32 * c + 8 * g + (n >> 2)) * C::VS + 4 * (n & 3);
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (16 * nb + n) * C::RS + 32 * c + 8 * g);
+          const s16x4 lo = lds_read_tr16(rowp + 16 * nb);
+          const s16x4 hi = lds_read_tr16(rowp + 4 * C::VS + 16 * nb);
+          s16x4 both[2] = {lo, hi};
+          const bf16x8 a = bit_cast_dev<bf16x8>(both);
           acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[nb], 0, 0, 0);
         }
       }
@@ -397,53 +395,83 @@ split_kv_kernel(const SplitParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[i] = (__bf16)sacc[0][i];
       const s16x4 pbs = bit_cast_dev<s16x4>(pb);
+      // lane (n, g) needs V[4g + j][16 nb + n], j = 0..3
+      const uint16_t* rowp = vs + (4 * g + (n >> 2)) * C::VS + 4 * (n & 3);
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
-        const s16x4 a = *reinterpret_cast<const s16x4*>(vt + (16 * nb + n) * C::RS + 4 * g);
+        const s16x4 a = lds_read_tr16(rowp + 16 * nb);
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pbs, acc[nb], 0, 0, 0);
       }
     }
-    wave_lds_sync();  // PV reads done before the next tile's V^T overwrites the tile
-  };
-
-  // Tiles wave, wave + 4, wave + 8, ... with the next tile's loads in flight.
-  // At the end the "next" tile repeats the last one so the loads stay
-  // unconditional (they hit in cache and are not consumed).
-  if (wave < ntiles) {
-    TileRegs<D, FP8> ra, rb;
-    int t = wave;
-    issue_loads(t, ra);
-    while (true) {
-      const int t1 = t + kWaves < ntiles ? t + kWaves : t;
-      issue_loads(t1, rb);
-      process(t, ra);
-      if (t1 == t) break;
-      t = t1;
-      const int t2 = t + kWaves < ntiles ? t + kWaves : t;
-      issue_loads(t2, ra);
-      process(t, rb);
-      if (t2 == t) break;
-      t = t2;
-    }
+    wave_lds_sync();  // PV reads done before the next tile overwrites the V tile
   }
 
-  // Combine the four waves' (m, l, O) in LDS.
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  // Sum of l over the four lane groups (every lane of head n gets it).
+  __device__ __forceinline__ float l_total() const {
+    const float l = l_run + __shfl_xor(l_run, 16);
+    return l + __shfl_xor(l, 32);
+  }
+};
+
+// Tiles first, first + step, ... (< ntiles): while tile t is processed the
+// next tile's K/V loads are in flight and the page entries of the tile after
+// that are being read.  At the end the "next" tile repeats the last one so
+// that the loads stay unconditional (they hit in cache and are not consumed).
+template <int D, bool FP8, typename Pages, typename Fetch, typename Issue>
+__device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int step, int ntiles, int s0,
+                                          int s1, uint16_t* vs, Fetch fetch, Issue issue) {
+  typedef Cfg<D, FP8> C;
+  if (first >= ntiles) return;
+  auto nxt = [&](int t) { return t + step < ntiles ? t + step : t; };
+  TileRegs<D, FP8> ra, rb;
+  Pages pa, pb;
+  int t = first;
+  fetch(t, pa);
+  issue(t, pa, ra);
+  int t1 = nxt(t);
+  fetch(t1, pb);
+  while (true) {
+    issue(t1, pb, rb);
+    int t2 = nxt(t1);
+    fetch(t2, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    A.process(ra, s0 + t * C::TT, s1, vs);
+    if (t1 == t) break;
+    t = t1;
+    t1 = t2;
+    issue(t1, pa, ra);
+    t2 = nxt(t1);
+    fetch(t2, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    A.process(rb, s0 + t * C::TT, s1, vs);
+    if (t1 == t) break;
+    t = t1;
+    t1 = t2;
+  }
+}
+
+// Combine the four waves' (m, l, O) of one workgroup in LDS (smem must hold
+// MERGE_BYTES) and hand every (head, dim) of the group to store(hh, d, o,
+// lse_nat): o = sum_w e_w O_w / sum_w e_w l_w (times vsc), with
+// e_w = 2^(m_w - max m), and the natural-log LSE.  Ends with the LDS still in
+// use: synchronise before reusing it.
+template <int D, bool FP8, typename Store>
+__device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* smem, int wave, int tid,
+                                           int heads_here, float vsc, Store store) {
+  typedef Cfg<D, FP8> C;
+  const float l_tot = A.l_total();
   __syncthreads();
   float* mw = reinterpret_cast<float*>(smem);  // [kWaves][16]
   float* lw = mw + kWaves * 16;                // [kWaves][16]
   float* ow = lw + kWaves * 16;                // [kWaves][16][OW_STRIDE]
-  if (g == 0) {
-    mw[wave * 16 + n] = m_run;
-    lw[wave * 16 + n] = l_tot;
+  if (A.g == 0) {
+    mw[wave * 16 + A.n] = A.m_run;
+    lw[wave * 16 + A.n] = l_tot;
   }
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb)
-    *reinterpret_cast<f32x4*>(ow + (wave * 16 + n) * C::OW_STRIDE + 16 * nb + 4 * g) = acc[nb];
+    *reinterpret_cast<f32x4*>(ow + (wave * 16 + A.n) * C::OW_STRIDE + 16 * nb + 4 * A.g) = A.acc[nb];
   __syncthreads();
-
-  const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
   for (int idx = tid; idx < heads_here * D; idx += kWaves * 64) {
     const int hh = idx / D, d = idx - (idx / D) * D;
     float M = -INFINITY;
@@ -456,14 +484,257 @@ split_kv_kernel(const SplitParams p) {
       num += e * ow[(w * 16 + hh) * C::OW_STRIDE + d];
       den += e * lw[w * 16 + hh];
     }
-    const float o = (num / den) * vsc;
-    const float lse_nat = (M + log2f(den)) * 0.69314718055994530942f;
+    store(hh, d, (num / den) * vsc, (M + log2f(den)) * 0.69314718055994530942f);
+  }
+}
+
+// ---- grid kernel ----------------------------------------------------------
+
+template <int D, bool FP8, bool PAGED16, bool DIRECT>
+__global__ void __launch_bounds__(kWaves * 64)
+split_kv_kernel(const SplitParams p) {
+  typedef Cfg<D, FP8> C;
+  typedef TilePages<D, FP8, PAGED16> Pages;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  WaveAttn<D, FP8> A;
+  A.init_lane(tid & 63);
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y / p.head_groups;
+  const int hg = blockIdx.y - kvh * p.head_groups;
+  const int b = blockIdx.z;
+  const int S = p.num_splits;
+
+  const int L = p.seq_lens[b];
+  const int chunk = p.chunk;  // tokens per split, the same for every sequence
+  const int s0 = (int)min((int64_t)split * chunk, (int64_t)L);
+  const int s1 = min(s0 + chunk, L);
+  const int heads_here = min(kHeadsPerGroup, p.group - hg * kHeadsPerGroup);
+  const int h0 = kvh * p.group + hg * kHeadsPerGroup;
+  const int64_t row0 = (int64_t)b * p.hq + h0;  // first output row of this workgroup
+
+  if (s0 >= s1) {
+    // Empty split (or an empty sequence): o = 0, lse = -inf.
+    for (int idx = tid; idx < heads_here * D; idx += kWaves * 64) {
+      const int hh = idx / D, d = idx - (idx / D) * D;
+      if constexpr (DIRECT) {
+        p.out[(row0 + hh) * D + d] = 0;
+        if (d == 0 && p.lse) p.lse[row0 + hh] = -INFINITY;
+      } else {
+        p.o_part[((row0 + hh) * S + split) * D + d] = 0.f;
+        if (d == 0) p.lse_part[(row0 + hh) * S + split] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
+  const int lim = s1 - 1;
+  const int tok_stride = p.hkv * C::ROWB;  // bytes between consecutive slots of a page
+  const int64_t head_off = (int64_t)kvh * C::ROWB;
+  const int ps = p.page_size;
+  // The block table is read-only for the whole launch (constant address space).
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_table + (int64_t)b * p.max_pages);
+
+  A.load_q(p.q, row0, heads_here);
+  A.qk_scale = p.qk_scale_log2;
+  if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
+  A.reset();
+
+  // The split's block-table entries are staged in LDS once (when they fit), so
+  // that per-tile page lookups are short LDS reads rather than dependent HBM
+  // reads on the path of every tile's loads.
+  int32_t* sbt = reinterpret_cast<int32_t*>(smem + C::BT_OFFSET);
+  const int first_page = s0 / ps;
+  const int n_pages = lim / ps - first_page + 1;
+  const bool staged = n_pages <= C::BT_ENTRIES;
+  if (staged)
+    for (int i = tid; i < n_pages; i += kWaves * 64) sbt[i] = bt[first_page + i];
+  __syncthreads();
+  auto page_of = [&](int pidx) -> int { return staged ? sbt[pidx - first_page] : bt[pidx]; };
+
+  auto fetch = [&](int tile, Pages& P) {
+    const int tb = s0 + tile * C::TT;
+    if constexpr (PAGED16) {
+#pragma unroll
+      for (int q = 0; q < C::NGRP; ++q) P.pg[q] = page_of((min(tb + 16 * q, lim) & ~15) / ps);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::NBLK + C::NV; ++i) P.pg[i] = page_of(min(tb + A.generic_row(i), lim) / ps);
+    }
+  };
+  auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R) {
+    const int tb = s0 + tile * C::TT;
+    if constexpr (PAGED16)
+      A.issue_paged16(p.k, p.v, tb, lim, P.pg, ps, tok_stride, head_off, R);
+    else
+      A.issue_generic(p.k, p.v, tb, lim, P.pg, ps, tok_stride, head_off, R);
+  };
+
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;  // this wave's V[TT][VS]
+  // Tiles wave, wave + 4, wave + 8, ...
+  run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, s1, vs, fetch, issue);
+
+  const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
+  wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
     if constexpr (DIRECT) {
       p.out[(row0 + hh) * D + d] = bit_cast_dev<uint16_t>((__bf16)o);
       if (d == 0 && p.lse) p.lse[row0 + hh] = lse_nat;
     } else {
       p.o_part[((row0 + hh) * S + split) * D + d] = o;
       if (d == 0) p.lse_part[(row0 + hh) * S + split] = lse_nat;
+    }
+  });
+}
+
+// ---- balanced persistent kernel ---------------------------------------------
+//
+// The work space is the sequence of segments s = (b * Hkv + kvh) * HG + hg
+// (HG head groups of up to 16 query heads per KV head), segment s holding the
+// n_b = ceil(L_b / 16) 16-token groups of sequence b; T groups in all.  With
+// NWE = min(workgroups, T) active workgroups, workgroup w takes groups
+// [floor(w T / NWE), floor((w + 1) T / NWE)); its four waves interleave the
+// tiles of each piece (the part of one segment inside the range) and combine
+// in LDS.  Each (workgroup, segment) piece writes its normalised partial and
+// LSE to slot w + s, which is unique and increasing along the work space; the
+// merge kernel finds segment s's pieces from the same formula.  page_size
+// must be a multiple of 16.
+
+template <int D, bool FP8>
+__global__ void __launch_bounds__(kWaves * 64)
+balanced_kernel(const BalancedParams p) {
+  typedef Cfg<D, FP8> C;
+  typedef TilePages<D, FP8, true> Pages;
+  constexpr int SMEM = C::VT_BYTES > C::MERGE_BYTES ? C::VT_BYTES : C::MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ int64_t spre[kBalancedMaxBatch + 1];  // spre[b] = groups of all segments of sequences < b
+  __shared__ int64_t stot[kWaves * 64];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int B = p.batch;
+  const int SPB = p.hkv * p.head_groups;  // segments per sequence
+
+  // Prefix sums of the group counts (every workgroup computes them; workgroup 0
+  // also stores them for the merge kernel).
+  {
+    constexpr int PER = kBalancedMaxBatch / (kWaves * 64);
+    int64_t run[PER];
+    int64_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int bb = tid * PER + i;
+      const int L = bb < B ? p.seq_lens[bb] : 0;
+      sum += (int64_t)((L + 15) >> 4) * SPB;
+      run[i] = sum;
+    }
+    stot[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kWaves * 64; off <<= 1) {
+      const int64_t add = tid >= off ? stot[tid - off] : 0;
+      __syncthreads();
+      stot[tid] += add;
+      __syncthreads();
+    }
+    const int64_t base = tid > 0 ? stot[tid - 1] : 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int bb = tid * PER + i;
+      if (bb < B) spre[bb + 1] = base + run[i];
+    }
+    if (tid == 0) spre[0] = 0;
+    __syncthreads();
+  }
+  const int64_t T = spre[B];
+  if (blockIdx.x == 0)
+    for (int i = tid; i <= B; i += kWaves * 64) p.prefix[i] = spre[i];
+  const int64_t nwe = min((int64_t)p.num_workers, T);
+  const int64_t w = blockIdx.x;
+  if (w >= nwe) return;  // the whole workgroup leaves together
+
+  int64_t pos = w * T / nwe;
+  const int64_t hi = (w + 1) * T / nwe;
+
+  // The sequence holding group pos: spre[b] <= pos < spre[b + 1].
+  int b = 0;
+  {
+    int lo_b = 0, hi_b = B;
+    while (hi_b - lo_b > 1) {
+      const int mid = (lo_b + hi_b) >> 1;
+      if (spre[mid] <= pos) lo_b = mid; else hi_b = mid;
+    }
+    b = lo_b;
+  }
+  int64_t nb = (spre[b + 1] - spre[b]) / SPB;  // groups per segment of sequence b
+  int seg = (int)((pos - spre[b]) / nb);
+  int grp = (int)((pos - spre[b]) - (int64_t)seg * nb);
+
+  WaveAttn<D, FP8> A;
+  A.init_lane(tid & 63);
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;
+  const int ps = p.page_size;
+  const int tok_stride = p.hkv * C::ROWB;
+
+  while (pos < hi) {
+    const int gend = (int)min(nb, (int64_t)grp + (hi - pos));
+    const int L = p.seq_lens[b];
+    const int s0 = grp * 16;
+    const int s1 = min(gend * 16, L);
+    const int lim = s1 - 1;
+    const int kvh = seg / p.head_groups;
+    const int hg = seg - kvh * p.head_groups;
+    const int heads_here = min(kHeadsPerGroup, p.group - hg * kHeadsPerGroup);
+    const int64_t row0 = (int64_t)b * p.hq + kvh * p.group + hg * kHeadsPerGroup;
+    const int64_t head_off = (int64_t)kvh * C::ROWB;
+
+    A.load_q(p.q, row0, heads_here);
+    A.qk_scale = p.qk_scale_log2;
+    if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
+    A.reset();
+
+    // Page window: lane j holds the page of index first_page + j.
+    const int32_t* btrow = p.block_table + (int64_t)b * p.max_pages;
+    const int first_page = s0 / ps;
+    const int last_page = lim / ps;
+    const int window = first_page + A.lane <= last_page ? btrow[first_page + A.lane] : 0;
+    const __attribute__((address_space(4))) int32_t* btc = (const __attribute__((address_space(4))) int32_t*)btrow;
+    auto page_of = [&](int pidx) -> int {
+      const int rel = pidx - first_page;
+      return rel < 64 ? __builtin_amdgcn_readlane(window, rel) : btc[pidx];
+    };
+    auto fetch = [&](int tile, Pages& P) {
+      const int tb = s0 + tile * C::TT;
+#pragma unroll
+      for (int q = 0; q < C::NGRP; ++q) P.pg[q] = page_of((min(tb + 16 * q, lim) & ~15) / ps);
+    };
+    auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R) {
+      A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, head_off, R);
+    };
+    const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
+    run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, s1, vs, fetch, issue);
+
+    // This piece's partial, for the group's heads.
+    const int64_t slot = w + (int64_t)b * SPB + seg;
+    const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
+    float* orow = p.o_part + slot * p.hpg * D;
+    float* lrow = p.lse_part + slot * p.hpg;
+    wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
+      orow[hh * D + d] = o;
+      if (d == 0) lrow[hh] = lse_nat;
+    });
+    __syncthreads();  // the LDS is reused by the next piece
+
+    // Next segment.
+    pos += gend - grp;
+    grp = 0;
+    if (++seg == SPB) {
+      seg = 0;
+      do { ++b; } while (b < B && spre[b + 1] == spre[b]);
+      if (b < B) nb = (spre[b + 1] - spre[b]) / SPB;
     }
   }
 }
@@ -481,6 +752,20 @@ hipError_t launch_d(const SplitParams& p, int batch, bool direct, bool paged16, 
   return direct ? launch_t<D, FP8, false, true>(p, batch, s) : launch_t<D, FP8, false, false>(p, batch, s);
 }
 
+template <int D, bool FP8>
+int occupancy_b() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_kernel<D, FP8>, kWaves * 64, 0) != hipSuccess)
+    return -1;
+  return n;
+}
+
+template <int D, bool FP8>
+hipError_t launch_b(const BalancedParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((balanced_kernel<D, FP8>), dim3(p.num_workers), dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_split_kv(const SplitParams& p, int batch, int head_dim, bool fp8, bool direct,
@@ -490,6 +775,26 @@ hipError_t launch_split_kv(const SplitParams& p, int batch, int head_dim, bool f
     case 64: return fp8 ? launch_d<64, true>(p, batch, direct, paged16, stream) : launch_d<64, false>(p, batch, direct, paged16, stream);
     case 128: return fp8 ? launch_d<128, true>(p, batch, direct, paged16, stream) : launch_d<128, false>(p, batch, direct, paged16, stream);
     case 256: return fp8 ? launch_d<256, true>(p, batch, direct, paged16, stream) : launch_d<256, false>(p, batch, direct, paged16, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int balanced_blocks_per_cu(int head_dim, bool fp8) {
+  switch (head_dim) {
+    case 32: return fp8 ? occupancy_b<32, true>() : occupancy_b<32, false>();
+    case 64: return fp8 ? occupancy_b<64, true>() : occupancy_b<64, false>();
+    case 128: return fp8 ? occupancy_b<128, true>() : occupancy_b<128, false>();
+    case 256: return fp8 ? occupancy_b<256, true>() : occupancy_b<256, false>();
+    default: return -1;
+  }
+}
+
+hipError_t launch_balanced(const BalancedParams& p, int head_dim, bool fp8, hipStream_t stream) {
+  switch (head_dim) {
+    case 32: return fp8 ? launch_b<32, true>(p, stream) : launch_b<32, false>(p, stream);
+    case 64: return fp8 ? launch_b<64, true>(p, stream) : launch_b<64, false>(p, stream);
+    case 128: return fp8 ? launch_b<128, true>(p, stream) : launch_b<128, false>(p, stream);
+    case 256: return fp8 ? launch_b<256, true>(p, stream) : launch_b<256, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -115,6 +115,8 @@ def test_non_finite_scale_is_rejected():
 def test_num_splits_and_workspace_rules():
     d = dims()
     assert call(d, S=b.PKD_MAX_SPLITS + 1) == b.PKD_ERR_NUM_SPLITS
+    assert call(d, S=-5) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_workspace_bytes(d, -5) == 0
     need = b.paged_decode_workspace_bytes(d, 3)
     # [B][Hq][S][D] fp32 + [B][Hq][S] fp32, each rounded up to 256 bytes
     assert need == 2 * 4 * 3 * 64 * 4 + 256
@@ -150,23 +152,53 @@ def test_partials_and_merge_argument_checks():
     assert b.paged_decode_check_tables(d, None, FAKE, FAKE, None) == b.PKD_ERR_NULL_POINTER
 
 
-def test_heuristic_is_in_range_and_monotone_in_work():
-    """The split heuristic: one split when (sequence, KV-head) items already fill
-    the device, more when they do not, never above the cap or the length bound."""
+def test_two_phase_argument_checks():
+    d = dims()
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1)
+    # direct output has no split phases
+    assert b.paged_decode_partition(d, *args, 1, FAKE, 1 << 20, None) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_finish(d, 1, FAKE, 1 << 20, FAKE, None, None) == b.PKD_ERR_NUM_SPLITS
+    need = b.paged_decode_workspace_bytes(d, 4)
+    assert b.paged_decode_partition(d, *args, 4, FAKE, need - 1, None) == b.PKD_ERR_WORKSPACE
+    assert b.paged_decode_finish(d, 4, None, need, FAKE, None, None) == b.PKD_ERR_WORKSPACE
+    assert b.paged_decode_finish(d, 4, FAKE, need, None, None, None) == b.PKD_ERR_NULL_POINTER
+    assert b.paged_decode_partition(d, *args, -7, FAKE, need, None) == b.PKD_ERR_NUM_SPLITS
+
+
+def test_heuristic_choices():
+    """One split when (sequence, KV-head) items already fill the device; the
+    balanced partition when they do not and it applies; otherwise a split count
+    bounded by the cap and by the length hint."""
     big = dims(batch=128, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
                num_pages=2048, max_pages_per_seq=16)
     assert b.paged_decode_num_splits(big, 0) == 1
     b32 = dims(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
                num_pages=1500, max_pages_per_seq=64)
-    s32 = b.paged_decode_num_splits(b32, 0)
-    assert 2 <= s32 <= 16
-    long1 = dims(batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=64,
-                 num_pages=2048, max_pages_per_seq=2048)
+    assert b.paged_decode_num_splits(b32, 0) == b.PKD_SPLITS_BALANCED
+    odd = dims(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=24,
+               num_pages=6000, max_pages_per_seq=171)
+    s_odd = b.paged_decode_num_splits(odd, 0)
+    assert 2 <= s_odd <= 16
+    long1 = dims(batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=40,
+                 num_pages=3277, max_pages_per_seq=3277)
     s1 = b.paged_decode_num_splits(long1, 0)
-    assert s32 < s1 <= b.PKD_MAX_SPLITS
+    assert s_odd < s1 <= b.PKD_MAX_SPLITS
     assert b.paged_decode_num_splits(long1, 256) == 1  # a short hint caps the split count
     tiny = dims()
-    assert b.paged_decode_num_splits(tiny, 0) == 1
+    assert b.paged_decode_num_splits(tiny, 0) == b.PKD_SPLITS_BALANCED
+
+
+def test_balanced_mode_rules():
+    ok = dims(batch=4, page_size=16)
+    need = b.paged_decode_workspace_bytes(ok, b.PKD_SPLITS_BALANCED)
+    assert need > 0
+    assert call(ok, S=b.PKD_SPLITS_BALANCED) == b.PKD_ERR_WORKSPACE
+    assert call(ok, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=need - 1) == b.PKD_ERR_WORKSPACE
+    odd_ps = dims(batch=4, page_size=24)
+    assert b.paged_decode_workspace_bytes(odd_ps, b.PKD_SPLITS_BALANCED) == 0
+    assert call(odd_ps, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=1 << 30) == b.PKD_ERR_NUM_SPLITS
+    too_many = dims(batch=b.PKD_BALANCED_MAX_BATCH + 1, page_size=16)
+    assert call(too_many, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=1 << 30) == b.PKD_ERR_NUM_SPLITS
 
 
 def test_one_hip_runtime_in_process():

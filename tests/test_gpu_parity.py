@@ -17,6 +17,7 @@ from paged_kv_decode_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
+BAL = -1000  # PKD_SPLITS_BALANCED
 OUT_ATOL = 1e-2
 OUT_RTOL = 1e-2
 LSE_ATOL = 1e-3
@@ -67,7 +68,7 @@ def oracle_full(w):
 
 # ---- the small case, direct and split -------------------------------------
 
-@pytest.mark.parametrize("S", [1, 3, 0])
+@pytest.mark.parametrize("S", [1, 3, 0, BAL])
 def test_tiny_workload(B, S):
     w = wl.make_workload(wl.WORKLOADS["tiny_b2_d64_ps16"])
     ref = oracle_full(w)
@@ -88,7 +89,7 @@ def test_head_dims_page_sizes_edge_lengths(B, dtype, d, ps):
     w = wl.custom_workload(len(lens), 8, 2, d, ps, lens, dtype, seed=1000 + d + ps)
     ref = oracle_full(w)
     t = dev(w)
-    for S in (1, 4, 11):
+    for S in (1, 4, 11) + ((BAL,) if ps % 16 == 0 else ()):
         out, lse = run(B, w, S, t)
         check(out, lse, *ref, what=f"{dtype} D={d} ps={ps} S={S}")
 
@@ -100,7 +101,7 @@ def test_gqa_group_sizes(B, hq, hkv):
     w = wl.custom_workload(len(lens), hq, hkv, 64, 16, lens, "bf16", seed=hq * 10 + hkv)
     ref = oracle_full(w)
     t = dev(w)
-    for S in (1, 3):
+    for S in (1, 3, BAL):
         out, lse = run(B, w, S, t)
         check(out, lse, *ref, what=f"Hq={hq} Hkv={hkv} S={S}")
 
@@ -110,7 +111,7 @@ def test_split_count_larger_than_tiles(B):
     w = wl.custom_workload(len(lens), 8, 2, 128, 16, lens, "bf16", seed=7)
     ref = oracle_full(w)
     t = dev(w)
-    for S in (2, 7, 64, 512):
+    for S in (2, 7, 64, 512, BAL):
         out, lse = run(B, w, S, t)
         check(out, lse, *ref, what=f"S={S}")
 
@@ -123,7 +124,7 @@ def test_all_zero_lengths(B):
     k = torch.full((1, 16, 1, 64), float("nan"), dtype=torch.bfloat16, device=cuda)
     bt = torch.full((3, 2), -1, dtype=torch.int32, device=cuda)
     lens = torch.zeros(3, dtype=torch.int32, device=cuda)
-    for S in (1, 5):
+    for S in (1, 5, BAL):
         out, lse = B.decode(q, k, k.clone(), bt, lens, 0.125, num_splits=S)
         torch.cuda.synchronize()
         assert torch.all(out.float() == 0) and torch.all(torch.isneginf(lse))
@@ -169,7 +170,7 @@ def test_bit_exact_one_hot_probe(B, dtype, d, ps):
     w, tstar = one_hot_workload(lens, hq, hkv, d, ps, dtype, seed=d * 7 + ps)
     t = dev(w)
     V = w.v_logical
-    for S in (1, 3, 0):
+    for S in (1, 3, 0) + ((BAL,) if ps % 16 == 0 else ()):
         out, lse = run(B, w, S, t)
         for b, ts in enumerate(tstar):
             row = V[int(w.token_offsets[b]) + ts]  # [Hkv, D]
@@ -194,7 +195,7 @@ def test_nan_tails_and_padding_are_never_read(B, dtype):
     w_nan = wl.custom_workload(len(lens), 8, 2, 64, 16, lens, dtype, seed=31, tail="nan")
     w_zero = wl.custom_workload(len(lens), 8, 2, 64, 16, lens, dtype, seed=31, tail="zero")
     assert (w_nan.block_table == -1).any()
-    for S in (1, 3):
+    for S in (1, 3, BAL):
         a = run(B, w_nan, S)
         z = run(B, w_zero, S)
         assert torch.isfinite(a[0].float()).all()
@@ -205,7 +206,7 @@ def test_nan_tails_and_padding_are_never_read(B, dtype):
 def test_bitwise_deterministic(B):
     w = wl.custom_workload(6, 32, 8, 128, 64, [300, 2049, 1, 64, 999, 4000], "bf16", seed=41)
     t = dev(w)
-    for S in (1, 5):
+    for S in (1, 5, BAL):
         a = run(B, w, S, t)
         b_ = run(B, w, S, t)
         assert torch.equal(a[0].view(torch.int16), b_[0].view(torch.int16)) and torch.equal(a[1], b_[1])
@@ -218,9 +219,9 @@ def test_bf16_and_fp8_interleaved_at_one_shape(B):
     wb = wl.custom_workload(3, 16, 2, 128, 64, lens, "bf16", seed=51)
     wf = wl.custom_workload(3, 16, 2, 128, 64, lens, "fp8_e4m3", seed=51)
     rb, rf = oracle_full(wb), oracle_full(wf)
-    for _ in range(2):
-        check(*run(B, wb, 2), *rb, what="bf16")
-        check(*run(B, wf, 2), *rf, what="fp8")
+    for S in (2, BAL, 2):
+        check(*run(B, wb, S), *rb, what=f"bf16 S={S}")
+        check(*run(B, wf, S), *rf, what=f"fp8 S={S}")
 
 
 def test_fp8_every_finite_code_decodes_exactly(B):
@@ -243,14 +244,18 @@ def test_fp8_every_finite_code_decodes_exactly(B):
 
 def test_sharpened_attention(B):
     """q scaled by 4: attention is far from flat, so the absolute tolerance is not
-    what makes the check pass."""
+    what makes the check pass.  Beyond the acceptance bound, the RMS error must be
+    below 0.5% of the RMS output (bf16 output rounding alone is about 0.1%)."""
     w = wl.custom_workload(4, 32, 8, 128, 64, [2048, 1024, 3000, 77], "bf16", seed=71)
     w = wl.rebuild_with_rows(w, q=(w.q.float() * 4).to(torch.bfloat16))
     ref = oracle_full(w)
-    for S in (1, 4):
+    for S in (1, 4, BAL):
         out, lse = run(B, w, S)
-        e_out, e_lse = check(out, lse, *ref, what=f"sharp S={S}")
-        assert e_out < 4e-3
+        check(out, lse, *ref, what=f"sharp S={S}")
+        o = out.double().numpy()
+        rms_err = float(np.sqrt(np.mean((o - ref[0]) ** 2)))
+        rms_ref = float(np.sqrt(np.mean(ref[0] ** 2)))
+        assert rms_err <= 5e-3 * rms_ref, f"S={S}: rms error {rms_err:.3g} vs rms output {rms_ref:.3g}"
 
 
 # ---- the partition and merge entry points on their own -----------------------
@@ -270,13 +275,11 @@ def test_partials_entry_matches_oracle_per_split(B):
     torch.cuda.synchronize()
     o_part = o_part.cpu().view(len(lens), 8, S, 64).double().numpy()
     l_part = l_part.cpu().view(len(lens), 8, S).double().numpy()
+    cap = w.block_table.shape[1] * w.spec.page_size
+    c = B.PKD_SPLIT_ALIGN * (-(-(-(-cap // S)) // B.PKD_SPLIT_ALIGN))
     for j in range(S):
-        tb, te = [], []
-        for L in lens:
-            per = -(-L // S)
-            c = B.PKD_SPLIT_ALIGN * (-(-per // B.PKD_SPLIT_ALIGN))
-            tb.append(min(j * c, L))
-            te.append(min((j + 1) * c, L))
+        tb = [min(j * c, L) for L in lens]
+        te = [min((j + 1) * c, L) for L in lens]
         ref_o, ref_l = oracle.paged_decode_ranges(w.q, w.k_cache, w.v_cache, w.block_table,
                                                   w.seq_lens, w.scale, tb, te)
         assert np.all(np.abs(o_part[:, :, j] - ref_o) <= 1e-2 + 1e-2 * np.abs(ref_o))
@@ -285,15 +288,18 @@ def test_partials_entry_matches_oracle_per_split(B):
         assert np.all(np.abs(np.where(inf, 0, l_part[:, :, j] - np.where(inf, 0, ref_l))) <= 1e-3)
 
 
+@pytest.mark.parametrize("S", [9, 37, 100])
 @pytest.mark.parametrize("d", [32, 64, 128, 256])
-def test_merge_entry_matches_oracle(B, d):
-    rng = np.random.default_rng(d)
-    R, S = 37, 9
+def test_merge_entry_matches_oracle(B, d, S):
+    """S = 9, 37, 100 take the one-, four- and sixteen-waves-per-row merges."""
+    rng = np.random.default_rng(d + S)
+    R = 37
     o = rng.standard_normal((R, S, d)).astype(np.float32)
     l = (rng.standard_normal((R, S)) * 4).astype(np.float32)
     l[3, 2] = -np.inf
     l[5, :] = -np.inf
     l[7, :-1] = -np.inf
+    l[9, 1:] = -np.inf
     out = torch.empty(R, d, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(R, dtype=torch.float32, device="cuda")
     st = B.paged_decode_merge(R, S, d, torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(), out, lse,
@@ -322,6 +328,33 @@ def test_check_tables(B):
     assert B.paged_decode_check_tables(dims, bt, lens, cnt, B.current_stream_handle(0)) == 0
     torch.cuda.synchronize()
     assert int(cnt.item()) == 3
+
+
+# ---- the balanced partition ---------------------------------------------------
+
+@pytest.mark.parametrize("case", [
+    # (lens, Hq, Hkv, D, ps, dtype)
+    ([0, 5, 0, 3000, 1, 16, 17, 0], 8, 2, 128, 16, "bf16"),   # empty and one-group sequences
+    ([1] * 300, 8, 8, 64, 16, "bf16"),                         # fewer groups than waves
+    ([33] * 700 + [2000, 0, 1], 4, 1, 64, 64, "bf16"),         # many segments per wave
+    ([4096, 1, 4095], 40, 2, 128, 64, "bf16"),                 # two head groups, the second partial
+    ([513, 8192, 64, 700], 64, 8, 128, 64, "fp8_e4m3"),        # fp8, G = 8
+    ([12000, 5], 16, 2, 256, 64, "bf16"),                      # D = 256
+    ([3000] * 4, 16, 2, 32, 128, "fp8_e4m3"),                  # fp8 D = 32
+])
+def test_balanced_partition(B, case):
+    lens, hq, hkv, d, ps, dtype = case
+    w = wl.custom_workload(len(lens), hq, hkv, d, ps, lens, dtype, seed=len(lens) + d + ps)
+    ref = oracle_full(w)
+    out, lse = run(B, w, BAL)
+    check(out, lse, *ref, what=f"balanced {case[1:]}")
+
+
+def test_balanced_largest_batch(B):
+    lens = [(i * 37) % 300 for i in range(1024)]
+    w = wl.custom_workload(1024, 4, 2, 64, 32, lens, "bf16", seed=3)
+    ref = oracle_full(w)
+    check(*run(B, w, BAL), *ref, what="balanced B=1024")
 
 
 # ---- full-size workloads: sampled rows against the oracle --------------------
@@ -353,15 +386,36 @@ def test_full_size_workload_sampled_rows(B, name):
     ref_o, ref_l = oracle.paged_decode_rows(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale,
                                             rows, w.k_scale, w.v_scale)
     outs = {}
-    for S in (0, 1):
+    for S in (BAL, 0, 1):
         out, lse = run(B, w, S, t)
         flat_o = out.view(-1, spec.head_dim)[rows]
         flat_l = lse.view(-1)[rows]
         check(flat_o, flat_l, ref_o, ref_l, what=f"{name} S={S}")
         outs[S] = (out, lse)
-    # Every row (not only the sampled ones): heuristic split vs direct output agree.
-    a, b_ = outs[0], outs[1]
-    diff = (a[0].float() - b_[0].float()).abs()
-    assert torch.all(diff <= 2e-2 + 2e-2 * b_[0].float().abs())
-    assert torch.all((a[1] - b_[1]).abs() <= 2e-3)
-    assert torch.isfinite(a[0].float()).all()
+    # Every row (not only the sampled ones): the partitions agree with direct output.
+    for S in (BAL, 0):
+        a, b_ = outs[S], outs[1]
+        diff = (a[0].float() - b_[0].float()).abs()
+        assert torch.all(diff <= 2e-2 + 2e-2 * b_[0].float().abs())
+        assert torch.all((a[1] - b_[1]).abs() <= 2e-3)
+        assert torch.isfinite(a[0].float()).all()
+
+
+@pytest.mark.parametrize("S", [4, BAL])
+def test_two_phases_equal_paged_decode(B, S):
+    """paged_decode_partition then paged_decode_finish is exactly paged_decode."""
+    w = wl.custom_workload(5, 16, 2, 128, 64, [700, 1, 0, 3000, 64], "bf16", seed=123)
+    t = dev(w)
+    ref_out, ref_lse = run(B, w, S, t)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    nbytes = B.paged_decode_workspace_bytes(dims, S)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+    h = B.current_stream_handle(0)
+    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, S,
+                                    ws, nbytes, h) == 0
+    assert B.paged_decode_finish(dims, S, ws, nbytes, out, lse, h) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse.cpu(), ref_lse)
