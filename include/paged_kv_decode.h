@@ -156,12 +156,12 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
                             size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
- * paged_decode_num_splits -- what paged_decode does for PKD_SPLITS_AUTO: 1 (direct
- * output) when the (sequence, KV-head) work items alone fill the current
- * device's compute units, otherwise PKD_SPLITS_BALANCED where it applies, else
- * a split count in [2, PKD_MAX_SPLITS] bounded by the longest sequence expected,
- * max_seq_len_hint (<= 0: max_pages_per_seq * page_size).  Host only; returns
- * that value, or a status in [-10, -1] for invalid dims.
+ * paged_decode_num_splits -- what paged_decode does for PKD_SPLITS_AUTO:
+ * PKD_SPLITS_BALANCED wherever it applies; otherwise 1 (direct output) when the
+ * (sequence, KV-head) work items alone fill the current device's compute units,
+ * else a split count in [2, PKD_MAX_SPLITS] bounded by the longest sequence
+ * expected, max_seq_len_hint (<= 0: max_pages_per_seq * page_size).  Host only;
+ * returns that value, or a status in [-10, -1] for invalid dims.
  */
 int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint);
 

@@ -118,12 +118,16 @@ int32_t split_chunk(const pkd_dims& d, int S) {
   return (int32_t)(c < INT32_MAX ? c : INT32_MAX);
 }
 
+// The split mode for PKD_SPLITS_AUTO.  The balanced partition wherever it
+// applies (it balances any length mix and pays each workgroup's start-up once);
+// otherwise direct output when the (sequence, KV head) items alone fill the
+// device, else enough splits to fill it, bounded by the longest sequence.
 int32_t heuristic_splits(const pkd_dims& d, int32_t max_len) {
+  if (balanced_ok(d)) return PKD_SPLITS_BALANCED;
   const int cus = current_cu_count();
   const int64_t target = 4LL * (cus > 0 ? cus : 256);  // workgroups to keep every CU busy
   const int64_t work = (int64_t)d.batch * d.num_kv_heads * head_groups(d);
   if (work <= 0 || work >= target) return 1;
-  if (balanced_ok(d)) return PKD_SPLITS_BALANCED;
   int64_t s = (target + work - 1) / work;
   const int64_t by_len = (max_len + 255) / 256;  // keep at least ~256 tokens per split
   if (s > by_len) s = by_len;

@@ -92,40 +92,63 @@ __global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(co
   os *= WPR;
 
   float M = -INFINITY;
-  for (int k = lane; k < mine; k += 64) M = fmaxf(M, lp[k * ls]);
-  M = wave_max(M);
   float W = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
   const bool live = lane * EPL < D;
-  if (M != -INFINITY) {
-    for (int k0 = 0; k0 < mine; k0 += 64) {
-      // weights of partials k0 .. k0+63, one per lane
-      const int kl = k0 + lane;
-      const float wl = kl < mine ? __builtin_amdgcn_exp2f((lp[kl * ls] - M) * kLog2e) : 0.f;
-      W += wl;
-      const int kn = min(64, mine - k0);
-      int k = 0;
-      for (; k + UNROLL <= kn; k += UNROLL) {
-        float v[UNROLL][EPL];
+  if (mine <= UNROLL) {
+    // Few partials (the common case): their LSEs and rows are loaded together,
+    // in one round trip, and combined once the maximum is known.
+    const float l_own = lane < mine ? lp[lane * ls] : -INFINITY;
+    float v[UNROLL][EPL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        v[u][e] = (live && u < mine) ? op[(int64_t)u * os + lane * EPL + e] : 0.f;
+    M = wave_max(l_own);
+    if (M != -INFINITY) {
+      const float wl = lane < mine ? __builtin_amdgcn_exp2f((l_own - M) * kLog2e) : 0.f;
+      W = wl;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const float wgt = __shfl(wl, u);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] += wgt * v[u][e];
+      }
+    }
+  } else {
+    for (int k = lane; k < mine; k += 64) M = fmaxf(M, lp[k * ls]);
+    M = wave_max(M);
+    if (M != -INFINITY) {
+      for (int k0 = 0; k0 < mine; k0 += 64) {
+        // weights of partials k0 .. k0+63, one per lane
+        const int kl = k0 + lane;
+        const float wl = kl < mine ? __builtin_amdgcn_exp2f((lp[kl * ls] - M) * kLog2e) : 0.f;
+        W += wl;
+        const int kn = min(64, mine - k0);
+        int k = 0;
+        for (; k + UNROLL <= kn; k += UNROLL) {
+          float v[UNROLL][EPL];
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+              v[u][e] = live ? op[(int64_t)(k0 + k + u) * os + lane * EPL + e] : 0.f;
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u) {
+            const float wgt = __shfl(wl, k + u);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[e] += wgt * v[u][e];
+          }
+        }
+        for (; k < kn; ++k) {
+          const float wgt = __shfl(wl, k);
 #pragma unroll
           for (int e = 0; e < EPL; ++e)
-            v[u][e] = live ? op[(int64_t)(k0 + k + u) * os + lane * EPL + e] : 0.f;
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const float wgt = __shfl(wl, k + u);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) o[e] += wgt * v[u][e];
+            o[e] += wgt * (live ? op[(int64_t)(k0 + k) * os + lane * EPL + e] : 0.f);
         }
-      }
-      for (; k < kn; ++k) {
-        const float wgt = __shfl(wl, k);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          o[e] += wgt * (live ? op[(int64_t)(k0 + k) * os + lane * EPL + e] : 0.f);
       }
     }
   }

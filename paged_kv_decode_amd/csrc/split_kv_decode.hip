@@ -59,9 +59,9 @@ template <int D, bool FP8>
 struct Cfg {
   static constexpr int ELEM = FP8 ? 1 : 2;                 // bytes per cached element
   static constexpr int ROWB = D * ELEM;                    // bytes of one token's row for one KV head
-  // Tokens per wave tile: 8 KiB of K (and of V) per tile for bf16; fp8 keeps
-  // the same bytes except at D = 32 where the tile would be 256 rows.
-  static constexpr int TT = FP8 ? (D == 32 ? 128 : 8192 / D) : 4096 / D;
+  // Tokens per wave tile: 4096 / D (8 KiB of K and 8 KiB of V for bf16, half
+  // that for fp8), which keeps two tiles of loads per wave within registers.
+  static constexpr int TT = 4096 / D;
   static constexpr int NBLK = TT / 16;                     // QK MFMA row blocks per tile
   static constexpr int KP = TT >= 32 ? 32 : 16;            // tokens per PV MFMA (its K depth)
   static constexpr int NCH = TT / KP;                      // PV chunks per tile
@@ -612,7 +612,7 @@ balanced_kernel(const BalancedParams p) {
   constexpr int SMEM = C::VT_BYTES > C::MERGE_BYTES ? C::VT_BYTES : C::MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ int64_t spre[kBalancedMaxBatch + 1];  // spre[b] = groups of all segments of sequences < b
-  __shared__ int64_t stot[kWaves * 64];
+  __shared__ int64_t stot[kWaves];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -620,9 +620,12 @@ balanced_kernel(const BalancedParams p) {
   const int SPB = p.hkv * p.head_groups;  // segments per sequence
 
   // Prefix sums of the group counts (every workgroup computes them; workgroup 0
-  // also stores them for the merge kernel).
+  // also stores them for the merge kernel): thread t sums sequences 4t..4t+3,
+  // a shuffle scan runs inside each wave, and the wave totals are added across
+  // waves through LDS.
   {
     constexpr int PER = kBalancedMaxBatch / (kWaves * 64);
+    const int lane = tid & 63;
     int64_t run[PER];
     int64_t sum = 0;
 #pragma unroll
@@ -632,15 +635,16 @@ balanced_kernel(const BalancedParams p) {
       sum += (int64_t)((L + 15) >> 4) * SPB;
       run[i] = sum;
     }
-    stot[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < kWaves * 64; off <<= 1) {
-      const int64_t add = tid >= off ? stot[tid - off] : 0;
-      __syncthreads();
-      stot[tid] += add;
-      __syncthreads();
+    int64_t incl = sum;  // inclusive scan of the thread sums within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t up = __shfl_up(incl, off);
+      if (lane >= off) incl += up;
     }
-    const int64_t base = tid > 0 ? stot[tid - 1] : 0;
+    if (lane == 63) stot[wave] = incl;
+    __syncthreads();
+    int64_t base = incl - sum;
+    for (int v = 0; v < wave; ++v) base += stot[v];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int bb = tid * PER + i;
@@ -679,6 +683,16 @@ balanced_kernel(const BalancedParams p) {
   const int ps = p.page_size;
   const int tok_stride = p.hkv * C::ROWB;
 
+  // Page window of a piece: lane j holds block-table entry first_page + j of
+  // sequence bb (entries past the row are not read; entries past the pieces's
+  // last page are never used).  The next piece's window is loaded while the
+  // current piece runs.
+  auto load_window = [&](int bb, int first_page) -> int {
+    const int idx = first_page + A.lane;
+    return idx < p.max_pages ? p.block_table[(int64_t)bb * p.max_pages + idx] : 0;
+  };
+  int window = load_window(b, grp * 16 / ps);
+
   while (pos < hi) {
     const int gend = (int)min(nb, (int64_t)grp + (hi - pos));
     const int L = p.seq_lens[b];
@@ -691,17 +705,23 @@ balanced_kernel(const BalancedParams p) {
     const int64_t row0 = (int64_t)b * p.hq + kvh * p.group + hg * kHeadsPerGroup;
     const int64_t head_off = (int64_t)kvh * C::ROWB;
 
+    // The next piece: the following segment (of this or a later sequence).
+    const int64_t npos = pos + (gend - grp);
+    int nseg = seg + 1, nbq = b;
+    if (nseg == SPB) {
+      nseg = 0;
+      do { ++nbq; } while (nbq < B && spre[nbq + 1] == spre[nbq]);
+    }
+    const int next_window = npos < hi ? load_window(nbq, 0) : 0;
+
     A.load_q(p.q, row0, heads_here);
     A.qk_scale = p.qk_scale_log2;
     if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
     A.reset();
 
-    // Page window: lane j holds the page of index first_page + j.
-    const int32_t* btrow = p.block_table + (int64_t)b * p.max_pages;
     const int first_page = s0 / ps;
-    const int last_page = lim / ps;
-    const int window = first_page + A.lane <= last_page ? btrow[first_page + A.lane] : 0;
-    const __attribute__((address_space(4))) int32_t* btc = (const __attribute__((address_space(4))) int32_t*)btrow;
+    const __attribute__((address_space(4))) int32_t* btc =
+        (const __attribute__((address_space(4))) int32_t*)(p.block_table + (int64_t)b * p.max_pages);
     auto page_of = [&](int pidx) -> int {
       const int rel = pidx - first_page;
       return rel < 64 ? __builtin_amdgcn_readlane(window, rel) : btc[pidx];
@@ -728,14 +748,14 @@ balanced_kernel(const BalancedParams p) {
     });
     __syncthreads();  // the LDS is reused by the next piece
 
-    // Next segment.
-    pos += gend - grp;
+    pos = npos;
     grp = 0;
-    if (++seg == SPB) {
-      seg = 0;
-      do { ++b; } while (b < B && spre[b + 1] == spre[b]);
+    seg = nseg;
+    if (nbq != b) {
+      b = nbq;
       if (b < B) nb = (spre[b + 1] - spre[b]) / SPB;
     }
+    window = next_window;
   }
 }
 

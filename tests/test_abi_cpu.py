@@ -166,11 +166,14 @@ def test_two_phase_argument_checks():
 
 
 def test_heuristic_choices():
-    """One split when (sequence, KV-head) items already fill the device; the
-    balanced partition when they do not and it applies; otherwise a split count
+    """The balanced partition wherever it applies; otherwise one split when the
+    (sequence, KV-head) items already fill the device, else a split count
     bounded by the cap and by the length hint."""
-    big = dims(batch=128, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
-               num_pages=2048, max_pages_per_seq=16)
+    b128 = dims(batch=128, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
+                num_pages=2048, max_pages_per_seq=16)
+    assert b.paged_decode_num_splits(b128, 0) == b.PKD_SPLITS_BALANCED
+    big = dims(batch=2048, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
+               num_pages=32768, max_pages_per_seq=16)
     assert b.paged_decode_num_splits(big, 0) == 1
     b32 = dims(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
                num_pages=1500, max_pages_per_seq=64)
