@@ -181,18 +181,96 @@ def cpu_baseline(w, nbytes):
             "seconds": dt, "queries_per_s": w.spec.batch / dt}
 
 
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_decode_amd", "csrc", "split_kv_decode.hip")
+CALIB_BYTES = 1 << 30  # the 1 GiB device-to-device copy made at start-up
+
+
+def _source_digest():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def _short_kernel(name):
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return n.split("(")[0]
+
+
+def _per_kernel(csv_path, counter):
+    """{kernel: [values]} of one rocprofv3 counter-collection CSV."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter:
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv, workload, command_fetch, command_write):
+    """Calibrated HBM bytes per launch of the partition kernel from a FETCH_SIZE
+    run and a WRITE_SIZE run (values in KiB per dispatch).  Each counter is
+    scaled by what it reads for the start-up copy of exactly 1 GiB."""
+    from paged_kv_decode_amd import workloads as wl
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+
+    def calib(d):
+        cands = [(max(v), k) for k, v in d.items() if "copy" in k.lower() and "pkd::" not in k]
+        best = max(cands)
+        return CALIB_BYTES / (best[0] * 1024.0), best[1]
+
+    f_fac, f_name = calib(fetch)
+    w_fac, w_name = calib(write)
+    part = [k for k in fetch if "pkd::" in k and ("balanced_kernel" in k or "split_kv_kernel" in k)]
+    merge = [k for k in fetch if "pkd::" in k and "lse_merge_kernel" in k]
+    assert part, "no partition kernel in the counter run"
+    k = max(part, key=lambda x: len(fetch[x]))
+    avg = lambda xs: sum(xs) / len(xs)
+    f_kib, w_kib = avg(fetch[k]), avg(write.get(k, [0.0]))
+    bytes_per_launch = f_kib * 1024.0 * f_fac + w_kib * 1024.0 * w_fac
+    w = wl.make_workload(wl.WORKLOADS[workload], tail="zero")
+    alg = algorithmic_bytes(w, split_kernel_only=True)
+    rec = {"workload": workload, "kernel": _short_kernel(k), "fetch_kib_per_dispatch": f_kib,
+           "write_kib_per_dispatch": w_kib, "fetch_scale": f_fac, "write_scale": w_fac,
+           "calibration_kernel_fetch": _short_kernel(f_name), "calibration_kernel_write": _short_kernel(w_name),
+           "calibration_bytes": CALIB_BYTES, "bytes_per_launch": bytes_per_launch,
+           "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": bytes_per_launch / alg,
+           "dispatches": len(fetch[k]), "kernel_source_sha256": _source_digest(),
+           "command_fetch": command_fetch, "command_write": command_write}
+    if merge:
+        m = merge[0]
+        rec["merge_kernel"] = _short_kernel(m)
+        rec["merge_bytes_per_launch"] = (avg(fetch[m]) * 1024.0 * f_fac
+                                         + avg(write.get(m, [0.0])) * 1024.0 * w_fac)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
+def summarize_trace(stats_csv, workload, command, out_name):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# Kernel trace: {workload}", "", "Command:", "", "```", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{_short_kernel(r['Name'])[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def traffic_from_profiles(name):
     """Measured HBM bytes per launch of the partition kernel, if a counter summary
-    for this workload and the current kernel source is committed under profiles/."""
-    import hashlib
+    for this workload and the current kernel source is committed under profiles/
+    (None once the kernel source has changed since the counters were taken)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
-    src = os.path.join(ROOT, "paged_kv_decode_amd", "csrc", "split_kv_decode.hip")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") != digest:
+        if rec.get("kernel_source_sha256") != _source_digest():
             return None
         return rec.get("bytes_per_launch")
     except (OSError, ValueError):
@@ -208,7 +286,19 @@ def main():
                     help="comma-separated workload names, or 'all'")
     ap.add_argument("--num-splits", type=int, default=0, help="0: the library's heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "CMD", "OUT_MD"),
+                    help="write a markdown summary of a rocprofv3 kernel_stats.csv to profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        f, w_, cf, cw = args.summarize_counters
+        print(json.dumps(summarize_counters(f, w_, args.workloads.split(",")[0], cf, cw), indent=1))
+        return
+    if args.summarize_trace:
+        st, cmd, out = args.summarize_trace
+        summarize_trace(st, args.workloads, cmd, out)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode path runs on a single MI355X and has no "
               "multi-GPU mode; run with --gpus 1.", file=sys.stderr)
@@ -219,6 +309,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     device = torch.device("cuda:0")
     scrub = torch.empty(1 << 28, dtype=torch.float32, device=device).fill_(1.0)  # 1 GiB
+    calib = torch.empty_like(scrub)
+    calib.copy_(scrub)  # a plain 1 GiB device copy: the reference dispatch for counter calibration
+    del calib
 
     names = list(wl.WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
     if PRIMARY not in names:
@@ -258,12 +351,13 @@ def main():
         "config": {"workload": PRIMARY, "batch": 32, "num_q_heads": 32, "num_kv_heads": 8,
                    "head_dim": 128, "page_size": 64, "seq_lens": "uniform integers in [1024, 4096]",
                    "kv_dtype": "bf16", "num_splits": p["num_splits"], "tokens": p["tokens"],
-                   "algorithmic_bytes": p["algorithmic_bytes"], "timing": "cold HBM (1 GiB scrub before each step), HIP events"},
+                   "algorithmic_bytes": p["algorithmic_bytes"], "timing": "cold HBM (1 GiB read-only scrub before each step), HIP events"},
         "pct_of_peak": round(p["pct_of_peak"], 2),
         "queries_per_s": round(p["queries_per_s"], 1),
         "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(roof_achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "split_kv_kernel<128, bf16>", "kernel_ms": p["split_kernel_ms"],
+                     "kernel": {-1000: "balanced_kernel<128, bf16>", 1: "split_kv_kernel<128, bf16, direct>"}.get(
+                         p["num_splits"], "split_kv_kernel<128, bf16, partials>"), "kernel_ms": p["split_kernel_ms"],
                      "kernel_bytes": p["split_kernel_bytes"]},
         "workloads": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in results.items()},

@@ -232,15 +232,17 @@ struct WaveAttn {
   // aligned group lies in one page when page_size % 16 == 0); a row past lim is
   // replaced by a valid row of its group (position min(pos, lim - group start))
   // and masked later.
+  // idle: read the same rows of physical page 0 instead (shared by every
+  // workgroup, so they come from cache); the data is not used.
   __device__ __forceinline__ void issue_paged16(const uint8_t* kc, const uint8_t* vc, int tb, int lim,
                                                 const int* pages, int ps, int tok_stride,
-                                                int64_t head_off, Regs& R) const {
+                                                int64_t head_off, Regs& R, bool idle) const {
     int64_t gbase[C::NGRP];
     int glim[C::NGRP];
 #pragma unroll
     for (int q = 0; q < C::NGRP; ++q) {
       const int gt = min(tb + 16 * q, lim) & ~15;
-      const int page = __builtin_amdgcn_readfirstlane(pages[q]);
+      const int page = idle ? 0 : __builtin_amdgcn_readfirstlane(pages[q]);
       gbase[q] = ((int64_t)page * ps + (gt - (gt / ps) * ps)) * tok_stride + head_off;
       glim[q] = lim - gt;
     }
@@ -274,11 +276,11 @@ struct WaveAttn {
   // blk, pages[NBLK + i] that of its row of V load i (rows clamped to lim).
   __device__ __forceinline__ void issue_generic(const uint8_t* kc, const uint8_t* vc, int tb, int lim,
                                                 const int* pages, int ps, int tok_stride,
-                                                int64_t head_off, Regs& R) const {
+                                                int64_t head_off, Regs& R, bool idle) const {
 #pragma unroll
     for (int blk = 0; blk < C::NBLK; ++blk) {
       const int tok = min(tb + k_row_token<C::KP>(blk, n), lim);
-      const int64_t off = ((int64_t)pages[blk] * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
+      const int64_t off = ((int64_t)(idle ? 0 : pages[blk]) * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
       const uint8_t* src = kc + off + k_doff;
 #pragma unroll
       for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = gload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
@@ -286,7 +288,8 @@ struct WaveAttn {
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
       const int tok = min(tb + i * C::RPI + v_rig, lim);
-      const int64_t off = ((int64_t)pages[C::NBLK + i] * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
+      const int64_t off =
+          ((int64_t)(idle ? 0 : pages[C::NBLK + i]) * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
       R.v[i] = gload<C::VLB>(vc + off + v_doff);
     }
   }
@@ -415,8 +418,10 @@ struct WaveAttn {
 
 // Tiles first, first + step, ... (< ntiles): while tile t is processed the
 // next tile's K/V loads are in flight and the page entries of the tile after
-// that are being read.  At the end the "next" tile repeats the last one so
-// that the loads stay unconditional (they hit in cache and are not consumed).
+// that are being read.  After the last tile the "next" loads stay in the
+// instruction stream (so the wait counts are the same on every iteration) but
+// are pointed at rows every workgroup shares by passing idle = true; they are
+// never consumed.
 template <int D, bool FP8, typename Pages, typename Fetch, typename Issue>
 __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int step, int ntiles, int s0,
                                           int s1, uint16_t* vs, Fetch fetch, Issue issue) {
@@ -427,11 +432,11 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
   Pages pa, pb;
   int t = first;
   fetch(t, pa);
-  issue(t, pa, ra);
+  issue(t, pa, ra, false);
   int t1 = nxt(t);
   fetch(t1, pb);
   while (true) {
-    issue(t1, pb, rb);
+    issue(t1, pb, rb, t1 == t);
     int t2 = nxt(t1);
     fetch(t2, pa);
     __builtin_amdgcn_sched_barrier(0);
@@ -439,7 +444,7 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
     if (t1 == t) break;
     t = t1;
     t1 = t2;
-    issue(t1, pa, ra);
+    issue(t1, pa, ra, t1 == t);
     t2 = nxt(t1);
     fetch(t2, pb);
     __builtin_amdgcn_sched_barrier(0);
@@ -488,10 +493,28 @@ __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* s
   }
 }
 
+// Waves per SIMD the register allocation targets.  Two resident waves per
+// SIMD hide the load latency of one another's tiles; the compiler keeps the
+// MFMA accumulators in ordinary VGPRs to fit 256 registers.  The instances
+// that would spill at two (bf16 K/V with per-row page lookups at D = 32 or
+// 256, and the balanced kernel at bf16 D = 256) are left at one; the
+// balanced kernel at D = 32 reaches two without the constraint.
+template <int D, bool FP8, bool PAGED16>
+constexpr int waves_per_simd() {
+  if (!FP8 && !PAGED16 && (D == 32 || D == 256)) return 1;
+  return 2;
+}
+template <int D, bool FP8>
+constexpr int balanced_waves_per_simd() {
+  if (D == 32 || (D == 256 && !FP8)) return 1;
+  return 2;
+}
+
 // ---- grid kernel ----------------------------------------------------------
 
 template <int D, bool FP8, bool PAGED16, bool DIRECT>
 __global__ void __launch_bounds__(kWaves * 64)
+    __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, FP8, PAGED16>())))
 split_kv_kernel(const SplitParams p) {
   typedef Cfg<D, FP8> C;
   typedef TilePages<D, FP8, PAGED16> Pages;
@@ -567,12 +590,12 @@ split_kv_kernel(const SplitParams p) {
       for (int i = 0; i < C::NBLK + C::NV; ++i) P.pg[i] = page_of(min(tb + A.generic_row(i), lim) / ps);
     }
   };
-  auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R) {
+  auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R, bool idle) {
     const int tb = s0 + tile * C::TT;
     if constexpr (PAGED16)
-      A.issue_paged16(p.k, p.v, tb, lim, P.pg, ps, tok_stride, head_off, R);
+      A.issue_paged16(p.k, p.v, tb, lim, P.pg, ps, tok_stride, head_off, R, idle);
     else
-      A.issue_generic(p.k, p.v, tb, lim, P.pg, ps, tok_stride, head_off, R);
+      A.issue_generic(p.k, p.v, tb, lim, P.pg, ps, tok_stride, head_off, R, idle);
   };
 
   uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;  // this wave's V[TT][VS]
@@ -606,6 +629,7 @@ split_kv_kernel(const SplitParams p) {
 
 template <int D, bool FP8>
 __global__ void __launch_bounds__(kWaves * 64)
+    __attribute__((amdgpu_waves_per_eu(balanced_waves_per_simd<D, FP8>())))
 balanced_kernel(const BalancedParams p) {
   typedef Cfg<D, FP8> C;
   typedef TilePages<D, FP8, true> Pages;
@@ -731,8 +755,8 @@ balanced_kernel(const BalancedParams p) {
 #pragma unroll
       for (int q = 0; q < C::NGRP; ++q) P.pg[q] = page_of((min(tb + 16 * q, lim) & ~15) / ps);
     };
-    auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R) {
-      A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, head_off, R);
+    auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R, bool idle) {
+      A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, head_off, R, idle);
     };
     const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
     run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, s1, vs, fetch, issue);
