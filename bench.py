@@ -19,7 +19,7 @@ reported alongside.  The fp64 CPU oracle is timed on the same host arrays
 (whole workload, all host threads up to 16) as a reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads NAMES|all]
-                       [--num-splits S] [--no-cpu-baseline]
+                       [--num-splits S] [--no-cpu-baseline] [--profile-only]
 """
 import argparse
 import json
@@ -286,6 +286,8 @@ def main():
                     help="comma-separated workload names, or 'all'")
     ap.add_argument("--num-splits", type=int, default=0, help="0: the library's heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="time only the named workloads (for a profiler run) and print no JSON line")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "CMD", "OUT_MD"),
@@ -314,7 +316,7 @@ def main():
     del calib
 
     names = list(wl.WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
-    if PRIMARY not in names:
+    if PRIMARY not in names and not args.profile_only:
         names = [PRIMARY] + names
     results = {}
     primary_w = None
@@ -331,6 +333,8 @@ def main():
               f"{res['queries_per_s']:.0f} queries/s; partition kernel {res['split_kernel_gbs']:.0f} GB/s; "
               f"merge share {100 * res['merge_share']:.1f}%; warm {res['warm_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
+    if args.profile_only:
+        return
 
     p = results[PRIMARY]
     roof_achieved = p["split_kernel_gbs"]

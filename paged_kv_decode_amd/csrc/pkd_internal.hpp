@@ -65,14 +65,11 @@ constexpr int kWaves = 4;            // waves per split-kernel workgroup
 constexpr int kSplitAlign = 64;      // tokens; split boundaries are multiples of this
 constexpr int kHeadsPerGroup = 16;   // query heads packed into one MFMA N dimension
 constexpr int kBalancedMaxBatch = 1024;  // largest batch the balanced kernel's prefix scan takes
-constexpr int kBalancedWgsPerCuDefault = 2;  // used when the occupancy cannot be queried
 
 // Launchers (defined in the .hip files).  head_dim in {32, 64, 128, 256}.
 hipError_t launch_split_kv(const SplitParams& p, int batch, int head_dim, bool fp8, bool direct,
                            bool paged16, hipStream_t stream);
 hipError_t launch_balanced(const BalancedParams& p, int head_dim, bool fp8, hipStream_t stream);
-// Resident balanced-kernel workgroups per compute unit for this instance, or -1.
-int balanced_blocks_per_cu(int head_dim, bool fp8);
 hipError_t launch_lse_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* block_table, const int32_t* seq_lens, int batch,
                                int max_pages, int page_size, int num_pages, int32_t* d_count,

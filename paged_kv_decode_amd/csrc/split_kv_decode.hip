@@ -796,13 +796,6 @@ hipError_t launch_d(const SplitParams& p, int batch, bool direct, bool paged16, 
   return direct ? launch_t<D, FP8, false, true>(p, batch, s) : launch_t<D, FP8, false, false>(p, batch, s);
 }
 
-template <int D, bool FP8>
-int occupancy_b() {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_kernel<D, FP8>, kWaves * 64, 0) != hipSuccess)
-    return -1;
-  return n;
-}
 
 template <int D, bool FP8>
 hipError_t launch_b(const BalancedParams& p, hipStream_t stream) {
@@ -823,15 +816,6 @@ hipError_t launch_split_kv(const SplitParams& p, int batch, int head_dim, bool f
   }
 }
 
-int balanced_blocks_per_cu(int head_dim, bool fp8) {
-  switch (head_dim) {
-    case 32: return fp8 ? occupancy_b<32, true>() : occupancy_b<32, false>();
-    case 64: return fp8 ? occupancy_b<64, true>() : occupancy_b<64, false>();
-    case 128: return fp8 ? occupancy_b<128, true>() : occupancy_b<128, false>();
-    case 256: return fp8 ? occupancy_b<256, true>() : occupancy_b<256, false>();
-    default: return -1;
-  }
-}
 
 hipError_t launch_balanced(const BalancedParams& p, int head_dim, bool fp8, hipStream_t stream) {
   switch (head_dim) {

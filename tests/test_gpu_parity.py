@@ -419,3 +419,35 @@ def test_two_phases_equal_paged_decode(B, S):
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.cpu(), ref_lse)
+
+
+@pytest.mark.parametrize("S", [BAL, 4, 1])
+def test_graph_replays(B, S):
+    """A captured decode replays correctly several times, with eager work and
+    synchronisations between the replays, and matches the eager call bitwise."""
+    lens = [(i * 1543) % 6000 + 100 for i in range(32)]
+    w = wl.custom_workload(32, 32, 8, 128, 64, lens, "bf16", seed=21)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    nbytes = B.paged_decode_workspace_bytes(dims, S)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+    eager_out, eager_lse = run(B, w, S, t)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            st = B.paged_decode(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, out, lse,
+                                S, ws if nbytes else None, nbytes, B.current_stream_handle(0))
+    torch.cuda.current_stream().wait_stream(side)
+    assert st == 0
+    for i in range(4):
+        out.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu().view(torch.int16), eager_out.view(torch.int16)), f"replay {i}: out"
+        assert torch.equal(lse.cpu().view(torch.int32), eager_lse.view(torch.int32)), f"replay {i}: lse"
