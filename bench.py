@@ -72,6 +72,7 @@ class Runner:
         self.vs = None if w.v_scale is None else w.v_scale.to(device)
         self.dims = B.dims_for(self.q, self.k, self.bt)
         self.S = num_splits if num_splits != 0 else B.paged_decode_num_splits(self.dims, 0)
+        self.launches = B.paged_decode_launches(self.dims, self.S)  # 1: the partition writes out itself
         s = w.spec
         self.rows = s.batch * s.num_q_heads
         self.out = torch.empty(self.q.shape, dtype=torch.bfloat16, device=device)
@@ -82,11 +83,12 @@ class Runner:
         self.handle = self.stream.cuda_stream
 
     def kernel1(self):
-        """The partition kernel (direct output when S == 1): paged_decode's first phase."""
+        """The partition kernel: the whole of paged_decode when it is one kernel
+        (direct output, or the balanced mode merging in place), else its first phase."""
         B = self.B
-        if self.S == 1:
+        if self.launches == 1:
             st = B.paged_decode(self.dims, self.q, self.k, self.v, self.bt, self.lens, self.ks, self.vs,
-                                self.w.scale, self.out, self.lse, 1, None, 0, self.handle)
+                                self.w.scale, self.out, self.lse, self.S, self.ws, self.ws_bytes, self.handle)
         else:
             st = B.paged_decode_partition(self.dims, self.q, self.k, self.v, self.bt, self.lens, self.ks,
                                           self.vs, self.w.scale, self.S, self.ws, self.ws_bytes, self.handle)
@@ -94,8 +96,8 @@ class Runner:
             raise B.PkdError(st)
 
     def kernel2(self):
-        """The merge kernel (split modes only): paged_decode's second phase."""
-        if self.S != 1:
+        """The merge kernel, when paged_decode uses one: its second phase."""
+        if self.launches == 2:
             st = self.B.paged_decode_finish(self.dims, self.S, self.ws, self.ws_bytes, self.out, self.lse,
                                             self.handle)
             if st != 0:
@@ -114,20 +116,33 @@ def bench_one(name, steps, warmup, num_splits, device, scrub):
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # Pass 1, the metric: one event pair around each whole step (partition and,
+    # when there is one, merge).  Every step starts from cold caches.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         scrub_sum = scrub.sum()  # evict L2 / Infinity Cache with clean lines (outside the events)
+        ev[i][0].record(r.stream)
+        r.step()
+        ev[i][1].record(r.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    # Pass 2: the partition kernel alone (an event after it as well), for the
+    # roofline of the dominant kernel and the merge's share.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        scrub_sum = scrub.sum()
         ev[i][0].record(r.stream)
         r.kernel1()
         ev[i][1].record(r.stream)
         r.kernel2()
         ev[i][2].record(r.stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(steps)]
     k1_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    split_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(steps)]
+    del scrub_sum
     # Warm back-to-back timing (KV partly cache-resident when it fits): secondary only.
     wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wa.record(r.stream)
@@ -141,18 +156,18 @@ def bench_one(name, steps, warmup, num_splits, device, scrub):
     k1_mean = sum(k1_ms) / steps
     srt = sorted(step_ms)
     nbytes = algorithmic_bytes(w)
-    k1_bytes = algorithmic_bytes(w, split_kernel_only=r.S != 1)
+    k1_bytes = algorithmic_bytes(w, split_kernel_only=r.launches == 2)
     res = dict(
         workload=name, batch=w.spec.batch, num_q_heads=w.spec.num_q_heads,
         num_kv_heads=w.spec.num_kv_heads, head_dim=w.spec.head_dim, page_size=w.spec.page_size,
-        kv_dtype=w.spec.kv_dtype, num_splits=r.S, tokens=int(w.seq_lens.sum()),
+        kv_dtype=w.spec.kv_dtype, num_splits=r.S, launches=r.launches, tokens=int(w.seq_lens.sum()),
         algorithmic_bytes=nbytes, ms_per_step=step_mean,
         ms_p10=srt[int(0.1 * (steps - 1))], ms_median=srt[(steps - 1) // 2], ms_p90=srt[int(0.9 * (steps - 1))],
         gbs=nbytes / (step_mean * 1e-3) / 1e9,
         queries_per_s=w.spec.batch / (step_mean * 1e-3),
         split_kernel_ms=k1_mean, split_kernel_bytes=k1_bytes,
         split_kernel_gbs=k1_bytes / (k1_mean * 1e-3) / 1e9,
-        merge_share=(step_mean - k1_mean) / step_mean,
+        merge_share=0.0 if r.launches == 1 else (sum(split_ms) / steps - k1_mean) / (sum(split_ms) / steps),
         warm_ms_per_step=warm_ms, warm_gbs=nbytes / (warm_ms * 1e-3) / 1e9,
         timed_wall_s=wall,
     )
@@ -228,7 +243,8 @@ def summarize_counters(fetch_csv, write_csv, workload, command_fetch, command_wr
     f_kib, w_kib = avg(fetch[k]), avg(write.get(k, [0.0]))
     bytes_per_launch = f_kib * 1024.0 * f_fac + w_kib * 1024.0 * w_fac
     w = wl.make_workload(wl.WORKLOADS[workload], tail="zero")
-    alg = algorithmic_bytes(w, split_kernel_only=True)
+    # Without a merge kernel in the run the partition kernel wrote out and lse itself.
+    alg = algorithmic_bytes(w, split_kernel_only=bool(merge))
     rec = {"workload": workload, "kernel": _short_kernel(k), "fetch_kib_per_dispatch": f_kib,
            "write_kib_per_dispatch": w_kib, "fetch_scale": f_fac, "write_scale": w_fac,
            "calibration_kernel_fetch": _short_kernel(f_name), "calibration_kernel_write": _short_kernel(w_name),
@@ -360,8 +376,10 @@ def main():
         "queries_per_s": round(p["queries_per_s"], 1),
         "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(roof_achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": {-1000: "balanced_kernel<128, bf16>", 1: "split_kv_kernel<128, bf16, direct>"}.get(
-                         p["num_splits"], "split_kv_kernel<128, bf16, partials>"), "kernel_ms": p["split_kernel_ms"],
+                     "kernel": ("balanced_kernel<128, bf16>" + (" (merging in place)" if p["launches"] == 1 else "")
+                                if p["num_splits"] == -1000 else "split_kv_kernel<128, bf16, direct>"
+                                if p["num_splits"] == 1 else "split_kv_kernel<128, bf16, partials>"),
+                     "kernel_ms": p["split_kernel_ms"],
                      "kernel_bytes": p["split_kernel_bytes"]},
         "workloads": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in results.items()},

@@ -123,7 +123,9 @@ typedef struct {
  *   lse          [B][Hq] fp32 natural-log log-sum-exp of the scaled scores, or NULL.
  *   num_splits   PKD_SPLITS_AUTO: chosen by paged_decode_num_splits(dims, 0);
  *                1: direct output (one kernel); 2..PKD_MAX_SPLITS: split-KV + merge (two kernels);
- *                PKD_SPLITS_BALANCED: balanced partition + merge (two kernels).
+ *                PKD_SPLITS_BALANCED: balanced partition, which merges the pieces of each
+ *                (sequence, KV head) itself when few are expected (one kernel; see
+ *                paged_decode_launches), else partition + merge (two kernels).
  *                Any other value is an error.
  *   workspace    device scratch for partials, at least paged_decode_workspace_bytes(dims,
  *                num_splits) bytes (may be NULL when that is 0).  Its contents on entry do
@@ -166,12 +168,24 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
 int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint);
 
 /*
+ * paged_decode_launches -- kernels paged_decode enqueues for num_splits
+ * (PKD_SPLITS_AUTO: the heuristic's choice): 1 for direct output and for the
+ * balanced mode when its partition kernel merges in place (when the
+ * (sequence, KV head, head group) segments are at least as many as the
+ * current device's compute units), else 2.
+ * Host only; returns a status in [-10, -1] for invalid dims or num_splits.
+ */
+int32_t paged_decode_launches(const pkd_dims* dims, int32_t num_splits);
+
+/*
  * paged_decode_workspace_bytes -- workspace paged_decode needs for num_splits
  * (PKD_SPLITS_AUTO: the heuristic's choice): 0 for one split; for S splits the
  * fp32 partials [B][Hq][S][D] and [B][Hq][S]; for PKD_SPLITS_BALANCED the fp32
  * partials of (W + B*Hkv*ceil(G/16)) slots of min(G,16) heads, W the
- * workgroups of the device-sized grid, plus B+1 int64 prefix sums; each part rounded up to
- * 256 bytes.  Returns 0 for invalid dims or an unsupported num_splits.
+ * workgroups of the device-sized grid (one per compute unit), B+1 int64 prefix
+ * sums and B*Hkv*ceil(G/16) uint64 merge counters; each part rounded up to 256
+ * bytes.  Returns 0 for invalid dims or an unsupported num_splits.  The
+ * counters carry a per-call tag, so the workspace never needs initialising.
  */
 size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits);
 

@@ -39,7 +39,7 @@ PKD_DTYPE_BF16 = 0
 PKD_DTYPE_FP8_E4M3 = 1
 
 EXPORTED = ("paged_decode", "paged_decode_partition", "paged_decode_finish", "paged_decode_num_splits",
-            "paged_decode_workspace_bytes", "paged_decode_partials", "paged_decode_merge",
+            "paged_decode_launches", "paged_decode_workspace_bytes", "paged_decode_partials", "paged_decode_merge",
             "paged_decode_check_tables", "paged_decode_status_string")
 
 
@@ -101,6 +101,8 @@ _lib.paged_decode_finish.argtypes = [_dims_p, _i32, _p, ctypes.c_size_t, _p, _p,
 _lib.paged_decode_finish.restype = _i32
 _lib.paged_decode_num_splits.argtypes = [_dims_p, _i32]
 _lib.paged_decode_num_splits.restype = _i32
+_lib.paged_decode_launches.argtypes = [_dims_p, _i32]
+_lib.paged_decode_launches.restype = _i32
 _lib.paged_decode_workspace_bytes.argtypes = [_dims_p, _i32]
 _lib.paged_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.paged_decode_partials.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _i32,
@@ -155,6 +157,10 @@ def paged_decode_finish(dims, num_splits, workspace, workspace_bytes, out, lse, 
 
 def paged_decode_num_splits(dims, max_seq_len_hint: int = 0) -> int:
     return _lib.paged_decode_num_splits(_dims_ref(dims), int(max_seq_len_hint))
+
+
+def paged_decode_launches(dims, num_splits: int) -> int:
+    return _lib.paged_decode_launches(_dims_ref(dims), int(num_splits))
 
 
 def paged_decode_workspace_bytes(dims, num_splits: int) -> int:

@@ -2,8 +2,10 @@
 // workspace sizing and kernel launches.  Nothing here synchronises with the
 // device or copies device memory to the host.
 #include <atomic>
+#include <chrono>
 #include <climits>
 #include <cmath>
+#include <unistd.h>
 
 #include "../../include/paged_kv_decode.h"
 #include "pkd_internal.hpp"
@@ -77,14 +79,41 @@ bool balanced_ok(const pkd_dims& d) {
   return T < ((int64_t)1 << 46);
 }
 
-size_t balanced_bytes(const pkd_dims& d, size_t* lse_offset, size_t* prefix_offset) {
-  const size_t slots = (size_t)balanced_workers(d) + (size_t)d.batch * d.num_kv_heads * head_groups(d);
+// Balanced workspace: partials [slots][hpg][D] fp32, LSEs [slots][hpg] fp32,
+// prefix sums [B + 1] int64, then one in-kernel-merge counter per segment
+// [B * Hkv * head_groups] uint64 (its contents never need initialising).
+size_t balanced_bytes(const pkd_dims& d, size_t* lse_offset, size_t* prefix_offset, size_t* count_offset) {
+  const size_t segments = (size_t)d.batch * d.num_kv_heads * head_groups(d);
+  const size_t slots = (size_t)balanced_workers(d) + segments;
   const size_t hpg = (size_t)heads_per_slot(d);
   const size_t o = align256(slots * hpg * d.head_dim * sizeof(float));
   const size_t l = align256(slots * hpg * sizeof(float));
+  const size_t pre = align256(((size_t)d.batch + 1) * sizeof(int64_t));
   if (lse_offset) *lse_offset = o;
   if (prefix_offset) *prefix_offset = o + l;
-  return o + l + align256(((size_t)d.batch + 1) * sizeof(int64_t));
+  if (count_offset) *count_offset = o + l + pre;
+  return o + l + pre + align256(segments * sizeof(uint64_t));
+}
+
+// Whether the balanced mode merges inside the partition kernel (paged_decode only).
+bool balanced_fused(const pkd_dims& d) {
+  return pkd::balanced_merge_in_kernel(balanced_workers(d), (int64_t)d.batch * d.num_kv_heads * head_groups(d));
+}
+
+// Call tags for the in-kernel merge counters: distinct for every call in this
+// process (40 bits, never 0), starting from a value that differs between
+// processes, so that a counter word left by an earlier call never matches.
+std::atomic<uint64_t> g_epoch{0};
+uint64_t next_epoch() {
+  uint64_t cur = g_epoch.load(std::memory_order_relaxed);
+  if (cur == 0) {
+    const uint64_t seed = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                          ((uint64_t)getpid() << 20);
+    uint64_t expect = 0;
+    g_epoch.compare_exchange_strong(expect, (seed & ((1ull << 40) - 1)) | 1);
+  }
+  uint64_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) & ((1ull << 40) - 1);
+  return e != 0 ? e : 1;
 }
 
 size_t partial_bytes(const pkd_dims& d, int S, size_t* lse_offset) {
@@ -183,7 +212,7 @@ size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits) {
   if (check_dims(dims) != PKD_OK) return 0;
   int S = num_splits;
   if (S == PKD_SPLITS_AUTO) S = heuristic_splits(*dims, dims->max_pages_per_seq * dims->page_size);
-  if (S == PKD_SPLITS_BALANCED) return balanced_ok(*dims) ? balanced_bytes(*dims, nullptr, nullptr) : 0;
+  if (S == PKD_SPLITS_BALANCED) return balanced_ok(*dims) ? balanced_bytes(*dims, nullptr, nullptr, nullptr) : 0;
   if (S < 1 || S > PKD_MAX_SPLITS) return 0;
   if (S == 1) return 0;
   return partial_bytes(*dims, S, nullptr);
@@ -234,7 +263,7 @@ struct Plan {
   int S;           // 1 = direct output, 2.. = grid splits, PKD_SPLITS_BALANCED
   bool balanced;
   size_t need;     // workspace bytes
-  size_t lse_off, prefix_off;
+  size_t lse_off, prefix_off, count_off;
 };
 
 int32_t make_plan(const pkd_dims& d, int32_t num_splits, Plan* pl) {
@@ -243,8 +272,8 @@ int32_t make_plan(const pkd_dims& d, int32_t num_splits, Plan* pl) {
   pl->S = S;
   pl->balanced = S == PKD_SPLITS_BALANCED;
   if (pl->balanced ? !balanced_ok(d) : (S < 1 || S > PKD_MAX_SPLITS)) return PKD_ERR_NUM_SPLITS;
-  pl->lse_off = pl->prefix_off = 0;
-  pl->need = pl->balanced ? balanced_bytes(d, &pl->lse_off, &pl->prefix_off)
+  pl->lse_off = pl->prefix_off = pl->count_off = 0;
+  pl->need = pl->balanced ? balanced_bytes(d, &pl->lse_off, &pl->prefix_off, &pl->count_off)
                           : (S > 1 ? partial_bytes(d, S, &pl->lse_off) : 0);
   return PKD_OK;
 }
@@ -319,6 +348,16 @@ int32_t run_finish(const pkd_dims& d, const void* ws, void* out, float* lse, con
 
 extern "C" {
 
+int32_t paged_decode_launches(const pkd_dims* dims, int32_t num_splits) {
+  const int32_t st = check_dims(dims);
+  if (st != PKD_OK) return st;
+  Plan pl;
+  const int32_t pst = make_plan(*dims, num_splits, &pl);
+  if (pst != PKD_OK) return pst;
+  if (pl.S == 1 || (pl.balanced && balanced_fused(*dims))) return 1;
+  return 2;
+}
+
 int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
                      const float* v_scale, float scale, void* out, float* lse, int32_t num_splits,
@@ -339,6 +378,18 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
     return launch_partition(*dims, p, true, s);
+  }
+  if (pl.balanced && balanced_fused(*dims)) {
+    // One kernel: the partition merges each segment's pieces itself.
+    pkd::BalancedParams b = make_balanced_params(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale,
+                                                 v_scale, scale, workspace, pl);
+    b.fused = 1;
+    b.out = static_cast<uint16_t*>(out);
+    b.lse = lse;
+    b.seg_count = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + pl.count_off);
+    b.epoch = next_epoch();
+    return pkd::launch_balanced(b, dims->head_dim, dims->kv_dtype == PKD_DTYPE_FP8_E4M3, s) == hipSuccess
+               ? PKD_OK : PKD_ERR_LAUNCH;
   }
   st = run_partition(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, workspace,
                      pl, s);

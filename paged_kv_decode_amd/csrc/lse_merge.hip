@@ -11,19 +11,11 @@
 // deterministic.
 //
 // Also: the optional block-table / length validation kernel.
+#include "merge_row.hpp"
 #include "pkd_internal.hpp"
 
 namespace pkd {
 namespace {
-
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLn2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
 
 // WPR waves per output row (WPR = 1: four rows per workgroup).  Wave `part`
 // of a row takes the row's partials j = part, part + WPR, ...: their LSEs are
@@ -34,8 +26,7 @@ __device__ __forceinline__ float wave_max(float x) {
 // in LDS by the same rule.
 template <int D, int WPR>
 __global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(const MergeParams p) {
-  constexpr int EPL = D >= 64 ? D / 64 : 1;  // elements per lane
-  constexpr int UNROLL = 8;
+  constexpr int EPL = RowMerge<D>::EPL;
   constexpr int WAVES = WPR == 1 ? 4 : WPR;
   __shared__ float sm_m[WAVES], sm_w[WAVES];
   __shared__ float sm_o[WPR == 1 ? 1 : WAVES * D];
@@ -91,111 +82,40 @@ __global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(co
   ls *= WPR;
   os *= WPR;
 
-  float M = -INFINITY;
-  float W = 0.f;
-  float o[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  const bool live = lane * EPL < D;
-  if (mine <= UNROLL) {
-    // Few partials (the common case): their LSEs and rows are loaded together,
-    // in one round trip, and combined once the maximum is known.
-    const float l_own = lane < mine ? lp[lane * ls] : -INFINITY;
-    float v[UNROLL][EPL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        v[u][e] = (live && u < mine) ? op[(int64_t)u * os + lane * EPL + e] : 0.f;
-    M = wave_max(l_own);
-    if (M != -INFINITY) {
-      const float wl = lane < mine ? __builtin_amdgcn_exp2f((l_own - M) * kLog2e) : 0.f;
-      W = wl;
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const float wgt = __shfl(wl, u);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] += wgt * v[u][e];
-      }
-    }
-  } else {
-    for (int k = lane; k < mine; k += 64) M = fmaxf(M, lp[k * ls]);
-    M = wave_max(M);
-    if (M != -INFINITY) {
-      for (int k0 = 0; k0 < mine; k0 += 64) {
-        // weights of partials k0 .. k0+63, one per lane
-        const int kl = k0 + lane;
-        const float wl = kl < mine ? __builtin_amdgcn_exp2f((lp[kl * ls] - M) * kLog2e) : 0.f;
-        W += wl;
-        const int kn = min(64, mine - k0);
-        int k = 0;
-        for (; k + UNROLL <= kn; k += UNROLL) {
-          float v[UNROLL][EPL];
-#pragma unroll
-          for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e)
-              v[u][e] = live ? op[(int64_t)(k0 + k + u) * os + lane * EPL + e] : 0.f;
-#pragma unroll
-          for (int u = 0; u < UNROLL; ++u) {
-            const float wgt = __shfl(wl, k + u);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] += wgt * v[u][e];
-          }
-        }
-        for (; k < kn; ++k) {
-          const float wgt = __shfl(wl, k);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e)
-            o[e] += wgt * (live ? op[(int64_t)(k0 + k) * os + lane * EPL + e] : 0.f);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) W += __shfl_xor(W, m);
+  RowMerge<D> r;
+  r.run(lp, ls, op, os, mine, lane);
 
   if constexpr (WPR > 1) {
     // Combine the waves: M = max M_w, W = sum e_w W_w, o = sum e_w o_w, e_w = exp(M_w - M).
+    const bool live = lane * EPL < D;
     if (lane == 0) {
-      sm_m[wave] = M;
-      sm_w[wave] = W;
+      sm_m[wave] = r.M;
+      sm_w[wave] = r.W;
     }
     if (live)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[wave * D + lane * EPL + e] = o[e];
+      for (int e = 0; e < EPL; ++e) sm_o[wave * D + lane * EPL + e] = r.o[e];
     __syncthreads();
     if (wave != 0) return;
     float Mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) Mx = fmaxf(Mx, sm_m[w]);
-    W = 0.f;
+    r.W = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+    for (int e = 0; e < EPL; ++e) r.o[e] = 0.f;
     if (Mx != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        const float ew = __builtin_amdgcn_exp2f((sm_m[w] - Mx) * kLog2e);  // 0 for an empty wave
-        W += ew * sm_w[w];
+        const float ew = __builtin_amdgcn_exp2f((sm_m[w] - Mx) * kMergeLog2e);  // 0 for an empty wave
+        r.W += ew * sm_w[w];
         if (live)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) o[e] += ew * sm_o[w * D + lane * EPL + e];
+          for (int e = 0; e < EPL; ++e) r.o[e] += ew * sm_o[w * D + lane * EPL + e];
       }
     }
-    M = Mx;
+    r.M = Mx;
   }
-
-  if (live) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float v = M != -INFINITY ? o[e] / W : 0.f;
-      const __bf16 h = (__bf16)v;
-      uint16_t bits;
-      __builtin_memcpy(&bits, &h, 2);
-      p.out[row * D + lane * EPL + e] = bits;
-    }
-  }
-  if (lane == 0 && p.lse) p.lse[row] = M != -INFINITY ? M + log2f(W) * kLn2 : -INFINITY;
+  r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane);
 }
 
 // Counts sequences with a length outside [0, max_pages * page_size] and used
@@ -238,9 +158,12 @@ hipError_t launch_merge_t(const MergeParams& p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_merge_d(const MergeParams& p, hipStream_t stream) {
-  // Waves per row from the partials a row is expected to hold.
-  int64_t per_row = p.num_splits;
-  if (p.balanced) per_row = p.num_workers / ((int64_t)p.batch * p.hkv * p.head_groups) + 2;
+  // Waves per row from the partials a row is expected to hold.  In the
+  // balanced layout one wave per row exactly when the partition kernel would
+  // merge in-kernel, so that both paths give the same bits.
+  const int64_t segments = (int64_t)p.batch * p.hkv * p.head_groups;
+  if (p.balanced && balanced_merge_in_kernel(p.num_workers, segments)) return launch_merge_t<D, 1>(p, stream);
+  const int64_t per_row = p.balanced ? p.num_workers / segments + 2 : p.num_splits;
   if (per_row >= 64) return launch_merge_t<D, 16>(p, stream);
   if (per_row >= 12) return launch_merge_t<D, 4>(p, stream);
   return launch_merge_t<D, 1>(p, stream);

@@ -44,7 +44,27 @@ struct BalancedParams {
   int32_t hpg;                 // heads per slot: min(group, 16)
   int32_t page_size, max_pages;
   int32_t num_workers;         // workgroups in the grid
+  // In-kernel merge (fused != 0): segments held by one piece write out/lse
+  // directly; for the others the last piece to finish (found with seg_count)
+  // merges the segment's partials.  seg_count[s] holds (epoch << 24) | pieces
+  // done; a word with another epoch counts as zero, and the merging piece
+  // resets it to (epoch << 24), so no initialisation is ever needed.
+  int32_t fused;
+  uint16_t* out;               // [B][Hq][D] bf16 (fused)
+  float* lse;                  // [B][Hq] or null (fused)
+  uint64_t* seg_count;         // [B * Hkv * head_groups] (fused)
+  uint64_t epoch;              // distinct per call, 1 .. 2^40 - 1 (fused)
 };
+
+// True when the balanced mode merges inside the partition kernel: when there
+// are at least as many segments as workgroups, so a segment spans one or two
+// pieces and a multi-piece merge is short.  (Measured: the same or faster
+// there; slower with ~8 pieces per segment, where the last piece's merge
+// lengthens the tail.)  The merge kernel then uses one wave per row, so both
+// paths run the same per-row merge and give the same bits.
+__host__ __device__ inline bool balanced_merge_in_kernel(int64_t workers, int64_t segments) {
+  return segments > 0 && workers <= segments;
+}
 
 // Arguments of the log-sum-exp merge kernel.  Grid-kernel partials sit at
 // [row][j] (j < num_splits); balanced-kernel partials of a row's segment sit at

@@ -37,6 +37,7 @@
 // Rows past the end of a range are clamped to the last valid row for
 // addressing (so no page past the sequence and no tail slot is ever read) and
 // masked to -inf by selection.  An empty range writes o = 0 and lse = -inf.
+#include "merge_row.hpp"
 #include "pkd_internal.hpp"
 
 namespace pkd {
@@ -497,16 +498,11 @@ __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* s
 // SIMD hide the load latency of one another's tiles; the compiler keeps the
 // MFMA accumulators in ordinary VGPRs to fit 256 registers.  The instances
 // that would spill at two (bf16 K/V with per-row page lookups at D = 32 or
-// 256, and the balanced kernel at bf16 D = 256) are left at one; the
-// balanced kernel at D = 32 reaches two without the constraint.
+// 256) are left at one.  The balanced kernel runs one workgroup per compute
+// unit, so it is not constrained.
 template <int D, bool FP8, bool PAGED16>
 constexpr int waves_per_simd() {
   if (!FP8 && !PAGED16 && (D == 32 || D == 256)) return 1;
-  return 2;
-}
-template <int D, bool FP8>
-constexpr int balanced_waves_per_simd() {
-  if (D == 32 || (D == 256 && !FP8)) return 1;
   return 2;
 }
 
@@ -628,15 +624,14 @@ split_kv_kernel(const SplitParams p) {
 // must be a multiple of 16.
 
 template <int D, bool FP8>
-__global__ void __launch_bounds__(kWaves * 64)
-    __attribute__((amdgpu_waves_per_eu(balanced_waves_per_simd<D, FP8>())))
-balanced_kernel(const BalancedParams p) {
+__global__ void __launch_bounds__(kWaves * 64) balanced_kernel(const BalancedParams p) {
   typedef Cfg<D, FP8> C;
   typedef TilePages<D, FP8, true> Pages;
   constexpr int SMEM = C::VT_BYTES > C::MERGE_BYTES ? C::VT_BYTES : C::MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ int64_t spre[kBalancedMaxBatch + 1];  // spre[b] = groups of all segments of sequences < b
   __shared__ int64_t stot[kWaves];
+  __shared__ int s_last;                           // in-kernel merge: this piece completes its segment
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -682,6 +677,15 @@ balanced_kernel(const BalancedParams p) {
     for (int i = tid; i <= B; i += kWaves * 64) p.prefix[i] = spre[i];
   const int64_t nwe = min((int64_t)p.num_workers, T);
   const int64_t w = blockIdx.x;
+  if (p.fused) {
+    // Sequences of length 0 have no piece: out = 0, lse = -inf (workgroup bb % W).
+    for (int bb = (int)w; bb < B; bb += p.num_workers) {
+      if (spre[bb + 1] != spre[bb]) continue;
+      for (int i = tid; i < p.hq * D; i += kWaves * 64) p.out[(int64_t)bb * p.hq * D + i] = 0;
+      if (p.lse)
+        for (int i = tid; i < p.hq; i += kWaves * 64) p.lse[(int64_t)bb * p.hq + i] = -INFINITY;
+    }
+  }
   if (w >= nwe) return;  // the whole workgroup leaves together
 
   int64_t pos = w * T / nwe;
@@ -761,16 +765,72 @@ balanced_kernel(const BalancedParams p) {
     const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
     run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, s1, vs, fetch, issue);
 
-    // This piece's partial, for the group's heads.
-    const int64_t slot = w + (int64_t)b * SPB + seg;
+    // This segment's pieces are those of workgroups w_first .. w_last, at
+    // slots w + s (s = b * SPB + seg).
+    const int64_t sidx = (int64_t)b * SPB + seg;
+    const int64_t seg_pos = spre[b] + (int64_t)seg * nb;
+    const int64_t w_first = ((seg_pos + 1) * nwe - 1) / T;
+    const int npieces = (int)(((seg_pos + nb) * nwe - 1) / T - w_first + 1);
     const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
-    float* orow = p.o_part + slot * p.hpg * D;
-    float* lrow = p.lse_part + slot * p.hpg;
-    wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
-      orow[hh * D + d] = o;
-      if (d == 0) lrow[hh] = lse_nat;
-    });
-    __syncthreads();  // the LDS is reused by the next piece
+    if (p.fused && npieces == 1) {
+      // The whole segment is this piece: write the result directly.
+      wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
+        p.out[(row0 + hh) * D + d] = bit_cast_dev<uint16_t>((__bf16)o);
+        if (d == 0 && p.lse) p.lse[row0 + hh] = lse_nat;
+      });
+      __syncthreads();  // the LDS is reused by the next piece
+    } else {
+      // This piece's partial, for the group's heads.
+      const int64_t slot = w + sidx;
+      float* orow = p.o_part + slot * p.hpg * D;
+      float* lrow = p.lse_part + slot * p.hpg;
+      if (!p.fused) {
+        wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
+          orow[hh * D + d] = o;
+          if (d == 0) lrow[hh] = lse_nat;
+        });
+      } else {
+        // Agent-scope stores write through to the coherent copy that another
+        // XCD's workgroup will read; waiting for their acknowledgement before the
+        // count makes the partial visible to whichever piece merges.  (A release
+        // fence would write back this XCD's whole L2, far too costly per piece.)
+        wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
+          __hip_atomic_store(orow + hh * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (d == 0) __hip_atomic_store(lrow + hh, lse_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        });
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are acknowledged
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // Count this piece in; the last of the segment's pieces merges them.
+        __syncthreads();
+        if (tid == 0) {
+          const uint64_t E = p.epoch;
+          uint64_t* cw = p.seg_count + sidx;
+          uint64_t old = __hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          uint64_t nv;
+          do {
+            nv = ((old >> 24) == E ? old : (E << 24)) + 1;
+          } while (!__hip_atomic_compare_exchange_weak(cw, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+          const bool last = (int)(nv & 0xFFFFFF) == npieces;
+          if (last) __hip_atomic_store(cw, E << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_last = last;
+        }
+        __syncthreads();
+        const bool last = s_last != 0;
+        if (last) {
+          // The other pieces' partials, read from the coherent copy.
+          const int64_t slot0 = w_first + sidx;
+          for (int hh = wave; hh < heads_here; hh += kWaves) {
+            RowMerge<D, true> r;
+            r.run(p.lse_part + slot0 * p.hpg + hh, p.hpg, p.o_part + (slot0 * p.hpg + hh) * D,
+                  (int64_t)p.hpg * D, npieces, tid & 63);
+            r.store(p.out + (row0 + hh) * D, p.lse ? p.lse + row0 + hh : nullptr, tid & 63);
+          }
+        }
+      }
+      __syncthreads();  // the LDS is reused by the next piece
+    }
 
     pos = npos;
     grp = 0;

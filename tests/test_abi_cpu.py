@@ -207,3 +207,19 @@ def test_balanced_mode_rules():
 def test_one_hip_runtime_in_process():
     """The library binds to PyTorch's HIP runtime instead of mapping a second one."""
     assert len(b._hip_runtimes_mapped()) <= 1
+
+
+def test_launch_counts():
+    """Direct output is one kernel; grid splits two; the balanced mode one where
+    segments are at least as many as workgroups (it merges in place), else two."""
+    b32 = dims(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
+               num_pages=1500, max_pages_per_seq=64)
+    assert b.paged_decode_launches(b32, 1) == 1
+    assert b.paged_decode_launches(b32, 4) == 2
+    assert b.paged_decode_launches(b32, b.PKD_SPLITS_BALANCED) == 1
+    assert b.paged_decode_launches(b32, 0) == 1
+    long1 = dims(batch=1, num_q_heads=16, num_kv_heads=2, head_dim=64, page_size=64,
+                 num_pages=2048, max_pages_per_seq=2048)
+    assert b.paged_decode_launches(long1, b.PKD_SPLITS_BALANCED) == 2
+    assert b.paged_decode_launches(b32, -5) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_launches(dims(head_dim=96), 1) == b.PKD_ERR_HEAD_DIM

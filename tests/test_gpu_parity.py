@@ -401,10 +401,18 @@ def test_full_size_workload_sampled_rows(B, name):
         assert torch.isfinite(a[0].float()).all()
 
 
-@pytest.mark.parametrize("S", [4, BAL])
-def test_two_phases_equal_paged_decode(B, S):
-    """paged_decode_partition then paged_decode_finish is exactly paged_decode."""
-    w = wl.custom_workload(5, 16, 2, 128, 64, [700, 1, 0, 3000, 64], "bf16", seed=123)
+TWO_PHASE_CASES = {
+    "small": (5, 16, 2, 128, 64, [700, 1, 0, 3000, 64]),  # few segments: partition + merge kernel
+    "b32": (32, 32, 8, 128, 64, [(i * 613) % 3500 + 1 for i in range(30)] + [0, 64]),
+}
+
+
+@pytest.mark.parametrize("S,case", [(4, "small"), (BAL, "small"), (BAL, "b32"), (0, "b32")])
+def test_two_phases_equal_paged_decode(B, S, case):
+    """paged_decode_partition then paged_decode_finish is exactly paged_decode,
+    also where paged_decode merges inside the partition kernel (b32)."""
+    bq, hq, hkv, d, ps, lens = TWO_PHASE_CASES[case]
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, "bf16", seed=123)
     t = dev(w)
     ref_out, ref_lse = run(B, w, S, t)
     dims = B.dims_for(t["q"], t["k"], t["bt"])
@@ -451,3 +459,25 @@ def test_graph_replays(B, S):
         torch.cuda.synchronize()
         assert torch.equal(out.cpu().view(torch.int16), eager_out.view(torch.int16)), f"replay {i}: out"
         assert torch.equal(lse.cpu().view(torch.int32), eager_lse.view(torch.int32)), f"replay {i}: lse"
+
+
+def test_in_kernel_merge_ignores_workspace_contents(B):
+    """The balanced mode that merges in place needs no initialised workspace:
+    garbage, zeros and the words a previous call left give the same bits."""
+    lens = [(i * 997) % 4000 + 1 for i in range(40)] + [0] * 3
+    w = wl.custom_workload(len(lens), 32, 8, 128, 64, lens, "bf16", seed=77)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    assert B.paged_decode_launches(dims, BAL) == 1
+    nbytes = B.paged_decode_workspace_bytes(dims, BAL)
+    outs = []
+    for fill in (0xFF, 0x00, None, 0x5A):
+        ws = torch.full((nbytes,), fill if fill is not None else 0, dtype=torch.uint8, device="cuda")
+        if fill is None:  # a workspace that a previous call has used
+            B.decode(t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale, num_splits=BAL, workspace=ws)
+        out, lse = B.decode(t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale, num_splits=BAL, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().view(torch.int16), lse.cpu().view(torch.int32)))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    check(outs[0][0].view(torch.bfloat16), outs[0][1].view(torch.float32), *oracle_full(w), what="in-kernel merge")
