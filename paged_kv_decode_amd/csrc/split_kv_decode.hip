@@ -461,15 +461,15 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
 // lse_nat): o = sum_w e_w O_w / sum_w e_w l_w (times vsc), with
 // e_w = 2^(m_w - max m), and the natural-log LSE.  Ends with the LDS still in
 // use: synchronise before reusing it.
-template <int D, bool FP8, typename Store>
+template <int D, bool FP8, int NWV = kWaves, typename Store>
 __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* smem, int wave, int tid,
                                            int heads_here, float vsc, Store store) {
   typedef Cfg<D, FP8> C;
   const float l_tot = A.l_total();
   __syncthreads();
-  float* mw = reinterpret_cast<float*>(smem);  // [kWaves][16]
-  float* lw = mw + kWaves * 16;                // [kWaves][16]
-  float* ow = lw + kWaves * 16;                // [kWaves][16][OW_STRIDE]
+  float* mw = reinterpret_cast<float*>(smem);  // [NWV][16]
+  float* lw = mw + NWV * 16;                // [NWV][16]
+  float* ow = lw + NWV * 16;                // [NWV][16][OW_STRIDE]
   if (A.g == 0) {
     mw[wave * 16 + A.n] = A.m_run;
     lw[wave * 16 + A.n] = l_tot;
@@ -478,14 +478,14 @@ __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* s
   for (int nb = 0; nb < C::NB; ++nb)
     *reinterpret_cast<f32x4*>(ow + (wave * 16 + A.n) * C::OW_STRIDE + 16 * nb + 4 * A.g) = A.acc[nb];
   __syncthreads();
-  for (int idx = tid; idx < heads_here * D; idx += kWaves * 64) {
+  for (int idx = tid; idx < heads_here * D; idx += NWV * 64) {
     const int hh = idx / D, d = idx - (idx / D) * D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w * 16 + hh]);
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, mw[w * 16 + hh]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NWV; ++w) {
       const float e = __builtin_amdgcn_exp2f(mw[w * 16 + hh] - M);
       num += e * ow[(w * 16 + hh) * C::OW_STRIDE + d];
       den += e * lw[w * 16 + hh];
@@ -623,14 +623,17 @@ split_kv_kernel(const SplitParams p) {
 // merge kernel finds segment s's pieces from the same formula.  page_size
 // must be a multiple of 16.
 
-template <int D, bool FP8>
-__global__ void __launch_bounds__(kWaves * 64) balanced_kernel(const BalancedParams p) {
+template <int D, bool FP8, int NWV>
+__global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4)))
+balanced_kernel(const BalancedParams p) {
   typedef Cfg<D, FP8> C;
   typedef TilePages<D, FP8, true> Pages;
-  constexpr int SMEM = C::VT_BYTES > C::MERGE_BYTES ? C::VT_BYTES : C::MERGE_BYTES;
+  constexpr int VT_BYTES = NWV * C::TT * C::VS * 2;                 // wave-private V tiles
+  constexpr int MERGE_BYTES = NWV * 16 * (2 + C::OW_STRIDE) * 4;   // combine staging
+  constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ int64_t spre[kBalancedMaxBatch + 1];  // spre[b] = groups of all segments of sequences < b
-  __shared__ int64_t stot[kWaves];
+  __shared__ int64_t stot[NWV];
   __shared__ int s_last;                           // in-kernel merge: this piece completes its segment
 
   const int tid = threadIdx.x;
@@ -643,7 +646,7 @@ __global__ void __launch_bounds__(kWaves * 64) balanced_kernel(const BalancedPar
   // a shuffle scan runs inside each wave, and the wave totals are added across
   // waves through LDS.
   {
-    constexpr int PER = kBalancedMaxBatch / (kWaves * 64);
+    constexpr int PER = kBalancedMaxBatch / (NWV * 64);
     const int lane = tid & 63;
     int64_t run[PER];
     int64_t sum = 0;
@@ -674,16 +677,16 @@ __global__ void __launch_bounds__(kWaves * 64) balanced_kernel(const BalancedPar
   }
   const int64_t T = spre[B];
   if (blockIdx.x == 0)
-    for (int i = tid; i <= B; i += kWaves * 64) p.prefix[i] = spre[i];
+    for (int i = tid; i <= B; i += NWV * 64) p.prefix[i] = spre[i];
   const int64_t nwe = min((int64_t)p.num_workers, T);
   const int64_t w = blockIdx.x;
   if (p.fused) {
     // Sequences of length 0 have no piece: out = 0, lse = -inf (workgroup bb % W).
     for (int bb = (int)w; bb < B; bb += p.num_workers) {
       if (spre[bb + 1] != spre[bb]) continue;
-      for (int i = tid; i < p.hq * D; i += kWaves * 64) p.out[(int64_t)bb * p.hq * D + i] = 0;
+      for (int i = tid; i < p.hq * D; i += NWV * 64) p.out[(int64_t)bb * p.hq * D + i] = 0;
       if (p.lse)
-        for (int i = tid; i < p.hq; i += kWaves * 64) p.lse[(int64_t)bb * p.hq + i] = -INFINITY;
+        for (int i = tid; i < p.hq; i += NWV * 64) p.lse[(int64_t)bb * p.hq + i] = -INFINITY;
     }
   }
   if (w >= nwe) return;  // the whole workgroup leaves together
@@ -763,7 +766,7 @@ __global__ void __launch_bounds__(kWaves * 64) balanced_kernel(const BalancedPar
       A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, head_off, R, idle);
     };
     const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
-    run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, s1, vs, fetch, issue);
+    run_tiles<D, FP8, Pages>(A, wave, NWV, ntiles, s0, s1, vs, fetch, issue);
 
     // This segment's pieces are those of workgroups w_first .. w_last, at
     // slots w + s (s = b * SPB + seg).
@@ -774,7 +777,7 @@ __global__ void __launch_bounds__(kWaves * 64) balanced_kernel(const BalancedPar
     const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
     if (p.fused && npieces == 1) {
       // The whole segment is this piece: write the result directly.
-      wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
+      wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
         p.out[(row0 + hh) * D + d] = bit_cast_dev<uint16_t>((__bf16)o);
         if (d == 0 && p.lse) p.lse[row0 + hh] = lse_nat;
       });
@@ -785,7 +788,7 @@ __global__ void __launch_bounds__(kWaves * 64) balanced_kernel(const BalancedPar
       float* orow = p.o_part + slot * p.hpg * D;
       float* lrow = p.lse_part + slot * p.hpg;
       if (!p.fused) {
-        wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
           orow[hh * D + d] = o;
           if (d == 0) lrow[hh] = lse_nat;
         });
@@ -794,7 +797,7 @@ __global__ void __launch_bounds__(kWaves * 64) balanced_kernel(const BalancedPar
         // XCD's workgroup will read; waiting for their acknowledgement before the
         // count makes the partial visible to whichever piece merges.  (A release
         // fence would write back this XCD's whole L2, far too costly per piece.)
-        wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
           __hip_atomic_store(orow + hh * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (d == 0) __hip_atomic_store(lrow + hh, lse_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         });
@@ -821,7 +824,7 @@ __global__ void __launch_bounds__(kWaves * 64) balanced_kernel(const BalancedPar
         if (last) {
           // The other pieces' partials, read from the coherent copy.
           const int64_t slot0 = w_first + sidx;
-          for (int hh = wave; hh < heads_here; hh += kWaves) {
+          for (int hh = wave; hh < heads_here; hh += NWV) {
             RowMerge<D, true> r;
             r.run(p.lse_part + slot0 * p.hpg + hh, p.hpg, p.o_part + (slot0 * p.hpg + hh) * D,
                   (int64_t)p.hpg * D, npieces, tid & 63);
@@ -857,9 +860,15 @@ hipError_t launch_d(const SplitParams& p, int batch, bool direct, bool paged16, 
 }
 
 
+// Waves per balanced workgroup: four (one per SIMD) for bf16 K/V; eight for
+// FP8, whose tiles carry half the bytes, so that as many bytes are in flight
+// per compute unit (measured: 3% faster for FP8, 4-20% slower for bf16).
+constexpr int balanced_waves(bool fp8) { return fp8 ? 8 : 4; }
+
 template <int D, bool FP8>
 hipError_t launch_b(const BalancedParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((balanced_kernel<D, FP8>), dim3(p.num_workers), dim3(kWaves * 64), 0, stream, p);
+  constexpr int NWV = balanced_waves(FP8);
+  hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV>), dim3(p.num_workers), dim3(NWV * 64), 0, stream, p);
   return hipGetLastError();
 }
 
