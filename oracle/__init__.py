@@ -29,11 +29,17 @@ _STATUS = {0: "ok", -1: "bad argument", -2: "block-table entry outside the page 
 
 
 def lib():
+    """The loaded oracle library.  PKD_ORACLE_LIB, when set, names another build of
+    paged_attention_ref.c to load instead (the mutation tests point it at copies
+    with planted mistakes); otherwise the in-tree build is used, built on demand."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        path = os.environ.get("PKD_ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        L = ctypes.CDLL(path)
         common = [_c_int] * 8 + [_p] * 7 + [_c_double]
         L.pkd_oracle_paged_decode.argtypes = common + [_p, _p, _c_int]
         L.pkd_oracle_paged_decode.restype = _c_int

@@ -13,14 +13,15 @@ SRC = os.path.join(HERE, "paged_attention_ref.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, src: str = SRC, lib: str = LIB) -> str:
+    """Compile `src` (the oracle source, or a copy of it) into the shared library `lib`."""
     cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
-           "-pthread", SRC, "-o", LIB + ".tmp", "-lm"]
+           "-pthread", src, "-o", lib + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
