@@ -49,6 +49,11 @@ def lib():
         L.pkd_oracle_paged_decode_rows.restype = _c_int
         L.pkd_oracle_paged_decode_ranges.argtypes = common + [_p, _p, _p, _p]
         L.pkd_oracle_paged_decode_ranges.restype = _c_int
+        multi = [_c_int] * 10 + [_p] * 7 + [_c_double]
+        L.pkd_oracle_paged_decode_multi.argtypes = multi + [_p, _p, _c_int]
+        L.pkd_oracle_paged_decode_multi.restype = _c_int
+        L.pkd_oracle_paged_decode_multi_rows.argtypes = multi + [_c_int, _p, _p, _p]
+        L.pkd_oracle_paged_decode_multi_rows.restype = _c_int
         L.pkd_oracle_lse_merge.argtypes = [ctypes.c_int64, _c_int, _c_int, _p, _p, _p, _p]
         L.pkd_oracle_lse_merge.restype = None
         L.pkd_oracle_bf16_value.argtypes = [ctypes.c_uint16]
@@ -90,7 +95,11 @@ class _Args:
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, scale, k_scale=None, v_scale=None,
                  kv_fp8=None):
         self.q = _raw(q, np.uint16)
-        B, hq, d = self.q.shape
+        if self.q.ndim == 4:  # [B][q_len][Hq][D]: several query tokens per sequence
+            B, self.q_len, hq, d = self.q.shape
+        else:
+            B, hq, d = self.q.shape
+            self.q_len = 1
         kv_fp8 = (np.asarray(k_cache).dtype.itemsize == 1 if not hasattr(k_cache, "element_size")
                   else k_cache.element_size() == 1) if kv_fp8 is None else kv_fp8
         self.fp8 = bool(kv_fp8)
@@ -107,8 +116,14 @@ class _Args:
         self.scale = float(scale)
 
     def head(self):
+        assert self.q_len == 1, "single-token entry points take q as [B][Hq][D]"
         return list(self.dims) + [_ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.bt),
                                   _ptr(self.lens), _ptr(self.ks), _ptr(self.vs), self.scale]
+
+    def head_multi(self, causal):
+        return list(self.dims) + [self.q_len, int(bool(causal))] + [
+            _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.bt), _ptr(self.lens), _ptr(self.ks),
+            _ptr(self.vs), self.scale]
 
 
 def paged_decode(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale=None, v_scale=None,
@@ -161,6 +176,32 @@ def paged_decode_ranges(q, k_cache, v_cache, block_table, seq_lens, scale, t_beg
     return out, lse
 
 
+def paged_decode_multi(q, k_cache, v_cache, block_table, seq_lens, scale, causal, k_scale=None,
+                       v_scale=None, nthreads: int = 1):
+    """Several query tokens per sequence: q [B, q_len, Hq, D]; query token i is at
+    position L - q_len + i and, with causal, sees tokens up to that position only.
+    Returns (out [B, q_len, Hq, D] float64, lse [B, q_len, Hq] float64)."""
+    a = _Args(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale, v_scale)
+    B, hq, _, d = a.dims[:4]
+    out = np.empty((B, a.q_len, hq, d), np.float64)
+    lse = np.empty((B, a.q_len, hq), np.float64)
+    _check(lib().pkd_oracle_paged_decode_multi(*a.head_multi(causal), _ptr(out), _ptr(lse), int(nthreads)))
+    return out, lse
+
+
+def paged_decode_multi_rows(q, k_cache, v_cache, block_table, seq_lens, scale, causal, rows,
+                            k_scale=None, v_scale=None):
+    """paged_decode_multi for rows = (b * q_len + i) * Hq + h only.  Returns (out [n, D], lse [n])."""
+    a = _Args(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale, v_scale)
+    d = a.dims[3]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.empty((rows.size, d), np.float64)
+    lse = np.empty((rows.size,), np.float64)
+    _check(lib().pkd_oracle_paged_decode_multi_rows(*a.head_multi(causal), int(rows.size), _ptr(rows),
+                                                    _ptr(out), _ptr(lse)))
+    return out, lse
+
+
 def lse_merge(o_part, lse_part):
     """o_part [R, S, D], lse_part [R, S] (float64) -> (out [R, D], lse [R])."""
     o = np.ascontiguousarray(o_part, dtype=np.float64)
@@ -185,6 +226,9 @@ def run_workload(w, nthreads: int = 1, num_splits: int = 0):
     """Oracle over a drawn workload object (q, k_cache, v_cache, block_table,
     seq_lens, scale, k_scale, v_scale attributes)."""
     args = (w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale)
+    if getattr(w.spec, "q_len", 1) > 1 or getattr(w.spec, "causal", False):
+        assert not num_splits
+        return paged_decode_multi(*args, w.spec.causal, w.k_scale, w.v_scale, nthreads)
     if num_splits:
         return paged_decode_split(*args, num_splits, w.k_scale, w.v_scale, nthreads)
     return paged_decode(*args, w.k_scale, w.v_scale, nthreads)

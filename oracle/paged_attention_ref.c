@@ -36,6 +36,19 @@
  * PagedPersistentMergeKernel; the merge_attn_states row of the sglang
  * fuse/overlap catalogue, vLLM section).
  *
+ * Several query tokens per sequence (pkd_oracle_paged_decode_multi): the
+ * speculative-verify / extend form that the b12x "Paged attention" row lists
+ * beside decode, and that the AstrAI log's causal offset (the position of the
+ * first query token) describes.  Each sequence b has q_len query tokens whose
+ * rows are q[b][i][h][:], i in [0, q_len); the query tokens are the last
+ * q_len positions of the sequence, so token i sits at position L - q_len + i.
+ * Without the causal mask every query token attends over all L tokens; with
+ * it, query token i attends over tokens t <= L - q_len + i only, i.e. over the
+ * first clamp(L - q_len + i + 1, 0, L) tokens (none when that is <= 0: out =
+ * 0, lse = -inf).  Each query token is then exactly the single-token
+ * definition above over its visible tokens.  q_len = 1 without the mask is the
+ * single-token decode.
+ *
  * Work is spread over an optional pthread pool by (sequence, KV head) items.
  * The items are independent and each is computed in a fixed order, so the
  * result is bitwise identical for any thread count.
@@ -92,8 +105,10 @@ typedef struct {
   const float* v_scale;
   double scale;
   int num_splits;             /* 0: plain definition; >= 1: split form */
-  double* out;                /* [B][Hq][D] */
-  double* lse;                /* [B][Hq] */
+  double* out;                /* [B][q_len][Hq][D] */
+  double* lse;                /* [B][q_len][Hq] */
+  int q_len;                  /* query tokens per sequence, >= 1 */
+  int causal;                 /* 0: every query token sees all L tokens; 1: causal mask */
 } problem;
 
 /* Value of element d of token t's key (is_v = 0) or value (is_v = 1) row for
@@ -112,15 +127,24 @@ static double kv_elem(const problem* P, int is_v, int b, int t, int g, int d) {
   return pkd_oracle_bf16_value(c[idx]);
 }
 
-/* Attention of query head h of sequence b over tokens [t0, t1), by the plain
- * two-pass definition.  Writes D values to o and returns the natural-log LSE;
- * an empty range gives o = 0 and lse = -inf.  `s` is caller scratch of at
- * least t1 - t0 doubles. */
-static double attend_range(const problem* P, int b, int h, int t0, int t1, double* o, double* s) {
+/* Tokens visible to query token qi of sequence b: all L without the causal
+ * mask, else those at positions <= L - q_len + qi. */
+static int visible_tokens(const problem* P, int b, int qi) {
+  const int L = P->seq_lens[b];
+  if (!P->causal) return L;
+  const int v = L - P->q_len + qi + 1;
+  return v < 0 ? 0 : (v > L ? L : v);
+}
+
+/* Attention of query token qi, head h of sequence b over tokens [t0, t1), by
+ * the plain two-pass definition.  Writes D values to o and returns the
+ * natural-log LSE; an empty range gives o = 0 and lse = -inf.  `s` is caller
+ * scratch of at least t1 - t0 doubles. */
+static double attend_range(const problem* P, int b, int qi, int h, int t0, int t1, double* o, double* s) {
   const int D = P->head_dim;
   const int G = P->hq / P->hkv;
   const int g = h / G;
-  const uint16_t* qrow = P->q + ((int64_t)b * P->hq + h) * D;
+  const uint16_t* qrow = P->q + (((int64_t)b * P->q_len + qi) * P->hq + h) * D;
   for (int d = 0; d < D; ++d) o[d] = 0.0;
   if (t1 <= t0) return -INFINITY;
 
@@ -211,21 +235,25 @@ static int run_item(const problem* P, int item) {
       return PKD_ORACLE_NO_MEM;
     }
   }
-  for (int h = g * G; h < (g + 1) * G; ++h) {
-    double* o = P->out + ((int64_t)b * P->hq + h) * D;
-    double* l = P->lse + (int64_t)b * P->hq + h;
-    if (S < 1) {
-      *l = attend_range(P, b, h, 0, L, o, s);
-    } else {
-      /* split j covers [j*c, min((j+1)*c, L)) with c = ceil(L / S) */
-      int c = (L + S - 1) / S;
-      for (int j = 0; j < S; ++j) {
-        int t0 = j * c, t1 = (j + 1) * c;
-        if (t0 > L) t0 = L;
-        if (t1 > L) t1 = L;
-        lp[j] = attend_range(P, b, h, t0, t1, op + (int64_t)j * D, s);
+  for (int qi = 0; qi < P->q_len; ++qi) {
+    const int V = visible_tokens(P, b, qi);
+    for (int h = g * G; h < (g + 1) * G; ++h) {
+      const int64_t row = ((int64_t)b * P->q_len + qi) * P->hq + h;
+      double* o = P->out + row * D;
+      double* l = P->lse + row;
+      if (S < 1) {
+        *l = attend_range(P, b, qi, h, 0, V, o, s);
+      } else {
+        /* split j covers [j*c, min((j+1)*c, V)) with c = ceil(V / S) */
+        int c = (V + S - 1) / S;
+        for (int j = 0; j < S; ++j) {
+          int t0 = j * c, t1 = (j + 1) * c;
+          if (t0 > V) t0 = V;
+          if (t1 > V) t1 = V;
+          lp[j] = attend_range(P, b, qi, h, t0, t1, op + (int64_t)j * D, s);
+        }
+        *l = merge_row(S, D, op, lp, o);
       }
-      *l = merge_row(S, D, op, lp, o);
     }
   }
   free(s); free(op); free(lp);
@@ -252,7 +280,8 @@ static void* worker(void* arg) {
 
 static int run(problem* P, int nthreads) {
   if (P->batch < 0 || P->hq < 1 || P->hkv < 1 || P->hq % P->hkv != 0 || P->head_dim < 1 ||
-      P->page_size < 1 || P->max_pages < 0 || P->num_pages < 0 || !P->out || !P->lse)
+      P->page_size < 1 || P->max_pages < 0 || P->num_pages < 0 || !P->out || !P->lse ||
+      P->q_len < 1 || (P->causal != 0 && P->causal != 1))
     return PKD_ORACLE_BAD_ARG;
   if (P->kv_fp8 && (!P->k_scale || !P->v_scale)) return PKD_ORACLE_BAD_ARG;
   for (int b = 0; b < P->batch; ++b) {
@@ -292,7 +321,7 @@ int pkd_oracle_paged_decode(int batch, int hq, int hkv, int head_dim, int page_s
                             double scale, double* out, double* lse, int nthreads) {
   problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
                q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
-               0, out, lse};
+               0, out, lse, 1, 0};
   return run(&P, nthreads);
 }
 
@@ -306,8 +335,33 @@ int pkd_oracle_paged_decode_split(int batch, int hq, int hkv, int head_dim, int 
   if (num_splits < 1) return PKD_ORACLE_BAD_ARG;
   problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
                q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
-               num_splits, out, lse};
+               num_splits, out, lse, 1, 0};
   return run(&P, nthreads);
+}
+
+/* The plain definition for a list of rows only (see the _rows entries). */
+static int rows_only(problem* P, int n_rows, const int64_t* rows, double* out, double* lse) {
+  if (P->batch < 0 || P->hq < 1 || P->hkv < 1 || P->hq % P->hkv != 0 || P->head_dim < 1 ||
+      P->page_size < 1 || P->q_len < 1 || (P->causal != 0 && P->causal != 1) || n_rows < 0 ||
+      !rows || !out || !lse)
+    return PKD_ORACLE_BAD_ARG;
+  if (P->kv_fp8 && (!P->k_scale || !P->v_scale)) return PKD_ORACLE_BAD_ARG;
+  const int64_t per_seq = (int64_t)P->q_len * P->hq;
+  for (int i = 0; i < n_rows; ++i) {
+    int64_t r = rows[i];
+    if (r < 0 || r >= (int64_t)P->batch * per_seq) return PKD_ORACLE_BAD_ARG;
+    int b = (int)(r / per_seq);
+    int qi = (int)((r % per_seq) / P->hq);
+    int h = (int)(r % P->hq);
+    int st = check_sequence(P, b);
+    if (st != PKD_ORACLE_OK) return st;
+    int V = visible_tokens(P, b, qi);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+    if (!s) return PKD_ORACLE_NO_MEM;
+    lse[i] = attend_range(P, b, qi, h, 0, V, out + (int64_t)i * P->head_dim, s);
+    free(s);
+  }
+  return PKD_ORACLE_OK;
 }
 
 /* Plain definition for a chosen list of (sequence, query head) rows only:
@@ -322,24 +376,38 @@ int pkd_oracle_paged_decode_rows(int batch, int hq, int hkv, int head_dim, int p
                                  int n_rows, const int64_t* rows, double* out, double* lse) {
   problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
                q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
-               0, out, lse};
-  if (batch < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || head_dim < 1 || page_size < 1 ||
-      n_rows < 0 || !rows || !out || !lse)
-    return PKD_ORACLE_BAD_ARG;
-  if (kv_fp8 && (!k_scale || !v_scale)) return PKD_ORACLE_BAD_ARG;
-  for (int i = 0; i < n_rows; ++i) {
-    int64_t r = rows[i];
-    if (r < 0 || r >= (int64_t)batch * hq) return PKD_ORACLE_BAD_ARG;
-    int b = (int)(r / hq), h = (int)(r % hq);
-    int st = check_sequence(&P, b);
-    if (st != PKD_ORACLE_OK) return st;
-    int L = seq_lens[b];
-    double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
-    if (!s) return PKD_ORACLE_NO_MEM;
-    lse[i] = attend_range(&P, b, h, 0, L, out + (int64_t)i * head_dim, s);
-    free(s);
-  }
-  return PKD_ORACLE_OK;
+               0, out, lse, 1, 0};
+  return rows_only(&P, n_rows, rows, out, lse);
+}
+
+/* Several query tokens per sequence (see the top of this file).  q: bf16 bits
+ * [B][q_len][Hq][D]; out [B][q_len][Hq][D] and lse [B][q_len][Hq], fp64;
+ * causal is 0 or 1; the other arguments as for pkd_oracle_paged_decode. */
+int pkd_oracle_paged_decode_multi(int batch, int hq, int hkv, int head_dim, int page_size,
+                                  int num_pages, int max_pages, int kv_fp8, int q_len, int causal,
+                                  const uint16_t* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  const float* k_scale, const float* v_scale, double scale,
+                                  double* out, double* lse, int nthreads) {
+  problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
+               q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+               0, out, lse, q_len, causal};
+  return run(&P, nthreads);
+}
+
+/* pkd_oracle_paged_decode_multi for a list of rows only: rows[i] =
+ * (b * q_len + i) * Hq + h; out [n_rows][D], lse [n_rows]; single thread. */
+int pkd_oracle_paged_decode_multi_rows(int batch, int hq, int hkv, int head_dim, int page_size,
+                                       int num_pages, int max_pages, int kv_fp8, int q_len,
+                                       int causal, const uint16_t* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_table,
+                                       const int32_t* seq_lens, const float* k_scale,
+                                       const float* v_scale, double scale, int n_rows,
+                                       const int64_t* rows, double* out, double* lse) {
+  problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
+               q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+               0, out, lse, q_len, causal};
+  return rows_only(&P, n_rows, rows, out, lse);
 }
 
 /* Plain definition restricted to one token range per sequence: row
@@ -355,7 +423,7 @@ int pkd_oracle_paged_decode_ranges(int batch, int hq, int hkv, int head_dim, int
                                    double* lse) {
   problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
                q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
-               0, out, lse};
+               0, out, lse, 1, 0};
   if (batch < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || head_dim < 1 || page_size < 1 ||
       !t_begin || !t_end || !out || !lse)
     return PKD_ORACLE_BAD_ARG;
@@ -369,7 +437,7 @@ int pkd_oracle_paged_decode_ranges(int batch, int hq, int hkv, int head_dim, int
     if (!s) return PKD_ORACLE_NO_MEM;
     for (int h = 0; h < hq; ++h)
       lse[(int64_t)b * hq + h] =
-          attend_range(&P, b, h, t0, t1, out + ((int64_t)b * hq + h) * head_dim, s);
+          attend_range(&P, b, 0, h, t0, t1, out + ((int64_t)b * hq + h) * head_dim, s);
     free(s);
   }
   return PKD_ORACLE_OK;

@@ -46,6 +46,8 @@ class WorkloadSpec:
     seq_lens: Optional[tuple] = None   # fixed lengths, or
     len_range: Optional[tuple] = None  # inclusive uniform integer range (lo, hi)
     max_len: int = 0                   # longest length the block table must allow
+    q_len: int = 1                     # query tokens per sequence (the last q_len positions)
+    causal: bool = False               # query token i sees positions <= L - q_len + i only
 
     @property
     def max_pages_per_seq(self) -> int:
@@ -56,15 +58,17 @@ class WorkloadSpec:
         return 1.0 / math.sqrt(self.head_dim)
 
 
-def _spec(name, B, hq, hkv, d, ps, dtype, seed, seq_lens=None, len_range=None):
+def _spec(name, B, hq, hkv, d, ps, dtype, seed, seq_lens=None, len_range=None, q_len=1, causal=False):
     max_len = max(seq_lens) if seq_lens is not None else len_range[1]
     return WorkloadSpec(name, B, hq, hkv, d, ps, dtype, seed,
                         tuple(seq_lens) if seq_lens is not None else None,
-                        tuple(len_range) if len_range is not None else None, max_len)
+                        tuple(len_range) if len_range is not None else None, max_len, q_len, causal)
 
 
 # The decode shapes the method is exercised on: a tiny case, a Llama-style
-# B=32 step, a B=128 step, long-context head-dim sweeps and an FP8 cache.
+# B=32 step, a B=128 step, long-context head-dim sweeps and an FP8 cache; and
+# the B=32 shape verifying 4 speculative tokens per sequence under the causal
+# mask (several query tokens per sequence).
 WORKLOADS = {w.name: w for w in [
     _spec("tiny_b2_d64_ps16", 2, 4, 1, 64, 16, "bf16", 1, seq_lens=(37, 100)),
     _spec("llama_b32_d128_ps64", 32, 32, 8, 128, 64, "bf16", 2, len_range=(1024, 4096)),
@@ -76,6 +80,8 @@ WORKLOADS = {w.name: w for w in [
     _spec("longctx_b16_d64", 16, 16, 2, 64, 64, "bf16", 45, len_range=(8192, 32768)),
     _spec("longctx_b16_d256", 16, 16, 2, 256, 64, "bf16", 46, len_range=(8192, 32768)),
     _spec("fp8kv_b64_d128_ps64", 64, 64, 8, 128, 64, "fp8_e4m3", 5, len_range=(512, 8192)),
+    _spec("verify_b32_q4_d128_ps64", 32, 32, 8, 128, 64, "bf16", 6, len_range=(1024, 4096),
+          q_len=4, causal=True),
 ]}
 
 
@@ -86,7 +92,7 @@ class Workload:
     seq_lens: torch.Tensor       # [B] int32
     block_table: torch.Tensor    # [B, max_pages] int32, -1 past the used pages
     num_pages: int
-    q: torch.Tensor              # [B, Hq, D] bfloat16
+    q: torch.Tensor              # [B, Hq, D] bfloat16, or [B, q_len, Hq, D] when q_len > 1
     k_cache: torch.Tensor        # [num_pages, ps, Hkv, D] bfloat16 or float8_e4m3fn
     v_cache: torch.Tensor
     k_scale: Optional[torch.Tensor]  # [Hkv] float32 (fp8 only)
@@ -201,7 +207,8 @@ def make_workload(spec: WorkloadSpec, tail: str = "nan",
     max_pages = max(spec.max_pages_per_seq, max((-(-int(L) // ps) for L in lens), default=0), 1)
     num_pages = sum(-(-int(L) // ps) for L in lens)
     perm = torch.randperm(num_pages, generator=g)
-    q = torch.randn(B, hq, d, generator=g).to(torch.bfloat16)
+    qshape = (B, hq, d) if spec.q_len == 1 else (B, spec.q_len, hq, d)
+    q = torch.randn(*qshape, generator=g).to(torch.bfloat16)
     total = int(lens.to(torch.int64).sum())
     k32 = torch.randn(total, hkv, d, generator=g)
     v32 = torch.randn(total, hkv, d, generator=g)
@@ -223,14 +230,15 @@ def make_workload(spec: WorkloadSpec, tail: str = "nan",
 
 def custom_workload(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                     seq_lens: Sequence[int], kv_dtype: str = "bf16", seed: int = 0,
-                    tail: str = "nan", max_pages: Optional[int] = None, name: str = "custom") -> Workload:
+                    tail: str = "nan", max_pages: Optional[int] = None, name: str = "custom",
+                    q_len: int = 1, causal: bool = False) -> Workload:
     """A one-off workload with explicit lengths (edge cases, small parity cases)."""
     lens = [int(x) for x in seq_lens]
     max_len = max(lens + [1])
     if max_pages is not None:
         max_len = max(max_len, max_pages * page_size)
     spec = WorkloadSpec(name, batch, num_q_heads, num_kv_heads, head_dim, page_size, kv_dtype, seed,
-                        tuple(lens), None, max_len)
+                        tuple(lens), None, max_len, q_len, causal)
     return make_workload(spec, tail=tail)
 
 

@@ -4,8 +4,9 @@ Each mutant below is a copy of paged_attention_ref.c with one planted slip of
 the kind a hand-written attention reference can plausibly contain: a wrong
 page or slot index, the wrong KV head for a query head, K and V swapped, the
 softmax scale dropped, a base-2 log-sum-exp, a wrong merge weight, a wrong
-split boundary, a wrong FP8 exponent bias, a wrong cache layout.  The copy is
-compiled with the oracle's own build command and the pin suite
+split boundary, a wrong FP8 exponent bias, a wrong cache layout, a causal
+mask off by one or aligned to the wrong end.  The copy is compiled with the
+oracle's own build command and the pin suite
 (test_oracle_pins.py) is run against it in a child process through
 PKD_ORACLE_LIB; every mutant must make at least one pin fail.  A control copy
 with no change must pass, which shows that the child really loads the copy.
@@ -41,7 +42,20 @@ MUTANTS = [
     ("gqa_interleaved_head_map",
      "const int g = h / G;", "const int g = h % P->hkv;"),
     ("query_rows_transposed",
-     "P->q + ((int64_t)b * P->hq + h) * D;", "P->q + ((int64_t)h * P->batch + b) * D;"),
+     "P->q + (((int64_t)b * P->q_len + qi) * P->hq + h) * D;",
+     "P->q + (((int64_t)h * P->q_len + qi) * P->batch + b) * D;"),
+    ("query_token_major_over_batch",
+     "P->q + (((int64_t)b * P->q_len + qi) * P->hq + h) * D;",
+     "P->q + (((int64_t)qi * P->batch + b) * P->hq + h) * D;"),
+    ("output_rows_head_major",
+     "const int64_t row = ((int64_t)b * P->q_len + qi) * P->hq + h;",
+     "const int64_t row = ((int64_t)b * P->hq + h) * P->q_len + qi;"),
+    ("causal_limit_off_by_one",
+     "const int v = L - P->q_len + qi + 1;", "const int v = L - P->q_len + qi;"),
+    ("causal_mask_top_left_aligned",
+     "const int v = L - P->q_len + qi + 1;", "const int v = qi + 1;"),
+    ("causal_flag_ignored",
+     "if (!P->causal) return L;", "if (P->causal < 2) return L;"),
     ("scale_dropped",
      "s[t - t0] = P->scale * acc;", "s[t - t0] = acc;"),
     ("values_read_from_keys",
@@ -61,7 +75,7 @@ MUTANTS = [
     ("merge_lse_missing_max",
      "double lse = M + log(z);", "double lse = log(z);"),
     ("split_chunk_rounds_down",
-     "int c = (L + S - 1) / S;", "int c = L / S > 0 ? L / S : 1;"),
+     "int c = (V + S - 1) / S;", "int c = V / S > 0 ? V / S : 1;"),
     ("fp8_subnormal_exponent",
      "mag = ldexp((double)m / 8.0, 1 - 7);", "mag = ldexp((double)m / 8.0, -7);"),
     ("fp8_exponent_bias_eight",

@@ -297,3 +297,114 @@ def test_ranges_entry_pieces_recombine_to_full():
     mo, ml = oracle.lse_merge(parts_o, parts_l)
     assert _close(mo.reshape(full_o.shape), full_o, 1e-12)
     assert _close(ml.reshape(full_l.shape), full_l, 1e-12)
+
+
+# ---- several query tokens per sequence (speculative verify / extend) -------
+
+def brute_force_multi(w):
+    """Dense attention for q [B, q_len, Hq, D] over the logical rows, with the causal
+    mask written as an explicit position comparison (query token i of a length-L
+    sequence sits at position L - q_len + i); scipy's softmax and logsumexp."""
+    B, QL, hq, d = w.q.shape
+    hkv = w.spec.num_kv_heads
+    G = hq // hkv
+    q = _f64(w.q)
+    K = _f64(w.k_logical)
+    V = _f64(w.v_logical)
+    if w.k_scale is not None:
+        K = K * w.k_scale.double().numpy()[None, :, None]
+        V = V * w.v_scale.double().numpy()[None, :, None]
+    out = np.zeros((B, QL, hq, d))
+    lse = np.full((B, QL, hq), -np.inf)
+    for b in range(B):
+        t0, t1 = int(w.token_offsets[b]), int(w.token_offsets[b + 1])
+        L = t1 - t0
+        pos = np.arange(L)
+        for i in range(QL):
+            visible = pos <= L - QL + i if w.spec.causal else np.ones(L, bool)
+            if not visible.any():
+                continue
+            for h in range(hq):
+                g = h // G
+                s = w.scale * (K[t0:t1, g, :] @ q[b, i, h])
+                s = s[visible]
+                out[b, i, h] = scipy.special.softmax(s) @ V[t0:t1, g, :][visible]
+                lse[b, i, h] = scipy.special.logsumexp(s)
+    return out, lse
+
+
+MULTI_CASES = [
+    # (B, Hq, Hkv, D, ps, seq_lens, q_len, causal, dtype, seed)
+    (2, 4, 2, 16, 3, [7, 20], 3, True, "bf16", 201),
+    (3, 8, 2, 16, 16, [5, 33, 2], 4, True, "bf16", 202),   # L = 2 < q_len: two rows see nothing
+    (2, 4, 1, 32, 4, [9, 17], 2, False, "bf16", 203),
+    (2, 4, 2, 16, 16, [12, 40], 5, True, "fp8_e4m3", 204),
+    (1, 2, 2, 8, 1, [6], 6, True, "bf16", 205),             # L = q_len: token 0 sees one row
+]
+
+
+@pytest.mark.parametrize("case", MULTI_CASES)
+def test_multi_matches_dense_brute_force_with_explicit_mask(case):
+    B, hq, hkv, d, ps, lens, ql, causal, dtype, seed = case
+    w = wl.custom_workload(B, hq, hkv, d, ps, lens, dtype, seed, q_len=ql, causal=causal)
+    out, lse = oracle.run_workload(w)
+    ref_o, ref_l = brute_force_multi(w)
+    assert _close(out, ref_o, 1e-12) and _close(lse, ref_l, 1e-12)
+
+
+def test_multi_with_one_query_token_is_single_token_decode_bitwise():
+    w1 = wl.custom_workload(3, 8, 2, 32, 16, [40, 3, 77], "bf16", 211)
+    out1, lse1 = oracle.run_workload(w1)
+    for causal in (False, True):
+        q4 = w1.q.unsqueeze(1).contiguous()  # [B, 1, Hq, D]
+        o, l = oracle.paged_decode_multi(q4, w1.k_cache, w1.v_cache, w1.block_table, w1.seq_lens,
+                                         w1.scale, causal)
+        assert np.array_equal(o[:, 0], out1) and np.array_equal(l[:, 0], lse1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_multi_token_i_is_single_token_decode_over_its_visible_prefix(causal):
+    """Query token i (causal) is the single-token definition over the first
+    L - q_len + i + 1 tokens of the same pages; without the mask, over all L."""
+    ql = 3
+    w = wl.custom_workload(3, 8, 4, 16, 5, [14, 30, 9], "bf16", 212, q_len=ql, causal=causal)
+    out, lse = oracle.run_workload(w)
+    L = w.seq_lens.to(torch.int64)
+    for i in range(ql):
+        vis = torch.clamp(L - ql + i + 1, min=0) if causal else L
+        o, l = oracle.paged_decode(w.q[:, i].contiguous(), w.k_cache, w.v_cache, w.block_table,
+                                   vis.to(torch.int32), w.scale)
+        assert np.array_equal(out[:, i], o) and np.array_equal(lse[:, i], l)
+
+
+def test_multi_first_token_of_a_just_filled_sequence_sees_only_token_zero():
+    """Causal, L = q_len: query token 0 sees token 0 alone, so out = V_0 exactly
+    and lse = s_0 (closed form)."""
+    w = wl.custom_workload(1, 4, 2, 16, 4, [5], "bf16", 213, q_len=5, causal=True)
+    out, lse = oracle.run_workload(w)
+    q = _f64(w.q)
+    K = _f64(w.k_logical)
+    V = _f64(w.v_logical)
+    for h in range(4):
+        g = h // 2
+        assert np.array_equal(out[0, 0, h], V[0, g])
+        assert abs(lse[0, 0, h] - w.scale * float(K[0, g] @ q[0, 0, h])) <= 1e-15
+
+
+def test_multi_rows_without_visible_tokens_are_zero_and_minus_inf():
+    w = wl.custom_workload(2, 4, 1, 16, 4, [2, 0], "bf16", 214, q_len=4, causal=True)
+    out, lse = oracle.run_workload(w)
+    # sequence 0 (L = 2): tokens 0 and 1 see nothing, tokens 2 and 3 see 1 and 2 rows
+    assert np.all(out[0, :2] == 0) and np.all(np.isneginf(lse[0, :2]))
+    assert np.all(np.isfinite(lse[0, 2:]))
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+def test_multi_rows_entry_matches_full_oracle():
+    w = wl.custom_workload(3, 8, 2, 32, 16, [40, 3, 77], "fp8_e4m3", 215, q_len=3, causal=True)
+    out, lse = oracle.run_workload(w)
+    rows = [0, 5, 9, 23, 17, 40, 71]
+    o_r, l_r = oracle.paged_decode_multi_rows(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens,
+                                              w.scale, True, rows, w.k_scale, w.v_scale)
+    flat_o, flat_l = out.reshape(-1, 32), lse.reshape(-1)
+    assert np.array_equal(o_r, flat_o[rows]) and np.array_equal(l_r, flat_l[rows])
