@@ -36,6 +36,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 METRIC = "decode-attention achieved HBM GB/s (% of peak) + queries/s at B=32 and B=128"
 PRIMARY = "llama_b32_d128_ps64"
 SECONDARY = "batch128_d128_ps128"
+VERIFY = "verify_b32_q4_d128_ps64"  # several query tokens per sequence, reported alongside
 
 
 def algorithmic_bytes(w, split_kernel_only=False):
@@ -44,9 +45,10 @@ def algorithmic_bytes(w, split_kernel_only=False):
     e = w.k_cache.element_size()
     lens = [int(x) for x in w.seq_lens]
     kv = sum(lens) * s.num_kv_heads * s.head_dim * 2 * e
-    q = s.batch * s.num_q_heads * s.head_dim * 2
-    out = s.batch * s.num_q_heads * s.head_dim * 2
-    lse = s.batch * s.num_q_heads * 4
+    rows = s.batch * s.q_len * s.num_q_heads  # (sequence, query token, head) rows
+    q = rows * s.head_dim * 2
+    out = rows * s.head_dim * 2
+    lse = rows * 4
     bt = sum(-(-L // s.page_size) for L in lens) * 4
     seq = s.batch * 4
     scales = 2 * s.num_kv_heads * 4 if w.k_scale is not None else 0
@@ -71,13 +73,11 @@ class Runner:
         self.lens = w.seq_lens.to(device)
         self.ks = None if w.k_scale is None else w.k_scale.to(device)
         self.vs = None if w.v_scale is None else w.v_scale.to(device)
-        self.dims = B.dims_for(self.q, self.k, self.bt)
+        self.dims = B.dims_for(self.q, self.k, self.bt, causal=w.spec.causal)
         self.S = num_splits if num_splits != 0 else B.paged_decode_num_splits(self.dims, 0)
         self.launches = B.paged_decode_launches(self.dims, self.S)  # 1: the partition writes out itself
-        s = w.spec
-        self.rows = s.batch * s.num_q_heads
         self.out = torch.empty(self.q.shape, dtype=torch.bfloat16, device=device)
-        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device=device)
+        self.lse = torch.empty(self.q.shape[:-1], dtype=torch.float32, device=device)
         self.ws_bytes = B.paged_decode_workspace_bytes(self.dims, self.S)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
         self.stream = torch.cuda.current_stream(device)
@@ -161,11 +161,13 @@ def bench_one(name, steps, warmup, num_splits, device, scrub):
     res = dict(
         workload=name, batch=w.spec.batch, num_q_heads=w.spec.num_q_heads,
         num_kv_heads=w.spec.num_kv_heads, head_dim=w.spec.head_dim, page_size=w.spec.page_size,
-        kv_dtype=w.spec.kv_dtype, num_splits=r.S, launches=r.launches, tokens=int(w.seq_lens.sum()),
+        kv_dtype=w.spec.kv_dtype, q_len=w.spec.q_len, causal=w.spec.causal,
+        num_splits=r.S, launches=r.launches, tokens=int(w.seq_lens.sum()),
         algorithmic_bytes=nbytes, ms_per_step=step_mean,
         ms_p10=srt[int(0.1 * (steps - 1))], ms_median=srt[(steps - 1) // 2], ms_p90=srt[int(0.9 * (steps - 1))],
         gbs=nbytes / (step_mean * 1e-3) / 1e9,
         queries_per_s=w.spec.batch / (step_mean * 1e-3),
+        query_tokens_per_s=w.spec.batch * w.spec.q_len / (step_mean * 1e-3),
         split_kernel_ms=k1_mean, split_kernel_bytes=k1_bytes,
         split_kernel_gbs=k1_bytes / (k1_mean * 1e-3) / 1e9,
         merge_share=0.0 if r.launches == 1 else (sum(split_ms) / steps - k1_mean) / (sum(split_ms) / steps),
@@ -308,7 +310,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workloads", default=f"{PRIMARY},{SECONDARY}",
+    ap.add_argument("--workloads", default=f"{PRIMARY},{SECONDARY},{VERIFY}",
                     help="comma-separated workload names, or 'all'")
     ap.add_argument("--num-splits", type=int, default=0, help="0: the library's heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -356,7 +358,7 @@ def main():
         print(f"# {name}: S={res['num_splits']} {res['ms_per_step'] * 1e3:.1f} us/step "
               f"(p10 {res['ms_p10'] * 1e3:.1f}, p90 {res['ms_p90'] * 1e3:.1f}) "
               f"{res['gbs']:.0f} GB/s = {res['pct_of_peak']:.1f}% of peak, "
-              f"{res['queries_per_s']:.0f} queries/s; partition kernel {res['split_kernel_gbs']:.0f} GB/s; "
+              f"{res['query_tokens_per_s']:.0f} query tokens/s; partition kernel {res['split_kernel_gbs']:.0f} GB/s; "
               f"merge share {100 * res['merge_share']:.1f}%; warm {res['warm_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
     if args.profile_only:
@@ -399,6 +401,11 @@ def main():
         line["b128"] = {"gbs": round(s["gbs"], 2), "pct_of_peak": round(s["pct_of_peak"], 2),
                         "queries_per_s": round(s["queries_per_s"], 1), "ms_per_step": s["ms_per_step"],
                         "num_splits": s["num_splits"]}
+    if VERIFY in results:
+        v = results[VERIFY]
+        line["verify"] = {"gbs": round(v["gbs"], 2), "pct_of_peak": round(v["pct_of_peak"], 2),
+                          "query_tokens_per_s": round(v["query_tokens_per_s"], 1), "ms_per_step": v["ms_per_step"],
+                          "q_len": v["q_len"], "causal": v["causal"], "num_splits": v["num_splits"]}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(primary_w, p["algorithmic_bytes"])
     print(json.dumps(line), flush=True)

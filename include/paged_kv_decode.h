@@ -19,6 +19,19 @@
  * row (BF16 and FP8-E4M3 KV caches, GQA, "split-KV or direct output", a
  * persistent merge kernel).
  *
+ * Several query tokens per sequence (dims.q_len > 1): the speculative-verify /
+ * extend form that the same b12x row lists beside decode ("decode/verify",
+ * "extend"), with the causal mask the AstrAI log expresses as the position of
+ * the first query token.  Sequence b then has q_len query tokens, the last
+ * q_len positions of the sequence: query token i sits at position
+ * seq_lens[b] - q_len + i.  Without the mask (dims.causal = 0) every query
+ * token attends over all seq_lens[b] tokens; with it (dims.causal = 1) query
+ * token i attends over positions <= seq_lens[b] - q_len + i only, and a token
+ * that sees no position gets out = 0 and lse = -inf.  q, out and lse gain a
+ * q_len dimension after the batch: row (b, i, h) of each is at
+ * (b * q_len + i) * Hq + h.  All the q_len * G rows that share a KV head are
+ * computed from one read of its K/V rows.
+ *
  * Split-KV: each sequence's tokens are cut into num_splits ranges; each range
  * produces a normalised partial output and its log-sum-exp, and a merge
  * combines them (out = sum_j exp(lse_j - lse) * o_j, lse = ln sum_j exp(lse_j)),
@@ -44,6 +57,11 @@
  *    paged_decode_check_tables reports them.
  *  - Outputs must not alias inputs.  Results are bitwise deterministic for
  *    fixed inputs and num_splits.
+ *  - Alignment: q, k_cache, v_cache, out, workspace and o_part must be 16-byte
+ *    aligned; every other pointer must be aligned to its element size (4 bytes
+ *    for int32 and fp32 arrays, 2 for the merge entry's bf16 out).  Memory from
+ *    hipMalloc or a torch allocation always is.  Misaligned pointers are
+ *    rejected with PKD_ERR_ALIGNMENT.
  */
 #ifndef PAGED_KV_DECODE_H
 #define PAGED_KV_DECODE_H
@@ -67,9 +85,15 @@ extern "C" {
 #define PKD_ERR_WORKSPACE (-8)       /* workspace NULL or smaller than required */
 #define PKD_ERR_LAUNCH (-9)          /* the HIP runtime refused a launch */
 #define PKD_ERR_DEVICE (-10)         /* no usable gfx950 device is current */
+#define PKD_ERR_ALIGNMENT (-11)      /* a pointer is not aligned as required (see below) */
 
 /* Largest num_splits accepted. */
 #define PKD_MAX_SPLITS 512
+
+/* Largest q_len accepted.  The q_len * G query rows of a KV head are computed
+ * 16 at a time, each group of 16 reading the KV head's K/V rows once, so the
+ * cost grows with q_len * G / 16: a verify / short-extend form, not prefill. */
+#define PKD_MAX_Q_LEN 64
 
 /* Special num_splits values.  PKD_SPLITS_AUTO lets the library choose
  * (paged_decode_num_splits).  PKD_SPLITS_BALANCED selects the balanced
@@ -104,13 +128,15 @@ typedef struct {
   int32_t num_pages;          /* pages in the pool, >= 1 */
   int32_t max_pages_per_seq;  /* row length of block_table, >= 1 */
   int32_t kv_dtype;           /* a pkd_dtype */
+  int32_t q_len;              /* query tokens per sequence, 1..PKD_MAX_Q_LEN (1 = decode) */
+  int32_t causal;             /* 0: every query token sees all tokens; 1: causal mask (above) */
 } pkd_dims;
 
 /*
  * paged_decode -- the whole decode-attention step (split-KV partition + merge).
  *
  *   dims         host; see pkd_dims.
- *   q            [B][Hq][D] bfloat16, contiguous.
+ *   q            [B][q_len][Hq][D] bfloat16, contiguous ([B][Hq][D] when q_len = 1).
  *   k_cache      [num_pages][page_size][Hkv][D] of kv_dtype, contiguous.
  *   v_cache      same layout as k_cache.
  *   block_table  [B][max_pages_per_seq] int32 physical page ids.
@@ -119,8 +145,8 @@ typedef struct {
  *                must be NULL for BF16.
  *   v_scale      [Hkv] fp32, as k_scale for V.
  *   scale        softmax scale applied to q.k (typically 1/sqrt(D)); included in lse.
- *   out          [B][Hq][D] bfloat16 result (fp32 accumulate, round-to-nearest-even).
- *   lse          [B][Hq] fp32 natural-log log-sum-exp of the scaled scores, or NULL.
+ *   out          [B][q_len][Hq][D] bfloat16 result (fp32 accumulate, round-to-nearest-even).
+ *   lse          [B][q_len][Hq] fp32 natural-log log-sum-exp of the scaled scores, or NULL.
  *   num_splits   PKD_SPLITS_AUTO: chosen by paged_decode_num_splits(dims, 0);
  *                1: direct output (one kernel); 2..PKD_MAX_SPLITS: split-KV + merge (two kernels);
  *                PKD_SPLITS_BALANCED: balanced partition, which merges the pieces of each
@@ -163,7 +189,7 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
  * (sequence, KV-head) work items alone fill the current device's compute units,
  * else a split count in [2, PKD_MAX_SPLITS] bounded by the longest sequence
  * expected, max_seq_len_hint (<= 0: max_pages_per_seq * page_size).  Host only;
- * returns that value, or a status in [-10, -1] for invalid dims.
+ * returns that value, or a status in [-11, -1] for invalid dims.
  */
 int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint);
 
@@ -172,18 +198,20 @@ int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint);
  * (PKD_SPLITS_AUTO: the heuristic's choice): 1 for direct output and for the
  * balanced mode when its partition kernel merges in place (when the
  * (sequence, KV head, head group) segments are at least as many as the
- * current device's compute units), else 2.
- * Host only; returns a status in [-10, -1] for invalid dims or num_splits.
+ * current device's compute units; a head group is 16 of the q_len * G query
+ * rows of a KV head), else 2.
+ * Host only; returns a status in [-11, -1] for invalid dims or num_splits.
  */
 int32_t paged_decode_launches(const pkd_dims* dims, int32_t num_splits);
 
 /*
  * paged_decode_workspace_bytes -- workspace paged_decode needs for num_splits
  * (PKD_SPLITS_AUTO: the heuristic's choice): 0 for one split; for S splits the
- * fp32 partials [B][Hq][S][D] and [B][Hq][S]; for PKD_SPLITS_BALANCED the fp32
- * partials of (W + B*Hkv*ceil(G/16)) slots of min(G,16) heads, W the
+ * fp32 partials [B][q_len][Hq][S][D] and [B][q_len][Hq][S]; for
+ * PKD_SPLITS_BALANCED, with R = q_len * G query rows per KV head, the fp32
+ * partials of (W + B*Hkv*ceil(R/16)) slots of min(R,16) rows, W the
  * workgroups of the device-sized grid (one per compute unit), B+1 int64 prefix
- * sums and B*Hkv*ceil(G/16) uint64 merge counters; each part rounded up to 256
+ * sums and B*Hkv*ceil(R/16) uint64 merge counters; each part rounded up to 256
  * bytes.  Returns 0 for invalid dims or an unsupported num_splits.  The
  * counters carry a per-call tag, so the workspace never needs initialising.
  */
@@ -194,8 +222,8 @@ size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits);
  * every (sequence, query head) writes its normalised partial output and
  * natural-log LSE.  An empty split writes o = 0 and lse = -inf, so every slot
  * is written and no clearing is needed.
- *   o_part    [B][Hq][num_splits][D] fp32.
- *   lse_part  [B][Hq][num_splits] fp32.
+ *   o_part    [B][q_len][Hq][num_splits][D] fp32.
+ *   lse_part  [B][q_len][Hq][num_splits] fp32.
  *   num_splits 1..PKD_MAX_SPLITS (no heuristic here).
  * Other arguments as for paged_decode.
  */

@@ -30,7 +30,9 @@ PKD_ERR_NUM_SPLITS = -7
 PKD_ERR_WORKSPACE = -8
 PKD_ERR_LAUNCH = -9
 PKD_ERR_DEVICE = -10
+PKD_ERR_ALIGNMENT = -11
 PKD_MAX_SPLITS = 512
+PKD_MAX_Q_LEN = 64
 PKD_SPLIT_ALIGN = 64
 PKD_SPLITS_AUTO = 0
 PKD_SPLITS_BALANCED = -1000
@@ -53,7 +55,8 @@ class pkd_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("max_pages_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+                ("max_pages_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -191,10 +194,15 @@ def paged_decode_status_string(status: int) -> str:
 
 # ---- torch conveniences (memory and streams only) ---------------------------
 
-def dims_for(q, k_cache, block_table) -> pkd_dims:
-    """pkd_dims from torch tensors q [B,Hq,D], k_cache [P,ps,Hkv,D], block_table [B,MP]."""
+def dims_for(q, k_cache, block_table, causal: bool = False) -> pkd_dims:
+    """pkd_dims from torch tensors q [B,Hq,D] (or [B,q_len,Hq,D]), k_cache [P,ps,Hkv,D],
+    block_table [B,MP]."""
     import torch
-    B, hq, d = q.shape
+    if q.dim() == 4:
+        B, q_len, hq, d = q.shape
+    else:
+        B, hq, d = q.shape
+        q_len = 1
     num_pages, ps, hkv, d2 = k_cache.shape
     if d2 != d:
         raise ValueError("q and k_cache head_dim differ")
@@ -204,7 +212,7 @@ def dims_for(q, k_cache, block_table) -> pkd_dims:
         kvd = PKD_DTYPE_FP8_E4M3
     else:
         raise TypeError(f"unsupported KV-cache dtype {k_cache.dtype}")
-    return pkd_dims(B, hq, hkv, d, ps, num_pages, block_table.shape[1], kvd)
+    return pkd_dims(B, hq, hkv, d, ps, num_pages, block_table.shape[1], kvd, q_len, int(bool(causal)))
 
 
 def current_stream_handle(device) -> int:
@@ -213,8 +221,11 @@ def current_stream_handle(device) -> int:
 
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=None, v_scale=None,
-           num_splits: int = 0, out=None, lse=None, workspace=None, stream: Optional[int] = None):
-    """Run paged_decode on torch device tensors; returns (out bf16 [B,Hq,D], lse fp32 [B,Hq])."""
+           num_splits: int = 0, out=None, lse=None, workspace=None, stream: Optional[int] = None,
+           causal: bool = False):
+    """Run paged_decode on torch device tensors; returns (out bf16 shaped like q, lse fp32
+    [B,Hq] or [B,q_len,Hq]).  q is [B,Hq,D], or [B,q_len,Hq,D] for several query tokens
+    per sequence (with the causal mask when `causal`)."""
     import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("block_table", block_table), ("seq_lens", seq_lens)):
@@ -226,14 +237,14 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=Non
         raise TypeError("block_table and seq_lens must be int32")
     if v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache must match")
-    dims = dims_for(q, k_cache, block_table)
+    dims = dims_for(q, k_cache, block_table, causal)
     dev = q.device
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     if lse is None:
-        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
     S = num_splits if num_splits != PKD_SPLITS_AUTO else paged_decode_num_splits(dims, 0)
-    if -10 <= S < 0:
+    if -11 <= S < 0:
         raise PkdError(S)
     need = paged_decode_workspace_bytes(dims, S)
     if workspace is None and need > 0:

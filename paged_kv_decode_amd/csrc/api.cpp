@@ -32,16 +32,20 @@ int current_cu_count() {
 
 bool valid_head_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
+// Query rows per KV head: the q_len query tokens of each of its G heads.
+int rows_per_kv(const pkd_dims& d) { return d.q_len * (d.num_q_heads / d.num_kv_heads); }
+
+// Head groups: the rows of a KV head taken 16 at a time.
 int head_groups(const pkd_dims& d) {
-  const int G = d.num_q_heads / d.num_kv_heads;
-  return (G + pkd::kHeadsPerGroup - 1) / pkd::kHeadsPerGroup;
+  return (rows_per_kv(d) + pkd::kHeadsPerGroup - 1) / pkd::kHeadsPerGroup;
 }
 
 // Shape checks shared by every entry that takes dims.
 int32_t check_dims(const pkd_dims* d) {
   if (!d) return PKD_ERR_NULL_POINTER;
   if (d->batch < 0 || d->batch > 65535 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
-      d->page_size < 1 || d->num_pages < 1 || d->max_pages_per_seq < 1)
+      d->page_size < 1 || d->num_pages < 1 || d->max_pages_per_seq < 1 || d->q_len < 1 ||
+      d->q_len > PKD_MAX_Q_LEN || (d->causal != 0 && d->causal != 1))
     return PKD_ERR_BAD_DIMS;
   if (d->num_q_heads % d->num_kv_heads != 0) return PKD_ERR_GQA;
   if (!valid_head_dim(d->head_dim)) return PKD_ERR_HEAD_DIM;
@@ -65,8 +69,8 @@ int balanced_workers(const pkd_dims&) {
 }
 
 int heads_per_slot(const pkd_dims& d) {
-  const int G = d.num_q_heads / d.num_kv_heads;
-  return G < pkd::kHeadsPerGroup ? G : pkd::kHeadsPerGroup;
+  const int R = rows_per_kv(d);
+  return R < pkd::kHeadsPerGroup ? R : pkd::kHeadsPerGroup;
 }
 
 // Whether the balanced partition applies: aligned 16-token groups lie in one
@@ -117,7 +121,7 @@ uint64_t next_epoch() {
 }
 
 size_t partial_bytes(const pkd_dims& d, int S, size_t* lse_offset) {
-  const size_t rows = (size_t)d.batch * d.num_q_heads;
+  const size_t rows = (size_t)d.batch * d.q_len * d.num_q_heads;
   const size_t o = align256(rows * (size_t)S * d.head_dim * sizeof(float));
   if (lse_offset) *lse_offset = o;
   return o + align256(rows * (size_t)S * sizeof(float));
@@ -167,6 +171,9 @@ pkd::SplitParams make_split_params(const pkd_dims& d, const void* q, const void*
   p.hq = d.num_q_heads;
   p.hkv = d.num_kv_heads;
   p.group = d.num_q_heads / d.num_kv_heads;
+  p.q_len = d.q_len;
+  p.causal = d.causal;
+  p.rows_kv = rows_per_kv(d);
   p.head_groups = head_groups(d);
   p.page_size = d.page_size;
   p.max_pages = d.max_pages_per_seq;
@@ -174,6 +181,9 @@ pkd::SplitParams make_split_params(const pkd_dims& d, const void* q, const void*
   p.chunk = split_chunk(d, S);
   return p;
 }
+
+// Whether p is a multiple of `bytes` (NULL passes: NULL is checked separately).
+bool aligned(const void* p, uintptr_t bytes) { return ((uintptr_t)p & (bytes - 1)) == 0; }
 
 int32_t check_inputs(const pkd_dims* dims, const void* q, const void* k, const void* v,
                      const int32_t* bt, const int32_t* lens, const float* ks, const float* vs,
@@ -185,7 +195,15 @@ int32_t check_inputs(const pkd_dims* dims, const void* q, const void* k, const v
   if (fp8 && (!ks || !vs)) return PKD_ERR_SCALES;
   if (!fp8 && (ks || vs)) return PKD_ERR_SCALES;
   if (!std::isfinite(scale)) return PKD_ERR_BAD_DIMS;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(bt, 4) || !aligned(lens, 4) ||
+      !aligned(ks, 4) || !aligned(vs, 4))
+    return PKD_ERR_ALIGNMENT;
   return PKD_OK;
+}
+
+// Alignment of the output and workspace pointers of paged_decode and its phases.
+int32_t check_out_ws(const void* out, const float* lse, const void* ws) {
+  return aligned(out, 16) && aligned(lse, 4) && aligned(ws, 16) ? PKD_OK : PKD_ERR_ALIGNMENT;
 }
 
 int32_t launch_partition(const pkd_dims& d, const pkd::SplitParams& p, bool direct, hipStream_t s) {
@@ -226,6 +244,7 @@ int32_t paged_decode_partials(const pkd_dims* dims, const void* q, const void* k
   int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
   if (st != PKD_OK) return st;
   if (!o_part || !lse_part) return PKD_ERR_NULL_POINTER;
+  if (!aligned(o_part, 16) || !aligned(lse_part, 4)) return PKD_ERR_ALIGNMENT;
   if (num_splits < 1 || num_splits > PKD_MAX_SPLITS) return PKD_ERR_NUM_SPLITS;
   if (dims->batch == 0) return PKD_OK;
   pkd::SplitParams p = make_split_params(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale,
@@ -241,6 +260,8 @@ int32_t paged_decode_merge(int64_t rows, int32_t num_splits, int32_t head_dim, c
   if (!valid_head_dim(head_dim)) return PKD_ERR_HEAD_DIM;
   if (num_splits < 1 || num_splits > PKD_MAX_SPLITS) return PKD_ERR_NUM_SPLITS;
   if (!o_part || !lse_part || !out) return PKD_ERR_NULL_POINTER;
+  if (!aligned(o_part, 4) || !aligned(lse_part, 4) || !aligned(out, 2) || !aligned(lse, 4))
+    return PKD_ERR_ALIGNMENT;
   if (rows == 0) return PKD_OK;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
   pkd::MergeParams m{};
@@ -297,6 +318,9 @@ pkd::BalancedParams make_balanced_params(const pkd_dims& d, const void* q, const
   b.hq = d.num_q_heads;
   b.hkv = d.num_kv_heads;
   b.group = d.num_q_heads / d.num_kv_heads;
+  b.q_len = d.q_len;
+  b.causal = d.causal;
+  b.rows_kv = rows_per_kv(d);
   b.head_groups = head_groups(d);
   b.hpg = heads_per_slot(d);
   b.page_size = d.page_size;
@@ -327,7 +351,7 @@ int32_t run_finish(const pkd_dims& d, const void* ws, void* out, float* lse, con
   m.lse_part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + pl.lse_off);
   m.out = static_cast<uint16_t*>(out);
   m.lse = lse;
-  m.rows = (int64_t)d.batch * d.num_q_heads;
+  m.rows = (int64_t)d.batch * d.q_len * d.num_q_heads;
   if (pl.balanced) {
     m.balanced = 1;
     m.prefix = reinterpret_cast<const int64_t*>(static_cast<const uint8_t*>(ws) + pl.prefix_off);
@@ -338,6 +362,7 @@ int32_t run_finish(const pkd_dims& d, const void* ws, void* out, float* lse, con
     m.head_groups = head_groups(d);
     m.hpg = heads_per_slot(d);
     m.num_workers = balanced_workers(d);
+    m.q_len = d.q_len;
   } else {
     m.num_splits = pl.S;
   }
@@ -365,6 +390,8 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
   int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
   if (st != PKD_OK) return st;
   if (!out) return PKD_ERR_NULL_POINTER;
+  st = check_out_ws(out, lse, workspace);
+  if (st != PKD_OK) return st;
   Plan pl;
   st = make_plan(*dims, num_splits, &pl);
   if (st != PKD_OK) return st;
@@ -409,6 +436,7 @@ int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* 
   if (st != PKD_OK) return st;
   if (pl.S == 1) return PKD_ERR_NUM_SPLITS;
   if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return PKD_ERR_ALIGNMENT;
   if (dims->batch == 0) return PKD_OK;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
   return run_partition(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, workspace,
@@ -420,6 +448,8 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
   int32_t st = check_dims(dims);
   if (st != PKD_OK) return st;
   if (!out) return PKD_ERR_NULL_POINTER;
+  st = check_out_ws(out, lse, workspace);
+  if (st != PKD_OK) return st;
   Plan pl;
   st = make_plan(*dims, num_splits, &pl);
   if (st != PKD_OK) return st;
@@ -435,6 +465,7 @@ int32_t paged_decode_check_tables(const pkd_dims* dims, const int32_t* block_tab
   const int32_t st = check_dims(dims);
   if (st != PKD_OK) return st;
   if (!block_table || !seq_lens || !d_error_count) return PKD_ERR_NULL_POINTER;
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(d_error_count, 4)) return PKD_ERR_ALIGNMENT;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
   const hipError_t e = pkd::launch_check_tables(block_table, seq_lens, dims->batch,
                                                 dims->max_pages_per_seq, dims->page_size,
@@ -456,6 +487,7 @@ const char* paged_decode_status_string(int32_t status) {
     case PKD_ERR_WORKSPACE: return "workspace missing or too small";
     case PKD_ERR_LAUNCH: return "kernel launch failed";
     case PKD_ERR_DEVICE: return "no usable device is current";
+    case PKD_ERR_ALIGNMENT: return "a pointer is not aligned as required";
     default: return "unknown status";
   }
 }

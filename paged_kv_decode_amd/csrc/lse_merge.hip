@@ -1,6 +1,6 @@
 // Log-sum-exp merge of split-KV partials for gfx950.
 //
-// One wave per output row (sequence, query head).  With M = max_j lse_j,
+// One wave per output row (sequence, query token, query head).  With M = max_j lse_j,
 // w_j = exp(lse_j - M) and W = sum_j w_j, the merged row is
 // out = sum_j w_j o_j / W (bf16, round-to-nearest-even) and lse = M + ln W.
 // This is the recombination behind split-KV decoding (the AstrAI commit log's
@@ -48,12 +48,17 @@ __global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(co
     ls = 1;
     os = D;
   } else {
-    // Segment s = (b * Hkv + kvh) * HG + hg starts at group P_s of the work
-    // space; its pieces were written by workgroups w_first .. w_last at slots w + s.
-    const int b = (int)(row / p.hq);
-    const int h = (int)(row - (int64_t)b * p.hq);
+    // Row (b * q_len + i) * Hq + h is packed row r = i * G + h % G of KV head
+    // h / G.  Segment s = (b * Hkv + kvh) * HG + hg starts at group P_s of the
+    // work space; its pieces were written by workgroups w_first .. w_last at
+    // slots w + s.
+    const int64_t per_seq = (int64_t)p.q_len * p.hq;
+    const int b = (int)(row / per_seq);
+    const int rem = (int)(row - (int64_t)b * per_seq);
+    const int qi = rem / p.hq;
+    const int h = rem - qi * p.hq;
     const int kvh = h / p.group;
-    const int hin = h - kvh * p.group;
+    const int hin = qi * p.group + (h - kvh * p.group);
     const int hg = hin / kHeadsPerGroup;
     const int nh = hin - hg * kHeadsPerGroup;
     const int spb = p.hkv * p.head_groups;

@@ -28,6 +28,9 @@ __device__ __forceinline__ float merge_wave_max(float x) {
 // op[k * os + d].  Lanes run along the head dimension (EPL elements each).
 // After run(), M is the maximum LSE seen, W the (wave-reduced) sum of
 // exp(lse_k - M) and o the unnormalised row.
+// With few partials (mine <= UNROLL) the same result can be had in two steps,
+// issue() then finish(), so that a wave merging several rows has all of their
+// loads in flight before it combines any; both run the same code as run().
 // COHERENT: read the partials with agent-scope atomic loads, which see the
 // coherent copy even when another XCD's workgroup wrote them during this
 // kernel (ordinary loads may hit a stale line of this XCD's L2).
@@ -38,6 +41,12 @@ struct RowMerge {
   float M, W;
   float o[EPL];
 
+  // Loads of the few-partials path, held between issue() and finish().
+  struct Staged {
+    float l_own;            // this lane's partial LSE
+    float v[UNROLL][EPL];   // the partial rows
+  };
+
   static __device__ __forceinline__ float ld(const float* a) {
     if constexpr (COHERENT)
       return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -45,34 +54,54 @@ struct RowMerge {
       return *a;
   }
 
-  __device__ __forceinline__ void run(const float* lp, int64_t ls, const float* op, int64_t os, int mine,
-                                      int lane) {
+  __device__ __forceinline__ void begin() {
     M = -INFINITY;
     W = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  }
+
+  // Few partials: their LSEs and rows are loaded together, in one round trip ...
+  static __device__ __forceinline__ void load_few(const float* lp, int64_t ls, const float* op, int64_t os,
+                                                  int mine, int lane, float& l_own, float (&v)[UNROLL][EPL]) {
+    const bool live = lane * EPL < D;
+    l_own = lane < mine ? ld(lp + lane * ls) : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        v[u][e] = (live && u < mine) ? ld(op + (int64_t)u * os + lane * EPL + e) : 0.f;
+  }
+
+  // ... and combined once the maximum is known.
+  __device__ __forceinline__ void combine_few(float l_own, const float (&v)[UNROLL][EPL], int mine, int lane) {
+    M = merge_wave_max(l_own);
+    if (M != -INFINITY) {
+      const float wl = lane < mine ? __builtin_amdgcn_exp2f((l_own - M) * kMergeLog2e) : 0.f;
+      W = wl;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const float wgt = __shfl(wl, u);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] += wgt * v[u][e];
+      }
+    }
+  }
+
+  __device__ __forceinline__ void reduce_w() {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) W += __shfl_xor(W, m);
+  }
+
+  __device__ __forceinline__ void run(const float* lp, int64_t ls, const float* op, int64_t os, int mine,
+                                      int lane) {
+    begin();
     const bool live = lane * EPL < D;
     if (mine <= UNROLL) {
-      // Few partials (the common case): their LSEs and rows are loaded together,
-      // in one round trip, and combined once the maximum is known.
-      const float l_own = lane < mine ? ld(lp + lane * ls) : -INFINITY;
+      float l_own;
       float v[UNROLL][EPL];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          v[u][e] = (live && u < mine) ? ld(op + (int64_t)u * os + lane * EPL + e) : 0.f;
-      M = merge_wave_max(l_own);
-      if (M != -INFINITY) {
-        const float wl = lane < mine ? __builtin_amdgcn_exp2f((l_own - M) * kMergeLog2e) : 0.f;
-        W = wl;
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const float wgt = __shfl(wl, u);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) o[e] += wgt * v[u][e];
-        }
-      }
+      load_few(lp, ls, op, os, mine, lane, l_own, v);
+      combine_few(l_own, v, mine, lane);
     } else {
       for (int k = lane; k < mine; k += 64) M = fmaxf(M, ld(lp + k * ls));
       M = merge_wave_max(M);
@@ -107,8 +136,18 @@ struct RowMerge {
         }
       }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) W += __shfl_xor(W, m);
+    reduce_w();
+  }
+
+  // The two-step form of run() for mine <= UNROLL.
+  static __device__ __forceinline__ void issue(const float* lp, int64_t ls, const float* op, int64_t os, int mine,
+                                               int lane, Staged& st) {
+    load_few(lp, ls, op, os, mine, lane, st.l_own, st.v);
+  }
+  __device__ __forceinline__ void finish(const Staged& st, int mine, int lane) {
+    begin();
+    combine_few(st.l_own, st.v, mine, lane);
+    reduce_w();
   }
 
   // Writes the normalised row (bf16, round-to-nearest-even) and, from lane 0,

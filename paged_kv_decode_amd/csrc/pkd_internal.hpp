@@ -6,22 +6,29 @@
 
 namespace pkd {
 
+// Rows.  Each sequence has q_len query tokens (1 for plain decode); the memory
+// row of (sequence b, query token i, head h) in q, out and lse is
+// (b * q_len + i) * Hq + h.  The q_len * G rows of one KV head are "packed
+// rows" r = i * G + (h - kvh * G), grouped 16 to a head group.
+
 // Arguments of the split-KV partition kernel (one launch).
 struct SplitParams {
-  const uint16_t* q;           // [B][Hq][D] bf16
+  const uint16_t* q;           // [B][q_len][Hq][D] bf16
   const uint8_t* k;            // [num_pages][ps][Hkv][D] kv elements (bf16 or fp8 codes)
   const uint8_t* v;
   const int32_t* block_table;  // [B][max_pages]
   const int32_t* seq_lens;     // [B]
   const float* k_scale;        // [Hkv] (fp8) or null
   const float* v_scale;
-  uint16_t* out;               // direct mode: [B][Hq][D] bf16
-  float* lse;                  // direct mode: [B][Hq] or null
-  float* o_part;               // split mode: [B][Hq][S][D]
-  float* lse_part;             // split mode: [B][Hq][S]
+  uint16_t* out;               // direct mode: [B][q_len][Hq][D] bf16
+  float* lse;                  // direct mode: [B][q_len][Hq] or null
+  float* o_part;               // split mode: [B][q_len][Hq][S][D]
+  float* lse_part;             // split mode: [B][q_len][Hq][S]
   float qk_scale_log2;         // scale * log2(e): scores are kept in base-2 units
   int32_t hq, hkv, group;      // group = G = Hq / Hkv
-  int32_t head_groups;         // ceil(G / 16): query heads are packed 16 per workgroup
+  int32_t q_len, causal;       // query tokens per sequence; causal mask on (1) or off (0)
+  int32_t rows_kv;             // packed rows per KV head: q_len * G
+  int32_t head_groups;         // ceil(rows_kv / 16): packed rows are taken 16 per workgroup
   int32_t page_size, max_pages;
   int32_t num_splits;
   int32_t chunk;               // tokens per split (a multiple of kSplitAlign, or >= every length)
@@ -41,7 +48,8 @@ struct BalancedParams {
   int64_t* prefix;             // [batch + 1] group prefix sums, written for the merge kernel
   float qk_scale_log2;
   int32_t batch, hq, hkv, group, head_groups;
-  int32_t hpg;                 // heads per slot: min(group, 16)
+  int32_t q_len, causal, rows_kv;  // as in SplitParams
+  int32_t hpg;                 // rows per slot: min(rows_kv, 16)
   int32_t page_size, max_pages;
   int32_t num_workers;         // workgroups in the grid
   // In-kernel merge (fused != 0): segments held by one piece write out/lse
@@ -50,8 +58,8 @@ struct BalancedParams {
   // done; a word with another epoch counts as zero, and the merging piece
   // resets it to (epoch << 24), so no initialisation is ever needed.
   int32_t fused;
-  uint16_t* out;               // [B][Hq][D] bf16 (fused)
-  float* lse;                  // [B][Hq] or null (fused)
+  uint16_t* out;               // [B][q_len][Hq][D] bf16 (fused)
+  float* lse;                  // [B][q_len][Hq] or null (fused)
   uint64_t* seg_count;         // [B * Hkv * head_groups] (fused)
   uint64_t epoch;              // distinct per call, 1 .. 2^40 - 1 (fused)
 };
@@ -79,6 +87,7 @@ struct MergeParams {
   int32_t balanced;            // 0: grid layout; 1: balanced layout
   const int64_t* prefix;       // balanced layout fields
   int32_t batch, hq, hkv, group, head_groups, hpg, num_workers;
+  int32_t q_len;               // balanced layout: rows are (b * q_len + i) * Hq + h
 };
 
 constexpr int kWaves = 4;            // waves per split-kernel workgroup

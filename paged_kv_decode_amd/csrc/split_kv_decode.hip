@@ -37,6 +37,15 @@
 // Rows past the end of a range are clamped to the last valid row for
 // addressing (so no page past the sequence and no tail slot is ever read) and
 // masked to -inf by selection.  An empty range writes o = 0 and lse = -inf.
+//
+// Several query tokens per sequence (speculative verify / extend, q_len > 1):
+// the q_len * G query rows of one KV head are packed 16 to an MFMA N dimension
+// exactly like G query heads, packed row r being query token r / G of head
+// kvh * G + r % G, so every K/V row read still serves all of them.  Under the
+// causal mask query token i of a length-L sequence sees positions
+// <= L - q_len + i (the position of that token), so each lane, which holds one
+// packed row, masks scores at its own end; a row that sees no token of a tile
+// or of a whole range keeps m = -inf and contributes nothing.
 #include "merge_row.hpp"
 #include "pkd_internal.hpp"
 
@@ -83,7 +92,7 @@ struct Cfg {
   static constexpr int BT_OFFSET = VT_BYTES;                // staged block-table entries
   static constexpr int BT_ENTRIES = 512;
   static constexpr int OW_STRIDE = D + 4;                  // merge staging row stride (floats)
-  static constexpr int MERGE_BYTES = kWaves * 16 * (2 + OW_STRIDE) * 4;
+  static constexpr int MERGE_BYTES = kWaves * 16 * (2 + OW_STRIDE) * 4 + 16 * (kWaves + 4) * 4;
   static constexpr int LOOP_BYTES = VT_BYTES + BT_ENTRIES * 4;
   static constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
   static_assert(KK == NPIECE * R, "K pieces must feed whole MFMAs");
@@ -102,11 +111,22 @@ __device__ __forceinline__ To bit_cast_dev(const From& f) {
   return t;
 }
 
-// K/V rows are streamed exactly once: non-temporal loads keep them from
-// displacing reusable lines in L2 and the Infinity Cache.
+// V rows are streamed exactly once, each load instruction covering whole
+// rows: non-temporal loads keep them from displacing reusable lines in L2 and
+// the Infinity Cache.
 template <int BYTES>
 __device__ __forceinline__ typename VecT<BYTES>::T gload(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const typename VecT<BYTES>::T*>(p));
+}
+
+// K loads are laid out for the MFMA A operand: one instruction reads 16 rows,
+// 4 lanes x 16 bytes of each, so every 128-byte line of a row is requested by
+// two consecutive instructions.  They are ordinary cached loads so that the
+// second request hits in the vector L1; streamed non-temporally, both went to
+// L2 and the step ran 3-6% slower (K streams at some row offsets 20-30% slower).
+template <int BYTES>
+__device__ __forceinline__ typename VecT<BYTES>::T kload(const uint8_t* p) {
+  return *reinterpret_cast<const typename VecT<BYTES>::T*>(p);
 }
 
 // Wave-local LDS ordering: all of this wave's LDS writes have landed before any
@@ -207,11 +227,11 @@ struct WaveAttn {
     v_doff = (lane % C::CPR) * C::VLB;
   }
 
-  // Lane (n, g) holds head n's dims (kk / R) * 4 * PIECE + g * PIECE + (kk % R) * 8 + [0, 8)
-  // for MFMA kk; the K loads use the same dim assignment.  Heads past the group are zero.
-  __device__ __forceinline__ void load_q(const uint16_t* q, int64_t row0, int heads_here) {
-    const bool hv = n < heads_here;
-    const uint16_t* qrow = q + (row0 + (hv ? n : 0)) * D;
+  // Lane (n, g) holds packed row n's dims (kk / R) * 4 * PIECE + g * PIECE + (kk % R) * 8 + [0, 8)
+  // for MFMA kk; the K loads use the same dim assignment.  qrow_n is the memory
+  // row of packed row n (any valid row when hv is false); rows past the group are zero.
+  __device__ __forceinline__ void load_q(const uint16_t* q, int64_t qrow_n, bool hv) {
+    const uint16_t* qrow = q + qrow_n * D;
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       const int d0 = (kk / C::R) * 4 * C::PIECE + g * C::PIECE + (kk % C::R) * 8;
@@ -263,7 +283,7 @@ struct WaveAttn {
       }
       const uint8_t* src = kc + base + min(k_rig[blk], gl) * tok_stride + k_doff;
 #pragma unroll
-      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = gload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
+      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = kload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
     }
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
@@ -284,7 +304,7 @@ struct WaveAttn {
       const int64_t off = ((int64_t)(idle ? 0 : pages[blk]) * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
       const uint8_t* src = kc + off + k_doff;
 #pragma unroll
-      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = gload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
+      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = kload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
     }
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
@@ -300,7 +320,8 @@ struct WaveAttn {
     return idx < C::NBLK ? k_row_token<C::KP>(idx, n) : (idx - C::NBLK) * C::RPI + v_rig;
   }
 
-  // One tile: V to LDS, QK^T, online softmax, PV.  Rows at or past s1 are masked.
+  // One tile: V to LDS, QK^T, online softmax, PV.  Tokens at or past s1 (this
+  // lane's packed row's end) are masked.
   __device__ __forceinline__ void process(const Regs& R, int tb, int s1, uint16_t* vs) {
     // V -> LDS, row-major bf16 (16-byte writes).
 #pragma unroll
@@ -356,14 +377,17 @@ struct WaveAttn {
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // A row that has seen no unmasked token keeps m = -inf; subtracting 0 then
+    // gives alpha = 0 and e = 0 instead of NaN.
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int blk = 0; blk < C::NBLK; ++blk)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(sacc[blk][i] - m_new);
+        const float e = __builtin_amdgcn_exp2f(sacc[blk][i] - m_use);
         sacc[blk][i] = e;
         psum += e;
       }
@@ -417,6 +441,33 @@ struct WaveAttn {
   }
 };
 
+// Memory row ((b * q_len + i) * Hq + h) of packed row r of KV head kvh of
+// sequence b: query token i = r / G, head h = kvh * G + r % G.
+__device__ __forceinline__ int64_t packed_row(int b, int kvh, int r, int q_len, int hq, int group) {
+  const int i = r / group;
+  return ((int64_t)b * q_len + i) * hq + kvh * group + (r - i * group);
+}
+
+// Per lane (packed row n = lane % 16 of head group hg): the memory row of its
+// query (a valid row even past the group), whether the row exists, and the end
+// of the tokens it sees within [.., s1): s1, or under the causal mask
+// min(s1, L - q_len + i + 1) for query token i.
+struct LaneRow {
+  int64_t row;
+  bool valid;
+  int end;
+};
+template <typename P>
+__device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, int n, int L, int s1) {
+  const int r = hg * kHeadsPerGroup + n;
+  LaneRow lr;
+  lr.valid = r < p.rows_kv;
+  const int rr = lr.valid ? r : hg * kHeadsPerGroup;
+  lr.row = packed_row(b, kvh, rr, p.q_len, p.hq, p.group);
+  lr.end = p.causal ? min(s1, L - p.q_len + rr / p.group + 1) : s1;
+  return lr;
+}
+
 // Tiles first, first + step, ... (< ntiles): while tile t is processed the
 // next tile's K/V loads are in flight and the page entries of the tile after
 // that are being read.  After the last tile the "next" loads stay in the
@@ -456,20 +507,26 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
   }
 }
 
-// Combine the four waves' (m, l, O) of one workgroup in LDS (smem must hold
-// MERGE_BYTES) and hand every (head, dim) of the group to store(hh, d, o,
-// lse_nat): o = sum_w e_w O_w / sum_w e_w l_w (times vsc), with
-// e_w = 2^(m_w - max m), and the natural-log LSE.  Ends with the LDS still in
-// use: synchronise before reusing it.
+// Combine the waves' (m, l, O) of one workgroup in LDS (smem must hold
+// NWV * 16 * (2 + OW_STRIDE) * 4 + 16 * (NWV + 4) * 4 bytes) and hand every
+// row of the group to store, four dims at a time: store(hh, d0, o4, lse_nat),
+// o4 = dims d0 .. d0 + 3 of o = sum_w e_w O_w * vsc / sum_w e_w l_w with
+// e_w = 2^(m_w - max m), and the natural-log LSE.  A row that saw no token in
+// any wave gets o = 0 and lse = -inf.  The per-row weights e_w * vsc / den are
+// computed once per row, then each element is a short weighted sum of the
+// staged wave rows.  Ends with the LDS still in use: synchronise before
+// reusing it.
 template <int D, bool FP8, int NWV = kWaves, typename Store>
 __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* smem, int wave, int tid,
                                            int heads_here, float vsc, Store store) {
   typedef Cfg<D, FP8> C;
+  constexpr int RWS = NWV + 4;                 // per-row table stride (floats): NWV weights, then the LSE
   const float l_tot = A.l_total();
   __syncthreads();
   float* mw = reinterpret_cast<float*>(smem);  // [NWV][16]
-  float* lw = mw + NWV * 16;                // [NWV][16]
-  float* ow = lw + NWV * 16;                // [NWV][16][OW_STRIDE]
+  float* lw = mw + NWV * 16;                   // [NWV][16]
+  float* ow = lw + NWV * 16;                   // [NWV][16][OW_STRIDE]
+  float* rw = ow + NWV * 16 * C::OW_STRIDE;    // [16][RWS]
   if (A.g == 0) {
     mw[wave * 16 + A.n] = A.m_run;
     lw[wave * 16 + A.n] = l_tot;
@@ -478,20 +535,42 @@ __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* s
   for (int nb = 0; nb < C::NB; ++nb)
     *reinterpret_cast<f32x4*>(ow + (wave * 16 + A.n) * C::OW_STRIDE + 16 * nb + 4 * A.g) = A.acc[nb];
   __syncthreads();
-  for (int idx = tid; idx < heads_here * D; idx += NWV * 64) {
-    const int hh = idx / D, d = idx - (idx / D) * D;
+  if (tid < heads_here) {
+    const int hh = tid;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) M = fmaxf(M, mw[w * 16 + hh]);
-    float num = 0.f, den = 0.f;
+    const float M_use = M == -INFINITY ? 0.f : M;
+    float e[NWV];
+    float den = 0.f;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) {
-      const float e = __builtin_amdgcn_exp2f(mw[w * 16 + hh] - M);
-      num += e * ow[(w * 16 + hh) * C::OW_STRIDE + d];
-      den += e * lw[w * 16 + hh];
+      e[w] = __builtin_amdgcn_exp2f(mw[w * 16 + hh] - M_use);
+      den += e[w] * lw[w * 16 + hh];
     }
-    store(hh, d, (num / den) * vsc, (M + log2f(den)) * 0.69314718055994530942f);
+    const float sc = den > 0.f ? vsc / den : 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) rw[hh * RWS + w] = e[w] * sc;
+    rw[hh * RWS + NWV] = (M_use + log2f(den)) * 0.69314718055994530942f;
   }
+  __syncthreads();
+  constexpr int Q4 = D / 4;
+  for (int idx = tid; idx < heads_here * Q4; idx += NWV * 64) {
+    const int hh = idx / Q4, d0 = (idx - hh * Q4) * 4;
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NWV; ++w)
+      o += rw[hh * RWS + w] * *reinterpret_cast<const f32x4*>(ow + (w * 16 + hh) * C::OW_STRIDE + d0);
+    store(hh, d0, o, rw[hh * RWS + NWV]);
+  }
+}
+
+// Four fp32 values rounded to bf16 (round-to-nearest-even), as one 8-byte word.
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 o) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (__bf16)o[i];
+  return r;
 }
 
 // Waves per SIMD the register allocation targets.  Two resident waves per
@@ -531,20 +610,21 @@ split_kv_kernel(const SplitParams p) {
   const int chunk = p.chunk;  // tokens per split, the same for every sequence
   const int s0 = (int)min((int64_t)split * chunk, (int64_t)L);
   const int s1 = min(s0 + chunk, L);
-  const int heads_here = min(kHeadsPerGroup, p.group - hg * kHeadsPerGroup);
-  const int h0 = kvh * p.group + hg * kHeadsPerGroup;
-  const int64_t row0 = (int64_t)b * p.hq + h0;  // first output row of this workgroup
+  const int heads_here = min(kHeadsPerGroup, p.rows_kv - hg * kHeadsPerGroup);
+  // Memory rows of the workgroup's packed rows (query token, head).
+  __shared__ int64_t s_rows[kHeadsPerGroup];
 
   if (s0 >= s1) {
     // Empty split (or an empty sequence): o = 0, lse = -inf.
     for (int idx = tid; idx < heads_here * D; idx += kWaves * 64) {
       const int hh = idx / D, d = idx - (idx / D) * D;
+      const int64_t row = packed_row(b, kvh, hg * kHeadsPerGroup + hh, p.q_len, p.hq, p.group);
       if constexpr (DIRECT) {
-        p.out[(row0 + hh) * D + d] = 0;
-        if (d == 0 && p.lse) p.lse[row0 + hh] = -INFINITY;
+        p.out[row * D + d] = 0;
+        if (d == 0 && p.lse) p.lse[row] = -INFINITY;
       } else {
-        p.o_part[((row0 + hh) * S + split) * D + d] = 0.f;
-        if (d == 0) p.lse_part[(row0 + hh) * S + split] = -INFINITY;
+        p.o_part[(row * S + split) * D + d] = 0.f;
+        if (d == 0) p.lse_part[row * S + split] = -INFINITY;
       }
     }
     return;
@@ -559,7 +639,9 @@ split_kv_kernel(const SplitParams p) {
   const __attribute__((address_space(4))) int32_t* bt =
       (const __attribute__((address_space(4))) int32_t*)(p.block_table + (int64_t)b * p.max_pages);
 
-  A.load_q(p.q, row0, heads_here);
+  const LaneRow lr = lane_row(p, b, kvh, hg, A.n, L, s1);
+  if (tid < kHeadsPerGroup) s_rows[tid] = lr.row;  // read after the barriers below
+  A.load_q(p.q, lr.row, lr.valid);
   A.qk_scale = p.qk_scale_log2;
   if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
   A.reset();
@@ -596,16 +678,17 @@ split_kv_kernel(const SplitParams p) {
 
   uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;  // this wave's V[TT][VS]
   // Tiles wave, wave + 4, wave + 8, ...
-  run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, s1, vs, fetch, issue);
+  run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, lr.end, vs, fetch, issue);
 
   const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
-  wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
+  wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
+    const int64_t row = s_rows[hh];
     if constexpr (DIRECT) {
-      p.out[(row0 + hh) * D + d] = bit_cast_dev<uint16_t>((__bf16)o);
-      if (d == 0 && p.lse) p.lse[row0 + hh] = lse_nat;
+      *reinterpret_cast<bf16x4*>(p.out + row * D + d0) = to_bf16x4(o);
+      if (d0 == 0 && p.lse) p.lse[row] = lse_nat;
     } else {
-      p.o_part[((row0 + hh) * S + split) * D + d] = o;
-      if (d == 0) p.lse_part[(row0 + hh) * S + split] = lse_nat;
+      *reinterpret_cast<f32x4*>(p.o_part + (row * S + split) * D + d0) = o;
+      if (d0 == 0) p.lse_part[row * S + split] = lse_nat;
     }
   });
 }
@@ -613,10 +696,10 @@ split_kv_kernel(const SplitParams p) {
 // ---- balanced persistent kernel ---------------------------------------------
 //
 // The work space is the sequence of segments s = (b * Hkv + kvh) * HG + hg
-// (HG head groups of up to 16 query heads per KV head), segment s holding the
+// (HG head groups of up to 16 query rows per KV head), segment s holding the
 // n_b = ceil(L_b / 16) 16-token groups of sequence b; T groups in all.  With
 // NWE = min(workgroups, T) active workgroups, workgroup w takes groups
-// [floor(w T / NWE), floor((w + 1) T / NWE)); its four waves interleave the
+// [floor(w T / NWE), floor((w + 1) T / NWE)); its waves interleave the
 // tiles of each piece (the part of one segment inside the range) and combine
 // in LDS.  Each (workgroup, segment) piece writes its normalised partial and
 // LSE to slot w + s, which is unique and increasing along the work space; the
@@ -629,12 +712,13 @@ balanced_kernel(const BalancedParams p) {
   typedef Cfg<D, FP8> C;
   typedef TilePages<D, FP8, true> Pages;
   constexpr int VT_BYTES = NWV * C::TT * C::VS * 2;                 // wave-private V tiles
-  constexpr int MERGE_BYTES = NWV * 16 * (2 + C::OW_STRIDE) * 4;   // combine staging
+  constexpr int MERGE_BYTES = NWV * 16 * (2 + C::OW_STRIDE) * 4 + 16 * (NWV + 4) * 4;  // combine staging
   constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ int64_t spre[kBalancedMaxBatch + 1];  // spre[b] = groups of all segments of sequences < b
   __shared__ int64_t stot[NWV];
   __shared__ int s_last;                           // in-kernel merge: this piece completes its segment
+  __shared__ int64_t s_rows[kHeadsPerGroup];       // memory rows of the current piece's packed rows
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -681,12 +765,14 @@ balanced_kernel(const BalancedParams p) {
   const int64_t nwe = min((int64_t)p.num_workers, T);
   const int64_t w = blockIdx.x;
   if (p.fused) {
-    // Sequences of length 0 have no piece: out = 0, lse = -inf (workgroup bb % W).
+    // Sequences of length 0 have no piece: out = 0, lse = -inf for all their
+    // q_len * Hq rows (workgroup bb % W).
+    const int rows_seq = p.q_len * p.hq;
     for (int bb = (int)w; bb < B; bb += p.num_workers) {
       if (spre[bb + 1] != spre[bb]) continue;
-      for (int i = tid; i < p.hq * D; i += NWV * 64) p.out[(int64_t)bb * p.hq * D + i] = 0;
+      for (int i = tid; i < rows_seq * D; i += NWV * 64) p.out[(int64_t)bb * rows_seq * D + i] = 0;
       if (p.lse)
-        for (int i = tid; i < p.hq; i += NWV * 64) p.lse[(int64_t)bb * p.hq + i] = -INFINITY;
+        for (int i = tid; i < rows_seq; i += NWV * 64) p.lse[(int64_t)bb * rows_seq + i] = -INFINITY;
     }
   }
   if (w >= nwe) return;  // the whole workgroup leaves together
@@ -732,8 +818,9 @@ balanced_kernel(const BalancedParams p) {
     const int lim = s1 - 1;
     const int kvh = seg / p.head_groups;
     const int hg = seg - kvh * p.head_groups;
-    const int heads_here = min(kHeadsPerGroup, p.group - hg * kHeadsPerGroup);
-    const int64_t row0 = (int64_t)b * p.hq + kvh * p.group + hg * kHeadsPerGroup;
+    const int heads_here = min(kHeadsPerGroup, p.rows_kv - hg * kHeadsPerGroup);
+    const LaneRow lr = lane_row(p, b, kvh, hg, A.n, L, s1);
+    if (tid < kHeadsPerGroup) s_rows[tid] = lr.row;  // read after the combine's barriers
     const int64_t head_off = (int64_t)kvh * C::ROWB;
 
     // The next piece: the following segment (of this or a later sequence).
@@ -745,7 +832,7 @@ balanced_kernel(const BalancedParams p) {
     }
     const int next_window = npos < hi ? load_window(nbq, 0) : 0;
 
-    A.load_q(p.q, row0, heads_here);
+    A.load_q(p.q, lr.row, lr.valid);
     A.qk_scale = p.qk_scale_log2;
     if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
     A.reset();
@@ -766,7 +853,7 @@ balanced_kernel(const BalancedParams p) {
       A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, head_off, R, idle);
     };
     const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
-    run_tiles<D, FP8, Pages>(A, wave, NWV, ntiles, s0, s1, vs, fetch, issue);
+    run_tiles<D, FP8, Pages>(A, wave, NWV, ntiles, s0, lr.end, vs, fetch, issue);
 
     // This segment's pieces are those of workgroups w_first .. w_last, at
     // slots w + s (s = b * SPB + seg).
@@ -777,9 +864,10 @@ balanced_kernel(const BalancedParams p) {
     const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
     if (p.fused && npieces == 1) {
       // The whole segment is this piece: write the result directly.
-      wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
-        p.out[(row0 + hh) * D + d] = bit_cast_dev<uint16_t>((__bf16)o);
-        if (d == 0 && p.lse) p.lse[row0 + hh] = lse_nat;
+      wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
+        const int64_t row = s_rows[hh];
+        *reinterpret_cast<bf16x4*>(p.out + row * D + d0) = to_bf16x4(o);
+        if (d0 == 0 && p.lse) p.lse[row] = lse_nat;
       });
       __syncthreads();  // the LDS is reused by the next piece
     } else {
@@ -788,18 +876,20 @@ balanced_kernel(const BalancedParams p) {
       float* orow = p.o_part + slot * p.hpg * D;
       float* lrow = p.lse_part + slot * p.hpg;
       if (!p.fused) {
-        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
-          orow[hh * D + d] = o;
-          if (d == 0) lrow[hh] = lse_nat;
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
+          *reinterpret_cast<f32x4*>(orow + hh * D + d0) = o;
+          if (d0 == 0) lrow[hh] = lse_nat;
         });
       } else {
         // Agent-scope stores write through to the coherent copy that another
         // XCD's workgroup will read; waiting for their acknowledgement before the
         // count makes the partial visible to whichever piece merges.  (A release
         // fence would write back this XCD's whole L2, far too costly per piece.)
-        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d, float o, float lse_nat) {
-          __hip_atomic_store(orow + hh * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (d == 0) __hip_atomic_store(lrow + hh, lse_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(orow + hh * D + d0 + i, o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (d0 == 0) __hip_atomic_store(lrow + hh, lse_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         });
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are acknowledged
@@ -822,13 +912,48 @@ balanced_kernel(const BalancedParams p) {
         __syncthreads();
         const bool last = s_last != 0;
         if (last) {
-          // The other pieces' partials, read from the coherent copy.
+          // The pieces' partials, read from the coherent copy.  Wave w merges
+          // rows w, w + NWV, ...  With few pieces the loads of RC rows at a
+          // time are issued before any of them is combined (RC rows of staged
+          // partials take at most 64 registers with one wave per SIMD, 32 with
+          // two); otherwise, or when only one row fits, one row at a time.
           const int64_t slot0 = w_first + sidx;
-          for (int hh = wave; hh < heads_here; hh += NWV) {
-            RowMerge<D, true> r;
-            r.run(p.lse_part + slot0 * p.hpg + hh, p.hpg, p.o_part + (slot0 * p.hpg + hh) * D,
-                  (int64_t)p.hpg * D, npieces, tid & 63);
-            r.store(p.out + (row0 + hh) * D, p.lse ? p.lse + row0 + hh : nullptr, tid & 63);
+          typedef RowMerge<D, true> RM;
+          constexpr int MAXR = kHeadsPerGroup / NWV;
+          constexpr int RC_REG = (NWV > 4 ? 32 : 64) / (RM::UNROLL * RM::EPL);
+          constexpr int RC = RC_REG < MAXR ? RC_REG : MAXR;
+          const float* lp0 = p.lse_part + slot0 * p.hpg;
+          const float* op0 = p.o_part + slot0 * p.hpg * D;
+          const int64_t ls = p.hpg, os = (int64_t)p.hpg * D;
+          const int lane = tid & 63;
+          if (RC < 2 || npieces > RM::UNROLL) {
+            for (int hh = wave; hh < heads_here; hh += NWV) {
+              RM r;
+              r.run(lp0 + hh, ls, op0 + hh * D, os, npieces, lane);
+              const int64_t row = s_rows[hh];
+              r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane);
+            }
+          } else {
+            constexpr int RCS = RC < 2 ? 2 : RC;  // (the branch above takes RC < 2)
+#pragma unroll
+            for (int k0 = 0; k0 < MAXR; k0 += RCS) {
+              typename RM::Staged st[RCS];
+#pragma unroll
+              for (int k = 0; k < RCS; ++k) {
+                const int hh = wave + (k0 + k) * NWV;
+                if (hh < heads_here) RM::issue(lp0 + hh, ls, op0 + hh * D, os, npieces, lane, st[k]);
+              }
+#pragma unroll
+              for (int k = 0; k < RCS; ++k) {
+                const int hh = wave + (k0 + k) * NWV;
+                if (hh < heads_here) {
+                  RM r;
+                  r.finish(st[k], npieces, lane);
+                  const int64_t row = s_rows[hh];
+                  r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane);
+                }
+              }
+            }
           }
         }
       }

@@ -49,11 +49,11 @@ def test_binding_constants_match_header():
 
 
 def test_dims_struct_layout():
-    assert ctypes.sizeof(b.pkd_dims) == 8 * 4
+    assert ctypes.sizeof(b.pkd_dims) == 10 * 4
 
 
 def test_status_strings_are_distinct():
-    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10]
+    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11]
     texts = [b.paged_decode_status_string(c) for c in codes]
     assert len(set(texts)) == len(texts)
     assert b.paged_decode_status_string(-12345) == "unknown status"
@@ -61,7 +61,7 @@ def test_status_strings_are_distinct():
 
 def dims(**kw):
     base = dict(batch=2, num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=16, num_pages=10,
-                max_pages_per_seq=7, kv_dtype=b.PKD_DTYPE_BF16)
+                max_pages_per_seq=7, kv_dtype=b.PKD_DTYPE_BF16, q_len=1, causal=0)
     base.update(kw)
     return b.pkd_dims(*[base[f] for f, _ in b.pkd_dims._fields_])
 
@@ -83,6 +83,10 @@ def call(d, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, ks=None, vs=None, scale=
     (dict(head_dim=512), b.PKD_ERR_HEAD_DIM),
     (dict(kv_dtype=7), b.PKD_ERR_DTYPE),
     (dict(max_pages_per_seq=2**20, page_size=2**12), b.PKD_ERR_BAD_DIMS),
+    (dict(q_len=0), b.PKD_ERR_BAD_DIMS),
+    (dict(q_len=b.PKD_MAX_Q_LEN + 1), b.PKD_ERR_BAD_DIMS),
+    (dict(causal=2), b.PKD_ERR_BAD_DIMS),
+    (dict(causal=-1), b.PKD_ERR_BAD_DIMS),
 ])
 def test_bad_dims_are_rejected(kw, status):
     d = dims(**kw)
@@ -107,6 +111,22 @@ def test_fp8_scales_rules():
     assert call(dims(), ks=FAKE, vs=FAKE) == b.PKD_ERR_SCALES
 
 
+def test_misaligned_pointers_are_rejected():
+    d = dims()
+    for kw in ("q", "k", "v", "out"):
+        assert call(d, **{kw: FAKE + 8}) == b.PKD_ERR_ALIGNMENT, kw
+    for kw in ("bt", "lens"):
+        assert call(d, **{kw: FAKE + 2}) == b.PKD_ERR_ALIGNMENT, kw
+    assert call(d, lse=FAKE + 1) == b.PKD_ERR_ALIGNMENT
+    need = b.paged_decode_workspace_bytes(d, 3)
+    assert call(d, S=3, ws=FAKE + 8, ws_bytes=need) == b.PKD_ERR_ALIGNMENT
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1)
+    assert b.paged_decode_partials(d, *args, 2, FAKE + 4, FAKE, None) == b.PKD_ERR_ALIGNMENT
+    assert b.paged_decode_merge(8, 2, 64, FAKE + 2, FAKE, FAKE, None, None) == b.PKD_ERR_ALIGNMENT
+    assert b.paged_decode_merge(8, 2, 64, FAKE, FAKE, FAKE + 1, None, None) == b.PKD_ERR_ALIGNMENT
+    assert b.paged_decode_check_tables(d, FAKE + 2, FAKE, FAKE, None) == b.PKD_ERR_ALIGNMENT
+
+
 def test_non_finite_scale_is_rejected():
     assert call(dims(), scale=float("nan")) == b.PKD_ERR_BAD_DIMS
     assert call(dims(), scale=float("inf")) == b.PKD_ERR_BAD_DIMS
@@ -124,6 +144,23 @@ def test_num_splits_and_workspace_rules():
     assert call(d, S=3, ws=FAKE, ws_bytes=need - 1) == b.PKD_ERR_WORKSPACE
     assert b.paged_decode_workspace_bytes(d, 1) == 0
     assert b.paged_decode_workspace_bytes(d, b.PKD_MAX_SPLITS + 1) == 0
+
+
+def test_workspace_grows_with_query_tokens():
+    """Several query tokens per sequence: grid partials are [B][q_len][Hq][S][D]; the
+    balanced mode packs the q_len * G rows of a KV head 16 to a head group."""
+    d3 = dims(q_len=3, causal=1)
+    # [B][q_len][Hq][S][D] fp32 + [B][q_len][Hq][S] fp32 (288 B, rounded up to 512)
+    assert b.paged_decode_workspace_bytes(d3, 3) == 2 * 3 * 4 * 3 * 64 * 4 + 512
+    # G = 4, q_len = 3: 12 rows per KV head, one head group of 12 rows per slot
+    one = b.paged_decode_workspace_bytes(dims(), b.PKD_SPLITS_BALANCED)
+    three = b.paged_decode_workspace_bytes(d3, b.PKD_SPLITS_BALANCED)
+    assert three > one
+    # G = 4, q_len = 5: 20 rows, two head groups per KV head
+    d5 = dims(q_len=5)
+    assert b.paged_decode_launches(d5, 4) == 2
+    assert b.paged_decode_workspace_bytes(d5, b.PKD_SPLITS_BALANCED) > three
+    assert call(dims(q_len=b.PKD_MAX_Q_LEN), S=3) == b.PKD_ERR_WORKSPACE  # accepted shape, no workspace
 
 
 def test_valid_call_without_gpu_reports_no_device():

@@ -43,7 +43,7 @@ def dev(w):
 def run(B, w, S=0, t=None, scale=None):
     t = t or dev(w)
     out, lse = B.decode(t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale if scale is None else scale,
-                        t["ks"], t["vs"], num_splits=S)
+                        t["ks"], t["vs"], num_splits=S, causal=w.spec.causal)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
 
@@ -481,3 +481,122 @@ def test_in_kernel_merge_ignores_workspace_contents(B):
     for o, l in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
     check(outs[0][0].view(torch.bfloat16), outs[0][1].view(torch.float32), *oracle_full(w), what="in-kernel merge")
+
+
+# ---- several query tokens per sequence (speculative verify / extend) --------
+
+MULTI_CASES = [
+    # (B, Hq, Hkv, D, ps, seq_lens, q_len, causal, dtype, seed)
+    (4, 8, 2, 64, 16, [1, 3, 37, 200], 4, True, "bf16", 301),      # L < q_len: rows that see nothing
+    (3, 32, 8, 128, 64, [700, 64, 2], 4, True, "bf16", 302),      # G = 4, q_len = 4: one full group of 16
+    (3, 16, 2, 128, 16, [100, 513, 17], 3, True, "bf16", 303),    # G = 8, q_len = 3: 24 rows, partial 2nd group
+    (2, 8, 8, 64, 24, [50, 77], 5, True, "bf16", 304),            # ps = 24: per-row page lookups
+    (3, 8, 2, 128, 64, [0, 130, 65], 2, False, "bf16", 305),      # no mask, an empty sequence
+    (3, 16, 2, 128, 64, [40, 300, 7], 8, True, "fp8_e4m3", 306),  # FP8, 64 rows per KV head
+    (2, 4, 1, 256, 16, [33, 90], 16, True, "bf16", 307),          # D = 256, q_len = 16
+    (2, 4, 4, 32, 16, [20, 45], 6, True, "bf16", 308),            # G = 1, D = 32
+]
+
+
+@pytest.mark.parametrize("case", MULTI_CASES)
+def test_multi_token_parity(B, case):
+    bq, hq, hkv, d, ps, lens, ql, causal, dtype, seed = case
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, dtype, seed, q_len=ql, causal=causal)
+    ref = oracle_full(w)
+    t = dev(w)
+    for S in (1, 3, 0) + ((BAL,) if ps % 16 == 0 else ()):
+        out, lse = run(B, w, S, t)
+        assert out.shape == (bq, ql, hq, d) and lse.shape == (bq, ql, hq)
+        check(out, lse, *ref, what=f"multi {case} S={S}")
+
+
+def test_multi_with_one_query_token_is_decode_bitwise(B):
+    lens = [5, 130, 64, 1, 700]
+    w = wl.custom_workload(len(lens), 32, 8, 128, 64, lens, "bf16", seed=311)
+    t = dev(w)
+    q4 = t["q"].unsqueeze(1).contiguous()
+    for S in (1, 4, BAL):
+        ref_o, ref_l = run(B, w, S, t)
+        for causal in (False, True):
+            o, l = B.decode(q4, t["k"], t["v"], t["bt"], t["lens"], w.scale, num_splits=S, causal=causal)
+            torch.cuda.synchronize()
+            assert torch.equal(o.cpu()[:, 0].view(torch.int16), ref_o.view(torch.int16))
+            assert torch.equal(l.cpu()[:, 0].view(torch.int32), ref_l.view(torch.int32))
+
+
+def test_multi_token_one_hot_probe_sees_exactly_its_prefix(B):
+    """Causal bit-exact probe: K[t][0] = 4096 at two tokens of each sequence, the
+    last position (visible to the last query token only) and position L - q_len
+    (visible to all).  With q = e_0 every query token but the last must return
+    V at L - q_len bit for bit, and the last the bf16 mean of the two V rows is
+    not bit-defined, so it is checked against the oracle instead."""
+    ql = 4
+    lens = [4, 37, 64, 129]
+    d = 64
+    w = wl.custom_workload(len(lens), 8, 2, d, 16, lens, "bf16", seed=312, q_len=ql, causal=True)
+    q = torch.zeros_like(w.q)
+    q[..., 0] = 1.0
+    k = torch.zeros_like(w.k_logical)
+    offs = w.token_offsets
+    for b, L in enumerate(lens):
+        k[int(offs[b]) + L - ql, :, 0] = 4096.0
+        k[int(offs[b]) + L - 1, :, 0] = 4096.0
+    w = wl.rebuild_with_rows(w, q=q, k_logical=k)
+    t = dev(w)
+    ref_o, ref_l = oracle_full(w)
+    for S in (1, 3, BAL):
+        out, lse = run(B, w, S, t)
+        check(out, lse, ref_o, ref_l, what=f"multi one-hot S={S}")
+        for b, L in enumerate(lens):
+            vrow = w.v_logical[int(offs[b]) + L - ql]  # [Hkv, D]
+            for i in range(ql - 1):
+                for h in range(8):
+                    assert torch.equal(out[b, i, h].view(torch.int16), vrow[h // 4].view(torch.int16)), (S, b, i, h)
+
+
+def test_multi_verify_workload_sampled_rows(B):
+    """The B=32 verify step (4 query tokens per sequence, causal) at full size:
+    sampled rows against the oracle, every row across the modes."""
+    spec = wl.WORKLOADS["verify_b32_q4_d128_ps64"]
+    w = wl.make_workload(spec, tail="nan")
+    t = dev(w)
+    n_rows = spec.batch * spec.q_len * spec.num_q_heads
+    g = torch.Generator().manual_seed(spec.seed)
+    rows = sorted(set([0, n_rows - 1] + torch.randint(0, n_rows, (46,), generator=g).tolist()))
+    ref_o, ref_l = oracle.paged_decode_multi_rows(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens,
+                                                  w.scale, True, rows)
+    dims = B.dims_for(t["q"], t["k"], t["bt"], causal=True)
+    assert B.paged_decode_launches(dims, BAL) == 1  # 256 segments: merged in place
+    outs = {}
+    for S in (BAL, 0, 1, 8):
+        out, lse = run(B, w, S, t)
+        check(out.view(-1, spec.head_dim)[rows], lse.view(-1)[rows], ref_o, ref_l, what=f"verify S={S}")
+        outs[S] = (out, lse)
+    for S in (0, 8):
+        a, b_ = outs[S], outs[1]
+        assert torch.all((a[0].float() - b_[0].float()).abs() <= 2e-2 + 2e-2 * b_[0].float().abs())
+        assert torch.all((a[1] - b_[1]).abs() <= 2e-3)
+    assert torch.equal(outs[BAL][0].view(torch.int16), outs[0][0].view(torch.int16))  # AUTO = balanced
+
+
+@pytest.mark.parametrize("lens", [[(i * 613) % 3500 + 1 for i in range(30)] + [0, 3], [700, 2, 0, 3000, 64]])
+def test_multi_two_phases_equal_paged_decode(B, lens):
+    """Balanced mode with several query tokens: partition + finish equals
+    paged_decode bitwise, whether paged_decode merges in place (32 sequences) or
+    not (5 sequences)."""
+    w = wl.custom_workload(len(lens), 32, 8, 128, 64, lens, "bf16", seed=313, q_len=4, causal=True)
+    t = dev(w)
+    ref_out, ref_lse = run(B, w, BAL, t)
+    dims = B.dims_for(t["q"], t["k"], t["bt"], causal=True)
+    nbytes = B.paged_decode_workspace_bytes(dims, BAL)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:-1], dtype=torch.float32, device="cuda")
+    h = B.current_stream_handle(0)
+    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, BAL,
+                                    ws, nbytes, h) == 0
+    assert B.paged_decode_finish(dims, BAL, ws, nbytes, out, lse, h) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse.cpu().view(torch.int32), ref_lse.view(torch.int32))
+    check(out.cpu(), lse.cpu(), *oracle_full(w), what="multi two phases")
