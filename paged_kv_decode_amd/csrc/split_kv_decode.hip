@@ -17,561 +17,12 @@
 //    latency chain (lengths -> block table -> first K/V) is paid once per wave
 //    rather than once per split.
 //
-// Per tile of TT tokens a wave:
-//   1. resolves the page of every row through the block table (per-token
-//      lookup as in the AstrAI commit log's unified paged path; with page_size
-//      a multiple of 16 one lookup per 16-token group suffices),
-//   2. has issued the tile's 16-byte K/V loads one tile earlier (register
-//      double buffering: the next tile's loads are in flight while this one
-//      computes),
-//   3. writes V row-major into a wave-private LDS tile,
-//   4. QK^T on MFMA (v_mfma_f32_16x16x32_bf16): A = 16 K rows x 32 dims straight
-//      from the load registers, B = the packed query heads (zero-padded to 16),
-//   5. online softmax in base 2 with the running max shared across the four
-//      lane groups by cross-lane xor shuffles,
-//   6. PV on MFMA: A = V^T gathered by transposing LDS reads
-//      (ds_read_b64_tr_b16), B = P^T taken from the QK accumulator registers
-//      without any shuffle (token order inside each 32-token chunk is permuted
-//      so that the QK output layout is already the PV operand layout).
-//
-// Rows past the end of a range are clamped to the last valid row for
-// addressing (so no page past the sequence and no tail slot is ever read) and
-// masked to -inf by selection.  An empty range writes o = 0 and lse = -inf.
-//
-// Several query tokens per sequence (speculative verify / extend, q_len > 1):
-// the q_len * G query rows of one KV head are packed 16 to an MFMA N dimension
-// exactly like G query heads, packed row r being query token r / G of head
-// kvh * G + r % G, so every K/V row read still serves all of them.  Under the
-// causal mask query token i of a length-L sequence sees positions
-// <= L - q_len + i (the position of that token), so each lane, which holds one
-// packed row, masks scores at its own end; a row that sees no token of a tile
-// or of a whole range keeps m = -inf and contributes nothing.
-#include "merge_row.hpp"
-#include "pkd_internal.hpp"
+// The per-tile machinery (loads, MFMA tile step, pipeline, combine) is in
+// wave_attn.hpp.
+#include "wave_attn.hpp"
 
 namespace pkd {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-template <int BYTES> struct VecT;
-template <> struct VecT<16> { typedef u32x4 T; };
-template <> struct VecT<8> { typedef u32x2 T; };
-
-// Compile-time shape of one (head_dim, kv dtype) instance.
-template <int D, bool FP8>
-struct Cfg {
-  static constexpr int ELEM = FP8 ? 1 : 2;                 // bytes per cached element
-  static constexpr int ROWB = D * ELEM;                    // bytes of one token's row for one KV head
-  // Tokens per wave tile: 4096 / D (8 KiB of K and 8 KiB of V for bf16, half
-  // that for fp8), which keeps two tiles of loads per wave within registers.
-  static constexpr int TT = 4096 / D;
-  static constexpr int NBLK = TT / 16;                     // QK MFMA row blocks per tile
-  static constexpr int KP = TT >= 32 ? 32 : 16;            // tokens per PV MFMA (its K depth)
-  static constexpr int NCH = TT / KP;                      // PV chunks per tile
-  static constexpr int PIECE = (FP8 && D >= 64) ? 16 : 8;  // dims per lane per K load
-  static constexpr int KLB = PIECE * ELEM;                 // K load bytes (16, or 8 for fp8 D=32)
-  static constexpr int NPIECE = D / (4 * PIECE);           // K loads per lane per row block
-  static constexpr int R = PIECE / 8;                      // QK MFMAs fed by one K load
-  static constexpr int KK = D / 32;                        // QK MFMAs per row block
-  static constexpr int VLB = ROWB >= 64 ? 16 : 8;          // V load bytes
-  static constexpr int VEPL = VLB / ELEM;                  // elements per V load
-  static constexpr int CPR = ROWB / VLB;                   // V loads per row
-  static constexpr int RPI = 64 / CPR;                     // rows per V load instruction (<= 16)
-  static constexpr int NV = TT * ROWB / (64 * VLB);        // V loads per lane per tile
-  static constexpr int VS = D + 16;                        // V tile LDS row stride (bf16 elements)
-  static constexpr int NB = D / 16;                        // PV output blocks of 16 dims
-  static constexpr int NGRP = TT / 16;                     // 16-token groups per tile
-  static constexpr int VT_BYTES = kWaves * TT * VS * 2;
-  static constexpr int BT_OFFSET = VT_BYTES;                // staged block-table entries
-  static constexpr int BT_ENTRIES = 512;
-  static constexpr int OW_STRIDE = D + 4;                  // merge staging row stride (floats)
-  static constexpr int MERGE_BYTES = kWaves * 16 * (2 + OW_STRIDE) * 4 + 16 * (kWaves + 4) * 4;
-  static constexpr int LOOP_BYTES = VT_BYTES + BT_ENTRIES * 4;
-  static constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
-  static_assert(KK == NPIECE * R, "K pieces must feed whole MFMAs");
-  static_assert(RPI <= 16 && 16 % RPI == 0, "a V load instruction must stay in one 16-row group");
-  static_assert(NV * 64 * VLB == TT * ROWB, "V loads must tile the rows exactly");
-  static_assert(LDS_BYTES <= 81920 + BT_ENTRIES * 4, "LDS budget");
-};
-
-typedef typename VecT<16>::T Ld16;
-
-template <typename To, typename From>
-__device__ __forceinline__ To bit_cast_dev(const From& f) {
-  static_assert(sizeof(To) == sizeof(From), "size mismatch");
-  To t;
-  __builtin_memcpy(&t, &f, sizeof(To));
-  return t;
-}
-
-// V rows are streamed exactly once, each load instruction covering whole
-// rows: non-temporal loads keep them from displacing reusable lines in L2 and
-// the Infinity Cache.
-template <int BYTES>
-__device__ __forceinline__ typename VecT<BYTES>::T gload(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const typename VecT<BYTES>::T*>(p));
-}
-
-// K loads are laid out for the MFMA A operand: one instruction reads 16 rows,
-// 4 lanes x 16 bytes of each, so every 128-byte line of a row is requested by
-// two consecutive instructions.  They are ordinary cached loads so that the
-// second request hits in the vector L1; streamed non-temporally, both went to
-// L2 and the step ran 3-6% slower (K streams at some row offsets 20-30% slower).
-template <int BYTES>
-__device__ __forceinline__ typename VecT<BYTES>::T kload(const uint8_t* p) {
-  return *reinterpret_cast<const typename VecT<BYTES>::T*>(p);
-}
-
-// Wave-local LDS ordering: all of this wave's LDS writes have landed before any
-// later LDS read of another lane's data, and the compiler does not move LDS
-// accesses across this point.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// result lane i, element r is element i % 4 of the 8 bytes that lane 4r + i/4
-// addressed.  So if lane k of a group addresses row r0 + k/4, columns
-// c0 + 4(k%4) .. +3 of a row-major bf16 tile, lane i receives column c0 + i of
-// rows r0 .. r0 + 3.
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-}
-
-// 8 fp8 E4M3FN codes (two dwords) -> 8 bf16 (exact: every E4M3 value is a bf16 value).
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 c) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, true);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, false);
-  bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, true);
-  bf16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = d[0]; r[5] = d[1]; r[6] = e[0]; r[7] = e[1];
-  return r;
-}
-
-// Row tokens.  Inside each 32-token chunk c, QK row block 2c+h, MFMA row r holds
-// token 32c + 8*(r/4) + 4h + r%4.  Then QK output lane group g, register i holds
-// token 32c + 8g + 4h + i, which is exactly element 4h+i of the 8-token P^T
-// operand lane group g needs for PV over tokens 32c + 8g .. 32c + 8g + 7.
-template <int KP>
-__device__ __forceinline__ int k_row_token(int blk, int r) {
-  if constexpr (KP == 32) {
-    return 32 * (blk >> 1) + 8 * (r >> 2) + 4 * (blk & 1) + (r & 3);
-  } else {
-    return 16 * blk + r;
-  }
-}
-template <int KP>
-__device__ __forceinline__ int s_out_token(int blk, int g, int i) {
-  if constexpr (KP == 32) {
-    return 32 * (blk >> 1) + 8 * g + 4 * (blk & 1) + i;
-  } else {
-    return 16 * blk + 4 * g + i;
-  }
-}
-
-template <int D, bool FP8>
-struct TileRegs {
-  typedef Cfg<D, FP8> C;
-  typename VecT<C::KLB>::T k[C::NBLK][C::NPIECE];
-  typename VecT<C::VLB>::T v[C::NV];
-};
-
-// Block-table entries of one tile, fetched one tile before they are used so
-// that address computation never waits on a block-table read.
-template <int D, bool FP8, bool PAGED16>
-struct TilePages {
-  typedef Cfg<D, FP8> C;
-  int pg[PAGED16 ? C::NGRP : C::NBLK + C::NV];  // PAGED16: per 16-token group; else per K / V row
-};
-
-
-// Per-wave attention state and tile operations, shared by both launch shapes.
-// Lane (n, g) = (lane % 16, lane / 16) in the MFMA operand layouts.
-template <int D, bool FP8>
-struct WaveAttn {
-  typedef Cfg<D, FP8> C;
-  typedef TileRegs<D, FP8> Regs;
-
-  int lane, n, g;
-  int k_rig[C::NBLK];  // position of this lane's K row (of each row block) inside its 16-token group
-  int v_rig;           // + (i * RPI) % 16: position of this lane's row of V load i
-  int k_doff, v_doff;  // byte offsets of this lane's K dims / V chunk inside a row
-  bf16x8 qf[C::KK];    // query heads as the B operand of QK^T
-  float qk_scale;      // scale * log2(e) (* k_scale for fp8)
-  float m_run;         // running max (base-2 units) of head n, equal in all lane groups
-  float l_run;         // this lane's partial sum of exp2(s - m_run) for head n
-  f32x4 acc[C::NB];    // O^T: acc[nb][i] = out[head n][16 nb + 4 g + i] (unnormalised)
-
-  __device__ __forceinline__ void init_lane(int lane_) {
-    lane = lane_;
-    n = lane & 15;
-    g = lane >> 4;
-#pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk) k_rig[blk] = k_row_token<C::KP>(blk, n) & 15;
-    v_rig = lane / C::CPR;
-    k_doff = g * C::PIECE * C::ELEM;
-    v_doff = (lane % C::CPR) * C::VLB;
-  }
-
-  // Lane (n, g) holds packed row n's dims (kk / R) * 4 * PIECE + g * PIECE + (kk % R) * 8 + [0, 8)
-  // for MFMA kk; the K loads use the same dim assignment.  qrow_n is the memory
-  // row of packed row n (any valid row when hv is false); rows past the group are zero.
-  __device__ __forceinline__ void load_q(const uint16_t* q, int64_t qrow_n, bool hv) {
-    const uint16_t* qrow = q + qrow_n * D;
-#pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) {
-      const int d0 = (kk / C::R) * 4 * C::PIECE + g * C::PIECE + (kk % C::R) * 8;
-      Ld16 raw = *reinterpret_cast<const Ld16*>(qrow + d0);
-      if (!hv) raw = Ld16{0, 0, 0, 0};
-      qf[kk] = bit_cast_dev<bf16x8>(raw);
-    }
-  }
-
-  __device__ __forceinline__ void reset() {
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // Issue every K and V load of the tile starting at token tb (a multiple of
-  // 16).  pages[q] is the physical page of the tile's 16-token group q (every
-  // aligned group lies in one page when page_size % 16 == 0); a row past lim is
-  // replaced by a valid row of its group (position min(pos, lim - group start))
-  // and masked later.
-  // idle: read the same rows of physical page 0 instead (shared by every
-  // workgroup, so they come from cache); the data is not used.
-  __device__ __forceinline__ void issue_paged16(const uint8_t* kc, const uint8_t* vc, int tb, int lim,
-                                                const int* pages, int ps, int tok_stride,
-                                                int64_t head_off, Regs& R, bool idle) const {
-    int64_t gbase[C::NGRP];
-    int glim[C::NGRP];
-#pragma unroll
-    for (int q = 0; q < C::NGRP; ++q) {
-      const int gt = min(tb + 16 * q, lim) & ~15;
-      const int page = idle ? 0 : __builtin_amdgcn_readfirstlane(pages[q]);
-      gbase[q] = ((int64_t)page * ps + (gt - (gt / ps) * ps)) * tok_stride + head_off;
-      glim[q] = lim - gt;
-    }
-#pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk) {
-      int64_t base;
-      int gl;
-      if constexpr (C::KP == 32) {
-        // The two halves of a 32-token row block come from groups 2c and 2c+1.
-        const int q0 = 2 * (blk >> 1);
-        const bool hi = (k_row_token<C::KP>(blk, n) >> 4) != q0;
-        base = hi ? gbase[q0 + 1] : gbase[q0];
-        gl = hi ? glim[q0 + 1] : glim[q0];
-      } else {
-        base = gbase[blk];
-        gl = glim[blk];
-      }
-      const uint8_t* src = kc + base + min(k_rig[blk], gl) * tok_stride + k_doff;
-#pragma unroll
-      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = kload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
-    }
-#pragma unroll
-    for (int i = 0; i < C::NV; ++i) {
-      const int q = (i * C::RPI) >> 4;
-      const int rig = ((i * C::RPI) & 15) + v_rig;
-      R.v[i] = gload<C::VLB>(vc + gbase[q] + min(rig, glim[q]) * tok_stride + v_doff);
-    }
-  }
-
-  // Any page size: pages[blk] is the page of this lane's K row of row block
-  // blk, pages[NBLK + i] that of its row of V load i (rows clamped to lim).
-  __device__ __forceinline__ void issue_generic(const uint8_t* kc, const uint8_t* vc, int tb, int lim,
-                                                const int* pages, int ps, int tok_stride,
-                                                int64_t head_off, Regs& R, bool idle) const {
-#pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk) {
-      const int tok = min(tb + k_row_token<C::KP>(blk, n), lim);
-      const int64_t off = ((int64_t)(idle ? 0 : pages[blk]) * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
-      const uint8_t* src = kc + off + k_doff;
-#pragma unroll
-      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = kload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
-    }
-#pragma unroll
-    for (int i = 0; i < C::NV; ++i) {
-      const int tok = min(tb + i * C::RPI + v_rig, lim);
-      const int64_t off =
-          ((int64_t)(idle ? 0 : pages[C::NBLK + i]) * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
-      R.v[i] = gload<C::VLB>(vc + off + v_doff);
-    }
-  }
-
-  // Tokens (relative to tb) whose pages the generic path needs, per lane.
-  __device__ __forceinline__ int generic_row(int idx) const {
-    return idx < C::NBLK ? k_row_token<C::KP>(idx, n) : (idx - C::NBLK) * C::RPI + v_rig;
-  }
-
-  // One tile: V to LDS, QK^T, online softmax, PV.  Tokens at or past s1 (this
-  // lane's packed row's end) are masked.
-  __device__ __forceinline__ void process(const Regs& R, int tb, int s1, uint16_t* vs) {
-    // V -> LDS, row-major bf16 (16-byte writes).
-#pragma unroll
-    for (int i = 0; i < C::NV; ++i) {
-      const int lin = i * 64 + lane;
-      uint16_t* dst = vs + (lin / C::CPR) * C::VS + (lin % C::CPR) * C::VEPL;
-      if constexpr (FP8) {
-#pragma unroll
-        for (int h = 0; h < C::VEPL / 8; ++h) {
-          u32x2 c8;
-          c8[0] = R.v[i][2 * h];
-          c8[1] = R.v[i][2 * h + 1];
-          *reinterpret_cast<bf16x8*>(dst + 8 * h) = fp8x8_to_bf16(c8);
-        }
-      } else {
-        *reinterpret_cast<u32x4*>(dst) = R.v[i];
-      }
-    }
-
-    // S^T = K Q^T for each 16-row block.
-    f32x4 sacc[C::NBLK];
-#pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk) {
-      sacc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        bf16x8 a;
-        if constexpr (FP8) {
-          const auto& raw = R.k[blk][kk / C::R];
-          u32x2 c8;
-          c8[0] = raw[2 * (kk % C::R)];
-          c8[1] = raw[2 * (kk % C::R) + 1];
-          a = fp8x8_to_bf16(c8);
-        } else {
-          a = bit_cast_dev<bf16x8>(R.k[blk][kk]);
-        }
-        sacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc[blk], 0, 0, 0);
-      }
-    }
-
-    // Online softmax (base 2).  Lane (n, g) holds scores of head n for tokens
-    // s_out_token(blk, g, i).
-    float mt = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = tb + s_out_token<C::KP>(blk, g, i);
-        const float x = sacc[blk][i] * qk_scale;
-        sacc[blk][i] = tok < s1 ? x : -INFINITY;
-        mt = fmaxf(mt, sacc[blk][i]);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    // A row that has seen no unmasked token keeps m = -inf; subtracting 0 then
-    // gives alpha = 0 and e = 0 instead of NaN.
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(sacc[blk][i] - m_use);
-        sacc[blk][i] = e;
-        psum += e;
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) acc[nb] *= alpha;
-
-    wave_lds_sync();  // the V tile is complete in LDS
-
-    // O^T += V^T P^T; the V^T operand comes from transposing LDS reads.
-    if constexpr (C::KP == 32) {
-#pragma unroll
-      for (int c = 0; c < C::NCH; ++c) {
-        bf16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = (__bf16)sacc[2 * c][i];
-          pb[4 + i] = (__bf16)sacc[2 * c + 1][i];
-        }
-        // lane (n, g) needs V[32c + 8g + j][16 nb + n], j = 0..7
-        const uint16_t* rowp = vs + (32 * c + 8 * g + (n >> 2)) * C::VS + 4 * (n & 3);
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          const s16x4 lo = lds_read_tr16(rowp + 16 * nb);
-          const s16x4 hi = lds_read_tr16(rowp + 4 * C::VS + 16 * nb);
-          s16x4 both[2] = {lo, hi};
-          const bf16x8 a = bit_cast_dev<bf16x8>(both);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[nb], 0, 0, 0);
-        }
-      }
-    } else {
-      bf16x4 pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = (__bf16)sacc[0][i];
-      const s16x4 pbs = bit_cast_dev<s16x4>(pb);
-      // lane (n, g) needs V[4g + j][16 nb + n], j = 0..3
-      const uint16_t* rowp = vs + (4 * g + (n >> 2)) * C::VS + 4 * (n & 3);
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const s16x4 a = lds_read_tr16(rowp + 16 * nb);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pbs, acc[nb], 0, 0, 0);
-      }
-    }
-    wave_lds_sync();  // PV reads done before the next tile overwrites the V tile
-  }
-
-  // Sum of l over the four lane groups (every lane of head n gets it).
-  __device__ __forceinline__ float l_total() const {
-    const float l = l_run + __shfl_xor(l_run, 16);
-    return l + __shfl_xor(l, 32);
-  }
-};
-
-// Memory row ((b * q_len + i) * Hq + h) of packed row r of KV head kvh of
-// sequence b: query token i = r / G, head h = kvh * G + r % G.
-__device__ __forceinline__ int64_t packed_row(int b, int kvh, int r, int q_len, int hq, int group) {
-  const int i = r / group;
-  return ((int64_t)b * q_len + i) * hq + kvh * group + (r - i * group);
-}
-
-// Per lane (packed row n = lane % 16 of head group hg): the memory row of its
-// query (a valid row even past the group), whether the row exists, and the end
-// of the tokens it sees within [.., s1): s1, or under the causal mask
-// min(s1, L - q_len + i + 1) for query token i.
-struct LaneRow {
-  int64_t row;
-  bool valid;
-  int end;
-};
-template <typename P>
-__device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, int n, int L, int s1) {
-  const int r = hg * kHeadsPerGroup + n;
-  LaneRow lr;
-  lr.valid = r < p.rows_kv;
-  const int rr = lr.valid ? r : hg * kHeadsPerGroup;
-  lr.row = packed_row(b, kvh, rr, p.q_len, p.hq, p.group);
-  lr.end = p.causal ? min(s1, L - p.q_len + rr / p.group + 1) : s1;
-  return lr;
-}
-
-// Tiles first, first + step, ... (< ntiles): while tile t is processed the
-// next tile's K/V loads are in flight and the page entries of the tile after
-// that are being read.  After the last tile the "next" loads stay in the
-// instruction stream (so the wait counts are the same on every iteration) but
-// are pointed at rows every workgroup shares by passing idle = true; they are
-// never consumed.
-template <int D, bool FP8, typename Pages, typename Fetch, typename Issue>
-__device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int step, int ntiles, int s0,
-                                          int s1, uint16_t* vs, Fetch fetch, Issue issue) {
-  typedef Cfg<D, FP8> C;
-  if (first >= ntiles) return;
-  auto nxt = [&](int t) { return t + step < ntiles ? t + step : t; };
-  TileRegs<D, FP8> ra, rb;
-  Pages pa, pb;
-  int t = first;
-  fetch(t, pa);
-  issue(t, pa, ra, false);
-  int t1 = nxt(t);
-  fetch(t1, pb);
-  while (true) {
-    issue(t1, pb, rb, t1 == t);
-    int t2 = nxt(t1);
-    fetch(t2, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    A.process(ra, s0 + t * C::TT, s1, vs);
-    if (t1 == t) break;
-    t = t1;
-    t1 = t2;
-    issue(t1, pa, ra, t1 == t);
-    t2 = nxt(t1);
-    fetch(t2, pb);
-    __builtin_amdgcn_sched_barrier(0);
-    A.process(rb, s0 + t * C::TT, s1, vs);
-    if (t1 == t) break;
-    t = t1;
-    t1 = t2;
-  }
-}
-
-// Combine the waves' (m, l, O) of one workgroup in LDS (smem must hold
-// NWV * 16 * (2 + OW_STRIDE) * 4 + 16 * (NWV + 4) * 4 bytes) and hand every
-// row of the group to store, four dims at a time: store(hh, d0, o4, lse_nat),
-// o4 = dims d0 .. d0 + 3 of o = sum_w e_w O_w * vsc / sum_w e_w l_w with
-// e_w = 2^(m_w - max m), and the natural-log LSE.  A row that saw no token in
-// any wave gets o = 0 and lse = -inf.  The per-row weights e_w * vsc / den are
-// computed once per row, then each element is a short weighted sum of the
-// staged wave rows.  Ends with the LDS still in use: synchronise before
-// reusing it.
-template <int D, bool FP8, int NWV = kWaves, typename Store>
-__device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* smem, int wave, int tid,
-                                           int heads_here, float vsc, Store store) {
-  typedef Cfg<D, FP8> C;
-  constexpr int RWS = NWV + 4;                 // per-row table stride (floats): NWV weights, then the LSE
-  const float l_tot = A.l_total();
-  __syncthreads();
-  float* mw = reinterpret_cast<float*>(smem);  // [NWV][16]
-  float* lw = mw + NWV * 16;                   // [NWV][16]
-  float* ow = lw + NWV * 16;                   // [NWV][16][OW_STRIDE]
-  float* rw = ow + NWV * 16 * C::OW_STRIDE;    // [16][RWS]
-  if (A.g == 0) {
-    mw[wave * 16 + A.n] = A.m_run;
-    lw[wave * 16 + A.n] = l_tot;
-  }
-#pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
-    *reinterpret_cast<f32x4*>(ow + (wave * 16 + A.n) * C::OW_STRIDE + 16 * nb + 4 * A.g) = A.acc[nb];
-  __syncthreads();
-  if (tid < heads_here) {
-    const int hh = tid;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) M = fmaxf(M, mw[w * 16 + hh]);
-    const float M_use = M == -INFINITY ? 0.f : M;
-    float e[NWV];
-    float den = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      e[w] = __builtin_amdgcn_exp2f(mw[w * 16 + hh] - M_use);
-      den += e[w] * lw[w * 16 + hh];
-    }
-    const float sc = den > 0.f ? vsc / den : 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) rw[hh * RWS + w] = e[w] * sc;
-    rw[hh * RWS + NWV] = (M_use + log2f(den)) * 0.69314718055994530942f;
-  }
-  __syncthreads();
-  constexpr int Q4 = D / 4;
-  for (int idx = tid; idx < heads_here * Q4; idx += NWV * 64) {
-    const int hh = idx / Q4, d0 = (idx - hh * Q4) * 4;
-    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NWV; ++w)
-      o += rw[hh * RWS + w] * *reinterpret_cast<const f32x4*>(ow + (w * 16 + hh) * C::OW_STRIDE + d0);
-    store(hh, d0, o, rw[hh * RWS + NWV]);
-  }
-}
-
-// Four fp32 values rounded to bf16 (round-to-nearest-even), as one 8-byte word.
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 o) {
-  bf16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (__bf16)o[i];
-  return r;
-}
 
 // Waves per SIMD the register allocation targets.  Two resident waves per
 // SIMD hide the load latency of one another's tiles; the compiler keeps the
