@@ -600,3 +600,39 @@ def test_multi_two_phases_equal_paged_decode(B, lens):
     assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.cpu().view(torch.int32), ref_lse.view(torch.int32))
     check(out.cpu(), lse.cpu(), *oracle_full(w), what="multi two phases")
+
+
+# ---- balanced mode: more segment and piece structures --------------------------
+
+BALANCED_CASES = [
+    # (B, Hq, Hkv, D, ps, seq_lens, seed): what the case exercises
+    (8, 32, 8, 128, 64, [0, 1, 15, 16, 17, 700, 0, 3000], 401),                  # edge lengths, merge kernel
+    (40, 32, 8, 64, 16, [(i * 977) % 500 + 1 for i in range(36)] + [0] * 4, 402),  # in-place merge
+    (4, 128, 4, 128, 16, [33, 1000, 0, 5], 403),                                   # G = 32: two head groups
+    (34, 16, 16, 32, 32, [(i * 331) % 900 + 1 for i in range(34)], 404),           # G = 1 at 16 KV heads
+    (1, 64, 8, 128, 16, [100000], 405),                                            # one sequence over all workgroups
+    (32, 32, 8, 128, 64, [60000] + [16] * 31, 406),                                # in place, > 8 partials per row
+]
+
+
+@pytest.mark.parametrize("case", BALANCED_CASES)
+def test_balanced_structures_parity(B, case):
+    bq, hq, hkv, d, ps, lens, seed = case
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, "bf16", seed)
+    ref = oracle_full(w)
+    t = dev(w)
+    out, lse = run(B, w, BAL, t)
+    check(out, lse, *ref, what=f"balanced {case[:5]}")
+    # the two phases give the same bits as paged_decode
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    nbytes = B.paged_decode_workspace_bytes(dims, BAL)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(t["q"])
+    l2 = torch.empty(t["q"].shape[:-1], dtype=torch.float32, device="cuda")
+    h = B.current_stream_handle(0)
+    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, BAL,
+                                    ws, nbytes, h) == 0
+    assert B.paged_decode_finish(dims, BAL, ws, nbytes, o2, l2, h) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu().view(torch.int16), out.view(torch.int16))
+    assert torch.equal(l2.cpu().view(torch.int32), lse.view(torch.int32))
