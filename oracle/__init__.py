@@ -60,6 +60,12 @@ def lib():
         L.pkd_oracle_bf16_value.restype = _c_double
         L.pkd_oracle_fp8e4m3_value.argtypes = [ctypes.c_uint8]
         L.pkd_oracle_fp8e4m3_value.restype = _c_double
+        L.pkd_oracle_fp8e4m3_encode.argtypes = [ctypes.c_float]
+        L.pkd_oracle_fp8e4m3_encode.restype = ctypes.c_uint8
+        L.pkd_oracle_bf16_round.argtypes = [ctypes.c_float]
+        L.pkd_oracle_bf16_round.restype = ctypes.c_uint16
+        L.pkd_oracle_kv_append.argtypes = [_c_int] * 5 + [ctypes.c_int64] + [_p] * 5 + [_c_int] + [_p] * 4
+        L.pkd_oracle_kv_append.restype = _c_int
         _lib = L
     return _lib
 
@@ -212,6 +218,42 @@ def lse_merge(o_part, lse_part):
     lse = np.empty((R,), np.float64)
     lib().pkd_oracle_lse_merge(R, S, D, _ptr(o), _ptr(l), _ptr(out), _ptr(lse))
     return out, lse
+
+
+def fp8e4m3_encode(x: float) -> int:
+    """E4M3FN code of an fp32 value within [-448, 448]: nearest, ties to the even code."""
+    return int(lib().pkd_oracle_fp8e4m3_encode(float(x)))
+
+
+def bf16_round(x: float) -> int:
+    """bf16 bits of an fp32 value, round to nearest even."""
+    return int(lib().pkd_oracle_bf16_round(float(x)))
+
+
+def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, positions=None,
+              cos_sin=None):
+    """Paged KV append (see paged_attention_ref.c).  k_new, v_new: bf16 [N, Hkv, D];
+    slot_mapping: int64 [N]; k_cache, v_cache: [num_pages, ps, Hkv, D] bf16 or float8_e4m3fn
+    (not modified); optional RoPE: positions int64 [N] and cos_sin float32 [max_position, D].
+    Returns the updated caches as raw numpy arrays (uint16 bf16 bits or uint8 FP8 codes)."""
+    kv_fp8 = (k_cache.element_size() if hasattr(k_cache, "element_size") else np.asarray(k_cache).dtype.itemsize) == 1
+    kn = _raw(k_new, np.uint16)
+    vn = _raw(v_new, np.uint16)
+    n, hkv, d = kn.shape
+    assert vn.shape == kn.shape
+    kc = _raw(k_cache, np.uint8 if kv_fp8 else np.uint16).copy()
+    vc = _raw(v_cache, np.uint8 if kv_fp8 else np.uint16).copy()
+    num_pages, ps, hkv2, d2 = kc.shape
+    assert (hkv2, d2) == (hkv, d) and vc.shape == kc.shape
+    sm = _raw(slot_mapping, np.int64)
+    pos = None if positions is None else _raw(positions, np.int64)
+    cs = None if cos_sin is None else _raw(cos_sin, np.float32)
+    max_pos = 0 if cs is None else cs.shape[0]
+    ks = _raw(k_scale, np.float32)
+    vs = _raw(v_scale, np.float32)
+    _check(lib().pkd_oracle_kv_append(hkv, d, ps, num_pages, 1 if kv_fp8 else 0, n, _ptr(kn), _ptr(vn), _ptr(sm),
+                                      _ptr(pos), _ptr(cs), max_pos, _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs)))
+    return kc, vc
 
 
 def bf16_value(bits: int) -> float:

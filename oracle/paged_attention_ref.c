@@ -49,6 +49,9 @@
  * definition above over its visible tokens.  q_len = 1 without the mask is the
  * single-token decode.
  *
+ * The file also defines the paged KV append that fills the cache (row f2,
+ * pkd_oracle_kv_append, at the end).
+ *
  * Work is spread over an optional pthread pool by (sequence, KV head) items.
  * The items are independent and each is computed in a fixed order, so the
  * result is bitwise identical for any thread count.
@@ -440,5 +443,116 @@ int pkd_oracle_paged_decode_ranges(int batch, int hq, int hkv, int head_dim, int
           attend_range(&P, b, 0, h, t0, t1, out + ((int64_t)b * hq + h) * head_dim, s);
     free(s);
   }
+  return PKD_ORACLE_OK;
+}
+
+/* ---- paged KV append (row f2) -------------------------------------------------
+ *
+ * Writing new K/V rows into the paged cache: the step before decode, which the
+ * sglang fuse/overlap catalogue lists as fused FP8 quantisation + paged K/V
+ * cache write (section 1, the TRTLLM FP8 KV row) and as RoPE fused with the KV
+ * cache store (section 1; section 14, the vLLM rope + cache rows).  Token n's
+ * rows k_new[n][h][:], v_new[n][h][:] (bf16) go to slot slot_mapping[n] of the
+ * pool, i.e. page slot / page_size, position slot % page_size; a slot outside
+ * [0, num_pages * page_size) (padding tokens use -1) writes nothing.  With a
+ * RoPE table, K is first rotated in the NeoX "rotate half" form: for d < D/2,
+ * with c = cos_sin[pos][d] and s = cos_sin[pos][D/2 + d],
+ *     k'[d]       = k[d] c - k[d + D/2] s
+ *     k'[d + D/2] = k[d + D/2] c + k[d] s
+ * (a position outside [0, max_position) writes nothing).  The cache value is
+ * then k' rounded to bf16, or for an FP8 cache the E4M3FN code of
+ * clamp(k' / scale[h], -448, 448), rounded to nearest, ties to the even code.
+ *
+ * Unlike the attention definition above, these steps are carried out in fp32
+ * exactly as written, because they end in a rounding to a code: the GPU kernel
+ * takes the same decisions in the same precision (products rounded to fp32,
+ * then one fused multiply-add, then an fp32 division by the scale), so that
+ * the codes can be compared bit for bit.
+ */
+
+/* bf16 bits of an fp32 value, round to nearest even (finite inputs). */
+uint16_t pkd_oracle_bf16_round(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* E4M3FN code of x (|x| <= 448 after the caller's clamp): the nearest finite
+ * code by the decoder above, ties to the even code; the sign bit from x. */
+uint8_t pkd_oracle_fp8e4m3_encode(float x) {
+  const int neg = signbit(x) != 0;
+  const double a = fabs((double)x);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) { /* 0x7F is NaN */
+    const double err = fabs(pkd_oracle_fp8e4m3_value((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(best | (neg ? 0x80 : 0));
+}
+
+/* A bf16 value as fp32 (exact: every bf16 value is an fp32 value). */
+static float bf16_float(uint16_t bits) { return (float)pkd_oracle_bf16_value(bits); }
+
+static void store_row(int kv_fp8, void* cache, int64_t elem0, const float* y, int D, float scale) {
+  if (kv_fp8) {
+    uint8_t* c = (uint8_t*)cache;
+    for (int d = 0; d < D; ++d) {
+      float q = y[d] / scale;
+      if (q > 448.0f) q = 448.0f;
+      if (q < -448.0f) q = -448.0f;
+      c[elem0 + d] = pkd_oracle_fp8e4m3_encode(q);
+    }
+  } else {
+    uint16_t* c = (uint16_t*)cache;
+    for (int d = 0; d < D; ++d) c[elem0 + d] = pkd_oracle_bf16_round(y[d]);
+  }
+}
+
+/* k_new, v_new: bf16 bits [n_tokens][hkv][head_dim]; slot_mapping [n_tokens];
+ * positions [n_tokens] and cos_sin [max_position][head_dim] fp32, or both NULL
+ * for no RoPE; k_cache / v_cache [num_pages][page_size][hkv][head_dim] of bf16
+ * bits or FP8 codes, updated in place; k_scale / v_scale [hkv] for FP8. */
+int pkd_oracle_kv_append(int hkv, int head_dim, int page_size, int num_pages, int kv_fp8, int64_t n_tokens,
+                         const uint16_t* k_new, const uint16_t* v_new, const int64_t* slot_mapping,
+                         const int64_t* positions, const float* cos_sin, int max_position, void* k_cache,
+                         void* v_cache, const float* k_scale, const float* v_scale) {
+  const int D = head_dim;
+  if (hkv < 1 || D < 2 || D % 2 != 0 || page_size < 1 || num_pages < 0 || n_tokens < 0 || !k_new || !v_new ||
+      !slot_mapping || !k_cache || !v_cache || ((positions == NULL) != (cos_sin == NULL)))
+    return PKD_ORACLE_BAD_ARG;
+  if (kv_fp8 && (!k_scale || !v_scale)) return PKD_ORACLE_BAD_ARG;
+  float* y = (float*)malloc(sizeof(float) * (size_t)D);
+  if (!y) return PKD_ORACLE_NO_MEM;
+  const int64_t capacity = (int64_t)num_pages * page_size;
+  for (int64_t n = 0; n < n_tokens; ++n) {
+    const int64_t slot = slot_mapping[n];
+    if (slot < 0 || slot >= capacity) continue;
+    const int64_t pos = positions ? positions[n] : 0;
+    if (positions && (pos < 0 || pos >= max_position)) continue;
+    for (int h = 0; h < hkv; ++h) {
+      const int64_t src = (n * hkv + h) * (int64_t)D;
+      const int64_t dst = (slot * hkv + h) * (int64_t)D;  /* page * ps + position, then head */
+      for (int d = 0; d < D; ++d) y[d] = bf16_float(k_new[src + d]);
+      if (positions) {
+        const float* cs = cos_sin + pos * (int64_t)D;
+        for (int d = 0; d < D / 2; ++d) {
+          const float x0 = bf16_float(k_new[src + d]), x1 = bf16_float(k_new[src + d + D / 2]);
+          const float c = cs[d], s = cs[D / 2 + d];
+          const float t0 = x1 * s, t1 = x0 * s;
+          y[d] = fmaf(x0, c, -t0);
+          y[d + D / 2] = fmaf(x1, c, t1);
+        }
+      }
+      store_row(kv_fp8, k_cache, dst, y, D, kv_fp8 ? k_scale[h] : 1.0f);
+      for (int d = 0; d < D; ++d) y[d] = bf16_float(v_new[src + d]);
+      store_row(kv_fp8, v_cache, dst, y, D, kv_fp8 ? v_scale[h] : 1.0f);
+    }
+  }
+  free(y);
   return PKD_ORACLE_OK;
 }

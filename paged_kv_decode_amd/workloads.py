@@ -266,3 +266,64 @@ def as_numpy_bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8).numpy()
     return t.numpy()
+
+
+@dataclasses.dataclass
+class AppendWorkload:
+    """Host tensors of one paged KV append: new K/V rows for N tokens, where they go,
+    optional RoPE inputs, and a cache pool with prior contents."""
+    k_new: torch.Tensor          # [N, Hkv, D] bfloat16
+    v_new: torch.Tensor
+    slot_mapping: torch.Tensor   # [N] int64: page * page_size + position; -1 (padding) and past-the-pool entries
+    positions: Optional[torch.Tensor]  # [N] int64 or None
+    cos_sin: Optional[torch.Tensor]    # [max_position, D] float32: cos of the D/2 angles, then their sin
+    k_cache: torch.Tensor        # [num_pages, ps, Hkv, D] bfloat16 or float8_e4m3fn (prior contents)
+    v_cache: torch.Tensor
+    k_scale: Optional[torch.Tensor]    # [Hkv] float32 (fp8)
+    v_scale: Optional[torch.Tensor]
+
+
+def rope_table(max_position: int, head_dim: int, base: float = 10000.0) -> torch.Tensor:
+    """Standard rotary table: angle p * base^(-2i/D) for i < D/2; cos values, then sin values."""
+    inv = base ** (-torch.arange(0, head_dim // 2, dtype=torch.float64) * 2.0 / head_dim)
+    ang = torch.arange(max_position, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32).contiguous()
+
+
+def append_workload(n_tokens: int, num_kv_heads: int, head_dim: int, page_size: int, num_pages: int,
+                    kv_dtype: str = "bf16", rope: bool = False, seed: int = 0, pad_every: int = 0,
+                    scale_range=(0.002, 0.02)) -> AppendWorkload:
+    """N tokens to distinct random slots of a random pool; every pad_every-th token is padding
+    (slot -1) and one token (if N > 2) points past the pool.  New values are N(0, 1) * 2 in bf16;
+    FP8 scales are drawn per KV head from scale_range, small enough that some values saturate."""
+    g = torch.Generator().manual_seed(seed)
+    capacity = num_pages * page_size
+    assert n_tokens <= capacity
+    slots = torch.randperm(capacity, generator=g)[:n_tokens].to(torch.int64)
+    if pad_every:
+        slots[::pad_every] = -1
+    if n_tokens > 2:
+        slots[1] = capacity + 5
+    k_new = (torch.randn(n_tokens, num_kv_heads, head_dim, generator=g) * 2).to(torch.bfloat16)
+    v_new = (torch.randn(n_tokens, num_kv_heads, head_dim, generator=g) * 2).to(torch.bfloat16)
+    positions = cos_sin = None
+    if rope:
+        max_pos = 4096
+        positions = torch.randint(0, max_pos, (n_tokens,), generator=g, dtype=torch.int64)
+        if n_tokens > 3:
+            positions[2] = max_pos + 1  # outside the table: that token writes nothing
+        cos_sin = rope_table(max_pos, head_dim)
+    shape = (num_pages, page_size, num_kv_heads, head_dim)
+    k_scale = v_scale = None
+    if kv_dtype == "bf16":
+        k_cache = torch.randn(*shape, generator=g).to(torch.bfloat16)
+        v_cache = torch.randn(*shape, generator=g).to(torch.bfloat16)
+    else:
+        lo, hi = scale_range
+        k_scale = (lo + (hi - lo) * torch.rand(num_kv_heads, generator=g)).to(torch.float32)
+        v_scale = (lo + (hi - lo) * torch.rand(num_kv_heads, generator=g)).to(torch.float32)
+        codes = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0  # no NaN codes among the prior contents
+        k_cache = codes.view(torch.float8_e4m3fn)
+        v_cache = torch.randint(0, 126, shape, generator=g, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    return AppendWorkload(k_new, v_new, slots, positions, cos_sin, k_cache, v_cache, k_scale, v_scale)

@@ -5,7 +5,8 @@ the kind a hand-written attention reference can plausibly contain: a wrong
 page or slot index, the wrong KV head for a query head, K and V swapped, the
 softmax scale dropped, a base-2 log-sum-exp, a wrong merge weight, a wrong
 split boundary, a wrong FP8 exponent bias, a wrong cache layout, a causal
-mask off by one or aligned to the wrong end.  The copy is compiled with the
+mask off by one or aligned to the wrong end, and in the KV append a RoPE sign,
+pairing or cos/sin swap, a wrong scale, rounding ties or slot.  The copy is compiled with the
 oracle's own build command and the pin suite
 (test_oracle_pins.py) is run against it in a child process through
 PKD_ORACLE_LIB; every mutant must make at least one pin fail.  A control copy
@@ -88,6 +89,22 @@ MUTANTS = [
      "((uint32_t)bits) << 16;", "((uint32_t)bits) << 15;"),
     ("page_bound_off_by_one",
      "if (p < 0 || p >= P->num_pages)", "if (p < 0 || p > P->num_pages)"),
+    ("append_rope_sign",
+     "y[d] = fmaf(x0, c, -t0);", "y[d] = fmaf(x0, c, t0);"),
+    ("append_rope_adjacent_pairs",
+     "const float x0 = bf16_float(k_new[src + d]), x1 = bf16_float(k_new[src + d + D / 2]);",
+     "const float x0 = bf16_float(k_new[src + d]), x1 = bf16_float(k_new[src + (d ^ 1)]);"),
+    ("append_cos_sin_swapped",
+     "const float c = cs[d], s = cs[D / 2 + d];", "const float c = cs[D / 2 + d], s = cs[d];"),
+    ("append_scale_of_head_zero",
+     "store_row(kv_fp8, k_cache, dst, y, D, kv_fp8 ? k_scale[h] : 1.0f);",
+     "store_row(kv_fp8, k_cache, dst, y, D, kv_fp8 ? k_scale[0] : 1.0f);"),
+    ("fp8_ties_to_odd",
+     "(err == best_err && (c & 1) == 0 && (best & 1) == 1)", "(err == best_err && (c & 1) == 1 && (best & 1) == 0)"),
+    ("bf16_round_truncates",
+     "u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0u;"),
+    ("append_writes_token_row_not_slot",
+     "const int64_t dst = (slot * hkv + h) * (int64_t)D;", "const int64_t dst = ((n % capacity) * hkv + h) * (int64_t)D;"),
 ]
 
 

@@ -6,6 +6,7 @@ of paged decode attention fixes.  Each is chosen so that a plausible slip in the
 oracle (a dropped term, a wrong sign, a wrong page/slot index, a transposed
 operand, the wrong KV head for a query head, a base-2 LSE) fails one of them.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -408,3 +409,152 @@ def test_multi_rows_entry_matches_full_oracle():
                                               w.scale, True, rows, w.k_scale, w.v_scale)
     flat_o, flat_l = out.reshape(-1, 32), lse.reshape(-1)
     assert np.array_equal(o_r, flat_o[rows]) and np.array_equal(l_r, flat_l[rows])
+
+
+# ---- paged KV append (quantised cache write with optional RoPE) -----------------
+
+dataclasses_replace = dataclasses.replace
+
+
+def _append(w, **kw):
+    return oracle.kv_append(w.k_new, w.v_new, w.slot_mapping, w.k_cache, w.v_cache, w.k_scale, w.v_scale,
+                            w.positions, w.cos_sin, **kw)
+
+
+def test_append_bf16_copies_rows_to_their_slots_and_nothing_else():
+    w = wl.append_workload(40, 3, 16, 8, 12, "bf16", seed=301, pad_every=7)
+    kc, vc = _append(w)
+    k0 = wl.as_numpy_bits(w.k_cache).copy()
+    v0 = wl.as_numpy_bits(w.v_cache).copy()
+    ps = 8
+    kn = wl.as_numpy_bits(w.k_new)
+    vn = wl.as_numpy_bits(w.v_new)
+    written = np.zeros(k0.shape[:2], bool)
+    for n, slot in enumerate(w.slot_mapping.tolist()):
+        if slot < 0 or slot >= 12 * ps:
+            continue
+        written[slot // ps, slot % ps] = True
+        assert np.array_equal(kc[slot // ps, slot % ps], kn[n]) and np.array_equal(vc[slot // ps, slot % ps], vn[n])
+    assert written.sum() == sum(1 for s in w.slot_mapping.tolist() if 0 <= s < 12 * ps)
+    assert np.array_equal(kc[~written], k0[~written]) and np.array_equal(vc[~written], v0[~written])
+
+
+def test_fp8_encoder_matches_torch_rounding():
+    """Nearest E4M3FN code with ties to even, against torch's float8_e4m3fn conversion, on
+    every bf16 value in [-448, 448], all exact midpoints between codes, and random floats."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    xs = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float32)
+    xs = xs[torch.isfinite(xs) & (xs.abs() <= 448)]
+    codes = torch.arange(0x7F, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float32)
+    mids = (codes[1:] + codes[:-1]) / 2
+    rnd = torch.empty(20000).uniform_(-448, 448, generator=torch.Generator().manual_seed(5))
+    xs = torch.cat([xs, mids, -mids, rnd]).to(torch.float32)
+    ref = xs.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = np.array([oracle.fp8e4m3_encode(float(x)) for x in xs.numpy()], dtype=np.uint8)
+    assert np.array_equal(ours, ref)
+
+
+def test_append_fp8_quantises_with_each_heads_scale_and_saturates():
+    w = wl.append_workload(30, 4, 32, 4, 10, "fp8_e4m3", seed=302)
+    kc, vc = _append(w)
+    kn = w.k_new.to(torch.float32).numpy()
+    vn = w.v_new.to(torch.float32).numpy()
+    ks, vs = w.k_scale.numpy(), w.v_scale.numpy()
+    saturated = 0
+    for n, slot in enumerate(w.slot_mapping.tolist()):
+        if slot < 0 or slot >= 40:
+            continue
+        for h in range(4):
+            qk = np.clip(kn[n, h] / ks[h], -448, 448).astype(np.float32)  # fp32 division, as specified
+            saturated += int((np.abs(kn[n, h] / ks[h]) > 448).sum())
+            exp_k = torch.from_numpy(qk).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            qv = np.clip(vn[n, h] / vs[h], -448, 448).astype(np.float32)
+            exp_v = torch.from_numpy(qv).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(kc[slot // 4, slot % 4, h], exp_k)
+            assert np.array_equal(vc[slot // 4, slot % 4, h], exp_v)
+    assert saturated > 0  # the draw exercises the clamp
+
+
+def test_rope_identity_and_quarter_turn():
+    """cos = 1, sin = 0 leaves K unchanged; cos = 0, sin = 1 maps (k[d], k[d + D/2]) to
+    (-k[d + D/2], k[d]) exactly (rotate-half pairing)."""
+    w = wl.append_workload(12, 2, 16, 4, 6, "bf16", seed=303, rope=True)
+    D = 16
+    table = torch.zeros(2, D)
+    table[0, : D // 2] = 1.0          # position 0: identity
+    table[1, D // 2:] = 1.0           # position 1: a quarter turn
+    pos = torch.tensor([n % 2 for n in range(12)], dtype=torch.int64)
+    w2 = dataclasses_replace(w, positions=pos, cos_sin=table.contiguous())
+    kc, _ = _append(w2)
+    kn = wl.as_numpy_bits(w.k_new)
+    kf = w.k_new.to(torch.float32).numpy()
+    for n, slot in enumerate(w.slot_mapping.tolist()):
+        if slot < 0 or slot >= 24:
+            continue
+        row = kc[slot // 4, slot % 4]
+        if n % 2 == 0:
+            assert np.array_equal(row, kn[n])
+        else:
+            expect = np.concatenate([-kf[n, :, D // 2:], kf[n, :, : D // 2]], axis=1)
+            got = torch.from_numpy(row.view(np.int16).copy()).view(torch.bfloat16).to(torch.float32).numpy()
+            assert np.array_equal(got, expect)
+
+
+def test_rope_rotations_compose_and_keep_pair_norms():
+    """Rotating by the table row of angle a and then of angle b matches one rotation by
+    a + b, and every (d, d + D/2) pair keeps its length, within fp32/bf16 rounding."""
+    D = 32
+    w = wl.append_workload(8, 1, D, 8, 1, "bf16", seed=304)
+    slots = torch.arange(8, dtype=torch.int64)
+    rng = np.random.default_rng(9)
+    a, b = rng.uniform(-3, 3, D // 2), rng.uniform(-3, 3, D // 2)
+    def table(ang):
+        return torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)])[None, :].astype(np.float32))
+    zero = torch.zeros(8, dtype=torch.int64)
+    def rotate(k_new, ang):
+        ww = dataclasses_replace(w, k_new=k_new, slot_mapping=slots, positions=zero, cos_sin=table(ang))
+        kc, _ = _append(ww)
+        return torch.from_numpy(kc.view(np.int16).copy()).view(torch.bfloat16).reshape(8, 1, D)
+    once = rotate(rotate(w.k_new, a), b).to(torch.float64).numpy()
+    both = rotate(w.k_new, a + b).to(torch.float64).numpy()
+    assert np.max(np.abs(once - both)) <= 0.05 * (1 + np.abs(both).max())
+    x = w.k_new.to(torch.float64).numpy()
+    r = rotate(w.k_new, a).to(torch.float64).numpy()
+    n0 = x[..., : D // 2] ** 2 + x[..., D // 2:] ** 2
+    n1 = r[..., : D // 2] ** 2 + r[..., D // 2:] ** 2
+    assert np.allclose(n1, n0, rtol=2e-2, atol=1e-3)
+    # and the rotation really moved the rows
+    assert np.max(np.abs(r - x)) > 0.1
+
+
+def test_rope_row_is_selected_by_position_and_out_of_table_positions_write_nothing():
+    w = wl.append_workload(20, 2, 16, 4, 10, "bf16", seed=305, rope=True)
+    kc, _ = _append(w)
+    k0 = wl.as_numpy_bits(w.k_cache)
+    for n, slot in enumerate(w.slot_mapping.tolist()):
+        if slot < 0 or slot >= 40:
+            continue
+        p = int(w.positions[n])
+        if p >= w.cos_sin.shape[0]:
+            assert np.array_equal(kc[slot // 4, slot % 4], k0[slot // 4, slot % 4])
+            continue
+        # the same token appended alone with a one-row table holding row p
+        ww = dataclasses_replace(w, k_new=w.k_new[n:n + 1].contiguous(), v_new=w.v_new[n:n + 1].contiguous(),
+                                 slot_mapping=torch.tensor([0]), positions=torch.tensor([0]),
+                                 cos_sin=w.cos_sin[p:p + 1].contiguous())
+        one, _ = _append(ww)
+        assert np.array_equal(kc[slot // 4, slot % 4], one[0, 0])
+
+
+def test_bf16_rounding_matches_torch():
+    """fp32 -> bf16 round to nearest even, against torch, on random values across the exponent
+    range and on exact midpoints between bf16 neighbours (both tie directions)."""
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(20000, generator=g) * torch.exp2(torch.randint(-60, 60, (20000,), generator=g).float())
+    lo = torch.randn(5000, generator=g).to(torch.bfloat16)
+    lo_bits = lo.view(torch.int16).to(torch.int32) & 0xFFFF
+    mids = ((lo_bits << 16) | 0x8000).to(torch.int32).view(torch.float32)  # halfway to the next bf16
+    xs = torch.cat([x, mids])
+    ref = xs.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = np.array([oracle.bf16_round(float(v)) for v in xs.numpy()], dtype=np.uint16)
+    assert np.array_equal(ours, ref)
