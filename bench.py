@@ -181,6 +181,60 @@ def bench_one(name, steps, warmup, num_splits, device, scrub):
 CPU_SAMPLE_S = 10.0  # length of the CPU-baseline sample
 
 
+# The KV append measured alongside: a prefill chunk of 8192 tokens written into an FP8 cache
+# with RoPE (8 KV heads, head_dim 128, 64-token pages, a pool twice the chunk).
+APPEND = dict(name="append_prefill8k_fp8_rope_d128", n_tokens=8192, num_kv_heads=8, head_dim=128,
+              page_size=64, num_pages=256, kv_dtype="fp8_e4m3", rope=True, seed=7)
+
+
+def append_bytes(w):
+    """Bytes an append must move: the new K and V rows of the tokens that are written, their
+    cache elements, the slot (and position and table row) of every token."""
+    n, hkv, d = w.k_new.shape
+    e = w.k_cache.element_size()
+    cap = w.k_cache.shape[0] * w.k_cache.shape[1]
+    ok = (w.slot_mapping >= 0) & (w.slot_mapping < cap)
+    if w.positions is not None:
+        ok &= (w.positions >= 0) & (w.positions < w.cos_sin.shape[0])
+    rows = int(ok.sum())
+    total = rows * hkv * d * (2 * 2 + 2 * e) + n * 8
+    if w.positions is not None:
+        total += n * 8 + rows * d * 4
+    return total
+
+
+def bench_append(steps, warmup, device, scrub):
+    import torch
+    from paged_kv_decode_amd import binding as B
+    from paged_kv_decode_amd import workloads as wl
+    a = dict(APPEND)
+    name = a.pop("name")
+    w = wl.append_workload(**a)
+    d = lambda t: None if t is None else t.to(device)
+    args = dict(k_new=d(w.k_new), v_new=d(w.v_new), slot_mapping=d(w.slot_mapping), positions=d(w.positions),
+                cos_sin=d(w.cos_sin), k_cache=d(w.k_cache), v_cache=d(w.v_cache), k_scale=d(w.k_scale),
+                v_scale=d(w.v_scale))
+    stream = torch.cuda.current_stream(device)
+    for _ in range(warmup):
+        B.append(**args)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        scrub.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        B.append(**args)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    mean = sum(ms) / len(ms)
+    nbytes = append_bytes(w)
+    return {"workload": name, "tokens": a["n_tokens"], "num_kv_heads": a["num_kv_heads"],
+            "head_dim": a["head_dim"], "kv_dtype": a["kv_dtype"], "rope": a["rope"], "ms_per_call": mean,
+            "algorithmic_bytes": nbytes, "gbs": nbytes / (mean * 1e-3) / 1e9,
+            "pct_of_peak": 100.0 * nbytes / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def cpu_baseline(w, nbytes):
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -363,6 +417,9 @@ def main():
               file=sys.stderr, flush=True)
     if args.profile_only:
         return
+    app = bench_append(args.steps, args.warmup, device, scrub)
+    print(f"# {app['workload']}: {app['ms_per_call'] * 1e3:.1f} us/call {app['gbs']:.0f} GB/s = "
+          f"{app['pct_of_peak']:.1f}% of peak", file=sys.stderr, flush=True)
 
     p = results[PRIMARY]
     roof_achieved = p["split_kernel_gbs"]
@@ -406,6 +463,7 @@ def main():
         line["verify"] = {"gbs": round(v["gbs"], 2), "pct_of_peak": round(v["pct_of_peak"], 2),
                           "query_tokens_per_s": round(v["query_tokens_per_s"], 1), "ms_per_step": v["ms_per_step"],
                           "q_len": v["q_len"], "causal": v["causal"], "num_splits": v["num_splits"]}
+    line["append"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in app.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(primary_w, p["algorithmic_bytes"])
     print(json.dumps(line), flush=True)

@@ -257,6 +257,41 @@ int32_t paged_decode_merge(int64_t rows, int32_t num_splits, int32_t head_dim, c
 int32_t paged_decode_check_tables(const pkd_dims* dims, const int32_t* block_table,
                                   const int32_t* seq_lens, int32_t* d_error_count, void* stream);
 
+/*
+ * paged_kv_append -- write new K/V rows into the paged cache: the step before
+ * decode that the sglang fuse/overlap catalogue lists as fused FP8 quantisation
+ * + paged K/V cache write (section 1, the TRTLLM FP8 KV row) and as RoPE fused
+ * with the KV cache store (sections 1 and 14).
+ *
+ *   dims          host; num_kv_heads, head_dim, page_size, num_pages and
+ *                 kv_dtype are used (the other fields are ignored).
+ *   num_tokens    N >= 0 (0 enqueues nothing).
+ *   k_new, v_new  [N][Hkv][D] bfloat16, contiguous.
+ *   slot_mapping  [N] int64: token n goes to page slot_mapping[n] / page_size,
+ *                 position slot_mapping[n] % page_size.  A negative slot
+ *                 (padding) or one >= num_pages * page_size writes nothing.
+ *                 Slots of one call must be distinct.
+ *   positions     [N] int64 and cos_sin [max_position][D] fp32, or both NULL:
+ *                 with them K is rotated first, NeoX rotate-half form: for
+ *                 d < D/2, c = cos_sin[pos][d], s = cos_sin[pos][D/2 + d],
+ *                 k'[d] = k[d] c - k[d + D/2] s, k'[d + D/2] = k[d + D/2] c + k[d] s,
+ *                 each an fp32 product followed by one fused multiply-add.  A
+ *                 position outside [0, max_position) writes nothing.
+ *   k_cache, v_cache  [num_pages][page_size][Hkv][D] of kv_dtype, updated in
+ *                 place: bf16 values rounded to nearest even; FP8 codes of
+ *                 clamp(x / scale[h], -448, 448) (fp32 division, nearest code,
+ *                 ties to even) with
+ *   k_scale, v_scale  [Hkv] fp32 per-KV-head scales (FP8 only; NULL for BF16),
+ *                 the same scales paged_decode dequantises with.
+ * Alignment: k_new, v_new, caches and cos_sin 16 bytes; slot_mapping and
+ * positions 8; scales 4.  Returns PKD_OK or a negative status; argument errors
+ * enqueue nothing.
+ */
+int32_t paged_kv_append(const pkd_dims* dims, int64_t num_tokens, const void* k_new, const void* v_new,
+                        const int64_t* slot_mapping, const int64_t* positions, const float* cos_sin,
+                        int32_t max_position, void* k_cache, void* v_cache, const float* k_scale,
+                        const float* v_scale, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* paged_decode_status_string(int32_t status);
 

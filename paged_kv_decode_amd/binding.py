@@ -42,7 +42,7 @@ PKD_DTYPE_FP8_E4M3 = 1
 
 EXPORTED = ("paged_decode", "paged_decode_partition", "paged_decode_finish", "paged_decode_num_splits",
             "paged_decode_launches", "paged_decode_workspace_bytes", "paged_decode_partials", "paged_decode_merge",
-            "paged_decode_check_tables", "paged_decode_status_string")
+            "paged_decode_check_tables", "paged_kv_append", "paged_decode_status_string")
 
 
 class PkdError(RuntimeError):
@@ -115,6 +115,8 @@ _lib.paged_decode_merge.argtypes = [ctypes.c_int64, _i32, _i32, _p, _p, _p, _p, 
 _lib.paged_decode_merge.restype = _i32
 _lib.paged_decode_check_tables.argtypes = [_dims_p, _p, _p, _p, _p]
 _lib.paged_decode_check_tables.restype = _i32
+_lib.paged_kv_append.argtypes = [_dims_p, ctypes.c_int64, _p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p]
+_lib.paged_kv_append.restype = _i32
 _lib.paged_decode_status_string.argtypes = [_i32]
 _lib.paged_decode_status_string.restype = ctypes.c_char_p
 
@@ -188,6 +190,13 @@ def paged_decode_check_tables(dims, block_table, seq_lens, d_error_count, stream
                                           _ptr(d_error_count), _ptr(stream))
 
 
+def paged_kv_append(dims, num_tokens, k_new, v_new, slot_mapping, positions, cos_sin, max_position, k_cache,
+                    v_cache, k_scale, v_scale, stream) -> int:
+    return _lib.paged_kv_append(_dims_ref(dims), int(num_tokens), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                                _ptr(positions), _ptr(cos_sin), int(max_position), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(k_scale), _ptr(v_scale), _ptr(stream))
+
+
 def paged_decode_status_string(status: int) -> str:
     return _lib.paged_decode_status_string(int(status)).decode()
 
@@ -257,3 +266,24 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=Non
     if st != PKD_OK:
         raise PkdError(st)
     return out, lse
+
+
+def append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, positions=None,
+           cos_sin=None, stream: Optional[int] = None):
+    """Run paged_kv_append on torch device tensors (k_cache / v_cache updated in place)."""
+    import torch
+    n, hkv, d = k_new.shape
+    num_pages, ps, hkv2, d2 = k_cache.shape
+    if (hkv2, d2) != (hkv, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between new rows and caches")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("k_new and v_new must be bfloat16")
+    kvd = PKD_DTYPE_FP8_E4M3 if k_cache.dtype == torch.float8_e4m3fn else PKD_DTYPE_BF16
+    dims = pkd_dims(0, hkv, hkv, d, ps, num_pages, 1, kvd, 1, 0)
+    max_pos = 0 if cos_sin is None else cos_sin.shape[0]
+    if stream is None:
+        stream = current_stream_handle(k_new.device)
+    st = paged_kv_append(dims, n, k_new, v_new, slot_mapping, positions, cos_sin, max_pos, k_cache, v_cache,
+                         k_scale, v_scale, stream)
+    if st != PKD_OK:
+        raise PkdError(st)

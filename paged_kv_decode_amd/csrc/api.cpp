@@ -474,6 +474,46 @@ int32_t paged_decode_check_tables(const pkd_dims* dims, const int32_t* block_tab
   return e == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
 }
 
+int32_t paged_kv_append(const pkd_dims* dims, int64_t num_tokens, const void* k_new, const void* v_new,
+                        const int64_t* slot_mapping, const int64_t* positions, const float* cos_sin,
+                        int32_t max_position, void* k_cache, void* v_cache, const float* k_scale,
+                        const float* v_scale, void* stream) {
+  if (!dims) return PKD_ERR_NULL_POINTER;
+  if (dims->num_kv_heads < 1 || dims->page_size < 1 || dims->num_pages < 1 || num_tokens < 0 ||
+      num_tokens > ((int64_t)1 << 40))
+    return PKD_ERR_BAD_DIMS;
+  if (!valid_head_dim(dims->head_dim)) return PKD_ERR_HEAD_DIM;
+  if (dims->kv_dtype != PKD_DTYPE_BF16 && dims->kv_dtype != PKD_DTYPE_FP8_E4M3) return PKD_ERR_DTYPE;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKD_ERR_NULL_POINTER;
+  if ((positions == nullptr) != (cos_sin == nullptr)) return PKD_ERR_NULL_POINTER;
+  if (positions && max_position < 1) return PKD_ERR_BAD_DIMS;
+  const bool fp8 = dims->kv_dtype == PKD_DTYPE_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale)) return PKD_ERR_SCALES;
+  if (!fp8 && (k_scale || v_scale)) return PKD_ERR_SCALES;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8) || !aligned(positions, 8) || !aligned(cos_sin, 16) || !aligned(k_scale, 4) ||
+      !aligned(v_scale, 4))
+    return PKD_ERR_ALIGNMENT;
+  if (num_tokens == 0) return PKD_OK;
+  if (current_cu_count() < 0) return PKD_ERR_DEVICE;
+  pkd::AppendParams a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.slot_mapping = slot_mapping;
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.num_tokens = num_tokens;
+  a.capacity = (int64_t)dims->num_pages * dims->page_size;
+  a.max_position = max_position;
+  a.hkv = dims->num_kv_heads;
+  return pkd::launch_kv_append(a, dims->head_dim, fp8, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKD_OK : PKD_ERR_LAUNCH;
+}
+
 const char* paged_decode_status_string(int32_t status) {
   switch (status) {
     case PKD_OK: return "ok";

@@ -90,6 +90,23 @@ struct MergeParams {
   int32_t q_len;               // balanced layout: rows are (b * q_len + i) * Hq + h
 };
 
+// Arguments of the paged KV append kernel.
+struct AppendParams {
+  const uint16_t* k_new;       // [N][Hkv][D] bf16
+  const uint16_t* v_new;
+  const int64_t* slot_mapping; // [N] page * page_size + position; < 0 or >= capacity: not written
+  const int64_t* positions;    // [N] or null (no RoPE)
+  const float* cos_sin;        // [max_position][D]: cos of the D/2 angles, then their sin
+  void* k_cache;               // [num_pages][page_size][Hkv][D] bf16 or fp8 codes
+  void* v_cache;
+  const float* k_scale;        // [Hkv] (fp8)
+  const float* v_scale;
+  int64_t num_tokens;
+  int64_t capacity;            // num_pages * page_size
+  int64_t max_position;
+  int32_t hkv;
+};
+
 constexpr int kWaves = 4;            // waves per split-kernel workgroup
 constexpr int kSplitAlign = 64;      // tokens; split boundaries are multiples of this
 constexpr int kHeadsPerGroup = 16;   // query heads packed into one MFMA N dimension
@@ -100,6 +117,7 @@ hipError_t launch_split_kv(const SplitParams& p, int batch, int head_dim, bool f
                            bool paged16, hipStream_t stream);
 hipError_t launch_balanced(const BalancedParams& p, int head_dim, bool fp8, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool fp8, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* block_table, const int32_t* seq_lens, int batch,
                                int max_pages, int page_size, int num_pages, int32_t* d_count,
                                hipStream_t stream);

@@ -636,3 +636,93 @@ def test_balanced_structures_parity(B, case):
     torch.cuda.synchronize()
     assert torch.equal(o2.cpu().view(torch.int16), out.view(torch.int16))
     assert torch.equal(l2.cpu().view(torch.int32), lse.view(torch.int32))
+
+
+# ---- paged KV append (quantised cache write with optional RoPE) --------------------
+
+APPEND_CASES = [
+    # (N, Hkv, D, page_size, num_pages, kv dtype, rope, seed)
+    (37, 2, 32, 16, 4, "bf16", False, 501),
+    (64, 8, 128, 64, 3, "bf16", True, 502),
+    (50, 4, 64, 16, 8, "fp8_e4m3", False, 503),
+    (129, 8, 128, 64, 4, "fp8_e4m3", True, 504),
+    (20, 1, 256, 16, 2, "fp8_e4m3", True, 505),
+    (700, 2, 256, 128, 8, "bf16", True, 506),
+]
+
+
+def _dev_append(w):
+    c = torch.device("cuda:0")
+    d = lambda t: None if t is None else t.to(c)
+    return dict(k_new=d(w.k_new), v_new=d(w.v_new), slot_mapping=d(w.slot_mapping), positions=d(w.positions),
+                cos_sin=d(w.cos_sin), k_cache=d(w.k_cache).clone(), v_cache=d(w.v_cache).clone(),
+                k_scale=d(w.k_scale), v_scale=d(w.v_scale))
+
+
+@pytest.mark.parametrize("case", APPEND_CASES)
+def test_append_matches_oracle_bitwise(B, case):
+    n, hkv, d, ps, pages, dtype, rope, seed = case
+    w = wl.append_workload(n, hkv, d, ps, pages, dtype, rope=rope, seed=seed, pad_every=9)
+    ref_k, ref_v = oracle.kv_append(w.k_new, w.v_new, w.slot_mapping, w.k_cache, w.v_cache, w.k_scale,
+                                    w.v_scale, w.positions, w.cos_sin)
+    t = _dev_append(w)
+    B.append(**t)
+    torch.cuda.synchronize()
+    got_k = wl.as_numpy_bits(t["k_cache"].cpu())
+    got_v = wl.as_numpy_bits(t["v_cache"].cpu())
+    assert np.array_equal(got_k, ref_k.reshape(got_k.shape)), f"K cache differs {case}"
+    assert np.array_equal(got_v, ref_v.reshape(got_v.shape)), f"V cache differs {case}"
+
+
+def test_append_fp8_conversion_on_every_bf16_value(B):
+    """Scale 1: every bf16 value in [-448, 448], including exact midpoints between FP8 codes,
+    is encoded by the kernel exactly as by the oracle's nearest-code, ties-to-even rule."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    f = vals.to(torch.float32)
+    vals = vals[torch.isfinite(f) & (f.abs() <= 448)]
+    d = 128
+    rows = -(-vals.numel() // d)
+    padded = torch.zeros(rows * d, dtype=torch.bfloat16)
+    padded[: vals.numel()] = vals
+    k_new = padded.view(rows, 1, d)
+    w = wl.append_workload(rows, 1, d, 16, -(-rows // 16), "fp8_e4m3", seed=507)
+    w.k_new, w.v_new = k_new, k_new.flip(0).contiguous()
+    w.slot_mapping = torch.arange(rows, dtype=torch.int64)
+    w.k_scale = torch.ones(1)
+    w.v_scale = torch.ones(1)
+    ref_k, ref_v = oracle.kv_append(w.k_new, w.v_new, w.slot_mapping, w.k_cache, w.v_cache, w.k_scale, w.v_scale)
+    t = _dev_append(w)
+    B.append(**t)
+    torch.cuda.synchronize()
+    assert np.array_equal(wl.as_numpy_bits(t["k_cache"].cpu()), ref_k)
+    assert np.array_equal(wl.as_numpy_bits(t["v_cache"].cpu()), ref_v)
+
+
+def test_append_then_decode(B):
+    """Fill a cache by appending every token of three sequences (FP8, RoPE off), then decode:
+    the result matches the oracle decode of the oracle-filled cache."""
+    lens = [37, 100, 64]
+    ps, hkv, hq, d = 16, 2, 8, 64
+    w = wl.custom_workload(len(lens), hq, hkv, d, ps, lens, "fp8_e4m3", seed=508)
+    # the logical rows as bf16 values to append, and the slot of every token
+    kl = (w.k_logical.to(torch.float32) * w.k_scale.view(1, -1, 1)).to(torch.bfloat16)
+    vl = (w.v_logical.to(torch.float32) * w.v_scale.view(1, -1, 1)).to(torch.bfloat16)
+    slots = []
+    for b, L in enumerate(lens):
+        for tok in range(L):
+            slots.append(int(w.block_table[b, tok // ps]) * ps + tok % ps)
+    slots = torch.tensor(slots, dtype=torch.int64)
+    empty = torch.zeros_like(w.k_cache.view(torch.uint8)).view(torch.float8_e4m3fn)
+    ref_k, ref_v = oracle.kv_append(kl, vl, slots, empty, empty, w.k_scale, w.v_scale)
+    c = torch.device("cuda:0")
+    kc, vc = empty.to(c).clone(), empty.to(c).clone()
+    B.append(kl.to(c), vl.to(c), slots.to(c), kc, vc, w.k_scale.to(c), w.v_scale.to(c))
+    torch.cuda.synchronize()
+    assert np.array_equal(wl.as_numpy_bits(kc.cpu()), ref_k) and np.array_equal(wl.as_numpy_bits(vc.cpu()), ref_v)
+    ref_o, ref_l = oracle.paged_decode(w.q, kc.cpu(), vc.cpu(), w.block_table, w.seq_lens, w.scale, w.k_scale,
+                                       w.v_scale)
+    out, lse = B.decode(w.q.to(c), kc, vc, w.block_table.to(c), w.seq_lens.to(c), w.scale, w.k_scale.to(c),
+                        w.v_scale.to(c), num_splits=0)
+    torch.cuda.synchronize()
+    check(out.cpu(), lse.cpu(), ref_o, ref_l, what="append then decode")
