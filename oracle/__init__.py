@@ -54,6 +54,11 @@ def lib():
         L.pkd_oracle_paged_decode_multi.restype = _c_int
         L.pkd_oracle_paged_decode_multi_rows.argtypes = multi + [_c_int, _p, _p, _p]
         L.pkd_oracle_paged_decode_multi_rows.restype = _c_int
+        ext = [_c_int] * 11 + [_p] * 8 + [_c_double]
+        L.pkd_oracle_paged_decode_ext.argtypes = ext + [_p, _p, _c_int]
+        L.pkd_oracle_paged_decode_ext.restype = _c_int
+        L.pkd_oracle_paged_decode_ext_rows.argtypes = ext + [_c_int, _p, _p, _p]
+        L.pkd_oracle_paged_decode_ext_rows.restype = _c_int
         L.pkd_oracle_lse_merge.argtypes = [ctypes.c_int64, _c_int, _c_int, _p, _p, _p, _p]
         L.pkd_oracle_lse_merge.restype = None
         L.pkd_oracle_bf16_value.argtypes = [ctypes.c_uint16]
@@ -125,6 +130,12 @@ class _Args:
         assert self.q_len == 1, "single-token entry points take q as [B][Hq][D]"
         return list(self.dims) + [_ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.bt),
                                   _ptr(self.lens), _ptr(self.ks), _ptr(self.vs), self.scale]
+
+    def head_ext(self, causal, window, sinks):
+        self.sinks = _raw(sinks, np.float32)
+        return list(self.dims) + [self.q_len, int(bool(causal)), int(window), _ptr(self.sinks)] + [
+            _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.bt), _ptr(self.lens), _ptr(self.ks),
+            _ptr(self.vs), self.scale]
 
     def head_multi(self, causal):
         return list(self.dims) + [self.q_len, int(bool(causal))] + [
@@ -208,6 +219,33 @@ def paged_decode_multi_rows(q, k_cache, v_cache, block_table, seq_lens, scale, c
     return out, lse
 
 
+def paged_decode_ext(q, k_cache, v_cache, block_table, seq_lens, scale, causal=False, window=0, sinks=None,
+                     k_scale=None, v_scale=None, nthreads: int = 1):
+    """Several query tokens with causal mask, sliding window and sinks (see
+    paged_attention_ref.c).  q [B, Hq, D] or [B, q_len, Hq, D]; sinks float32 [Hq] or None.
+    Returns (out [B, q_len, Hq, D], lse [B, q_len, Hq]) as float64."""
+    a = _Args(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale, v_scale)
+    B, hq, _, d = a.dims[:4]
+    out = np.empty((B, a.q_len, hq, d), np.float64)
+    lse = np.empty((B, a.q_len, hq), np.float64)
+    _check(lib().pkd_oracle_paged_decode_ext(*a.head_ext(causal, window, sinks), _ptr(out), _ptr(lse),
+                                             int(nthreads)))
+    return out, lse
+
+
+def paged_decode_ext_rows(q, k_cache, v_cache, block_table, seq_lens, scale, rows, causal=False, window=0,
+                          sinks=None, k_scale=None, v_scale=None):
+    """paged_decode_ext for rows = (b * q_len + i) * Hq + h only.  Returns (out [n, D], lse [n])."""
+    a = _Args(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale, v_scale)
+    d = a.dims[3]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.empty((rows.size, d), np.float64)
+    lse = np.empty((rows.size,), np.float64)
+    _check(lib().pkd_oracle_paged_decode_ext_rows(*a.head_ext(causal, window, sinks), int(rows.size), _ptr(rows),
+                                                  _ptr(out), _ptr(lse)))
+    return out, lse
+
+
 def lse_merge(o_part, lse_part):
     """o_part [R, S, D], lse_part [R, S] (float64) -> (out [R, D], lse [R])."""
     o = np.ascontiguousarray(o_part, dtype=np.float64)
@@ -268,6 +306,9 @@ def run_workload(w, nthreads: int = 1, num_splits: int = 0):
     """Oracle over a drawn workload object (q, k_cache, v_cache, block_table,
     seq_lens, scale, k_scale, v_scale attributes)."""
     args = (w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale)
+    if getattr(w.spec, "window", 0) or getattr(w, "sinks", None) is not None:
+        assert not num_splits
+        return paged_decode_ext(*args, w.spec.causal, w.spec.window, w.sinks, w.k_scale, w.v_scale, nthreads)
     if getattr(w.spec, "q_len", 1) > 1 or getattr(w.spec, "causal", False):
         assert not num_splits
         return paged_decode_multi(*args, w.spec.causal, w.k_scale, w.v_scale, nthreads)

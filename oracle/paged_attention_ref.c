@@ -49,6 +49,19 @@
  * definition above over its visible tokens.  q_len = 1 without the mask is the
  * single-token decode.
  *
+ * Sliding window and attention sinks (pkd_oracle_paged_decode_ext): the b12x
+ * "Paged attention" row lists sliding-window attention and an attention-sink
+ * bias among its variants.  With a window W > 0, query token i (at position
+ * p = L - q_len + i) attends only over positions t > p - W (besides the causal
+ * limit, if any); for plain decode that is the last W tokens.  With sinks,
+ * query head h has a logit sink[h] that joins the softmax denominator without
+ * a value row:
+ *     out = sum_t exp(s_t) v_t / (exp(sink[h]) + sum_t exp(s_t)),
+ *     lse = ln(exp(sink[h]) + sum_t exp(s_t)),
+ * so a token that sees no position gets out = 0 and lse = sink[h].  The
+ * oracle computes the plain result over the visible tokens, then folds the sink
+ * in: lse' = ln(e^lse + e^sink), out' = out * e^(lse - lse').
+ *
  * The file also defines the paged KV append that fills the cache (row f2,
  * pkd_oracle_kv_append, at the end).
  *
@@ -112,6 +125,8 @@ typedef struct {
   double* lse;                /* [B][q_len][Hq] */
   int q_len;                  /* query tokens per sequence, >= 1 */
   int causal;                 /* 0: every query token sees all L tokens; 1: causal mask */
+  int window;                 /* 0: no window; > 0: positions t > p - window only */
+  const float* sinks;         /* [Hq] sink logits, or NULL */
 } problem;
 
 /* Value of element d of token t's key (is_v = 0) or value (is_v = 1) row for
@@ -137,6 +152,34 @@ static int visible_tokens(const problem* P, int b, int qi) {
   if (!P->causal) return L;
   const int v = L - P->q_len + qi + 1;
   return v < 0 ? 0 : (v > L ? L : v);
+}
+
+/* First position visible to query token qi of sequence b (the window's lower
+ * end; 0 without a window), never past visible_tokens. */
+static int first_visible(const problem* P, int b, int qi) {
+  const int V = visible_tokens(P, b, qi);
+  if (P->window <= 0) return 0;
+  const int p = P->seq_lens[b] - P->q_len + qi;  /* the query token's position */
+  int lo = p - P->window + 1;
+  if (lo < 0) lo = 0;
+  return lo < V ? lo : V;
+}
+
+/* Folds query head h's sink logit into a finished row (see the top of the
+ * file): lse' = ln(e^lse + e^sink), out' = out e^(lse - lse'). */
+static double apply_sink(const problem* P, int h, double lse, double* o) {
+  if (!P->sinks) return lse;
+  const double sk = (double)P->sinks[h];
+  if (sk == -INFINITY) return lse;
+  if (lse == -INFINITY) {
+    for (int d = 0; d < P->head_dim; ++d) o[d] = 0.0;
+    return sk;
+  }
+  const double mx = lse > sk ? lse : sk;
+  const double l2 = mx + log(exp(lse - mx) + exp(sk - mx));
+  const double f = exp(lse - l2);
+  for (int d = 0; d < P->head_dim; ++d) o[d] *= f;
+  return l2;
 }
 
 /* Attention of query token qi, head h of sequence b over tokens [t0, t1), by
@@ -240,23 +283,25 @@ static int run_item(const problem* P, int item) {
   }
   for (int qi = 0; qi < P->q_len; ++qi) {
     const int V = visible_tokens(P, b, qi);
+    const int lo = first_visible(P, b, qi);
     for (int h = g * G; h < (g + 1) * G; ++h) {
       const int64_t row = ((int64_t)b * P->q_len + qi) * P->hq + h;
       double* o = P->out + row * D;
       double* l = P->lse + row;
       if (S < 1) {
-        *l = attend_range(P, b, qi, h, 0, V, o, s);
+        *l = attend_range(P, b, qi, h, lo, V, o, s);
       } else {
-        /* split j covers [j*c, min((j+1)*c, V)) with c = ceil(V / S) */
-        int c = (V + S - 1) / S;
+        /* split j covers [lo + j*c, min(lo + (j+1)*c, V)) with c = ceil((V - lo) / S) */
+        int c = (V - lo + S - 1) / S;
         for (int j = 0; j < S; ++j) {
-          int t0 = j * c, t1 = (j + 1) * c;
+          int t0 = lo + j * c, t1 = lo + (j + 1) * c;
           if (t0 > V) t0 = V;
           if (t1 > V) t1 = V;
           lp[j] = attend_range(P, b, qi, h, t0, t1, op + (int64_t)j * D, s);
         }
         *l = merge_row(S, D, op, lp, o);
       }
+      *l = apply_sink(P, h, *l, o);
     }
   }
   free(s); free(op); free(lp);
@@ -359,9 +404,11 @@ static int rows_only(problem* P, int n_rows, const int64_t* rows, double* out, d
     int st = check_sequence(P, b);
     if (st != PKD_ORACLE_OK) return st;
     int V = visible_tokens(P, b, qi);
+    int lo = first_visible(P, b, qi);
     double* s = (double*)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
     if (!s) return PKD_ORACLE_NO_MEM;
-    lse[i] = attend_range(P, b, qi, h, 0, V, out + (int64_t)i * P->head_dim, s);
+    double* o = out + (int64_t)i * P->head_dim;
+    lse[i] = apply_sink(P, h, attend_range(P, b, qi, h, lo, V, o, s), o);
     free(s);
   }
   return PKD_ORACLE_OK;
@@ -396,6 +443,35 @@ int pkd_oracle_paged_decode_multi(int batch, int hq, int hkv, int head_dim, int 
                q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
                0, out, lse, q_len, causal};
   return run(&P, nthreads);
+}
+
+/* Several query tokens, causal mask, sliding window and sinks (see the top of
+ * the file): window >= 0 (0 = none), sinks [hq] fp32 or NULL; other arguments
+ * as for pkd_oracle_paged_decode_multi. */
+int pkd_oracle_paged_decode_ext(int batch, int hq, int hkv, int head_dim, int page_size, int num_pages,
+                                int max_pages, int kv_fp8, int q_len, int causal, int window,
+                                const float* sinks, const uint16_t* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                                const float* v_scale, double scale, double* out, double* lse, int nthreads) {
+  if (window < 0) return PKD_ORACLE_BAD_ARG;
+  problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
+               q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+               0, out, lse, q_len, causal, window, sinks};
+  return run(&P, nthreads);
+}
+
+/* pkd_oracle_paged_decode_ext for a list of rows only (rows as in _multi_rows). */
+int pkd_oracle_paged_decode_ext_rows(int batch, int hq, int hkv, int head_dim, int page_size, int num_pages,
+                                     int max_pages, int kv_fp8, int q_len, int causal, int window,
+                                     const float* sinks, const uint16_t* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                     const float* k_scale, const float* v_scale, double scale, int n_rows,
+                                     const int64_t* rows, double* out, double* lse) {
+  if (window < 0) return PKD_ORACLE_BAD_ARG;
+  problem P = {batch, hq, hkv, head_dim, page_size, num_pages, max_pages, kv_fp8,
+               q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+               0, out, lse, q_len, causal, window, sinks};
+  return rows_only(&P, n_rows, rows, out, lse);
 }
 
 /* pkd_oracle_paged_decode_multi for a list of rows only: rows[i] =

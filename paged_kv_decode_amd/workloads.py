@@ -48,6 +48,8 @@ class WorkloadSpec:
     max_len: int = 0                   # longest length the block table must allow
     q_len: int = 1                     # query tokens per sequence (the last q_len positions)
     causal: bool = False               # query token i sees positions <= L - q_len + i only
+    window: int = 0                    # > 0: query token at position p sees positions > p - window only
+    sinks: bool = False                # draw a sink logit per query head (U[0, 8])
 
     @property
     def max_pages_per_seq(self) -> int:
@@ -101,6 +103,7 @@ class Workload:
     v_logical: torch.Tensor
     token_offsets: torch.Tensor  # [B + 1] int64 prefix sums of seq_lens
     perm: torch.Tensor           # [num_pages] int64 physical page of each logical page
+    sinks: Optional[torch.Tensor] = None  # [Hq] float32 sink logits (natural log), or None
 
     @property
     def scale(self) -> float:
@@ -221,24 +224,25 @@ def make_workload(spec: WorkloadSpec, tail: str = "nan",
     else:
         raise ValueError(spec.kv_dtype)
     del k32, v32
+    sinks = (torch.rand(hq, generator=g) * 8).to(torch.float32) if spec.sinks else None
     k_cache, v_cache, bt = scatter_to_pages(k_log, v_log, lens.tolist(), ps, perm, max_pages, tail)
     offs = torch.zeros(B + 1, dtype=torch.int64)
     offs[1:] = torch.cumsum(lens.to(torch.int64), 0)
     return Workload(spec, lens, bt, num_pages, q, k_cache, v_cache, k_scale, v_scale,
-                    k_log, v_log, offs, perm)
+                    k_log, v_log, offs, perm, sinks)
 
 
 def custom_workload(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                     seq_lens: Sequence[int], kv_dtype: str = "bf16", seed: int = 0,
                     tail: str = "nan", max_pages: Optional[int] = None, name: str = "custom",
-                    q_len: int = 1, causal: bool = False) -> Workload:
+                    q_len: int = 1, causal: bool = False, window: int = 0, sinks: bool = False) -> Workload:
     """A one-off workload with explicit lengths (edge cases, small parity cases)."""
     lens = [int(x) for x in seq_lens]
     max_len = max(lens + [1])
     if max_pages is not None:
         max_len = max(max_len, max_pages * page_size)
     spec = WorkloadSpec(name, batch, num_q_heads, num_kv_heads, head_dim, page_size, kv_dtype, seed,
-                        tuple(lens), None, max_len, q_len, causal)
+                        tuple(lens), None, max_len, q_len, causal, window, sinks)
     return make_workload(spec, tail=tail)
 
 

@@ -5,7 +5,7 @@ the kind a hand-written attention reference can plausibly contain: a wrong
 page or slot index, the wrong KV head for a query head, K and V swapped, the
 softmax scale dropped, a base-2 log-sum-exp, a wrong merge weight, a wrong
 split boundary, a wrong FP8 exponent bias, a wrong cache layout, a causal
-mask off by one or aligned to the wrong end, and in the KV append a RoPE sign,
+mask off by one or aligned to the wrong end, a window or sink slip, and in the KV append a RoPE sign,
 pairing or cos/sin swap, a wrong scale, rounding ties or slot.  The copy is compiled with the
 oracle's own build command and the pin suite
 (test_oracle_pins.py) is run against it in a child process through
@@ -76,7 +76,7 @@ MUTANTS = [
     ("merge_lse_missing_max",
      "double lse = M + log(z);", "double lse = log(z);"),
     ("split_chunk_rounds_down",
-     "int c = (V + S - 1) / S;", "int c = V / S > 0 ? V / S : 1;"),
+     "int c = (V - lo + S - 1) / S;", "int c = (V - lo) / S > 0 ? (V - lo) / S : 1;"),
     ("fp8_subnormal_exponent",
      "mag = ldexp((double)m / 8.0, 1 - 7);", "mag = ldexp((double)m / 8.0, -7);"),
     ("fp8_exponent_bias_eight",
@@ -89,6 +89,15 @@ MUTANTS = [
      "((uint32_t)bits) << 16;", "((uint32_t)bits) << 15;"),
     ("page_bound_off_by_one",
      "if (p < 0 || p >= P->num_pages)", "if (p < 0 || p > P->num_pages)"),
+    ("window_off_by_one",
+     "int lo = p - P->window + 1;", "int lo = p - P->window;"),
+    ("window_from_last_position",
+     "const int p = P->seq_lens[b] - P->q_len + qi;  /* the query token's position */",
+     "const int p = P->seq_lens[b] - 1;  /* the query token's position */"),
+    ("sink_of_head_zero",
+     "const double sk = (double)P->sinks[h];", "const double sk = (double)P->sinks[0];"),
+    ("sink_only_in_lse",
+     "const double f = exp(lse - l2);", "const double f = 1.0;"),
     ("append_rope_sign",
      "y[d] = fmaf(x0, c, -t0);", "y[d] = fmaf(x0, c, t0);"),
     ("append_rope_adjacent_pairs",

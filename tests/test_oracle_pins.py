@@ -558,3 +558,100 @@ def test_bf16_rounding_matches_torch():
     ref = xs.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     ours = np.array([oracle.bf16_round(float(v)) for v in xs.numpy()], dtype=np.uint16)
     assert np.array_equal(ours, ref)
+
+
+# ---- sliding window and attention sinks -------------------------------------------
+
+def brute_force_ext(w):
+    """Dense attention with the visible set written as explicit position tests (window
+    lower end, causal upper end) and the sink as one more logit with no value row."""
+    q = _f64(w.q)
+    if q.ndim == 3:
+        q = q[:, None]
+    B, QL, hq, d = q.shape
+    G = hq // w.spec.num_kv_heads
+    K, V = _f64(w.k_logical), _f64(w.v_logical)
+    if w.k_scale is not None:
+        K = K * w.k_scale.double().numpy()[None, :, None]
+        V = V * w.v_scale.double().numpy()[None, :, None]
+    W = w.spec.window
+    sinks = None if w.sinks is None else w.sinks.double().numpy()
+    out = np.zeros((B, QL, hq, d))
+    lse = np.full((B, QL, hq), -np.inf)
+    for b in range(B):
+        t0, t1 = int(w.token_offsets[b]), int(w.token_offsets[b + 1])
+        L = t1 - t0
+        pos = np.arange(L)
+        for i in range(QL):
+            p = L - QL + i
+            vis = np.ones(L, bool)
+            if w.spec.causal:
+                vis &= pos <= p
+            if W:
+                vis &= pos > p - W
+            for h in range(hq):
+                s = w.scale * (K[t0:t1, h // G, :] @ q[b, i, h])[vis]
+                logits = s if sinks is None else np.append(s, sinks[h])
+                if logits.size == 0:
+                    continue
+                lse[b, i, h] = scipy.special.logsumexp(logits)
+                wts = np.exp(s - lse[b, i, h])
+                out[b, i, h] = wts @ V[t0:t1, h // G, :][vis]
+    return out, lse
+
+
+EXT_CASES = [
+    # (B, Hq, Hkv, D, ps, lens, q_len, causal, window, sinks, dtype, seed)
+    (3, 4, 2, 16, 4, [20, 7, 33], 1, False, 8, False, "bf16", 401),
+    (2, 8, 2, 16, 16, [40, 5], 3, True, 6, True, "bf16", 402),
+    (2, 4, 1, 32, 3, [11, 0], 1, False, 0, True, "bf16", 403),
+    (2, 4, 2, 16, 16, [30, 18], 4, False, 5, True, "fp8_e4m3", 404),
+    (1, 2, 1, 8, 4, [9], 2, True, 1, True, "bf16", 405),
+]
+
+
+@pytest.mark.parametrize("case", EXT_CASES)
+def test_window_and_sinks_match_brute_force(case):
+    B, hq, hkv, d, ps, lens, ql, causal, window, sinks, dtype, seed = case
+    w = wl.custom_workload(B, hq, hkv, d, ps, lens, dtype, seed, q_len=ql, causal=causal, window=window,
+                           sinks=sinks)
+    out, lse = oracle.run_workload(w)
+    ref_o, ref_l = brute_force_ext(w)
+    assert _close(out, ref_o, 1e-12) and _close(lse, ref_l, 1e-12)
+
+
+def test_no_window_and_no_sinks_is_the_multi_token_entry_bitwise():
+    w = wl.custom_workload(3, 8, 2, 16, 4, [19, 40, 2], "bf16", 406, q_len=3, causal=True)
+    ref = oracle.run_workload(w)
+    args = (w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale)
+    for window in (0, 10 ** 6):
+        out, lse = oracle.paged_decode_ext(*args, True, window, None)
+        assert np.array_equal(out, ref[0]) and np.array_equal(lse, ref[1])
+    minus_inf = torch.full((8,), float("-inf"))
+    out, lse = oracle.paged_decode_ext(*args, True, 0, minus_inf)
+    assert np.array_equal(out, ref[0]) and np.array_equal(lse, ref[1])
+
+
+def test_decode_window_is_attention_over_the_last_window_tokens():
+    w = wl.custom_workload(3, 4, 2, 16, 5, [30, 4, 17], "bf16", 407)
+    L = w.seq_lens.numpy()
+    args = (w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale)
+    for window in (1, 6, 17):
+        out, lse = oracle.paged_decode_ext(*args, False, window, None)
+        o_r, l_r = oracle.paged_decode_ranges(*args, np.maximum(L - window, 0), L)
+        assert np.array_equal(out[:, 0], o_r) and np.array_equal(lse[:, 0], l_r)
+
+
+def test_sink_closed_form_and_empty_rows():
+    """One visible token: out = v0 e^s0 / (e^s0 + e^sink), lse = ln(e^s0 + e^sink); no
+    visible token: out = 0, lse = sink."""
+    w = wl.custom_workload(2, 2, 1, 8, 4, [1, 0], "bf16", 408, sinks=True)
+    out, lse = oracle.run_workload(w)
+    q, K, V = _f64(w.q), _f64(w.k_logical), _f64(w.v_logical)
+    sk = w.sinks.double().numpy()
+    for h in range(2):
+        s0 = w.scale * float(K[0, 0] @ q[0, h])
+        z = math.exp(s0) + math.exp(sk[h])
+        assert np.max(np.abs(out[0, 0, h] - V[0, 0] * math.exp(s0) / z)) <= 1e-13
+        assert abs(lse[0, 0, h] - math.log(z)) <= 1e-13
+        assert np.all(out[1, 0, h] == 0) and lse[1, 0, h] == np.float32(sk[h])
