@@ -10,12 +10,14 @@ write-back inside the timed step.  Each step is timed
 with HIP events on the stream the kernels run on; the JSON line reports the
 mean.  The metric is achieved HBM bandwidth, algorithmic bytes / step time,
 where the algorithmic bytes are what the step must move: the K and V rows of
-exactly seq_lens[b] tokens, q, out, lse, the block-table entries used,
-seq_lens and (FP8) the scales.  Split partials and cache effects are not
-counted.
+exactly the tokens the step must see (seq_lens[b] of them, or with a sliding
+window those from the lowest window start on), q, out, lse, the block-table
+entries used, seq_lens and (FP8) the scales, (sinks) the sink logits.  Split
+partials and cache effects are not counted.
 
-The primary workload is the B=32 Llama-style decode step; the B=128 step is
-reported alongside.  The fp64 CPU oracle is timed on the same host arrays
+The primary workload is the B=32 Llama-style decode step; the B=128 step, the
+B=32 verify step (4 query tokens, causal) and the B=32 step with a 1024-token
+window and sinks are reported alongside.  The fp64 CPU oracle is timed on the same host arrays
 (whole passes over the workload for about 10 s, all host threads up to 16) as
 a reported baseline.
 
@@ -37,6 +39,7 @@ METRIC = "decode-attention achieved HBM GB/s (% of peak) + queries/s at B=32 and
 PRIMARY = "llama_b32_d128_ps64"
 SECONDARY = "batch128_d128_ps128"
 VERIFY = "verify_b32_q4_d128_ps64"  # several query tokens per sequence, reported alongside
+WINDOW = "window1k_sinks_b32_d128_ps64"  # sliding window and sinks, reported alongside
 
 
 def algorithmic_bytes(w, split_kernel_only=False):
@@ -44,17 +47,20 @@ def algorithmic_bytes(w, split_kernel_only=False):
     s = w.spec
     e = w.k_cache.element_size()
     lens = [int(x) for x in w.seq_lens]
-    kv = sum(lens) * s.num_kv_heads * s.head_dim * 2 * e
+    # First position any query token of a sequence sees (a sliding window's lower end).
+    lo = [max(L - s.q_len - s.window + 1, 0) if s.window > 0 else 0 for L in lens]
+    kv = sum(L - a for L, a in zip(lens, lo)) * s.num_kv_heads * s.head_dim * 2 * e
     rows = s.batch * s.q_len * s.num_q_heads  # (sequence, query token, head) rows
     q = rows * s.head_dim * 2
     out = rows * s.head_dim * 2
     lse = rows * 4
-    bt = sum(-(-L // s.page_size) for L in lens) * 4
+    bt = sum(-(-L // s.page_size) - a // s.page_size for L, a in zip(lens, lo)) * 4
     seq = s.batch * 4
     scales = 2 * s.num_kv_heads * 4 if w.k_scale is not None else 0
+    sinks = s.num_q_heads * 4 if getattr(w, "sinks", None) is not None else 0
     if split_kernel_only:
         return kv + q + bt + seq + scales
-    return kv + q + out + lse + bt + seq + scales
+    return kv + q + out + lse + bt + seq + scales + sinks
 
 
 class Runner:
@@ -73,7 +79,8 @@ class Runner:
         self.lens = w.seq_lens.to(device)
         self.ks = None if w.k_scale is None else w.k_scale.to(device)
         self.vs = None if w.v_scale is None else w.v_scale.to(device)
-        self.dims = B.dims_for(self.q, self.k, self.bt, causal=w.spec.causal)
+        self.sinks = None if getattr(w, "sinks", None) is None else w.sinks.to(device)
+        self.dims = B.dims_for(self.q, self.k, self.bt, causal=w.spec.causal, window=w.spec.window)
         self.S = num_splits if num_splits != 0 else B.paged_decode_num_splits(self.dims, 0)
         self.launches = B.paged_decode_launches(self.dims, self.S)  # 1: the partition writes out itself
         self.out = torch.empty(self.q.shape, dtype=torch.bfloat16, device=device)
@@ -89,7 +96,7 @@ class Runner:
         B = self.B
         if self.launches == 1:
             st = B.paged_decode(self.dims, self.q, self.k, self.v, self.bt, self.lens, self.ks, self.vs,
-                                self.w.scale, self.out, self.lse, self.S, self.ws, self.ws_bytes, self.handle)
+                                self.sinks, self.w.scale, self.out, self.lse, self.S, self.ws, self.ws_bytes, self.handle)
         else:
             st = B.paged_decode_partition(self.dims, self.q, self.k, self.v, self.bt, self.lens, self.ks,
                                           self.vs, self.w.scale, self.S, self.ws, self.ws_bytes, self.handle)
@@ -99,7 +106,7 @@ class Runner:
     def kernel2(self):
         """The merge kernel, when paged_decode uses one: its second phase."""
         if self.launches == 2:
-            st = self.B.paged_decode_finish(self.dims, self.S, self.ws, self.ws_bytes, self.out, self.lse,
+            st = self.B.paged_decode_finish(self.dims, self.S, self.ws, self.ws_bytes, self.sinks, self.out, self.lse,
                                             self.handle)
             if st != 0:
                 raise self.B.PkdError(st)
@@ -161,7 +168,8 @@ def bench_one(name, steps, warmup, num_splits, device, scrub):
     res = dict(
         workload=name, batch=w.spec.batch, num_q_heads=w.spec.num_q_heads,
         num_kv_heads=w.spec.num_kv_heads, head_dim=w.spec.head_dim, page_size=w.spec.page_size,
-        kv_dtype=w.spec.kv_dtype, q_len=w.spec.q_len, causal=w.spec.causal,
+        kv_dtype=w.spec.kv_dtype, q_len=w.spec.q_len, causal=w.spec.causal, window=w.spec.window,
+        sinks=getattr(w, "sinks", None) is not None,
         num_splits=r.S, launches=r.launches, tokens=int(w.seq_lens.sum()),
         algorithmic_bytes=nbytes, ms_per_step=step_mean,
         ms_p10=srt[int(0.1 * (steps - 1))], ms_median=srt[(steps - 1) // 2], ms_p90=srt[int(0.9 * (steps - 1))],
@@ -364,7 +372,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workloads", default=f"{PRIMARY},{SECONDARY},{VERIFY}",
+    ap.add_argument("--workloads", default=f"{PRIMARY},{SECONDARY},{VERIFY},{WINDOW}",
                     help="comma-separated workload names, or 'all'")
     ap.add_argument("--num-splits", type=int, default=0, help="0: the library's heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -463,6 +471,11 @@ def main():
         line["verify"] = {"gbs": round(v["gbs"], 2), "pct_of_peak": round(v["pct_of_peak"], 2),
                           "query_tokens_per_s": round(v["query_tokens_per_s"], 1), "ms_per_step": v["ms_per_step"],
                           "q_len": v["q_len"], "causal": v["causal"], "num_splits": v["num_splits"]}
+    if WINDOW in results:
+        v = results[WINDOW]
+        line["window"] = {"gbs": round(v["gbs"], 2), "pct_of_peak": round(v["pct_of_peak"], 2),
+                          "queries_per_s": round(v["queries_per_s"], 1), "ms_per_step": v["ms_per_step"],
+                          "window": v["window"], "sinks": v["sinks"], "num_splits": v["num_splits"]}
     line["append"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in app.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(primary_w, p["algorithmic_bytes"])

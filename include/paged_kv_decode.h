@@ -32,6 +32,21 @@
  * (b * q_len + i) * Hq + h.  All the q_len * G rows that share a KV head are
  * computed from one read of its K/V rows.
  *
+ * Sliding window and attention sinks: two variants the same b12x row lists
+ * for its paged attention.  With dims.window = W > 0, query token i (position
+ * p = seq_lens[b] - q_len + i) sees only positions t > p - W, besides the
+ * limit above (t < seq_lens[b], and t <= p with the causal mask); for plain
+ * decode that is the last W tokens.  K/V rows below the lowest window start of
+ * a sequence (rounded down to a multiple of 16) are not read.  With a sinks
+ * array, query head h has a logit sinks[h] that joins the softmax denominator
+ * and contributes no value:
+ *
+ *   out = sum_t exp(s_t) V[t] / (exp(sinks[h]) + sum_t exp(s_t)),
+ *   lse = ln(exp(sinks[h]) + sum_t exp(s_t)),
+ *
+ * so a token that sees no position gets out = 0 and lse = sinks[h].  Split
+ * partials never include the sink; it is folded in where out is written.
+ *
  * Split-KV: each sequence's tokens are cut into num_splits ranges; each range
  * produces a normalised partial output and its log-sum-exp, and a merge
  * combines them (out = sum_j exp(lse_j - lse) * o_j, lse = ln sum_j exp(lse_j)),
@@ -106,10 +121,13 @@ extern "C" {
 #define PKD_BALANCED_MAX_BATCH 1024
 
 /* Split boundaries: with S splits, sequence b's split j covers tokens
- * [min(j*c, L_b), min((j+1)*c, L_b)) where
- * c = PKD_SPLIT_ALIGN * ceil(ceil(max_pages_per_seq * page_size / S) / PKD_SPLIT_ALIGN),
- * the same for every sequence of the batch, so that every split carries about
- * the same work; trailing splits of shorter sequences are empty. */
+ * [min(lo_b + j*c, L_b), min(lo_b + (j+1)*c, L_b)) where
+ * c = PKD_SPLIT_ALIGN * ceil(ceil(N / S) / PKD_SPLIT_ALIGN),
+ * N = max_pages_per_seq * page_size, the same for every sequence of the batch,
+ * so that every split carries about the same work; trailing splits of shorter
+ * sequences are empty.  lo_b = 0 without a window; with window W,
+ * lo_b = max(L_b - q_len - W + 1, 0) rounded down to a multiple of 16 (the
+ * sequence's first visible 16-token group) and N = min(N, W + q_len + 14). */
 #define PKD_SPLIT_ALIGN 64
 
 /* KV-cache element types.  q and out are always bfloat16. */
@@ -130,6 +148,7 @@ typedef struct {
   int32_t kv_dtype;           /* a pkd_dtype */
   int32_t q_len;              /* query tokens per sequence, 1..PKD_MAX_Q_LEN (1 = decode) */
   int32_t causal;             /* 0: every query token sees all tokens; 1: causal mask (above) */
+  int32_t window;             /* 0: no window; W > 0: sliding window of W positions (above) */
 } pkd_dims;
 
 /*
@@ -144,6 +163,7 @@ typedef struct {
  *   k_scale      [Hkv] fp32 dequantisation scales for an FP8 cache (K = code * k_scale[kv]);
  *                must be NULL for BF16.
  *   v_scale      [Hkv] fp32, as k_scale for V.
+ *   sinks        [Hq] fp32 sink logits (above; -inf means no sink for that head), or NULL.
  *   scale        softmax scale applied to q.k (typically 1/sqrt(D)); included in lse.
  *   out          [B][q_len][Hq][D] bfloat16 result (fp32 accumulate, round-to-nearest-even).
  *   lse          [B][q_len][Hq] fp32 natural-log log-sum-exp of the scaled scores, or NULL.
@@ -162,8 +182,8 @@ typedef struct {
  */
 int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
-                     const float* v_scale, float scale, void* out, float* lse, int32_t num_splits,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     const float* v_scale, const float* sinks, float scale, void* out, float* lse,
+                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * paged_decode_partition / paged_decode_finish -- the two phases of paged_decode
@@ -173,7 +193,8 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
  * the workspace, then the merge kernel reads them and writes out and lse.
  * Issued back to back on one stream with the same dims, num_splits and
  * workspace they are exactly paged_decode; split apart they let a caller
- * schedule or time the phases.  Arguments as for paged_decode.
+ * schedule or time the phases.  Arguments as for paged_decode; the sinks are
+ * folded in by paged_decode_finish.
  */
 int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
@@ -181,7 +202,8 @@ int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* 
                                float scale, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, void* stream);
 int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void* workspace,
-                            size_t workspace_bytes, void* out, float* lse, void* stream);
+                            size_t workspace_bytes, const float* sinks, void* out, float* lse,
+                            void* stream);
 
 /*
  * paged_decode_num_splits -- what paged_decode does for PKD_SPLITS_AUTO:

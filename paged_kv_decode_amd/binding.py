@@ -56,7 +56,7 @@ class pkd_dims(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32)]
+                ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -94,13 +94,13 @@ _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _dims_p = ctypes.POINTER(pkd_dims)
 
-_lib.paged_decode.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _i32,
+_lib.paged_decode.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _i32,
                               _p, ctypes.c_size_t, _p]
 _lib.paged_decode.restype = _i32
 _lib.paged_decode_partition.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _i32,
                                         _p, ctypes.c_size_t, _p]
 _lib.paged_decode_partition.restype = _i32
-_lib.paged_decode_finish.argtypes = [_dims_p, _i32, _p, ctypes.c_size_t, _p, _p, _p]
+_lib.paged_decode_finish.argtypes = [_dims_p, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p]
 _lib.paged_decode_finish.restype = _i32
 _lib.paged_decode_num_splits.argtypes = [_dims_p, _i32]
 _lib.paged_decode_num_splits.restype = _i32
@@ -139,11 +139,11 @@ def _dims_ref(dims):
     return ctypes.byref(dims)
 
 
-def paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, out, lse,
-                 num_splits, workspace, workspace_bytes, stream) -> int:
+def paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, scale, out,
+                 lse, num_splits, workspace, workspace_bytes, stream) -> int:
     return _lib.paged_decode(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                             _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), float(scale), _ptr(out),
-                             _ptr(lse), int(num_splits), _ptr(workspace), int(workspace_bytes),
+                             _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), _ptr(sinks), float(scale),
+                             _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace), int(workspace_bytes),
                              _ptr(stream))
 
 
@@ -155,9 +155,9 @@ def paged_decode_partition(dims, q, k_cache, v_cache, block_table, seq_lens, k_s
                                        _ptr(stream))
 
 
-def paged_decode_finish(dims, num_splits, workspace, workspace_bytes, out, lse, stream) -> int:
+def paged_decode_finish(dims, num_splits, workspace, workspace_bytes, sinks, out, lse, stream) -> int:
     return _lib.paged_decode_finish(_dims_ref(dims), int(num_splits), _ptr(workspace), int(workspace_bytes),
-                                    _ptr(out), _ptr(lse), _ptr(stream))
+                                    _ptr(sinks), _ptr(out), _ptr(lse), _ptr(stream))
 
 
 def paged_decode_num_splits(dims, max_seq_len_hint: int = 0) -> int:
@@ -203,9 +203,9 @@ def paged_decode_status_string(status: int) -> str:
 
 # ---- torch conveniences (memory and streams only) ---------------------------
 
-def dims_for(q, k_cache, block_table, causal: bool = False) -> pkd_dims:
+def dims_for(q, k_cache, block_table, causal: bool = False, window: int = 0) -> pkd_dims:
     """pkd_dims from torch tensors q [B,Hq,D] (or [B,q_len,Hq,D]), k_cache [P,ps,Hkv,D],
-    block_table [B,MP]."""
+    block_table [B,MP]; window 0 = no sliding window."""
     import torch
     if q.dim() == 4:
         B, q_len, hq, d = q.shape
@@ -221,7 +221,8 @@ def dims_for(q, k_cache, block_table, causal: bool = False) -> pkd_dims:
         kvd = PKD_DTYPE_FP8_E4M3
     else:
         raise TypeError(f"unsupported KV-cache dtype {k_cache.dtype}")
-    return pkd_dims(B, hq, hkv, d, ps, num_pages, block_table.shape[1], kvd, q_len, int(bool(causal)))
+    return pkd_dims(B, hq, hkv, d, ps, num_pages, block_table.shape[1], kvd, q_len, int(bool(causal)),
+                    int(window))
 
 
 def current_stream_handle(device) -> int:
@@ -231,10 +232,11 @@ def current_stream_handle(device) -> int:
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=None, v_scale=None,
            num_splits: int = 0, out=None, lse=None, workspace=None, stream: Optional[int] = None,
-           causal: bool = False):
+           causal: bool = False, window: int = 0, sinks=None):
     """Run paged_decode on torch device tensors; returns (out bf16 shaped like q, lse fp32
     [B,Hq] or [B,q_len,Hq]).  q is [B,Hq,D], or [B,q_len,Hq,D] for several query tokens
-    per sequence (with the causal mask when `causal`)."""
+    per sequence (with the causal mask when `causal`); `window` > 0 is a sliding window
+    in tokens and `sinks` an fp32 [Hq] device tensor of sink logits."""
     import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("block_table", block_table), ("seq_lens", seq_lens)):
@@ -246,7 +248,9 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=Non
         raise TypeError("block_table and seq_lens must be int32")
     if v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache must match")
-    dims = dims_for(q, k_cache, block_table, causal)
+    if sinks is not None and (not sinks.is_cuda or sinks.dtype != torch.float32 or sinks.numel() != q.shape[-2]):
+        raise ValueError("sinks must be an fp32 device tensor of num_q_heads values")
+    dims = dims_for(q, k_cache, block_table, causal, window)
     dev = q.device
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
@@ -261,7 +265,7 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=Non
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = current_stream_handle(dev)
-    st = paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, out,
+    st = paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, scale, out,
                       lse, S, workspace, ws_bytes, stream)
     if st != PKD_OK:
         raise PkdError(st)
@@ -279,7 +283,7 @@ def append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=N
     if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
         raise TypeError("k_new and v_new must be bfloat16")
     kvd = PKD_DTYPE_FP8_E4M3 if k_cache.dtype == torch.float8_e4m3fn else PKD_DTYPE_BF16
-    dims = pkd_dims(0, hkv, hkv, d, ps, num_pages, 1, kvd, 1, 0)
+    dims = pkd_dims(0, hkv, hkv, d, ps, num_pages, 1, kvd, 1, 0, 0)
     max_pos = 0 if cos_sin is None else cos_sin.shape[0]
     if stream is None:
         stream = current_stream_handle(k_new.device)

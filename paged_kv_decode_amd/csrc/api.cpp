@@ -45,7 +45,7 @@ int32_t check_dims(const pkd_dims* d) {
   if (!d) return PKD_ERR_NULL_POINTER;
   if (d->batch < 0 || d->batch > 65535 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
       d->page_size < 1 || d->num_pages < 1 || d->max_pages_per_seq < 1 || d->q_len < 1 ||
-      d->q_len > PKD_MAX_Q_LEN || (d->causal != 0 && d->causal != 1))
+      d->q_len > PKD_MAX_Q_LEN || (d->causal != 0 && d->causal != 1) || d->window < 0)
     return PKD_ERR_BAD_DIMS;
   if (d->num_q_heads % d->num_kv_heads != 0) return PKD_ERR_GQA;
   if (!valid_head_dim(d->head_dim)) return PKD_ERR_HEAD_DIM;
@@ -127,12 +127,22 @@ size_t partial_bytes(const pkd_dims& d, int S, size_t* lse_offset) {
   return o + align256(rows * (size_t)S * sizeof(float));
 }
 
-// Tokens per split: the longest sequence the block table can hold, cut into S
-// equal pieces rounded up to PKD_SPLIT_ALIGN.  Every split of every sequence
-// then covers the same number of tokens (or is the sequence's shorter last
-// piece, or empty), so workgroups carry equal work whatever the length mix.
-int32_t split_chunk(const pkd_dims& d, int S) {
+// Most tokens one sequence's splits cover: what the block table can hold, or
+// with a sliding window the visible span of the q_len query tokens (window +
+// q_len - 1) plus up to 15 tokens before it (splits start on a 16-token group).
+int64_t visible_span(const pkd_dims& d) {
   const int64_t cap = (int64_t)d.max_pages_per_seq * d.page_size;
+  if (d.window <= 0) return cap;
+  const int64_t span = (int64_t)d.window + d.q_len - 1 + 15;
+  return span < cap ? span : cap;
+}
+
+// Tokens per split: the longest span a sequence can need, cut into S equal
+// pieces rounded up to PKD_SPLIT_ALIGN.  Every split of every sequence then
+// covers the same number of tokens (or is the sequence's shorter last piece,
+// or empty), so workgroups carry equal work whatever the length mix.
+int32_t split_chunk(const pkd_dims& d, int S) {
+  const int64_t cap = visible_span(d);
   const int64_t per = (cap + S - 1) / S;
   const int64_t c = (per + PKD_SPLIT_ALIGN - 1) / PKD_SPLIT_ALIGN * PKD_SPLIT_ALIGN;
   return (int32_t)(c < INT32_MAX ? c : INT32_MAX);
@@ -149,7 +159,8 @@ int32_t heuristic_splits(const pkd_dims& d, int32_t max_len) {
   const int64_t work = (int64_t)d.batch * d.num_kv_heads * head_groups(d);
   if (work <= 0 || work >= target) return 1;
   int64_t s = (target + work - 1) / work;
-  const int64_t by_len = (max_len + 255) / 256;  // keep at least ~256 tokens per split
+  const int64_t span = max_len < visible_span(d) ? max_len : visible_span(d);
+  const int64_t by_len = (span + 255) / 256;  // keep at least ~256 tokens per split
   if (s > by_len) s = by_len;
   if (s < 1) s = 1;
   if (s > PKD_MAX_SPLITS) s = PKD_MAX_SPLITS;
@@ -173,6 +184,7 @@ pkd::SplitParams make_split_params(const pkd_dims& d, const void* q, const void*
   p.group = d.num_q_heads / d.num_kv_heads;
   p.q_len = d.q_len;
   p.causal = d.causal;
+  p.window = d.window;
   p.rows_kv = rows_per_kv(d);
   p.head_groups = head_groups(d);
   p.page_size = d.page_size;
@@ -187,7 +199,7 @@ bool aligned(const void* p, uintptr_t bytes) { return ((uintptr_t)p & (bytes - 1
 
 int32_t check_inputs(const pkd_dims* dims, const void* q, const void* k, const void* v,
                      const int32_t* bt, const int32_t* lens, const float* ks, const float* vs,
-                     float scale) {
+                     float scale, const float* sinks = nullptr) {
   const int32_t st = check_dims(dims);
   if (st != PKD_OK) return st;
   if (!q || !k || !v || !bt || !lens) return PKD_ERR_NULL_POINTER;
@@ -196,7 +208,7 @@ int32_t check_inputs(const pkd_dims* dims, const void* q, const void* k, const v
   if (!fp8 && (ks || vs)) return PKD_ERR_SCALES;
   if (!std::isfinite(scale)) return PKD_ERR_BAD_DIMS;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(bt, 4) || !aligned(lens, 4) ||
-      !aligned(ks, 4) || !aligned(vs, 4))
+      !aligned(ks, 4) || !aligned(vs, 4) || !aligned(sinks, 4))
     return PKD_ERR_ALIGNMENT;
   return PKD_OK;
 }
@@ -320,6 +332,7 @@ pkd::BalancedParams make_balanced_params(const pkd_dims& d, const void* q, const
   b.group = d.num_q_heads / d.num_kv_heads;
   b.q_len = d.q_len;
   b.causal = d.causal;
+  b.window = d.window;
   b.rows_kv = rows_per_kv(d);
   b.head_groups = head_groups(d);
   b.hpg = heads_per_slot(d);
@@ -344,9 +357,12 @@ int32_t run_partition(const pkd_dims& d, const void* q, const void* k, const voi
   return launch_partition(d, p, false, s);
 }
 
-// Merge phase of a split plan from the workspace.
-int32_t run_finish(const pkd_dims& d, const void* ws, void* out, float* lse, const Plan& pl, hipStream_t s) {
+// Merge phase of a split plan from the workspace (sinks: [Hq] or null).
+int32_t run_finish(const pkd_dims& d, const void* ws, const float* sinks, void* out, float* lse,
+                   const Plan& pl, hipStream_t s) {
   pkd::MergeParams m{};
+  m.sinks = sinks;
+  m.hq = d.num_q_heads;
   m.o_part = static_cast<const float*>(ws);
   m.lse_part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + pl.lse_off);
   m.out = static_cast<uint16_t*>(out);
@@ -356,7 +372,6 @@ int32_t run_finish(const pkd_dims& d, const void* ws, void* out, float* lse, con
     m.balanced = 1;
     m.prefix = reinterpret_cast<const int64_t*>(static_cast<const uint8_t*>(ws) + pl.prefix_off);
     m.batch = d.batch;
-    m.hq = d.num_q_heads;
     m.hkv = d.num_kv_heads;
     m.group = d.num_q_heads / d.num_kv_heads;
     m.head_groups = head_groups(d);
@@ -385,9 +400,9 @@ int32_t paged_decode_launches(const pkd_dims* dims, int32_t num_splits) {
 
 int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
-                     const float* v_scale, float scale, void* out, float* lse, int32_t num_splits,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
+                     const float* v_scale, const float* sinks, float scale, void* out, float* lse,
+                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, sinks);
   if (st != PKD_OK) return st;
   if (!out) return PKD_ERR_NULL_POINTER;
   st = check_out_ws(out, lse, workspace);
@@ -404,6 +419,7 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
                                            v_scale, scale, 1);
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
+    p.sinks = sinks;
     return launch_partition(*dims, p, true, s);
   }
   if (pl.balanced && balanced_fused(*dims)) {
@@ -413,6 +429,7 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
     b.fused = 1;
     b.out = static_cast<uint16_t*>(out);
     b.lse = lse;
+    b.sinks = sinks;
     b.seg_count = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + pl.count_off);
     b.epoch = next_epoch();
     return pkd::launch_balanced(b, dims->head_dim, dims->kv_dtype == PKD_DTYPE_FP8_E4M3, s) == hipSuccess
@@ -421,7 +438,7 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
   st = run_partition(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, workspace,
                      pl, s);
   if (st != PKD_OK) return st;
-  return run_finish(*dims, workspace, out, lse, pl, s);
+  return run_finish(*dims, workspace, sinks, out, lse, pl, s);
 }
 
 int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* k_cache,
@@ -444,12 +461,13 @@ int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* 
 }
 
 int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void* workspace,
-                            size_t workspace_bytes, void* out, float* lse, void* stream) {
+                            size_t workspace_bytes, const float* sinks, void* out, float* lse, void* stream) {
   int32_t st = check_dims(dims);
   if (st != PKD_OK) return st;
   if (!out) return PKD_ERR_NULL_POINTER;
   st = check_out_ws(out, lse, workspace);
   if (st != PKD_OK) return st;
+  if (!aligned(sinks, 4)) return PKD_ERR_ALIGNMENT;
   Plan pl;
   st = make_plan(*dims, num_splits, &pl);
   if (st != PKD_OK) return st;
@@ -457,7 +475,7 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
   if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
   if (dims->batch == 0) return PKD_OK;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
-  return run_finish(*dims, workspace, out, lse, pl, static_cast<hipStream_t>(stream));
+  return run_finish(*dims, workspace, sinks, out, lse, pl, static_cast<hipStream_t>(stream));
 }
 
 int32_t paged_decode_check_tables(const pkd_dims* dims, const int32_t* block_table,

@@ -8,7 +8,8 @@
 // in the sglang fuse/overlap catalogue).  Partials of empty splits carry
 // lse = -inf and weigh 0; a row with no non-empty split gets out = 0 and
 // lse = -inf.  Splits are summed in index order, so the result is
-// deterministic.
+// deterministic.  With sink logits the head's sink joins the denominator at
+// the end (out scaled by e^(lse - lse'), lse' = ln(e^lse + e^sink)).
 //
 // Also: the optional block-table / length validation kernel.
 #include "merge_row.hpp"
@@ -120,7 +121,8 @@ __global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(co
     }
     r.M = Mx;
   }
-  r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane);
+  r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane,
+          p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY);
 }
 
 // Counts sequences with a length outside [0, max_pages * page_size] and used

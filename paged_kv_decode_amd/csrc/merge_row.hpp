@@ -24,6 +24,22 @@ __device__ __forceinline__ float merge_wave_max(float x) {
   return x;
 }
 
+// Folds a query head's sink logit into a finished row (natural-log lse):
+// lse' = ln(e^lse + e^sink); returns the factor e^(lse - lse') that scales the
+// output (0 for a row that saw no token, whose lse becomes the sink).
+__device__ __forceinline__ float fold_sink(float& lse, float sink) {
+  if (sink == -INFINITY) return 1.f;
+  if (lse == -INFINITY) {
+    lse = sink;
+    return 0.f;
+  }
+  const float mx = fmaxf(lse, sink);
+  const float l2 = mx + log1pf(expf(-fabsf(lse - sink)));
+  const float f = expf(lse - l2);
+  lse = l2;
+  return f;
+}
+
 // One wave's share of a row: partials k < mine, LSE at lp[k * ls], row at
 // op[k * os + d].  Lanes run along the head dimension (EPL elements each).
 // After run(), M is the maximum LSE seen, W the (wave-reduced) sum of
@@ -151,19 +167,23 @@ struct RowMerge {
   }
 
   // Writes the normalised row (bf16, round-to-nearest-even) and, from lane 0,
-  // its natural-log LSE (when lse is not null).
-  __device__ __forceinline__ void store(uint16_t* out_row, float* lse, int lane) const {
+  // its natural-log LSE (when lse is not null).  A finite sink logit joins the
+  // denominator: the row is scaled by 1 / (1 + e^(sink - lse)) and the LSE
+  // becomes ln(e^lse + e^sink); a row with no partial then gets 0 and the sink.
+  __device__ __forceinline__ void store(uint16_t* out_row, float* lse, int lane, float sink = -INFINITY) const {
+    float l = M != -INFINITY ? M + log2f(W) * kMergeLn2 : -INFINITY;
+    const float f = fold_sink(l, sink);
     if (lane * EPL < D) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float v = M != -INFINITY ? o[e] / W : 0.f;
+        const float v = M != -INFINITY ? (o[e] / W) * f : 0.f;
         const __bf16 h = (__bf16)v;
         uint16_t bits;
         __builtin_memcpy(&bits, &h, 2);
         out_row[lane * EPL + e] = bits;
       }
     }
-    if (lane == 0 && lse) *lse = M != -INFINITY ? M + log2f(W) * kMergeLn2 : -INFINITY;
+    if (lane == 0 && lse) *lse = l;
   }
 };
 

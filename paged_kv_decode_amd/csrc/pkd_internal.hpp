@@ -27,11 +27,14 @@ struct SplitParams {
   float qk_scale_log2;         // scale * log2(e): scores are kept in base-2 units
   int32_t hq, hkv, group;      // group = G = Hq / Hkv
   int32_t q_len, causal;       // query tokens per sequence; causal mask on (1) or off (0)
+  int32_t window;              // sliding window in tokens (0: none)
+  const float* sinks;          // [Hq] sink logits or null (direct mode only)
   int32_t rows_kv;             // packed rows per KV head: q_len * G
   int32_t head_groups;         // ceil(rows_kv / 16): packed rows are taken 16 per workgroup
   int32_t page_size, max_pages;
   int32_t num_splits;
-  int32_t chunk;               // tokens per split (a multiple of kSplitAlign, or >= every length)
+  int32_t chunk;               // tokens per split (a multiple of kSplitAlign, or >= every visible span);
+                               // splits start at the sequence's first visible 16-token group
 };
 
 // Arguments of the balanced persistent partition kernel.
@@ -49,6 +52,8 @@ struct BalancedParams {
   float qk_scale_log2;
   int32_t batch, hq, hkv, group, head_groups;
   int32_t q_len, causal, rows_kv;  // as in SplitParams
+  int32_t window;              // as in SplitParams; a sequence's groups start at its first visible one
+  const float* sinks;          // [Hq] or null (fused: applied to out/lse)
   int32_t hpg;                 // rows per slot: min(rows_kv, 16)
   int32_t page_size, max_pages;
   int32_t num_workers;         // workgroups in the grid
@@ -88,6 +93,7 @@ struct MergeParams {
   const int64_t* prefix;       // balanced layout fields
   int32_t batch, hq, hkv, group, head_groups, hpg, num_workers;
   int32_t q_len;               // balanced layout: rows are (b * q_len + i) * Hq + h
+  const float* sinks;          // [Hq] sink logits or null; row r has head r % hq (hq set whenever sinks is)
 };
 
 // Arguments of the paged KV append kernel.

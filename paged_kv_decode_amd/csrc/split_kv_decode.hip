@@ -59,20 +59,24 @@ split_kv_kernel(const SplitParams p) {
 
   const int L = p.seq_lens[b];
   const int chunk = p.chunk;  // tokens per split, the same for every sequence
-  const int s0 = (int)min((int64_t)split * chunk, (int64_t)L);
-  const int s1 = min(s0 + chunk, L);
+  // Splits cover [lo, L): tokens below the first visible 16-token group (with
+  // a sliding window) are never read.
+  const int lo = seq_first_token(p, L);
+  const int s0 = (int)min((int64_t)lo + (int64_t)split * chunk, (int64_t)L);
+  const int s1 = (int)min((int64_t)s0 + chunk, (int64_t)L);
   const int heads_here = min(kHeadsPerGroup, p.rows_kv - hg * kHeadsPerGroup);
   // Memory rows of the workgroup's packed rows (query token, head).
   __shared__ int64_t s_rows[kHeadsPerGroup];
 
   if (s0 >= s1) {
-    // Empty split (or an empty sequence): o = 0, lse = -inf.
+    // Empty split (or an empty sequence): o = 0, lse = -inf (the sink logit
+    // for a direct row with a sink).
     for (int idx = tid; idx < heads_here * D; idx += kWaves * 64) {
       const int hh = idx / D, d = idx - (idx / D) * D;
       const int64_t row = packed_row(b, kvh, hg * kHeadsPerGroup + hh, p.q_len, p.hq, p.group);
       if constexpr (DIRECT) {
         p.out[row * D + d] = 0;
-        if (d == 0 && p.lse) p.lse[row] = -INFINITY;
+        if (d == 0 && p.lse) p.lse[row] = p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY;
       } else {
         p.o_part[(row * S + split) * D + d] = 0.f;
         if (d == 0) p.lse_part[row * S + split] = -INFINITY;
@@ -129,10 +133,10 @@ split_kv_kernel(const SplitParams p) {
 
   uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;  // this wave's V[TT][VS]
   // Tiles wave, wave + 4, wave + 8, ...
-  run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, lr.end, vs, fetch, issue);
+  run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, lr.start, lr.end, vs, fetch, issue);
 
   const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
-  wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
+  auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
     const int64_t row = s_rows[hh];
     if constexpr (DIRECT) {
       *reinterpret_cast<bf16x4*>(p.out + row * D + d0) = to_bf16x4(o);
@@ -141,14 +145,20 @@ split_kv_kernel(const SplitParams p) {
       *reinterpret_cast<f32x4*>(p.o_part + (row * S + split) * D + d0) = o;
       if (d0 == 0) p.lse_part[row * S + split] = lse_nat;
     }
-  });
+  };
+  if (DIRECT && p.sinks)
+    wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, store,
+                       [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
+  else
+    wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, store, NoSink());
 }
 
 // ---- balanced persistent kernel ---------------------------------------------
 //
 // The work space is the sequence of segments s = (b * Hkv + kvh) * HG + hg
 // (HG head groups of up to 16 query rows per KV head), segment s holding the
-// n_b = ceil(L_b / 16) 16-token groups of sequence b; T groups in all.  With
+// n_b = ceil((L_b - lo_b) / 16) 16-token groups of sequence b, from its first
+// visible group lo_b (0 without a sliding window); T groups in all.  With
 // NWE = min(workgroups, T) active workgroups, workgroup w takes groups
 // [floor(w T / NWE), floor((w + 1) T / NWE)); its waves interleave the
 // tiles of each piece (the part of one segment inside the range) and combine
@@ -189,7 +199,7 @@ balanced_kernel(const BalancedParams p) {
     for (int i = 0; i < PER; ++i) {
       const int bb = tid * PER + i;
       const int L = bb < B ? p.seq_lens[bb] : 0;
-      sum += (int64_t)((L + 15) >> 4) * SPB;
+      sum += (int64_t)((L - seq_first_token(p, L) + 15) >> 4) * SPB;
       run[i] = sum;
     }
     int64_t incl = sum;  // inclusive scan of the thread sums within the wave
@@ -216,14 +226,15 @@ balanced_kernel(const BalancedParams p) {
   const int64_t nwe = min((int64_t)p.num_workers, T);
   const int64_t w = blockIdx.x;
   if (p.fused) {
-    // Sequences of length 0 have no piece: out = 0, lse = -inf for all their
-    // q_len * Hq rows (workgroup bb % W).
+    // Sequences of length 0 have no piece: out = 0, lse = -inf (or the head's
+    // sink logit) for all their q_len * Hq rows (workgroup bb % W).
     const int rows_seq = p.q_len * p.hq;
     for (int bb = (int)w; bb < B; bb += p.num_workers) {
       if (spre[bb + 1] != spre[bb]) continue;
       for (int i = tid; i < rows_seq * D; i += NWV * 64) p.out[(int64_t)bb * rows_seq * D + i] = 0;
       if (p.lse)
-        for (int i = tid; i < rows_seq; i += NWV * 64) p.lse[(int64_t)bb * rows_seq + i] = -INFINITY;
+        for (int i = tid; i < rows_seq; i += NWV * 64)
+          p.lse[(int64_t)bb * rows_seq + i] = p.sinks ? p.sinks[i % p.hq] : -INFINITY;
     }
   }
   if (w >= nwe) return;  // the whole workgroup leaves together
@@ -259,13 +270,16 @@ balanced_kernel(const BalancedParams p) {
     const int idx = first_page + A.lane;
     return idx < p.max_pages ? p.block_table[(int64_t)bb * p.max_pages + idx] : 0;
   };
-  int window = load_window(b, grp * 16 / ps);
+  // First visible token (16-aligned) of a sequence: where its groups start.
+  auto first_of = [&](int bb) -> int { return p.window > 0 ? seq_first_token(p, p.seq_lens[bb]) : 0; };
+  int lo = first_of(b);
+  int window = load_window(b, (lo + grp * 16) / ps);
 
   while (pos < hi) {
     const int gend = (int)min(nb, (int64_t)grp + (hi - pos));
     const int L = p.seq_lens[b];
-    const int s0 = grp * 16;
-    const int s1 = min(gend * 16, L);
+    const int s0 = lo + grp * 16;
+    const int s1 = min(lo + gend * 16, L);
     const int lim = s1 - 1;
     const int kvh = seg / p.head_groups;
     const int hg = seg - kvh * p.head_groups;
@@ -281,7 +295,8 @@ balanced_kernel(const BalancedParams p) {
       nseg = 0;
       do { ++nbq; } while (nbq < B && spre[nbq + 1] == spre[nbq]);
     }
-    const int next_window = npos < hi ? load_window(nbq, 0) : 0;
+    const int nlo = npos < hi ? (nbq == b ? lo : first_of(nbq)) : 0;
+    const int next_window = npos < hi ? load_window(nbq, nlo / ps) : 0;
 
     A.load_q(p.q, lr.row, lr.valid);
     A.qk_scale = p.qk_scale_log2;
@@ -304,7 +319,7 @@ balanced_kernel(const BalancedParams p) {
       A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, head_off, R, idle);
     };
     const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
-    run_tiles<D, FP8, Pages>(A, wave, NWV, ntiles, s0, lr.end, vs, fetch, issue);
+    run_tiles<D, FP8, Pages>(A, wave, NWV, ntiles, s0, lr.start, lr.end, vs, fetch, issue);
 
     // This segment's pieces are those of workgroups w_first .. w_last, at
     // slots w + s (s = b * SPB + seg).
@@ -315,11 +330,16 @@ balanced_kernel(const BalancedParams p) {
     const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
     if (p.fused && npieces == 1) {
       // The whole segment is this piece: write the result directly.
-      wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
+      auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
         const int64_t row = s_rows[hh];
         *reinterpret_cast<bf16x4*>(p.out + row * D + d0) = to_bf16x4(o);
         if (d0 == 0 && p.lse) p.lse[row] = lse_nat;
-      });
+      };
+      if (p.sinks)
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, store,
+                                [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
+      else
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, store, NoSink());
       __syncthreads();  // the LDS is reused by the next piece
     } else {
       // This piece's partial, for the group's heads.
@@ -330,7 +350,7 @@ balanced_kernel(const BalancedParams p) {
         wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
           *reinterpret_cast<f32x4*>(orow + hh * D + d0) = o;
           if (d0 == 0) lrow[hh] = lse_nat;
-        });
+        }, NoSink());
       } else {
         // Agent-scope stores write through to the coherent copy that another
         // XCD's workgroup will read; waiting for their acknowledgement before the
@@ -341,7 +361,7 @@ balanced_kernel(const BalancedParams p) {
           for (int i = 0; i < 4; ++i)
             __hip_atomic_store(orow + hh * D + d0 + i, o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (d0 == 0) __hip_atomic_store(lrow + hh, lse_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        });
+        }, NoSink());
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are acknowledged
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -382,7 +402,8 @@ balanced_kernel(const BalancedParams p) {
               RM r;
               r.run(lp0 + hh, ls, op0 + hh * D, os, npieces, lane);
               const int64_t row = s_rows[hh];
-              r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane);
+              r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane,
+                      p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY);
             }
           } else {
             constexpr int RCS = RC < 2 ? 2 : RC;  // (the branch above takes RC < 2)
@@ -401,7 +422,8 @@ balanced_kernel(const BalancedParams p) {
                   RM r;
                   r.finish(st[k], npieces, lane);
                   const int64_t row = s_rows[hh];
-                  r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane);
+                  r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane,
+                          p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY);
                 }
               }
             }
@@ -416,6 +438,7 @@ balanced_kernel(const BalancedParams p) {
     seg = nseg;
     if (nbq != b) {
       b = nbq;
+      lo = nlo;
       if (b < B) nb = (spre[b + 1] - spre[b]) / SPB;
     }
     window = next_window;

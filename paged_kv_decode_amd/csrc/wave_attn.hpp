@@ -313,9 +313,9 @@ struct WaveAttn {
     return idx < C::NBLK ? k_row_token<C::KP>(idx, n) : (idx - C::NBLK) * C::RPI + v_rig;
   }
 
-  // One tile: V to LDS, QK^T, online softmax, PV.  Tokens at or past s1 (this
-  // lane's packed row's end) are masked.
-  __device__ __forceinline__ void process(const Regs& R, int tb, int s1, uint16_t* vs) {
+  // One tile: V to LDS, QK^T, online softmax, PV.  Tokens before s_lo or at or
+  // past s1 (this lane's packed row's window start and end) are masked.
+  __device__ __forceinline__ void process(const Regs& R, int tb, int s_lo, int s1, uint16_t* vs) {
     // V -> LDS, row-major bf16 (16-byte writes).
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
@@ -364,7 +364,7 @@ struct WaveAttn {
       for (int i = 0; i < 4; ++i) {
         const int tok = tb + s_out_token<C::KP>(blk, g, i);
         const float x = sacc[blk][i] * qk_scale;
-        sacc[blk][i] = tok < s1 ? x : -INFINITY;
+        sacc[blk][i] = (tok < s1 && tok >= s_lo) ? x : -INFINITY;
         mt = fmaxf(mt, sacc[blk][i]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -448,6 +448,7 @@ __device__ __forceinline__ int64_t packed_row(int b, int kvh, int r, int q_len, 
 struct LaneRow {
   int64_t row;
   bool valid;
+  int start;  // first position the row sees (its sliding window's lower end; 0 without a window)
   int end;
 };
 template <typename P>
@@ -457,8 +458,19 @@ __device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, 
   lr.valid = r < p.rows_kv;
   const int rr = lr.valid ? r : hg * kHeadsPerGroup;
   lr.row = packed_row(b, kvh, rr, p.q_len, p.hq, p.group);
-  lr.end = p.causal ? min(s1, L - p.q_len + rr / p.group + 1) : s1;
+  const int pos = L - p.q_len + rr / p.group;  // the query token's position
+  lr.end = p.causal ? min(s1, pos + 1) : s1;
+  lr.start = p.window > 0 ? max(pos - p.window + 1, 0) : 0;
   return lr;
+}
+
+// First token of sequence b that any of its query tokens sees, rounded down to
+// a multiple of 16 (tiles start on 16-token groups): the lowest window start
+// when there is a window, else 0.  Tokens below it are never read.
+template <typename P>
+__device__ __forceinline__ int seq_first_token(const P& p, int L) {
+  if (p.window <= 0) return 0;
+  return max(L - p.q_len - p.window + 1, 0) & ~15;
 }
 
 // Tiles first, first + step, ... (< ntiles): while tile t is processed the
@@ -469,7 +481,7 @@ __device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, 
 // never consumed.
 template <int D, bool FP8, typename Pages, typename Fetch, typename Issue>
 __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int step, int ntiles, int s0,
-                                          int s1, uint16_t* vs, Fetch fetch, Issue issue) {
+                                          int s_lo, int s1, uint16_t* vs, Fetch fetch, Issue issue) {
   typedef Cfg<D, FP8> C;
   if (first >= ntiles) return;
   auto nxt = [&](int t) { return t + step < ntiles ? t + step : t; };
@@ -485,7 +497,7 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
     int t2 = nxt(t1);
     fetch(t2, pa);
     __builtin_amdgcn_sched_barrier(0);
-    A.process(ra, s0 + t * C::TT, s1, vs);
+    A.process(ra, s0 + t * C::TT, s_lo, s1, vs);
     if (t1 == t) break;
     t = t1;
     t1 = t2;
@@ -493,7 +505,7 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
     t2 = nxt(t1);
     fetch(t2, pb);
     __builtin_amdgcn_sched_barrier(0);
-    A.process(rb, s0 + t * C::TT, s1, vs);
+    A.process(rb, s0 + t * C::TT, s_lo, s1, vs);
     if (t1 == t) break;
     t = t1;
     t1 = t2;
@@ -505,13 +517,14 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
 // row of the group to store, four dims at a time: store(hh, d0, o4, lse_nat),
 // o4 = dims d0 .. d0 + 3 of o = sum_w e_w O_w * vsc / sum_w e_w l_w with
 // e_w = 2^(m_w - max m), and the natural-log LSE.  A row that saw no token in
-// any wave gets o = 0 and lse = -inf.  The per-row weights e_w * vsc / den are
-// computed once per row, then each element is a short weighted sum of the
-// staged wave rows.  Ends with the LDS still in use: synchronise before
-// reusing it.
-template <int D, bool FP8, int NWV = kWaves, typename Store>
+// any wave gets o = 0 and lse = -inf.  sink_of(hh) is row hh's sink logit
+// (-inf for none), folded in as fold_sink describes; partials take none.  The
+// per-row weights e_w * vsc / den are computed once per row, then each element
+// is a short weighted sum of the staged wave rows.  Ends with the LDS still in
+// use: synchronise before reusing it.
+template <int D, bool FP8, int NWV = kWaves, typename Store, typename SinkOf>
 __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* smem, int wave, int tid,
-                                           int heads_here, float vsc, Store store) {
+                                           int heads_here, float vsc, Store store, SinkOf sink_of) {
   typedef Cfg<D, FP8> C;
   constexpr int RWS = NWV + 4;                 // per-row table stride (floats): NWV weights, then the LSE
   const float l_tot = A.l_total();
@@ -541,10 +554,12 @@ __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* s
       e[w] = __builtin_amdgcn_exp2f(mw[w * 16 + hh] - M_use);
       den += e[w] * lw[w * 16 + hh];
     }
-    const float sc = den > 0.f ? vsc / den : 0.f;
+    float lse_nat = (M_use + log2f(den)) * 0.69314718055994530942f;
+    const float f = fold_sink(lse_nat, sink_of(hh));
+    const float sc = den > 0.f ? vsc * f / den : 0.f;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) rw[hh * RWS + w] = e[w] * sc;
-    rw[hh * RWS + NWV] = (M_use + log2f(den)) * 0.69314718055994530942f;
+    rw[hh * RWS + NWV] = lse_nat;
   }
   __syncthreads();
   constexpr int Q4 = D / 4;
@@ -557,6 +572,11 @@ __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* s
     store(hh, d0, o, rw[hh * RWS + NWV]);
   }
 }
+
+// No sink (partials, and rows of a call without sinks).
+struct NoSink {
+  __device__ __forceinline__ float operator()(int) const { return -INFINITY; }
+};
 
 // Four fp32 values rounded to bf16 (round-to-nearest-even), as one 8-byte word.
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 o) {

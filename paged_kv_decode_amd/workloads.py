@@ -60,17 +60,21 @@ class WorkloadSpec:
         return 1.0 / math.sqrt(self.head_dim)
 
 
-def _spec(name, B, hq, hkv, d, ps, dtype, seed, seq_lens=None, len_range=None, q_len=1, causal=False):
+def _spec(name, B, hq, hkv, d, ps, dtype, seed, seq_lens=None, len_range=None, q_len=1, causal=False,
+          window=0, sinks=False):
     max_len = max(seq_lens) if seq_lens is not None else len_range[1]
     return WorkloadSpec(name, B, hq, hkv, d, ps, dtype, seed,
                         tuple(seq_lens) if seq_lens is not None else None,
-                        tuple(len_range) if len_range is not None else None, max_len, q_len, causal)
+                        tuple(len_range) if len_range is not None else None, max_len, q_len, causal,
+                        window, sinks)
 
 
 # The decode shapes the method is exercised on: a tiny case, a Llama-style
 # B=32 step, a B=128 step, long-context head-dim sweeps and an FP8 cache; and
 # the B=32 shape verifying 4 speculative tokens per sequence under the causal
-# mask (several query tokens per sequence).
+# mask (several query tokens per sequence); and the B=32 shape with a
+# 1024-token sliding window and a sink logit per query head (the window size
+# is a choice: the variant's source names none).
 WORKLOADS = {w.name: w for w in [
     _spec("tiny_b2_d64_ps16", 2, 4, 1, 64, 16, "bf16", 1, seq_lens=(37, 100)),
     _spec("llama_b32_d128_ps64", 32, 32, 8, 128, 64, "bf16", 2, len_range=(1024, 4096)),
@@ -84,6 +88,8 @@ WORKLOADS = {w.name: w for w in [
     _spec("fp8kv_b64_d128_ps64", 64, 64, 8, 128, 64, "fp8_e4m3", 5, len_range=(512, 8192)),
     _spec("verify_b32_q4_d128_ps64", 32, 32, 8, 128, 64, "bf16", 6, len_range=(1024, 4096),
           q_len=4, causal=True),
+    _spec("window1k_sinks_b32_d128_ps64", 32, 32, 8, 128, 64, "bf16", 7, len_range=(1024, 4096),
+          window=1024, sinks=True),
 ]}
 
 

@@ -49,7 +49,7 @@ def test_binding_constants_match_header():
 
 
 def test_dims_struct_layout():
-    assert ctypes.sizeof(b.pkd_dims) == 10 * 4
+    assert ctypes.sizeof(b.pkd_dims) == 11 * 4
 
 
 def test_status_strings_are_distinct():
@@ -61,14 +61,14 @@ def test_status_strings_are_distinct():
 
 def dims(**kw):
     base = dict(batch=2, num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=16, num_pages=10,
-                max_pages_per_seq=7, kv_dtype=b.PKD_DTYPE_BF16, q_len=1, causal=0)
+                max_pages_per_seq=7, kv_dtype=b.PKD_DTYPE_BF16, q_len=1, causal=0, window=0)
     base.update(kw)
     return b.pkd_dims(*[base[f] for f, _ in b.pkd_dims._fields_])
 
 
 def call(d, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, ks=None, vs=None, scale=0.125, out=FAKE,
-         lse=None, S=1, ws=None, ws_bytes=0):
-    return b.paged_decode(d, q, k, v, bt, lens, ks, vs, scale, out, lse, S, ws, ws_bytes, None)
+         lse=None, S=1, ws=None, ws_bytes=0, sinks=None):
+    return b.paged_decode(d, q, k, v, bt, lens, ks, vs, sinks, scale, out, lse, S, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -87,6 +87,7 @@ def call(d, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, ks=None, vs=None, scale=
     (dict(q_len=b.PKD_MAX_Q_LEN + 1), b.PKD_ERR_BAD_DIMS),
     (dict(causal=2), b.PKD_ERR_BAD_DIMS),
     (dict(causal=-1), b.PKD_ERR_BAD_DIMS),
+    (dict(window=-1), b.PKD_ERR_BAD_DIMS),
 ])
 def test_bad_dims_are_rejected(kw, status):
     d = dims(**kw)
@@ -97,7 +98,7 @@ def test_bad_dims_are_rejected(kw, status):
 
 def test_null_pointers_are_rejected():
     d = dims()
-    assert b.paged_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1, FAKE, None, 1, None, 0,
+    assert b.paged_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0.1, FAKE, None, 1, None, 0,
                           None) == b.PKD_ERR_NULL_POINTER
     for kw in ("q", "k", "v", "bt", "lens", "out"):
         assert call(d, **{kw: None}) == b.PKD_ERR_NULL_POINTER, kw
@@ -118,6 +119,7 @@ def test_misaligned_pointers_are_rejected():
     for kw in ("bt", "lens"):
         assert call(d, **{kw: FAKE + 2}) == b.PKD_ERR_ALIGNMENT, kw
     assert call(d, lse=FAKE + 1) == b.PKD_ERR_ALIGNMENT
+    assert call(d, sinks=FAKE + 2) == b.PKD_ERR_ALIGNMENT
     need = b.paged_decode_workspace_bytes(d, 3)
     assert call(d, S=3, ws=FAKE + 8, ws_bytes=need) == b.PKD_ERR_ALIGNMENT
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1)
@@ -125,6 +127,19 @@ def test_misaligned_pointers_are_rejected():
     assert b.paged_decode_merge(8, 2, 64, FAKE + 2, FAKE, FAKE, None, None) == b.PKD_ERR_ALIGNMENT
     assert b.paged_decode_merge(8, 2, 64, FAKE, FAKE, FAKE + 1, None, None) == b.PKD_ERR_ALIGNMENT
     assert b.paged_decode_check_tables(d, FAKE + 2, FAKE, FAKE, None) == b.PKD_ERR_ALIGNMENT
+
+
+def test_window_bounds_the_split_count():
+    """With a sliding window the splits cover only the visible span, so the
+    heuristic asks for no more splits than that span needs (a page size that
+    is not a multiple of 16 keeps it on the grid mode)."""
+    d = dims(batch=1, num_q_heads=8, num_kv_heads=8, page_size=8, max_pages_per_seq=4096, num_pages=4096)
+    full = b.paged_decode_num_splits(d, 0)
+    dw = dims(batch=1, num_q_heads=8, num_kv_heads=8, page_size=8, max_pages_per_seq=4096, num_pages=4096,
+              window=256)
+    windowed = b.paged_decode_num_splits(dw, 0)
+    assert 1 <= windowed < full
+    assert windowed <= (256 + 15 + 255) // 256
 
 
 def test_non_finite_scale_is_rejected():
@@ -194,11 +209,11 @@ def test_two_phase_argument_checks():
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1)
     # direct output has no split phases
     assert b.paged_decode_partition(d, *args, 1, FAKE, 1 << 20, None) == b.PKD_ERR_NUM_SPLITS
-    assert b.paged_decode_finish(d, 1, FAKE, 1 << 20, FAKE, None, None) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_finish(d, 1, FAKE, 1 << 20, None, FAKE, None, None) == b.PKD_ERR_NUM_SPLITS
     need = b.paged_decode_workspace_bytes(d, 4)
     assert b.paged_decode_partition(d, *args, 4, FAKE, need - 1, None) == b.PKD_ERR_WORKSPACE
-    assert b.paged_decode_finish(d, 4, None, need, FAKE, None, None) == b.PKD_ERR_WORKSPACE
-    assert b.paged_decode_finish(d, 4, FAKE, need, None, None, None) == b.PKD_ERR_NULL_POINTER
+    assert b.paged_decode_finish(d, 4, None, need, None, FAKE, None, None) == b.PKD_ERR_WORKSPACE
+    assert b.paged_decode_finish(d, 4, FAKE, need, None, None, None, None) == b.PKD_ERR_NULL_POINTER
     assert b.paged_decode_partition(d, *args, -7, FAKE, need, None) == b.PKD_ERR_NUM_SPLITS
 
 

@@ -6,6 +6,7 @@ Every call goes through the C ABI (paged_kv_decode_amd.binding).  Acceptance:
 is checked bit-exactly by one-hot probes; tails are NaN-poisoned and unused
 block-table entries are -1 so that any stray read shows.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -37,13 +38,15 @@ def dev(w):
              bt=w.block_table.to(cuda), lens=w.seq_lens.to(cuda))
     t["ks"] = None if w.k_scale is None else w.k_scale.to(cuda)
     t["vs"] = None if w.v_scale is None else w.v_scale.to(cuda)
+    t["sinks"] = None if getattr(w, "sinks", None) is None else w.sinks.to(cuda)
     return t
 
 
 def run(B, w, S=0, t=None, scale=None):
     t = t or dev(w)
     out, lse = B.decode(t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale if scale is None else scale,
-                        t["ks"], t["vs"], num_splits=S, causal=w.spec.causal)
+                        t["ks"], t["vs"], num_splits=S, causal=w.spec.causal, window=w.spec.window,
+                        sinks=t["sinks"])
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
 
@@ -423,7 +426,7 @@ def test_two_phases_equal_paged_decode(B, S, case):
     h = B.current_stream_handle(0)
     assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, S,
                                     ws, nbytes, h) == 0
-    assert B.paged_decode_finish(dims, S, ws, nbytes, out, lse, h) == 0
+    assert B.paged_decode_finish(dims, S, ws, nbytes, None, out, lse, h) == 0
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.cpu(), ref_lse)
@@ -447,7 +450,7 @@ def test_graph_replays(B, S):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            st = B.paged_decode(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, out, lse,
+            st = B.paged_decode(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, None, w.scale, out, lse,
                                 S, ws if nbytes else None, nbytes, B.current_stream_handle(0))
     torch.cuda.current_stream().wait_stream(side)
     assert st == 0
@@ -595,7 +598,7 @@ def test_multi_two_phases_equal_paged_decode(B, lens):
     h = B.current_stream_handle(0)
     assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, BAL,
                                     ws, nbytes, h) == 0
-    assert B.paged_decode_finish(dims, BAL, ws, nbytes, out, lse, h) == 0
+    assert B.paged_decode_finish(dims, BAL, ws, nbytes, None, out, lse, h) == 0
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.cpu().view(torch.int32), ref_lse.view(torch.int32))
@@ -632,7 +635,7 @@ def test_balanced_structures_parity(B, case):
     h = B.current_stream_handle(0)
     assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, BAL,
                                     ws, nbytes, h) == 0
-    assert B.paged_decode_finish(dims, BAL, ws, nbytes, o2, l2, h) == 0
+    assert B.paged_decode_finish(dims, BAL, ws, nbytes, None, o2, l2, h) == 0
     torch.cuda.synchronize()
     assert torch.equal(o2.cpu().view(torch.int16), out.view(torch.int16))
     assert torch.equal(l2.cpu().view(torch.int32), lse.view(torch.int32))
@@ -726,3 +729,130 @@ def test_append_then_decode(B):
                         w.v_scale.to(c), num_splits=0)
     torch.cuda.synchronize()
     check(out.cpu(), lse.cpu(), ref_o, ref_l, what="append then decode")
+
+
+# ---- sliding window and attention sinks ------------------------------------
+
+WINDOW_CASES = [
+    # (B, Hq, Hkv, D, ps, seq_lens, q_len, causal, window, sinks, dtype, seed)
+    (8, 16, 4, 128, 16, [0, 1, 63, 64, 65, 200, 1000, 17], 1, False, 64, False, "bf16", 401),
+    (4, 8, 2, 64, 16, [1, 2, 17, 300], 1, False, 1, True, "bf16", 402),        # the last token only
+    (3, 32, 4, 128, 64, [700, 50, 0], 1, False, 100, True, "bf16", 403),       # window not a multiple of 16
+    (3, 16, 4, 128, 16, [3, 40, 500], 4, True, 32, True, "bf16", 404),         # q_len 4 under the causal mask
+    (3, 8, 2, 128, 64, [90, 600, 5], 3, False, 20, True, "fp8_e4m3", 405),     # no mask, FP8
+    (3, 8, 2, 128, 24, [50, 333, 1], 2, True, 50, True, "bf16", 406),          # ps 24: per-row page lookups
+    (3, 8, 2, 64, 16, [10, 300, 0], 1, False, 10000, True, "bf16", 407),       # window past every length
+    (2, 4, 4, 32, 16, [20, 45], 1, False, 16, False, "bf16", 408),             # D 32, G 1
+    (2, 8, 1, 256, 64, [129, 700], 8, True, 70, True, "bf16", 409),            # D 256, q_len 8
+    (3, 8, 2, 128, 64, [4, 300, 0], 6, True, 0, True, "bf16", 410),            # sinks alone; L < q_len
+]
+
+
+def first_group(L, q_len, window):
+    """First token a sequence's splits start at: its lowest window start rounded
+    down to a multiple of 16 (0 without a window)."""
+    return (max(L - q_len - window + 1, 0) // 16) * 16 if window > 0 else 0
+
+
+def poison_below_window(w):
+    """NaN in every K and V row below each sequence's first visible 16-token
+    group: the kernels must never read them (the oracle does not either)."""
+    kc, vc = w.k_cache.clone(), w.v_cache.clone()
+    nan = float("nan")
+    ps = w.spec.page_size
+    for b, L in enumerate(w.seq_lens.tolist()):
+        for t_ in range(first_group(L, w.spec.q_len, w.spec.window)):
+            page = int(w.block_table[b, t_ // ps])
+            if kc.dtype == torch.float8_e4m3fn:
+                kc.view(torch.uint8)[page, t_ % ps] = 0x7F  # an E4M3FN NaN code
+                vc.view(torch.uint8)[page, t_ % ps] = 0x7F
+            else:
+                kc[page, t_ % ps] = nan
+                vc[page, t_ % ps] = nan
+    return kc, vc
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES)
+def test_window_and_sinks_parity(B, case):
+    """Every split mode against the oracle, with K/V below the window poisoned."""
+    bq, hq, hkv, d, ps, lens, ql, causal, win, sinks, dtype, seed = case
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, dtype, seed, q_len=ql, causal=causal, window=win,
+                           sinks=sinks)
+    kc, vc = poison_below_window(w)
+    w = dataclasses.replace(w, k_cache=kc, v_cache=vc)
+    ref = oracle_full(w)
+    t = dev(w)
+    for S in (1, 3, 0) + ((BAL,) if ps % 16 == 0 else ()):
+        out, lse = run(B, w, S, t)
+        check(out, lse, *ref, what=f"window {case} S={S}")
+    if sinks:
+        # Empty rows carry the sink as their LSE and a zero output.
+        ref_l = ref[1].reshape(bq, ql, hq)
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.allclose(ref_l[b], w.sinks.numpy()[None, :].astype(np.float64), atol=1e-6)
+
+
+def test_window_ignores_pages_below_it_bitwise(B):
+    """With a window of W, dropping the whole pages below each sequence's window
+    (shifting its block-table row and length) changes no bit of the result."""
+    ps, win = 16, 48  # window a multiple of the page size: the shifted table is whole pages
+    lens = [300, 48, 49, 500, 17]
+    w = wl.custom_workload(len(lens), 16, 4, 128, ps, lens, "bf16", seed=420, window=win)
+    t = dev(w)
+    bt_short = torch.full_like(w.block_table, -1)
+    lens_short = []
+    for b, L in enumerate(lens):
+        drop = max(L - win, 0) // ps  # whole pages below the window
+        n = -(-L // ps) - drop
+        bt_short[b, :n] = w.block_table[b, drop:drop + n]
+        lens_short.append(L - drop * ps)
+    t2 = dict(t, bt=bt_short.cuda(), lens=torch.tensor(lens_short, dtype=torch.int32, device="cuda"))
+    for S in (1, BAL):
+        o1, l1 = run(B, w, S, t)
+        o2, l2 = run(B, w, S, t2)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), S
+        assert torch.equal(l1, l2), S
+
+
+@pytest.mark.parametrize("S", [4, BAL])
+def test_two_phases_fold_sinks(B, S):
+    """paged_decode_finish folds the sinks in exactly as paged_decode does."""
+    lens = [700, 1, 0, 3000, 64]
+    w = wl.custom_workload(len(lens), 16, 2, 128, 64, lens, "bf16", seed=430, window=500, sinks=True)
+    t = dev(w)
+    ref_out, ref_lse = run(B, w, S, t)
+    dims = B.dims_for(t["q"], t["k"], t["bt"], window=500)
+    nbytes = B.paged_decode_workspace_bytes(dims, S)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+    h = B.current_stream_handle(0)
+    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, S,
+                                    ws, nbytes, h) == 0
+    assert B.paged_decode_finish(dims, S, ws, nbytes, t["sinks"], out, lse, h) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse.cpu(), ref_lse)
+
+
+def test_window_sinks_workload_sampled_rows(B):
+    """The B=32 step with a 1024-token window and sinks at full size: sampled
+    rows against the oracle in every mode, every row across the modes."""
+    spec = wl.WORKLOADS["window1k_sinks_b32_d128_ps64"]
+    w = wl.make_workload(spec, tail="nan")
+    kc, vc = poison_below_window(w)
+    w = dataclasses.replace(w, k_cache=kc, v_cache=vc)
+    t = dev(w)
+    rows = sample_rows(w, 40, seed=spec.seed)
+    ref_o, ref_l = oracle.paged_decode_ext_rows(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale,
+                                                rows, window=spec.window, sinks=w.sinks)
+    outs = {}
+    for S in (BAL, 0, 1, 8):
+        out, lse = run(B, w, S, t)
+        check(out.view(-1, spec.head_dim)[rows], lse.view(-1)[rows], ref_o, ref_l, what=f"window S={S}")
+        outs[S] = (out, lse)
+    for S in (BAL, 8):
+        a, b_ = outs[S], outs[1]
+        assert torch.all((a[0].float() - b_[0].float()).abs() <= 2e-2 + 2e-2 * b_[0].float().abs())
+        assert torch.all((a[1] - b_[1]).abs() <= 2e-3)
