@@ -71,6 +71,8 @@ def lib():
         L.pkd_oracle_bf16_round.restype = ctypes.c_uint16
         L.pkd_oracle_kv_append.argtypes = [_c_int] * 5 + [ctypes.c_int64] + [_p] * 5 + [_c_int] + [_p] * 4
         L.pkd_oracle_kv_append.restype = _c_int
+        L.pkd_oracle_decode_metadata.argtypes = [_c_int] * 8 + [_p] * 8
+        L.pkd_oracle_decode_metadata.restype = _c_int
         _lib = L
     return _lib
 
@@ -292,6 +294,31 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scal
     _check(lib().pkd_oracle_kv_append(hkv, d, ps, num_pages, 1 if kv_fp8 else 0, n, _ptr(kn), _ptr(vn), _ptr(sm),
                                       _ptr(pos), _ptr(cs), max_pos, _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs)))
     return kc, vc
+
+
+def decode_metadata(req_to_token, req_pool_indices, seq_lens, page_size, max_pages, q_len=1, window=0,
+                    extend=0):
+    """Decode metadata preparation (see paged_attention_ref.c).  req_to_token int32
+    [req_rows, req_stride]; req_pool_indices, seq_lens int64 [B].  Returns (dict of numpy
+    arrays cache_seqlens [B], cu_seqlens_k [B + 1], page_table [B, max_pages] and, with a
+    window, swa_seqlens [B], swa_page_table [B, max_pages]; count of invalid entries)."""
+    rt = np.ascontiguousarray(_raw(req_to_token, np.int32))
+    rp = np.ascontiguousarray(_raw(req_pool_indices, np.int64))
+    sl = np.ascontiguousarray(_raw(seq_lens, np.int64))
+    R, C = rt.shape
+    B = rp.shape[0]
+    assert sl.shape == (B,)
+    res = dict(cache_seqlens=np.empty(B, np.int32), cu_seqlens_k=np.empty(B + 1, np.int32),
+               page_table=np.empty((B, max_pages), np.int32))
+    if window > 0:
+        res["swa_seqlens"] = np.empty(B, np.int32)
+        res["swa_page_table"] = np.empty((B, max_pages), np.int32)
+    bad = lib().pkd_oracle_decode_metadata(B, R, C, int(page_size), int(max_pages), int(q_len), int(window),
+                                           int(extend), _ptr(rt), _ptr(rp), _ptr(sl), _ptr(res["cache_seqlens"]),
+                                           _ptr(res["cu_seqlens_k"]), _ptr(res["page_table"]),
+                                           _ptr(res.get("swa_seqlens")), _ptr(res.get("swa_page_table")))
+    _check(min(bad, 0))
+    return res, bad
 
 
 def bf16_value(bits: int) -> float:

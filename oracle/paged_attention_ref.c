@@ -62,8 +62,9 @@
  * oracle computes the plain result over the visible tokens, then folds the sink
  * in: lse' = ln(e^lse + e^sink), out' = out * e^(lse - lse').
  *
- * The file also defines the paged KV append that fills the cache (row f2,
- * pkd_oracle_kv_append, at the end).
+ * The file also defines the paged KV append that fills the cache
+ * (pkd_oracle_kv_append) and the decode metadata preparation that builds the
+ * block table and lengths (pkd_oracle_decode_metadata), both at the end.
  *
  * Work is spread over an optional pthread pool by (sequence, KV head) items.
  * The items are independent and each is computed in a fixed order, so the
@@ -631,4 +632,80 @@ int pkd_oracle_kv_append(int hkv, int head_dim, int page_size, int num_pages, in
   }
   free(y);
   return PKD_ORACLE_OK;
+}
+
+/* ---- decode metadata preparation ----------------------------------------
+ *
+ * The fused decode metadata setup of the sglang fuse/overlap catalogue
+ * (section 1, the flashattention backend's normal_decode_set_metadata row):
+ * from the serving runtime's per-request token map it builds what decode
+ * reads, in the order the row lists its steps.
+ *
+ * Inputs: req_to_token [req_rows][req_stride] int32, the KV slot
+ * (page * page_size + position in the page) of every token of every request
+ * row; req_pool_indices [batch] int64, the request row of batch entry b;
+ * seq_lens [batch] int64, its cached tokens before this step; extend, the
+ * tokens this step adds to every sequence.
+ *
+ *   seq-len cast/add:  L_b = seq_lens[b] + extend, stored as int32
+ *                      (cache_seqlens[b]);
+ *   prefix sum:        cu_seqlens_k[0] = 0, cu_seqlens_k[b + 1] =
+ *                      cu_seqlens_k[b] + L_b;
+ *   req-to-token gather and page-table divide: for every page j of
+ *                      sequence b (j < ceil(L_b / page_size)),
+ *                      page_table[b][j] = req_to_token[r_b][j * page_size]
+ *                      / page_size (the page of the page's first token; a
+ *                      negative slot gives -1); entries past the last page
+ *                      are -1;
+ *   SWA metadata (window W > 0): the pages from the first one that holds a
+ *                      visible position, f_b = max(L_b - q_len - W + 1, 0)
+ *                      / page_size, on: swa_page_table[b][j] =
+ *                      page_table[b][f_b + j], swa_seqlens[b] = L_b - f_b *
+ *                      page_size (the same sequence with its first f_b pages
+ *                      dropped, which decode with the same window reads as
+ *                      the full one).
+ *
+ * A batch entry whose request row is outside [0, req_rows) or whose L_b is
+ * outside [0, min(max_pages * page_size, req_stride)] is invalid: it is
+ * counted, its lengths are written as 0 and its table rows as -1.  Returns the
+ * count of invalid entries, or a negative status for bad arguments.
+ */
+static int64_t slot_page(int32_t slot, int page_size) { return slot >= 0 ? slot / page_size : -1; }
+
+int pkd_oracle_decode_metadata(int batch, int req_rows, int req_stride, int page_size, int max_pages, int q_len,
+                               int window, int extend, const int32_t* req_to_token,
+                               const int64_t* req_pool_indices, const int64_t* seq_lens, int32_t* cache_seqlens,
+                               int32_t* cu_seqlens_k, int32_t* page_table, int32_t* swa_seqlens,
+                               int32_t* swa_page_table) {
+  if (batch < 0 || req_rows < 1 || req_stride < 1 || page_size < 1 || max_pages < 1 || q_len < 1 || window < 0 ||
+      extend < 0 || !req_to_token || !req_pool_indices || !seq_lens || !cache_seqlens || !cu_seqlens_k ||
+      !page_table || (window > 0 && (!swa_seqlens || !swa_page_table)))
+    return PKD_ORACLE_BAD_ARG;
+  int bad = 0;
+  int64_t run = 0;
+  cu_seqlens_k[0] = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t r = req_pool_indices[b];
+    const int64_t L = seq_lens[b] + extend;
+    const int valid = r >= 0 && r < req_rows && L >= 0 && L <= (int64_t)max_pages * page_size && L <= req_stride;
+    bad += !valid;
+    const int64_t len = valid ? L : 0;
+    cache_seqlens[b] = (int32_t)len;
+    run += len;
+    cu_seqlens_k[b + 1] = (int32_t)run;
+    const int64_t n_pages = (len + page_size - 1) / page_size;
+    for (int j = 0; j < max_pages; ++j)
+      page_table[(int64_t)b * max_pages + j] =
+          j < n_pages ? (int32_t)slot_page(req_to_token[r * req_stride + (int64_t)j * page_size], page_size) : -1;
+    if (window > 0) {
+      int64_t lo = len - q_len - window + 1;
+      if (lo < 0) lo = 0;
+      const int64_t f = valid ? lo / page_size : 0;
+      swa_seqlens[b] = (int32_t)(len - f * page_size);
+      for (int j = 0; j < max_pages; ++j)
+        swa_page_table[(int64_t)b * max_pages + j] =
+            j < n_pages - f ? page_table[(int64_t)b * max_pages + f + j] : -1;
+    }
+  }
+  return bad;
 }

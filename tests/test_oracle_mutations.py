@@ -5,10 +5,12 @@ the kind a hand-written attention reference can plausibly contain: a wrong
 page or slot index, the wrong KV head for a query head, K and V swapped, the
 softmax scale dropped, a base-2 log-sum-exp, a wrong merge weight, a wrong
 split boundary, a wrong FP8 exponent bias, a wrong cache layout, a causal
-mask off by one or aligned to the wrong end, a window or sink slip, and in the KV append a RoPE sign,
-pairing or cos/sin swap, a wrong scale, rounding ties or slot.  The copy is compiled with the
-oracle's own build command and the pin suite
-(test_oracle_pins.py) is run against it in a child process through
+mask off by one or aligned to the wrong end, a window or sink slip; in the KV
+append a RoPE sign, pairing or cos/sin swap, a wrong scale, rounding ties or
+slot; in the decode metadata a prefix sum, gather stride, page divide,
+extension, request row or window page slip.  The copy is compiled with the
+oracle's own build command and the pin suite (test_oracle_pins.py) is run
+against it in a child process through
 PKD_ORACLE_LIB; every mutant must make at least one pin fail.  A control copy
 with no change must pass, which shows that the child really loads the copy.
 
@@ -114,6 +116,20 @@ MUTANTS = [
      "u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0u;"),
     ("append_writes_token_row_not_slot",
      "const int64_t dst = (slot * hkv + h) * (int64_t)D;", "const int64_t dst = ((n % capacity) * hkv + h) * (int64_t)D;"),
+    ("metadata_prefix_sum_inclusive",
+     "cu_seqlens_k[b + 1] = (int32_t)run;", "cu_seqlens_k[b] = (int32_t)run; cu_seqlens_k[b + 1] = (int32_t)run;"),
+    ("metadata_gather_stride_one",
+     "req_to_token[r * req_stride + (int64_t)j * page_size]", "req_to_token[r * req_stride + (int64_t)j]"),
+    ("metadata_no_page_divide",
+     "return slot >= 0 ? slot / page_size : -1;", "return slot >= 0 ? slot : -1;"),
+    ("metadata_extend_ignored",
+     "const int64_t L = seq_lens[b] + extend;", "const int64_t L = seq_lens[b];"),
+    ("metadata_pool_index_ignored",
+     "const int64_t r = req_pool_indices[b];", "const int64_t r = b;"),
+    ("metadata_swa_first_page_off_by_one",
+     "int64_t lo = len - q_len - window + 1;", "int64_t lo = len - q_len - window;"),
+    ("metadata_swa_length_not_shifted",
+     "swa_seqlens[b] = (int32_t)(len - f * page_size);", "swa_seqlens[b] = (int32_t)len;"),
 ]
 
 

@@ -7,7 +7,9 @@ oracle (a dropped term, a wrong sign, a wrong page/slot index, a transposed
 operand, the wrong KV head for a query head, a base-2 LSE) fails one of them.
 """
 import dataclasses
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -655,3 +657,109 @@ def test_sink_closed_form_and_empty_rows():
         assert np.max(np.abs(out[0, 0, h] - V[0, 0] * math.exp(s0) / z)) <= 1e-13
         assert abs(lse[0, 0, h] - math.log(z)) <= 1e-13
         assert np.all(out[1, 0, h] == 0) and lse[1, 0, h] == np.float32(sk[h])
+
+
+# ---- decode metadata preparation --------------------------------------------
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_metadata_hand_worked_example():
+    """The oracle reproduces a case worked by hand (tests/golden), with and
+    without the sliding-window tables."""
+    with open(os.path.join(GOLDEN, "decode_metadata_hand_example.json")) as f:
+        g = json.load(f)
+    rt = np.array(g["req_to_token"], np.int32)
+    rp = np.array(g["req_pool_indices"], np.int64)
+    sl = np.array(g["seq_lens"], np.int64)
+    e = g["expected"]
+    res, bad = oracle.decode_metadata(rt, rp, sl, g["page_size"], g["max_pages"], extend=g["extend"])
+    assert bad == e["invalid"]
+    assert res["cache_seqlens"].tolist() == e["cache_seqlens"]
+    assert res["cu_seqlens_k"].tolist() == e["cu_seqlens_k"]
+    assert res["page_table"].tolist() == e["page_table"]
+    for c in g["swa_cases"]:
+        r2, bad2 = oracle.decode_metadata(rt, rp, sl, g["page_size"], g["max_pages"], q_len=c["q_len"],
+                                          window=c["window"], extend=g["extend"])
+        assert bad2 == e["invalid"]
+        assert r2["page_table"].tolist() == e["page_table"]
+        assert r2["swa_seqlens"].tolist() == c["swa_seqlens"], c["why"]
+        assert r2["swa_page_table"].tolist() == c["swa_page_table"], c["why"]
+
+
+def token_map_from_block_table(bt, lens, ps, req_rows, stride, seed):
+    """A req_to_token pool holding the given block tables in shuffled request
+    rows: token t of sequence b is slot bt[b][t // ps] * ps + t % ps; every
+    other cell is random garbage.  Returns (req_to_token, req_pool_indices)."""
+    rng = np.random.default_rng(seed)
+    B = bt.shape[0]
+    rt = rng.integers(-5, 10 ** 6, size=(req_rows, stride)).astype(np.int32)
+    rows = rng.permutation(req_rows)[:B]
+    for b in range(B):
+        for t in range(int(lens[b])):
+            rt[rows[b], t] = bt[b, t // ps] * ps + t % ps
+    return rt, rows.astype(np.int64)
+
+
+@pytest.mark.parametrize("ps", [1, 16, 24, 64])
+def test_metadata_recovers_the_block_table_and_lengths(ps):
+    """Built from a token map that was itself built from a block table, the
+    page table is that block table (then -1), the lengths are the lengths plus
+    the extension, and the prefix sums step by them."""
+    rng = np.random.default_rng(ps)
+    B, MP, extend = 9, 7, 2
+    lens = rng.integers(0, MP * ps - extend + 1, size=B)
+    lens[0], lens[1] = 0, MP * ps - extend
+    bt = rng.permutation(B * MP * 3)[:B * MP].reshape(B, MP).astype(np.int32)
+    rt, rows = token_map_from_block_table(bt, lens + extend, ps, 2 * B + 3, MP * ps + 5, seed=ps)
+    res, bad = oracle.decode_metadata(rt, rows, lens.astype(np.int64), ps, MP, extend=extend)
+    assert bad == 0
+    L = lens + extend
+    assert res["cache_seqlens"].tolist() == L.tolist()
+    cu = res["cu_seqlens_k"].astype(np.int64)
+    assert cu[0] == 0 and np.diff(cu).tolist() == L.tolist()
+    for b in range(B):
+        n = -(-int(L[b]) // ps)
+        assert res["page_table"][b, :n].tolist() == bt[b, :n].tolist()
+        assert (res["page_table"][b, n:] == -1).all()
+
+
+@pytest.mark.parametrize("ps,q_len,window", [(16, 1, 40), (16, 3, 17), (64, 1, 100), (24, 2, 50), (1, 1, 5)])
+def test_metadata_swa_tables_drop_only_pages_below_the_window(ps, q_len, window):
+    """The SWA tables drop whole pages that hold no visible position and nothing
+    else, and the oracle's decode over them (same window) equals its decode
+    over the full tables bit for bit."""
+    lens = [0, 1, window - 1, window, window + q_len, 3 * window + 7, 500]
+    w = wl.custom_workload(len(lens), 8, 2, 64, ps, lens, "bf16", seed=ps + window, q_len=q_len, causal=True,
+                           window=window, sinks=True)
+    MP = w.block_table.shape[1]
+    bt = w.block_table.numpy()
+    rt, rows = token_map_from_block_table(bt, lens, ps, len(lens) + 4, MP * ps, seed=window)
+    res, bad = oracle.decode_metadata(rt, rows, np.array(lens, np.int64), ps, MP, q_len=q_len, window=window)
+    assert bad == 0
+    for b, L in enumerate(lens):
+        lo = max(L - q_len - window + 1, 0)
+        dropped = L - int(res["swa_seqlens"][b])
+        assert dropped % ps == 0 and dropped <= lo < dropped + ps
+        n = -(-L // ps)
+        f = dropped // ps
+        assert res["swa_page_table"][b, :n - f].tolist() == bt[b, f:n].tolist()
+        assert (res["swa_page_table"][b, n - f:] == -1).all()
+    full = oracle.paged_decode_ext(w.q, w.k_cache, w.v_cache, torch.from_numpy(res["page_table"]),
+                                   torch.from_numpy(res["cache_seqlens"]), w.scale, True, window, w.sinks)
+    swa = oracle.paged_decode_ext(w.q, w.k_cache, w.v_cache, torch.from_numpy(res["swa_page_table"]),
+                                  torch.from_numpy(res["swa_seqlens"]), w.scale, True, window, w.sinks)
+    assert np.array_equal(full[0], swa[0]) and np.array_equal(full[1], swa[1])
+
+
+def test_metadata_invalid_entries_are_counted_and_blanked():
+    rt = np.arange(4 * 32, dtype=np.int32).reshape(4, 32)
+    rp = np.array([0, -1, 4, 3, 2], np.int64)
+    sl = np.array([5, 5, 5, 40, -1], np.int64)  # 40 > 4 pages of 8 tokens; -1 < 0
+    res, bad = oracle.decode_metadata(rt, rp, sl, 8, 4, window=3)
+    assert bad == 4
+    assert res["cache_seqlens"].tolist() == [5, 0, 0, 0, 0]
+    assert res["cu_seqlens_k"].tolist() == [0, 5, 5, 5, 5, 5]
+    assert res["page_table"][0].tolist() == [0, -1, -1, -1]
+    assert (res["page_table"][1:] == -1).all() and (res["swa_page_table"][1:] == -1).all()
+    assert res["swa_seqlens"].tolist() == [5, 0, 0, 0, 0]
