@@ -243,6 +243,35 @@ def bench_append(steps, warmup, device, scrub):
             "pct_of_peak": 100.0 * nbytes / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def bench_metadata(w, steps, warmup, device, scrub, window):
+    """Decode metadata preparation for workload w's batch (token map in a pool of 4 B request
+    rows; each step adds one token; the sliding-window tables too when window > 0)."""
+    import torch
+    from paged_kv_decode_amd import binding as B
+    from paged_kv_decode_amd import workloads as wl
+    m = wl.metadata_workload(w, req_rows=4 * w.spec.batch, extend=1, seed=11)
+    rt, rp, sl = m.req_to_token.to(device), m.req_pool_indices.to(device), m.seq_lens.to(device)
+    call = lambda: B.metadata(rt, rp, sl, m.page_size, m.max_pages, window=window, extend=m.extend)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(device)
+    ms = []
+    for _ in range(steps):
+        scrub.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        res = call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    if not torch.equal(res["page_table"].cpu(), m.block_table.where(m.block_table >= 0, -1)):
+        raise RuntimeError("metadata: page table differs from the workload's block table")
+    return {"workload": w.spec.name + " token map", "batch": w.spec.batch, "window": window,
+            "us_per_call": 1e3 * sum(ms) / len(ms),
+            "note": "one launch; latency-bound (tens of KB moved), so no bandwidth figure"}
+
+
 def cpu_baseline(w, nbytes):
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -426,8 +455,11 @@ def main():
     if args.profile_only:
         return
     app = bench_append(args.steps, args.warmup, device, scrub)
+    meta = bench_metadata(primary_w, args.steps, args.warmup, device, scrub, window=1024)
     print(f"# {app['workload']}: {app['ms_per_call'] * 1e3:.1f} us/call {app['gbs']:.0f} GB/s = "
           f"{app['pct_of_peak']:.1f}% of peak", file=sys.stderr, flush=True)
+    print(f"# decode metadata (B={meta['batch']}, window {meta['window']}): {meta['us_per_call']:.1f} us/call",
+          file=sys.stderr, flush=True)
 
     p = results[PRIMARY]
     roof_achieved = p["split_kernel_gbs"]
@@ -477,6 +509,7 @@ def main():
                           "queries_per_s": round(v["queries_per_s"], 1), "ms_per_step": v["ms_per_step"],
                           "window": v["window"], "sinks": v["sinks"], "num_splits": v["num_splits"]}
     line["append"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in app.items()}
+    line["metadata"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in meta.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(primary_w, p["algorithmic_bytes"])
     print(json.dumps(line), flush=True)

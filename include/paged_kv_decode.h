@@ -314,6 +314,58 @@ int32_t paged_kv_append(const pkd_dims* dims, int64_t num_tokens, const void* k_
                         int32_t max_position, void* k_cache, void* v_cache, const float* k_scale,
                         const float* v_scale, void* stream);
 
+/* Dimensions of paged_decode_metadata (passed as a host pointer). */
+typedef struct {
+  int32_t batch;              /* B, 0..65535 (0: only cu_seqlens_k[0] = 0 and the error count are
+                                 written, and the other arrays may be NULL) */
+  int32_t req_rows;           /* rows of req_to_token, >= 1 */
+  int32_t req_stride;         /* columns of req_to_token (token slots per request row), >= 1 */
+  int32_t page_size;          /* tokens per page, >= 1 */
+  int32_t max_pages_per_seq;  /* row length of page_table / swa_page_table, >= 1 */
+  int32_t q_len;              /* query tokens per sequence, 1..PKD_MAX_Q_LEN (for the window) */
+  int32_t window;             /* 0: no window tables; W > 0: sliding window (as pkd_dims.window) */
+  int32_t extend;             /* tokens this step adds to every seq_lens[b], >= 0 */
+} pkd_meta_dims;
+
+/*
+ * paged_decode_metadata -- build the block table and lengths that paged_decode
+ * reads from a serving runtime's token map, in one launch: the fused decode
+ * metadata setup of the sglang fuse/overlap catalogue (section 1, the
+ * flashattention backend's normal_decode_set_metadata row: seq-len cast/add,
+ * prefix sum, req-to-token gather, page-table divide, optional SWA tables).
+ *
+ *   md                host; see pkd_meta_dims.
+ *   req_to_token      [req_rows][req_stride] int32: the KV slot (page * page_size +
+ *                     position) of every token of every request row.
+ *   req_pool_indices  [B] int64: the request row r_b of batch entry b.
+ *   seq_lens          [B] int64: tokens of entry b before this step.
+ * Outputs (device, written for every entry):
+ *   cache_seqlens     [B] int32: L_b = seq_lens[b] + extend (paged_decode's seq_lens).
+ *   cu_seqlens_k      [B + 1] int32: 0, L_0, L_0 + L_1, ...
+ *   page_table        [B][max_pages_per_seq] int32: entry j < ceil(L_b / page_size) is
+ *                     req_to_token[r_b][j * page_size] / page_size (the page of the page's
+ *                     first token; -1 for a negative slot); the rest -1.  This is
+ *                     paged_decode's block_table.
+ *   swa_seqlens, swa_page_table  (window > 0; may be NULL otherwise): the same
+ *                     sequence without its first f_b = max(L_b - q_len - W + 1, 0) /
+ *                     page_size pages, which hold no visible position:
+ *                     swa_page_table[b][j] = page_table[b][f_b + j] (then -1),
+ *                     swa_seqlens[b] = L_b - f_b * page_size.  paged_decode with the
+ *                     same window gives the same result on these as on the full ones.
+ *   d_error_count     int32 or NULL: the number of invalid entries, written (not
+ *                     accumulated).  An entry is invalid when r_b is outside
+ *                     [0, req_rows) or L_b outside [0, min(max_pages_per_seq *
+ *                     page_size, req_stride)]; its lengths are written as 0 and its
+ *                     table rows as -1, so decode reads nothing for it.
+ * Requires batch * max_pages_per_seq * page_size <= INT32_MAX (the prefix sums are
+ * int32).  Alignment: int64 arrays 8 bytes, int32 arrays 4.  Returns PKD_OK or a
+ * negative status; argument errors enqueue nothing.
+ */
+int32_t paged_decode_metadata(const pkd_meta_dims* md, const int32_t* req_to_token,
+                              const int64_t* req_pool_indices, const int64_t* seq_lens, int32_t* cache_seqlens,
+                              int32_t* cu_seqlens_k, int32_t* page_table, int32_t* swa_seqlens,
+                              int32_t* swa_page_table, int32_t* d_error_count, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* paged_decode_status_string(int32_t status);
 

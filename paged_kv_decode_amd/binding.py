@@ -42,7 +42,7 @@ PKD_DTYPE_FP8_E4M3 = 1
 
 EXPORTED = ("paged_decode", "paged_decode_partition", "paged_decode_finish", "paged_decode_num_splits",
             "paged_decode_launches", "paged_decode_workspace_bytes", "paged_decode_partials", "paged_decode_merge",
-            "paged_decode_check_tables", "paged_kv_append", "paged_decode_status_string")
+            "paged_decode_check_tables", "paged_kv_append", "paged_decode_metadata", "paged_decode_status_string")
 
 
 class PkdError(RuntimeError):
@@ -57,6 +57,12 @@ class pkd_dims(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("window", ctypes.c_int32)]
+
+
+class pkd_meta_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("req_rows", ctypes.c_int32), ("req_stride", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("extend", ctypes.c_int32)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -117,6 +123,8 @@ _lib.paged_decode_check_tables.argtypes = [_dims_p, _p, _p, _p, _p]
 _lib.paged_decode_check_tables.restype = _i32
 _lib.paged_kv_append.argtypes = [_dims_p, ctypes.c_int64, _p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p]
 _lib.paged_kv_append.restype = _i32
+_lib.paged_decode_metadata.argtypes = [ctypes.POINTER(pkd_meta_dims)] + [_p] * 10
+_lib.paged_decode_metadata.restype = _i32
 _lib.paged_decode_status_string.argtypes = [_i32]
 _lib.paged_decode_status_string.restype = ctypes.c_char_p
 
@@ -195,6 +203,14 @@ def paged_kv_append(dims, num_tokens, k_new, v_new, slot_mapping, positions, cos
     return _lib.paged_kv_append(_dims_ref(dims), int(num_tokens), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
                                 _ptr(positions), _ptr(cos_sin), int(max_position), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(k_scale), _ptr(v_scale), _ptr(stream))
+
+
+def paged_decode_metadata(md, req_to_token, req_pool_indices, seq_lens, cache_seqlens, cu_seqlens_k, page_table,
+                          swa_seqlens, swa_page_table, d_error_count, stream) -> int:
+    return _lib.paged_decode_metadata(None if md is None else ctypes.byref(md), _ptr(req_to_token),
+                                      _ptr(req_pool_indices), _ptr(seq_lens), _ptr(cache_seqlens),
+                                      _ptr(cu_seqlens_k), _ptr(page_table), _ptr(swa_seqlens),
+                                      _ptr(swa_page_table), _ptr(d_error_count), _ptr(stream))
 
 
 def paged_decode_status_string(status: int) -> str:
@@ -291,3 +307,35 @@ def append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=N
                          k_scale, v_scale, stream)
     if st != PKD_OK:
         raise PkdError(st)
+
+
+def metadata(req_to_token, req_pool_indices, seq_lens, page_size: int, max_pages: int, q_len: int = 1,
+             window: int = 0, extend: int = 0, stream: Optional[int] = None):
+    """Run paged_decode_metadata on torch device tensors (req_to_token int32 [R, C],
+    req_pool_indices and seq_lens int64 [B]).  Returns a dict of device tensors:
+    cache_seqlens, cu_seqlens_k, page_table and, with a window, swa_seqlens and
+    swa_page_table, plus error_count (int32 [1])."""
+    import torch
+    for name, t, dt in (("req_to_token", req_to_token, torch.int32), ("req_pool_indices", req_pool_indices,
+                        torch.int64), ("seq_lens", seq_lens, torch.int64)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt:
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    R, C = req_to_token.shape
+    B = req_pool_indices.shape[0]
+    dev = req_to_token.device
+    res = dict(cache_seqlens=torch.empty(B, dtype=torch.int32, device=dev),
+               cu_seqlens_k=torch.empty(B + 1, dtype=torch.int32, device=dev),
+               page_table=torch.empty(B, max_pages, dtype=torch.int32, device=dev),
+               error_count=torch.empty(1, dtype=torch.int32, device=dev))
+    if window > 0:
+        res["swa_seqlens"] = torch.empty(B, dtype=torch.int32, device=dev)
+        res["swa_page_table"] = torch.empty(B, max_pages, dtype=torch.int32, device=dev)
+    md = pkd_meta_dims(B, R, C, page_size, max_pages, q_len, window, extend)
+    if stream is None:
+        stream = current_stream_handle(dev)
+    st = paged_decode_metadata(md, req_to_token, req_pool_indices, seq_lens, res["cache_seqlens"],
+                               res["cu_seqlens_k"], res["page_table"], res.get("swa_seqlens"),
+                               res.get("swa_page_table"), res["error_count"], stream)
+    if st != PKD_OK:
+        raise PkdError(st)
+    return res

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpaged_kv_decode.so")
-SOURCES = ["split_kv_decode.hip", "lse_merge.hip", "kv_append.hip", "api.cpp"]
+SOURCES = ["split_kv_decode.hip", "lse_merge.hip", "kv_append.hip", "decode_metadata.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",

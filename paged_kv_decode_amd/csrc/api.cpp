@@ -532,6 +532,53 @@ int32_t paged_kv_append(const pkd_dims* dims, int64_t num_tokens, const void* k_
              ? PKD_OK : PKD_ERR_LAUNCH;
 }
 
+int32_t paged_decode_metadata(const pkd_meta_dims* md, const int32_t* req_to_token,
+                              const int64_t* req_pool_indices, const int64_t* seq_lens, int32_t* cache_seqlens,
+                              int32_t* cu_seqlens_k, int32_t* page_table, int32_t* swa_seqlens,
+                              int32_t* swa_page_table, int32_t* d_error_count, void* stream) {
+  if (!md) return PKD_ERR_NULL_POINTER;
+  if (md->batch < 0 || md->batch > 65535 || md->req_rows < 1 || md->req_stride < 1 || md->page_size < 1 ||
+      md->max_pages_per_seq < 1 || md->q_len < 1 || md->q_len > PKD_MAX_Q_LEN || md->window < 0 ||
+      md->extend < 0)
+    return PKD_ERR_BAD_DIMS;
+  // Every length and prefix sum fits int32.
+  const int64_t cap = (int64_t)md->max_pages_per_seq * md->page_size;
+  if (cap > INT32_MAX || (int64_t)md->batch * cap > INT32_MAX) return PKD_ERR_BAD_DIMS;
+  // With an empty batch only cu_seqlens_k[0] (and the error count) is written.
+  if (!cu_seqlens_k) return PKD_ERR_NULL_POINTER;
+  if (md->batch > 0) {
+    if (!req_to_token || !req_pool_indices || !seq_lens || !cache_seqlens || !page_table)
+      return PKD_ERR_NULL_POINTER;
+    if (md->window > 0 && (!swa_seqlens || !swa_page_table)) return PKD_ERR_NULL_POINTER;
+  }
+  if (!aligned(req_to_token, 4) || !aligned(req_pool_indices, 8) || !aligned(seq_lens, 8) ||
+      !aligned(cache_seqlens, 4) || !aligned(cu_seqlens_k, 4) || !aligned(page_table, 4) ||
+      !aligned(swa_seqlens, 4) || !aligned(swa_page_table, 4) || !aligned(d_error_count, 4))
+    return PKD_ERR_ALIGNMENT;
+  if (current_cu_count() < 0) return PKD_ERR_DEVICE;
+  pkd::MetaParams m{};
+  m.req_to_token = req_to_token;
+  m.req_pool_indices = req_pool_indices;
+  m.seq_lens = seq_lens;
+  m.cache_seqlens = cache_seqlens;
+  m.cu_seqlens_k = cu_seqlens_k;
+  m.page_table = page_table;
+  m.swa_seqlens = md->window > 0 ? swa_seqlens : nullptr;
+  m.swa_page_table = md->window > 0 ? swa_page_table : nullptr;
+  m.error_count = d_error_count;
+  m.req_rows = md->req_rows;
+  m.req_stride = md->req_stride;
+  m.max_len = cap < md->req_stride ? cap : md->req_stride;
+  m.batch = md->batch;
+  m.page_size = md->page_size;
+  m.max_pages = md->max_pages_per_seq;
+  m.q_len = md->q_len;
+  m.window = md->window;
+  m.extend = md->extend;
+  return pkd::launch_decode_metadata(m, static_cast<hipStream_t>(stream)) == hipSuccess ? PKD_OK
+                                                                                         : PKD_ERR_LAUNCH;
+}
+
 const char* paged_decode_status_string(int32_t status) {
   switch (status) {
     case PKD_OK: return "ok";

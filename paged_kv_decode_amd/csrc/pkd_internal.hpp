@@ -113,6 +113,22 @@ struct AppendParams {
   int32_t hkv;
 };
 
+// Arguments of the decode metadata kernel.
+struct MetaParams {
+  const int32_t* req_to_token;      // [req_rows][req_stride] KV slot of every token of every request row
+  const int64_t* req_pool_indices;  // [batch]
+  const int64_t* seq_lens;          // [batch] tokens before this step
+  int32_t* cache_seqlens;           // [batch] out
+  int32_t* cu_seqlens_k;            // [batch + 1] out
+  int32_t* page_table;              // [batch][max_pages] out
+  int32_t* swa_seqlens;             // [batch] out (window > 0)
+  int32_t* swa_page_table;          // [batch][max_pages] out (window > 0)
+  int32_t* error_count;             // out or null: invalid batch entries
+  int64_t req_rows, req_stride;
+  int64_t max_len;                  // min(max_pages * page_size, req_stride)
+  int32_t batch, page_size, max_pages, q_len, window, extend;
+};
+
 constexpr int kWaves = 4;            // waves per split-kernel workgroup
 constexpr int kSplitAlign = 64;      // tokens; split boundaries are multiples of this
 constexpr int kHeadsPerGroup = 16;   // query heads packed into one MFMA N dimension
@@ -124,6 +140,7 @@ hipError_t launch_split_kv(const SplitParams& p, int batch, int head_dim, bool f
 hipError_t launch_balanced(const BalancedParams& p, int head_dim, bool fp8, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool fp8, hipStream_t stream);
+hipError_t launch_decode_metadata(const MetaParams& p, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* block_table, const int32_t* seq_lens, int batch,
                                int max_pages, int page_size, int num_pages, int32_t* d_count,
                                hipStream_t stream);

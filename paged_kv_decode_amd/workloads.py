@@ -337,3 +337,36 @@ def append_workload(n_tokens: int, num_kv_heads: int, head_dim: int, page_size: 
         k_cache = codes.view(torch.float8_e4m3fn)
         v_cache = torch.randint(0, 126, shape, generator=g, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
     return AppendWorkload(k_new, v_new, slots, positions, cos_sin, k_cache, v_cache, k_scale, v_scale)
+
+
+@dataclasses.dataclass
+class MetadataWorkload:
+    """Host tensors of one decode-metadata preparation: a runtime's token map
+    holding the block tables of a decode workload in shuffled request rows."""
+    req_to_token: torch.Tensor      # [req_rows, req_stride] int32 KV slots
+    req_pool_indices: torch.Tensor  # [B] int64
+    seq_lens: torch.Tensor          # [B] int64, before the step's `extend` tokens
+    block_table: torch.Tensor       # [B, MP] int32, what the page table must come out as
+    page_size: int
+    max_pages: int
+    extend: int
+
+
+def metadata_workload(w: Workload, req_rows: int, extend: int = 1, seed: int = 0) -> MetadataWorkload:
+    """The token map of decode workload w: sequence b sits in a random request
+    row of a pool of req_rows rows, token t at slot bt[b][t // ps] * ps + t % ps;
+    every other cell holds a random slot.  seq_lens are w's lengths minus extend
+    (the step adds them back)."""
+    g = torch.Generator().manual_seed(seed)
+    bt = w.block_table
+    B, MP = bt.shape
+    ps = w.spec.page_size
+    stride = MP * ps
+    rt = torch.randint(0, int(w.k_cache.shape[0]) * ps, (req_rows, stride), generator=g, dtype=torch.int32)
+    rows = torch.randperm(req_rows, generator=g)[:B].to(torch.int64)
+    for b in range(B):
+        L = int(w.seq_lens[b])
+        t = torch.arange(L)
+        rt[rows[b], :L] = (bt[b, t // ps].to(torch.int64) * ps + t % ps).to(torch.int32)
+    lens = (w.seq_lens.to(torch.int64) - extend).clamp(min=0)
+    return MetadataWorkload(rt, rows, lens, bt, ps, MP, extend)

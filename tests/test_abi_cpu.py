@@ -275,3 +275,47 @@ def test_launch_counts():
     assert b.paged_decode_launches(long1, b.PKD_SPLITS_BALANCED) == 2
     assert b.paged_decode_launches(b32, -5) == b.PKD_ERR_NUM_SPLITS
     assert b.paged_decode_launches(dims(head_dim=96), 1) == b.PKD_ERR_HEAD_DIM
+
+
+# ---- paged_decode_metadata argument checks ----------------------------------
+
+def meta(**kw):
+    base = dict(batch=4, req_rows=8, req_stride=256, page_size=16, max_pages_per_seq=16, q_len=1, window=0,
+                extend=1)
+    base.update(kw)
+    return b.pkd_meta_dims(*[base[f] for f, _ in b.pkd_meta_dims._fields_])
+
+
+def meta_call(md, rt=FAKE, rp=FAKE, sl=FAKE, cs=FAKE, cu=FAKE, pt=FAKE, ss=None, sp=None, err=None):
+    return b.paged_decode_metadata(md, rt, rp, sl, cs, cu, pt, ss, sp, err, None)
+
+
+def test_meta_dims_struct_layout():
+    assert ctypes.sizeof(b.pkd_meta_dims) == 8 * 4
+
+
+@pytest.mark.parametrize("kw", [dict(batch=-1), dict(batch=65536), dict(req_rows=0), dict(req_stride=0),
+                                dict(page_size=0), dict(max_pages_per_seq=0), dict(q_len=0),
+                                dict(q_len=b.PKD_MAX_Q_LEN + 1), dict(window=-1), dict(extend=-1),
+                                dict(batch=65535, max_pages_per_seq=4096, page_size=16)])
+def test_metadata_bad_dims(kw):
+    assert meta_call(meta(**kw)) == b.PKD_ERR_BAD_DIMS
+
+
+def test_metadata_pointer_rules():
+    assert meta_call(None) == b.PKD_ERR_NULL_POINTER
+    for i in range(6):
+        args = [FAKE] * 6
+        args[i] = None
+        assert meta_call(meta(), *args) == b.PKD_ERR_NULL_POINTER, i
+    assert meta_call(meta(window=8)) == b.PKD_ERR_NULL_POINTER  # window tables required
+    assert meta_call(meta(window=8), ss=FAKE) == b.PKD_ERR_NULL_POINTER
+    assert meta_call(meta(), rp=FAKE + 4) == b.PKD_ERR_ALIGNMENT
+    assert meta_call(meta(), pt=FAKE + 2) == b.PKD_ERR_ALIGNMENT
+    assert meta_call(meta(), err=FAKE + 1) == b.PKD_ERR_ALIGNMENT
+    # An empty batch needs cu_seqlens_k only.
+    assert meta_call(meta(batch=0, window=3), None, None, None, None, FAKE, None) == b.PKD_ERR_DEVICE
+    assert meta_call(meta(batch=0), cu=None) == b.PKD_ERR_NULL_POINTER
+    # Valid arguments reach the device check (no device here).
+    assert meta_call(meta()) == b.PKD_ERR_DEVICE
+    assert meta_call(meta(window=8), ss=FAKE, sp=FAKE, err=FAKE) == b.PKD_ERR_DEVICE

@@ -856,3 +856,79 @@ def test_window_sinks_workload_sampled_rows(B):
         a, b_ = outs[S], outs[1]
         assert torch.all((a[0].float() - b_[0].float()).abs() <= 2e-2 + 2e-2 * b_[0].float().abs())
         assert torch.all((a[1] - b_[1]).abs() <= 2e-3)
+
+
+# ---- decode metadata preparation ---------------------------------------------
+
+def token_map(bt, lens, ps, req_rows, stride, seed):
+    """req_to_token pool holding block tables bt in shuffled request rows (token t
+    of sequence b at slot bt[b][t // ps] * ps + t % ps), random elsewhere."""
+    rng = np.random.default_rng(seed)
+    B = bt.shape[0]
+    rt = rng.integers(-5, 10 ** 6, size=(req_rows, stride)).astype(np.int32)
+    rows = rng.permutation(req_rows)[:B]
+    for b in range(B):
+        L = int(lens[b])
+        t = np.arange(L)
+        rt[rows[b], :L] = bt[b, t // ps] * ps + t % ps
+    return rt, rows.astype(np.int64)
+
+
+def meta_device(B, rt, rows, lens, ps, MP, q_len=1, window=0, extend=0):
+    cuda = torch.device("cuda:0")
+    res = B.metadata(torch.from_numpy(rt).to(cuda), torch.from_numpy(rows).to(cuda),
+                     torch.from_numpy(np.asarray(lens, np.int64)).to(cuda), ps, MP, q_len=q_len, window=window,
+                     extend=extend)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+META_CASES = [
+    # (B, ps, MP, q_len, window, extend, seed)
+    (5, 16, 8, 1, 0, 1, 501),
+    (7, 1, 40, 1, 9, 0, 502),
+    (9, 24, 6, 3, 50, 2, 503),
+    (300, 64, 16, 1, 200, 1, 504),     # more entries than one scan chunk
+    (1000, 16, 4, 4, 7, 0, 505),       # several chunks
+    (0, 16, 4, 1, 5, 0, 506),          # empty batch
+]
+
+
+@pytest.mark.parametrize("case", META_CASES)
+def test_metadata_matches_oracle_bitwise(B, case):
+    bq, ps, MP, ql, win, ext, seed = case
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, MP * ps - ext + 1, size=bq)
+    if bq > 2:
+        lens[0], lens[1] = 0, MP * ps - ext
+    bt = rng.integers(0, 5000, size=(bq, MP)).astype(np.int32)
+    rt, rows = token_map(bt, lens + ext, ps, bq + 5, MP * ps + 3, seed)
+    if bq > 4:
+        rows[2] = bq + 5          # invalid request row
+        lens[3] = MP * ps         # too long once extended (when ext > 0)
+        rows[4] = -1
+    ref, bad = oracle.decode_metadata(rt, rows, lens.astype(np.int64), ps, MP, q_len=ql, window=win, extend=ext)
+    got = meta_device(B, rt, rows, lens, ps, MP, ql, win, ext)
+    for k, v in ref.items():
+        assert np.array_equal(got[k], v), k
+    assert int(got["error_count"][0]) == bad
+
+
+def test_metadata_feeds_decode_bitwise(B):
+    """Decode on device-built tables equals decode on the original ones, and the
+    window tables decode to the same bits as the full tables with the window."""
+    lens = [(i * 997) % 3000 + 1 for i in range(24)] + [0, 64, 4096]
+    w = wl.custom_workload(len(lens), 32, 8, 128, 64, lens, "bf16", seed=510, window=700, sinks=True)
+    t = dev(w)
+    MP = w.block_table.shape[1]
+    bt = w.block_table.numpy()
+    rt, rows = token_map(np.where(bt < 0, 0, bt), lens, 64, len(lens) + 7, MP * 64, seed=511)
+    m = meta_device(B, rt, rows, lens, 64, MP, window=700)
+    assert int(m["error_count"][0]) == 0
+    for S in (1, BAL, 0):
+        ref_o, ref_l = run(B, w, S, t)
+        for bt_key, len_key in (("page_table", "cache_seqlens"), ("swa_page_table", "swa_seqlens")):
+            t2 = dict(t, bt=torch.from_numpy(m[bt_key]).cuda(), lens=torch.from_numpy(m[len_key]).cuda())
+            o, l = run(B, w, S, t2)
+            assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), (S, bt_key)
+            assert torch.equal(l, ref_l), (S, bt_key)
