@@ -73,6 +73,8 @@ def lib():
         L.pkd_oracle_kv_append.restype = _c_int
         L.pkd_oracle_decode_metadata.argtypes = [_c_int] * 8 + [_p] * 8
         L.pkd_oracle_decode_metadata.restype = _c_int
+        L.pkd_oracle_contiguous_decode.argtypes = [_c_int] * 9 + [_p] * 9 + [_c_double, _p, _p, _c_int]
+        L.pkd_oracle_contiguous_decode.restype = _c_int
         _lib = L
     return _lib
 
@@ -319,6 +321,48 @@ def decode_metadata(req_to_token, req_pool_indices, seq_lens, page_size, max_pag
                                            _ptr(res.get("swa_seqlens")), _ptr(res.get("swa_page_table")))
     _check(min(bad, 0))
     return res, bad
+
+
+def _strided(x, dtype):
+    """(numpy array over x's whole storage as raw `dtype`, element offset of x, x's strides)
+    for a CPU torch tensor view whose last dimension is contiguous."""
+    import torch
+    assert x.stride(-1) == 1, "the head dimension must be contiguous"
+    flat = torch.empty(0, dtype=x.dtype).set_(x.untyped_storage())
+    return _raw(flat, dtype), x.storage_offset(), x.stride()
+
+
+def contiguous_decode(q, k_cache, v_cache, seq_lens, scale, causal=False, window=0, sinks=None, k_scale=None,
+                      v_scale=None, nthreads: int = 1):
+    """Decode over contiguous, strided K/V (see paged_attention_ref.c).  k_cache, v_cache:
+    CPU tensor views shaped [B, L_max, Hkv, D] with any strides (the last one 1), e.g. a
+    permuted [B, Hkv, L_max, D] tensor or a slice of a larger one; q a view shaped
+    [B, Hq, D] or [B, q_len, Hq, D], also any strides.  Returns (out [B, q_len, Hq, D],
+    lse [B, q_len, Hq]) as float64."""
+    kv_fp8 = k_cache.element_size() == 1
+    kt = np.uint8 if kv_fp8 else np.uint16
+    kb, ko, ks_ = _strided(k_cache, kt)
+    vb, vo, vs_ = _strided(v_cache, kt)
+    assert ks_ == vs_ and k_cache.shape == v_cache.shape, "k and v must share shape and strides"
+    q4 = q if q.dim() == 4 else q.unsqueeze(1)
+    qb, qo, qs_ = _strided(q4, np.uint16)
+    B, q_len, hq, d = q4.shape
+    _, max_len, hkv, d2 = k_cache.shape
+    assert d2 == d
+    kv_str = np.array([ks_[0], ks_[1], ks_[2]], np.int64)
+    q_str = np.array([qs_[0], qs_[1], qs_[2]], np.int64)
+    lens = np.ascontiguousarray(_raw(seq_lens, np.int32))
+    sk = None if sinks is None else np.ascontiguousarray(_raw(sinks, np.float32))
+    ksc = _raw(k_scale, np.float32)
+    vsc = _raw(v_scale, np.float32)
+    out = np.empty((B, q_len, hq, d), np.float64)
+    lse = np.empty((B, q_len, hq), np.float64)
+    at = lambda a, off: ctypes.c_void_p(a.ctypes.data + off * a.itemsize)
+    _check(lib().pkd_oracle_contiguous_decode(B, hq, hkv, d, max_len, 1 if kv_fp8 else 0, q_len, int(bool(causal)),
+                                              int(window), _ptr(sk), at(qb, qo), _ptr(q_str), at(kb, ko), at(vb, vo),
+                                              _ptr(kv_str), _ptr(lens), _ptr(ksc), _ptr(vsc), float(scale),
+                                              _ptr(out), _ptr(lse), int(nthreads)))
+    return out, lse
 
 
 def bf16_value(bits: int) -> float:

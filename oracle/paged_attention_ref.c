@@ -63,8 +63,9 @@
  * in: lse' = ln(e^lse + e^sink), out' = out * e^(lse - lse').
  *
  * The file also defines the paged KV append that fills the cache
- * (pkd_oracle_kv_append) and the decode metadata preparation that builds the
- * block table and lengths (pkd_oracle_decode_metadata), both at the end.
+ * (pkd_oracle_kv_append), the decode metadata preparation that builds the
+ * block table and lengths (pkd_oracle_decode_metadata) and decode over a
+ * contiguous, strided KV layout (pkd_oracle_contiguous_decode), at the end.
  *
  * Work is spread over an optional pthread pool by (sequence, KV head) items.
  * The items are independent and each is computed in a fixed order, so the
@@ -128,15 +129,27 @@ typedef struct {
   int causal;                 /* 0: every query token sees all L tokens; 1: causal mask */
   int window;                 /* 0: no window; > 0: positions t > p - window only */
   const float* sinks;         /* [Hq] sink logits, or NULL */
+  /* Contiguous (strided) layout, used when kv_strides is not NULL: key
+   * element (b, t, g, d) is k_cache[b*s[0] + t*s[1] + g*s[2] + d] (s =
+   * kv_strides, in elements) and no block table is used; page_size is then
+   * the token capacity of each sequence.  q_strides (or NULL: dense) likewise
+   * places query row (b, i, h) at q[b*s[0] + i*s[1] + h*s[2]]. */
+  const int64_t* kv_strides;
+  const int64_t* q_strides;
 } problem;
 
 /* Value of element d of token t's key (is_v = 0) or value (is_v = 1) row for
  * KV head g of sequence b; the page lookup is the per-token one described
  * above.  Page validity is checked by the caller. */
 static double kv_elem(const problem* P, int is_v, int b, int t, int g, int d) {
-  int32_t page = P->block_table[(int64_t)b * P->max_pages + t / P->page_size];
-  int slot = t % P->page_size;
-  int64_t idx = (((int64_t)page * P->page_size + slot) * P->hkv + g) * P->head_dim + d;
+  int64_t idx;
+  if (P->kv_strides) {
+    idx = (int64_t)b * P->kv_strides[0] + (int64_t)t * P->kv_strides[1] + (int64_t)g * P->kv_strides[2] + d;
+  } else {
+    int32_t page = P->block_table[(int64_t)b * P->max_pages + t / P->page_size];
+    int slot = t % P->page_size;
+    idx = (((int64_t)page * P->page_size + slot) * P->hkv + g) * P->head_dim + d;
+  }
   if (P->kv_fp8) {
     const uint8_t* c = (const uint8_t*)(is_v ? P->v_cache : P->k_cache);
     const float* sc = is_v ? P->v_scale : P->k_scale;
@@ -191,7 +204,9 @@ static double attend_range(const problem* P, int b, int qi, int h, int t0, int t
   const int D = P->head_dim;
   const int G = P->hq / P->hkv;
   const int g = h / G;
-  const uint16_t* qrow = P->q + (((int64_t)b * P->q_len + qi) * P->hq + h) * D;
+  const uint16_t* qrow = P->q_strides ? P->q + (int64_t)b * P->q_strides[0] + (int64_t)qi * P->q_strides[1] +
+                                             (int64_t)h * P->q_strides[2]
+                                       : P->q + (((int64_t)b * P->q_len + qi) * P->hq + h) * D;
   for (int d = 0; d < D; ++d) o[d] = 0.0;
   if (t1 <= t0) return -INFINITY;
 
@@ -254,6 +269,7 @@ typedef struct {
 static int check_sequence(const problem* P, int b) {
   int L = P->seq_lens[b];
   if (L < 0 || (int64_t)L > (int64_t)P->max_pages * P->page_size) return PKD_ORACLE_BAD_LEN;
+  if (P->kv_strides) return PKD_ORACLE_OK;
   int used = (L + P->page_size - 1) / P->page_size;
   for (int i = 0; i < used; ++i) {
     int32_t p = P->block_table[(int64_t)b * P->max_pages + i];
@@ -708,4 +724,28 @@ int pkd_oracle_decode_metadata(int batch, int req_rows, int req_stride, int page
     }
   }
   return bad;
+}
+
+/* ---- contiguous KV decode ----------------------------------------------
+ *
+ * The same attention (several query tokens, causal mask, window, sinks) over
+ * K/V held in one contiguous tensor per cache rather than in pages: the
+ * contiguous decode kernels of the AstrAI commit log, with its stride-based
+ * addressing for Q, K/V and O (any layout, e.g. [B][L][Hkv][D] or
+ * [B][Hkv][L][D], read in place).  k_cache / v_cache: element (b, t, g, d) at
+ * b*kv_strides[0] + t*kv_strides[1] + g*kv_strides[2] + d; q row (b, i, h) at
+ * b*q_strides[0] + i*q_strides[1] + h*q_strides[2] (strides in elements, the
+ * head dimension contiguous).  seq_lens[b] <= max_seq_len.  out [B][q_len][Hq][D]
+ * and lse [B][q_len][Hq] (fp64, dense) as for the paged entries.
+ */
+int pkd_oracle_contiguous_decode(int batch, int hq, int hkv, int head_dim, int max_seq_len, int kv_fp8, int q_len,
+                                 int causal, int window, const float* sinks, const uint16_t* q,
+                                 const int64_t* q_strides, const void* k_cache, const void* v_cache,
+                                 const int64_t* kv_strides, const int32_t* seq_lens, const float* k_scale,
+                                 const float* v_scale, double scale, double* out, double* lse, int nthreads) {
+  if (window < 0 || max_seq_len < 1 || !q_strides || !kv_strides) return PKD_ORACLE_BAD_ARG;
+  problem P = {batch, hq, hkv, head_dim, max_seq_len, 1, 1, kv_fp8,
+               q, k_cache, v_cache, NULL, seq_lens, k_scale, v_scale, scale,
+               0, out, lse, q_len, causal, window, sinks, kv_strides, q_strides};
+  return run(&P, nthreads);
 }

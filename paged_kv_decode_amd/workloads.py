@@ -370,3 +370,53 @@ def metadata_workload(w: Workload, req_rows: int, extend: int = 1, seed: int = 0
         rt[rows[b], :L] = (bt[b, t // ps].to(torch.int64) * ps + t % ps).to(torch.int32)
     lens = (w.seq_lens.to(torch.int64) - extend).clamp(min=0)
     return MetadataWorkload(rt, rows, lens, bt, ps, MP, extend)
+
+
+def contiguous_kv(w: Workload, layout: str = "blhd", capacity: Optional[int] = None):
+    """K and V of workload w in contiguous tensors, returned as views shaped
+    [B, capacity, Hkv, D] (capacity defaults to the longest length):
+      "blhd"         a dense [B, capacity, Hkv, D] tensor;
+      "bhld"         a dense [B, Hkv, capacity, D] tensor, permuted;
+      "blhd_padded"  a slice of a [B, capacity + 5, Hkv + 1, D] tensor.
+    Token t < L_b of sequence b holds the sequence's logical row t; every other
+    element (tokens past L_b, padding) is NaN, so that a read of one shows."""
+    B = w.spec.batch
+    hkv, d = w.spec.num_kv_heads, w.spec.head_dim
+    lens = [int(x) for x in w.seq_lens]
+    cap = capacity if capacity is not None else max(max(lens), 1)
+    fp8 = w.k_cache.dtype == torch.float8_e4m3fn
+    out = []
+    for logical in (w.k_logical, w.v_logical):
+        if layout == "blhd":
+            shape = (B, cap, hkv, d)
+        elif layout == "bhld":
+            shape = (B, hkv, cap, d)
+        elif layout == "blhd_padded":
+            shape = (B, cap + 5, hkv + 1, d)
+        else:
+            raise ValueError(layout)
+        if fp8:
+            buf = torch.full(shape, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn)  # 0x7F: an E4M3FN NaN
+        else:
+            buf = torch.full(shape, float("nan"), dtype=logical.dtype)
+        view = buf.permute(0, 2, 1, 3) if layout == "bhld" else buf[:, :cap, :hkv]
+        for b in range(B):
+            o = int(w.token_offsets[b])
+            if lens[b]:
+                if fp8:
+                    view.view(torch.uint8)[b, :lens[b]] = logical[o:o + lens[b]].view(torch.uint8)
+                else:
+                    view[b, :lens[b]] = logical[o:o + lens[b]]
+        out.append(view)
+    return out[0], out[1]
+
+
+def strided_q(q: torch.Tensor) -> torch.Tensor:
+    """q ([B, Hq, D] or [B, q_len, Hq, D]) copied into a slice of a larger NaN-filled
+    tensor (two extra heads, one extra query token), so its strides are not dense."""
+    q4 = q if q.dim() == 4 else q.unsqueeze(1)
+    B, ql, hq, d = q4.shape
+    buf = torch.full((B, ql + 1, hq + 2, d), float("nan"), dtype=q.dtype)
+    view = buf[:, :ql, 1:hq + 1]
+    view.copy_(q4)
+    return view if q.dim() == 4 else view[:, 0]

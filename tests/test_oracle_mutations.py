@@ -8,10 +8,10 @@ split boundary, a wrong FP8 exponent bias, a wrong cache layout, a causal
 mask off by one or aligned to the wrong end, a window or sink slip; in the KV
 append a RoPE sign, pairing or cos/sin swap, a wrong scale, rounding ties or
 slot; in the decode metadata a prefix sum, gather stride, page divide,
-extension, request row or window page slip.  The copy is compiled with the
-oracle's own build command and the pin suite (test_oracle_pins.py) is run
-against it in a child process through
-PKD_ORACLE_LIB; every mutant must make at least one pin fail.  A control copy
+extension, request row or window page slip; in the contiguous layout a
+stride slip.  The copy is compiled with the oracle's own build command and
+the pin suite (test_oracle_pins.py) is run against it in a child process
+through PKD_ORACLE_LIB; every mutant must make at least one pin fail.  A control copy
 with no change must pass, which shows that the child really loads the copy.
 
 The mistakes are planted in the oracle only, on the CPU; nothing here touches
@@ -128,6 +128,13 @@ MUTANTS = [
      "const int64_t r = req_pool_indices[b];", "const int64_t r = b;"),
     ("metadata_swa_first_page_off_by_one",
      "int64_t lo = len - q_len - window + 1;", "int64_t lo = len - q_len - window;"),
+    ("contiguous_token_and_head_strides_swapped",
+     "(int64_t)t * P->kv_strides[1] + (int64_t)g * P->kv_strides[2]",
+     "(int64_t)t * P->kv_strides[2] + (int64_t)g * P->kv_strides[1]"),
+    ("contiguous_batch_stride_dropped",
+     "idx = (int64_t)b * P->kv_strides[0] + (int64_t)t", "idx = (int64_t)t"),
+    ("contiguous_q_strides_ignored",
+     "const uint16_t* qrow = P->q_strides ?", "const uint16_t* qrow = 0 ?"),
     ("metadata_swa_length_not_shifted",
      "swa_seqlens[b] = (int32_t)(len - f * page_size);", "swa_seqlens[b] = (int32_t)len;"),
 ]

@@ -763,3 +763,53 @@ def test_metadata_invalid_entries_are_counted_and_blanked():
     assert res["page_table"][0].tolist() == [0, -1, -1, -1]
     assert (res["page_table"][1:] == -1).all() and (res["swa_page_table"][1:] == -1).all()
     assert res["swa_seqlens"].tolist() == [5, 0, 0, 0, 0]
+
+
+# ---- contiguous (strided) KV decode ------------------------------------------
+
+CONTIG_CASES = [
+    # (B, Hq, Hkv, D, ps, seq_lens, q_len, causal, window, sinks, dtype, seed)
+    (3, 8, 2, 64, 16, [37, 1, 100], 1, False, 0, False, "bf16", 601),
+    (3, 8, 2, 64, 16, [0, 50, 9], 3, True, 20, True, "bf16", 602),
+    (2, 4, 4, 32, 24, [70, 33], 2, False, 0, True, "fp8_e4m3", 603),
+]
+
+
+@pytest.mark.parametrize("case", CONTIG_CASES)
+@pytest.mark.parametrize("layout", ["blhd", "bhld", "blhd_padded"])
+def test_contiguous_equals_paged_on_the_same_rows(case, layout):
+    """Decode over the sequences' rows laid out contiguously (three layouts, a
+    strided q; NaN in every element that is not a sequence row) gives the same
+    bits as the paged decode of the same rows."""
+    bq, hq, hkv, d, ps, lens, ql, causal, win, sinks, dtype, seed = case
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, dtype, seed, q_len=ql, causal=causal, window=win, sinks=sinks)
+    paged = oracle.paged_decode_ext(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.scale, causal, win,
+                                    w.sinks, w.k_scale, w.v_scale)
+    k, v = wl.contiguous_kv(w, layout, capacity=max(lens) + 3)
+    got = oracle.contiguous_decode(wl.strided_q(w.q), k, v, w.seq_lens, w.scale, causal, win, w.sinks,
+                                   w.k_scale, w.v_scale)
+    assert np.array_equal(got[0], paged[0].reshape(got[0].shape)) and np.array_equal(got[1], paged[1].reshape(got[1].shape))
+
+
+def test_contiguous_layout_reads_each_stride():
+    """Swapping two tokens, two KV heads or two sequences in the contiguous
+    tensor changes exactly the rows that read them."""
+    lens = [40, 40]
+    w = wl.custom_workload(2, 4, 2, 32, 16, lens, "bf16", seed=610)
+    k, v = wl.contiguous_kv(w, "bhld")
+    base = oracle.contiguous_decode(w.q, k, v, w.seq_lens, w.scale)
+    k2, v2 = k.clone(), v.clone()
+    k2[0, [3, 7]] = k2[0, [7, 3]]  # two tokens of sequence 0 (K and V rows): the sum is order-free
+    v2[0, [3, 7]] = v2[0, [7, 3]]
+    same = oracle.contiguous_decode(w.q, k2, v2, w.seq_lens, w.scale)
+    assert np.allclose(same[0], base[0], atol=1e-12) and not torch.equal(k2[0, 3], k[0, 3])
+    v2 = v.clone()
+    v2[0, 5] = v2[0, 5] + 1.0      # one value row of sequence 0, both heads
+    moved = oracle.contiguous_decode(w.q, k, v2, w.seq_lens, w.scale)
+    assert not np.allclose(moved[0][0], base[0][0]) and np.array_equal(moved[0][1], base[0][1])
+    k3 = k.clone()
+    k3[1, :, 0] = k3[1, :, 1].clone()  # KV head 0 of sequence 1 := KV head 1
+    heads = oracle.contiguous_decode(w.q, k3, v, w.seq_lens, w.scale)
+    assert np.array_equal(heads[0][0], base[0][0])
+    assert np.array_equal(heads[0][1, :, 2:], base[0][1, :, 2:])  # query heads 2, 3 read KV head 1
+    assert not np.allclose(heads[0][1, :, :2], base[0][1, :, :2])
