@@ -272,6 +272,50 @@ def bench_metadata(w, steps, warmup, device, scrub, window):
             "note": "one launch; latency-bound (tens of KB moved), so no bandwidth figure"}
 
 
+def bench_contiguous(w, steps, warmup, device, scrub):
+    """Decode of workload w's batch with its K/V in contiguous head-major tensors
+    [B, Hkv, L_max, D] (read through strides as [B, L_max, Hkv, D]), the mode the
+    library picks by default."""
+    import torch
+    from paged_kv_decode_amd import binding as B
+    from paged_kv_decode_amd import workloads as wl
+    k, v = wl.contiguous_kv(w, "bhld", capacity=w.spec.max_len)
+    to_dev = lambda x: torch.empty(0, dtype=x.dtype).set_(x.untyped_storage()).to(device).as_strided(
+        x.shape, x.stride(), x.storage_offset())
+    k, v = to_dev(k), to_dev(v)
+    q = w.q.to(device)
+    lens = w.seq_lens.to(device)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=device)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=device)
+    cd = B.contig_dims_for(q, k, out)
+    need = B.contiguous_decode_workspace_bytes(cd, 0)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device)
+    h = stream.cuda_stream
+
+    def call():
+        st = B.contiguous_decode(cd, q, k, v, lens, None, None, None, w.scale, out, lse, 0, ws, need, h)
+        if st != 0:
+            raise B.PkdError(st)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        scrub.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    mean = sum(ms) / len(ms)
+    nbytes = algorithmic_bytes(w) - sum(-(-int(L) // w.spec.page_size) for L in w.seq_lens) * 4  # no block table
+    return {"workload": w.spec.name + " K/V contiguous [B, Hkv, 4096, D]", "ms_per_step": mean,
+            "algorithmic_bytes": nbytes, "gbs": nbytes / (mean * 1e-3) / 1e9,
+            "pct_of_peak": 100.0 * nbytes / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def cpu_baseline(w, nbytes):
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -456,10 +500,13 @@ def main():
         return
     app = bench_append(args.steps, args.warmup, device, scrub)
     meta = bench_metadata(primary_w, args.steps, args.warmup, device, scrub, window=1024)
+    contig = bench_contiguous(primary_w, args.steps, args.warmup, device, scrub)
     print(f"# {app['workload']}: {app['ms_per_call'] * 1e3:.1f} us/call {app['gbs']:.0f} GB/s = "
           f"{app['pct_of_peak']:.1f}% of peak", file=sys.stderr, flush=True)
     print(f"# decode metadata (B={meta['batch']}, window {meta['window']}): {meta['us_per_call']:.1f} us/call",
           file=sys.stderr, flush=True)
+    print(f"# {contig['workload']}: {contig['ms_per_step'] * 1e3:.1f} us/step {contig['gbs']:.0f} GB/s = "
+          f"{contig['pct_of_peak']:.1f}% of peak", file=sys.stderr, flush=True)
 
     p = results[PRIMARY]
     roof_achieved = p["split_kernel_gbs"]
@@ -510,6 +557,7 @@ def main():
                           "window": v["window"], "sinks": v["sinks"], "num_splits": v["num_splits"]}
     line["append"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in app.items()}
     line["metadata"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in meta.items()}
+    line["contiguous"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in contig.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(primary_w, p["algorithmic_bytes"])
     print(json.dumps(line), flush=True)

@@ -366,6 +366,55 @@ int32_t paged_decode_metadata(const pkd_meta_dims* md, const int32_t* req_to_tok
                               int32_t* cu_seqlens_k, int32_t* page_table, int32_t* swa_seqlens,
                               int32_t* swa_page_table, int32_t* d_error_count, void* stream);
 
+/* Dimensions and strides of contiguous_decode (passed as a host pointer). */
+typedef struct {
+  int32_t batch;              /* B >= 0 */
+  int32_t num_q_heads;        /* Hq >= 1 */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;           /* D in {32, 64, 128, 256} */
+  int32_t max_seq_len;        /* token capacity of the K/V tensors, >= 1; every seq_lens[b] <= it */
+  int32_t kv_dtype;           /* a pkd_dtype */
+  int32_t q_len;              /* query tokens per sequence, 1..PKD_MAX_Q_LEN */
+  int32_t causal;             /* as in pkd_dims */
+  int32_t window;             /* as in pkd_dims */
+  int32_t reserved;           /* must be 0 */
+  int64_t q_strides[3];       /* element strides of q: sequence, query token, head (>= 0, multiples of 8) */
+  int64_t kv_strides[3];      /* element strides of k and v: sequence, token, KV head (>= 0; each a multiple
+                                 of 16 bytes; 16 * token stride in bytes < 2^31) */
+  int64_t out_strides[3];     /* element strides of out: sequence, query token, head (>= 0, multiples of 8) */
+} pkd_contig_dims;
+
+/*
+ * contiguous_decode -- the same attention as paged_decode (GQA, several query
+ * tokens, causal mask, window, sinks, BF16 or FP8 K/V, every num_splits mode)
+ * over K/V held in one contiguous tensor each rather than in pages: the
+ * contiguous decode kernels of the AstrAI commit log, with its stride-based
+ * addressing for Q, K/V and O, which reads any layout in place (for instance
+ * [B][L][Hkv][D], or [B][Hkv][L][D] with strides (Hkv L D, D, L D)).
+ *
+ *   k, v      key element (b, t, h, d) at k[b*kv_strides[0] + t*kv_strides[1] +
+ *             h*kv_strides[2] + d] (of kv_dtype; v alike with the same strides).
+ *             Tokens t >= seq_lens[b] are never read.
+ *   q         query row (b, i, h) at q + b*q_strides[0] + i*q_strides[1] + h*q_strides[2].
+ *   out       row (b, i, h) at out + b*out_strides[0] + i*out_strides[1] +
+ *             h*out_strides[2] (bfloat16; rows must not overlap).
+ *   lse       [B][q_len][Hq] fp32, dense, or NULL.
+ *   seq_lens, k_scale, v_scale, sinks, scale, num_splits, workspace, stream:
+ *             as for paged_decode.
+ * The head dimension of every tensor is contiguous.  Internally each sequence
+ * is one page of max_seq_len rounded up to 16 tokens, so num_splits and the
+ * workspace size follow paged_decode's rules for that paged problem
+ * (contiguous_decode_workspace_bytes).  Pointer alignment as for paged_decode.
+ * Returns PKD_OK or a negative status.
+ */
+int32_t contiguous_decode(const pkd_contig_dims* dims, const void* q, const void* k, const void* v,
+                          const int32_t* seq_lens, const float* k_scale, const float* v_scale, const float* sinks,
+                          float scale, void* out, float* lse, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes contiguous_decode needs for num_splits (0 for invalid dims). */
+size_t contiguous_decode_workspace_bytes(const pkd_contig_dims* dims, int32_t num_splits);
+
 /* Human-readable text for a status code (static storage). */
 const char* paged_decode_status_string(int32_t status);
 

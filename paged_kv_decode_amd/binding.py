@@ -42,7 +42,8 @@ PKD_DTYPE_FP8_E4M3 = 1
 
 EXPORTED = ("paged_decode", "paged_decode_partition", "paged_decode_finish", "paged_decode_num_splits",
             "paged_decode_launches", "paged_decode_workspace_bytes", "paged_decode_partials", "paged_decode_merge",
-            "paged_decode_check_tables", "paged_kv_append", "paged_decode_metadata", "paged_decode_status_string")
+            "paged_decode_check_tables", "paged_kv_append", "paged_decode_metadata", "contiguous_decode",
+            "contiguous_decode_workspace_bytes", "paged_decode_status_string")
 
 
 class PkdError(RuntimeError):
@@ -63,6 +64,14 @@ class pkd_meta_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("req_rows", ctypes.c_int32), ("req_stride", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("q_len", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("extend", ctypes.c_int32)]
+
+
+class pkd_contig_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_seq_len", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("q_strides", ctypes.c_int64 * 3), ("kv_strides", ctypes.c_int64 * 3),
+                ("out_strides", ctypes.c_int64 * 3)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -125,6 +134,11 @@ _lib.paged_kv_append.argtypes = [_dims_p, ctypes.c_int64, _p, _p, _p, _p, _p, _i
 _lib.paged_kv_append.restype = _i32
 _lib.paged_decode_metadata.argtypes = [ctypes.POINTER(pkd_meta_dims)] + [_p] * 10
 _lib.paged_decode_metadata.restype = _i32
+_lib.contiguous_decode.argtypes = [ctypes.POINTER(pkd_contig_dims), _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
+                                   _p, _p, _i32, _p, ctypes.c_size_t, _p]
+_lib.contiguous_decode.restype = _i32
+_lib.contiguous_decode_workspace_bytes.argtypes = [ctypes.POINTER(pkd_contig_dims), _i32]
+_lib.contiguous_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.paged_decode_status_string.argtypes = [_i32]
 _lib.paged_decode_status_string.restype = ctypes.c_char_p
 
@@ -211,6 +225,17 @@ def paged_decode_metadata(md, req_to_token, req_pool_indices, seq_lens, cache_se
                                       _ptr(req_pool_indices), _ptr(seq_lens), _ptr(cache_seqlens),
                                       _ptr(cu_seqlens_k), _ptr(page_table), _ptr(swa_seqlens),
                                       _ptr(swa_page_table), _ptr(d_error_count), _ptr(stream))
+
+
+def contiguous_decode(cd, q, k, v, seq_lens, k_scale, v_scale, sinks, scale, out, lse, num_splits, workspace,
+                      workspace_bytes, stream) -> int:
+    return _lib.contiguous_decode(None if cd is None else ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), _ptr(sinks), float(scale), _ptr(out),
+                                  _ptr(lse), int(num_splits), _ptr(workspace), int(workspace_bytes), _ptr(stream))
+
+
+def contiguous_decode_workspace_bytes(cd, num_splits: int) -> int:
+    return _lib.contiguous_decode_workspace_bytes(None if cd is None else ctypes.byref(cd), int(num_splits))
 
 
 def paged_decode_status_string(status: int) -> str:
@@ -339,3 +364,44 @@ def metadata(req_to_token, req_pool_indices, seq_lens, page_size: int, max_pages
     if st != PKD_OK:
         raise PkdError(st)
     return res
+
+
+def contig_dims_for(q, k, out, causal: bool = False, window: int = 0) -> pkd_contig_dims:
+    """pkd_contig_dims from torch views q and out [B, Hq, D] or [B, q_len, Hq, D] and
+    k [B, L_max, Hkv, D] (any strides; the last dimension contiguous)."""
+    import torch
+    q4 = q if q.dim() == 4 else q.unsqueeze(1)
+    o4 = out if out.dim() == 4 else out.unsqueeze(1)
+    B, q_len, hq, d = q4.shape
+    _, cap, hkv, d2 = k.shape
+    if d2 != d or q.stride(-1) != 1 or k.stride(-1) != 1 or out.stride(-1) != 1:
+        raise ValueError("head dims differ or are not contiguous")
+    kvd = PKD_DTYPE_FP8_E4M3 if k.dtype == torch.float8_e4m3fn else PKD_DTYPE_BF16
+    arr = ctypes.c_int64 * 3
+    return pkd_contig_dims(B, hq, hkv, d, cap, kvd, q_len, int(bool(causal)), int(window), 0,
+                           arr(*q4.stride()[:3]), arr(*k.stride()[:3]), arr(*o4.stride()[:3]))
+
+
+def contiguous(q, k, v, seq_lens, scale: float, k_scale=None, v_scale=None, num_splits: int = 0, out=None,
+               lse=None, stream: Optional[int] = None, causal: bool = False, window: int = 0, sinks=None):
+    """Run contiguous_decode on torch device views q ([B, Hq, D] or [B, q_len, Hq, D]) and
+    k, v ([B, L_max, Hkv, D], any strides: e.g. a permuted [B, Hkv, L_max, D] tensor).
+    out defaults to a dense tensor shaped like q; returns (out, lse)."""
+    import torch
+    if k.stride() != v.stride() or k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must share shape, strides and dtype")
+    dev = q.device
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    cd = contig_dims_for(q, k, out, causal, window)
+    need = contiguous_decode_workspace_bytes(cd, num_splits)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = current_stream_handle(dev)
+    st = contiguous_decode(cd, q, k, v, seq_lens, k_scale, v_scale, sinks, scale, out, lse, num_splits, ws, need,
+                           stream)
+    if st != PKD_OK:
+        raise PkdError(st)
+    return out, lse

@@ -167,10 +167,35 @@ int32_t heuristic_splits(const pkd_dims& d, int32_t max_len) {
   return (int32_t)s;
 }
 
-pkd::SplitParams make_split_params(const pkd_dims& d, const void* q, const void* k, const void* v,
-                                   const int32_t* bt, const int32_t* lens, const float* ks,
+// Where q, out and the K/V rows are.  Paged caches use the dense layouts of the
+// header; contiguous K/V and strided q / out come from contiguous_decode.
+struct Layout {
+  pkd::RowStrides qs, os;
+  pkd::KvLayout kv;
+  bool dense_out;  // os is the dense [B][q_len][Hq][D] layout
+};
+
+int64_t kv_elem_bytes(const pkd_dims& d) { return d.kv_dtype == PKD_DTYPE_FP8_E4M3 ? 1 : 2; }
+
+Layout paged_layout(const pkd_dims& d) {
+  Layout L;
+  const int64_t D = d.head_dim;
+  L.qs = {(int64_t)d.q_len * d.num_q_heads * D, (int64_t)d.num_q_heads * D, D};
+  L.os = L.qs;
+  L.kv.head_stride = D * kv_elem_bytes(d);
+  L.kv.tok_stride = (int32_t)(d.num_kv_heads * L.kv.head_stride);
+  L.kv.page_stride = (int64_t)d.page_size * L.kv.tok_stride;
+  L.dense_out = true;
+  return L;
+}
+
+pkd::SplitParams make_split_params(const pkd_dims& d, const Layout& lay, const void* q, const void* k,
+                                   const void* v, const int32_t* bt, const int32_t* lens, const float* ks,
                                    const float* vs, float scale, int S) {
   pkd::SplitParams p{};
+  p.qs = lay.qs;
+  p.os = lay.os;
+  p.kv = lay.kv;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint8_t*>(k);
   p.v = static_cast<const uint8_t*>(v);
@@ -259,8 +284,8 @@ int32_t paged_decode_partials(const pkd_dims* dims, const void* q, const void* k
   if (!aligned(o_part, 16) || !aligned(lse_part, 4)) return PKD_ERR_ALIGNMENT;
   if (num_splits < 1 || num_splits > PKD_MAX_SPLITS) return PKD_ERR_NUM_SPLITS;
   if (dims->batch == 0) return PKD_OK;
-  pkd::SplitParams p = make_split_params(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale,
-                                         v_scale, scale, num_splits);
+  pkd::SplitParams p = make_split_params(*dims, paged_layout(*dims), q, k_cache, v_cache, block_table, seq_lens,
+                                         k_scale, v_scale, scale, num_splits);
   p.o_part = o_part;
   p.lse_part = lse_part;
   return launch_partition(*dims, p, false, static_cast<hipStream_t>(stream));
@@ -311,10 +336,13 @@ int32_t make_plan(const pkd_dims& d, int32_t num_splits, Plan* pl) {
   return PKD_OK;
 }
 
-pkd::BalancedParams make_balanced_params(const pkd_dims& d, const void* q, const void* k, const void* v,
-                                         const int32_t* bt, const int32_t* lens, const float* ks,
+pkd::BalancedParams make_balanced_params(const pkd_dims& d, const Layout& lay, const void* q, const void* k,
+                                         const void* v, const int32_t* bt, const int32_t* lens, const float* ks,
                                          const float* vs, float scale, void* ws, const Plan& pl) {
   pkd::BalancedParams b{};
+  b.qs = lay.qs;
+  b.os = lay.os;
+  b.kv = lay.kv;
   b.q = static_cast<const uint16_t*>(q);
   b.k = static_cast<const uint8_t*>(k);
   b.v = static_cast<const uint8_t*>(v);
@@ -343,26 +371,29 @@ pkd::BalancedParams make_balanced_params(const pkd_dims& d, const void* q, const
 }
 
 // Partition phase of a split plan (S > 1 or balanced) into the workspace.
-int32_t run_partition(const pkd_dims& d, const void* q, const void* k, const void* v, const int32_t* bt,
-                      const int32_t* lens, const float* ks, const float* vs, float scale, void* ws,
-                      const Plan& pl, hipStream_t s) {
+int32_t run_partition(const pkd_dims& d, const Layout& lay, const void* q, const void* k, const void* v,
+                      const int32_t* bt, const int32_t* lens, const float* ks, const float* vs, float scale,
+                      void* ws, const Plan& pl, hipStream_t s) {
   if (pl.balanced) {
-    const pkd::BalancedParams b = make_balanced_params(d, q, k, v, bt, lens, ks, vs, scale, ws, pl);
+    const pkd::BalancedParams b = make_balanced_params(d, lay, q, k, v, bt, lens, ks, vs, scale, ws, pl);
     return pkd::launch_balanced(b, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, s) == hipSuccess
                ? PKD_OK : PKD_ERR_LAUNCH;
   }
-  pkd::SplitParams p = make_split_params(d, q, k, v, bt, lens, ks, vs, scale, pl.S);
+  pkd::SplitParams p = make_split_params(d, lay, q, k, v, bt, lens, ks, vs, scale, pl.S);
   p.o_part = static_cast<float*>(ws);
   p.lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.lse_off);
   return launch_partition(d, p, false, s);
 }
 
 // Merge phase of a split plan from the workspace (sinks: [Hq] or null).
-int32_t run_finish(const pkd_dims& d, const void* ws, const float* sinks, void* out, float* lse,
-                   const Plan& pl, hipStream_t s) {
+int32_t run_finish(const pkd_dims& d, const Layout& lay, const void* ws, const float* sinks, void* out,
+                   float* lse, const Plan& pl, hipStream_t s) {
   pkd::MergeParams m{};
   m.sinks = sinks;
   m.hq = d.num_q_heads;
+  m.q_len = d.q_len;
+  m.strided_out = lay.dense_out ? 0 : 1;
+  m.os = lay.os;
   m.o_part = static_cast<const float*>(ws);
   m.lse_part = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + pl.lse_off);
   m.out = static_cast<uint16_t*>(out);
@@ -382,6 +413,42 @@ int32_t run_finish(const pkd_dims& d, const void* ws, const float* sinks, void* 
     m.num_splits = pl.S;
   }
   return pkd::launch_lse_merge(m, d.head_dim, s) == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
+}
+
+// The whole decode once every argument has been checked: plan, then one
+// partition kernel (direct output or in-kernel merge) or partition + merge.
+int32_t decode_checked(const pkd_dims& d, const Layout& lay, const void* q, const void* k, const void* v,
+                       const int32_t* bt, const int32_t* lens, const float* ks, const float* vs, const float* sinks,
+                       float scale, void* out, float* lse, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes, hipStream_t s) {
+  Plan pl;
+  int32_t st = make_plan(d, num_splits, &pl);
+  if (st != PKD_OK) return st;
+  if (pl.need > 0 && (!workspace || workspace_bytes < pl.need)) return PKD_ERR_WORKSPACE;
+  if (d.batch == 0) return PKD_OK;
+  if (current_cu_count() < 0) return PKD_ERR_DEVICE;
+  if (pl.S == 1) {
+    pkd::SplitParams p = make_split_params(d, lay, q, k, v, bt, lens, ks, vs, scale, 1);
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.sinks = sinks;
+    return launch_partition(d, p, true, s);
+  }
+  if (pl.balanced && balanced_fused(d)) {
+    // One kernel: the partition merges each segment's pieces itself.
+    pkd::BalancedParams b = make_balanced_params(d, lay, q, k, v, bt, lens, ks, vs, scale, workspace, pl);
+    b.fused = 1;
+    b.out = static_cast<uint16_t*>(out);
+    b.lse = lse;
+    b.sinks = sinks;
+    b.seg_count = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + pl.count_off);
+    b.epoch = next_epoch();
+    return pkd::launch_balanced(b, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, s) == hipSuccess
+               ? PKD_OK : PKD_ERR_LAUNCH;
+  }
+  st = run_partition(d, lay, q, k, v, bt, lens, ks, vs, scale, workspace, pl, s);
+  if (st != PKD_OK) return st;
+  return run_finish(d, lay, workspace, sinks, out, lse, pl, s);
 }
 
 }  // namespace
@@ -407,38 +474,9 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
   if (!out) return PKD_ERR_NULL_POINTER;
   st = check_out_ws(out, lse, workspace);
   if (st != PKD_OK) return st;
-  Plan pl;
-  st = make_plan(*dims, num_splits, &pl);
-  if (st != PKD_OK) return st;
-  if (pl.need > 0 && (!workspace || workspace_bytes < pl.need)) return PKD_ERR_WORKSPACE;
-  if (dims->batch == 0) return PKD_OK;
-  if (current_cu_count() < 0) return PKD_ERR_DEVICE;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pl.S == 1) {
-    pkd::SplitParams p = make_split_params(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale,
-                                           v_scale, scale, 1);
-    p.out = static_cast<uint16_t*>(out);
-    p.lse = lse;
-    p.sinks = sinks;
-    return launch_partition(*dims, p, true, s);
-  }
-  if (pl.balanced && balanced_fused(*dims)) {
-    // One kernel: the partition merges each segment's pieces itself.
-    pkd::BalancedParams b = make_balanced_params(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale,
-                                                 v_scale, scale, workspace, pl);
-    b.fused = 1;
-    b.out = static_cast<uint16_t*>(out);
-    b.lse = lse;
-    b.sinks = sinks;
-    b.seg_count = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + pl.count_off);
-    b.epoch = next_epoch();
-    return pkd::launch_balanced(b, dims->head_dim, dims->kv_dtype == PKD_DTYPE_FP8_E4M3, s) == hipSuccess
-               ? PKD_OK : PKD_ERR_LAUNCH;
-  }
-  st = run_partition(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, workspace,
-                     pl, s);
-  if (st != PKD_OK) return st;
-  return run_finish(*dims, workspace, sinks, out, lse, pl, s);
+  return decode_checked(*dims, paged_layout(*dims), q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                        sinks, scale, out, lse, num_splits, workspace, workspace_bytes,
+                        static_cast<hipStream_t>(stream));
 }
 
 int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* k_cache,
@@ -456,8 +494,8 @@ int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* 
   if (!aligned(workspace, 16)) return PKD_ERR_ALIGNMENT;
   if (dims->batch == 0) return PKD_OK;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
-  return run_partition(*dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, workspace,
-                       pl, static_cast<hipStream_t>(stream));
+  return run_partition(*dims, paged_layout(*dims), q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                       scale, workspace, pl, static_cast<hipStream_t>(stream));
 }
 
 int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void* workspace,
@@ -475,7 +513,7 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
   if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
   if (dims->batch == 0) return PKD_OK;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
-  return run_finish(*dims, workspace, sinks, out, lse, pl, static_cast<hipStream_t>(stream));
+  return run_finish(*dims, paged_layout(*dims), workspace, sinks, out, lse, pl, static_cast<hipStream_t>(stream));
 }
 
 int32_t paged_decode_check_tables(const pkd_dims* dims, const int32_t* block_table,
@@ -577,6 +615,71 @@ int32_t paged_decode_metadata(const pkd_meta_dims* md, const int32_t* req_to_tok
   m.extend = md->extend;
   return pkd::launch_decode_metadata(m, static_cast<hipStream_t>(stream)) == hipSuccess ? PKD_OK
                                                                                          : PKD_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The paged problem a contiguous one is run as (one page per sequence, page b
+// = sequence b, page_size the capacity rounded up to 16) and its layout.
+int32_t contiguous_plan(const pkd_contig_dims* c, pkd_dims* d, Layout* lay) {
+  if (!c) return PKD_ERR_NULL_POINTER;
+  if (c->max_seq_len < 1 || c->reserved != 0) return PKD_ERR_BAD_DIMS;
+  const int64_t ps = ((int64_t)c->max_seq_len + 15) / 16 * 16;
+  if (ps > INT32_MAX) return PKD_ERR_BAD_DIMS;
+  *d = pkd_dims{c->batch, c->num_q_heads, c->num_kv_heads, c->head_dim, (int32_t)ps, c->batch > 0 ? c->batch : 1,
+                1, c->kv_dtype, c->q_len, c->causal, c->window};
+  const int32_t st = check_dims(d);
+  if (st != PKD_OK) return st;
+  for (int i = 0; i < 3; ++i)
+    if (c->q_strides[i] < 0 || c->kv_strides[i] < 0 || c->out_strides[i] < 0) return PKD_ERR_BAD_DIMS;
+  const int64_t e = kv_elem_bytes(*d);
+  if (c->kv_strides[1] * e > INT32_MAX / 16) return PKD_ERR_BAD_DIMS;
+  for (int i = 0; i < 3; ++i)
+    if (c->q_strides[i] % 8 != 0 || c->out_strides[i] % 8 != 0 || (c->kv_strides[i] * e) % 16 != 0)
+      return PKD_ERR_ALIGNMENT;
+  lay->qs = {c->q_strides[0], c->q_strides[1], c->q_strides[2]};
+  lay->os = {c->out_strides[0], c->out_strides[1], c->out_strides[2]};
+  lay->kv.page_stride = c->kv_strides[0] * e;
+  lay->kv.tok_stride = (int32_t)(c->kv_strides[1] * e);
+  lay->kv.head_stride = c->kv_strides[2] * e;
+  const Layout dense = paged_layout(*d);
+  lay->dense_out = lay->os.b == dense.os.b && lay->os.i == dense.os.i && lay->os.h == dense.os.h;
+  return PKD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t contiguous_decode_workspace_bytes(const pkd_contig_dims* dims, int32_t num_splits) {
+  pkd_dims d;
+  Layout lay;
+  if (contiguous_plan(dims, &d, &lay) != PKD_OK) return 0;
+  return paged_decode_workspace_bytes(&d, num_splits);
+}
+
+int32_t contiguous_decode(const pkd_contig_dims* dims, const void* q, const void* k, const void* v,
+                          const int32_t* seq_lens, const float* k_scale, const float* v_scale, const float* sinks,
+                          float scale, void* out, float* lse, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  pkd_dims d;
+  Layout lay;
+  int32_t st = contiguous_plan(dims, &d, &lay);
+  if (st != PKD_OK) return st;
+  if (!q || !k || !v || !seq_lens || !out) return PKD_ERR_NULL_POINTER;
+  const bool fp8 = d.kv_dtype == PKD_DTYPE_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale)) return PKD_ERR_SCALES;
+  if (!fp8 && (k_scale || v_scale)) return PKD_ERR_SCALES;
+  if (!std::isfinite(scale)) return PKD_ERR_BAD_DIMS;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(seq_lens, 4) || !aligned(k_scale, 4) ||
+      !aligned(v_scale, 4) || !aligned(sinks, 4))
+    return PKD_ERR_ALIGNMENT;
+  st = check_out_ws(out, lse, workspace);
+  if (st != PKD_OK) return st;
+  return decode_checked(d, lay, q, k, v, nullptr, seq_lens, k_scale, v_scale, sinks, scale, out, lse, num_splits,
+                        workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 const char* paged_decode_status_string(int32_t status) {

@@ -121,8 +121,15 @@ __global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(co
     }
     r.M = Mx;
   }
-  r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane,
-          p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY);
+  int64_t ooff = row * D;
+  if (p.strided_out) {
+    const int64_t per_seq = (int64_t)p.q_len * p.hq;
+    const int64_t b = row / per_seq;
+    const int rem = (int)(row - b * per_seq);
+    const int qi = rem / p.hq;
+    ooff = p.os.at(b, qi, rem - qi * p.hq);
+  }
+  r.store(p.out + ooff, p.lse ? p.lse + row : nullptr, lane, p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY);
 }
 
 // Counts sequences with a length outside [0, max_pages * page_size] and used

@@ -11,16 +11,34 @@ namespace pkd {
 // (b * q_len + i) * Hq + h.  The q_len * G rows of one KV head are "packed
 // rows" r = i * G + (h - kvh * G), grouped 16 to a head group.
 
+// Element strides of a (sequence, query token, head) row of q or out; the
+// head dimension is contiguous.  Dense [B][q_len][Hq][D]: (q_len Hq D, Hq D, D).
+struct RowStrides {
+  int64_t b, i, h;
+  __host__ __device__ int64_t at(int64_t bb, int64_t ii, int64_t hh) const { return bb * b + ii * i + hh * h; }
+};
+
+// Where K/V rows sit, in bytes: row (page, slot, KV head) at page * page_stride
+// + slot * tok_stride + head * head_stride.  A paged cache [P][ps][Hkv][D] has
+// (ps Hkv D e, Hkv D e, D e).  A contiguous cache is read as one page per
+// sequence (page = b, no block table) whose page_size covers every length, with
+// the tensor's own sequence, token and head strides.
+struct KvLayout {
+  int64_t page_stride;
+  int64_t head_stride;
+  int32_t tok_stride;          // 16 * tok_stride < 2^31 (offsets inside a 16-token group are 32-bit)
+};
+
 // Arguments of the split-KV partition kernel (one launch).
 struct SplitParams {
-  const uint16_t* q;           // [B][q_len][Hq][D] bf16
-  const uint8_t* k;            // [num_pages][ps][Hkv][D] kv elements (bf16 or fp8 codes)
+  const uint16_t* q;           // rows at qs.at(b, i, h), bf16
+  const uint8_t* k;            // kv elements (bf16 or fp8 codes) placed by kv
   const uint8_t* v;
-  const int32_t* block_table;  // [B][max_pages]
+  const int32_t* block_table;  // [B][max_pages], or null: page b holds sequence b (contiguous K/V)
   const int32_t* seq_lens;     // [B]
   const float* k_scale;        // [Hkv] (fp8) or null
   const float* v_scale;
-  uint16_t* out;               // direct mode: [B][q_len][Hq][D] bf16
+  uint16_t* out;               // direct mode: rows at os.at(b, i, h), bf16
   float* lse;                  // direct mode: [B][q_len][Hq] or null
   float* o_part;               // split mode: [B][q_len][Hq][S][D]
   float* lse_part;             // split mode: [B][q_len][Hq][S]
@@ -35,6 +53,8 @@ struct SplitParams {
   int32_t num_splits;
   int32_t chunk;               // tokens per split (a multiple of kSplitAlign, or >= every visible span);
                                // splits start at the sequence's first visible 16-token group
+  RowStrides qs, os;
+  KvLayout kv;
 };
 
 // Arguments of the balanced persistent partition kernel.
@@ -67,6 +87,8 @@ struct BalancedParams {
   float* lse;                  // [B][q_len][Hq] or null (fused)
   uint64_t* seg_count;         // [B * Hkv * head_groups] (fused)
   uint64_t epoch;              // distinct per call, 1 .. 2^40 - 1 (fused)
+  RowStrides qs, os;           // as in SplitParams
+  KvLayout kv;
 };
 
 // True when the balanced mode merges inside the partition kernel: when there
@@ -94,6 +116,8 @@ struct MergeParams {
   int32_t batch, hq, hkv, group, head_groups, hpg, num_workers;
   int32_t q_len;               // balanced layout: rows are (b * q_len + i) * Hq + h
   const float* sinks;          // [Hq] sink logits or null; row r has head r % hq (hq set whenever sinks is)
+  int32_t strided_out;         // 0: out row r at r * D; 1: at os.at(b, i, h) of row r = (b q_len + i) Hq + h
+  RowStrides os;               //    (q_len and hq set)
 };
 
 // Arguments of the paged KV append kernel.

@@ -65,17 +65,20 @@ split_kv_kernel(const SplitParams p) {
   const int s0 = (int)min((int64_t)lo + (int64_t)split * chunk, (int64_t)L);
   const int s1 = (int)min((int64_t)s0 + chunk, (int64_t)L);
   const int heads_here = min(kHeadsPerGroup, p.rows_kv - hg * kHeadsPerGroup);
-  // Memory rows of the workgroup's packed rows (query token, head).
+  // Row indices and out offsets of the workgroup's packed rows (query token, head).
   __shared__ int64_t s_rows[kHeadsPerGroup];
+  __shared__ int64_t s_orow[kHeadsPerGroup];
 
   if (s0 >= s1) {
     // Empty split (or an empty sequence): o = 0, lse = -inf (the sink logit
     // for a direct row with a sink).
     for (int idx = tid; idx < heads_here * D; idx += kWaves * 64) {
       const int hh = idx / D, d = idx - (idx / D) * D;
-      const int64_t row = packed_row(b, kvh, hg * kHeadsPerGroup + hh, p.q_len, p.hq, p.group);
+      const int r = hg * kHeadsPerGroup + hh;
+      const int qi = r / p.group, h = kvh * p.group + (r - qi * p.group);
+      const int64_t row = ((int64_t)b * p.q_len + qi) * p.hq + h;
       if constexpr (DIRECT) {
-        p.out[row * D + d] = 0;
+        p.out[p.os.at(b, qi, h) + d] = 0;
         if (d == 0 && p.lse) p.lse[row] = p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY;
       } else {
         p.o_part[(row * S + split) * D + d] = 0.f;
@@ -87,31 +90,37 @@ split_kv_kernel(const SplitParams p) {
 
   const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
   const int lim = s1 - 1;
-  const int tok_stride = p.hkv * C::ROWB;  // bytes between consecutive slots of a page
-  const int64_t head_off = (int64_t)kvh * C::ROWB;
+  const int tok_stride = p.kv.tok_stride;  // bytes between consecutive slots of a page
+  const int64_t page_stride = p.kv.page_stride;
+  const int64_t head_off = (int64_t)kvh * p.kv.head_stride;
   const int ps = p.page_size;
   // The block table is read-only for the whole launch (constant address space).
   const __attribute__((address_space(4))) int32_t* bt =
       (const __attribute__((address_space(4))) int32_t*)(p.block_table + (int64_t)b * p.max_pages);
 
   const LaneRow lr = lane_row(p, b, kvh, hg, A.n, L, s1);
-  if (tid < kHeadsPerGroup) s_rows[tid] = lr.row;  // read after the barriers below
-  A.load_q(p.q, lr.row, lr.valid);
+  if (tid < kHeadsPerGroup) {  // read after the barriers below
+    s_rows[tid] = lr.row;
+    s_orow[tid] = lr.ooff;
+  }
+  A.load_q(p.q + lr.qoff, lr.valid);
   A.qk_scale = p.qk_scale_log2;
   if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
   A.reset();
 
   // The split's block-table entries are staged in LDS once (when they fit), so
   // that per-tile page lookups are short LDS reads rather than dependent HBM
-  // reads on the path of every tile's loads.
+  // reads on the path of every tile's loads.  Without a block table (contiguous
+  // K/V) sequence b is page b.
   int32_t* sbt = reinterpret_cast<int32_t*>(smem + C::BT_OFFSET);
+  const bool contiguous = p.block_table == nullptr;
   const int first_page = s0 / ps;
   const int n_pages = lim / ps - first_page + 1;
-  const bool staged = n_pages <= C::BT_ENTRIES;
+  const bool staged = !contiguous && n_pages <= C::BT_ENTRIES;
   if (staged)
     for (int i = tid; i < n_pages; i += kWaves * 64) sbt[i] = bt[first_page + i];
   __syncthreads();
-  auto page_of = [&](int pidx) -> int { return staged ? sbt[pidx - first_page] : bt[pidx]; };
+  auto page_of = [&](int pidx) -> int { return contiguous ? b : staged ? sbt[pidx - first_page] : bt[pidx]; };
 
   auto fetch = [&](int tile, Pages& P) {
     const int tb = s0 + tile * C::TT;
@@ -126,9 +135,9 @@ split_kv_kernel(const SplitParams p) {
   auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R, bool idle) {
     const int tb = s0 + tile * C::TT;
     if constexpr (PAGED16)
-      A.issue_paged16(p.k, p.v, tb, lim, P.pg, ps, tok_stride, head_off, R, idle);
+      A.issue_paged16(p.k, p.v, tb, lim, P.pg, ps, tok_stride, page_stride, head_off, R, idle);
     else
-      A.issue_generic(p.k, p.v, tb, lim, P.pg, ps, tok_stride, head_off, R, idle);
+      A.issue_generic(p.k, p.v, tb, lim, P.pg, ps, tok_stride, page_stride, head_off, R, idle);
   };
 
   uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;  // this wave's V[TT][VS]
@@ -139,7 +148,7 @@ split_kv_kernel(const SplitParams p) {
   auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
     const int64_t row = s_rows[hh];
     if constexpr (DIRECT) {
-      *reinterpret_cast<bf16x4*>(p.out + row * D + d0) = to_bf16x4(o);
+      *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + d0) = to_bf16x4(o);
       if (d0 == 0 && p.lse) p.lse[row] = lse_nat;
     } else {
       *reinterpret_cast<f32x4*>(p.o_part + (row * S + split) * D + d0) = o;
@@ -179,7 +188,8 @@ balanced_kernel(const BalancedParams p) {
   __shared__ int64_t spre[kBalancedMaxBatch + 1];  // spre[b] = groups of all segments of sequences < b
   __shared__ int64_t stot[NWV];
   __shared__ int s_last;                           // in-kernel merge: this piece completes its segment
-  __shared__ int64_t s_rows[kHeadsPerGroup];       // memory rows of the current piece's packed rows
+  __shared__ int64_t s_rows[kHeadsPerGroup];       // row indices of the current piece's packed rows
+  __shared__ int64_t s_orow[kHeadsPerGroup];       // their out offsets
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -231,7 +241,10 @@ balanced_kernel(const BalancedParams p) {
     const int rows_seq = p.q_len * p.hq;
     for (int bb = (int)w; bb < B; bb += p.num_workers) {
       if (spre[bb + 1] != spre[bb]) continue;
-      for (int i = tid; i < rows_seq * D; i += NWV * 64) p.out[(int64_t)bb * rows_seq * D + i] = 0;
+      for (int i = tid; i < rows_seq * D; i += NWV * 64) {
+        const int rr = i / D, qi = rr / p.hq;
+        p.out[p.os.at(bb, qi, rr - qi * p.hq) + (i - rr * D)] = 0;
+      }
       if (p.lse)
         for (int i = tid; i < rows_seq; i += NWV * 64)
           p.lse[(int64_t)bb * rows_seq + i] = p.sinks ? p.sinks[i % p.hq] : -INFINITY;
@@ -260,13 +273,16 @@ balanced_kernel(const BalancedParams p) {
   A.init_lane(tid & 63);
   uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;
   const int ps = p.page_size;
-  const int tok_stride = p.hkv * C::ROWB;
+  const int tok_stride = p.kv.tok_stride;
+  const int64_t page_stride = p.kv.page_stride;
 
   // Page window of a piece: lane j holds block-table entry first_page + j of
   // sequence bb (entries past the row are not read; entries past the pieces's
   // last page are never used).  The next piece's window is loaded while the
-  // current piece runs.
+  // current piece runs.  Without a block table (contiguous K/V) sequence bb is
+  // page bb, its only page.
   auto load_window = [&](int bb, int first_page) -> int {
+    if (p.block_table == nullptr) return bb;
     const int idx = first_page + A.lane;
     return idx < p.max_pages ? p.block_table[(int64_t)bb * p.max_pages + idx] : 0;
   };
@@ -285,8 +301,11 @@ balanced_kernel(const BalancedParams p) {
     const int hg = seg - kvh * p.head_groups;
     const int heads_here = min(kHeadsPerGroup, p.rows_kv - hg * kHeadsPerGroup);
     const LaneRow lr = lane_row(p, b, kvh, hg, A.n, L, s1);
-    if (tid < kHeadsPerGroup) s_rows[tid] = lr.row;  // read after the combine's barriers
-    const int64_t head_off = (int64_t)kvh * C::ROWB;
+    if (tid < kHeadsPerGroup) {  // read after the combine's barriers
+      s_rows[tid] = lr.row;
+      s_orow[tid] = lr.ooff;
+    }
+    const int64_t head_off = (int64_t)kvh * p.kv.head_stride;
 
     // The next piece: the following segment (of this or a later sequence).
     const int64_t npos = pos + (gend - grp);
@@ -298,7 +317,7 @@ balanced_kernel(const BalancedParams p) {
     const int nlo = npos < hi ? (nbq == b ? lo : first_of(nbq)) : 0;
     const int next_window = npos < hi ? load_window(nbq, nlo / ps) : 0;
 
-    A.load_q(p.q, lr.row, lr.valid);
+    A.load_q(p.q + lr.qoff, lr.valid);
     A.qk_scale = p.qk_scale_log2;
     if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
     A.reset();
@@ -316,7 +335,7 @@ balanced_kernel(const BalancedParams p) {
       for (int q = 0; q < C::NGRP; ++q) P.pg[q] = page_of((min(tb + 16 * q, lim) & ~15) / ps);
     };
     auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R, bool idle) {
-      A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, head_off, R, idle);
+      A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, page_stride, head_off, R, idle);
     };
     const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
     run_tiles<D, FP8, Pages>(A, wave, NWV, ntiles, s0, lr.start, lr.end, vs, fetch, issue);
@@ -332,7 +351,7 @@ balanced_kernel(const BalancedParams p) {
       // The whole segment is this piece: write the result directly.
       auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
         const int64_t row = s_rows[hh];
-        *reinterpret_cast<bf16x4*>(p.out + row * D + d0) = to_bf16x4(o);
+        *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + d0) = to_bf16x4(o);
         if (d0 == 0 && p.lse) p.lse[row] = lse_nat;
       };
       if (p.sinks)
@@ -402,7 +421,7 @@ balanced_kernel(const BalancedParams p) {
               RM r;
               r.run(lp0 + hh, ls, op0 + hh * D, os, npieces, lane);
               const int64_t row = s_rows[hh];
-              r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane,
+              r.store(p.out + s_orow[hh], p.lse ? p.lse + row : nullptr, lane,
                       p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY);
             }
           } else {
@@ -422,7 +441,7 @@ balanced_kernel(const BalancedParams p) {
                   RM r;
                   r.finish(st[k], npieces, lane);
                   const int64_t row = s_rows[hh];
-                  r.store(p.out + row * D, p.lse ? p.lse + row : nullptr, lane,
+                  r.store(p.out + s_orow[hh], p.lse ? p.lse + row : nullptr, lane,
                           p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY);
                 }
               }

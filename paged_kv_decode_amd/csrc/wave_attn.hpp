@@ -223,8 +223,7 @@ struct WaveAttn {
   // Lane (n, g) holds packed row n's dims (kk / R) * 4 * PIECE + g * PIECE + (kk % R) * 8 + [0, 8)
   // for MFMA kk; the K loads use the same dim assignment.  qrow_n is the memory
   // row of packed row n (any valid row when hv is false); rows past the group are zero.
-  __device__ __forceinline__ void load_q(const uint16_t* q, int64_t qrow_n, bool hv) {
-    const uint16_t* qrow = q + qrow_n * D;
+  __device__ __forceinline__ void load_q(const uint16_t* qrow, bool hv) {
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       const int d0 = (kk / C::R) * 4 * C::PIECE + g * C::PIECE + (kk % C::R) * 8;
@@ -249,7 +248,7 @@ struct WaveAttn {
   // idle: read the same rows of physical page 0 instead (shared by every
   // workgroup, so they come from cache); the data is not used.
   __device__ __forceinline__ void issue_paged16(const uint8_t* kc, const uint8_t* vc, int tb, int lim,
-                                                const int* pages, int ps, int tok_stride,
+                                                const int* pages, int ps, int tok_stride, int64_t page_stride,
                                                 int64_t head_off, Regs& R, bool idle) const {
     int64_t gbase[C::NGRP];
     int glim[C::NGRP];
@@ -257,7 +256,7 @@ struct WaveAttn {
     for (int q = 0; q < C::NGRP; ++q) {
       const int gt = min(tb + 16 * q, lim) & ~15;
       const int page = idle ? 0 : __builtin_amdgcn_readfirstlane(pages[q]);
-      gbase[q] = ((int64_t)page * ps + (gt - (gt / ps) * ps)) * tok_stride + head_off;
+      gbase[q] = (int64_t)page * page_stride + (int64_t)(gt - (gt / ps) * ps) * tok_stride + head_off;
       glim[q] = lim - gt;
     }
 #pragma unroll
@@ -289,12 +288,13 @@ struct WaveAttn {
   // Any page size: pages[blk] is the page of this lane's K row of row block
   // blk, pages[NBLK + i] that of its row of V load i (rows clamped to lim).
   __device__ __forceinline__ void issue_generic(const uint8_t* kc, const uint8_t* vc, int tb, int lim,
-                                                const int* pages, int ps, int tok_stride,
+                                                const int* pages, int ps, int tok_stride, int64_t page_stride,
                                                 int64_t head_off, Regs& R, bool idle) const {
 #pragma unroll
     for (int blk = 0; blk < C::NBLK; ++blk) {
       const int tok = min(tb + k_row_token<C::KP>(blk, n), lim);
-      const int64_t off = ((int64_t)(idle ? 0 : pages[blk]) * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
+      const int64_t off = (int64_t)(idle ? 0 : pages[blk]) * page_stride + (int64_t)(tok - (tok / ps) * ps) * tok_stride +
+                          head_off;
       const uint8_t* src = kc + off + k_doff;
 #pragma unroll
       for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = kload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
@@ -302,8 +302,8 @@ struct WaveAttn {
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
       const int tok = min(tb + i * C::RPI + v_rig, lim);
-      const int64_t off =
-          ((int64_t)(idle ? 0 : pages[C::NBLK + i]) * ps + (tok - (tok / ps) * ps)) * tok_stride + head_off;
+      const int64_t off = (int64_t)(idle ? 0 : pages[C::NBLK + i]) * page_stride +
+                          (int64_t)(tok - (tok / ps) * ps) * tok_stride + head_off;
       R.v[i] = gload<C::VLB>(vc + off + v_doff);
     }
   }
@@ -441,12 +441,14 @@ __device__ __forceinline__ int64_t packed_row(int b, int kvh, int r, int q_len, 
   return ((int64_t)b * q_len + i) * hq + kvh * group + (r - i * group);
 }
 
-// Per lane (packed row n = lane % 16 of head group hg): the memory row of its
-// query (a valid row even past the group), whether the row exists, and the end
-// of the tokens it sees within [.., s1): s1, or under the causal mask
-// min(s1, L - q_len + i + 1) for query token i.
+// Per lane (packed row n = lane % 16 of head group hg): the row index of its
+// query (a valid row even past the group), the element offsets of that row in
+// q and out, whether the row exists, and the range of tokens it sees within
+// [.., s1): to s1, or under the causal mask min(s1, L - q_len + i + 1) for
+// query token i; from its window start.
 struct LaneRow {
   int64_t row;
+  int64_t qoff, ooff;
   bool valid;
   int start;  // first position the row sees (its sliding window's lower end; 0 without a window)
   int end;
@@ -457,8 +459,11 @@ __device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, 
   LaneRow lr;
   lr.valid = r < p.rows_kv;
   const int rr = lr.valid ? r : hg * kHeadsPerGroup;
-  lr.row = packed_row(b, kvh, rr, p.q_len, p.hq, p.group);
-  const int pos = L - p.q_len + rr / p.group;  // the query token's position
+  const int i = rr / p.group, h = kvh * p.group + (rr - i * p.group);
+  lr.row = ((int64_t)b * p.q_len + i) * p.hq + h;
+  lr.qoff = p.qs.at(b, i, h);
+  lr.ooff = p.os.at(b, i, h);
+  const int pos = L - p.q_len + i;  // the query token's position
   lr.end = p.causal ? min(s1, pos + 1) : s1;
   lr.start = p.window > 0 ? max(pos - p.window + 1, 0) : 0;
   return lr;

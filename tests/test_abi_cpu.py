@@ -319,3 +319,59 @@ def test_metadata_pointer_rules():
     # Valid arguments reach the device check (no device here).
     assert meta_call(meta()) == b.PKD_ERR_DEVICE
     assert meta_call(meta(window=8), ss=FAKE, sp=FAKE, err=FAKE) == b.PKD_ERR_DEVICE
+
+
+# ---- contiguous_decode argument checks ----------------------------------------
+
+def cdims(**kw):
+    base = dict(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=64, max_seq_len=100, kv_dtype=b.PKD_DTYPE_BF16,
+                q_len=1, causal=0, window=0, reserved=0, q_strides=(256, 256, 64), kv_strides=(12800, 128, 64),
+                out_strides=(256, 256, 64))
+    base.update(kw)
+    arr = ctypes.c_int64 * 3
+    vals = [arr(*base[f]) if f.endswith("strides") else base[f] for f, _ in b.pkd_contig_dims._fields_]
+    return b.pkd_contig_dims(*vals)
+
+
+def ccall(cd, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, ks=None, vs=None, sinks=None, out=FAKE, lse=None, S=1, ws=None,
+          ws_bytes=0):
+    return b.contiguous_decode(cd, q, k, v, lens, ks, vs, sinks, 0.125, out, lse, S, ws, ws_bytes, None)
+
+
+def test_contig_dims_struct_layout():
+    assert ctypes.sizeof(b.pkd_contig_dims) == 10 * 4 + 9 * 8
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(max_seq_len=0), b.PKD_ERR_BAD_DIMS),
+    (dict(reserved=1), b.PKD_ERR_BAD_DIMS),
+    (dict(batch=-1), b.PKD_ERR_BAD_DIMS),
+    (dict(head_dim=48), b.PKD_ERR_HEAD_DIM),
+    (dict(num_q_heads=3), b.PKD_ERR_GQA),
+    (dict(window=-2), b.PKD_ERR_BAD_DIMS),
+    (dict(q_strides=(256, -8, 64)), b.PKD_ERR_BAD_DIMS),
+    (dict(kv_strides=(12800, 1 << 27, 64)), b.PKD_ERR_BAD_DIMS),   # 16 token rows overflow 32-bit offsets
+    (dict(q_strides=(256, 256, 68)), b.PKD_ERR_ALIGNMENT),          # q rows not 16-byte aligned
+    (dict(out_strides=(260, 256, 64)), b.PKD_ERR_ALIGNMENT),
+    (dict(kv_strides=(12800, 132, 64)), b.PKD_ERR_ALIGNMENT),
+    (dict(kv_dtype=b.PKD_DTYPE_FP8_E4M3, kv_strides=(12800, 136, 64)), b.PKD_ERR_ALIGNMENT),  # 136 B: not 16-aligned
+])
+def test_contiguous_bad_dims(kw, status):
+    cd = cdims(**kw)
+    assert ccall(cd) == status
+    assert b.contiguous_decode_workspace_bytes(cd, 3) == 0
+
+
+def test_contiguous_pointer_and_scale_rules():
+    assert ccall(None) == b.PKD_ERR_NULL_POINTER
+    for kw in ("q", "k", "v", "lens", "out"):
+        assert ccall(cdims(), **{kw: None}) == b.PKD_ERR_NULL_POINTER, kw
+    assert ccall(cdims(), ks=FAKE, vs=FAKE) == b.PKD_ERR_SCALES
+    assert ccall(cdims(kv_dtype=b.PKD_DTYPE_FP8_E4M3, kv_strides=(12800, 128, 64))) == b.PKD_ERR_SCALES
+    assert ccall(cdims(), q=FAKE + 8) == b.PKD_ERR_ALIGNMENT
+    assert ccall(cdims(), sinks=FAKE + 2) == b.PKD_ERR_ALIGNMENT
+    need = b.contiguous_decode_workspace_bytes(cdims(), 3)
+    assert need > 0
+    assert ccall(cdims(), S=3, ws=None, ws_bytes=0) == b.PKD_ERR_WORKSPACE
+    assert ccall(cdims()) == b.PKD_ERR_DEVICE  # valid arguments reach the device check
+    assert ccall(cdims(batch=0)) == b.PKD_OK

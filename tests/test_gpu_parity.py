@@ -932,3 +932,72 @@ def test_metadata_feeds_decode_bitwise(B):
             o, l = run(B, w, S, t2)
             assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), (S, bt_key)
             assert torch.equal(l, ref_l), (S, bt_key)
+
+
+# ---- contiguous K/V with stride-based addressing -------------------------------
+
+CONTIG_GPU_CASES = [
+    # (B, Hq, Hkv, D, seq_lens, q_len, causal, window, sinks, dtype, seed)
+    (4, 8, 2, 128, [1, 37, 200, 0], 1, False, 0, False, "bf16", 701),
+    (3, 16, 2, 64, [513, 17, 90], 3, True, 40, True, "bf16", 702),
+    (3, 8, 2, 128, [300, 64, 5], 2, False, 0, True, "fp8_e4m3", 703),
+    (2, 4, 4, 256, [129, 33], 4, True, 0, False, "bf16", 704),
+    (2, 8, 8, 32, [70, 1], 1, False, 16, True, "bf16", 705),
+]
+
+
+def contig_dev(w, layout, strided_out):
+    cuda = torch.device("cuda:0")
+    k, v = wl.contiguous_kv(w, layout, capacity=int(w.seq_lens.max()) + 5)
+    # Keep the views' strides on the device: move whole storages, then re-view.
+    def to_dev(x):
+        base = torch.empty(0, dtype=x.dtype).set_(x.untyped_storage()).to(cuda)
+        return base.as_strided(x.shape, x.stride(), x.storage_offset())
+    q = wl.strided_q(w.q)
+    t = dict(q=to_dev(q), k=to_dev(k), v=to_dev(v), lens=w.seq_lens.to(cuda))
+    t["ks"] = None if w.k_scale is None else w.k_scale.to(cuda)
+    t["vs"] = None if w.v_scale is None else w.v_scale.to(cuda)
+    t["sinks"] = None if w.sinks is None else w.sinks.to(cuda)
+    if strided_out:
+        buf = torch.full(w.q.shape[:-2] + (w.q.shape[-2] + 3, w.q.shape[-1]), float("nan"), dtype=torch.bfloat16,
+                         device=cuda)
+        t["out"] = buf[..., 2:2 + w.q.shape[-2], :]
+    else:
+        t["out"] = None
+    return t, k, v, q
+
+
+def run_contig(B, w, t, S):
+    out, lse = B.contiguous(t["q"], t["k"], t["v"], t["lens"], w.scale, t["ks"], t["vs"], num_splits=S,
+                            out=t["out"], causal=w.spec.causal, window=w.spec.window, sinks=t["sinks"])
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("case", CONTIG_GPU_CASES)
+@pytest.mark.parametrize("layout", ["blhd", "bhld", "blhd_padded"])
+def test_contiguous_parity(B, case, layout):
+    """Every split mode against the oracle in three K/V layouts, with a strided
+    q and (padded layout) a strided out; NaN in every element that is not a
+    sequence row, so that any stray read shows."""
+    bq, hq, hkv, d, lens, ql, causal, win, sinks, dtype, seed = case
+    w = wl.custom_workload(bq, hq, hkv, d, 16, lens, dtype, seed, q_len=ql, causal=causal, window=win, sinks=sinks)
+    t, k, v, q = contig_dev(w, layout, strided_out=layout == "blhd_padded")
+    ref = oracle.contiguous_decode(q, k, v, w.seq_lens, w.scale, causal, win, w.sinks, w.k_scale, w.v_scale)
+    for S in (1, 3, 0, BAL):
+        out, lse = run_contig(B, w, t, S)
+        check(out.contiguous(), lse, *ref, what=f"contiguous {layout} {case} S={S}")
+
+
+def test_contiguous_equals_paged_bitwise(B):
+    """Direct output and the balanced mode give the same bits on contiguous K/V
+    as on the same rows in pages (the same tokens meet in the same order)."""
+    lens = [(i * 613) % 3000 + 1 for i in range(14)] + [0, 64]
+    w = wl.custom_workload(len(lens), 32, 8, 128, 64, lens, "bf16", seed=720, window=900, sinks=True)
+    tp = dev(w)
+    t, _, _, _ = contig_dev(w, "bhld", strided_out=True)
+    for S in (1, BAL):
+        po, pl = run(B, w, S, tp)
+        co, cl = run_contig(B, w, t, S)
+        assert torch.equal(co.contiguous().view(torch.int16), po.view(torch.int16)), S
+        assert torch.equal(cl, pl), S
