@@ -343,13 +343,18 @@ def cpu_baseline(w, nbytes):
             "seconds": dt, "passes": passes, "queries_per_s": w.spec.batch / dt}
 
 
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_decode_amd", "csrc", "split_kv_decode.hip")
+# The sources the partition kernels are built from (their digest tags the counter summaries).
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_decode_amd", "csrc", f) for f in
+               ("decode_kernels.hpp", "wave_attn.hpp", "merge_row.hpp", "pkd_internal.hpp", "decode_d128.hip")]
 CALIB_BYTES = 1 << 30  # the 1 GiB device-to-device copy made at start-up
 
 
 def _source_digest():
     import hashlib
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def _short_kernel(name):

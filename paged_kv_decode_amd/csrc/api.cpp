@@ -173,6 +173,7 @@ struct Layout {
   pkd::RowStrides qs, os;
   pkd::KvLayout kv;
   bool dense_out;  // os is the dense [B][q_len][Hq][D] layout
+  bool strided;    // not the paged_decode layouts: run the kernels that read the strides
 };
 
 int64_t kv_elem_bytes(const pkd_dims& d) { return d.kv_dtype == PKD_DTYPE_FP8_E4M3 ? 1 : 2; }
@@ -186,6 +187,7 @@ Layout paged_layout(const pkd_dims& d) {
   L.kv.tok_stride = (int32_t)(d.num_kv_heads * L.kv.head_stride);
   L.kv.page_stride = (int64_t)d.page_size * L.kv.tok_stride;
   L.dense_out = true;
+  L.strided = false;
   return L;
 }
 
@@ -196,6 +198,7 @@ pkd::SplitParams make_split_params(const pkd_dims& d, const Layout& lay, const v
   p.qs = lay.qs;
   p.os = lay.os;
   p.kv = lay.kv;
+  p.strided = lay.strided ? 1 : 0;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint8_t*>(k);
   p.v = static_cast<const uint8_t*>(v);
@@ -246,8 +249,8 @@ int32_t check_out_ws(const void* out, const float* lse, const void* ws) {
 int32_t launch_partition(const pkd_dims& d, const pkd::SplitParams& p, bool direct, hipStream_t s) {
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
   const bool paged16 = d.page_size % 16 == 0;
-  const hipError_t e = pkd::launch_split_kv(p, d.batch, d.head_dim,
-                                            d.kv_dtype == PKD_DTYPE_FP8_E4M3, direct, paged16, s);
+  const hipError_t e = pkd::launch_split_kv(p, d.batch, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, direct,
+                                            paged16, p.strided != 0, s);
   return e == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
 }
 
@@ -343,6 +346,7 @@ pkd::BalancedParams make_balanced_params(const pkd_dims& d, const Layout& lay, c
   b.qs = lay.qs;
   b.os = lay.os;
   b.kv = lay.kv;
+  b.strided = lay.strided ? 1 : 0;
   b.q = static_cast<const uint16_t*>(q);
   b.k = static_cast<const uint8_t*>(k);
   b.v = static_cast<const uint8_t*>(v);
@@ -376,7 +380,7 @@ int32_t run_partition(const pkd_dims& d, const Layout& lay, const void* q, const
                       void* ws, const Plan& pl, hipStream_t s) {
   if (pl.balanced) {
     const pkd::BalancedParams b = make_balanced_params(d, lay, q, k, v, bt, lens, ks, vs, scale, ws, pl);
-    return pkd::launch_balanced(b, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, s) == hipSuccess
+    return pkd::launch_balanced(b, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, b.strided != 0, s) == hipSuccess
                ? PKD_OK : PKD_ERR_LAUNCH;
   }
   pkd::SplitParams p = make_split_params(d, lay, q, k, v, bt, lens, ks, vs, scale, pl.S);
@@ -443,7 +447,7 @@ int32_t decode_checked(const pkd_dims& d, const Layout& lay, const void* q, cons
     b.sinks = sinks;
     b.seg_count = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + pl.count_off);
     b.epoch = next_epoch();
-    return pkd::launch_balanced(b, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, s) == hipSuccess
+    return pkd::launch_balanced(b, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, b.strided != 0, s) == hipSuccess
                ? PKD_OK : PKD_ERR_LAUNCH;
   }
   st = run_partition(d, lay, q, k, v, bt, lens, ks, vs, scale, workspace, pl, s);
@@ -646,6 +650,7 @@ int32_t contiguous_plan(const pkd_contig_dims* c, pkd_dims* d, Layout* lay) {
   lay->kv.head_stride = c->kv_strides[2] * e;
   const Layout dense = paged_layout(*d);
   lay->dense_out = lay->os.b == dense.os.b && lay->os.i == dense.os.i && lay->os.h == dense.os.h;
+  lay->strided = true;
   return PKD_OK;
 }
 

@@ -1,0 +1,7 @@
+// Partition-kernel instances for head dimension 128 (see decode_kernels.hpp).
+#include "decode_kernels.hpp"
+
+namespace pkd {
+template hipError_t launch_split_kv_dim<128>(const SplitParams&, int, bool, bool, bool, bool, hipStream_t);
+template hipError_t launch_balanced_dim<128>(const BalancedParams&, bool, bool, hipStream_t);
+}  // namespace pkd

@@ -1,0 +1,544 @@
+// Split-KV paged decode attention for gfx950 (CDNA4): the partition kernels.
+// Included by one translation unit per head dimension (decode_d*.hip), which
+// instantiates the launchers below for its D, so the many kernel instances
+// compile in parallel.
+//
+// Work is done by waves.  A wave owns a token range of one (sequence b, KV head)
+// pair and up to 16 query heads of that KV head (GQA head packing: every K/V
+// row read from HBM serves all query heads that share the KV head), and keeps
+// its own online-softmax state for them.  Two launch shapes share that wave
+// machinery (WaveAttn below):
+//
+//  * grid kernel: one workgroup of four waves per (split j, KV head, sequence);
+//    the waves interleave the tiles of the split and combine their states in
+//    LDS at the end.  One split writes out/lse directly; several write
+//    partials for the merge kernel.
+//  * balanced kernel: a persistent grid sized to the device; every wave gets an
+//    equal share of the flattened (sequence, KV head, 16-token group) space,
+//    walks it segment by segment and writes one partial per (wave, segment)
+//    piece.  Work per wave is equal whatever the length mix, and the start-up
+//    latency chain (lengths -> block table -> first K/V) is paid once per wave
+//    rather than once per split.
+//
+// The per-tile machinery (loads, MFMA tile step, pipeline, combine) is in
+// wave_attn.hpp.
+#pragma once
+
+#include "wave_attn.hpp"
+
+namespace pkd {
+namespace {
+
+// Waves per SIMD the register allocation targets.  Two resident waves per
+// SIMD hide the load latency of one another's tiles; the compiler keeps the
+// MFMA accumulators in ordinary VGPRs to fit 256 registers.  The instances
+// that would spill at two (bf16 K/V with per-row page lookups at D = 32 or
+// 256) are left at one.  The balanced kernel runs one workgroup per compute
+// unit, so it is not constrained.
+template <int D, bool FP8, bool PAGED16>
+constexpr int waves_per_simd() {
+  if (!FP8 && !PAGED16 && (D == 32 || D == 256)) return 1;
+  return 2;
+}
+
+// ---- grid kernel ----------------------------------------------------------
+
+template <int D, bool FP8, bool PAGED16, bool DIRECT, bool STRIDED>
+__global__ void __launch_bounds__(kWaves * 64)
+    __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, FP8, PAGED16>())))
+split_kv_kernel(const SplitParams p) {
+  typedef Cfg<D, FP8> C;
+  typedef Geometry<D, FP8, STRIDED> Geo;
+  typedef TilePages<D, FP8, PAGED16> Pages;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  WaveAttn<D, FP8> A;
+  A.init_lane(tid & 63);
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y / p.head_groups;
+  const int hg = blockIdx.y - kvh * p.head_groups;
+  const int b = blockIdx.z;
+  const int S = p.num_splits;
+
+  const int L = p.seq_lens[b];
+  const int chunk = p.chunk;  // tokens per split, the same for every sequence
+  // Splits cover [lo, L): tokens below the first visible 16-token group (with
+  // a sliding window) are never read.
+  const int lo = seq_first_token(p, L, p.window);
+  const int s0 = (int)min((int64_t)lo + (int64_t)split * chunk, (int64_t)L);
+  const int s1 = (int)min((int64_t)s0 + chunk, (int64_t)L);
+  const int heads_here = min(kHeadsPerGroup, p.rows_kv - hg * kHeadsPerGroup);
+  // Row indices and out offsets of the workgroup's packed rows (query token, head).
+  __shared__ int64_t s_rows[kHeadsPerGroup];
+  __shared__ int64_t s_orow[kHeadsPerGroup];
+
+  if (s0 >= s1) {
+    // Empty split (or an empty sequence): o = 0, lse = -inf (the sink logit
+    // for a direct row with a sink).
+    for (int idx = tid; idx < heads_here * D; idx += kWaves * 64) {
+      const int hh = idx / D, d = idx - (idx / D) * D;
+      const int r = hg * kHeadsPerGroup + hh;
+      const int qi = r / p.group, h = kvh * p.group + (r - qi * p.group);
+      const int64_t row = ((int64_t)b * p.q_len + qi) * p.hq + h;
+      if constexpr (DIRECT) {
+        p.out[Geo::os(p).at(b, qi, h) + d] = 0;
+        if (d == 0 && p.lse) p.lse[row] = p.sinks ? p.sinks[(int)(row % p.hq)] : -INFINITY;
+      } else {
+        p.o_part[(row * S + split) * D + d] = 0.f;
+        if (d == 0) p.lse_part[row * S + split] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
+  const int lim = s1 - 1;
+  const int tok_stride = Geo::tok_stride(p);  // bytes between consecutive slots of a page
+  const int64_t page_stride = Geo::page_stride(p);
+  const int64_t head_off = (int64_t)kvh * Geo::head_stride(p);
+  const int ps = p.page_size;
+  // The block table is read-only for the whole launch (constant address space).
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_table + (int64_t)b * p.max_pages);
+
+  const LaneRow lr = lane_row<D, STRIDED>(p, b, kvh, hg, A.n, L, s1, p.window);
+  if (tid < kHeadsPerGroup) {  // read after the barriers below
+    s_rows[tid] = lr.row;
+    s_orow[tid] = lr.ooff;
+  }
+  A.load_q(p.q + lr.qoff, lr.valid);
+  A.qk_scale = p.qk_scale_log2;
+  if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
+  A.reset();
+
+  // The split's block-table entries are staged in LDS once (when they fit), so
+  // that per-tile page lookups are short LDS reads rather than dependent HBM
+  // reads on the path of every tile's loads.  Without a block table (contiguous
+  // K/V) sequence b is page b.
+  int32_t* sbt = reinterpret_cast<int32_t*>(smem + C::BT_OFFSET);
+  const bool contiguous = Geo::contiguous(p);
+  const int first_page = s0 / ps;
+  const int n_pages = lim / ps - first_page + 1;
+  const bool staged = !contiguous && n_pages <= C::BT_ENTRIES;
+  if (staged)
+    for (int i = tid; i < n_pages; i += kWaves * 64) sbt[i] = bt[first_page + i];
+  __syncthreads();
+  auto page_of = [&](int pidx) -> int { return contiguous ? b : staged ? sbt[pidx - first_page] : bt[pidx]; };
+
+  auto fetch = [&](int tile, Pages& P) {
+    const int tb = s0 + tile * C::TT;
+    if constexpr (PAGED16) {
+#pragma unroll
+      for (int q = 0; q < C::NGRP; ++q) P.pg[q] = page_of((min(tb + 16 * q, lim) & ~15) / ps);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::NBLK + C::NV; ++i) P.pg[i] = page_of(min(tb + A.generic_row(i), lim) / ps);
+    }
+  };
+  auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R, bool idle) {
+    const int tb = s0 + tile * C::TT;
+    if constexpr (PAGED16)
+      A.issue_paged16(p.k, p.v, tb, lim, P.pg, ps, tok_stride, page_stride, head_off, R, idle);
+    else
+      A.issue_generic(p.k, p.v, tb, lim, P.pg, ps, tok_stride, page_stride, head_off, R, idle);
+  };
+
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;  // this wave's V[TT][VS]
+  // Tiles wave, wave + 4, wave + 8, ...
+  run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, lr, vs, fetch, issue);
+
+  const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
+  auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
+    const int64_t row = s_rows[hh];
+    if constexpr (DIRECT) {
+      *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + d0) = to_bf16x4(o);
+      if (d0 == 0 && p.lse) p.lse[row] = lse_nat;
+    } else {
+      *reinterpret_cast<f32x4*>(p.o_part + (row * S + split) * D + d0) = o;
+      if (d0 == 0) p.lse_part[row * S + split] = lse_nat;
+    }
+  };
+  if (DIRECT && p.sinks)
+    wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, store,
+                       [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
+  else
+    wg_combine<D, FP8>(A, smem, wave, tid, heads_here, vsc, store, NoSink());
+}
+
+// ---- balanced persistent kernel ---------------------------------------------
+//
+// The work space is the sequence of segments s = (b * Hkv + kvh) * HG + hg
+// (HG head groups of up to 16 query rows per KV head), segment s holding the
+// n_b = ceil((L_b - lo_b) / 16) 16-token groups of sequence b, from its first
+// visible group lo_b (0 without a sliding window); T groups in all.  With
+// NWE = min(workgroups, T) active workgroups, workgroup w takes groups
+// [floor(w T / NWE), floor((w + 1) T / NWE)); its waves interleave the
+// tiles of each piece (the part of one segment inside the range) and combine
+// in LDS.  Each (workgroup, segment) piece writes its normalised partial and
+// LSE to slot w + s, which is unique and increasing along the work space; the
+// merge kernel finds segment s's pieces from the same formula.  page_size
+// must be a multiple of 16.
+
+template <int D, bool FP8, int NWV, bool STRIDED, bool WINDOW, bool SINKS>
+__global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4)))
+balanced_kernel(const BalancedParams p) {
+  typedef Cfg<D, FP8> C;
+  typedef Geometry<D, FP8, STRIDED> Geo;
+  // Without a window (the instance for window = 0) nothing of it stays live.
+  const int win = WINDOW ? p.window : 0;
+  typedef TilePages<D, FP8, true> Pages;
+  constexpr int VT_BYTES = NWV * C::TT * C::VS * 2;                 // wave-private V tiles
+  constexpr int MERGE_BYTES = NWV * 16 * (2 + C::OW_STRIDE) * 4 + 16 * (NWV + 4) * 4;  // combine staging
+  constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ int64_t spre[kBalancedMaxBatch + 1];  // spre[b] = groups of all segments of sequences < b
+  __shared__ int64_t stot[NWV];
+  __shared__ int s_last;                           // in-kernel merge: this piece completes its segment
+  __shared__ int64_t s_rows[kHeadsPerGroup];       // row indices of the current piece's packed rows
+  __shared__ int64_t s_orow[kHeadsPerGroup];       // their out offsets
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int B = p.batch;
+  const int SPB = p.hkv * p.head_groups;  // segments per sequence
+
+  // Prefix sums of the group counts (every workgroup computes them; workgroup 0
+  // also stores them for the merge kernel): thread t sums sequences 4t..4t+3,
+  // a shuffle scan runs inside each wave, and the wave totals are added across
+  // waves through LDS.
+  {
+    constexpr int PER = kBalancedMaxBatch / (NWV * 64);
+    const int lane = tid & 63;
+    int64_t run[PER];
+    int64_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int bb = tid * PER + i;
+      const int L = bb < B ? p.seq_lens[bb] : 0;
+      sum += (int64_t)((L - seq_first_token(p, L, win) + 15) >> 4) * SPB;
+      run[i] = sum;
+    }
+    int64_t incl = sum;  // inclusive scan of the thread sums within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t up = __shfl_up(incl, off);
+      if (lane >= off) incl += up;
+    }
+    if (lane == 63) stot[wave] = incl;
+    __syncthreads();
+    int64_t base = incl - sum;
+    for (int v = 0; v < wave; ++v) base += stot[v];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int bb = tid * PER + i;
+      if (bb < B) spre[bb + 1] = base + run[i];
+    }
+    if (tid == 0) spre[0] = 0;
+    __syncthreads();
+  }
+  const int64_t T = spre[B];
+  if (blockIdx.x == 0)
+    for (int i = tid; i <= B; i += NWV * 64) p.prefix[i] = spre[i];
+  const int64_t nwe = min((int64_t)p.num_workers, T);
+  const int64_t w = blockIdx.x;
+  if (p.fused) {
+    // Sequences of length 0 have no piece: out = 0, lse = -inf (or the head's
+    // sink logit) for all their q_len * Hq rows (workgroup bb % W).
+    const int rows_seq = p.q_len * p.hq;
+    for (int bb = (int)w; bb < B; bb += p.num_workers) {
+      if (spre[bb + 1] != spre[bb]) continue;
+      for (int i = tid; i < rows_seq * D; i += NWV * 64) {
+        const int rr = i / D, qi = rr / p.hq;
+        p.out[Geo::os(p).at(bb, qi, rr - qi * p.hq) + (i - rr * D)] = 0;
+      }
+      if (p.lse)
+        for (int i = tid; i < rows_seq; i += NWV * 64)
+          p.lse[(int64_t)bb * rows_seq + i] = SINKS ? p.sinks[i % p.hq] : -INFINITY;
+    }
+  }
+  if (w >= nwe) return;  // the whole workgroup leaves together
+
+  int64_t pos = w * T / nwe;
+  const int64_t hi = (w + 1) * T / nwe;
+
+  // The sequence holding group pos: spre[b] <= pos < spre[b + 1].
+  int b = 0;
+  {
+    int lo_b = 0, hi_b = B;
+    while (hi_b - lo_b > 1) {
+      const int mid = (lo_b + hi_b) >> 1;
+      if (spre[mid] <= pos) lo_b = mid; else hi_b = mid;
+    }
+    b = lo_b;
+  }
+  int64_t nb = (spre[b + 1] - spre[b]) / SPB;  // groups per segment of sequence b
+  int seg = (int)((pos - spre[b]) / nb);
+  int grp = (int)((pos - spre[b]) - (int64_t)seg * nb);
+
+  WaveAttn<D, FP8> A;
+  A.init_lane(tid & 63);
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;
+  const int ps = p.page_size;
+  const int tok_stride = Geo::tok_stride(p);
+  const int64_t page_stride = Geo::page_stride(p);
+
+  // Page window of a piece: lane j holds block-table entry first_page + j of
+  // sequence bb (entries past the row are not read; entries past the pieces's
+  // last page are never used).  The next piece's window is loaded while the
+  // current piece runs.  Without a block table (contiguous K/V) sequence bb is
+  // page bb, its only page.
+  auto load_window = [&](int bb, int first_page) -> int {
+    if (Geo::contiguous(p)) return bb;
+    const int idx = first_page + A.lane;
+    return idx < p.max_pages ? p.block_table[(int64_t)bb * p.max_pages + idx] : 0;
+  };
+  // First visible token (16-aligned) of a sequence: where its groups start.
+  auto first_of = [&](int bb) -> int { return WINDOW ? seq_first_token(p, p.seq_lens[bb], win) : 0; };
+  int lo = first_of(b);
+  int window = load_window(b, (lo + grp * 16) / ps);
+
+  while (pos < hi) {
+    const int gend = (int)min(nb, (int64_t)grp + (hi - pos));
+    const int L = p.seq_lens[b];
+    const int s0 = lo + grp * 16;
+    const int s1 = min(lo + gend * 16, L);
+    const int lim = s1 - 1;
+    const int kvh = seg / p.head_groups;
+    const int hg = seg - kvh * p.head_groups;
+    const int heads_here = min(kHeadsPerGroup, p.rows_kv - hg * kHeadsPerGroup);
+    const LaneRow lr = lane_row<D, STRIDED>(p, b, kvh, hg, A.n, L, s1, win);
+    if (tid < kHeadsPerGroup) {  // read after the combine's barriers
+      s_rows[tid] = lr.row;
+      s_orow[tid] = lr.ooff;
+    }
+    const int64_t head_off = (int64_t)kvh * Geo::head_stride(p);
+
+    // The next piece: the following segment (of this or a later sequence).
+    const int64_t npos = pos + (gend - grp);
+    int nseg = seg + 1, nbq = b;
+    if (nseg == SPB) {
+      nseg = 0;
+      do { ++nbq; } while (nbq < B && spre[nbq + 1] == spre[nbq]);
+    }
+    const int nlo = npos < hi ? (nbq == b ? lo : first_of(nbq)) : 0;
+    const int next_window = npos < hi ? load_window(nbq, nlo / ps) : 0;
+
+    A.load_q(p.q + lr.qoff, lr.valid);
+    A.qk_scale = p.qk_scale_log2;
+    if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
+    A.reset();
+
+    const int first_page = s0 / ps;
+    const __attribute__((address_space(4))) int32_t* btc =
+        (const __attribute__((address_space(4))) int32_t*)(p.block_table + (int64_t)b * p.max_pages);
+    auto page_of = [&](int pidx) -> int {
+      const int rel = pidx - first_page;
+      return rel < 64 ? __builtin_amdgcn_readlane(window, rel) : btc[pidx];
+    };
+    auto fetch = [&](int tile, Pages& P) {
+      const int tb = s0 + tile * C::TT;
+#pragma unroll
+      for (int q = 0; q < C::NGRP; ++q) P.pg[q] = page_of((min(tb + 16 * q, lim) & ~15) / ps);
+    };
+    auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R, bool idle) {
+      A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, page_stride, head_off, R, idle);
+    };
+    const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
+    run_tiles<D, FP8, Pages>(A, wave, NWV, ntiles, s0, lr, vs, fetch, issue);
+
+    // This segment's pieces are those of workgroups w_first .. w_last, at
+    // slots w + s (s = b * SPB + seg).
+    const int64_t sidx = (int64_t)b * SPB + seg;
+    const int64_t seg_pos = spre[b] + (int64_t)seg * nb;
+    const int64_t w_first = ((seg_pos + 1) * nwe - 1) / T;
+    const int npieces = (int)(((seg_pos + nb) * nwe - 1) / T - w_first + 1);
+    const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
+    if (p.fused && npieces == 1) {
+      // The whole segment is this piece: write the result directly.
+      auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
+        const int64_t row = s_rows[hh];
+        *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + d0) = to_bf16x4(o);
+        if (d0 == 0 && p.lse) p.lse[row] = lse_nat;
+      };
+      if constexpr (SINKS)
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, store,
+                                [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
+      else
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, store, NoSink());
+      __syncthreads();  // the LDS is reused by the next piece
+    } else {
+      // This piece's partial, for the group's heads.
+      const int64_t slot = w + sidx;
+      float* orow = p.o_part + slot * p.hpg * D;
+      float* lrow = p.lse_part + slot * p.hpg;
+      if (!p.fused) {
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
+          *reinterpret_cast<f32x4*>(orow + hh * D + d0) = o;
+          if (d0 == 0) lrow[hh] = lse_nat;
+        }, NoSink());
+      } else {
+        // Agent-scope stores write through to the coherent copy that another
+        // XCD's workgroup will read; waiting for their acknowledgement before the
+        // count makes the partial visible to whichever piece merges.  (A release
+        // fence would write back this XCD's whole L2, far too costly per piece.)
+        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(orow + hh * D + d0 + i, o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (d0 == 0) __hip_atomic_store(lrow + hh, lse_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }, NoSink());
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are acknowledged
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // Count this piece in; the last of the segment's pieces merges them.
+        __syncthreads();
+        if (tid == 0) {
+          const uint64_t E = p.epoch;
+          uint64_t* cw = p.seg_count + sidx;
+          uint64_t old = __hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          uint64_t nv;
+          do {
+            nv = ((old >> 24) == E ? old : (E << 24)) + 1;
+          } while (!__hip_atomic_compare_exchange_weak(cw, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+          const bool last = (int)(nv & 0xFFFFFF) == npieces;
+          if (last) __hip_atomic_store(cw, E << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_last = last;
+        }
+        __syncthreads();
+        const bool last = s_last != 0;
+        if (last) {
+          // The pieces' partials, read from the coherent copy.  Wave w merges
+          // rows w, w + NWV, ...  With few pieces the loads of RC rows at a
+          // time are issued before any of them is combined (RC rows of staged
+          // partials take at most 64 registers with one wave per SIMD, 32 with
+          // two); otherwise, or when only one row fits, one row at a time.
+          const int64_t slot0 = w_first + sidx;
+          typedef RowMerge<D, true> RM;
+          constexpr int MAXR = kHeadsPerGroup / NWV;
+          constexpr int RC_REG = (NWV > 4 ? 32 : 64) / (RM::UNROLL * RM::EPL);
+          constexpr int RC = RC_REG < MAXR ? RC_REG : MAXR;
+          const float* lp0 = p.lse_part + slot0 * p.hpg;
+          const float* op0 = p.o_part + slot0 * p.hpg * D;
+          const int64_t ls = p.hpg, os = (int64_t)p.hpg * D;
+          const int lane = tid & 63;
+          if (RC < 2 || npieces > RM::UNROLL) {
+            for (int hh = wave; hh < heads_here; hh += NWV) {
+              RM r;
+              r.run(lp0 + hh, ls, op0 + hh * D, os, npieces, lane);
+              const int64_t row = s_rows[hh];
+              r.store(p.out + s_orow[hh], p.lse ? p.lse + row : nullptr, lane,
+                      SINKS ? p.sinks[(int)(row % p.hq)] : -INFINITY);
+            }
+          } else {
+            constexpr int RCS = RC < 2 ? 2 : RC;  // (the branch above takes RC < 2)
+#pragma unroll
+            for (int k0 = 0; k0 < MAXR; k0 += RCS) {
+              typename RM::Staged st[RCS];
+#pragma unroll
+              for (int k = 0; k < RCS; ++k) {
+                const int hh = wave + (k0 + k) * NWV;
+                if (hh < heads_here) RM::issue(lp0 + hh, ls, op0 + hh * D, os, npieces, lane, st[k]);
+              }
+#pragma unroll
+              for (int k = 0; k < RCS; ++k) {
+                const int hh = wave + (k0 + k) * NWV;
+                if (hh < heads_here) {
+                  RM r;
+                  r.finish(st[k], npieces, lane);
+                  const int64_t row = s_rows[hh];
+                  r.store(p.out + s_orow[hh], p.lse ? p.lse + row : nullptr, lane,
+                          SINKS ? p.sinks[(int)(row % p.hq)] : -INFINITY);
+                }
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();  // the LDS is reused by the next piece
+    }
+
+    pos = npos;
+    grp = 0;
+    seg = nseg;
+    if (nbq != b) {
+      b = nbq;
+      lo = nlo;
+      if (b < B) nb = (spre[b + 1] - spre[b]) / SPB;
+    }
+    window = next_window;
+  }
+}
+
+template <int D, bool FP8, bool PAGED16, bool DIRECT>
+hipError_t launch_t(const SplitParams& p, int batch, bool strided, hipStream_t stream) {
+  const dim3 grid(DIRECT ? 1 : p.num_splits, p.hkv * p.head_groups, batch);
+  if (strided)
+    hipLaunchKernelGGL((split_kv_kernel<D, FP8, PAGED16, DIRECT, true>), grid, dim3(kWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((split_kv_kernel<D, FP8, PAGED16, DIRECT, false>), grid, dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch_d(const SplitParams& p, int batch, bool direct, bool paged16, bool strided, hipStream_t s) {
+  if (paged16)
+    return direct ? launch_t<D, FP8, true, true>(p, batch, strided, s) : launch_t<D, FP8, true, false>(p, batch, strided, s);
+  return direct ? launch_t<D, FP8, false, true>(p, batch, strided, s) : launch_t<D, FP8, false, false>(p, batch, strided, s);
+}
+
+
+// Waves per balanced workgroup: four (one per SIMD) for bf16 K/V; eight for
+// FP8, whose tiles carry half the bytes, so that as many bytes are in flight
+// per compute unit (measured: 3% faster for FP8, 4-20% slower for bf16).
+constexpr int balanced_waves(bool fp8) { return fp8 ? 8 : 4; }
+
+// Instances without a window or without sinks keep none of their state live
+// (the kernel is at the edge of its scalar registers).
+template <int D, bool FP8, bool STRIDED, bool WINDOW>
+void launch_bw(const BalancedParams& p, hipStream_t stream) {
+  constexpr int NWV = balanced_waves(FP8);
+  if (p.sinks)
+    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, true>), dim3(p.num_workers), dim3(NWV * 64),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, false>), dim3(p.num_workers), dim3(NWV * 64),
+                       0, stream, p);
+}
+
+template <int D, bool FP8, bool STRIDED>
+void launch_bs(const BalancedParams& p, hipStream_t stream) {
+  if (p.window > 0)
+    launch_bw<D, FP8, STRIDED, true>(p, stream);
+  else
+    launch_bw<D, FP8, STRIDED, false>(p, stream);
+}
+
+template <int D, bool FP8>
+hipError_t launch_b(const BalancedParams& p, bool strided, hipStream_t stream) {
+  if (strided)
+    launch_bs<D, FP8, true>(p, stream);
+  else
+    launch_bs<D, FP8, false>(p, stream);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The launchers for one head dimension (explicitly instantiated per D).
+template <int D>
+hipError_t launch_split_kv_dim(const SplitParams& p, int batch, bool fp8, bool direct, bool paged16, bool strided,
+                               hipStream_t stream) {
+  return fp8 ? launch_d<D, true>(p, batch, direct, paged16, strided, stream)
+             : launch_d<D, false>(p, batch, direct, paged16, strided, stream);
+}
+
+template <int D>
+hipError_t launch_balanced_dim(const BalancedParams& p, bool fp8, bool strided, hipStream_t stream) {
+  return fp8 ? launch_b<D, true>(p, strided, stream) : launch_b<D, false>(p, strided, stream);
+}
+
+}  // namespace pkd

@@ -55,6 +55,7 @@ struct SplitParams {
                                // splits start at the sequence's first visible 16-token group
   RowStrides qs, os;
   KvLayout kv;
+  int32_t strided;             // 1: qs, os, kv and a null block table are honoured (host picks the kernel)
 };
 
 // Arguments of the balanced persistent partition kernel.
@@ -89,6 +90,7 @@ struct BalancedParams {
   uint64_t epoch;              // distinct per call, 1 .. 2^40 - 1 (fused)
   RowStrides qs, os;           // as in SplitParams
   KvLayout kv;
+  int32_t strided;
 };
 
 // True when the balanced mode merges inside the partition kernel: when there
@@ -159,9 +161,11 @@ constexpr int kHeadsPerGroup = 16;   // query heads packed into one MFMA N dimen
 constexpr int kBalancedMaxBatch = 1024;  // largest batch the balanced kernel's prefix scan takes
 
 // Launchers (defined in the .hip files).  head_dim in {32, 64, 128, 256}.
+// strided: take the q/out strides and the K/V layout from the parameters (and
+// allow a null block table); otherwise the dense q/out and paged cache layouts.
 hipError_t launch_split_kv(const SplitParams& p, int batch, int head_dim, bool fp8, bool direct,
-                           bool paged16, hipStream_t stream);
-hipError_t launch_balanced(const BalancedParams& p, int head_dim, bool fp8, hipStream_t stream);
+                           bool paged16, bool strided, hipStream_t stream);
+hipError_t launch_balanced(const BalancedParams& p, int head_dim, bool fp8, bool strided, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool fp8, hipStream_t stream);
 hipError_t launch_decode_metadata(const MetaParams& p, hipStream_t stream);

@@ -315,7 +315,9 @@ struct WaveAttn {
 
   // One tile: V to LDS, QK^T, online softmax, PV.  Tokens before s_lo or at or
   // past s1 (this lane's packed row's window start and end) are masked.
-  __device__ __forceinline__ void process(const Regs& R, int tb, int s_lo, int s1, uint16_t* vs) {
+  // lo_all (uniform) is at least every lane's s_lo: tiles starting there or
+  // later skip the lower-bound test.
+  __device__ __forceinline__ void process(const Regs& R, int tb, int s_lo, int s1, int lo_all, uint16_t* vs) {
     // V -> LDS, row-major bf16 (16-byte writes).
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
@@ -358,15 +360,27 @@ struct WaveAttn {
     // Online softmax (base 2).  Lane (n, g) holds scores of head n for tokens
     // s_out_token(blk, g, i).
     float mt = -INFINITY;
+    if (tb >= lo_all) {
 #pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk)
+      for (int blk = 0; blk < C::NBLK; ++blk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = tb + s_out_token<C::KP>(blk, g, i);
-        const float x = sacc[blk][i] * qk_scale;
-        sacc[blk][i] = (tok < s1 && tok >= s_lo) ? x : -INFINITY;
-        mt = fmaxf(mt, sacc[blk][i]);
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int tok = tb + s_out_token<C::KP>(blk, g, i);
+          const float x = sacc[blk][i] * qk_scale;
+          sacc[blk][i] = tok < s1 ? x : -INFINITY;
+          mt = fmaxf(mt, sacc[blk][i]);
+        }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < C::NBLK; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = tb + s_out_token<C::KP>(blk, g, i);
+          const float x = sacc[blk][i] * qk_scale;
+          sacc[blk][i] = (tok < s1 && tok >= s_lo) ? x : -INFINITY;
+          mt = fmaxf(mt, sacc[blk][i]);
+        }
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
@@ -450,32 +464,78 @@ struct LaneRow {
   int64_t row;
   int64_t qoff, ooff;
   bool valid;
-  int start;  // first position the row sees (its sliding window's lower end; 0 without a window)
+  int start;      // first position the row sees (its sliding window's lower end; 0 without a window)
   int end;
+  int start_max;  // uniform: no row of the sequence starts later (L - window, or 0)
 };
-template <typename P>
-__device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, int n, int L, int s1) {
+template <int D, bool STRIDED, typename P>
+__device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, int n, int L, int s1, int window) {
   const int r = hg * kHeadsPerGroup + n;
   LaneRow lr;
   lr.valid = r < p.rows_kv;
   const int rr = lr.valid ? r : hg * kHeadsPerGroup;
   const int i = rr / p.group, h = kvh * p.group + (rr - i * p.group);
   lr.row = ((int64_t)b * p.q_len + i) * p.hq + h;
-  lr.qoff = p.qs.at(b, i, h);
-  lr.ooff = p.os.at(b, i, h);
+  if constexpr (STRIDED) {
+    lr.qoff = p.qs.at(b, i, h);
+    lr.ooff = p.os.at(b, i, h);
+  } else {
+    lr.qoff = lr.ooff = lr.row * D;
+  }
   const int pos = L - p.q_len + i;  // the query token's position
   lr.end = p.causal ? min(s1, pos + 1) : s1;
-  lr.start = p.window > 0 ? max(pos - p.window + 1, 0) : 0;
+  lr.start = window > 0 ? max(pos - window + 1, 0) : 0;
+  lr.start_max = window > 0 ? max(L - window, 0) : 0;
   return lr;
 }
+
+// Where q/out rows and K/V rows are.  STRIDED: the strides the host passed
+// (contiguous K/V, strided q / out).  Otherwise the dense q/out layout and the
+// paged [P][ps][Hkv][D] cache, derived from the shape, so that the paged
+// kernels keep no stride parameters in scalar registers.
+template <int D, bool FP8, bool STRIDED>
+struct Geometry {
+  typedef Cfg<D, FP8> C;
+  template <typename P>
+  static __device__ __forceinline__ RowStrides qs(const P& p) {
+    if constexpr (STRIDED) return p.qs;
+    else return RowStrides{(int64_t)p.q_len * p.hq * D, (int64_t)p.hq * D, D};
+  }
+  template <typename P>
+  static __device__ __forceinline__ RowStrides os(const P& p) {
+    if constexpr (STRIDED) return p.os;
+    else return RowStrides{(int64_t)p.q_len * p.hq * D, (int64_t)p.hq * D, D};
+  }
+  template <typename P>
+  static __device__ __forceinline__ int tok_stride(const P& p) {
+    if constexpr (STRIDED) return p.kv.tok_stride;
+    else return p.hkv * C::ROWB;
+  }
+  template <typename P>
+  static __device__ __forceinline__ int64_t page_stride(const P& p) {
+    if constexpr (STRIDED) return p.kv.page_stride;
+    else return (int64_t)p.page_size * (p.hkv * C::ROWB);
+  }
+  template <typename P>
+  static __device__ __forceinline__ int64_t head_stride(const P& p) {
+    if constexpr (STRIDED) return p.kv.head_stride;
+    else return C::ROWB;
+  }
+  // No block table: sequence b is page b (contiguous K/V).
+  template <typename P>
+  static __device__ __forceinline__ bool contiguous(const P& p) {
+    if constexpr (STRIDED) return p.block_table == nullptr;
+    else return false;
+  }
+};
 
 // First token of sequence b that any of its query tokens sees, rounded down to
 // a multiple of 16 (tiles start on 16-token groups): the lowest window start
 // when there is a window, else 0.  Tokens below it are never read.
 template <typename P>
-__device__ __forceinline__ int seq_first_token(const P& p, int L) {
-  if (p.window <= 0) return 0;
-  return max(L - p.q_len - p.window + 1, 0) & ~15;
+__device__ __forceinline__ int seq_first_token(const P& p, int L, int window) {
+  if (window <= 0) return 0;
+  return max(L - p.q_len - window + 1, 0) & ~15;
 }
 
 // Tiles first, first + step, ... (< ntiles): while tile t is processed the
@@ -486,7 +546,7 @@ __device__ __forceinline__ int seq_first_token(const P& p, int L) {
 // never consumed.
 template <int D, bool FP8, typename Pages, typename Fetch, typename Issue>
 __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int step, int ntiles, int s0,
-                                          int s_lo, int s1, uint16_t* vs, Fetch fetch, Issue issue) {
+                                          const LaneRow& lr, uint16_t* vs, Fetch fetch, Issue issue) {
   typedef Cfg<D, FP8> C;
   if (first >= ntiles) return;
   auto nxt = [&](int t) { return t + step < ntiles ? t + step : t; };
@@ -502,7 +562,7 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
     int t2 = nxt(t1);
     fetch(t2, pa);
     __builtin_amdgcn_sched_barrier(0);
-    A.process(ra, s0 + t * C::TT, s_lo, s1, vs);
+    A.process(ra, s0 + t * C::TT, lr.start, lr.end, lr.start_max, vs);
     if (t1 == t) break;
     t = t1;
     t1 = t2;
@@ -510,7 +570,7 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
     t2 = nxt(t1);
     fetch(t2, pb);
     __builtin_amdgcn_sched_barrier(0);
-    A.process(rb, s0 + t * C::TT, s_lo, s1, vs);
+    A.process(rb, s0 + t * C::TT, lr.start, lr.end, lr.start_max, vs);
     if (t1 == t) break;
     t = t1;
     t1 = t2;
