@@ -1001,3 +1001,99 @@ def test_contiguous_equals_paged_bitwise(B):
         co, cl = run_contig(B, w, t, S)
         assert torch.equal(co.contiguous().view(torch.int16), po.view(torch.int16)), S
         assert torch.equal(cl, pl), S
+
+
+# ---- HIP graph capture of the other entry points -------------------------------
+
+def _capture(fn):
+    """Capture fn() into a HIP graph on a side stream; returns the graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("S", [BAL, 1, 3])
+def test_graph_replays_window_sinks_and_contiguous(B, S):
+    """Captured window/sink decodes (paged) and contiguous decodes replay several
+    times, with eager work between, bitwise equal to the eager calls."""
+    lens = [(i * 613) % 3000 + 1 for i in range(30)] + [0, 64]
+    w = wl.custom_workload(len(lens), 32, 8, 128, 64, lens, "bf16", seed=740, window=500, sinks=True)
+    t = dev(w)
+    eager_o, eager_l = run(B, w, S, t)
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+    dims = B.dims_for(t["q"], t["k"], t["bt"], window=500)
+    nbytes = B.paged_decode_workspace_bytes(dims, S)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    tc, _, _, _ = contig_dev(w, "bhld", strided_out=True)
+    co_eager, cl_eager = run_contig(B, w, tc, S)
+    cd = B.contig_dims_for(tc["q"], tc["k"], tc["out"], window=500)
+    cbytes = B.contiguous_decode_workspace_bytes(cd, S)
+    cws = torch.empty(max(cbytes, 1), dtype=torch.uint8, device="cuda")
+    clse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+    st = []
+
+    def body():
+        h = B.current_stream_handle(0)
+        st.append(B.paged_decode(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, t["sinks"], w.scale,
+                                 out, lse, S, ws if nbytes else None, nbytes, h))
+        st.append(B.contiguous_decode(cd, tc["q"], tc["k"], tc["v"], tc["lens"], None, None, tc["sinks"], w.scale,
+                                      tc["out"], clse, S, cws if cbytes else None, cbytes, h))
+    g = _capture(body)
+    assert st == [0, 0]
+    for i in range(4):
+        out.fill_(0)
+        lse.fill_(0)
+        tc["out"].fill_(0)
+        clse.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu().view(torch.int16), eager_o.view(torch.int16)), f"replay {i}"
+        assert torch.equal(lse.cpu(), eager_l), f"replay {i}"
+        assert torch.equal(tc["out"].cpu().contiguous().view(torch.int16), co_eager.contiguous().view(torch.int16))
+        assert torch.equal(clse.cpu(), cl_eager), f"replay {i}"
+
+
+def test_graph_replays_append_and_metadata(B):
+    """A captured append (FP8, RoPE) and metadata preparation replay several
+    times onto reset buffers, bitwise equal to the oracle each time."""
+    aw = wl.append_workload(300, 8, 128, 64, 16, "fp8_e4m3", rope=True, seed=750, pad_every=7)
+    ref_k, ref_v = oracle.kv_append(aw.k_new, aw.v_new, aw.slot_mapping, aw.k_cache, aw.v_cache, aw.k_scale,
+                                    aw.v_scale, aw.positions, aw.cos_sin)
+    t = _dev_append(aw)
+    k0, v0 = t["k_cache"].clone(), t["v_cache"].clone()
+    rng = np.random.default_rng(751)
+    lens = rng.integers(0, 16 * 64, size=40)
+    bt = rng.integers(0, 5000, size=(40, 16)).astype(np.int32)
+    rt, rows = token_map(bt, lens, 64, 50, 16 * 64, seed=752)
+    ref_m, bad = oracle.decode_metadata(rt, rows, lens.astype(np.int64), 64, 16, window=100)
+    cuda = torch.device("cuda:0")
+    rt_d, rows_d = torch.from_numpy(rt).to(cuda), torch.from_numpy(rows).to(cuda)
+    lens_d = torch.from_numpy(lens.astype(np.int64)).to(cuda)
+    m_out = {}
+
+    def body():
+        B.append(**t)
+        m_out.update(B.metadata(rt_d, rows_d, lens_d, 64, 16, window=100))
+    g = _capture(body)
+    for i in range(3):
+        t["k_cache"].copy_(k0)
+        t["v_cache"].copy_(v0)
+        for v in m_out.values():
+            v.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_k, got_v = wl.as_numpy_bits(t["k_cache"].cpu()), wl.as_numpy_bits(t["v_cache"].cpu())
+        assert np.array_equal(got_k, ref_k.reshape(got_k.shape)), f"replay {i}: K"
+        assert np.array_equal(got_v, ref_v.reshape(got_v.shape)), f"replay {i}: V"
+        for k, v in ref_m.items():
+            assert np.array_equal(m_out[k].cpu().numpy(), v), f"replay {i}: {k}"
+        assert int(m_out["error_count"].cpu()[0]) == bad
