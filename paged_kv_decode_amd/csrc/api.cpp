@@ -347,6 +347,9 @@ pkd::BalancedParams make_balanced_params(const pkd_dims& d, const Layout& lay, c
   b.os = lay.os;
   b.kv = lay.kv;
   b.strided = lay.strided ? 1 : 0;
+  // Head rows shorter than a 128-byte line put several KV heads in each line;
+  // those heads' workgroups are kept on one XCD so each line is fetched once.
+  b.xcd_ranges = !lay.strided && lay.kv.head_stride < 128 && d.num_kv_heads > 1 ? 1 : 0;
   b.q = static_cast<const uint16_t*>(q);
   b.k = static_cast<const uint8_t*>(k);
   b.v = static_cast<const uint8_t*>(v);

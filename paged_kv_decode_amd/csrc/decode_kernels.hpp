@@ -243,7 +243,16 @@ balanced_kernel(const BalancedParams p) {
   if (blockIdx.x == 0)
     for (int i = tid; i <= B; i += NWV * 64) p.prefix[i] = spre[i];
   const int64_t nwe = min((int64_t)p.num_workers, T);
-  const int64_t w = blockIdx.x;
+  // Workgroups are dealt to the XCDs round-robin (workgroup i runs on XCD
+  // i % kXcds).  With xcd_ranges, and every worker busy, worker ranges are
+  // assigned so that each XCD takes one contiguous 1/kXcds of the work space:
+  // the KV heads of a sequence then stream the same tokens on the same XCD, so
+  // that heads whose rows share 128-byte lines fetch each line from HBM once
+  // and find it in that XCD's L2 for the other head.
+  const int N = p.num_workers;
+  const int64_t w = (p.xcd_ranges && T >= N && N % kXcds == 0)
+                        ? (int64_t)(blockIdx.x % kXcds) * (N / kXcds) + blockIdx.x / kXcds
+                        : (int64_t)blockIdx.x;
   if (p.fused) {
     // Sequences of length 0 have no piece: out = 0, lse = -inf (or the head's
     // sink logit) for all their q_len * Hq rows (workgroup bb % W).

@@ -91,6 +91,7 @@ struct BalancedParams {
   RowStrides qs, os;           // as in SplitParams
   KvLayout kv;
   int32_t strided;
+  int32_t xcd_ranges;          // give each XCD a contiguous part of the work space (heads sharing cache lines)
 };
 
 // True when the balanced mode merges inside the partition kernel: when there
@@ -159,6 +160,7 @@ constexpr int kWaves = 4;            // waves per split-kernel workgroup
 constexpr int kSplitAlign = 64;      // tokens; split boundaries are multiples of this
 constexpr int kHeadsPerGroup = 16;   // query heads packed into one MFMA N dimension
 constexpr int kBalancedMaxBatch = 1024;  // largest batch the balanced kernel's prefix scan takes
+constexpr int kXcds = 8;                 // accelerator complex dies of an MI355X (gfx950), each with its own L2
 
 // Launchers (defined in the .hip files).  head_dim in {32, 64, 128, 256}.
 // strided: take the q/out strides and the K/V layout from the parameters (and
