@@ -231,11 +231,14 @@ int32_t paged_decode_launches(const pkd_dims* dims, int32_t num_splits);
  * (PKD_SPLITS_AUTO: the heuristic's choice): 0 for one split; for S splits the
  * fp32 partials [B][q_len][Hq][S][D] and [B][q_len][Hq][S]; for
  * PKD_SPLITS_BALANCED, with R = q_len * G query rows per KV head, the fp32
- * partials of (W + B*Hkv*ceil(R/16)) slots of min(R,16) rows, W the
- * workgroups of the device-sized grid (one per compute unit), B+1 int64 prefix
- * sums and B*Hkv*ceil(R/16) uint64 merge counters; each part rounded up to 256
- * bytes.  Returns 0 for invalid dims or an unsupported num_splits.  The
- * counters carry a per-call tag, so the workspace never needs initialising.
+ * partials of D floats per row in (W + B*Hkv*ceil(R/16)) slots of min(R,16)
+ * rows, W the workgroups of the device-sized grid (one per compute unit), B+1
+ * int64 prefix sums, and B*Hkv*ceil(R/16) uint64 merge counters;
+ * each part rounded up to 256 bytes.  When KV heads are read in pairs (head
+ * rows under 128 bytes, no window, 2R <= 16: two heads sharing each cache line
+ * are read together), Hkv counts pairs and R doubles.  Returns 0 for invalid
+ * dims or an unsupported num_splits.  The counters carry a per-call tag, so
+ * the workspace never needs initialising.
  */
 size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits);
 

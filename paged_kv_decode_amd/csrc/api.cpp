@@ -83,13 +83,40 @@ bool balanced_ok(const pkd_dims& d) {
   return T < ((int64_t)1 << 46);
 }
 
-// Balanced workspace: partials [slots][hpg][D] fp32, LSEs [slots][hpg] fp32,
-// prefix sums [B + 1] int64, then one in-kernel-merge counter per segment
-// [B * Hkv * head_groups] uint64 (its contents never need initialising).
-size_t balanced_bytes(const pkd_dims& d, size_t* lse_offset, size_t* prefix_offset, size_t* count_offset) {
-  const size_t segments = (size_t)d.batch * d.num_kv_heads * head_groups(d);
-  const size_t slots = (size_t)balanced_workers(d) + segments;
-  const size_t hpg = (size_t)heads_per_slot(d);
+// KV heads the balanced kernel reads as one: 2 when adjacent heads of the paged
+// layout share 128-byte lines (head rows of fewer than 128 bytes), the pair's
+// query rows still fit one 16-row group and the pair's width has a kernel
+// instance (64 or 128); else 1.  A pair is then one wide head (see the
+// kernel), so that each line is fetched once.  Not with a window or strided
+// (contiguous) K/V.  A function of the shape alone, so workspace sizes agree.
+int pair_heads(const pkd_dims& d, bool strided) {
+  if (strided || d.window != 0) return 1;
+  const int e = d.kv_dtype == PKD_DTYPE_FP8_E4M3 ? 1 : 2;
+  if (d.head_dim * e >= 128 || d.num_kv_heads % 2 != 0) return 1;
+  if (2 * rows_per_kv(d) > pkd::kHeadsPerGroup) return 1;
+  if (2 * d.head_dim != 64 && 2 * d.head_dim != 128) return 1;
+  return 2;
+}
+
+// The problem as the balanced kernel's work space sees it: pair KV heads of
+// head_dim D become one KV head of pair * D dims.
+pkd_dims balanced_view(const pkd_dims& d, int pair) {
+  pkd_dims v = d;
+  v.num_kv_heads /= pair;
+  v.head_dim *= pair;
+  return v;
+}
+
+// Balanced workspace: partials [slots][hpg][D] fp32 (D of a real head), LSEs
+// [slots][hpg] fp32, prefix sums [B + 1] int64, then one in-kernel-merge
+// counter per segment [B * Hkv * head_groups] uint64 (its contents never need
+// initialising); slots, hpg and the segments as in balanced_view.
+size_t balanced_bytes(const pkd_dims& d, int pair, size_t* lse_offset, size_t* prefix_offset,
+                      size_t* count_offset) {
+  const pkd_dims v = balanced_view(d, pair);
+  const size_t segments = (size_t)v.batch * v.num_kv_heads * head_groups(v);
+  const size_t slots = (size_t)balanced_workers(v) + segments;
+  const size_t hpg = (size_t)heads_per_slot(v);
   const size_t o = align256(slots * hpg * d.head_dim * sizeof(float));
   const size_t l = align256(slots * hpg * sizeof(float));
   const size_t pre = align256(((size_t)d.batch + 1) * sizeof(int64_t));
@@ -100,8 +127,9 @@ size_t balanced_bytes(const pkd_dims& d, size_t* lse_offset, size_t* prefix_offs
 }
 
 // Whether the balanced mode merges inside the partition kernel (paged_decode only).
-bool balanced_fused(const pkd_dims& d) {
-  return pkd::balanced_merge_in_kernel(balanced_workers(d), (int64_t)d.batch * d.num_kv_heads * head_groups(d));
+bool balanced_fused(const pkd_dims& d, int pair) {
+  const pkd_dims v = balanced_view(d, pair);
+  return pkd::balanced_merge_in_kernel(balanced_workers(v), (int64_t)v.batch * v.num_kv_heads * head_groups(v));
 }
 
 // Call tags for the in-kernel merge counters: distinct for every call in this
@@ -270,7 +298,8 @@ size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits) {
   if (check_dims(dims) != PKD_OK) return 0;
   int S = num_splits;
   if (S == PKD_SPLITS_AUTO) S = heuristic_splits(*dims, dims->max_pages_per_seq * dims->page_size);
-  if (S == PKD_SPLITS_BALANCED) return balanced_ok(*dims) ? balanced_bytes(*dims, nullptr, nullptr, nullptr) : 0;
+  if (S == PKD_SPLITS_BALANCED)
+    return balanced_ok(*dims) ? balanced_bytes(*dims, pair_heads(*dims, false), nullptr, nullptr, nullptr) : 0;
   if (S < 1 || S > PKD_MAX_SPLITS) return 0;
   if (S == 1) return 0;
   return partial_bytes(*dims, S, nullptr);
@@ -323,18 +352,20 @@ namespace {
 struct Plan {
   int S;           // 1 = direct output, 2.. = grid splits, PKD_SPLITS_BALANCED
   bool balanced;
+  int pair;        // balanced: KV heads read as one (pair_heads), else 1
   size_t need;     // workspace bytes
   size_t lse_off, prefix_off, count_off;
 };
 
-int32_t make_plan(const pkd_dims& d, int32_t num_splits, Plan* pl) {
+int32_t make_plan(const pkd_dims& d, int32_t num_splits, bool strided, Plan* pl) {
   int S = num_splits;
   if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size);
   pl->S = S;
   pl->balanced = S == PKD_SPLITS_BALANCED;
   if (pl->balanced ? !balanced_ok(d) : (S < 1 || S > PKD_MAX_SPLITS)) return PKD_ERR_NUM_SPLITS;
+  pl->pair = pl->balanced ? pair_heads(d, strided) : 1;
   pl->lse_off = pl->prefix_off = pl->count_off = 0;
-  pl->need = pl->balanced ? balanced_bytes(d, &pl->lse_off, &pl->prefix_off, &pl->count_off)
+  pl->need = pl->balanced ? balanced_bytes(d, pl->pair, &pl->lse_off, &pl->prefix_off, &pl->count_off)
                           : (S > 1 ? partial_bytes(d, S, &pl->lse_off) : 0);
   return PKD_OK;
 }
@@ -347,9 +378,10 @@ pkd::BalancedParams make_balanced_params(const pkd_dims& d, const Layout& lay, c
   b.os = lay.os;
   b.kv = lay.kv;
   b.strided = lay.strided ? 1 : 0;
+  b.pair_heads = pl.pair;
   // Head rows shorter than a 128-byte line put several KV heads in each line;
   // those heads' workgroups are kept on one XCD so each line is fetched once.
-  b.xcd_ranges = !lay.strided && lay.kv.head_stride < 128 && d.num_kv_heads > 1 ? 1 : 0;
+  b.xcd_ranges = !lay.strided && pl.pair == 1 && lay.kv.head_stride < 128 && d.num_kv_heads > 1 ? 1 : 0;
   b.q = static_cast<const uint16_t*>(q);
   b.k = static_cast<const uint8_t*>(k);
   b.v = static_cast<const uint8_t*>(v);
@@ -362,15 +394,16 @@ pkd::BalancedParams make_balanced_params(const pkd_dims& d, const Layout& lay, c
   b.prefix = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(ws) + pl.prefix_off);
   b.qk_scale_log2 = scale * 1.44269504088896340736f;
   b.batch = d.batch;
-  b.hq = d.num_q_heads;
-  b.hkv = d.num_kv_heads;
-  b.group = d.num_q_heads / d.num_kv_heads;
-  b.q_len = d.q_len;
-  b.causal = d.causal;
-  b.window = d.window;
-  b.rows_kv = rows_per_kv(d);
-  b.head_groups = head_groups(d);
-  b.hpg = heads_per_slot(d);
+  const pkd_dims bv = balanced_view(d, pl.pair);  // segments count wide heads when paired
+  b.hq = bv.num_q_heads;
+  b.hkv = bv.num_kv_heads;
+  b.group = bv.num_q_heads / bv.num_kv_heads;
+  b.q_len = bv.q_len;
+  b.causal = bv.causal;
+  b.window = bv.window;
+  b.rows_kv = rows_per_kv(bv);
+  b.head_groups = head_groups(bv);
+  b.hpg = heads_per_slot(bv);
   b.page_size = d.page_size;
   b.max_pages = d.max_pages_per_seq;
   b.num_workers = balanced_workers(d);
@@ -383,7 +416,8 @@ int32_t run_partition(const pkd_dims& d, const Layout& lay, const void* q, const
                       void* ws, const Plan& pl, hipStream_t s) {
   if (pl.balanced) {
     const pkd::BalancedParams b = make_balanced_params(d, lay, q, k, v, bt, lens, ks, vs, scale, ws, pl);
-    return pkd::launch_balanced(b, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, b.strided != 0, s) == hipSuccess
+    return pkd::launch_balanced(b, d.head_dim * pl.pair, d.kv_dtype == PKD_DTYPE_FP8_E4M3, b.strided != 0, s) ==
+                   hipSuccess
                ? PKD_OK : PKD_ERR_LAUNCH;
   }
   pkd::SplitParams p = make_split_params(d, lay, q, k, v, bt, lens, ks, vs, scale, pl.S);
@@ -409,13 +443,14 @@ int32_t run_finish(const pkd_dims& d, const Layout& lay, const void* ws, const f
   if (pl.balanced) {
     m.balanced = 1;
     m.prefix = reinterpret_cast<const int64_t*>(static_cast<const uint8_t*>(ws) + pl.prefix_off);
-    m.batch = d.batch;
-    m.hkv = d.num_kv_heads;
-    m.group = d.num_q_heads / d.num_kv_heads;
-    m.head_groups = head_groups(d);
-    m.hpg = heads_per_slot(d);
-    m.num_workers = balanced_workers(d);
-    m.q_len = d.q_len;
+    const pkd_dims v = balanced_view(d, pl.pair);  // the partition's segments
+    m.batch = v.batch;
+    m.hkv = v.num_kv_heads;
+    m.group = v.num_q_heads / v.num_kv_heads;
+    m.head_groups = head_groups(v);
+    m.hpg = heads_per_slot(v);
+    m.num_workers = balanced_workers(v);
+    m.q_len = v.q_len;
   } else {
     m.num_splits = pl.S;
   }
@@ -429,7 +464,7 @@ int32_t decode_checked(const pkd_dims& d, const Layout& lay, const void* q, cons
                        float scale, void* out, float* lse, int32_t num_splits, void* workspace,
                        size_t workspace_bytes, hipStream_t s) {
   Plan pl;
-  int32_t st = make_plan(d, num_splits, &pl);
+  int32_t st = make_plan(d, num_splits, lay.strided, &pl);
   if (st != PKD_OK) return st;
   if (pl.need > 0 && (!workspace || workspace_bytes < pl.need)) return PKD_ERR_WORKSPACE;
   if (d.batch == 0) return PKD_OK;
@@ -441,7 +476,7 @@ int32_t decode_checked(const pkd_dims& d, const Layout& lay, const void* q, cons
     p.sinks = sinks;
     return launch_partition(d, p, true, s);
   }
-  if (pl.balanced && balanced_fused(d)) {
+  if (pl.balanced && balanced_fused(d, pl.pair)) {
     // One kernel: the partition merges each segment's pieces itself.
     pkd::BalancedParams b = make_balanced_params(d, lay, q, k, v, bt, lens, ks, vs, scale, workspace, pl);
     b.fused = 1;
@@ -450,7 +485,8 @@ int32_t decode_checked(const pkd_dims& d, const Layout& lay, const void* q, cons
     b.sinks = sinks;
     b.seg_count = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + pl.count_off);
     b.epoch = next_epoch();
-    return pkd::launch_balanced(b, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, b.strided != 0, s) == hipSuccess
+    return pkd::launch_balanced(b, d.head_dim * pl.pair, d.kv_dtype == PKD_DTYPE_FP8_E4M3, b.strided != 0, s) ==
+                   hipSuccess
                ? PKD_OK : PKD_ERR_LAUNCH;
   }
   st = run_partition(d, lay, q, k, v, bt, lens, ks, vs, scale, workspace, pl, s);
@@ -466,9 +502,9 @@ int32_t paged_decode_launches(const pkd_dims* dims, int32_t num_splits) {
   const int32_t st = check_dims(dims);
   if (st != PKD_OK) return st;
   Plan pl;
-  const int32_t pst = make_plan(*dims, num_splits, &pl);
+  const int32_t pst = make_plan(*dims, num_splits, false, &pl);
   if (pst != PKD_OK) return pst;
-  if (pl.S == 1 || (pl.balanced && balanced_fused(*dims))) return 1;
+  if (pl.S == 1 || (pl.balanced && balanced_fused(*dims, pl.pair))) return 1;
   return 2;
 }
 
@@ -494,7 +530,7 @@ int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* 
   int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
   if (st != PKD_OK) return st;
   Plan pl;
-  st = make_plan(*dims, num_splits, &pl);
+  st = make_plan(*dims, num_splits, false, &pl);
   if (st != PKD_OK) return st;
   if (pl.S == 1) return PKD_ERR_NUM_SPLITS;
   if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
@@ -514,7 +550,7 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
   if (st != PKD_OK) return st;
   if (!aligned(sinks, 4)) return PKD_ERR_ALIGNMENT;
   Plan pl;
-  st = make_plan(*dims, num_splits, &pl);
+  st = make_plan(*dims, num_splits, false, &pl);
   if (st != PKD_OK) return st;
   if (pl.S == 1) return PKD_ERR_NUM_SPLITS;
   if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
@@ -665,7 +701,9 @@ size_t contiguous_decode_workspace_bytes(const pkd_contig_dims* dims, int32_t nu
   pkd_dims d;
   Layout lay;
   if (contiguous_plan(dims, &d, &lay) != PKD_OK) return 0;
-  return paged_decode_workspace_bytes(&d, num_splits);
+  Plan pl;
+  if (make_plan(d, num_splits, true, &pl) != PKD_OK) return 0;
+  return pl.need;
 }
 
 int32_t contiguous_decode(const pkd_contig_dims* dims, const void* q, const void* k, const void* v,

@@ -182,11 +182,18 @@ split_kv_kernel(const SplitParams p) {
 // merge kernel finds segment s's pieces from the same formula.  page_size
 // must be a multiple of 16.
 
-template <int D, bool FP8, int NWV, bool STRIDED, bool WINDOW, bool SINKS>
+// VK > 1 pairs KV heads whose rows share 128-byte lines: the kernel runs on
+// "wide" heads of D = VK * DR dims (VK adjacent real heads, the parameters'
+// hkv and group counting wide heads), each query row zero-padded outside its
+// own head's dims, and writes only its own head's DR dims (see load_q).  Each
+// line is then read once, by one workgroup.
+template <int D, bool FP8, int NWV, bool STRIDED, bool WINDOW, bool SINKS, int VK>
 __global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4)))
 balanced_kernel(const BalancedParams p) {
   typedef Cfg<D, FP8> C;
-  typedef Geometry<D, FP8, STRIDED> Geo;
+  constexpr int DR = D / VK;  // dims of a real head
+  typedef Geometry<D, FP8, STRIDED> Geo;    // K/V rows (of wide heads when paired)
+  typedef Geometry<DR, FP8, STRIDED> GeoQ;  // q / out rows, which are real heads' rows
   // Without a window (the instance for window = 0) nothing of it stays live.
   const int win = WINDOW ? p.window : 0;
   typedef TilePages<D, FP8, true> Pages;
@@ -199,6 +206,7 @@ balanced_kernel(const BalancedParams p) {
   __shared__ int s_last;                           // in-kernel merge: this piece completes its segment
   __shared__ int64_t s_rows[kHeadsPerGroup];       // row indices of the current piece's packed rows
   __shared__ int64_t s_orow[kHeadsPerGroup];       // their out offsets
+  __shared__ int s_slice[kHeadsPerGroup];          // paired heads: the row's head within its wide head
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -259,9 +267,9 @@ balanced_kernel(const BalancedParams p) {
     const int rows_seq = p.q_len * p.hq;
     for (int bb = (int)w; bb < B; bb += p.num_workers) {
       if (spre[bb + 1] != spre[bb]) continue;
-      for (int i = tid; i < rows_seq * D; i += NWV * 64) {
-        const int rr = i / D, qi = rr / p.hq;
-        p.out[Geo::os(p).at(bb, qi, rr - qi * p.hq) + (i - rr * D)] = 0;
+      for (int i = tid; i < rows_seq * DR; i += NWV * 64) {
+        const int rr = i / DR, qi = rr / p.hq;
+        p.out[GeoQ::os(p).at(bb, qi, rr - qi * p.hq) + (i - rr * DR)] = 0;
       }
       if (p.lse)
         for (int i = tid; i < rows_seq; i += NWV * 64)
@@ -318,10 +326,13 @@ balanced_kernel(const BalancedParams p) {
     const int kvh = seg / p.head_groups;
     const int hg = seg - kvh * p.head_groups;
     const int heads_here = min(kHeadsPerGroup, p.rows_kv - hg * kHeadsPerGroup);
-    const LaneRow lr = lane_row<D, STRIDED>(p, b, kvh, hg, A.n, L, s1, win);
+    const LaneRow lr = lane_row<DR, STRIDED>(p, b, kvh, hg, A.n, L, s1, win);
+    // Paired heads: the lane's row belongs to real head kvh * VK + slice.
+    const int slice = VK > 1 ? (lr.head / (p.group / VK)) % VK : 0;
     if (tid < kHeadsPerGroup) {  // read after the combine's barriers
       s_rows[tid] = lr.row;
       s_orow[tid] = lr.ooff;
+      s_slice[tid] = slice;
     }
     const int64_t head_off = (int64_t)kvh * Geo::head_stride(p);
 
@@ -335,9 +346,9 @@ balanced_kernel(const BalancedParams p) {
     const int nlo = npos < hi ? (nbq == b ? lo : first_of(nbq)) : 0;
     const int next_window = npos < hi ? load_window(nbq, nlo / ps) : 0;
 
-    A.load_q(p.q + lr.qoff, lr.valid);
+    A.template load_q<VK>(p.q + lr.qoff, lr.valid, slice);
     A.qk_scale = p.qk_scale_log2;
-    if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
+    if constexpr (FP8) A.qk_scale *= p.k_scale[kvh * VK + slice];
     A.reset();
 
     const int first_page = s0 / ps;
@@ -364,40 +375,53 @@ balanced_kernel(const BalancedParams p) {
     const int64_t seg_pos = spre[b] + (int64_t)seg * nb;
     const int64_t w_first = ((seg_pos + 1) * nwe - 1) / T;
     const int npieces = (int)(((seg_pos + nb) * nwe - 1) / T - w_first + 1);
-    const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
+    // Row hh's V scale, and whether dims d0.. of the wide row are its own head's
+    // (always, without pairing); own_dim gives their place in the real row.
+    const float vsc = FP8 ? p.v_scale[kvh * VK] : 1.0f;
+    auto vsc_of = [&](int hh) -> float { return FP8 && VK > 1 ? p.v_scale[kvh * VK + s_slice[hh]] : vsc; };
+    auto mine = [&](int hh, int d0) -> bool { return VK == 1 || d0 / DR == s_slice[hh]; };
+    auto own_dim = [&](int hh, int d0) -> int { return VK == 1 ? d0 : d0 - s_slice[hh] * DR; };
     if (p.fused && npieces == 1) {
       // The whole segment is this piece: write the result directly.
       auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
+        if (!mine(hh, d0)) return;
         const int64_t row = s_rows[hh];
-        *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + d0) = to_bf16x4(o);
-        if (d0 == 0 && p.lse) p.lse[row] = lse_nat;
+        const int dd = own_dim(hh, d0);
+        *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + dd) = to_bf16x4(o);
+        if (dd == 0 && p.lse) p.lse[row] = lse_nat;
       };
       if constexpr (SINKS)
-        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, store,
-                                [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
+        wg_combine_rows<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc_of, store,
+                                     [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
       else
-        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, store, NoSink());
+        wg_combine_rows<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc_of, store, NoSink());
       __syncthreads();  // the LDS is reused by the next piece
     } else {
-      // This piece's partial, for the group's heads.
+      // This piece's partial, for the group's heads (DR dims per row).
       const int64_t slot = w + sidx;
-      float* orow = p.o_part + slot * p.hpg * D;
+      float* orow = p.o_part + slot * p.hpg * DR;
       float* lrow = p.lse_part + slot * p.hpg;
       if (!p.fused) {
-        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
-          *reinterpret_cast<f32x4*>(orow + hh * D + d0) = o;
-          if (d0 == 0) lrow[hh] = lse_nat;
+        wg_combine_rows<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc_of,
+                                     [&](int hh, int d0, f32x4 o, float lse_nat) {
+          if (!mine(hh, d0)) return;
+          const int dd = own_dim(hh, d0);
+          *reinterpret_cast<f32x4*>(orow + hh * DR + dd) = o;
+          if (dd == 0) lrow[hh] = lse_nat;
         }, NoSink());
       } else {
         // Agent-scope stores write through to the coherent copy that another
         // XCD's workgroup will read; waiting for their acknowledgement before the
         // count makes the partial visible to whichever piece merges.  (A release
         // fence would write back this XCD's whole L2, far too costly per piece.)
-        wg_combine<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc, [&](int hh, int d0, f32x4 o, float lse_nat) {
+        wg_combine_rows<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc_of,
+                                     [&](int hh, int d0, f32x4 o, float lse_nat) {
+          if (!mine(hh, d0)) return;
+          const int dd = own_dim(hh, d0);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            __hip_atomic_store(orow + hh * D + d0 + i, o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (d0 == 0) __hip_atomic_store(lrow + hh, lse_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(orow + hh * DR + dd + i, o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (dd == 0) __hip_atomic_store(lrow + hh, lse_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }, NoSink());
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are acknowledged
@@ -426,18 +450,18 @@ balanced_kernel(const BalancedParams p) {
           // partials take at most 64 registers with one wave per SIMD, 32 with
           // two); otherwise, or when only one row fits, one row at a time.
           const int64_t slot0 = w_first + sidx;
-          typedef RowMerge<D, true> RM;
+          typedef RowMerge<DR, true> RM;
           constexpr int MAXR = kHeadsPerGroup / NWV;
           constexpr int RC_REG = (NWV > 4 ? 32 : 64) / (RM::UNROLL * RM::EPL);
           constexpr int RC = RC_REG < MAXR ? RC_REG : MAXR;
           const float* lp0 = p.lse_part + slot0 * p.hpg;
-          const float* op0 = p.o_part + slot0 * p.hpg * D;
-          const int64_t ls = p.hpg, os = (int64_t)p.hpg * D;
+          const float* op0 = p.o_part + slot0 * p.hpg * DR;
+          const int64_t ls = p.hpg, os = (int64_t)p.hpg * DR;
           const int lane = tid & 63;
           if (RC < 2 || npieces > RM::UNROLL) {
             for (int hh = wave; hh < heads_here; hh += NWV) {
               RM r;
-              r.run(lp0 + hh, ls, op0 + hh * D, os, npieces, lane);
+              r.run(lp0 + hh, ls, op0 + hh * DR, os, npieces, lane);
               const int64_t row = s_rows[hh];
               r.store(p.out + s_orow[hh], p.lse ? p.lse + row : nullptr, lane,
                       SINKS ? p.sinks[(int)(row % p.hq)] : -INFINITY);
@@ -450,7 +474,7 @@ balanced_kernel(const BalancedParams p) {
 #pragma unroll
               for (int k = 0; k < RCS; ++k) {
                 const int hh = wave + (k0 + k) * NWV;
-                if (hh < heads_here) RM::issue(lp0 + hh, ls, op0 + hh * D, os, npieces, lane, st[k]);
+                if (hh < heads_here) RM::issue(lp0 + hh, ls, op0 + hh * DR, os, npieces, lane, st[k]);
               }
 #pragma unroll
               for (int k = 0; k < RCS; ++k) {
@@ -469,7 +493,6 @@ balanced_kernel(const BalancedParams p) {
       }
       __syncthreads();  // the LDS is reused by the next piece
     }
-
     pos = npos;
     grp = 0;
     seg = nseg;
@@ -507,15 +530,15 @@ constexpr int balanced_waves(bool fp8) { return fp8 ? 8 : 4; }
 
 // Instances without a window or without sinks keep none of their state live
 // (the kernel is at the edge of its scalar registers).
-template <int D, bool FP8, bool STRIDED, bool WINDOW>
+template <int D, bool FP8, bool STRIDED, bool WINDOW, int VK = 1>
 void launch_bw(const BalancedParams& p, hipStream_t stream) {
   constexpr int NWV = balanced_waves(FP8);
   if (p.sinks)
-    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, true>), dim3(p.num_workers), dim3(NWV * 64),
-                       0, stream, p);
+    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, true, VK>), dim3(p.num_workers),
+                       dim3(NWV * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, false>), dim3(p.num_workers), dim3(NWV * 64),
-                       0, stream, p);
+    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, false, VK>), dim3(p.num_workers),
+                       dim3(NWV * 64), 0, stream, p);
 }
 
 template <int D, bool FP8, bool STRIDED>
@@ -528,6 +551,16 @@ void launch_bs(const BalancedParams& p, hipStream_t stream) {
 
 template <int D, bool FP8>
 hipError_t launch_b(const BalancedParams& p, bool strided, hipStream_t stream) {
+  if (p.pair_heads > 1) {
+    // Paired KV heads (D is the wide head's dims): the paged layout without a window.
+    if constexpr (D == 64 || D == 128) {
+      if (strided || p.window > 0 || p.pair_heads != 2) return hipErrorInvalidValue;
+      launch_bw<D, FP8, false, false, 2>(p, stream);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (strided)
     launch_bs<D, FP8, true>(p, stream);
   else

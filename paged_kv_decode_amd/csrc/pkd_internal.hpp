@@ -92,6 +92,8 @@ struct BalancedParams {
   KvLayout kv;
   int32_t strided;
   int32_t xcd_ranges;          // give each XCD a contiguous part of the work space (heads sharing cache lines)
+  int32_t pair_heads;          // 1, or 2: hkv / group / head dims count wide heads of two real KV heads
+                               // (q / out rows, partials and scales stay per real head)
 };
 
 // True when the balanced mode merges inside the partition kernel: when there

@@ -223,12 +223,19 @@ struct WaveAttn {
   // Lane (n, g) holds packed row n's dims (kk / R) * 4 * PIECE + g * PIECE + (kk % R) * 8 + [0, 8)
   // for MFMA kk; the K loads use the same dim assignment.  qrow_n is the memory
   // row of packed row n (any valid row when hv is false); rows past the group are zero.
-  __device__ __forceinline__ void load_q(const uint16_t* qrow, bool hv) {
+  // This lane's query row.  With paired KV heads (VK > 1) the wave's D dims are
+  // VK real heads of DR = D / VK dims each; the row (of real head slice s)
+  // fills dims [s DR, (s + 1) DR) and is zero elsewhere, so that its scores
+  // take only its own head's keys.
+  template <int VK = 1>
+  __device__ __forceinline__ void load_q(const uint16_t* qrow, bool hv, int s = 0) {
+    constexpr int DR = D / VK;
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       const int d0 = (kk / C::R) * 4 * C::PIECE + g * C::PIECE + (kk % C::R) * 8;
-      Ld16 raw = *reinterpret_cast<const Ld16*>(qrow + d0);
-      if (!hv) raw = Ld16{0, 0, 0, 0};
+      const bool mine = VK == 1 || d0 / DR == s;
+      Ld16 raw = Ld16{0, 0, 0, 0};
+      if (hv && mine) raw = *reinterpret_cast<const Ld16*>(qrow + (d0 - s * DR));
       qf[kk] = bit_cast_dev<bf16x8>(raw);
     }
   }
@@ -463,6 +470,7 @@ __device__ __forceinline__ int64_t packed_row(int b, int kvh, int r, int q_len, 
 struct LaneRow {
   int64_t row;
   int64_t qoff, ooff;
+  int head;       // query head of the row
   bool valid;
   int start;      // first position the row sees (its sliding window's lower end; 0 without a window)
   int end;
@@ -476,6 +484,7 @@ __device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, 
   const int rr = lr.valid ? r : hg * kHeadsPerGroup;
   const int i = rr / p.group, h = kvh * p.group + (rr - i * p.group);
   lr.row = ((int64_t)b * p.q_len + i) * p.hq + h;
+  lr.head = h;
   if constexpr (STRIDED) {
     lr.qoff = p.qs.at(b, i, h);
     lr.ooff = p.os.at(b, i, h);
@@ -584,12 +593,12 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
 // e_w = 2^(m_w - max m), and the natural-log LSE.  A row that saw no token in
 // any wave gets o = 0 and lse = -inf.  sink_of(hh) is row hh's sink logit
 // (-inf for none), folded in as fold_sink describes; partials take none.  The
-// per-row weights e_w * vsc / den are computed once per row, then each element
+// per-row weights e_w * vsc / den (vsc_of(hh) for row hh) are computed once per row, then each element
 // is a short weighted sum of the staged wave rows.  Ends with the LDS still in
 // use: synchronise before reusing it.
-template <int D, bool FP8, int NWV = kWaves, typename Store, typename SinkOf>
-__device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* smem, int wave, int tid,
-                                           int heads_here, float vsc, Store store, SinkOf sink_of) {
+template <int D, bool FP8, int NWV = kWaves, typename Store, typename SinkOf, typename VscOf>
+__device__ __forceinline__ void wg_combine_rows(const WaveAttn<D, FP8>& A, uint8_t* smem, int wave, int tid,
+                                                int heads_here, VscOf vsc_of, Store store, SinkOf sink_of) {
   typedef Cfg<D, FP8> C;
   constexpr int RWS = NWV + 4;                 // per-row table stride (floats): NWV weights, then the LSE
   const float l_tot = A.l_total();
@@ -621,7 +630,7 @@ __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* s
     }
     float lse_nat = (M_use + log2f(den)) * 0.69314718055994530942f;
     const float f = fold_sink(lse_nat, sink_of(hh));
-    const float sc = den > 0.f ? vsc * f / den : 0.f;
+    const float sc = den > 0.f ? vsc_of(hh) * f / den : 0.f;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) rw[hh * RWS + w] = e[w] * sc;
     rw[hh * RWS + NWV] = lse_nat;
@@ -636,6 +645,13 @@ __device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* s
       o += rw[hh * RWS + w] * *reinterpret_cast<const f32x4*>(ow + (w * 16 + hh) * C::OW_STRIDE + d0);
     store(hh, d0, o, rw[hh * RWS + NWV]);
   }
+}
+
+// wg_combine_rows with one V scale for every row.
+template <int D, bool FP8, int NWV = kWaves, typename Store, typename SinkOf>
+__device__ __forceinline__ void wg_combine(const WaveAttn<D, FP8>& A, uint8_t* smem, int wave, int tid,
+                                           int heads_here, float vsc, Store store, SinkOf sink_of) {
+  wg_combine_rows<D, FP8, NWV>(A, smem, wave, tid, heads_here, [vsc](int) { return vsc; }, store, sink_of);
 }
 
 // No sink (partials, and rows of a call without sinks).
