@@ -1097,3 +1097,18 @@ def test_graph_replays_append_and_metadata(B):
         for k, v in ref_m.items():
             assert np.array_equal(m_out[k].cpu().numpy(), v), f"replay {i}: {k}"
         assert int(m_out["error_count"].cpu()[0]) == bad
+
+
+def test_largest_q_len_with_causal_window_and_sinks(B):
+    """q_len at its maximum (64 query tokens: 64 and 128 packed rows per KV head,
+    i.e. 4 and 8 head groups) under the causal mask with a window and sinks,
+    in every split mode, against the oracle."""
+    for hq, hkv in ((4, 4), (8, 4)):
+        lens = [64, 200, 3, 700]
+        w = wl.custom_workload(len(lens), hq, hkv, 64, 16, lens, "bf16", seed=760 + hq, q_len=64, causal=True,
+                               window=40, sinks=True)
+        ref = oracle_full(w)
+        t = dev(w)
+        for S in (1, 3, BAL):
+            out, lse = run(B, w, S, t)
+            check(out, lse, *ref, what=f"q_len 64 Hq={hq} S={S}")
