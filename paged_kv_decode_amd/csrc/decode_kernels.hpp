@@ -13,12 +13,14 @@
 //    the waves interleave the tiles of the split and combine their states in
 //    LDS at the end.  One split writes out/lse directly; several write
 //    partials for the merge kernel.
-//  * balanced kernel: a persistent grid sized to the device; every wave gets an
-//    equal share of the flattened (sequence, KV head, 16-token group) space,
-//    walks it segment by segment and writes one partial per (wave, segment)
-//    piece.  Work per wave is equal whatever the length mix, and the start-up
-//    latency chain (lengths -> block table -> first K/V) is paid once per wave
-//    rather than once per split.
+//  * balanced kernel: a persistent grid of one workgroup per compute unit;
+//    every workgroup gets an equal share of the flattened (sequence, KV head,
+//    head group, 16-token group) space, walks it segment by segment (its waves
+//    interleaving each piece's tiles) and writes one partial per (workgroup,
+//    segment) piece, or merges a segment's pieces itself when it completes
+//    the segment.  Work per workgroup is equal whatever the length mix, and the
+//    start-up latency chain (lengths -> block table -> first K/V) is paid once
+//    per workgroup rather than once per split.
 //
 // The per-tile machinery (loads, MFMA tile step, pipeline, combine) is in
 // wave_attn.hpp.

@@ -37,6 +37,13 @@
 // <= L - q_len + i (the position of that token), so each lane, which holds one
 // packed row, masks scores at its own end; a row that sees no token of a tile
 // or of a whole range keeps m = -inf and contributes nothing.
+//
+// A sliding window adds a per-lane lower bound (the row's window start) to the
+// same select; per-head sink logits are folded into the finished rows (see
+// fold_sink).  K/V rows are addressed through byte strides of a page (or, for
+// contiguous K/V, a sequence), a token and a head (Geometry), and with paired
+// heads a wave's D dims span two real heads, each query row zero-padded
+// outside its own (load_q).
 #pragma once
 
 #include "merge_row.hpp"
