@@ -350,10 +350,16 @@ CALIB_BYTES = 1 << 30  # the 1 GiB device-to-device copy made at start-up
 
 
 def _source_digest():
+    """sha256 of the partition kernels' code: the sources with comments and
+    whitespace removed, so that a comment edit does not orphan the counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
