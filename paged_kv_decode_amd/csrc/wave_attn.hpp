@@ -199,6 +199,11 @@ struct TilePages {
 };
 
 
+// How far (base-2 units) a tile's score maximum may exceed a row's reference
+// maximum before the reference is raised: softmax weights then stay at most
+// 2^8, far inside the range of the bf16 P operand and the fp32 sums.
+constexpr float kRescaleSlack = 8.f;
+
 // Per-wave attention state and tile operations, shared by both launch shapes.
 // Lane (n, g) = (lane % 16, lane / 16) in the MFMA operand layouts.
 template <int D, bool FP8>
@@ -212,7 +217,7 @@ struct WaveAttn {
   int k_doff, v_doff;  // byte offsets of this lane's K dims / V chunk inside a row
   bf16x8 qf[C::KK];    // query heads as the B operand of QK^T
   float qk_scale;      // scale * log2(e) (* k_scale for fp8)
-  float m_run;         // running max (base-2 units) of head n, equal in all lane groups
+  float m_run;         // reference max (base-2 units) of head n, equal in all lane groups
   float l_run;         // this lane's partial sum of exp2(s - m_run) for head n
   f32x4 acc[C::NB];    // O^T: acc[nb][i] = out[head n][16 nb + 4 g + i] (unnormalised)
 
@@ -329,9 +334,11 @@ struct WaveAttn {
 
   // One tile: V to LDS, QK^T, online softmax, PV.  Tokens before s_lo or at or
   // past s1 (this lane's packed row's window start and end) are masked.
-  // lo_all (uniform) is at least every lane's s_lo: tiles starting there or
-  // later skip the lower-bound test.
-  __device__ __forceinline__ void process(const Regs& R, int tb, int s_lo, int s1, int lo_all, uint16_t* vs) {
+  // lo_all and hi_all (uniform) bound every lane's s_lo from above and s1 from
+  // below: tiles starting at lo_all or later skip the lower-bound test, and
+  // tiles inside [lo_all, hi_all) skip masking altogether.
+  __device__ __forceinline__ void process(const Regs& R, int tb, int s_lo, int s1, int lo_all, int hi_all,
+                                          uint16_t* vs) {
     // V -> LDS, row-major bf16 (16-byte writes).
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
@@ -374,7 +381,15 @@ struct WaveAttn {
     // Online softmax (base 2).  Lane (n, g) holds scores of head n for tokens
     // s_out_token(blk, g, i).
     float mt = -INFINITY;
-    if (tb >= lo_all) {
+    if (tb >= lo_all && tb + C::TT <= hi_all) {
+#pragma unroll
+      for (int blk = 0; blk < C::NBLK; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sacc[blk][i] *= qk_scale;
+          mt = fmaxf(mt, sacc[blk][i]);
+        }
+    } else if (tb >= lo_all) {
 #pragma unroll
       for (int blk = 0; blk < C::NBLK; ++blk)
 #pragma unroll
@@ -397,12 +412,22 @@ struct WaveAttn {
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    // A row that has seen no unmasked token keeps m = -inf; subtracting 0 then
-    // gives alpha = 0 and e = 0 instead of NaN.
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    // m_run is a reference maximum rather than the exact running maximum: it
+    // is raised (and l and O rescaled by 2^(old - new)) only when a tile's
+    // maximum exceeds it by more than kRescaleSlack, so every weight
+    // 2^(s - m_run) stays at most 2^kRescaleSlack and, after the first tiles,
+    // the rescale of the accumulators is skipped.  Raised, it becomes the
+    // tile's maximum.  A row that has seen no unmasked token keeps m = -inf;
+    // subtracting 0 then gives e = 0 instead of NaN.
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
+      const float m_new = mt > m_run + kRescaleSlack ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) acc[nb] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
     for (int blk = 0; blk < C::NBLK; ++blk)
@@ -412,9 +437,7 @@ struct WaveAttn {
         sacc[blk][i] = e;
         psum += e;
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) acc[nb] *= alpha;
+    l_run += psum;
 
     wave_lds_sync();  // the V tile is complete in LDS
 
@@ -482,6 +505,7 @@ struct LaneRow {
   int start;      // first position the row sees (its sliding window's lower end; 0 without a window)
   int end;
   int start_max;  // uniform: no row of the sequence starts later (L - window, or 0)
+  int end_min;    // uniform: no row of the group ends earlier
 };
 template <int D, bool STRIDED, typename P>
 __device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, int n, int L, int s1, int window) {
@@ -500,6 +524,8 @@ __device__ __forceinline__ LaneRow lane_row(const P& p, int b, int kvh, int hg, 
   }
   const int pos = L - p.q_len + i;  // the query token's position
   lr.end = p.causal ? min(s1, pos + 1) : s1;
+  // The group's first row holds its earliest query token.
+  lr.end_min = p.causal ? min(s1, L - p.q_len + (hg * kHeadsPerGroup) / p.group + 1) : s1;
   lr.start = window > 0 ? max(pos - window + 1, 0) : 0;
   lr.start_max = window > 0 ? max(L - window, 0) : 0;
   return lr;
@@ -578,7 +604,7 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
     int t2 = nxt(t1);
     fetch(t2, pa);
     __builtin_amdgcn_sched_barrier(0);
-    A.process(ra, s0 + t * C::TT, lr.start, lr.end, lr.start_max, vs);
+    A.process(ra, s0 + t * C::TT, lr.start, lr.end, lr.start_max, lr.end_min, vs);
     if (t1 == t) break;
     t = t1;
     t1 = t2;
@@ -586,7 +612,7 @@ __device__ __forceinline__ void run_tiles(WaveAttn<D, FP8>& A, int first, int st
     t2 = nxt(t1);
     fetch(t2, pb);
     __builtin_amdgcn_sched_barrier(0);
-    A.process(rb, s0 + t * C::TT, lr.start, lr.end, lr.start_max, vs);
+    A.process(rb, s0 + t * C::TT, lr.start, lr.end, lr.start_max, lr.end_min, vs);
     if (t1 == t) break;
     t = t1;
     t1 = t2;
