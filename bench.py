@@ -17,9 +17,12 @@ partials and cache effects are not counted.
 
 The primary workload is the B=32 Llama-style decode step; the B=128 step, the
 B=32 verify step (4 query tokens, causal) and the B=32 step with a 1024-token
-window and sinks are reported alongside.  The fp64 CPU oracle is timed on the same host arrays
-(whole passes over the workload for about 10 s, all host threads up to 16) as
-a reported baseline.
+window and sinks are reported alongside, with a sweep of fixed num_splits
+values against the balanced mode at B=32 and B=128, and, as context for the
+roofline, torch's read-only sum over a buffer of the B=32 step's bytes timed
+the same way.  The fp64 CPU oracle is timed on the same host arrays (whole
+passes over the workload for about 10 s, all host threads up to 16) as a
+reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads NAMES|all]
                        [--num-splits S] [--no-cpu-baseline] [--profile-only]
@@ -316,6 +319,60 @@ def bench_contiguous(w, steps, warmup, device, scrub):
             "pct_of_peak": 100.0 * nbytes / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+SWEEP_SPLITS = (1, 2, 4, 8, 16)
+
+
+def _cold_steps(stream, steps, scrub, fn):
+    """Mean ms of fn over steps calls, each from cold caches, one event pair per call."""
+    import torch
+    ms = []
+    for _ in range(steps):
+        scrub.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return sum(ms) / len(ms)
+
+
+def split_sweep(w, steps, warmup, device, scrub):
+    """GB/s of workload w's whole step with num_splits fixed at 1, 2, 4, 8 and 16
+    (the grid kernel, plus the merge kernel when S > 1) and in the balanced mode
+    (the library's choice here), each timed like the metric."""
+    import torch
+    from paged_kv_decode_amd import binding as B
+    nbytes = algorithmic_bytes(w)
+    out = {}
+    for S in SWEEP_SPLITS + (B.PKD_SPLITS_BALANCED,):
+        r = Runner(w, S, device)
+        for _ in range(warmup):
+            r.step()
+        torch.cuda.synchronize()
+        mean = _cold_steps(r.stream, steps, scrub, r.step)
+        out["balanced" if S == B.PKD_SPLITS_BALANCED else f"S={S}"] = round(nbytes / (mean * 1e-3) / 1e9, 1)
+        del r
+    return out
+
+
+def stream_ceiling(nbytes, steps, warmup, device, scrub):
+    """Context for the roofline, not a metric: torch's read-only sum over a
+    float32 buffer of the decode step's algorithmic bytes, timed cold like the
+    decode steps.  A plain library read of the same footprint."""
+    import torch
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    stream = torch.cuda.current_stream(device)
+    for _ in range(warmup):
+        buf.sum()
+    torch.cuda.synchronize()
+    mean = _cold_steps(stream, steps, scrub, buf.sum)
+    del buf
+    gbs = (nbytes // 4) * 4 / (mean * 1e-3) / 1e9
+    return {"kernel": "torch.sum over float32 (read-only)", "bytes": (nbytes // 4) * 4, "ms": round(mean, 4),
+            "gbs": round(gbs, 1), "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2)}
+
+
 def cpu_baseline(w, nbytes):
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -344,8 +401,10 @@ def cpu_baseline(w, nbytes):
 
 
 # The sources the partition kernels are built from (their digest tags the counter summaries).
+# The kernels' sources and the host code that picks which kernel a workload runs.
 KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_decode_amd", "csrc", f) for f in
-               ("decode_kernels.hpp", "wave_attn.hpp", "merge_row.hpp", "pkd_internal.hpp", "decode_d128.hip")]
+               ("decode_kernels.hpp", "wave_attn.hpp", "merge_row.hpp", "pkd_internal.hpp", "decode_d128.hip",
+                "api.cpp")]
 CALIB_BYTES = 1 << 30  # the 1 GiB device-to-device copy made at start-up
 
 
@@ -454,8 +513,8 @@ def traffic_from_profiles(name):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads", default=f"{PRIMARY},{SECONDARY},{VERIFY},{WINDOW}",
                     help="comma-separated workload names, or 'all'")
     ap.add_argument("--num-splits", type=int, default=0, help="0: the library's heuristic")
@@ -494,13 +553,15 @@ def main():
         names = [PRIMARY] + names
     results = {}
     primary_w = None
+    sweep_w = {}
     for name in names:
         res, w = bench_one(name, args.steps, args.warmup, args.num_splits, device, scrub)
         results[name] = res
         if name == PRIMARY:
             primary_w = w
-        else:
-            del w
+        if name in (PRIMARY, SECONDARY) and not args.profile_only:
+            sweep_w[name] = w
+        del w
         print(f"# {name}: S={res['num_splits']} {res['ms_per_step'] * 1e3:.1f} us/step "
               f"(p10 {res['ms_p10'] * 1e3:.1f}, p90 {res['ms_p90'] * 1e3:.1f}) "
               f"{res['gbs']:.0f} GB/s = {res['pct_of_peak']:.1f}% of peak, "
@@ -509,6 +570,14 @@ def main():
               file=sys.stderr, flush=True)
     if args.profile_only:
         return
+    sweep_steps, sweep_warmup = max(args.steps // 5, 5), 3
+    sweep = {name: split_sweep(w, sweep_steps, sweep_warmup, device, scrub) for name, w in sweep_w.items()}
+    for name, row in sweep.items():
+        print(f"# num_splits sweep {name} (GB/s): {row}", file=sys.stderr, flush=True)
+    del sweep_w
+    ceiling = stream_ceiling(results[PRIMARY]["algorithmic_bytes"], args.steps, args.warmup, device, scrub)
+    print(f"# stream ceiling ({ceiling['kernel']}, {ceiling['bytes']} bytes): {ceiling['gbs']:.0f} GB/s = "
+          f"{ceiling['pct_of_peak']:.1f}% of peak", file=sys.stderr, flush=True)
     app = bench_append(args.steps, args.warmup, device, scrub)
     meta = bench_metadata(primary_w, args.steps, args.warmup, device, scrub, window=1024)
     contig = bench_contiguous(primary_w, args.steps, args.warmup, device, scrub)
@@ -566,6 +635,8 @@ def main():
         line["window"] = {"gbs": round(v["gbs"], 2), "pct_of_peak": round(v["pct_of_peak"], 2),
                           "queries_per_s": round(v["queries_per_s"], 1), "ms_per_step": v["ms_per_step"],
                           "window": v["window"], "sinks": v["sinks"], "num_splits": v["num_splits"]}
+    line["split_sweep"] = {"steps": sweep_steps, "warmup": sweep_warmup, "gbs": sweep}
+    line["stream_ceiling"] = ceiling
     line["append"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in app.items()}
     line["metadata"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in meta.items()}
     line["contiguous"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in contig.items()}

@@ -206,12 +206,17 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
                             void* stream);
 
 /*
- * paged_decode_num_splits -- what paged_decode does for PKD_SPLITS_AUTO:
- * PKD_SPLITS_BALANCED wherever it applies; otherwise 1 (direct output) when the
- * (sequence, KV-head) work items alone fill the current device's compute units,
- * else a split count in [2, PKD_MAX_SPLITS] bounded by the longest sequence
- * expected, max_seq_len_hint (<= 0: max_pages_per_seq * page_size).  Host only;
- * returns that value, or a status in [-11, -1] for invalid dims.
+ * paged_decode_num_splits -- what paged_decode does for PKD_SPLITS_AUTO.
+ * Work items are (sequence, KV head, head group), a head group being up to 16
+ * of a KV head's q_len * G query rows.
+ *  - 1 (direct output) for a BF16 cache with head_dim >= 64 when the items
+ *    number exactly the current device's compute units (one whole item per
+ *    unit, nothing to merge);
+ *  - else PKD_SPLITS_BALANCED wherever it applies;
+ *  - else 1 when the items alone fill the device's compute units, else a split
+ *    count in [2, PKD_MAX_SPLITS] bounded by the longest sequence expected,
+ *    max_seq_len_hint (<= 0: max_pages_per_seq * page_size).
+ * Host only; returns that value, or a status in [-11, -1] for invalid dims.
  */
 int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint);
 

@@ -176,17 +176,28 @@ int32_t split_chunk(const pkd_dims& d, int S) {
   return (int32_t)(c < INT32_MAX ? c : INT32_MAX);
 }
 
-// The split mode for PKD_SPLITS_AUTO.  The balanced partition wherever it
-// applies (it balances any length mix and pays each workgroup's start-up once);
-// otherwise direct output when the (sequence, KV head) items alone fill the
-// device, else enough splits to fill it, bounded by the longest sequence.
+// The split mode for PKD_SPLITS_AUTO.
+//  - Direct output (one split) when a bf16 cache whose head rows are at least
+//    128 bytes has exactly one (sequence, KV head, head group) item per compute
+//    unit: each unit streams one whole item and nothing is merged.  There the
+//    balanced partition's even cuts give most workgroups two pieces, and the
+//    second piece's combine, acknowledged partial store, count and merge cost
+//    more than the length imbalance that whole items leave (measured at 256
+//    items: 4% faster at B = 32 with lengths 1024-4096, 11% for 4 causal query
+//    tokens, 24% with a 1024-token window, a tie for another length draw; with
+//    224 or 288 items, or an FP8 cache, the balanced partition was faster).
+//  - Otherwise the balanced partition wherever it applies (it balances any
+//    length mix and pays each workgroup's start-up once).
+//  - Otherwise direct output when the items alone fill the device, else
+//    enough splits to fill it, bounded by the longest sequence.
 int32_t heuristic_splits(const pkd_dims& d, int32_t max_len) {
-  if (balanced_ok(d)) return PKD_SPLITS_BALANCED;
   const int cus = current_cu_count();
+  const int64_t items = (int64_t)d.batch * d.num_kv_heads * head_groups(d);
+  if (d.kv_dtype == PKD_DTYPE_BF16 && d.head_dim >= 64 && cus > 0 && items == cus) return 1;
+  if (balanced_ok(d)) return PKD_SPLITS_BALANCED;
   const int64_t target = 4LL * (cus > 0 ? cus : 256);  // workgroups to keep every CU busy
-  const int64_t work = (int64_t)d.batch * d.num_kv_heads * head_groups(d);
-  if (work <= 0 || work >= target) return 1;
-  int64_t s = (target + work - 1) / work;
+  if (items <= 0 || items >= target) return 1;
+  int64_t s = (target + items - 1) / items;
   const int64_t span = max_len < visible_span(d) ? max_len : visible_span(d);
   const int64_t by_len = (span + 255) / 256;  // keep at least ~256 tokens per split
   if (s > by_len) s = by_len;

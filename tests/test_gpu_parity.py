@@ -407,10 +407,11 @@ def test_full_size_workload_sampled_rows(B, name):
 TWO_PHASE_CASES = {
     "small": (5, 16, 2, 128, 64, [700, 1, 0, 3000, 64]),  # few segments: partition + merge kernel
     "b32": (32, 32, 8, 128, 64, [(i * 613) % 3500 + 1 for i in range(30)] + [0, 64]),
+    "b24": (24, 32, 8, 128, 64, [(i * 613) % 3500 + 1 for i in range(22)] + [0, 64]),  # AUTO: balanced
 }
 
 
-@pytest.mark.parametrize("S,case", [(4, "small"), (BAL, "small"), (BAL, "b32"), (0, "b32")])
+@pytest.mark.parametrize("S,case", [(4, "small"), (BAL, "small"), (BAL, "b32"), (0, "b24")])
 def test_two_phases_equal_paged_decode(B, S, case):
     """paged_decode_partition then paged_decode_finish is exactly paged_decode,
     also where paged_decode merges inside the partition kernel (b32)."""
@@ -430,6 +431,48 @@ def test_two_phases_equal_paged_decode(B, S, case):
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.cpu(), ref_lse)
+
+
+def _cu_count():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("hkv,d,dtype,expect", [(8, 128, "bf16", 1), (8, 64, "bf16", 1), (8, 32, "bf16", BAL),
+                                                 (8, 128, "fp8_e4m3", BAL)])
+def test_auto_one_item_per_cu(B, hkv, d, dtype, expect):
+    """PKD_SPLITS_AUTO picks direct output when a bf16 cache with head rows of at
+    least 128 bytes has exactly one (sequence, KV head, head group) item per
+    compute unit, else the balanced partition; one item more or fewer also
+    gives the balanced partition."""
+    cus = _cu_count()
+    if cus % hkv:
+        pytest.skip("compute units not a multiple of the KV heads")
+    kvd = B.PKD_DTYPE_FP8_E4M3 if dtype == "fp8_e4m3" else B.PKD_DTYPE_BF16
+    for batch, want in ((cus // hkv, expect), (cus // hkv - 1, BAL), (cus // hkv + 1, BAL)):
+        dims = B.pkd_dims(batch, 4 * hkv, hkv, d, 64, 4096, 64, kvd, 1, 0, 0)
+        assert B.paged_decode_num_splits(dims, 0) == want, (batch, hkv, d, dtype)
+
+
+def test_two_phases_reject_auto_direct(B):
+    """Where PKD_SPLITS_AUTO resolves to direct output, the two-phase entries
+    return PKD_ERR_NUM_SPLITS and write nothing."""
+    cus = _cu_count()
+    if cus % 8:
+        pytest.skip("compute units not a multiple of 8")
+    bq = cus // 8
+    w = wl.custom_workload(bq, 32, 8, 128, 64, [(i * 613) % 3500 + 1 for i in range(bq)], "bf16", seed=124)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    assert B.paged_decode_num_splits(dims, 0) == 1
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    h = B.current_stream_handle(0)
+    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, 0,
+                                    ws, ws.numel(), h) == B.PKD_ERR_NUM_SPLITS
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+    # and paged_decode itself, with AUTO, matches the oracle
+    out, lse = run(B, w, 0, t)
+    check(out, lse, *oracle_full(w), what="AUTO direct at one item per compute unit")
 
 
 @pytest.mark.parametrize("S", [BAL, 4, 1])
@@ -579,7 +622,9 @@ def test_multi_verify_workload_sampled_rows(B):
         a, b_ = outs[S], outs[1]
         assert torch.all((a[0].float() - b_[0].float()).abs() <= 2e-2 + 2e-2 * b_[0].float().abs())
         assert torch.all((a[1] - b_[1]).abs() <= 2e-3)
-    assert torch.equal(outs[BAL][0].view(torch.int16), outs[0][0].view(torch.int16))  # AUTO = balanced
+    s_auto = B.paged_decode_num_splits(dims, 0)  # AUTO runs exactly the mode it resolves to
+    assert s_auto in outs
+    assert torch.equal(outs[s_auto][0].view(torch.int16), outs[0][0].view(torch.int16))
 
 
 @pytest.mark.parametrize("lens", [[(i * 613) % 3500 + 1 for i in range(30)] + [0, 3], [700, 2, 0, 3000, 64]])
