@@ -212,6 +212,9 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
  *  - 1 (direct output) for a BF16 cache with head_dim >= 64 when the items
  *    number exactly the current device's compute units (one whole item per
  *    unit, nothing to merge);
+ *  - else 1 when no sequence can show more than 256 tokens
+ *    (max_pages_per_seq * page_size, or with a window window + q_len + 14,
+ *    whichever is smaller);
  *  - else PKD_SPLITS_BALANCED wherever it applies;
  *  - else 1 when the items alone fill the device's compute units, else a split
  *    count in [2, PKD_MAX_SPLITS] bounded by the longest sequence expected,

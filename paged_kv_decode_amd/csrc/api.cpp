@@ -186,6 +186,11 @@ int32_t split_chunk(const pkd_dims& d, int S) {
 //    items: 4% faster at B = 32 with lengths 1024-4096, 11% for 4 causal query
 //    tokens, 24% with a 1024-token window, a tie for another length draw; with
 //    224 or 288 items, or an FP8 cache, the balanced partition was faster).
+//  - Direct output when no sequence can show more than 256 tokens (the block
+//    table's capacity, or the window's span): a whole item is then at most 16
+//    groups, which one workgroup streams in about the time the balanced
+//    partition takes to spread it and launch its merge (the two-sequence,
+//    112-token case: 8.5 against 16.4 us).
 //  - Otherwise the balanced partition wherever it applies (it balances any
 //    length mix and pays each workgroup's start-up once).
 //  - Otherwise direct output when the items alone fill the device, else
@@ -194,6 +199,7 @@ int32_t heuristic_splits(const pkd_dims& d, int32_t max_len) {
   const int cus = current_cu_count();
   const int64_t items = (int64_t)d.batch * d.num_kv_heads * head_groups(d);
   if (d.kv_dtype == PKD_DTYPE_BF16 && d.head_dim >= 64 && cus > 0 && items == cus) return 1;
+  if (visible_span(d) <= 256) return 1;
   if (balanced_ok(d)) return PKD_SPLITS_BALANCED;
   const int64_t target = 4LL * (cus > 0 ? cus : 256);  // workgroups to keep every CU busy
   if (items <= 0 || items >= target) return 1;

@@ -218,9 +218,11 @@ def test_two_phase_argument_checks():
 
 
 def test_heuristic_choices():
-    """The balanced partition wherever it applies; otherwise one split when the
-    (sequence, KV-head) items already fill the device, else a split count
-    bounded by the cap and by the length hint."""
+    """Without a device (so without the one-item-per-compute-unit rule, which
+    the GPU tests cover): one split when no sequence can show more than 256
+    tokens; the balanced partition wherever it applies; otherwise one split
+    when the (sequence, KV-head) items already fill the device, else a split
+    count bounded by the cap and by the length hint."""
     b128 = dims(batch=128, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
                 num_pages=2048, max_pages_per_seq=16)
     assert b.paged_decode_num_splits(b128, 0) == b.PKD_SPLITS_BALANCED
@@ -239,8 +241,14 @@ def test_heuristic_choices():
     s1 = b.paged_decode_num_splits(long1, 0)
     assert s_odd < s1 <= b.PKD_MAX_SPLITS
     assert b.paged_decode_num_splits(long1, 256) == 1  # a short hint caps the split count
-    tiny = dims()
-    assert b.paged_decode_num_splits(tiny, 0) == b.PKD_SPLITS_BALANCED
+    tiny = dims()  # 7 pages of 16 tokens
+    assert b.paged_decode_num_splits(tiny, 0) == 1
+    assert b.paged_decode_num_splits(dims(max_pages_per_seq=16), 0) == 1  # 256 tokens
+    assert b.paged_decode_num_splits(dims(max_pages_per_seq=17), 0) == b.PKD_SPLITS_BALANCED
+    # a window bounds the span: 200 + 1 + 14 = 215 visible tokens of a 4096-token table
+    assert b.paged_decode_num_splits(dims(max_pages_per_seq=256, num_pages=512, window=200), 0) == 1
+    assert b.paged_decode_num_splits(dims(max_pages_per_seq=256, num_pages=512, window=300), 0) == \
+        b.PKD_SPLITS_BALANCED
 
 
 def test_balanced_mode_rules():
