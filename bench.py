@@ -494,6 +494,23 @@ def summarize_trace(stats_csv, workload, command, out_name):
         fh.write("\n".join(lines) + "\n")
 
 
+def trace_avg_from_profiles(name, kernel_prefix):
+    """Average duration (us) of the kernel whose name starts with kernel_prefix
+    in the committed rocprofv3 kernel-trace summary of workload name, or None.
+    The trace times the kernel alone; the bench's events add the dispatch gap."""
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path, encoding="utf-8"):
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) > 4 and cells[1].strip("`").startswith(kernel_prefix):
+            try:
+                return float(cells[3])
+            except ValueError:
+                return None
+    return None
+
+
 def traffic_from_profiles(name):
     """Measured HBM bytes per launch of the partition kernel, if a counter summary
     for this workload and the current kernel source is committed under profiles/
@@ -616,7 +633,10 @@ def main():
                                 if p["num_splits"] == -1000 else "split_kv_kernel<128, bf16, direct>"
                                 if p["num_splits"] == 1 else "split_kv_kernel<128, bf16, partials>"),
                      "kernel_ms": p["split_kernel_ms"],
-                     "kernel_bytes": p["split_kernel_bytes"]},
+                     "kernel_bytes": p["split_kernel_bytes"],
+                     "trace_avg_us": trace_avg_from_profiles(
+                         PRIMARY, "pkd::balanced_kernel<128" if p["num_splits"] == -1000
+                         else "pkd::split_kv_kernel<128")},
         "workloads": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in results.items()},
     }
