@@ -394,10 +394,27 @@ def cpu_baseline(w, nbytes):
                 break
     except OSError:
         pass
+    # The same oracle on one thread, for a bounded sample: the first sequences
+    # of the step, whole passes until about CPU_SAMPLE_S seconds have run.
+    sub = max(1, w.spec.batch // 8)
+    sub_lens = [int(x) for x in w.seq_lens[:sub]]
+    sub_bytes = nbytes * sum(sub_lens) / max(1, int(w.seq_lens.sum()))  # K/V dominate; scaled by tokens
+    passes1 = 0
+    t1 = time.perf_counter()
+    while True:
+        oracle.paged_decode(w.q[:sub], w.k_cache, w.v_cache, w.block_table[:sub], w.seq_lens[:sub], w.scale,
+                            w.k_scale, w.v_scale, nthreads=1)
+        passes1 += 1
+        if time.perf_counter() - t1 >= CPU_SAMPLE_S:
+            break
+    dt1 = (time.perf_counter() - t1) / passes1
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"whole {w.spec.name} step (all {w.spec.batch} sequences x {w.spec.num_q_heads} "
                       f"heads), mean of {passes} passes ({passes * dt:.1f} s), fp64, {threads} threads on {model}",
-            "seconds": dt, "passes": passes, "queries_per_s": w.spec.batch / dt}
+            "seconds": dt, "passes": passes, "queries_per_s": w.spec.batch / dt,
+            "single_thread": {"value": sub_bytes / dt1 / 1e9, "unit": "GB/s", "cores": 1,
+                              "sample": f"the first {sub} sequences of the step ({sum(sub_lens)} tokens, bytes "
+                                        f"scaled by tokens), mean of {passes1} passes ({passes1 * dt1:.1f} s)"}}
 
 
 # The sources the partition kernels are built from (their digest tags the counter summaries).
