@@ -180,7 +180,7 @@ def test_workspace_grows_with_query_tokens():
 
 def test_valid_call_without_gpu_reports_no_device():
     """With correct arguments and no usable GPU the library reports it instead of
-    computing anything (on a GPU machine this case is covered by the GPU tests)."""
+    computing anything (with a GPU present this case is covered by the GPU tests)."""
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
