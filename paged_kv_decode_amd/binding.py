@@ -43,7 +43,8 @@ PKD_DTYPE_FP8_E4M3 = 1
 EXPORTED = ("paged_decode", "paged_decode_partition", "paged_decode_finish", "paged_decode_num_splits",
             "paged_decode_launches", "paged_decode_workspace_bytes", "paged_decode_partials", "paged_decode_merge",
             "paged_decode_check_tables", "paged_kv_append", "paged_decode_metadata", "contiguous_decode",
-            "contiguous_decode_workspace_bytes", "paged_decode_status_string")
+            "contiguous_decode_workspace_bytes", "paged_decode_status_string", "pkd_stream_read",
+            "pkd_stream_read_sink_bytes")
 
 
 class PkdError(RuntimeError):
@@ -139,6 +140,10 @@ _lib.contiguous_decode.argtypes = [ctypes.POINTER(pkd_contig_dims), _p, _p, _p, 
 _lib.contiguous_decode.restype = _i32
 _lib.contiguous_decode_workspace_bytes.argtypes = [ctypes.POINTER(pkd_contig_dims), _i32]
 _lib.contiguous_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.pkd_stream_read.argtypes = [_p, ctypes.c_int64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]
+_lib.pkd_stream_read.restype = _i32
+_lib.pkd_stream_read_sink_bytes.argtypes = [_i32, _i32]
+_lib.pkd_stream_read_sink_bytes.restype = ctypes.c_size_t
 _lib.paged_decode_status_string.argtypes = [_i32]
 _lib.paged_decode_status_string.restype = ctypes.c_char_p
 
@@ -236,6 +241,17 @@ def contiguous_decode(cd, q, k, v, seq_lens, k_scale, v_scale, sinks, scale, out
 
 def contiguous_decode_workspace_bytes(cd, num_splits: int) -> int:
     return _lib.contiguous_decode_workspace_bytes(None if cd is None else ctypes.byref(cd), int(num_splits))
+
+
+def pkd_stream_read(buf, nbytes, row_bytes, chunk_bytes, pattern, workgroups, waves, batch_kb, nontemporal, sink,
+                    stream) -> int:
+    return _lib.pkd_stream_read(_ptr(buf), int(nbytes), int(row_bytes), int(chunk_bytes), int(pattern),
+                                int(workgroups), int(waves), int(batch_kb), int(nontemporal), _ptr(sink),
+                                _ptr(stream))
+
+
+def pkd_stream_read_sink_bytes(workgroups, waves) -> int:
+    return _lib.pkd_stream_read_sink_bytes(int(workgroups), int(waves))
 
 
 def paged_decode_status_string(status: int) -> str:

@@ -137,7 +137,8 @@ split_kv_kernel(const SplitParams p) {
       for (int q = 0; q < C::NGRP; ++q) P.pg[q] = page_of((min(tb + 16 * q, lim) & ~15) / ps);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::NBLK + C::NV; ++i) P.pg[i] = page_of(min(tb + A.generic_row(i), lim) / ps);
+      for (int i = 0; i < (C::KLDS ? C::NV : C::NBLK + C::NV); ++i)
+        P.pg[i] = page_of(min(tb + A.generic_row(i), lim) / ps);
     }
   };
   auto issue = [&](int tile, const Pages& P, TileRegs<D, FP8>& R, bool idle) {
@@ -148,7 +149,7 @@ split_kv_kernel(const SplitParams p) {
       A.issue_generic(p.k, p.v, tb, lim, P.pg, ps, tok_stride, page_stride, head_off, R, idle);
   };
 
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;  // this wave's V[TT][VS]
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::WT;  // this wave's V[TT][VS] (and K[TT][KS])
   // Tiles wave, wave + 4, wave + 8, ...
   run_tiles<D, FP8, Pages>(A, wave, kWaves, ntiles, s0, lr, vs, fetch, issue);
 
@@ -199,7 +200,7 @@ balanced_kernel(const BalancedParams p) {
   // Without a window (the instance for window = 0) nothing of it stays live.
   const int win = WINDOW ? p.window : 0;
   typedef TilePages<D, FP8, true> Pages;
-  constexpr int VT_BYTES = NWV * C::TT * C::VS * 2;                 // wave-private V tiles
+  constexpr int VT_BYTES = NWV * C::WT * 2;                         // wave-private V (and K) tiles
   constexpr int MERGE_BYTES = NWV * 16 * (2 + C::OW_STRIDE) * 4 + 16 * (NWV + 4) * 4;  // combine staging
   constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
@@ -299,7 +300,7 @@ balanced_kernel(const BalancedParams p) {
 
   WaveAttn<D, FP8> A;
   A.init_lane(tid & 63);
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::TT * C::VS;
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * C::WT;
   const int ps = p.page_size;
   const int tok_stride = Geo::tok_stride(p);
   const int64_t page_stride = Geo::page_stride(p);

@@ -15,9 +15,11 @@
 //   2. has issued the tile's 16-byte K/V loads one tile earlier (register
 //      double buffering: the next tile's loads are in flight while this one
 //      computes),
-//   3. writes V row-major into a wave-private LDS tile,
-//   4. QK^T on MFMA (v_mfma_f32_16x16x32_bf16): A = 16 K rows x 32 dims straight
-//      from the load registers, B = the packed query heads (zero-padded to 16),
+//   3. writes V (and K, for rows of a 128-byte line or more) row-major into
+//      wave-private LDS tiles: those loads read whole lines of consecutive rows,
+//   4. QK^T on MFMA (v_mfma_f32_16x16x32_bf16): A = 16 K rows x 32 dims read
+//      from the LDS tile (or, for shorter rows, loaded straight in that layout),
+//      B = the packed query heads (zero-padded to 16),
 //   5. online softmax in base 2 with the running max shared across the four
 //      lane groups by cross-lane xor shuffles,
 //   6. PV on MFMA: A = V^T gathered by transposing LDS reads
@@ -86,9 +88,23 @@ struct Cfg {
   static constexpr int RPI = 64 / CPR;                     // rows per V load instruction (<= 16)
   static constexpr int NV = TT * ROWB / (64 * VLB);        // V loads per lane per tile
   static constexpr int VS = D + 16;                        // V tile LDS row stride (bf16 elements)
+  // K rows of at least one 128-byte line are loaded like V (each instruction
+  // reads whole lines of consecutive rows) and staged in LDS, from where the
+  // matrix-core operand (16 rows x 32 dims, a row per lane) is read.  Loaded
+  // straight in the operand layout, every instruction would read half lines of
+  // 16 rows, a pattern a plain read stream measured about 20% slower than whole
+  // lines.  Shorter rows (64 bytes) are whole lines in the operand layout too
+  // and are loaded straight into it.  FP8 K stays in registers: its tile loop is
+  // bound by instruction issue (the code conversions), and staging measured
+  // slower there (B = 64: 128.4 -> 134.6 us).
+  static constexpr bool KLDS = !FP8 && ROWB >= 128;
+  static constexpr int KS = D + 8;                         // K tile LDS row stride (bf16 elements)
+  static constexpr int NKL = KLDS ? NV : NBLK * NPIECE;    // K loads per lane per tile
+  static constexpr int KLOAD = KLDS ? VLB : KLB;           // bytes per K load
+  static constexpr int WT = TT * VS + (KLDS ? TT * KS : 0);  // LDS elements of one wave's tiles (V, then K)
   static constexpr int NB = D / 16;                        // PV output blocks of 16 dims
   static constexpr int NGRP = TT / 16;                     // 16-token groups per tile
-  static constexpr int VT_BYTES = kWaves * TT * VS * 2;
+  static constexpr int VT_BYTES = kWaves * WT * 2;
   static constexpr int BT_OFFSET = VT_BYTES;                // staged block-table entries
   static constexpr int BT_ENTRIES = 512;
   static constexpr int OW_STRIDE = D + 4;                  // merge staging row stride (floats)
@@ -186,7 +202,9 @@ __device__ __forceinline__ int s_out_token(int blk, int g, int i) {
 template <int D, bool FP8>
 struct TileRegs {
   typedef Cfg<D, FP8> C;
-  typename VecT<C::KLB>::T k[C::NBLK][C::NPIECE];
+  // K: load i covers the rows of V load i (KLDS), or piece pc of row block
+  // blk at i = blk * NPIECE + pc (operand layout).
+  typename VecT<C::KLOAD>::T k[C::NKL];
   typename VecT<C::VLB>::T v[C::NV];
 };
 
@@ -195,7 +213,9 @@ struct TileRegs {
 template <int D, bool FP8, bool PAGED16>
 struct TilePages {
   typedef Cfg<D, FP8> C;
-  int pg[PAGED16 ? C::NGRP : C::NBLK + C::NV];  // PAGED16: per 16-token group; else per K / V row
+  // PAGED16: per 16-token group; else per row a lane loads (K rows in the
+  // operand layout, then V rows; or V rows alone, which K shares, with KLDS).
+  int pg[PAGED16 ? C::NGRP : (C::KLDS ? C::NV : C::NBLK + C::NV)];
 };
 
 
@@ -203,6 +223,18 @@ struct TilePages {
 // maximum before the reference is raised: softmax weights then stay at most
 // 2^8, far inside the range of the bf16 P operand and the fp32 sums.
 constexpr float kRescaleSlack = 8.f;
+
+// First of the 8 dims lane group g contributes to QK MFMA kk.  K staged in LDS
+// is read as dims kk * 32 + g * 8 .. + 8; K loaded straight into the operand
+// layout takes dims (kk / R) * 4 * PIECE + g * PIECE + (kk % R) * 8 .., those
+// its 16-byte (or 8-byte) piece of a row holds.  q uses the same assignment,
+// so each MFMA sums the products of matching dims.
+template <int D, bool FP8>
+__device__ __forceinline__ int q_dim0(int kk, int g) {
+  typedef Cfg<D, FP8> C;
+  if constexpr (C::KLDS) return kk * 32 + g * 8;
+  else return (kk / C::R) * 4 * C::PIECE + g * C::PIECE + (kk % C::R) * 8;
+}
 
 // Per-wave attention state and tile operations, shared by both launch shapes.
 // Lane (n, g) = (lane % 16, lane / 16) in the MFMA operand layouts.
@@ -232,8 +264,8 @@ struct WaveAttn {
     v_doff = (lane % C::CPR) * C::VLB;
   }
 
-  // Lane (n, g) holds packed row n's dims (kk / R) * 4 * PIECE + g * PIECE + (kk % R) * 8 + [0, 8)
-  // for MFMA kk; the K loads use the same dim assignment.  qrow_n is the memory
+  // Lane (n, g) holds packed row n's dims q_dim0(kk, g) + [0, 8) for MFMA kk;
+  // the K operand uses the same dim assignment.  qrow_n is the memory
   // row of packed row n (any valid row when hv is false); rows past the group are zero.
   // This lane's query row.  With paired KV heads (VK > 1) the wave's D dims are
   // VK real heads of DR = D / VK dims each; the row (of real head slice s)
@@ -244,7 +276,7 @@ struct WaveAttn {
     constexpr int DR = D / VK;
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
-      const int d0 = (kk / C::R) * 4 * C::PIECE + g * C::PIECE + (kk % C::R) * 8;
+      const int d0 = q_dim0<D, FP8>(kk, g);
       const bool mine = VK == 1 || d0 / DR == s;
       Ld16 raw = Ld16{0, 0, 0, 0};
       if (hv && mine) raw = *reinterpret_cast<const Ld16*>(qrow + (d0 - s * DR));
@@ -278,8 +310,17 @@ struct WaveAttn {
       gbase[q] = (int64_t)page * page_stride + (int64_t)(gt - (gt / ps) * ps) * tok_stride + head_off;
       glim[q] = lim - gt;
     }
+    if constexpr (C::KLDS) {
+      // K rows are loaded exactly like V rows (whole lines per instruction).
 #pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk) {
+      for (int i = 0; i < C::NV; ++i) {
+        const int q = (i * C::RPI) >> 4;
+        const int rig = ((i * C::RPI) & 15) + v_rig;
+        R.k[i] = gload<C::VLB>(kc + gbase[q] + min(rig, glim[q]) * tok_stride + v_doff);
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < (C::KLDS ? 0 : C::NBLK); ++blk) {
       int64_t base;
       int gl;
       if constexpr (C::KP == 32) {
@@ -294,7 +335,8 @@ struct WaveAttn {
       }
       const uint8_t* src = kc + base + min(k_rig[blk], gl) * tok_stride + k_doff;
 #pragma unroll
-      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = kload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
+      for (int pc = 0; pc < C::NPIECE; ++pc)
+        R.k[blk * C::NPIECE + pc] = kload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
     }
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
@@ -305,23 +347,35 @@ struct WaveAttn {
   }
 
   // Any page size: pages[blk] is the page of this lane's K row of row block
-  // blk, pages[NBLK + i] that of its row of V load i (rows clamped to lim).
+  // blk, pages[NBLK + i] that of its row of V load i (rows clamped to lim);
+  // with KLDS, pages[i] is the page of its row of V load i, which K shares.
   __device__ __forceinline__ void issue_generic(const uint8_t* kc, const uint8_t* vc, int tb, int lim,
                                                 const int* pages, int ps, int tok_stride, int64_t page_stride,
                                                 int64_t head_off, Regs& R, bool idle) const {
+    constexpr int VP = C::KLDS ? 0 : C::NBLK;  // index of the first V row's page
+    if constexpr (C::KLDS) {
 #pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk) {
+      for (int i = 0; i < C::NV; ++i) {
+        const int tok = min(tb + i * C::RPI + v_rig, lim);
+        const int64_t off = (int64_t)(idle ? 0 : pages[i]) * page_stride +
+                            (int64_t)(tok - (tok / ps) * ps) * tok_stride + head_off;
+        R.k[i] = gload<C::VLB>(kc + off + v_doff);
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < (C::KLDS ? 0 : C::NBLK); ++blk) {
       const int tok = min(tb + k_row_token<C::KP>(blk, n), lim);
       const int64_t off = (int64_t)(idle ? 0 : pages[blk]) * page_stride + (int64_t)(tok - (tok / ps) * ps) * tok_stride +
                           head_off;
       const uint8_t* src = kc + off + k_doff;
 #pragma unroll
-      for (int pc = 0; pc < C::NPIECE; ++pc) R.k[blk][pc] = kload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
+      for (int pc = 0; pc < C::NPIECE; ++pc)
+        R.k[blk * C::NPIECE + pc] = kload<C::KLB>(src + pc * 4 * C::PIECE * C::ELEM);
     }
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) {
       const int tok = min(tb + i * C::RPI + v_rig, lim);
-      const int64_t off = (int64_t)(idle ? 0 : pages[C::NBLK + i]) * page_stride +
+      const int64_t off = (int64_t)(idle ? 0 : pages[VP + i]) * page_stride +
                           (int64_t)(tok - (tok / ps) * ps) * tok_stride + head_off;
       R.v[i] = gload<C::VLB>(vc + off + v_doff);
     }
@@ -329,32 +383,48 @@ struct WaveAttn {
 
   // Tokens (relative to tb) whose pages the generic path needs, per lane.
   __device__ __forceinline__ int generic_row(int idx) const {
+    if constexpr (C::KLDS) return idx * C::RPI + v_rig;
     return idx < C::NBLK ? k_row_token<C::KP>(idx, n) : (idx - C::NBLK) * C::RPI + v_rig;
   }
 
-  // One tile: V to LDS, QK^T, online softmax, PV.  Tokens before s_lo or at or
+  // One row-pattern load (V, or K with KLDS) into a row-major bf16 LDS tile of
+  // row stride STRIDE: lane `lane` of load i holds row (i * 64 + lane) / CPR,
+  // elements VEPL * ((i * 64 + lane) % CPR) ..; FP8 codes are widened to bf16
+  // (exactly).
+  template <int STRIDE>
+  __device__ __forceinline__ void stage_rows(const typename VecT<C::VLB>::T& raw, int i, uint16_t* tile) const {
+    const int lin = i * 64 + lane;
+    uint16_t* dst = tile + (lin / C::CPR) * STRIDE + (lin % C::CPR) * C::VEPL;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int h = 0; h < C::VEPL / 8; ++h) {
+        u32x2 c8;
+        c8[0] = raw[2 * h];
+        c8[1] = raw[2 * h + 1];
+        *reinterpret_cast<bf16x8*>(dst + 8 * h) = fp8x8_to_bf16(c8);
+      }
+    } else if constexpr (C::VLB == 16) {
+      *reinterpret_cast<u32x4*>(dst) = raw;
+    } else {
+      *reinterpret_cast<u32x2*>(dst) = raw;
+    }
+  }
+
+  // One tile: V (and K) to LDS, QK^T, online softmax, PV.  Tokens before s_lo or at or
   // past s1 (this lane's packed row's window start and end) are masked.
   // lo_all and hi_all (uniform) bound every lane's s_lo from above and s1 from
   // below: tiles starting at lo_all or later skip the lower-bound test, and
   // tiles inside [lo_all, hi_all) skip masking altogether.
   __device__ __forceinline__ void process(const Regs& R, int tb, int s_lo, int s1, int lo_all, int hi_all,
                                           uint16_t* vs) {
-    // V -> LDS, row-major bf16 (16-byte writes).
+    // V -> LDS, row-major bf16 (16-byte writes); K too when it is staged there.
 #pragma unroll
-    for (int i = 0; i < C::NV; ++i) {
-      const int lin = i * 64 + lane;
-      uint16_t* dst = vs + (lin / C::CPR) * C::VS + (lin % C::CPR) * C::VEPL;
-      if constexpr (FP8) {
+    for (int i = 0; i < C::NV; ++i) stage_rows<C::VS>(R.v[i], i, vs);
+    uint16_t* ks = vs + C::TT * C::VS;  // this wave's K[TT][KS] (KLDS)
+    if constexpr (C::KLDS) {
 #pragma unroll
-        for (int h = 0; h < C::VEPL / 8; ++h) {
-          u32x2 c8;
-          c8[0] = R.v[i][2 * h];
-          c8[1] = R.v[i][2 * h + 1];
-          *reinterpret_cast<bf16x8*>(dst + 8 * h) = fp8x8_to_bf16(c8);
-        }
-      } else {
-        *reinterpret_cast<u32x4*>(dst) = R.v[i];
-      }
+      for (int i = 0; i < C::NV; ++i) stage_rows<C::KS>(R.k[i], i, ks);
+      wave_lds_sync();  // the K and V tiles are complete in LDS
     }
 
     // S^T = K Q^T for each 16-row block.
@@ -365,14 +435,17 @@ struct WaveAttn {
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk) {
         bf16x8 a;
-        if constexpr (FP8) {
-          const auto& raw = R.k[blk][kk / C::R];
+        if constexpr (C::KLDS) {
+          // Row n of the block, dims kk * 32 + g * 8 .. + 8 (ds_read_b128).
+          a = *reinterpret_cast<const bf16x8*>(ks + k_row_token<C::KP>(blk, n) * C::KS + kk * 32 + g * 8);
+        } else if constexpr (FP8) {
+          const auto& raw = R.k[blk * C::NPIECE + kk / C::R];
           u32x2 c8;
           c8[0] = raw[2 * (kk % C::R)];
           c8[1] = raw[2 * (kk % C::R) + 1];
           a = fp8x8_to_bf16(c8);
         } else {
-          a = bit_cast_dev<bf16x8>(R.k[blk][kk]);
+          a = bit_cast_dev<bf16x8>(R.k[blk * C::NPIECE + kk]);
         }
         sacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc[blk], 0, 0, 0);
       }
@@ -439,7 +512,7 @@ struct WaveAttn {
       }
     l_run += psum;
 
-    wave_lds_sync();  // the V tile is complete in LDS
+    if constexpr (!C::KLDS) wave_lds_sync();  // the V tile is complete in LDS
 
     // O^T += V^T P^T; the V^T operand comes from transposing LDS reads.
     if constexpr (C::KP == 32) {

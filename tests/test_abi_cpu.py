@@ -20,9 +20,15 @@ FAKE = 0x1000  # a non-NULL address that is never dereferenced on these paths
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    """Every function declared in the public headers (include/*.h)."""
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if not h.endswith(".h"):
+            continue
+        text = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def header_defines():
@@ -383,3 +389,25 @@ def test_contiguous_pointer_and_scale_rules():
     assert ccall(cdims(), S=3, ws=None, ws_bytes=0) == b.PKD_ERR_WORKSPACE
     assert ccall(cdims()) == b.PKD_ERR_DEVICE  # valid arguments reach the device check
     assert ccall(cdims(batch=0)) == b.PKD_OK
+
+
+def test_stream_read_argument_checks():
+    """The measurement stream kernel rejects bad shapes on the host."""
+    sink = FAKE
+    ok = dict(buf=FAKE, nbytes=1 << 20, row_bytes=2048, chunk_bytes=256, pattern=0, workgroups=8, waves=4,
+              batch_kb=8, nontemporal=1, sink=sink, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return b.pkd_stream_read(a["buf"], a["nbytes"], a["row_bytes"], a["chunk_bytes"], a["pattern"],
+                                 a["workgroups"], a["waves"], a["batch_kb"], a["nontemporal"], a["sink"], a["stream"])
+    assert call(buf=None) == b.PKD_ERR_NULL_POINTER
+    assert call(sink=None) == b.PKD_ERR_NULL_POINTER
+    assert call(buf=FAKE + 8) == b.PKD_ERR_ALIGNMENT
+    for kw in (dict(chunk_bytes=48), dict(chunk_bytes=8), dict(row_bytes=1000), dict(nbytes=2048 * 3 + 1024),
+               dict(pattern=2), dict(waves=9), dict(workgroups=0), dict(batch_kb=12), dict(nontemporal=2),
+               dict(pattern=1, chunk_bytes=32), dict(pattern=1, nbytes=2048 * 8)):
+        assert call(**kw) == b.PKD_ERR_BAD_DIMS, kw
+    assert b.pkd_stream_read_sink_bytes(256, 4) == 256 * 4 * 64 * 4
+    assert b.pkd_stream_read_sink_bytes(0, 4) == 0

@@ -46,26 +46,38 @@ def test_trace_average_is_read_from_the_committed_summary():
 
 
 def test_traffic_is_dropped_when_the_kernel_sources_change(tmp_path, monkeypatch):
-    """The committed traffic figure is used only while the digest of the
+    """A traffic figure under profiles/ is used only while the digest of the
     kernels' sources matches the one it was taken with."""
-    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_llama_b32_d128_ps64.json")))
-    assert rec["kernel_source_sha256"] == bench._source_digest()
-    assert bench.traffic_from_profiles("llama_b32_d128_ps64") == rec["bytes_per_launch"]
     prof = tmp_path / "profiles"
     prof.mkdir()
-    stale = dict(rec, kernel_source_sha256="0" * 64)
-    (prof / "traffic_llama_b32_d128_ps64.json").write_text(json.dumps(stale))
+    rec = {"workload": "llama_b32_d128_ps64", "bytes_per_launch": 123456789.0,
+           "kernel_source_sha256": bench._source_digest()}
+    (prof / "traffic_llama_b32_d128_ps64.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.traffic_from_profiles("llama_b32_d128_ps64") == 123456789.0
+    (prof / "traffic_llama_b32_d128_ps64.json").write_text(json.dumps(dict(rec, kernel_source_sha256="0" * 64)))
     assert bench.traffic_from_profiles("llama_b32_d128_ps64") is None
+    assert bench.traffic_from_profiles("no_such_workload") is None
 
 
 @pytest.mark.parametrize("src", ["/* a comment */\n", "// another\n", "\n\n   \n"])
 def test_digest_ignores_comments_and_whitespace(tmp_path, monkeypatch, src):
+    want = bench._source_digest()
     files = []
     for f in bench.KERNEL_SRCS:
         p = tmp_path / os.path.basename(f)
         p.write_text(open(f, encoding="utf-8").read() + src)
         files.append(str(p))
     monkeypatch.setattr(bench, "KERNEL_SRCS", files)
-    assert bench._source_digest() == json.load(
-        open(os.path.join(ROOT, "profiles", "traffic_llama_b32_d128_ps64.json")))["kernel_source_sha256"]
+    assert bench._source_digest() == want
+
+
+def test_digest_changes_with_the_code(tmp_path, monkeypatch):
+    want = bench._source_digest()
+    files = []
+    for i, f in enumerate(bench.KERNEL_SRCS):
+        p = tmp_path / os.path.basename(f)
+        p.write_text(open(f, encoding="utf-8").read() + ("\nint extra_symbol;\n" if i == 0 else ""))
+        files.append(str(p))
+    monkeypatch.setattr(bench, "KERNEL_SRCS", files)
+    assert bench._source_digest() != want
