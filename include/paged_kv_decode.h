@@ -210,8 +210,8 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
  * Work items are (sequence, KV head, head group), a head group being up to 16
  * of a KV head's q_len * G query rows.
  *  - 1 (direct output) for a BF16 cache with head_dim >= 64 when the items
- *    number exactly the current device's compute units (one whole item per
- *    unit, nothing to merge);
+ *    number between three quarters of the current device's compute units and
+ *    all of them (one whole item per unit, nothing to merge);
  *  - else 1 when no sequence can show more than 256 tokens
  *    (max_pages_per_seq * page_size, or with a window window + q_len + 14,
  *    whichever is smaller);

@@ -178,14 +178,15 @@ int32_t split_chunk(const pkd_dims& d, int S) {
 
 // The split mode for PKD_SPLITS_AUTO.
 //  - Direct output (one split) when a bf16 cache whose head rows are at least
-//    128 bytes has exactly one (sequence, KV head, head group) item per compute
-//    unit: each unit streams one whole item and nothing is merged.  There the
-//    balanced partition's even cuts give most workgroups two pieces, and the
-//    second piece's combine, acknowledged partial store, count and merge cost
-//    more than the length imbalance that whole items leave (measured at 256
-//    items: 4% faster at B = 32 with lengths 1024-4096, 11% for 4 causal query
-//    tokens, 24% with a 1024-token window, a tie for another length draw; with
-//    224 or 288 items, or an FP8 cache, the balanced partition was faster).
+//    128 bytes has between three quarters of one and one (sequence, KV head,
+//    head group) item per compute unit: each unit streams one whole item and
+//    nothing is merged.  There the balanced partition's even cuts give most
+//    workgroups two pieces, and the second piece's combine, acknowledged
+//    partial store, count and merge cost more than the length imbalance that
+//    whole items leave (measured, lengths 1024-4096, 8 KV heads: direct output
+//    faster by 2.5% at 192 items and by 5-7% at 224-256; with 264 items or
+//    more, where a second round of workgroups would follow, and for an FP8
+//    cache, the balanced partition was faster).
 //  - Direct output when no sequence can show more than 256 tokens (the block
 //    table's capacity, or the window's span): a whole item is then at most 16
 //    groups, which one workgroup streams in about the time the balanced
@@ -198,7 +199,8 @@ int32_t split_chunk(const pkd_dims& d, int S) {
 int32_t heuristic_splits(const pkd_dims& d, int32_t max_len) {
   const int cus = current_cu_count();
   const int64_t items = (int64_t)d.batch * d.num_kv_heads * head_groups(d);
-  if (d.kv_dtype == PKD_DTYPE_BF16 && d.head_dim >= 64 && cus > 0 && items == cus) return 1;
+  if (d.kv_dtype == PKD_DTYPE_BF16 && d.head_dim >= 64 && cus > 0 && items <= cus && 4 * items >= 3LL * cus)
+    return 1;
   if (visible_span(d) <= 256) return 1;
   if (balanced_ok(d)) return PKD_SPLITS_BALANCED;
   const int64_t target = 4LL * (cus > 0 ? cus : 256);  // workgroups to keep every CU busy

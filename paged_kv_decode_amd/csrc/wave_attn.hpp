@@ -71,9 +71,12 @@ template <int D, bool FP8>
 struct Cfg {
   static constexpr int ELEM = FP8 ? 1 : 2;                 // bytes per cached element
   static constexpr int ROWB = D * ELEM;                    // bytes of one token's row for one KV head
-  // Tokens per wave tile: 4096 / D (8 KiB of K and 8 KiB of V for bf16, half
-  // that for fp8), which keeps two tiles of loads per wave within registers.
-  static constexpr int TT = 4096 / D;
+  // Tokens per wave tile: 2048 / D for bf16 (4 KiB of K and 4 KiB of V, at
+  // least 16 tokens) and 4096 / D for fp8 (4 KiB of codes each).  Two tiles of
+  // loads are in flight per wave; with 8 KiB tiles instead, the B = 32 and
+  // B = 128 steps measured 1-2 us slower (a read stream likewise ran faster
+  // with 8-16 KiB in flight per wave than with 16-32 KiB).
+  static constexpr int TT = FP8 ? 4096 / D : (2048 / D > 16 ? 2048 / D : 16);
   static constexpr int NBLK = TT / 16;                     // QK MFMA row blocks per tile
   static constexpr int KP = TT >= 32 ? 32 : 16;            // tokens per PV MFMA (its K depth)
   static constexpr int NCH = TT / KP;                      // PV chunks per tile
