@@ -82,12 +82,15 @@ class Runner:
         self.ks = None if w.k_scale is None else w.k_scale.to(device)
         self.vs = None if w.v_scale is None else w.v_scale.to(device)
         self.sinks = None if getattr(w, "sinks", None) is None else w.sinks.to(device)
-        self.dims = B.dims_for(self.q, self.k, self.bt, causal=w.spec.causal, window=w.spec.window)
-        self.S = num_splits if num_splits != 0 else B.paged_decode_num_splits(self.dims, 0)
-        self.launches = B.paged_decode_launches(self.dims, self.S)  # 1: the partition writes out itself
+        self.dims = B.dims_for(self.q, self.k, self.bt)
+        self.ext = B.ext_for(self.q, causal=w.spec.causal, window=w.spec.window)
+        self.S = num_splits if num_splits != 0 else B.paged_decode_num_splits_ext(self.dims, self.ext, 0)
+        self.launches = B.paged_decode_launches(self.dims, self.ext, self.S)  # 1: the partition writes out itself
+        # plain decode in a numbered split mode goes through paged_decode itself
+        self.plain = self.ext is None and self.sinks is None and 1 <= self.S <= B.PKD_MAX_SPLITS
         self.out = torch.empty(self.q.shape, dtype=torch.bfloat16, device=device)
         self.lse = torch.empty(self.q.shape[:-1], dtype=torch.float32, device=device)
-        self.ws_bytes = B.paged_decode_workspace_bytes(self.dims, self.S)
+        self.ws_bytes = B.paged_decode_workspace_bytes_ext(self.dims, self.ext, self.S)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
         self.stream = torch.cuda.current_stream(device)
         self.handle = self.stream.cuda_stream
@@ -96,11 +99,15 @@ class Runner:
         """The partition kernel: the whole of paged_decode when it is one kernel
         (direct output, or the balanced mode merging in place), else its first phase."""
         B = self.B
-        if self.launches == 1:
+        if self.launches == 1 and self.plain:
             st = B.paged_decode(self.dims, self.q, self.k, self.v, self.bt, self.lens, self.ks, self.vs,
-                                self.sinks, self.w.scale, self.out, self.lse, self.S, self.ws, self.ws_bytes, self.handle)
+                                self.w.scale, self.out, self.lse, self.S, self.ws, self.ws_bytes, self.handle)
+        elif self.launches == 1:
+            st = B.paged_decode_ext(self.dims, self.ext, self.q, self.k, self.v, self.bt, self.lens, self.ks,
+                                    self.vs, self.sinks, self.w.scale, self.out, self.lse, self.S, self.ws,
+                                    self.ws_bytes, self.handle)
         else:
-            st = B.paged_decode_partition(self.dims, self.q, self.k, self.v, self.bt, self.lens, self.ks,
+            st = B.paged_decode_partition(self.dims, self.ext, self.q, self.k, self.v, self.bt, self.lens, self.ks,
                                           self.vs, self.w.scale, self.S, self.ws, self.ws_bytes, self.handle)
         if st != 0:
             raise B.PkdError(st)
@@ -108,8 +115,8 @@ class Runner:
     def kernel2(self):
         """The merge kernel, when paged_decode uses one: its second phase."""
         if self.launches == 2:
-            st = self.B.paged_decode_finish(self.dims, self.S, self.ws, self.ws_bytes, self.sinks, self.out, self.lse,
-                                            self.handle)
+            st = self.B.paged_decode_finish(self.dims, self.ext, self.S, self.ws, self.ws_bytes, self.sinks, self.out,
+                                            self.lse, self.handle)
             if st != 0:
                 raise self.B.PkdError(st)
 

@@ -19,13 +19,13 @@
  * row (BF16 and FP8-E4M3 KV caches, GQA, "split-KV or direct output", a
  * persistent merge kernel).
  *
- * Several query tokens per sequence (dims.q_len > 1): the speculative-verify /
+ * Several query tokens per sequence (ext.q_len > 1, paged_decode_ext): the speculative-verify /
  * extend form that the same b12x row lists beside decode ("decode/verify",
  * "extend"), with the causal mask the AstrAI log expresses as the position of
  * the first query token.  Sequence b then has q_len query tokens, the last
  * q_len positions of the sequence: query token i sits at position
- * seq_lens[b] - q_len + i.  Without the mask (dims.causal = 0) every query
- * token attends over all seq_lens[b] tokens; with it (dims.causal = 1) query
+ * seq_lens[b] - q_len + i.  Without the mask (ext.causal = 0) every query
+ * token attends over all seq_lens[b] tokens; with it (ext.causal = 1) query
  * token i attends over positions <= seq_lens[b] - q_len + i only, and a token
  * that sees no position gets out = 0 and lse = -inf.  q, out and lse gain a
  * q_len dimension after the batch: row (b, i, h) of each is at
@@ -33,7 +33,7 @@
  * computed from one read of its K/V rows.
  *
  * Sliding window and attention sinks: two variants the same b12x row lists
- * for its paged attention.  With dims.window = W > 0, query token i (position
+ * for its paged attention.  With ext.window = W > 0, query token i (position
  * p = seq_lens[b] - q_len + i) sees only positions t > p - W, besides the
  * limit above (t < seq_lens[b], and t <= p with the causal mask); for plain
  * decode that is the last W tokens.  K/V rows below the lowest window start of
@@ -66,10 +66,12 @@
  *  - Device-side contents are the caller's contract: every block-table entry
  *    for a page a sequence uses (i < ceil(seq_lens[b] / page_size)) must lie
  *    in [0, num_pages), and 0 <= seq_lens[b] <= max_pages_per_seq * page_size.
- *    Entries past a sequence's last page are never read (they may hold -1), nor
- *    are cache slots past seq_lens[b] in its last page (they may hold
- *    anything, NaN included).  Violations are undefined behaviour;
- *    paged_decode_check_tables reports them.
+ *    Entries past a sequence's last page are never used: their values do not
+ *    matter (they may hold -1), although the kernels may load them, since
+ *    every row of block_table is read only within its max_pages_per_seq
+ *    entries.  Cache slots past seq_lens[b] in its last page never contribute
+ *    (they may hold anything, NaN included).  Violations are undefined
+ *    behaviour; paged_decode_check_tables reports them.
  *  - Outputs must not alias inputs.  Results are bitwise deterministic for
  *    fixed inputs and num_splits.
  *  - Alignment: q, k_cache, v_cache, out, workspace and o_part must be 16-byte
@@ -99,7 +101,7 @@ extern "C" {
 #define PKD_ERR_NUM_SPLITS (-7)      /* num_splits above PKD_MAX_SPLITS */
 #define PKD_ERR_WORKSPACE (-8)       /* workspace NULL or smaller than required */
 #define PKD_ERR_LAUNCH (-9)          /* the HIP runtime refused a launch */
-#define PKD_ERR_DEVICE (-10)         /* no usable gfx950 device is current */
+#define PKD_ERR_DEVICE (-10)         /* the current device is not a usable gfx950 */
 #define PKD_ERR_ALIGNMENT (-11)      /* a pointer is not aligned as required (see below) */
 
 /* Largest num_splits accepted. */
@@ -146,16 +148,25 @@ typedef struct {
   int32_t num_pages;          /* pages in the pool, >= 1 */
   int32_t max_pages_per_seq;  /* row length of block_table, >= 1 */
   int32_t kv_dtype;           /* a pkd_dtype */
+} pkd_dims;
+
+/* The extended forms (passed as a host pointer; NULL means q_len = 1, no mask,
+ * no window: plain decode). */
+typedef struct {
   int32_t q_len;              /* query tokens per sequence, 1..PKD_MAX_Q_LEN (1 = decode) */
   int32_t causal;             /* 0: every query token sees all tokens; 1: causal mask (above) */
   int32_t window;             /* 0: no window; W > 0: sliding window of W positions (above) */
-} pkd_dims;
+  int32_t reserved;           /* must be 0 */
+} pkd_ext;
 
 /*
- * paged_decode -- the whole decode-attention step (split-KV partition + merge).
+ * paged_decode -- the whole decode-attention step (split-KV partition + merge):
+ * the single paged_decode entry of the AstrAI log (the bullets on
+ * attn_pack_paged_params and on unifying the paged decode path), one query
+ * token per sequence.
  *
  *   dims         host; see pkd_dims.
- *   q            [B][q_len][Hq][D] bfloat16, contiguous ([B][Hq][D] when q_len = 1).
+ *   q            [B][Hq][D] bfloat16, contiguous.
  *   k_cache      [num_pages][page_size][Hkv][D] of kv_dtype, contiguous.
  *   v_cache      same layout as k_cache.
  *   block_table  [B][max_pages_per_seq] int32 physical page ids.
@@ -163,50 +174,69 @@ typedef struct {
  *   k_scale      [Hkv] fp32 dequantisation scales for an FP8 cache (K = code * k_scale[kv]);
  *                must be NULL for BF16.
  *   v_scale      [Hkv] fp32, as k_scale for V.
- *   sinks        [Hq] fp32 sink logits (above; -inf means no sink for that head), or NULL.
  *   scale        softmax scale applied to q.k (typically 1/sqrt(D)); included in lse.
- *   out          [B][q_len][Hq][D] bfloat16 result (fp32 accumulate, round-to-nearest-even).
- *   lse          [B][q_len][Hq] fp32 natural-log log-sum-exp of the scaled scores, or NULL.
- *   num_splits   PKD_SPLITS_AUTO: chosen by paged_decode_num_splits(dims, 0);
- *                1: direct output (one kernel); 2..PKD_MAX_SPLITS: split-KV + merge (two kernels);
- *                PKD_SPLITS_BALANCED: balanced partition, which merges the pieces of each
- *                (sequence, KV head) itself when few are expected (one kernel; see
- *                paged_decode_launches), else partition + merge (two kernels).
- *                Any other value is an error.
- *   workspace    device scratch for partials, at least paged_decode_workspace_bytes(dims,
- *                num_splits) bytes (may be NULL when that is 0).  Its contents on entry do
- *                not matter.
+ *   out          [B][Hq][D] bfloat16 result (fp32 accumulate, round-to-nearest-even).
+ *   lse          [B][Hq] fp32 natural-log log-sum-exp of the scaled scores, or NULL.
+ *   num_splits   <= 0: the heuristic's choice, paged_decode_num_splits(dims, 0) (the log's
+ *                compute_num_splits helper names such a choice but not its rule);
+ *                1: direct output (one kernel);
+ *                2..PKD_MAX_SPLITS: split-KV + merge (two kernels).  Above: PKD_ERR_NUM_SPLITS.
+ *   workspace    device scratch for partials (the log's alloc_split_partials bullet: taken per
+ *                call and never cleared), at least paged_decode_workspace_bytes(dims, num_splits)
+ *                bytes; may be NULL when that is 0.  Its contents on entry do not matter.
  *   workspace_bytes  size of workspace.
  *   stream       hipStream_t.
  * Returns PKD_OK or a negative status.
  */
 int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
-                     const float* v_scale, const float* sinks, float scale, void* out, float* lse,
-                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+                     const float* v_scale, float scale, void* out, float* lse, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * paged_decode_partition / paged_decode_finish -- the two phases of paged_decode
- * for a split mode (num_splits = 2..PKD_MAX_SPLITS or PKD_SPLITS_BALANCED, or
- * PKD_SPLITS_AUTO when it resolves to one of them; a resolution to direct output
- * is PKD_ERR_NUM_SPLITS here): the partition kernel writes its partials into
- * the workspace, then the merge kernel reads them and writes out and lse.
- * Issued back to back on one stream with the same dims, num_splits and
- * workspace they are exactly paged_decode; split apart they let a caller
- * schedule or time the phases.  Arguments as for paged_decode; the sinks are
- * folded in by paged_decode_finish.
+ * paged_decode_ext -- paged_decode with the extended forms and the special
+ * split modes.
+ *   ext          host; see pkd_ext (NULL: plain decode).  With q_len > 1, q is
+ *                [B][q_len][Hq][D], out [B][q_len][Hq][D] and lse [B][q_len][Hq].
+ *   sinks        [Hq] fp32 sink logits (above; -inf means no sink for that head), or NULL.
+ *   num_splits   PKD_SPLITS_AUTO: chosen by paged_decode_num_splits_ext(dims, ext, 0);
+ *                1: direct output; 2..PKD_MAX_SPLITS: split-KV + merge;
+ *                PKD_SPLITS_BALANCED: balanced partition, which merges the pieces of each
+ *                (sequence, KV head) itself when few are expected (one kernel; see
+ *                paged_decode_launches), else partition + merge (two kernels).
+ *                Any other value is PKD_ERR_NUM_SPLITS.
+ *   workspace    at least paged_decode_workspace_bytes_ext(dims, ext, num_splits) bytes.
+ * Other arguments as for paged_decode.  With ext NULL, sinks NULL and num_splits
+ * in 1..PKD_MAX_SPLITS it is paged_decode, bit for bit.
  */
-int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* k_cache,
+int32_t paged_decode_ext(const pkd_dims* dims, const pkd_ext* ext, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                         const float* k_scale, const float* v_scale, const float* sinks, float scale, void* out,
+                         float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_decode_partition / paged_decode_finish -- the two phases of
+ * paged_decode_ext for a split mode (num_splits = 2..PKD_MAX_SPLITS or
+ * PKD_SPLITS_BALANCED, or PKD_SPLITS_AUTO when it resolves to one of them; a
+ * resolution to direct output is PKD_ERR_NUM_SPLITS here): the partition kernel
+ * writes its partials into the workspace, then the merge kernel reads them and
+ * writes out and lse.  Issued back to back on one stream with the same dims,
+ * ext, num_splits and workspace they are exactly paged_decode_ext; split apart
+ * they let a caller schedule or time the phases.  Arguments as for
+ * paged_decode_ext; the sinks are folded in by paged_decode_finish.
+ */
+int32_t paged_decode_partition(const pkd_dims* dims, const pkd_ext* ext, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
                                const int32_t* seq_lens, const float* k_scale, const float* v_scale,
                                float scale, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, void* stream);
-int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void* workspace,
+int32_t paged_decode_finish(const pkd_dims* dims, const pkd_ext* ext, int32_t num_splits, const void* workspace,
                             size_t workspace_bytes, const float* sinks, void* out, float* lse,
                             void* stream);
 
 /*
- * paged_decode_num_splits -- what paged_decode does for PKD_SPLITS_AUTO.
+ * paged_decode_num_splits -- what paged_decode does for num_splits <= 0 (and
+ * paged_decode_num_splits_ext what paged_decode_ext does for PKD_SPLITS_AUTO).
  * Work items are (sequence, KV head, head group), a head group being up to 16
  * of a KV head's q_len * G query rows.
  *  - 1 (direct output) for a BF16 cache with head_dim >= 64 when the items
@@ -220,47 +250,52 @@ int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void
  *    count in [2, PKD_MAX_SPLITS] bounded by the longest sequence expected,
  *    max_seq_len_hint (<= 0: max_pages_per_seq * page_size).
  * Host only; returns that value, or a status in [-11, -1] for invalid dims.
+ * Since the value may be PKD_SPLITS_BALANCED, pass it to paged_decode_ext (to
+ * paged_decode it would mean the heuristic again, which is the same choice).
  */
 int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint);
+int32_t paged_decode_num_splits_ext(const pkd_dims* dims, const pkd_ext* ext, int32_t max_seq_len_hint);
 
 /*
- * paged_decode_launches -- kernels paged_decode enqueues for num_splits
+ * paged_decode_launches -- kernels paged_decode_ext enqueues for num_splits
  * (PKD_SPLITS_AUTO: the heuristic's choice): 1 for direct output and for the
  * balanced mode when its partition kernel merges in place (when the
  * (sequence, KV head, head group) segments are at least as many as the
  * current device's compute units; a head group is 16 of the q_len * G query
- * rows of a KV head), else 2.
+ * rows of a KV head), else 2.  ext may be NULL.
  * Host only; returns a status in [-11, -1] for invalid dims or num_splits.
  */
-int32_t paged_decode_launches(const pkd_dims* dims, int32_t num_splits);
+int32_t paged_decode_launches(const pkd_dims* dims, const pkd_ext* ext, int32_t num_splits);
 
 /*
  * paged_decode_workspace_bytes -- workspace paged_decode needs for num_splits
- * (PKD_SPLITS_AUTO: the heuristic's choice): 0 for one split; for S splits the
- * fp32 partials [B][q_len][Hq][S][D] and [B][q_len][Hq][S]; for
- * PKD_SPLITS_BALANCED, with R = q_len * G query rows per KV head, the fp32
- * partials of D floats per row in (W + B*Hkv*ceil(R/16)) slots of min(R,16)
- * rows, W the workgroups of the device-sized grid (one per compute unit), B+1
- * int64 prefix sums, and B*Hkv*ceil(R/16) uint64 merge counters;
- * each part rounded up to 256 bytes.  When KV heads are read in pairs (head
- * rows under 128 bytes, no window, 2R <= 16: two heads sharing each cache line
- * are read together), Hkv counts pairs and R doubles.  Returns 0 for invalid
- * dims or an unsupported num_splits.  The counters carry a per-call tag, so
- * the workspace never needs initialising.
+ * (<= 0: the heuristic's choice); paged_decode_workspace_bytes_ext the same
+ * for paged_decode_ext (PKD_SPLITS_AUTO: the heuristic's choice).  0 for one
+ * split; for S splits the fp32 partials [B][q_len][Hq][S][D] and
+ * [B][q_len][Hq][S]; for PKD_SPLITS_BALANCED, with R = q_len * G query rows per
+ * KV head, the fp32 partials of D floats per row in (W + B*Hkv*ceil(R/16))
+ * slots of min(R,16) rows, W the workgroups of the device-sized grid (one per
+ * compute unit), B+1 int64 prefix sums, and B*Hkv*ceil(R/16) uint64 merge
+ * counters; each part rounded up to 256 bytes.  When KV heads are read in
+ * pairs (head rows under 128 bytes, no window, 2R <= 16: two heads sharing each
+ * cache line are read together), Hkv counts pairs and R doubles.  Returns 0 for
+ * invalid dims or an unsupported num_splits.  The counters carry a per-call
+ * tag, so the workspace never needs initialising.
  */
 size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits);
+size_t paged_decode_workspace_bytes_ext(const pkd_dims* dims, const pkd_ext* ext, int32_t num_splits);
 
 /*
  * paged_decode_partials -- the split-KV partition step alone: every split of
- * every (sequence, query head) writes its normalised partial output and
+ * every (sequence, query row) writes its normalised partial output and
  * natural-log LSE.  An empty split writes o = 0 and lse = -inf, so every slot
  * is written and no clearing is needed.
  *   o_part    [B][q_len][Hq][num_splits][D] fp32.
  *   lse_part  [B][q_len][Hq][num_splits] fp32.
  *   num_splits 1..PKD_MAX_SPLITS (no heuristic here).
- * Other arguments as for paged_decode.
+ * Other arguments as for paged_decode_ext (no sinks: partials never hold them).
  */
-int32_t paged_decode_partials(const pkd_dims* dims, const void* q, const void* k_cache,
+int32_t paged_decode_partials(const pkd_dims* dims, const pkd_ext* ext, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_table,
                               const int32_t* seq_lens, const float* k_scale, const float* v_scale,
                               float scale, int32_t num_splits, float* o_part, float* lse_part,
@@ -334,7 +369,7 @@ typedef struct {
   int32_t page_size;          /* tokens per page, >= 1 */
   int32_t max_pages_per_seq;  /* row length of page_table / swa_page_table, >= 1 */
   int32_t q_len;              /* query tokens per sequence, 1..PKD_MAX_Q_LEN (for the window) */
-  int32_t window;             /* 0: no window tables; W > 0: sliding window (as pkd_dims.window) */
+  int32_t window;             /* 0: no window tables; W > 0: sliding window (as pkd_ext.window) */
   int32_t extend;             /* tokens this step adds to every seq_lens[b], >= 0 */
 } pkd_meta_dims;
 
@@ -386,8 +421,8 @@ typedef struct {
   int32_t max_seq_len;        /* token capacity of the K/V tensors, >= 1; every seq_lens[b] <= it */
   int32_t kv_dtype;           /* a pkd_dtype */
   int32_t q_len;              /* query tokens per sequence, 1..PKD_MAX_Q_LEN */
-  int32_t causal;             /* as in pkd_dims */
-  int32_t window;             /* as in pkd_dims */
+  int32_t causal;             /* as in pkd_ext */
+  int32_t window;             /* as in pkd_ext */
   int32_t reserved;           /* must be 0 */
   int64_t q_strides[3];       /* element strides of q: sequence, query token, head (>= 0, multiples of 8) */
   int64_t kv_strides[3];      /* element strides of k and v: sequence, token, KV head (>= 0; each a multiple

@@ -40,8 +40,10 @@ PKD_BALANCED_MAX_BATCH = 1024
 PKD_DTYPE_BF16 = 0
 PKD_DTYPE_FP8_E4M3 = 1
 
-EXPORTED = ("paged_decode", "paged_decode_partition", "paged_decode_finish", "paged_decode_num_splits",
-            "paged_decode_launches", "paged_decode_workspace_bytes", "paged_decode_partials", "paged_decode_merge",
+EXPORTED = ("paged_decode", "paged_decode_ext", "paged_decode_partition", "paged_decode_finish",
+            "paged_decode_num_splits", "paged_decode_num_splits_ext", "paged_decode_launches",
+            "paged_decode_workspace_bytes", "paged_decode_workspace_bytes_ext", "paged_decode_partials",
+            "paged_decode_merge",
             "paged_decode_check_tables", "paged_kv_append", "paged_decode_metadata", "contiguous_decode",
             "contiguous_decode_workspace_bytes", "paged_decode_status_string", "pkd_stream_read",
             "pkd_stream_read_sink_bytes")
@@ -57,8 +59,12 @@ class pkd_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("max_pages_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("max_pages_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+class pkd_ext(ctypes.Structure):
+    _fields_ = [("q_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class pkd_meta_dims(ctypes.Structure):
@@ -109,22 +115,30 @@ if len(_hip_runtimes_mapped()) > 1:
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _dims_p = ctypes.POINTER(pkd_dims)
+_ext_p = ctypes.POINTER(pkd_ext)
 
-_lib.paged_decode.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _i32,
+_lib.paged_decode.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _i32,
                               _p, ctypes.c_size_t, _p]
 _lib.paged_decode.restype = _i32
-_lib.paged_decode_partition.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _i32,
+_lib.paged_decode_ext.argtypes = [_dims_p, _ext_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _i32,
+                                  _p, ctypes.c_size_t, _p]
+_lib.paged_decode_ext.restype = _i32
+_lib.paged_decode_partition.argtypes = [_dims_p, _ext_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _i32,
                                         _p, ctypes.c_size_t, _p]
 _lib.paged_decode_partition.restype = _i32
-_lib.paged_decode_finish.argtypes = [_dims_p, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p]
+_lib.paged_decode_finish.argtypes = [_dims_p, _ext_p, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p]
 _lib.paged_decode_finish.restype = _i32
 _lib.paged_decode_num_splits.argtypes = [_dims_p, _i32]
 _lib.paged_decode_num_splits.restype = _i32
-_lib.paged_decode_launches.argtypes = [_dims_p, _i32]
+_lib.paged_decode_num_splits_ext.argtypes = [_dims_p, _ext_p, _i32]
+_lib.paged_decode_num_splits_ext.restype = _i32
+_lib.paged_decode_launches.argtypes = [_dims_p, _ext_p, _i32]
 _lib.paged_decode_launches.restype = _i32
 _lib.paged_decode_workspace_bytes.argtypes = [_dims_p, _i32]
 _lib.paged_decode_workspace_bytes.restype = ctypes.c_size_t
-_lib.paged_decode_partials.argtypes = [_dims_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _i32,
+_lib.paged_decode_workspace_bytes_ext.argtypes = [_dims_p, _ext_p, _i32]
+_lib.paged_decode_workspace_bytes_ext.restype = ctypes.c_size_t
+_lib.paged_decode_partials.argtypes = [_dims_p, _ext_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _i32,
                                        _p, _p, _p]
 _lib.paged_decode_partials.restype = _i32
 _lib.paged_decode_merge.argtypes = [ctypes.c_int64, _i32, _i32, _p, _p, _p, _p, _p]
@@ -166,42 +180,57 @@ def _dims_ref(dims):
     return ctypes.byref(dims)
 
 
-def paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, scale, out,
-                 lse, num_splits, workspace, workspace_bytes, stream) -> int:
+def paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, out, lse,
+                 num_splits, workspace, workspace_bytes, stream) -> int:
     return _lib.paged_decode(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                             _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), _ptr(sinks), float(scale),
-                             _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace), int(workspace_bytes),
-                             _ptr(stream))
+                             _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), float(scale), _ptr(out), _ptr(lse),
+                             int(num_splits), _ptr(workspace), int(workspace_bytes), _ptr(stream))
 
 
-def paged_decode_partition(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+def paged_decode_ext(dims, ext, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, scale, out,
+                     lse, num_splits, workspace, workspace_bytes, stream) -> int:
+    return _lib.paged_decode_ext(_dims_ref(dims), _dims_ref(ext), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(block_table), _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), _ptr(sinks),
+                                 float(scale), _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace),
+                                 int(workspace_bytes), _ptr(stream))
+
+
+def paged_decode_partition(dims, ext, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
                            num_splits, workspace, workspace_bytes, stream) -> int:
-    return _lib.paged_decode_partition(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+    return _lib.paged_decode_partition(_dims_ref(dims), _dims_ref(ext), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(block_table), _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale),
                                        float(scale), int(num_splits), _ptr(workspace), int(workspace_bytes),
                                        _ptr(stream))
 
 
-def paged_decode_finish(dims, num_splits, workspace, workspace_bytes, sinks, out, lse, stream) -> int:
-    return _lib.paged_decode_finish(_dims_ref(dims), int(num_splits), _ptr(workspace), int(workspace_bytes),
-                                    _ptr(sinks), _ptr(out), _ptr(lse), _ptr(stream))
+def paged_decode_finish(dims, ext, num_splits, workspace, workspace_bytes, sinks, out, lse, stream) -> int:
+    return _lib.paged_decode_finish(_dims_ref(dims), _dims_ref(ext), int(num_splits), _ptr(workspace),
+                                    int(workspace_bytes), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(stream))
 
 
 def paged_decode_num_splits(dims, max_seq_len_hint: int = 0) -> int:
     return _lib.paged_decode_num_splits(_dims_ref(dims), int(max_seq_len_hint))
 
 
-def paged_decode_launches(dims, num_splits: int) -> int:
-    return _lib.paged_decode_launches(_dims_ref(dims), int(num_splits))
+def paged_decode_num_splits_ext(dims, ext, max_seq_len_hint: int = 0) -> int:
+    return _lib.paged_decode_num_splits_ext(_dims_ref(dims), _dims_ref(ext), int(max_seq_len_hint))
+
+
+def paged_decode_launches(dims, ext, num_splits: int) -> int:
+    return _lib.paged_decode_launches(_dims_ref(dims), _dims_ref(ext), int(num_splits))
 
 
 def paged_decode_workspace_bytes(dims, num_splits: int) -> int:
     return _lib.paged_decode_workspace_bytes(_dims_ref(dims), int(num_splits))
 
 
-def paged_decode_partials(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+def paged_decode_workspace_bytes_ext(dims, ext, num_splits: int) -> int:
+    return _lib.paged_decode_workspace_bytes_ext(_dims_ref(dims), _dims_ref(ext), int(num_splits))
+
+
+def paged_decode_partials(dims, ext, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
                           num_splits, o_part, lse_part, stream) -> int:
-    return _lib.paged_decode_partials(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+    return _lib.paged_decode_partials(_dims_ref(dims), _dims_ref(ext), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                       _ptr(block_table), _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale),
                                       float(scale), int(num_splits), _ptr(o_part), _ptr(lse_part),
                                       _ptr(stream))
@@ -260,15 +289,14 @@ def paged_decode_status_string(status: int) -> str:
 
 # ---- torch conveniences (memory and streams only) ---------------------------
 
-def dims_for(q, k_cache, block_table, causal: bool = False, window: int = 0) -> pkd_dims:
+def dims_for(q, k_cache, block_table) -> pkd_dims:
     """pkd_dims from torch tensors q [B,Hq,D] (or [B,q_len,Hq,D]), k_cache [P,ps,Hkv,D],
-    block_table [B,MP]; window 0 = no sliding window."""
+    block_table [B,MP]."""
     import torch
     if q.dim() == 4:
-        B, q_len, hq, d = q.shape
+        B, _, hq, d = q.shape
     else:
         B, hq, d = q.shape
-        q_len = 1
     num_pages, ps, hkv, d2 = k_cache.shape
     if d2 != d:
         raise ValueError("q and k_cache head_dim differ")
@@ -278,8 +306,16 @@ def dims_for(q, k_cache, block_table, causal: bool = False, window: int = 0) -> 
         kvd = PKD_DTYPE_FP8_E4M3
     else:
         raise TypeError(f"unsupported KV-cache dtype {k_cache.dtype}")
-    return pkd_dims(B, hq, hkv, d, ps, num_pages, block_table.shape[1], kvd, q_len, int(bool(causal)),
-                    int(window))
+    return pkd_dims(B, hq, hkv, d, ps, num_pages, block_table.shape[1], kvd)
+
+
+def ext_for(q, causal: bool = False, window: int = 0) -> Optional[pkd_ext]:
+    """pkd_ext for q [B,Hq,D] or [B,q_len,Hq,D] with the causal mask when `causal` and a
+    sliding window of `window` tokens (0: none); None for plain decode."""
+    q_len = q.shape[1] if q.dim() == 4 else 1
+    if q_len == 1 and not causal and window == 0:
+        return None
+    return pkd_ext(q_len, int(bool(causal)), int(window), 0)
 
 
 def current_stream_handle(device) -> int:
@@ -290,10 +326,12 @@ def current_stream_handle(device) -> int:
 def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=None, v_scale=None,
            num_splits: int = 0, out=None, lse=None, workspace=None, stream: Optional[int] = None,
            causal: bool = False, window: int = 0, sinks=None):
-    """Run paged_decode on torch device tensors; returns (out bf16 shaped like q, lse fp32
+    """Run the decode on torch device tensors; returns (out bf16 shaped like q, lse fp32
     [B,Hq] or [B,q_len,Hq]).  q is [B,Hq,D], or [B,q_len,Hq,D] for several query tokens
     per sequence (with the causal mask when `causal`); `window` > 0 is a sliding window
-    in tokens and `sinks` an fp32 [Hq] device tensor of sink logits."""
+    in tokens and `sinks` an fp32 [Hq] device tensor of sink logits.  Plain decode with
+    num_splits in 1..PKD_MAX_SPLITS or 0 (the heuristic) goes through paged_decode, the
+    rest through paged_decode_ext."""
     import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("block_table", block_table), ("seq_lens", seq_lens)):
@@ -307,23 +345,28 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, k_scale=Non
         raise ValueError("k_cache and v_cache must match")
     if sinks is not None and (not sinks.is_cuda or sinks.dtype != torch.float32 or sinks.numel() != q.shape[-2]):
         raise ValueError("sinks must be an fp32 device tensor of num_q_heads values")
-    dims = dims_for(q, k_cache, block_table, causal, window)
+    dims = dims_for(q, k_cache, block_table)
+    ext = ext_for(q, causal, window)
     dev = q.device
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
-    S = num_splits if num_splits != PKD_SPLITS_AUTO else paged_decode_num_splits(dims, 0)
+    S = num_splits if num_splits != PKD_SPLITS_AUTO else paged_decode_num_splits_ext(dims, ext, 0)
     if -11 <= S < 0:
         raise PkdError(S)
-    need = paged_decode_workspace_bytes(dims, S)
+    need = paged_decode_workspace_bytes_ext(dims, ext, S)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = current_stream_handle(dev)
-    st = paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, scale, out,
-                      lse, S, workspace, ws_bytes, stream)
+    if ext is None and sinks is None and 1 <= S <= PKD_MAX_SPLITS:
+        st = paged_decode(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, out, lse, S,
+                          workspace, ws_bytes, stream)
+    else:
+        st = paged_decode_ext(dims, ext, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks,
+                              scale, out, lse, S, workspace, ws_bytes, stream)
     if st != PKD_OK:
         raise PkdError(st)
     return out, lse
@@ -340,7 +383,7 @@ def append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=N
     if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
         raise TypeError("k_new and v_new must be bfloat16")
     kvd = PKD_DTYPE_FP8_E4M3 if k_cache.dtype == torch.float8_e4m3fn else PKD_DTYPE_BF16
-    dims = pkd_dims(0, hkv, hkv, d, ps, num_pages, 1, kvd, 1, 0, 0)
+    dims = pkd_dims(0, hkv, hkv, d, ps, num_pages, 1, kvd)
     max_pos = 0 if cos_sin is None else cos_sin.shape[0]
     if stream is None:
         stream = current_stream_handle(k_new.device)

@@ -2,6 +2,7 @@
 // workspace sizing and kernel launches.  Nothing here synchronises with the
 // device or copies device memory to the host.
 #include <atomic>
+#include <cstring>
 #include <chrono>
 #include <climits>
 #include <cmath>
@@ -12,19 +13,48 @@
 
 namespace {
 
+// The whole problem shape: pkd_dims plus the extensions of pkd_ext (one query
+// token, no mask and no window for the plain paged_decode).
+struct Dims {
+  int32_t batch, num_q_heads, num_kv_heads, head_dim;
+  int32_t page_size, num_pages, max_pages_per_seq;
+  int32_t kv_dtype;
+  int32_t q_len, causal, window;
+};
+
+// Dims of a call: the plain shape and its extensions (ext may be NULL).  An
+// extension record with a non-zero reserved field gives q_len 0, which
+// check_dims rejects.
+Dims make_dims(const pkd_dims& d, const pkd_ext* e) {
+  Dims f{d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim, d.page_size, d.num_pages, d.max_pages_per_seq,
+         d.kv_dtype, 1, 0, 0};
+  if (e) {
+    f.q_len = e->reserved == 0 ? e->q_len : 0;
+    f.causal = e->causal;
+    f.window = e->window;
+  }
+  return f;
+}
+
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not yet queried
 
 // Compute units of the current device (cached per device id), or -1.
+// Compute units of the current device, or -1 when there is none or it is not
+// a gfx950 (the only target the kernels are built for).  Cached per device.
 int current_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
   if (dev < kMaxDevices) {
     const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
-    if (cached > 0) return cached;
+    if (cached != 0) return cached;
   }
   int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0 || (prop.gcnArchName[6] != '\0' && prop.gcnArchName[6] != ':'))
+    cus = -1;
+  else if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return -1;
   if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
   return cus;
@@ -33,15 +63,15 @@ int current_cu_count() {
 bool valid_head_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
 // Query rows per KV head: the q_len query tokens of each of its G heads.
-int rows_per_kv(const pkd_dims& d) { return d.q_len * (d.num_q_heads / d.num_kv_heads); }
+int rows_per_kv(const Dims& d) { return d.q_len * (d.num_q_heads / d.num_kv_heads); }
 
 // Head groups: the rows of a KV head taken 16 at a time.
-int head_groups(const pkd_dims& d) {
+int head_groups(const Dims& d) {
   return (rows_per_kv(d) + pkd::kHeadsPerGroup - 1) / pkd::kHeadsPerGroup;
 }
 
 // Shape checks shared by every entry that takes dims.
-int32_t check_dims(const pkd_dims* d) {
+int32_t check_dims(const Dims* d) {
   if (!d) return PKD_ERR_NULL_POINTER;
   if (d->batch < 0 || d->batch > 65535 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
       d->page_size < 1 || d->num_pages < 1 || d->max_pages_per_seq < 1 || d->q_len < 1 ||
@@ -63,12 +93,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // sit on the unit's four SIMDs; with a second workgroup on the unit the
 // hardware favours the older one's waves, the two finish far apart, and the
 // whole measured 2-8% slower on every workload shape.
-int balanced_workers(const pkd_dims&) {
+int balanced_workers(const Dims&) {
   const int cus = current_cu_count();
   return cus > 0 ? cus : 256;
 }
 
-int heads_per_slot(const pkd_dims& d) {
+int heads_per_slot(const Dims& d) {
   const int R = rows_per_kv(d);
   return R < pkd::kHeadsPerGroup ? R : pkd::kHeadsPerGroup;
 }
@@ -76,7 +106,7 @@ int heads_per_slot(const pkd_dims& d) {
 // Whether the balanced partition applies: aligned 16-token groups lie in one
 // page, the prefix scan takes the batch, and the work-space arithmetic stays
 // far inside int64 (T * workers < 2^62).
-bool balanced_ok(const pkd_dims& d) {
+bool balanced_ok(const Dims& d) {
   if (d.page_size % 16 != 0 || d.batch > PKD_BALANCED_MAX_BATCH) return false;
   const int64_t groups = ((int64_t)d.max_pages_per_seq * d.page_size + 15) / 16;
   const int64_t T = groups * d.batch * d.num_kv_heads * head_groups(d);
@@ -89,7 +119,7 @@ bool balanced_ok(const pkd_dims& d) {
 // instance (64 or 128); else 1.  A pair is then one wide head (see the
 // kernel), so that each line is fetched once.  Not with a window or strided
 // (contiguous) K/V.  A function of the shape alone, so workspace sizes agree.
-int pair_heads(const pkd_dims& d, bool strided) {
+int pair_heads(const Dims& d, bool strided) {
   if (strided || d.window != 0) return 1;
   const int e = d.kv_dtype == PKD_DTYPE_FP8_E4M3 ? 1 : 2;
   if (d.head_dim * e >= 128 || d.num_kv_heads % 2 != 0) return 1;
@@ -100,8 +130,8 @@ int pair_heads(const pkd_dims& d, bool strided) {
 
 // The problem as the balanced kernel's work space sees it: pair KV heads of
 // head_dim D become one KV head of pair * D dims.
-pkd_dims balanced_view(const pkd_dims& d, int pair) {
-  pkd_dims v = d;
+Dims balanced_view(const Dims& d, int pair) {
+  Dims v = d;
   v.num_kv_heads /= pair;
   v.head_dim *= pair;
   return v;
@@ -111,9 +141,9 @@ pkd_dims balanced_view(const pkd_dims& d, int pair) {
 // [slots][hpg] fp32, prefix sums [B + 1] int64, then one in-kernel-merge
 // counter per segment [B * Hkv * head_groups] uint64 (its contents never need
 // initialising); slots, hpg and the segments as in balanced_view.
-size_t balanced_bytes(const pkd_dims& d, int pair, size_t* lse_offset, size_t* prefix_offset,
+size_t balanced_bytes(const Dims& d, int pair, size_t* lse_offset, size_t* prefix_offset,
                       size_t* count_offset) {
-  const pkd_dims v = balanced_view(d, pair);
+  const Dims v = balanced_view(d, pair);
   const size_t segments = (size_t)v.batch * v.num_kv_heads * head_groups(v);
   const size_t slots = (size_t)balanced_workers(v) + segments;
   const size_t hpg = (size_t)heads_per_slot(v);
@@ -127,8 +157,8 @@ size_t balanced_bytes(const pkd_dims& d, int pair, size_t* lse_offset, size_t* p
 }
 
 // Whether the balanced mode merges inside the partition kernel (paged_decode only).
-bool balanced_fused(const pkd_dims& d, int pair) {
-  const pkd_dims v = balanced_view(d, pair);
+bool balanced_fused(const Dims& d, int pair) {
+  const Dims v = balanced_view(d, pair);
   return pkd::balanced_merge_in_kernel(balanced_workers(v), (int64_t)v.batch * v.num_kv_heads * head_groups(v));
 }
 
@@ -148,7 +178,7 @@ uint64_t next_epoch() {
   return e != 0 ? e : 1;
 }
 
-size_t partial_bytes(const pkd_dims& d, int S, size_t* lse_offset) {
+size_t partial_bytes(const Dims& d, int S, size_t* lse_offset) {
   const size_t rows = (size_t)d.batch * d.q_len * d.num_q_heads;
   const size_t o = align256(rows * (size_t)S * d.head_dim * sizeof(float));
   if (lse_offset) *lse_offset = o;
@@ -158,7 +188,7 @@ size_t partial_bytes(const pkd_dims& d, int S, size_t* lse_offset) {
 // Most tokens one sequence's splits cover: what the block table can hold, or
 // with a sliding window the visible span of the q_len query tokens (window +
 // q_len - 1) plus up to 15 tokens before it (splits start on a 16-token group).
-int64_t visible_span(const pkd_dims& d) {
+int64_t visible_span(const Dims& d) {
   const int64_t cap = (int64_t)d.max_pages_per_seq * d.page_size;
   if (d.window <= 0) return cap;
   const int64_t span = (int64_t)d.window + d.q_len - 1 + 15;
@@ -169,7 +199,7 @@ int64_t visible_span(const pkd_dims& d) {
 // pieces rounded up to PKD_SPLIT_ALIGN.  Every split of every sequence then
 // covers the same number of tokens (or is the sequence's shorter last piece,
 // or empty), so workgroups carry equal work whatever the length mix.
-int32_t split_chunk(const pkd_dims& d, int S) {
+int32_t split_chunk(const Dims& d, int S) {
   const int64_t cap = visible_span(d);
   const int64_t per = (cap + S - 1) / S;
   const int64_t c = (per + PKD_SPLIT_ALIGN - 1) / PKD_SPLIT_ALIGN * PKD_SPLIT_ALIGN;
@@ -196,7 +226,7 @@ int32_t split_chunk(const pkd_dims& d, int S) {
 //    length mix and pays each workgroup's start-up once).
 //  - Otherwise direct output when the items alone fill the device, else
 //    enough splits to fill it, bounded by the longest sequence.
-int32_t heuristic_splits(const pkd_dims& d, int32_t max_len) {
+int32_t heuristic_splits(const Dims& d, int32_t max_len) {
   const int cus = current_cu_count();
   const int64_t items = (int64_t)d.batch * d.num_kv_heads * head_groups(d);
   if (d.kv_dtype == PKD_DTYPE_BF16 && d.head_dim >= 64 && cus > 0 && items <= cus && 4 * items >= 3LL * cus)
@@ -223,9 +253,9 @@ struct Layout {
   bool strided;    // not the paged_decode layouts: run the kernels that read the strides
 };
 
-int64_t kv_elem_bytes(const pkd_dims& d) { return d.kv_dtype == PKD_DTYPE_FP8_E4M3 ? 1 : 2; }
+int64_t kv_elem_bytes(const Dims& d) { return d.kv_dtype == PKD_DTYPE_FP8_E4M3 ? 1 : 2; }
 
-Layout paged_layout(const pkd_dims& d) {
+Layout paged_layout(const Dims& d) {
   Layout L;
   const int64_t D = d.head_dim;
   L.qs = {(int64_t)d.q_len * d.num_q_heads * D, (int64_t)d.num_q_heads * D, D};
@@ -238,7 +268,7 @@ Layout paged_layout(const pkd_dims& d) {
   return L;
 }
 
-pkd::SplitParams make_split_params(const pkd_dims& d, const Layout& lay, const void* q, const void* k,
+pkd::SplitParams make_split_params(const Dims& d, const Layout& lay, const void* q, const void* k,
                                    const void* v, const int32_t* bt, const int32_t* lens, const float* ks,
                                    const float* vs, float scale, int S) {
   pkd::SplitParams p{};
@@ -272,7 +302,7 @@ pkd::SplitParams make_split_params(const pkd_dims& d, const Layout& lay, const v
 // Whether p is a multiple of `bytes` (NULL passes: NULL is checked separately).
 bool aligned(const void* p, uintptr_t bytes) { return ((uintptr_t)p & (bytes - 1)) == 0; }
 
-int32_t check_inputs(const pkd_dims* dims, const void* q, const void* k, const void* v,
+int32_t check_inputs(const Dims* dims, const void* q, const void* k, const void* v,
                      const int32_t* bt, const int32_t* lens, const float* ks, const float* vs,
                      float scale, const float* sinks = nullptr) {
   const int32_t st = check_dims(dims);
@@ -293,7 +323,7 @@ int32_t check_out_ws(const void* out, const float* lse, const void* ws) {
   return aligned(out, 16) && aligned(lse, 4) && aligned(ws, 16) ? PKD_OK : PKD_ERR_ALIGNMENT;
 }
 
-int32_t launch_partition(const pkd_dims& d, const pkd::SplitParams& p, bool direct, hipStream_t s) {
+int32_t launch_partition(const Dims& d, const pkd::SplitParams& p, bool direct, hipStream_t s) {
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
   const bool paged16 = d.page_size % 16 == 0;
   const hipError_t e = pkd::launch_split_kv(p, d.batch, d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, direct,
@@ -301,45 +331,69 @@ int32_t launch_partition(const pkd_dims& d, const pkd::SplitParams& p, bool dire
   return e == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
 }
 
+// The heuristic's choice for a checked shape, and the workspace of a mode
+// (PKD_SPLITS_AUTO: of the heuristic's choice); 0 for an unsupported mode.
+int32_t num_splits_of(const Dims& d, int32_t max_seq_len_hint) {
+  const int32_t max_len = max_seq_len_hint > 0 ? max_seq_len_hint : d.max_pages_per_seq * d.page_size;
+  return heuristic_splits(d, max_len);
+}
+
+size_t workspace_of(const Dims& d, int32_t num_splits) {
+  int S = num_splits;
+  if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size);
+  if (S == PKD_SPLITS_BALANCED)
+    return balanced_ok(d) ? balanced_bytes(d, pair_heads(d, false), nullptr, nullptr, nullptr) : 0;
+  if (S < 1 || S > PKD_MAX_SPLITS) return 0;
+  if (S == 1) return 0;
+  return partial_bytes(d, S, nullptr);
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t paged_decode_num_splits(const pkd_dims* dims, int32_t max_seq_len_hint) {
-  const int32_t st = check_dims(dims);
+  return paged_decode_num_splits_ext(dims, nullptr, max_seq_len_hint);
+}
+
+int32_t paged_decode_num_splits_ext(const pkd_dims* dims, const pkd_ext* ext, int32_t max_seq_len_hint) {
+  if (!dims) return PKD_ERR_NULL_POINTER;
+  const Dims d = make_dims(*dims, ext);
+  const int32_t st = check_dims(&d);
   if (st != PKD_OK) return st;
-  const int32_t max_len = max_seq_len_hint > 0 ? max_seq_len_hint
-                                               : dims->max_pages_per_seq * dims->page_size;
-  return heuristic_splits(*dims, max_len);
+  return num_splits_of(d, max_seq_len_hint);
 }
 
 size_t paged_decode_workspace_bytes(const pkd_dims* dims, int32_t num_splits) {
-  if (check_dims(dims) != PKD_OK) return 0;
-  int S = num_splits;
-  if (S == PKD_SPLITS_AUTO) S = heuristic_splits(*dims, dims->max_pages_per_seq * dims->page_size);
-  if (S == PKD_SPLITS_BALANCED)
-    return balanced_ok(*dims) ? balanced_bytes(*dims, pair_heads(*dims, false), nullptr, nullptr, nullptr) : 0;
-  if (S < 1 || S > PKD_MAX_SPLITS) return 0;
-  if (S == 1) return 0;
-  return partial_bytes(*dims, S, nullptr);
+  // Every num_splits <= 0 asks for the heuristic here.
+  return paged_decode_workspace_bytes_ext(dims, nullptr, num_splits <= 0 ? PKD_SPLITS_AUTO : num_splits);
 }
 
-int32_t paged_decode_partials(const pkd_dims* dims, const void* q, const void* k_cache,
+size_t paged_decode_workspace_bytes_ext(const pkd_dims* dims, const pkd_ext* ext, int32_t num_splits) {
+  if (!dims) return 0;
+  const Dims d = make_dims(*dims, ext);
+  if (check_dims(&d) != PKD_OK) return 0;
+  return workspace_of(d, num_splits);
+}
+
+int32_t paged_decode_partials(const pkd_dims* dims, const pkd_ext* ext, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_table,
                               const int32_t* seq_lens, const float* k_scale, const float* v_scale,
                               float scale, int32_t num_splits, float* o_part, float* lse_part,
                               void* stream) {
-  int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
+  if (!dims) return PKD_ERR_NULL_POINTER;
+  const Dims d = make_dims(*dims, ext);
+  int32_t st = check_inputs(&d, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
   if (st != PKD_OK) return st;
   if (!o_part || !lse_part) return PKD_ERR_NULL_POINTER;
   if (!aligned(o_part, 16) || !aligned(lse_part, 4)) return PKD_ERR_ALIGNMENT;
   if (num_splits < 1 || num_splits > PKD_MAX_SPLITS) return PKD_ERR_NUM_SPLITS;
-  if (dims->batch == 0) return PKD_OK;
-  pkd::SplitParams p = make_split_params(*dims, paged_layout(*dims), q, k_cache, v_cache, block_table, seq_lens,
+  if (d.batch == 0) return PKD_OK;
+  pkd::SplitParams p = make_split_params(d, paged_layout(d), q, k_cache, v_cache, block_table, seq_lens,
                                          k_scale, v_scale, scale, num_splits);
   p.o_part = o_part;
   p.lse_part = lse_part;
-  return launch_partition(*dims, p, false, static_cast<hipStream_t>(stream));
+  return launch_partition(d, p, false, static_cast<hipStream_t>(stream));
 }
 
 int32_t paged_decode_merge(int64_t rows, int32_t num_splits, int32_t head_dim, const float* o_part,
@@ -376,7 +430,7 @@ struct Plan {
   size_t lse_off, prefix_off, count_off;
 };
 
-int32_t make_plan(const pkd_dims& d, int32_t num_splits, bool strided, Plan* pl) {
+int32_t make_plan(const Dims& d, int32_t num_splits, bool strided, Plan* pl) {
   int S = num_splits;
   if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size);
   pl->S = S;
@@ -389,7 +443,7 @@ int32_t make_plan(const pkd_dims& d, int32_t num_splits, bool strided, Plan* pl)
   return PKD_OK;
 }
 
-pkd::BalancedParams make_balanced_params(const pkd_dims& d, const Layout& lay, const void* q, const void* k,
+pkd::BalancedParams make_balanced_params(const Dims& d, const Layout& lay, const void* q, const void* k,
                                          const void* v, const int32_t* bt, const int32_t* lens, const float* ks,
                                          const float* vs, float scale, void* ws, const Plan& pl) {
   pkd::BalancedParams b{};
@@ -413,7 +467,7 @@ pkd::BalancedParams make_balanced_params(const pkd_dims& d, const Layout& lay, c
   b.prefix = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(ws) + pl.prefix_off);
   b.qk_scale_log2 = scale * 1.44269504088896340736f;
   b.batch = d.batch;
-  const pkd_dims bv = balanced_view(d, pl.pair);  // segments count wide heads when paired
+  const Dims bv = balanced_view(d, pl.pair);  // segments count wide heads when paired
   b.hq = bv.num_q_heads;
   b.hkv = bv.num_kv_heads;
   b.group = bv.num_q_heads / bv.num_kv_heads;
@@ -430,7 +484,7 @@ pkd::BalancedParams make_balanced_params(const pkd_dims& d, const Layout& lay, c
 }
 
 // Partition phase of a split plan (S > 1 or balanced) into the workspace.
-int32_t run_partition(const pkd_dims& d, const Layout& lay, const void* q, const void* k, const void* v,
+int32_t run_partition(const Dims& d, const Layout& lay, const void* q, const void* k, const void* v,
                       const int32_t* bt, const int32_t* lens, const float* ks, const float* vs, float scale,
                       void* ws, const Plan& pl, hipStream_t s) {
   if (pl.balanced) {
@@ -446,7 +500,7 @@ int32_t run_partition(const pkd_dims& d, const Layout& lay, const void* q, const
 }
 
 // Merge phase of a split plan from the workspace (sinks: [Hq] or null).
-int32_t run_finish(const pkd_dims& d, const Layout& lay, const void* ws, const float* sinks, void* out,
+int32_t run_finish(const Dims& d, const Layout& lay, const void* ws, const float* sinks, void* out,
                    float* lse, const Plan& pl, hipStream_t s) {
   pkd::MergeParams m{};
   m.sinks = sinks;
@@ -462,7 +516,7 @@ int32_t run_finish(const pkd_dims& d, const Layout& lay, const void* ws, const f
   if (pl.balanced) {
     m.balanced = 1;
     m.prefix = reinterpret_cast<const int64_t*>(static_cast<const uint8_t*>(ws) + pl.prefix_off);
-    const pkd_dims v = balanced_view(d, pl.pair);  // the partition's segments
+    const Dims v = balanced_view(d, pl.pair);  // the partition's segments
     m.batch = v.batch;
     m.hkv = v.num_kv_heads;
     m.group = v.num_q_heads / v.num_kv_heads;
@@ -478,7 +532,7 @@ int32_t run_finish(const pkd_dims& d, const Layout& lay, const void* ws, const f
 
 // The whole decode once every argument has been checked: plan, then one
 // partition kernel (direct output or in-kernel merge) or partition + merge.
-int32_t decode_checked(const pkd_dims& d, const Layout& lay, const void* q, const void* k, const void* v,
+int32_t decode_checked(const Dims& d, const Layout& lay, const void* q, const void* k, const void* v,
                        const int32_t* bt, const int32_t* lens, const float* ks, const float* vs, const float* sinks,
                        float scale, void* out, float* lse, int32_t num_splits, void* workspace,
                        size_t workspace_bytes, hipStream_t s) {
@@ -513,74 +567,101 @@ int32_t decode_checked(const pkd_dims& d, const Layout& lay, const void* q, cons
   return run_finish(d, lay, workspace, sinks, out, lse, pl, s);
 }
 
+// Argument checks and the decode of paged_decode / paged_decode_ext.
+int32_t decode_entry(const pkd_dims* dims, const pkd_ext* ext, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                     const float* k_scale, const float* v_scale, const float* sinks, float scale, void* out,
+                     float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dims) return PKD_ERR_NULL_POINTER;
+  const Dims d = make_dims(*dims, ext);
+  int32_t st = check_inputs(&d, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, sinks);
+  if (st != PKD_OK) return st;
+  if (!out) return PKD_ERR_NULL_POINTER;
+  st = check_out_ws(out, lse, workspace);
+  if (st != PKD_OK) return st;
+  return decode_checked(d, paged_layout(d), q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks,
+                        scale, out, lse, num_splits, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t paged_decode_launches(const pkd_dims* dims, int32_t num_splits) {
-  const int32_t st = check_dims(dims);
+int32_t paged_decode_launches(const pkd_dims* dims, const pkd_ext* ext, int32_t num_splits) {
+  if (!dims) return PKD_ERR_NULL_POINTER;
+  const Dims d = make_dims(*dims, ext);
+  const int32_t st = check_dims(&d);
   if (st != PKD_OK) return st;
   Plan pl;
-  const int32_t pst = make_plan(*dims, num_splits, false, &pl);
+  const int32_t pst = make_plan(d, num_splits, false, &pl);
   if (pst != PKD_OK) return pst;
-  if (pl.S == 1 || (pl.balanced && balanced_fused(*dims, pl.pair))) return 1;
+  if (pl.S == 1 || (pl.balanced && balanced_fused(d, pl.pair))) return 1;
   return 2;
 }
 
 int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
-                     const float* v_scale, const float* sinks, float scale, void* out, float* lse,
-                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale, sinks);
-  if (st != PKD_OK) return st;
-  if (!out) return PKD_ERR_NULL_POINTER;
-  st = check_out_ws(out, lse, workspace);
-  if (st != PKD_OK) return st;
-  return decode_checked(*dims, paged_layout(*dims), q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
-                        sinks, scale, out, lse, num_splits, workspace, workspace_bytes,
-                        static_cast<hipStream_t>(stream));
+                     const float* v_scale, float scale, void* out, float* lse, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  // Every num_splits <= 0 asks for the heuristic here.
+  return decode_entry(dims, nullptr, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, nullptr, scale,
+                      out, lse, num_splits <= 0 ? PKD_SPLITS_AUTO : num_splits, workspace, workspace_bytes, stream);
 }
 
-int32_t paged_decode_partition(const pkd_dims* dims, const void* q, const void* k_cache,
+int32_t paged_decode_ext(const pkd_dims* dims, const pkd_ext* ext, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                         const float* k_scale, const float* v_scale, const float* sinks, float scale, void* out,
+                         float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_entry(dims, ext, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, scale, out,
+                      lse, num_splits, workspace, workspace_bytes, stream);
+}
+
+int32_t paged_decode_partition(const pkd_dims* dims, const pkd_ext* ext, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
                                const int32_t* seq_lens, const float* k_scale, const float* v_scale,
                                float scale, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  int32_t st = check_inputs(dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
+  if (!dims) return PKD_ERR_NULL_POINTER;
+  const Dims d = make_dims(*dims, ext);
+  int32_t st = check_inputs(&d, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale);
   if (st != PKD_OK) return st;
   Plan pl;
-  st = make_plan(*dims, num_splits, false, &pl);
+  st = make_plan(d, num_splits, false, &pl);
   if (st != PKD_OK) return st;
   if (pl.S == 1) return PKD_ERR_NUM_SPLITS;
   if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return PKD_ERR_ALIGNMENT;
-  if (dims->batch == 0) return PKD_OK;
+  if (d.batch == 0) return PKD_OK;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
-  return run_partition(*dims, paged_layout(*dims), q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
-                       scale, workspace, pl, static_cast<hipStream_t>(stream));
+  return run_partition(d, paged_layout(d), q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,
+                       workspace, pl, static_cast<hipStream_t>(stream));
 }
 
-int32_t paged_decode_finish(const pkd_dims* dims, int32_t num_splits, const void* workspace,
+int32_t paged_decode_finish(const pkd_dims* dims, const pkd_ext* ext, int32_t num_splits, const void* workspace,
                             size_t workspace_bytes, const float* sinks, void* out, float* lse, void* stream) {
-  int32_t st = check_dims(dims);
+  if (!dims) return PKD_ERR_NULL_POINTER;
+  const Dims d = make_dims(*dims, ext);
+  int32_t st = check_dims(&d);
   if (st != PKD_OK) return st;
   if (!out) return PKD_ERR_NULL_POINTER;
   st = check_out_ws(out, lse, workspace);
   if (st != PKD_OK) return st;
   if (!aligned(sinks, 4)) return PKD_ERR_ALIGNMENT;
   Plan pl;
-  st = make_plan(*dims, num_splits, false, &pl);
+  st = make_plan(d, num_splits, false, &pl);
   if (st != PKD_OK) return st;
   if (pl.S == 1) return PKD_ERR_NUM_SPLITS;
   if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
-  if (dims->batch == 0) return PKD_OK;
+  if (d.batch == 0) return PKD_OK;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;
-  return run_finish(*dims, paged_layout(*dims), workspace, sinks, out, lse, pl, static_cast<hipStream_t>(stream));
+  return run_finish(d, paged_layout(d), workspace, sinks, out, lse, pl, static_cast<hipStream_t>(stream));
 }
 
 int32_t paged_decode_check_tables(const pkd_dims* dims, const int32_t* block_table,
                                   const int32_t* seq_lens, int32_t* d_error_count, void* stream) {
-  const int32_t st = check_dims(dims);
+  if (!dims) return PKD_ERR_NULL_POINTER;
+  const Dims d = make_dims(*dims, nullptr);
+  const int32_t st = check_dims(&d);
   if (st != PKD_OK) return st;
   if (!block_table || !seq_lens || !d_error_count) return PKD_ERR_NULL_POINTER;
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(d_error_count, 4)) return PKD_ERR_ALIGNMENT;
@@ -685,12 +766,12 @@ namespace {
 
 // The paged problem a contiguous one is run as (one page per sequence, page b
 // = sequence b, page_size the capacity rounded up to 16) and its layout.
-int32_t contiguous_plan(const pkd_contig_dims* c, pkd_dims* d, Layout* lay) {
+int32_t contiguous_plan(const pkd_contig_dims* c, Dims* d, Layout* lay) {
   if (!c) return PKD_ERR_NULL_POINTER;
   if (c->max_seq_len < 1 || c->reserved != 0) return PKD_ERR_BAD_DIMS;
   const int64_t ps = ((int64_t)c->max_seq_len + 15) / 16 * 16;
   if (ps > INT32_MAX) return PKD_ERR_BAD_DIMS;
-  *d = pkd_dims{c->batch, c->num_q_heads, c->num_kv_heads, c->head_dim, (int32_t)ps, c->batch > 0 ? c->batch : 1,
+  *d = Dims{c->batch, c->num_q_heads, c->num_kv_heads, c->head_dim, (int32_t)ps, c->batch > 0 ? c->batch : 1,
                 1, c->kv_dtype, c->q_len, c->causal, c->window};
   const int32_t st = check_dims(d);
   if (st != PKD_OK) return st;
@@ -717,7 +798,7 @@ int32_t contiguous_plan(const pkd_contig_dims* c, pkd_dims* d, Layout* lay) {
 extern "C" {
 
 size_t contiguous_decode_workspace_bytes(const pkd_contig_dims* dims, int32_t num_splits) {
-  pkd_dims d;
+  Dims d;
   Layout lay;
   if (contiguous_plan(dims, &d, &lay) != PKD_OK) return 0;
   Plan pl;
@@ -729,7 +810,7 @@ int32_t contiguous_decode(const pkd_contig_dims* dims, const void* q, const void
                           const int32_t* seq_lens, const float* k_scale, const float* v_scale, const float* sinks,
                           float scale, void* out, float* lse, int32_t num_splits, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  pkd_dims d;
+  Dims d;
   Layout lay;
   int32_t st = contiguous_plan(dims, &d, &lay);
   if (st != PKD_OK) return st;
@@ -759,7 +840,7 @@ const char* paged_decode_status_string(int32_t status) {
     case PKD_ERR_NUM_SPLITS: return "num_splits out of range";
     case PKD_ERR_WORKSPACE: return "workspace missing or too small";
     case PKD_ERR_LAUNCH: return "kernel launch failed";
-    case PKD_ERR_DEVICE: return "no usable device is current";
+    case PKD_ERR_DEVICE: return "the current device is not a usable gfx950";
     case PKD_ERR_ALIGNMENT: return "a pointer is not aligned as required";
     default: return "unknown status";
   }

@@ -55,7 +55,8 @@ def test_binding_constants_match_header():
 
 
 def test_dims_struct_layout():
-    assert ctypes.sizeof(b.pkd_dims) == 11 * 4
+    assert ctypes.sizeof(b.pkd_dims) == 8 * 4
+    assert ctypes.sizeof(b.pkd_ext) == 4 * 4
 
 
 def test_status_strings_are_distinct():
@@ -67,14 +68,110 @@ def test_status_strings_are_distinct():
 
 def dims(**kw):
     base = dict(batch=2, num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=16, num_pages=10,
-                max_pages_per_seq=7, kv_dtype=b.PKD_DTYPE_BF16, q_len=1, causal=0, window=0)
+                max_pages_per_seq=7, kv_dtype=b.PKD_DTYPE_BF16)
     base.update(kw)
     return b.pkd_dims(*[base[f] for f, _ in b.pkd_dims._fields_])
 
 
+def ext(q_len=1, causal=0, window=0, reserved=0):
+    return b.pkd_ext(q_len, causal, window, reserved)
+
+
 def call(d, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, ks=None, vs=None, scale=0.125, out=FAKE,
-         lse=None, S=1, ws=None, ws_bytes=0, sinks=None):
-    return b.paged_decode(d, q, k, v, bt, lens, ks, vs, sinks, scale, out, lse, S, ws, ws_bytes, None)
+         lse=None, S=1, ws=None, ws_bytes=0):
+    """paged_decode, the plain entry."""
+    return b.paged_decode(d, q, k, v, bt, lens, ks, vs, scale, out, lse, S, ws, ws_bytes, None)
+
+
+def call_ext(d, e=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, ks=None, vs=None, scale=0.125, out=FAKE,
+             lse=None, S=1, ws=None, ws_bytes=0, sinks=None):
+    """paged_decode_ext, the entry with the extended forms and special split modes."""
+    return b.paged_decode_ext(d, e, q, k, v, bt, lens, ks, vs, sinks, scale, out, lse, S, ws, ws_bytes, None)
+
+
+# The plain entry's prototype as the boundary's contract writes it (scope table,
+# part (b)): dims, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+# scale, out, lse, num_splits, workspace, workspace_bytes, stream.
+CONTRACT_PARAMS = ["const pkd_dims*", "const void*", "const void*", "const void*", "const int32_t*",
+                   "const int32_t*", "const float*", "const float*", "float", "void*", "float*", "int32_t",
+                   "void*", "size_t", "void*"]
+CONTRACT_DIMS = ["batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages",
+                 "max_pages_per_seq", "kv_dtype"]
+
+
+def _prototype_params(name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    params = []
+    for part in m.group(1).split(","):
+        part = " ".join(part.split())
+        typ = re.sub(r"\s*\b\w+$", "", part)  # drop the parameter name
+        params.append(typ.replace(" *", "*"))
+    return params
+
+
+def test_plain_entry_matches_the_contract_prototype():
+    """The header declares paged_decode and pkd_dims exactly as the contract
+    writes them: the same parameter types in the same order, and the same
+    eight int32 fields."""
+    assert _prototype_params("paged_decode") == CONTRACT_PARAMS
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} pkd_dims;", text).group(1)
+    assert re.findall(r"int32_t\s+(\w+);", body) == CONTRACT_DIMS
+    assert [f for f, _ in b.pkd_dims._fields_] == CONTRACT_DIMS
+
+
+def test_contract_prototype_compiles_against_the_header(tmp_path):
+    """A C caller written to the contract: its function-pointer type must accept
+    &paged_decode without a conversion (gcc with incompatible pointer types an
+    error), and its pkd_dims must be 32 bytes."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(
+        '#include "paged_kv_decode.h"\n'
+        "typedef int32_t (*contract_fn)(const pkd_dims*, const void*, const void*, const void*,\n"
+        "                               const int32_t*, const int32_t*, const float*, const float*, float,\n"
+        "                               void*, float*, int32_t, void*, size_t, void*);\n"
+        "contract_fn entry = &paged_decode;\n"
+        "typedef char dims_is_32_bytes[sizeof(pkd_dims) == 32 ? 1 : -1];\n")
+    r = subprocess.run([cc, "-std=c11", "-fsyntax-only", "-Werror=incompatible-pointer-types",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_contract_prototype_called_through_ctypes():
+    """Calls the exported symbol through a prototype built from the contract alone
+    (not the binding's), so a drift in the argument order would show."""
+    lib = ctypes.CDLL(b.LIB_PATH)
+    fn = lib.paged_decode
+    P = ctypes.c_void_p
+
+    class Dims(ctypes.Structure):
+        _fields_ = [(n, ctypes.c_int32) for n in CONTRACT_DIMS]
+
+    fn.argtypes = [ctypes.POINTER(Dims), P, P, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_int32, P,
+                   ctypes.c_size_t, P]
+    fn.restype = ctypes.c_int32
+    d = Dims(2, 4, 1, 64, 16, 10, 7, b.PKD_DTYPE_BF16)
+    ok = (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert fn(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.125, FAKE, None, 1, None, 0, None) == \
+        b.PKD_ERR_NULL_POINTER
+    # the float scale sits in its own position: a NaN there is rejected
+    assert fn(*ok, float("nan"), FAKE, None, 1, None, 0, None) == b.PKD_ERR_BAD_DIMS
+    # lse is the eleventh argument: a misaligned lse is rejected
+    assert fn(*ok, 0.125, FAKE, FAKE + 1, 1, None, 0, None) == b.PKD_ERR_ALIGNMENT
+    # num_splits above the cap is rejected; a workspace too small for 3 splits is rejected
+    assert fn(*ok, 0.125, FAKE, None, b.PKD_MAX_SPLITS + 1, None, 0, None) == b.PKD_ERR_NUM_SPLITS
+    assert fn(*ok, 0.125, FAKE, None, 3, FAKE, 16, None) == b.PKD_ERR_WORKSPACE
+    # FP8 without scales is rejected
+    d8 = Dims(2, 4, 1, 64, 16, 10, 7, b.PKD_DTYPE_FP8_E4M3)
+    assert fn(ctypes.byref(d8), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.125, FAKE, None, 1, None, 0, None) == \
+        b.PKD_ERR_SCALES
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -89,25 +186,44 @@ def call(d, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, ks=None, vs=None, scale=
     (dict(head_dim=512), b.PKD_ERR_HEAD_DIM),
     (dict(kv_dtype=7), b.PKD_ERR_DTYPE),
     (dict(max_pages_per_seq=2**20, page_size=2**12), b.PKD_ERR_BAD_DIMS),
-    (dict(q_len=0), b.PKD_ERR_BAD_DIMS),
-    (dict(q_len=b.PKD_MAX_Q_LEN + 1), b.PKD_ERR_BAD_DIMS),
-    (dict(causal=2), b.PKD_ERR_BAD_DIMS),
-    (dict(causal=-1), b.PKD_ERR_BAD_DIMS),
-    (dict(window=-1), b.PKD_ERR_BAD_DIMS),
 ])
 def test_bad_dims_are_rejected(kw, status):
     d = dims(**kw)
     assert call(d) == status
+    assert call_ext(d) == status
     assert b.paged_decode_num_splits(d, 0) == status
     assert b.paged_decode_workspace_bytes(d, 2) == 0
 
 
+@pytest.mark.parametrize("kw", [dict(q_len=0), dict(q_len=b.PKD_MAX_Q_LEN + 1), dict(causal=2),
+                                dict(causal=-1), dict(window=-1), dict(reserved=1)])
+def test_bad_ext_is_rejected(kw):
+    d, e = dims(), ext(**kw)
+    assert call_ext(d, e) == b.PKD_ERR_BAD_DIMS
+    assert b.paged_decode_num_splits_ext(d, e, 0) == b.PKD_ERR_BAD_DIMS
+    assert b.paged_decode_workspace_bytes_ext(d, e, 2) == 0
+    assert b.paged_decode_launches(d, e, 1) == b.PKD_ERR_BAD_DIMS
+
+
+def test_null_ext_is_plain_decode():
+    """ext NULL and ext {1, 0, 0, 0} describe the same problem."""
+    d = dims(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, num_pages=1500,
+             max_pages_per_seq=64)
+    for S in (1, 3, 0, b.PKD_SPLITS_BALANCED):
+        assert b.paged_decode_workspace_bytes_ext(d, None, S) == b.paged_decode_workspace_bytes_ext(d, ext(), S)
+        assert b.paged_decode_launches(d, None, S) == b.paged_decode_launches(d, ext(), S)
+    assert b.paged_decode_num_splits_ext(d, None, 0) == b.paged_decode_num_splits(d, 0)
+    assert b.paged_decode_num_splits_ext(d, ext(), 0) == b.paged_decode_num_splits(d, 0)
+
+
 def test_null_pointers_are_rejected():
     d = dims()
-    assert b.paged_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0.1, FAKE, None, 1, None, 0,
+    assert b.paged_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1, FAKE, None, 1, None, 0,
                           None) == b.PKD_ERR_NULL_POINTER
+    assert call_ext(None) == b.PKD_ERR_NULL_POINTER
     for kw in ("q", "k", "v", "bt", "lens", "out"):
         assert call(d, **{kw: None}) == b.PKD_ERR_NULL_POINTER, kw
+        assert call_ext(d, **{kw: None}) == b.PKD_ERR_NULL_POINTER, kw
 
 
 def test_fp8_scales_rules():
@@ -125,11 +241,11 @@ def test_misaligned_pointers_are_rejected():
     for kw in ("bt", "lens"):
         assert call(d, **{kw: FAKE + 2}) == b.PKD_ERR_ALIGNMENT, kw
     assert call(d, lse=FAKE + 1) == b.PKD_ERR_ALIGNMENT
-    assert call(d, sinks=FAKE + 2) == b.PKD_ERR_ALIGNMENT
+    assert call_ext(d, sinks=FAKE + 2) == b.PKD_ERR_ALIGNMENT
     need = b.paged_decode_workspace_bytes(d, 3)
     assert call(d, S=3, ws=FAKE + 8, ws_bytes=need) == b.PKD_ERR_ALIGNMENT
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1)
-    assert b.paged_decode_partials(d, *args, 2, FAKE + 4, FAKE, None) == b.PKD_ERR_ALIGNMENT
+    assert b.paged_decode_partials(d, None, *args, 2, FAKE + 4, FAKE, None) == b.PKD_ERR_ALIGNMENT
     assert b.paged_decode_merge(8, 2, 64, FAKE + 2, FAKE, FAKE, None, None) == b.PKD_ERR_ALIGNMENT
     assert b.paged_decode_merge(8, 2, 64, FAKE, FAKE, FAKE + 1, None, None) == b.PKD_ERR_ALIGNMENT
     assert b.paged_decode_check_tables(d, FAKE + 2, FAKE, FAKE, None) == b.PKD_ERR_ALIGNMENT
@@ -141,9 +257,7 @@ def test_window_bounds_the_split_count():
     is not a multiple of 16 keeps it on the grid mode)."""
     d = dims(batch=1, num_q_heads=8, num_kv_heads=8, page_size=8, max_pages_per_seq=4096, num_pages=4096)
     full = b.paged_decode_num_splits(d, 0)
-    dw = dims(batch=1, num_q_heads=8, num_kv_heads=8, page_size=8, max_pages_per_seq=4096, num_pages=4096,
-              window=256)
-    windowed = b.paged_decode_num_splits(dw, 0)
+    windowed = b.paged_decode_num_splits_ext(d, ext(window=256), 0)
     assert 1 <= windowed < full
     assert windowed <= (256 + 15 + 255) // 256
 
@@ -156,8 +270,13 @@ def test_non_finite_scale_is_rejected():
 def test_num_splits_and_workspace_rules():
     d = dims()
     assert call(d, S=b.PKD_MAX_SPLITS + 1) == b.PKD_ERR_NUM_SPLITS
-    assert call(d, S=-5) == b.PKD_ERR_NUM_SPLITS
-    assert b.paged_decode_workspace_bytes(d, -5) == 0
+    assert call_ext(d, S=b.PKD_MAX_SPLITS + 1) == b.PKD_ERR_NUM_SPLITS
+    # paged_decode: every num_splits <= 0 is the heuristic; paged_decode_ext: only
+    # PKD_SPLITS_AUTO and PKD_SPLITS_BALANCED are accepted below 1
+    assert call(d, S=-5) == call(d, S=0) == call(d, S=b.PKD_SPLITS_BALANCED)
+    assert call_ext(d, S=-5) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_workspace_bytes(d, -5) == b.paged_decode_workspace_bytes(d, 0)
+    assert b.paged_decode_workspace_bytes_ext(d, None, -5) == 0
     need = b.paged_decode_workspace_bytes(d, 3)
     # [B][Hq][S][D] fp32 + [B][Hq][S] fp32, each rounded up to 256 bytes
     assert need == 2 * 4 * 3 * 64 * 4 + 256
@@ -170,18 +289,18 @@ def test_num_splits_and_workspace_rules():
 def test_workspace_grows_with_query_tokens():
     """Several query tokens per sequence: grid partials are [B][q_len][Hq][S][D]; the
     balanced mode packs the q_len * G rows of a KV head 16 to a head group."""
-    d3 = dims(q_len=3, causal=1)
+    d, e3 = dims(), ext(q_len=3, causal=1)
     # [B][q_len][Hq][S][D] fp32 + [B][q_len][Hq][S] fp32 (288 B, rounded up to 512)
-    assert b.paged_decode_workspace_bytes(d3, 3) == 2 * 3 * 4 * 3 * 64 * 4 + 512
+    assert b.paged_decode_workspace_bytes_ext(d, e3, 3) == 2 * 3 * 4 * 3 * 64 * 4 + 512
     # G = 4, q_len = 3: 12 rows per KV head, one head group of 12 rows per slot
-    one = b.paged_decode_workspace_bytes(dims(), b.PKD_SPLITS_BALANCED)
-    three = b.paged_decode_workspace_bytes(d3, b.PKD_SPLITS_BALANCED)
+    one = b.paged_decode_workspace_bytes_ext(d, None, b.PKD_SPLITS_BALANCED)
+    three = b.paged_decode_workspace_bytes_ext(d, e3, b.PKD_SPLITS_BALANCED)
     assert three > one
     # G = 4, q_len = 5: 20 rows, two head groups per KV head
-    d5 = dims(q_len=5)
-    assert b.paged_decode_launches(d5, 4) == 2
-    assert b.paged_decode_workspace_bytes(d5, b.PKD_SPLITS_BALANCED) > three
-    assert call(dims(q_len=b.PKD_MAX_Q_LEN), S=3) == b.PKD_ERR_WORKSPACE  # accepted shape, no workspace
+    e5 = ext(q_len=5)
+    assert b.paged_decode_launches(d, e5, 4) == 2
+    assert b.paged_decode_workspace_bytes_ext(d, e5, b.PKD_SPLITS_BALANCED) > three
+    assert call_ext(d, ext(q_len=b.PKD_MAX_Q_LEN), S=3) == b.PKD_ERR_WORKSPACE  # accepted shape, no workspace
 
 
 def test_valid_call_without_gpu_reports_no_device():
@@ -192,16 +311,19 @@ def test_valid_call_without_gpu_reports_no_device():
         pytest.skip("a GPU is present")
     d = dims()
     assert call(d) == b.PKD_ERR_DEVICE
+    assert call_ext(d, ext(q_len=2, causal=1)) == b.PKD_ERR_DEVICE
     need = b.paged_decode_workspace_bytes(d, 3)
     assert call(d, S=3, ws=FAKE, ws_bytes=need) == b.PKD_ERR_DEVICE
     assert call(dims(batch=0)) == b.PKD_OK  # an empty batch enqueues nothing
+    assert call_ext(dims(batch=0)) == b.PKD_OK
 
 
 def test_partials_and_merge_argument_checks():
     d = dims()
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1)
-    assert b.paged_decode_partials(d, *args, 0, FAKE, FAKE, None) == b.PKD_ERR_NUM_SPLITS
-    assert b.paged_decode_partials(d, *args, 2, None, FAKE, None) == b.PKD_ERR_NULL_POINTER
+    assert b.paged_decode_partials(d, None, *args, 0, FAKE, FAKE, None) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_partials(d, None, *args, 2, None, FAKE, None) == b.PKD_ERR_NULL_POINTER
+    assert b.paged_decode_partials(d, ext(reserved=3), *args, 2, FAKE, FAKE, None) == b.PKD_ERR_BAD_DIMS
     assert b.paged_decode_merge(8, 2, 100, FAKE, FAKE, FAKE, None, None) == b.PKD_ERR_HEAD_DIM
     assert b.paged_decode_merge(8, 0, 64, FAKE, FAKE, FAKE, None, None) == b.PKD_ERR_NUM_SPLITS
     assert b.paged_decode_merge(-1, 2, 64, FAKE, FAKE, FAKE, None, None) == b.PKD_ERR_BAD_DIMS
@@ -214,13 +336,19 @@ def test_two_phase_argument_checks():
     d = dims()
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0.1)
     # direct output has no split phases
-    assert b.paged_decode_partition(d, *args, 1, FAKE, 1 << 20, None) == b.PKD_ERR_NUM_SPLITS
-    assert b.paged_decode_finish(d, 1, FAKE, 1 << 20, None, FAKE, None, None) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_partition(d, None, *args, 1, FAKE, 1 << 20, None) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_finish(d, None, 1, FAKE, 1 << 20, None, FAKE, None, None) == b.PKD_ERR_NUM_SPLITS
     need = b.paged_decode_workspace_bytes(d, 4)
-    assert b.paged_decode_partition(d, *args, 4, FAKE, need - 1, None) == b.PKD_ERR_WORKSPACE
-    assert b.paged_decode_finish(d, 4, None, need, None, FAKE, None, None) == b.PKD_ERR_WORKSPACE
-    assert b.paged_decode_finish(d, 4, FAKE, need, None, None, None, None) == b.PKD_ERR_NULL_POINTER
-    assert b.paged_decode_partition(d, *args, -7, FAKE, need, None) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_partition(d, None, *args, 4, FAKE, need - 1, None) == b.PKD_ERR_WORKSPACE
+    assert b.paged_decode_finish(d, None, 4, None, need, None, FAKE, None, None) == b.PKD_ERR_WORKSPACE
+    assert b.paged_decode_finish(d, None, 4, FAKE, need, None, None, None, None) == b.PKD_ERR_NULL_POINTER
+    assert b.paged_decode_partition(d, None, *args, -7, FAKE, need, None) == b.PKD_ERR_NUM_SPLITS
+    # the workspace of 3 query tokens is larger than that of one
+    e3 = ext(q_len=3)
+    need3 = b.paged_decode_workspace_bytes_ext(d, e3, 4)
+    assert need3 > need
+    assert b.paged_decode_partition(d, e3, *args, 4, FAKE, need, None) == b.PKD_ERR_WORKSPACE
+    assert b.paged_decode_finish(d, e3, 4, FAKE, need, None, FAKE, None, None) == b.PKD_ERR_WORKSPACE
 
 
 def test_heuristic_choices():
@@ -252,22 +380,22 @@ def test_heuristic_choices():
     assert b.paged_decode_num_splits(dims(max_pages_per_seq=16), 0) == 1  # 256 tokens
     assert b.paged_decode_num_splits(dims(max_pages_per_seq=17), 0) == b.PKD_SPLITS_BALANCED
     # a window bounds the span: 200 + 1 + 14 = 215 visible tokens of a 4096-token table
-    assert b.paged_decode_num_splits(dims(max_pages_per_seq=256, num_pages=512, window=200), 0) == 1
-    assert b.paged_decode_num_splits(dims(max_pages_per_seq=256, num_pages=512, window=300), 0) == \
-        b.PKD_SPLITS_BALANCED
+    wide = dims(max_pages_per_seq=256, num_pages=512)
+    assert b.paged_decode_num_splits_ext(wide, ext(window=200), 0) == 1
+    assert b.paged_decode_num_splits_ext(wide, ext(window=300), 0) == b.PKD_SPLITS_BALANCED
 
 
 def test_balanced_mode_rules():
     ok = dims(batch=4, page_size=16)
-    need = b.paged_decode_workspace_bytes(ok, b.PKD_SPLITS_BALANCED)
+    need = b.paged_decode_workspace_bytes_ext(ok, None, b.PKD_SPLITS_BALANCED)
     assert need > 0
-    assert call(ok, S=b.PKD_SPLITS_BALANCED) == b.PKD_ERR_WORKSPACE
-    assert call(ok, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=need - 1) == b.PKD_ERR_WORKSPACE
+    assert call_ext(ok, S=b.PKD_SPLITS_BALANCED) == b.PKD_ERR_WORKSPACE
+    assert call_ext(ok, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=need - 1) == b.PKD_ERR_WORKSPACE
     odd_ps = dims(batch=4, page_size=24)
-    assert b.paged_decode_workspace_bytes(odd_ps, b.PKD_SPLITS_BALANCED) == 0
-    assert call(odd_ps, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=1 << 30) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_workspace_bytes_ext(odd_ps, None, b.PKD_SPLITS_BALANCED) == 0
+    assert call_ext(odd_ps, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=1 << 30) == b.PKD_ERR_NUM_SPLITS
     too_many = dims(batch=b.PKD_BALANCED_MAX_BATCH + 1, page_size=16)
-    assert call(too_many, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=1 << 30) == b.PKD_ERR_NUM_SPLITS
+    assert call_ext(too_many, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=1 << 30) == b.PKD_ERR_NUM_SPLITS
 
 
 def test_one_hip_runtime_in_process():
@@ -280,15 +408,15 @@ def test_launch_counts():
     segments are at least as many as workgroups (it merges in place), else two."""
     b32 = dims(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
                num_pages=1500, max_pages_per_seq=64)
-    assert b.paged_decode_launches(b32, 1) == 1
-    assert b.paged_decode_launches(b32, 4) == 2
-    assert b.paged_decode_launches(b32, b.PKD_SPLITS_BALANCED) == 1
-    assert b.paged_decode_launches(b32, 0) == 1
+    assert b.paged_decode_launches(b32, None, 1) == 1
+    assert b.paged_decode_launches(b32, None, 4) == 2
+    assert b.paged_decode_launches(b32, None, b.PKD_SPLITS_BALANCED) == 1
+    assert b.paged_decode_launches(b32, None, 0) == 1
     long1 = dims(batch=1, num_q_heads=16, num_kv_heads=2, head_dim=64, page_size=64,
                  num_pages=2048, max_pages_per_seq=2048)
-    assert b.paged_decode_launches(long1, b.PKD_SPLITS_BALANCED) == 2
-    assert b.paged_decode_launches(b32, -5) == b.PKD_ERR_NUM_SPLITS
-    assert b.paged_decode_launches(dims(head_dim=96), 1) == b.PKD_ERR_HEAD_DIM
+    assert b.paged_decode_launches(long1, None, b.PKD_SPLITS_BALANCED) == 2
+    assert b.paged_decode_launches(b32, None, -5) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_launches(dims(head_dim=96), None, 1) == b.PKD_ERR_HEAD_DIM
 
 
 # ---- paged_decode_metadata argument checks ----------------------------------

@@ -331,7 +331,7 @@ def test_partials_entry_matches_oracle_per_split(B):
     R = len(lens) * 8
     o_part = torch.empty(R * S * 64, dtype=torch.float32, device="cuda")
     l_part = torch.empty(R * S, dtype=torch.float32, device="cuda")
-    st = B.paged_decode_partials(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale,
+    st = B.paged_decode_partials(dims, None, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale,
                                  S, o_part, l_part, B.current_stream_handle(0))
     assert st == 0
     torch.cuda.synchronize()
@@ -463,14 +463,14 @@ def test_two_phases_equal_paged_decode(B, S, case):
     t = dev(w)
     ref_out, ref_lse = run(B, w, S, t)
     dims = B.dims_for(t["q"], t["k"], t["bt"])
-    nbytes = B.paged_decode_workspace_bytes(dims, S)
+    nbytes = B.paged_decode_workspace_bytes_ext(dims, None, S)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["q"])
     lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
     h = B.current_stream_handle(0)
-    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, S,
-                                    ws, nbytes, h) == 0
-    assert B.paged_decode_finish(dims, S, ws, nbytes, None, out, lse, h) == 0
+    assert B.paged_decode_partition(dims, None, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale,
+                                    S, ws, nbytes, h) == 0
+    assert B.paged_decode_finish(dims, None, S, ws, nbytes, None, out, lse, h) == 0
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.cpu(), ref_lse)
@@ -493,7 +493,7 @@ def test_auto_mode_around_one_item_per_cu(B, hkv, d, dtype, expect):
     kvd = B.PKD_DTYPE_FP8_E4M3 if dtype == "fp8_e4m3" else B.PKD_DTYPE_BF16
     for batch, want in ((cus // hkv // 2, BAL), (3 * cus // 4 // hkv, expect), (cus // hkv - 1, expect),
                         (cus // hkv, expect), (cus // hkv + 1, BAL)):
-        dims = B.pkd_dims(batch, 4 * hkv, hkv, d, 64, 4096, 64, kvd, 1, 0, 0)
+        dims = B.pkd_dims(batch, 4 * hkv, hkv, d, 64, 4096, 64, kvd)
         assert B.paged_decode_num_splits(dims, 0) == want, (batch, hkv, d, dtype)
 
 
@@ -510,13 +510,43 @@ def test_two_phases_reject_auto_direct(B):
     assert B.paged_decode_num_splits(dims, 0) == 1
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
     h = B.current_stream_handle(0)
-    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, 0,
-                                    ws, ws.numel(), h) == B.PKD_ERR_NUM_SPLITS
+    assert B.paged_decode_partition(dims, None, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale,
+                                    0, ws, ws.numel(), h) == B.PKD_ERR_NUM_SPLITS
     torch.cuda.synchronize()
     assert int(ws.count_nonzero()) == 0
     # and paged_decode itself, with AUTO, matches the oracle
     out, lse = run(B, w, 0, t)
     check(out, lse, *oracle_full(w), what="AUTO direct at one item per compute unit")
+
+
+@pytest.mark.parametrize("case", ["b32", "b5", "long"])
+def test_plain_entry_heuristic(B, case):
+    """paged_decode, the plain entry, with num_splits <= 0: every such value is
+    the heuristic's choice, the workspace paged_decode_workspace_bytes gives for
+    it suffices, and the result equals paged_decode_ext in the mode the heuristic
+    names, bit for bit, and the oracle."""
+    shapes = {"b32": (32, 32, 8, 128, 64, [(i * 613) % 3500 + 1 for i in range(32)]),
+              "b5": (5, 32, 8, 128, 64, [700, 2, 0, 3000, 64]),
+              "long": (1, 16, 2, 64, 64, [20000])}
+    bq, hq, hkv, d, ps, lens = shapes[case]
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, "bf16", seed=125)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    chosen = B.paged_decode_num_splits(dims, 0)
+    nbytes = B.paged_decode_workspace_bytes(dims, 0)
+    assert nbytes == B.paged_decode_workspace_bytes_ext(dims, None, chosen)
+    h = B.current_stream_handle(0)
+    ref_out, ref_lse = run(B, w, chosen, t)
+    for S in (0, -1, -77):
+        ws = torch.full((max(nbytes, 1),), 0xA5, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(t["q"])
+        lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+        assert B.paged_decode(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, out, lse, S,
+                              ws if nbytes else None, nbytes, h) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16)), (case, S)
+        assert torch.equal(lse.cpu().view(torch.int32), ref_lse.view(torch.int32)), (case, S)
+    check(ref_out, ref_lse, *oracle_full(w), what=f"plain entry heuristic {case}")
 
 
 @pytest.mark.parametrize("S", [BAL, 4, 1])
@@ -527,7 +557,7 @@ def test_graph_replays(B, S):
     w = wl.custom_workload(32, 32, 8, 128, 64, lens, "bf16", seed=21)
     t = dev(w)
     dims = B.dims_for(t["q"], t["k"], t["bt"])
-    nbytes = B.paged_decode_workspace_bytes(dims, S)
+    nbytes = B.paged_decode_workspace_bytes_ext(dims, None, S)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["q"])
     lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
@@ -537,8 +567,9 @@ def test_graph_replays(B, S):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            st = B.paged_decode(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, None, w.scale, out, lse,
-                                S, ws if nbytes else None, nbytes, B.current_stream_handle(0))
+            st = B.paged_decode_ext(dims, None, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, None,
+                                    w.scale, out, lse, S, ws if nbytes else None, nbytes,
+                                    B.current_stream_handle(0))
     torch.cuda.current_stream().wait_stream(side)
     assert st == 0
     for i in range(4):
@@ -558,8 +589,8 @@ def test_in_kernel_merge_ignores_workspace_contents(B):
     w = wl.custom_workload(len(lens), 32, 8, 128, 64, lens, "bf16", seed=77)
     t = dev(w)
     dims = B.dims_for(t["q"], t["k"], t["bt"])
-    assert B.paged_decode_launches(dims, BAL) == 1
-    nbytes = B.paged_decode_workspace_bytes(dims, BAL)
+    assert B.paged_decode_launches(dims, None, BAL) == 1
+    nbytes = B.paged_decode_workspace_bytes_ext(dims, None, BAL)
     outs = []
     for fill in (0xFF, 0x00, None, 0x5A):
         ws = torch.full((nbytes,), fill if fill is not None else 0, dtype=torch.uint8, device="cuda")
@@ -652,14 +683,14 @@ def test_multi_verify_workload_modes(B):
     w = wl.make_workload(spec, tail="nan")
     t = dev(w)
     ref = oracle_full(w)
-    dims = B.dims_for(t["q"], t["k"], t["bt"], causal=True)
-    assert B.paged_decode_launches(dims, BAL) == 1  # 256 segments: merged in place
+    dims, e = B.dims_for(t["q"], t["k"], t["bt"]), B.ext_for(t["q"], causal=True)
+    assert B.paged_decode_launches(dims, e, BAL) == 1  # 256 segments: merged in place
     outs = {}
     for S in (BAL, 0, 1, 8):
         out, lse = run(B, w, S, t)
         check(out, lse, *ref, what=f"verify S={S}")
         outs[S] = (out, lse)
-    s_auto = B.paged_decode_num_splits(dims, 0)
+    s_auto = B.paged_decode_num_splits_ext(dims, e, 0)
     assert s_auto in outs
     assert torch.equal(outs[s_auto][0].view(torch.int16), outs[0][0].view(torch.int16))
 
@@ -672,15 +703,15 @@ def test_multi_two_phases_equal_paged_decode(B, lens):
     w = wl.custom_workload(len(lens), 32, 8, 128, 64, lens, "bf16", seed=313, q_len=4, causal=True)
     t = dev(w)
     ref_out, ref_lse = run(B, w, BAL, t)
-    dims = B.dims_for(t["q"], t["k"], t["bt"], causal=True)
-    nbytes = B.paged_decode_workspace_bytes(dims, BAL)
+    dims, e = B.dims_for(t["q"], t["k"], t["bt"]), B.ext_for(t["q"], causal=True)
+    nbytes = B.paged_decode_workspace_bytes_ext(dims, e, BAL)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["q"])
     lse = torch.empty(t["q"].shape[:-1], dtype=torch.float32, device="cuda")
     h = B.current_stream_handle(0)
-    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, BAL,
+    assert B.paged_decode_partition(dims, e, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, BAL,
                                     ws, nbytes, h) == 0
-    assert B.paged_decode_finish(dims, BAL, ws, nbytes, None, out, lse, h) == 0
+    assert B.paged_decode_finish(dims, e, BAL, ws, nbytes, None, out, lse, h) == 0
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.cpu().view(torch.int32), ref_lse.view(torch.int32))
@@ -710,14 +741,14 @@ def test_balanced_structures_parity(B, case):
     check(out, lse, *ref, what=f"balanced {case[:5]}")
     # the two phases give the same bits as paged_decode
     dims = B.dims_for(t["q"], t["k"], t["bt"])
-    nbytes = B.paged_decode_workspace_bytes(dims, BAL)
+    nbytes = B.paged_decode_workspace_bytes_ext(dims, None, BAL)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     o2 = torch.empty_like(t["q"])
     l2 = torch.empty(t["q"].shape[:-1], dtype=torch.float32, device="cuda")
     h = B.current_stream_handle(0)
-    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, BAL,
-                                    ws, nbytes, h) == 0
-    assert B.paged_decode_finish(dims, BAL, ws, nbytes, None, o2, l2, h) == 0
+    assert B.paged_decode_partition(dims, None, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale,
+                                    BAL, ws, nbytes, h) == 0
+    assert B.paged_decode_finish(dims, None, BAL, ws, nbytes, None, o2, l2, h) == 0
     torch.cuda.synchronize()
     assert torch.equal(o2.cpu().view(torch.int16), out.view(torch.int16))
     assert torch.equal(l2.cpu().view(torch.int32), lse.view(torch.int32))
@@ -904,15 +935,15 @@ def test_two_phases_fold_sinks(B, S):
     w = wl.custom_workload(len(lens), 16, 2, 128, 64, lens, "bf16", seed=430, window=500, sinks=True)
     t = dev(w)
     ref_out, ref_lse = run(B, w, S, t)
-    dims = B.dims_for(t["q"], t["k"], t["bt"], window=500)
-    nbytes = B.paged_decode_workspace_bytes(dims, S)
+    dims, e = B.dims_for(t["q"], t["k"], t["bt"]), B.ext_for(t["q"], window=500)
+    nbytes = B.paged_decode_workspace_bytes_ext(dims, e, S)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["q"])
     lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
     h = B.current_stream_handle(0)
-    assert B.paged_decode_partition(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, S,
+    assert B.paged_decode_partition(dims, e, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale, S,
                                     ws, nbytes, h) == 0
-    assert B.paged_decode_finish(dims, S, ws, nbytes, t["sinks"], out, lse, h) == 0
+    assert B.paged_decode_finish(dims, e, S, ws, nbytes, t["sinks"], out, lse, h) == 0
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse.cpu(), ref_lse)
@@ -1103,8 +1134,8 @@ def test_graph_replays_window_sinks_and_contiguous(B, S):
     eager_o, eager_l = run(B, w, S, t)
     out = torch.empty_like(t["q"])
     lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
-    dims = B.dims_for(t["q"], t["k"], t["bt"], window=500)
-    nbytes = B.paged_decode_workspace_bytes(dims, S)
+    dims, e = B.dims_for(t["q"], t["k"], t["bt"]), B.ext_for(t["q"], window=500)
+    nbytes = B.paged_decode_workspace_bytes_ext(dims, e, S)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     tc, _, _, _ = contig_dev(w, "bhld", strided_out=True)
     co_eager, cl_eager = run_contig(B, w, tc, S)
@@ -1116,8 +1147,8 @@ def test_graph_replays_window_sinks_and_contiguous(B, S):
 
     def body():
         h = B.current_stream_handle(0)
-        st.append(B.paged_decode(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, t["sinks"], w.scale,
-                                 out, lse, S, ws if nbytes else None, nbytes, h))
+        st.append(B.paged_decode_ext(dims, e, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, t["sinks"],
+                                     w.scale, out, lse, S, ws if nbytes else None, nbytes, h))
         st.append(B.contiguous_decode(cd, tc["q"], tc["k"], tc["v"], tc["lens"], None, None, tc["sinks"], w.scale,
                                       tc["out"], clse, S, cws if cbytes else None, cbytes, h))
     g = _capture(body)
