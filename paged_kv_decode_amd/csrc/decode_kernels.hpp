@@ -413,10 +413,13 @@ balanced_kernel(const BalancedParams p) {
           if (dd == 0) lrow[hh] = lse_nat;
         }, NoSink());
       } else {
-        // Agent-scope stores write through to the coherent copy that another
-        // XCD's workgroup will read; waiting for their acknowledgement before the
-        // count makes the partial visible to whichever piece merges.  (A release
-        // fence would write back this XCD's whole L2, far too costly per piece.)
+        // Release, done by hand: agent-scope atomic stores write through this
+        // XCD's L2 to the agent's coherent memory, and vmcnt(0) waits until the
+        // memory has acknowledged every one of them, so the partial is visible to
+        // any agent-scope reader before the count below is taken.  That is what
+        // an agent-scope release fence does for such stores; the fence would
+        // also write back the XCD's whole L2 (for ordinary stores, of which
+        // there are none here), which is far too costly per piece.
         wg_combine_rows<D, FP8, NWV>(A, smem, wave, tid, heads_here, vsc_of,
                                      [&](int hh, int d0, f32x4 o, float lse_nat) {
           if (!mine(hh, d0)) return;
@@ -441,7 +444,13 @@ balanced_kernel(const BalancedParams p) {
           } while (!__hip_atomic_compare_exchange_weak(cw, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT));
           const bool last = (int)(nv & 0xFFFFFF) == npieces;
-          if (last) __hip_atomic_store(cw, E << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (last) {
+            // Acquire at agent scope: the other pieces' partials, which their
+            // counts made visible before this count saw them, are read after it.
+            // Only a merging piece pays for it (one per multi-piece segment).
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(cw, E << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
           s_last = last;
         }
         __syncthreads();
