@@ -103,6 +103,7 @@ extern "C" {
 #define PKD_ERR_LAUNCH (-9)          /* the HIP runtime refused a launch */
 #define PKD_ERR_DEVICE (-10)         /* the current device is not a usable gfx950 */
 #define PKD_ERR_ALIGNMENT (-11)      /* a pointer is not aligned as required (see below) */
+#define PKD_ERR_SCRATCH_LIMIT (-12)  /* paged_decode_ext_noalloc: the mode needs more than its fixed scratch */
 
 /* Largest num_splits accepted. */
 #define PKD_MAX_SPLITS 512
@@ -213,6 +214,31 @@ int32_t paged_decode_ext(const pkd_dims* dims, const pkd_ext* ext, const void* q
                          const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                          const float* k_scale, const float* v_scale, const float* sinks, float scale, void* out,
                          float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the fixed device array paged_decode_ext_noalloc uses as its workspace. */
+#define PKD_NOALLOC_SCRATCH_BYTES 16777216  /* 16 MiB */
+
+/*
+ * paged_decode_ext_noalloc -- paged_decode_ext for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid it): the workspace is a fixed array of PKD_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per device, which each device holds until the
+ * process ends.  The call itself allocates and frees nothing.
+ *   Arguments as for paged_decode_ext, without workspace and workspace_bytes.
+ *   A mode whose paged_decode_workspace_bytes_ext exceeds
+ *   PKD_NOALLOC_SCRATCH_BYTES returns PKD_ERR_SCRATCH_LIMIT and enqueues nothing
+ *   (the balanced mode needs a few MB for batches up to 1024; many grid splits of
+ *   large batches need more).
+ *   All calls on one device share its array: calls that overlap in time there
+ *   (on different streams, or from different threads) race and their results
+ *   are undefined; calls in one stream's order are safe.  The array is never
+ *   cleared and never needs to be.
+ * Returns PKD_OK or a negative status.
+ */
+int32_t paged_decode_ext_noalloc(const pkd_dims* dims, const pkd_ext* ext, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                 const float* k_scale, const float* v_scale, const float* sinks, float scale,
+                                 void* out, float* lse, int32_t num_splits, void* stream);
 
 /*
  * paged_decode_partition / paged_decode_finish -- the two phases of

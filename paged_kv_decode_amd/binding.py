@@ -31,7 +31,9 @@ PKD_ERR_WORKSPACE = -8
 PKD_ERR_LAUNCH = -9
 PKD_ERR_DEVICE = -10
 PKD_ERR_ALIGNMENT = -11
+PKD_ERR_SCRATCH_LIMIT = -12
 PKD_MAX_SPLITS = 512
+PKD_NOALLOC_SCRATCH_BYTES = 16 << 20
 PKD_MAX_Q_LEN = 64
 PKD_SPLIT_ALIGN = 64
 PKD_SPLITS_AUTO = 0
@@ -46,7 +48,7 @@ EXPORTED = ("paged_decode", "paged_decode_ext", "paged_decode_partition", "paged
             "paged_decode_merge",
             "paged_decode_check_tables", "paged_kv_append", "paged_decode_metadata", "contiguous_decode",
             "contiguous_decode_workspace_bytes", "paged_decode_status_string", "pkd_stream_read",
-            "pkd_stream_read_sink_bytes")
+            "pkd_stream_read_sink_bytes", "paged_decode_ext_noalloc")
 
 
 class PkdError(RuntimeError):
@@ -123,6 +125,9 @@ _lib.paged_decode.restype = _i32
 _lib.paged_decode_ext.argtypes = [_dims_p, _ext_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _i32,
                                   _p, ctypes.c_size_t, _p]
 _lib.paged_decode_ext.restype = _i32
+_lib.paged_decode_ext_noalloc.argtypes = [_dims_p, _ext_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p,
+                                          _i32, _p]
+_lib.paged_decode_ext_noalloc.restype = _i32
 _lib.paged_decode_partition.argtypes = [_dims_p, _ext_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _i32,
                                         _p, ctypes.c_size_t, _p]
 _lib.paged_decode_partition.restype = _i32
@@ -193,6 +198,14 @@ def paged_decode_ext(dims, ext, q, k_cache, v_cache, block_table, seq_lens, k_sc
                                  _ptr(block_table), _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), _ptr(sinks),
                                  float(scale), _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace),
                                  int(workspace_bytes), _ptr(stream))
+
+
+def paged_decode_ext_noalloc(dims, ext, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, scale,
+                             out, lse, num_splits, stream) -> int:
+    return _lib.paged_decode_ext_noalloc(_dims_ref(dims), _dims_ref(ext), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(block_table), _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale),
+                                         _ptr(sinks), float(scale), _ptr(out), _ptr(lse), int(num_splits),
+                                         _ptr(stream))
 
 
 def paged_decode_partition(dims, ext, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, scale,

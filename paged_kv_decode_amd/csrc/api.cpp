@@ -841,6 +841,7 @@ const char* paged_decode_status_string(int32_t status) {
     case PKD_ERR_WORKSPACE: return "workspace missing or too small";
     case PKD_ERR_LAUNCH: return "kernel launch failed";
     case PKD_ERR_DEVICE: return "the current device is not a usable gfx950";
+    case PKD_ERR_SCRATCH_LIMIT: return "the mode needs more workspace than the fixed scratch array holds";
     case PKD_ERR_ALIGNMENT: return "a pointer is not aligned as required";
     default: return "unknown status";
   }

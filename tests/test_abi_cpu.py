@@ -60,7 +60,7 @@ def test_dims_struct_layout():
 
 
 def test_status_strings_are_distinct():
-    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11]
+    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12]
     texts = [b.paged_decode_status_string(c) for c in codes]
     assert len(set(texts)) == len(texts)
     assert b.paged_decode_status_string(-12345) == "unknown status"
@@ -224,6 +224,30 @@ def test_null_pointers_are_rejected():
     for kw in ("q", "k", "v", "bt", "lens", "out"):
         assert call(d, **{kw: None}) == b.PKD_ERR_NULL_POINTER, kw
         assert call_ext(d, **{kw: None}) == b.PKD_ERR_NULL_POINTER, kw
+
+
+def test_noalloc_argument_checks():
+    """paged_decode_ext_noalloc: argument errors as paged_decode_ext's, a mode
+    whose workspace exceeds the fixed array rejected before anything else is
+    touched, and, without a GPU, a valid call reports the missing device."""
+    def na(d, e=None, q=FAKE, S=1, out=FAKE, sinks=None):
+        return b.paged_decode_ext_noalloc(d, e, q, FAKE, FAKE, FAKE, FAKE, None, None, sinks, 0.125, out, None, S,
+                                          None)
+    assert na(None) == b.PKD_ERR_NULL_POINTER
+    assert na(dims(head_dim=96)) == b.PKD_ERR_HEAD_DIM
+    assert na(dims(), ext(reserved=1)) == b.PKD_ERR_BAD_DIMS
+    assert na(dims(), q=None) == b.PKD_ERR_NULL_POINTER
+    assert na(dims(), S=3, out=None) == b.PKD_ERR_NULL_POINTER
+    assert na(dims(), S=-5) == b.PKD_ERR_NUM_SPLITS
+    big = dims(batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, num_pages=4096,
+               max_pages_per_seq=64)
+    assert b.paged_decode_workspace_bytes_ext(big, None, 64) > b.PKD_NOALLOC_SCRATCH_BYTES
+    assert na(big, S=64) == b.PKD_ERR_SCRATCH_LIMIT
+    import torch
+    if not torch.cuda.is_available():
+        assert na(dims()) == b.PKD_ERR_DEVICE
+        assert na(dims(), S=3) == b.PKD_ERR_DEVICE
+        assert na(big, S=b.PKD_SPLITS_BALANCED) == b.PKD_ERR_DEVICE
 
 
 def test_fp8_scales_rules():
