@@ -15,11 +15,15 @@ window those from the lowest window start on), q, out, lse, the block-table
 entries used, seq_lens and (FP8) the scales, (sinks) the sink logits.  Split
 partials and cache effects are not counted.
 
-The primary workload is the B=32 Llama-style decode step; the B=128 step, the
-B=32 verify step (4 query tokens, causal) and the B=32 step with a 1024-token
-window and sinks are reported alongside, with a sweep of fixed num_splits
-values against the balanced mode at B=32 and B=128, and, as context, torch's
-read-only sum over a buffer of the B=32 step's bytes timed the same way.  The fp64 CPU oracle is timed on the same host arrays (whole
+The primary workload is the B=32 Llama-style decode step.  Every other
+workload is reported alongside with its own roofline entry (its partition
+kernel's GB/s against the HBM peak): the tiny two-sequence case, the B=128
+step, the long-context head-dim sweep (B=1 and B=16 at D = 32, 64, 256), the
+FP8 cache at B=64, the B=32 verify step (4 query tokens, causal) and the B=32
+step with a 1024-token window and sinks; with a sweep of fixed num_splits values
+against the balanced mode at B=32 and B=128, and the library's read-only
+stream kernel over a buffer of the B=32 step's bytes, timed the same way, as the
+measured ceiling.  The fp64 CPU oracle is timed on the same host arrays (whole
 passes over the workload for about 10 s, all host threads up to 16) as a
 reported baseline.
 
@@ -125,7 +129,10 @@ class Runner:
         self.kernel2()
 
 
-def bench_one(name, steps, warmup, num_splits, device, scrub):
+def bench_one(name, steps, warmup, num_splits, device, scrub, warm_pass=True):
+    """Times workload `name`: the metric pass, the partition-kernel pass and
+    (warm_pass) back-to-back warm steps; a profiled run leaves out the warm pass
+    so that every launch in its kernel trace starts from cold caches."""
     import torch
     from paged_kv_decode_amd import workloads as wl
     w = wl.make_workload(wl.WORKLOADS[name], tail="zero")
@@ -161,13 +168,15 @@ def bench_one(name, steps, warmup, num_splits, device, scrub):
     split_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(steps)]
     del scrub_sum
     # Warm back-to-back timing (KV partly cache-resident when it fits): secondary only.
-    wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wa.record(r.stream)
-    for _ in range(steps):
-        r.step()
-    wb.record(r.stream)
-    torch.cuda.synchronize()
-    warm_ms = wa.elapsed_time(wb) / steps
+    warm_ms = float("nan")
+    if warm_pass:
+        wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wa.record(r.stream)
+        for _ in range(steps):
+            r.step()
+        wb.record(r.stream)
+        torch.cuda.synchronize()
+        warm_ms = wa.elapsed_time(wb) / steps
 
     step_mean = sum(step_ms) / steps
     k1_mean = sum(k1_ms) / steps
@@ -192,7 +201,22 @@ def bench_one(name, steps, warmup, num_splits, device, scrub):
         timed_wall_s=wall,
     )
     res["pct_of_peak"] = 100.0 * res["gbs"] / PEAK_HBM_GBS
+    # The row's roofline: its dominant kernel (the partition kernel, which is the
+    # whole step when there is no merge kernel) against the HBM peak.
+    res["roofline"] = {"bound": "hbm", "achieved": round(res["split_kernel_gbs"], 2), "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": round(res["split_kernel_gbs"] / PEAK_HBM_GBS, 4),
+                       "kernel": kernel_label(w.spec, r.S, r.launches), "step_frac": round(res["gbs"] / PEAK_HBM_GBS, 4)}
     return res, w
+
+
+def kernel_label(spec, S, launches):
+    """The partition kernel a mode runs, as the profiles name it."""
+    t = f"<{spec.head_dim}, {'fp8' if spec.kv_dtype != 'bf16' else 'bf16'}>"
+    if S == -1000:
+        return "balanced_kernel" + t + (" (merging in place)" if launches == 1 else " + lse_merge_kernel")
+    if S == 1:
+        return "split_kv_kernel" + t + " (direct output)"
+    return "split_kv_kernel" + t + " (partials) + lse_merge_kernel"
 
 
 CPU_SAMPLE_S = 10.0  # length of the CPU-baseline sample
@@ -362,22 +386,50 @@ def split_sweep(w, steps, warmup, device, scrub):
     return out
 
 
-def read_reference(nbytes, steps, warmup, device, scrub):
-    """Context, not a metric: torch's read-only sum over a float32 buffer of the
-    decode step's algorithmic bytes, timed cold like the decode steps.  What a
-    plain library read of the same footprint achieves (a reduction kernel, not a
-    tuned stream, so it is no ceiling)."""
+# Launch shapes of the read-only stream kernel (pkd_stream_read) timed as the
+# measured ceiling: (pattern, workgroups, waves, KiB in flight per batch).
+# Pattern 0 reads whole lines of each 256-byte column (one KV head's slice of
+# a 2 KiB token row: Hkv = 8, D = 128, bf16), the way the decode kernels load
+# K and V; pattern 1 reads the same bytes in the 16x16x32 matrix-core operand
+# layout (64 bytes of each of 16 rows per load), for comparison.
+STREAM_SHAPES = [(0, 256, 4, 8), (0, 256, 4, 16), (0, 1024, 4, 8), (0, 2048, 4, 4), (1, 256, 4, 8),
+                 (1, 1024, 4, 8)]
+
+
+def stream_ceiling(nbytes, steps, warmup, device, scrub):
+    """The read-only stream kernel over a buffer of the B=32 step's size, timed
+    cold like the decode steps, in the launch shapes above: the fastest
+    row-order shape is the practical ceiling the decode is compared with."""
     import torch
-    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    from paged_kv_decode_amd import binding as B
+    row, chunk = 2048, 256
+    unit = row * 16
+    n = (nbytes + unit - 1) // unit * unit
+    buf = torch.ones(n // 4, dtype=torch.float32, device=device)
     stream = torch.cuda.current_stream(device)
-    for _ in range(warmup):
-        buf.sum()
-    torch.cuda.synchronize()
-    mean = _cold_steps(stream, steps, scrub, buf.sum)
+    h = stream.cuda_stream
+    rows = []
+    for pattern, wgs, waves, kb in STREAM_SHAPES:
+        sink = torch.empty(B.pkd_stream_read_sink_bytes(wgs, waves) // 4, dtype=torch.int32, device=device)
+
+        def call():
+            st = B.pkd_stream_read(buf, n, row, chunk, pattern, wgs, waves, kb, 1, sink, h)
+            if st != 0:
+                raise B.PkdError(st)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        mean = _cold_steps(stream, steps, scrub, call)
+        gbs = n / (mean * 1e-3) / 1e9
+        rows.append({"pattern": "row order" if pattern == 0 else "matrix-core operand layout",
+                     "workgroups": wgs, "waves": waves, "kib_in_flight_per_batch": kb, "us": round(mean * 1e3, 2),
+                     "gbs": round(gbs, 1), "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2)})
     del buf
-    gbs = (nbytes // 4) * 4 / (mean * 1e-3) / 1e9
-    return {"kernel": "torch.sum over float32 (read-only)", "bytes": (nbytes // 4) * 4, "ms": round(mean, 4),
-            "gbs": round(gbs, 1), "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2)}
+    best = max((r for r in rows if r["pattern"] == "row order"), key=lambda r: r["gbs"])
+    best_mfma = max((r for r in rows if r["pattern"] != "row order"), key=lambda r: r["gbs"])
+    return {"kernel": "pkd_stream_read (read-only, 16-byte non-temporal loads)", "bytes": n,
+            "row_bytes": row, "column_bytes": chunk, "gbs": best["gbs"], "pct_of_peak": best["pct_of_peak"],
+            "best_shape": best, "operand_layout_best_gbs": best_mfma["gbs"], "shapes": rows}
 
 
 def cpu_baseline(w, nbytes):
@@ -556,8 +608,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workloads", default=f"{PRIMARY},{SECONDARY},{VERIFY},{WINDOW}",
-                    help="comma-separated workload names, or 'all'")
+    ap.add_argument("--workloads", default="all",
+                    help="comma-separated workload names, or 'all' (the default)")
     ap.add_argument("--num-splits", type=int, default=0, help="0: the library's heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
@@ -596,7 +648,8 @@ def main():
     primary_w = None
     sweep_w = {}
     for name in names:
-        res, w = bench_one(name, args.steps, args.warmup, args.num_splits, device, scrub)
+        res, w = bench_one(name, args.steps, args.warmup, args.num_splits, device, scrub,
+                           warm_pass=not args.profile_only)
         results[name] = res
         if name == PRIMARY:
             primary_w = w
@@ -616,9 +669,10 @@ def main():
     for name, row in sweep.items():
         print(f"# num_splits sweep {name} (GB/s): {row}", file=sys.stderr, flush=True)
     del sweep_w
-    reference = read_reference(results[PRIMARY]["algorithmic_bytes"], args.steps, args.warmup, device, scrub)
-    print(f"# read reference ({reference['kernel']}, {reference['bytes']} bytes): {reference['gbs']:.0f} GB/s = "
-          f"{reference['pct_of_peak']:.1f}% of peak", file=sys.stderr, flush=True)
+    ceiling = stream_ceiling(results[PRIMARY]["algorithmic_bytes"], max(args.steps // 2, 10), 3, device, scrub)
+    print(f"# stream ceiling ({ceiling['bytes']} bytes, 256 of every 2048): {ceiling['gbs']:.0f} GB/s = "
+          f"{ceiling['pct_of_peak']:.1f}% of peak (shape {ceiling['best_shape']}); operand layout "
+          f"{ceiling['operand_layout_best_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     app = bench_append(args.steps, args.warmup, device, scrub)
     meta = bench_metadata(primary_w, args.steps, args.warmup, device, scrub, window=1024)
     contig = bench_contiguous(primary_w, args.steps, args.warmup, device, scrub)
@@ -653,9 +707,7 @@ def main():
         "queries_per_s": round(p["queries_per_s"], 1),
         "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(roof_achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": ("balanced_kernel<128, bf16>" + (" (merging in place)" if p["launches"] == 1 else "")
-                                if p["num_splits"] == -1000 else "split_kv_kernel<128, bf16, direct>"
-                                if p["num_splits"] == 1 else "split_kv_kernel<128, bf16, partials>"),
+                     "kernel": p["roofline"]["kernel"],
                      "kernel_ms": p["split_kernel_ms"],
                      "kernel_bytes": p["split_kernel_bytes"],
                      "trace_avg_us": trace_avg_from_profiles(
@@ -680,7 +732,8 @@ def main():
                           "queries_per_s": round(v["queries_per_s"], 1), "ms_per_step": v["ms_per_step"],
                           "window": v["window"], "sinks": v["sinks"], "num_splits": v["num_splits"]}
     line["split_sweep"] = {"steps": sweep_steps, "warmup": sweep_warmup, "gbs": sweep}
-    line["read_reference"] = reference
+    line["stream_ceiling"] = ceiling
+    line["roofline"]["frac_of_stream_ceiling"] = round(roof_achieved / ceiling["gbs"], 4)
     line["append"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in app.items()}
     line["metadata"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in meta.items()}
     line["contiguous"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in contig.items()}

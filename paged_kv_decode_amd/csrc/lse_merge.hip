@@ -25,9 +25,15 @@ namespace {
 // partials per batch of independent loads, accumulated with weights
 // exp(lse_j - M_w).  With WPR > 1 the waves' (M_w, W_w, o_w) are then combined
 // in LDS by the same rule.
+// The merge kernel's waves take up to 16 partials in one round trip of loads
+// (a wave of the partition kernel's in-place merge, at the edge of its
+// registers, takes 8).
+template <int D>
+using KernelRowMerge = RowMerge<D, false, 16>;
+
 template <int D, int WPR>
 __global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(const MergeParams p) {
-  constexpr int EPL = RowMerge<D>::EPL;
+  constexpr int EPL = KernelRowMerge<D>::EPL;
   constexpr int WAVES = WPR == 1 ? 4 : WPR;
   __shared__ float sm_m[WAVES], sm_w[WAVES];
   __shared__ float sm_o[WPR == 1 ? 1 : WAVES * D];
@@ -88,7 +94,7 @@ __global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(co
   ls *= WPR;
   os *= WPR;
 
-  RowMerge<D> r;
+  KernelRowMerge<D> r;
   r.run(lp, ls, op, os, mine, lane);
 
   if constexpr (WPR > 1) {

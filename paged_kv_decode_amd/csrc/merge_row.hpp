@@ -50,10 +50,14 @@ __device__ __forceinline__ float fold_sink(float& lse, float sink) {
 // COHERENT: read the partials with agent-scope atomic loads, which see the
 // coherent copy even when another XCD's workgroup wrote them during this
 // kernel (ordinary loads may hit a stale line of this XCD's L2).
-template <int D, bool COHERENT = false>
+// UNROLL: partials loaded per batch (and the most the one-round-trip path
+// takes).  For up to 64 partials both paths add the same products in the same
+// order, so the choice changes no bit of the result (but for the sign of a
+// row that sums to zero exactly).
+template <int D, bool COHERENT = false, int UNROLL_ = 8>
 struct RowMerge {
   static constexpr int EPL = D >= 64 ? D / 64 : 1;  // elements per lane
-  static constexpr int UNROLL = 8;
+  static constexpr int UNROLL = UNROLL_;
   float M, W;
   float o[EPL];
 
