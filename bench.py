@@ -386,6 +386,35 @@ def split_sweep(w, steps, warmup, device, scrub):
     return out
 
 
+def inner_loop_ab(w, steps, warmup, device, scrub):
+    """Direct output (one workgroup per (sequence, KV head)) with the matrix-core
+    inner loop (paged_decode, num_splits = 1) against the vector-ALU inner loop
+    (pkd_decode_valu) on the same inputs, each timed like the metric."""
+    import torch
+    from paged_kv_decode_amd import binding as B
+    nbytes = algorithmic_bytes(w)
+    r = Runner(w, 1, device)
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    mfma = _cold_steps(r.stream, steps, scrub, r.step)
+    out = torch.empty_like(r.out)
+    lse = torch.empty_like(r.lse)
+
+    def valu():
+        st = B.pkd_decode_valu(r.dims, r.q, r.k, r.v, r.bt, r.lens, w.scale, out, lse, r.handle)
+        if st != 0:
+            raise B.PkdError(st)
+    for _ in range(warmup):
+        valu()
+    torch.cuda.synchronize()
+    vt = _cold_steps(r.stream, steps, scrub, valu)
+    del r
+    g = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
+    return {"matrix_core_us": round(mfma * 1e3, 2), "matrix_core_gbs": g(mfma), "vector_alu_us": round(vt * 1e3, 2),
+            "vector_alu_gbs": g(vt)}
+
+
 # Launch shapes of the read-only stream kernel (pkd_stream_read) timed as the
 # measured ceiling: (pattern, workgroups, waves, KiB in flight per batch).
 # Pattern 0 reads whole lines of each 256-byte column (one KV head's slice of
@@ -614,6 +643,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="time only the named workloads (for a profiler run) and print no JSON line")
+    ap.add_argument("--inner-loop-ab-only", action="store_true",
+                    help="time only the matrix-core / vector-ALU direct-output A/B of the named workloads "
+                         "(for a profiler run) and print no JSON line")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "CMD", "OUT_MD"),
@@ -642,6 +674,12 @@ def main():
     del calib
 
     names = list(wl.WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
+    if args.inner_loop_ab_only:
+        for name in names:
+            w = wl.make_workload(wl.WORKLOADS[name], tail="zero")
+            print(f"# inner loop A/B {name}: {inner_loop_ab(w, args.steps, args.warmup, device, scrub)}",
+                  file=sys.stderr, flush=True)
+        return
     if PRIMARY not in names and not args.profile_only:
         names = [PRIMARY] + names
     results = {}
@@ -668,7 +706,9 @@ def main():
     sweep = {name: split_sweep(w, sweep_steps, sweep_warmup, device, scrub) for name, w in sweep_w.items()}
     for name, row in sweep.items():
         print(f"# num_splits sweep {name} (GB/s): {row}", file=sys.stderr, flush=True)
-    del sweep_w
+    ab = {name: inner_loop_ab(w, sweep_steps, sweep_warmup, device, scrub) for name, w in sweep_w.items()}
+    for name, row in ab.items():
+        print(f"# inner loop A/B {name} (direct output): {row}", file=sys.stderr, flush=True)
     ceiling = stream_ceiling(results[PRIMARY]["algorithmic_bytes"], max(args.steps // 2, 10), 3, device, scrub)
     print(f"# stream ceiling ({ceiling['bytes']} bytes, 256 of every 2048): {ceiling['gbs']:.0f} GB/s = "
           f"{ceiling['pct_of_peak']:.1f}% of peak (shape {ceiling['best_shape']}); operand layout "
@@ -733,6 +773,7 @@ def main():
                           "window": v["window"], "sinks": v["sinks"], "num_splits": v["num_splits"]}
     line["split_sweep"] = {"steps": sweep_steps, "warmup": sweep_warmup, "gbs": sweep}
     line["stream_ceiling"] = ceiling
+    line["inner_loop_ab"] = {"steps": sweep_steps, "rows": ab}
     line["roofline"]["frac_of_stream_ceiling"] = round(roof_achieved / ceiling["gbs"], 4)
     line["append"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in app.items()}
     line["metadata"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in meta.items()}

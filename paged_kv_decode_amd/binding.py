@@ -48,7 +48,7 @@ EXPORTED = ("paged_decode", "paged_decode_ext", "paged_decode_partition", "paged
             "paged_decode_merge",
             "paged_decode_check_tables", "paged_kv_append", "paged_decode_metadata", "contiguous_decode",
             "contiguous_decode_workspace_bytes", "paged_decode_status_string", "pkd_stream_read",
-            "pkd_stream_read_sink_bytes", "paged_decode_ext_noalloc")
+            "pkd_stream_read_sink_bytes", "paged_decode_ext_noalloc", "pkd_decode_valu")
 
 
 class PkdError(RuntimeError):
@@ -159,6 +159,8 @@ _lib.contiguous_decode.argtypes = [ctypes.POINTER(pkd_contig_dims), _p, _p, _p, 
 _lib.contiguous_decode.restype = _i32
 _lib.contiguous_decode_workspace_bytes.argtypes = [ctypes.POINTER(pkd_contig_dims), _i32]
 _lib.contiguous_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.pkd_decode_valu.argtypes = [_dims_p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p]
+_lib.pkd_decode_valu.restype = _i32
 _lib.pkd_stream_read.argtypes = [_p, ctypes.c_int64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]
 _lib.pkd_stream_read.restype = _i32
 _lib.pkd_stream_read_sink_bytes.argtypes = [_i32, _i32]
@@ -283,6 +285,11 @@ def contiguous_decode(cd, q, k, v, seq_lens, k_scale, v_scale, sinks, scale, out
 
 def contiguous_decode_workspace_bytes(cd, num_splits: int) -> int:
     return _lib.contiguous_decode_workspace_bytes(None if cd is None else ctypes.byref(cd), int(num_splits))
+
+
+def pkd_decode_valu(dims, q, k_cache, v_cache, block_table, seq_lens, scale, out, lse, stream) -> int:
+    return _lib.pkd_decode_valu(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _ptr(stream))
 
 
 def pkd_stream_read(buf, nbytes, row_bytes, chunk_bytes, pattern, workgroups, waves, batch_kb, nontemporal, sink,

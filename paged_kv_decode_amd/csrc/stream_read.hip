@@ -148,6 +148,8 @@ int32_t pkd_stream_read(const void* buf, int64_t bytes, int32_t row_bytes, int32
   if (workgroups < 1 || workgroups > (1 << 20) || waves < 1 || waves > 8 || (nontemporal != 0 && nontemporal != 1))
     return PKD_ERR_BAD_DIMS;
   if (batch_kb != 4 && batch_kb != 8 && batch_kb != 16 && batch_kb != 32) return PKD_ERR_BAD_DIMS;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PKD_ERR_DEVICE;
   pkd::StreamParams p{};
   p.buf = static_cast<const uint8_t*>(buf);
   p.blocks = bytes / 1024;

@@ -422,6 +422,27 @@ def test_balanced_mode_rules():
     assert call_ext(too_many, S=b.PKD_SPLITS_BALANCED, ws=FAKE, ws_bytes=1 << 30) == b.PKD_ERR_NUM_SPLITS
 
 
+def test_valu_entry_argument_checks():
+    """pkd_decode_valu takes a bf16 cache, head_dim 64 or 128, G in {1, 2, 4} and
+    page sizes that are multiples of 16; everything else is rejected on the host."""
+    def v(d, q=FAKE, lse=None, out=FAKE):
+        return b.pkd_decode_valu(d, q, FAKE, FAKE, FAKE, FAKE, 0.125, out, lse, None)
+    assert v(None) == b.PKD_ERR_NULL_POINTER
+    assert v(dims(head_dim=256)) == b.PKD_ERR_HEAD_DIM
+    assert v(dims(head_dim=32)) == b.PKD_ERR_HEAD_DIM
+    assert v(dims(kv_dtype=b.PKD_DTYPE_FP8_E4M3)) == b.PKD_ERR_DTYPE
+    assert v(dims(num_q_heads=8, num_kv_heads=1)) == b.PKD_ERR_BAD_DIMS  # G = 8
+    assert v(dims(num_q_heads=6, num_kv_heads=4)) == b.PKD_ERR_GQA
+    assert v(dims(page_size=24)) == b.PKD_ERR_BAD_DIMS
+    assert v(dims(), q=None) == b.PKD_ERR_NULL_POINTER
+    assert v(dims(), q=FAKE + 8) == b.PKD_ERR_ALIGNMENT
+    assert v(dims(), lse=FAKE + 2) == b.PKD_ERR_ALIGNMENT
+    assert v(dims(batch=0)) == b.PKD_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert v(dims()) == b.PKD_ERR_DEVICE
+
+
 def test_one_hip_runtime_in_process():
     """The library binds to PyTorch's HIP runtime instead of mapping a second one."""
     assert len(b._hip_runtimes_mapped()) <= 1

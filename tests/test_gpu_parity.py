@@ -1218,3 +1218,43 @@ def test_largest_q_len_with_causal_window_and_sinks(B):
         for S in (1, 3, BAL):
             out, lse = run(B, w, S, t)
             check(out, lse, *ref, what=f"q_len 64 Hq={hq} S={S}")
+
+
+# ---- the vector-ALU inner loop (measurement entry) ------------------------------
+
+VALU_CASES = [
+    # (B, Hq, Hkv, D, ps, seq_lens, seed)
+    (5, 32, 8, 128, 64, [700, 2, 0, 3000, 64], 901),
+    (4, 16, 8, 64, 16, [1, 17, 300, 33], 902),
+    (3, 8, 8, 128, 32, [5000, 31, 129], 903),
+    (6, 8, 4, 64, 48, [95, 96, 97, 1, 480, 0], 904),
+]
+
+
+def run_valu(B, w, t):
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    out = torch.full(t["q"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(t["q"].shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    st = B.pkd_decode_valu(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale, out, lse,
+                           B.current_stream_handle(0))
+    assert st == 0, B.paged_decode_status_string(st)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("case", VALU_CASES)
+def test_valu_entry_matches_oracle(B, case):
+    """The vector-ALU kernel against the oracle (NaN tails, -1 padding), G = 4, 2, 1
+    and page sizes 16 to 64."""
+    bq, hq, hkv, d, ps, lens, seed = case
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, "bf16", seed)
+    out, lse = run_valu(B, w, dev(w))
+    check(out, lse, *oracle_full(w), what=f"valu {case[:5]}")
+
+
+@pytest.mark.parametrize("name", ["llama_b32_d128_ps64", "batch128_d128_ps128"])
+def test_valu_entry_full_size(B, name):
+    """Every row of the B=32 and B=128 steps, as timed beside the matrix-core kernels."""
+    w = wl.make_workload(wl.WORKLOADS[name], tail="nan")
+    out, lse = run_valu(B, w, dev(w))
+    check(out, lse, *oracle_full(w), what=f"valu {name}")
