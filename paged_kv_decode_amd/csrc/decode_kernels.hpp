@@ -67,6 +67,25 @@ split_kv_kernel(const SplitParams p) {
 
   const int L = p.seq_lens[b];
   const int chunk = p.chunk;  // tokens per split, the same for every sequence
+
+  // Loads that do not depend on the length, issued while it is in flight: the
+  // query rows, and (without a window, so that the split starts at token
+  // split * chunk) the block-table entries the split can use, staged in LDS.
+  // Entries past the sequence's last page may be among them; they are not used.
+  int32_t* sbt = reinterpret_cast<int32_t*>(smem + C::BT_OFFSET);
+  const bool contiguous = Geo::contiguous(p);
+  const int ps = p.page_size;
+  const int64_t spec_tok = (int64_t)split * chunk;
+  const int spec_first = (int)min(spec_tok / ps, (int64_t)p.max_pages);
+  const int spec_n = (int)min((int64_t)p.max_pages - spec_first, (int64_t)chunk / ps + 2);
+  const bool spec = !contiguous && p.window == 0 && spec_n <= C::BT_ENTRIES;
+  if (spec)
+    for (int i = tid; i < spec_n; i += kWaves * 64) sbt[i] = p.block_table[(int64_t)b * p.max_pages + spec_first + i];
+  {
+    const LaneRow lq = lane_row<D, STRIDED>(p, b, kvh, hg, A.n, 0, 0, 0);
+    A.load_q(p.q + lq.qoff, lq.valid);
+  }
+
   // Splits cover [lo, L): tokens below the first visible 16-token group (with
   // a sliding window) are never read.
   const int lo = seq_first_token(p, L, p.window);
@@ -101,7 +120,6 @@ split_kv_kernel(const SplitParams p) {
   const int tok_stride = Geo::tok_stride(p);  // bytes between consecutive slots of a page
   const int64_t page_stride = Geo::page_stride(p);
   const int64_t head_off = (int64_t)kvh * Geo::head_stride(p);
-  const int ps = p.page_size;
   // The block table is read-only for the whole launch (constant address space).
   const __attribute__((address_space(4))) int32_t* bt =
       (const __attribute__((address_space(4))) int32_t*)(p.block_table + (int64_t)b * p.max_pages);
@@ -111,21 +129,19 @@ split_kv_kernel(const SplitParams p) {
     s_rows[tid] = lr.row;
     s_orow[tid] = lr.ooff;
   }
-  A.load_q(p.q + lr.qoff, lr.valid);
   A.qk_scale = p.qk_scale_log2;
   if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
   A.reset();
 
   // The split's block-table entries are staged in LDS once (when they fit), so
   // that per-tile page lookups are short LDS reads rather than dependent HBM
-  // reads on the path of every tile's loads.  Without a block table (contiguous
-  // K/V) sequence b is page b.
-  int32_t* sbt = reinterpret_cast<int32_t*>(smem + C::BT_OFFSET);
-  const bool contiguous = Geo::contiguous(p);
+  // reads on the path of every tile's loads (already done above without a
+  // window: there the split's first page is spec_first).  Without a block
+  // table (contiguous K/V) sequence b is page b.
   const int first_page = s0 / ps;
   const int n_pages = lim / ps - first_page + 1;
-  const bool staged = !contiguous && n_pages <= C::BT_ENTRIES;
-  if (staged)
+  const bool staged = spec || (!contiguous && n_pages <= C::BT_ENTRIES);
+  if (staged && !spec)
     for (int i = tid; i < n_pages; i += kWaves * 64) sbt[i] = bt[first_page + i];
   __syncthreads();
   auto page_of = [&](int pidx) -> int { return contiguous ? b : staged ? sbt[pidx - first_page] : bt[pidx]; };
