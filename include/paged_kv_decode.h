@@ -401,10 +401,12 @@ typedef struct {
 
 /*
  * paged_decode_metadata -- build the block table and lengths that paged_decode
- * reads from a serving runtime's token map, in one launch: the fused decode
- * metadata setup of the sglang fuse/overlap catalogue (section 1, the
- * flashattention backend's normal_decode_set_metadata row: seq-len cast/add,
- * prefix sum, req-to-token gather, page-table divide, optional SWA tables).
+ * reads from a serving runtime's token map, in one launch (the decode metadata
+ * step that the sglang fuse/overlap catalogue, section 1, lists as fused for
+ * the flashattention backend).  It extends each length by the step's new
+ * tokens, forms their running sums, looks up each page through the token map
+ * and, with a window, also builds the tables without the pages below it;
+ * the outputs below define each of these.
  *
  *   md                host; see pkd_meta_dims.
  *   req_to_token      [req_rows][req_stride] int32: the KV slot (page * page_size +

@@ -1,11 +1,10 @@
 // Decode metadata preparation for gfx950: the block table and lengths that
 // decode reads, built on the device from the serving runtime's token map.
 //
-// This is the fused decode metadata setup of the sglang fuse/overlap catalogue
-// (section 1, the flashattention backend's normal_decode_set_metadata row):
-// seq-len cast/add, prefix sum, req-to-token gather, page-table divide and the
-// optional sliding-window tables, here in one launch.  For batch entry b with
-// request row r = req_pool_indices[b] and L = seq_lens[b] + extend:
+// The sglang fuse/overlap catalogue (section 1) lists this step as one fused
+// kernel for its flashattention backend's decode.  Here it is one launch that
+// derives, for batch entry b with request row r = req_pool_indices[b] and
+// L = seq_lens[b] + extend (the lengths after this step's new tokens):
 //   cache_seqlens[b] = L (int32), cu_seqlens_k = exclusive prefix sums,
 //   page_table[b][j] = req_to_token[r][j * ps] / ps for j < ceil(L / ps), else -1,
 //   with a window W: f = max(L - q_len - W + 1, 0) / ps pages are dropped:
