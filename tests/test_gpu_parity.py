@@ -790,6 +790,23 @@ def test_append_matches_oracle_bitwise(B, case):
     assert np.array_equal(got_v, ref_v.reshape(got_v.shape)), f"V cache differs {case}"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_append_rope_against_fp64_rotation(B, dtype):
+    """The kernel's rotated K rows against the rotation computed in fp64 (not only against
+    the oracle's fp32 recipe): every stored value within half a code step plus the fp32
+    recipe's error bound, codes within one of the exact code where the two terms do not
+    cancel, and nearly all exactly the exact code."""
+    import rope_reference as rr
+    w = wl.append_workload(2000, 8, 128, 64, 40, dtype, rope=True, seed=512, scale_range=(0.01, 0.05))
+    t = _dev_append(w)
+    B.append(**t)
+    torch.cuda.synchronize()
+    worst, exact_share, dist = rr.check(w, wl.as_numpy_bits(t["k_cache"].cpu()), dtype)
+    assert worst <= 1.0, f"error / derived bound {worst:.3g}"
+    assert dist <= 1
+    assert exact_share > 0.99
+
+
 def test_append_fp8_conversion_on_every_bf16_value(B):
     """Scale 1: every bf16 value in [-448, 448], including exact midpoints between FP8 codes,
     is encoded by the kernel exactly as by the oracle's nearest-code, ties-to-even rule."""

@@ -529,6 +529,22 @@ def test_rope_rotations_compose_and_keep_pair_norms():
     assert np.max(np.abs(r - x)) > 0.1
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_rope_append_within_one_code_of_the_fp64_rotation(kv_dtype):
+    """The append's fp32 recipe (a product, then one fused multiply-add, then the cache
+    rounding) against the rotation computed in fp64: every stored value is within half
+    a code step plus the fp32 recipe's error bound of the exact value, every code is the
+    exact code or a neighbour where that fp32 error is under a quarter step (no
+    cancellation), and nearly all codes are the exact value's code."""
+    import rope_reference as rr
+    w = wl.append_workload(300, 4, 64, 16, 40, kv_dtype, seed=310, rope=True, scale_range=(0.01, 0.05))
+    kc, _ = _append(w)
+    worst, exact_share, dist = rr.check(w, kc, kv_dtype)
+    assert worst <= 1.0, f"error / derived bound {worst:.3g}"
+    assert dist <= 1
+    assert exact_share > 0.99
+
+
 def test_rope_row_is_selected_by_position_and_out_of_table_positions_write_nothing():
     w = wl.append_workload(20, 2, 16, 4, 10, "bf16", seed=305, rope=True)
     kc, _ = _append(w)
