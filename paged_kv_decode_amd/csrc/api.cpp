@@ -81,6 +81,8 @@ int32_t check_dims(const Dims* d) {
   if (!valid_head_dim(d->head_dim)) return PKD_ERR_HEAD_DIM;
   if (d->kv_dtype != PKD_DTYPE_BF16 && d->kv_dtype != PKD_DTYPE_FP8_E4M3) return PKD_ERR_DTYPE;
   if ((int64_t)d->max_pages_per_seq * d->page_size > INT32_MAX) return PKD_ERR_BAD_DIMS;
+  // Query rows per sequence (and so per KV head) stay far inside int32.
+  if ((int64_t)d->q_len * d->num_q_heads > (1 << 24)) return PKD_ERR_BAD_DIMS;
   if ((int64_t)d->num_kv_heads * head_groups(*d) > 65535) return PKD_ERR_BAD_DIMS;
   // Offsets inside one 16-token group of a page are computed in 32 bits.
   if ((int64_t)d->num_kv_heads * d->head_dim * 2 * 16 > INT32_MAX) return PKD_ERR_BAD_DIMS;

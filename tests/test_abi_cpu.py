@@ -186,6 +186,8 @@ def test_contract_prototype_called_through_ctypes():
     (dict(head_dim=512), b.PKD_ERR_HEAD_DIM),
     (dict(kv_dtype=7), b.PKD_ERR_DTYPE),
     (dict(max_pages_per_seq=2**20, page_size=2**12), b.PKD_ERR_BAD_DIMS),
+    (dict(num_q_heads=2**25, num_kv_heads=1), b.PKD_ERR_BAD_DIMS),
+    (dict(num_q_heads=2**31 - 1, num_kv_heads=1), b.PKD_ERR_BAD_DIMS),
 ])
 def test_bad_dims_are_rejected(kw, status):
     d = dims(**kw)
