@@ -193,8 +193,11 @@ def test_bit_exact_one_hot_probe(B, dtype, d, ps):
 # The full-size shapes the probe and the determinism check also run at: the
 # B=32, B=128 and FP8 B=64 workloads' heads, page sizes and lengths.
 FULL_SHAPES = {
+    "tiny": ("tiny_b2_d64_ps16", "bf16"),
     "llama_b32": ("llama_b32_d128_ps64", "bf16"),
     "batch128": ("batch128_d128_ps128", "bf16"),
+    "longctx_b1_d32": ("longctx_b1_d32", "bf16"),
+    "longctx_b16_d256": ("longctx_b16_d256", "bf16"),
     "fp8kv_b64": ("fp8kv_b64_d128_ps64", "fp8_e4m3"),
 }
 
