@@ -20,8 +20,9 @@
 //   4. QK^T on MFMA (v_mfma_f32_16x16x32_bf16): A = 16 K rows x 32 dims read
 //      from the LDS tile (or, for shorter rows, loaded straight in that layout),
 //      B = the packed query heads (zero-padded to 16),
-//   5. online softmax in base 2 with the running max shared across the four
-//      lane groups by cross-lane xor shuffles,
+//   5. online softmax in base 2 against a per-row reference maximum, common
+//      to the four lane groups that hold the row's scores (formed with
+//      cross-lane xor shuffles only in the tiles that raise it),
 //   6. PV on MFMA: A = V^T gathered by transposing LDS reads
 //      (ds_read_b64_tr_b16), B = P^T taken from the QK accumulator registers
 //      without any shuffle (token order inside each 32-token chunk is permuted
@@ -486,8 +487,6 @@ struct WaveAttn {
           mt = fmaxf(mt, sacc[blk][i]);
         }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
     // m_run is a reference maximum rather than the exact running maximum: it
     // is raised (and l and O rescaled by 2^(old - new)) only when a tile's
     // maximum exceeds it by more than kRescaleSlack, so every weight
@@ -495,7 +494,13 @@ struct WaveAttn {
     // the rescale of the accumulators is skipped.  Raised, it becomes the
     // tile's maximum.  A row that has seen no unmasked token keeps m = -inf;
     // subtracting 0 then gives e = 0 instead of NaN.
+    // A row's tile maximum exceeds the threshold exactly when one of its four
+    // lane groups' maxima does, so the wave-wide test needs no cross-lane
+    // exchange; the row maximum (two shuffles through LDS) is formed only when
+    // some row is raised.
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float m_new = mt > m_run + kRescaleSlack ? mt : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
       m_run = m_new;
