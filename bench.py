@@ -91,6 +91,7 @@ class Runner:
         self.ext = B.ext_for(self.q, causal=w.spec.causal, window=w.spec.window)
         self.S = num_splits if num_splits != 0 else B.paged_decode_num_splits_ext(self.dims, self.ext, 0)
         self.launches = B.paged_decode_launches(self.dims, self.ext, self.S)  # 1: the partition writes out itself
+        self.path = B.paged_decode_path(self.dims, self.ext, 0 if self.sinks is None else 1, self.S)
         # plain decode in a numbered split mode goes through paged_decode itself
         self.plain = self.ext is None and self.sinks is None and 1 <= self.S <= B.PKD_MAX_SPLITS
         self.out = torch.empty(self.q.shape, dtype=torch.bfloat16, device=device)
@@ -233,7 +234,7 @@ def bench_one(name, steps, warmup, num_splits, device, scrub, warm_pass=True):
         num_kv_heads=w.spec.num_kv_heads, head_dim=w.spec.head_dim, page_size=w.spec.page_size,
         kv_dtype=w.spec.kv_dtype, q_len=w.spec.q_len, causal=w.spec.causal, window=w.spec.window,
         sinks=getattr(w, "sinks", None) is not None,
-        num_splits=r.S, launches=r.launches, tokens=int(w.seq_lens.sum()),
+        num_splits=r.S, launches=r.launches, path=r.path, tokens=int(w.seq_lens.sum()),
         algorithmic_bytes=nbytes, ms_per_step=step_mean,
         ms_p10=srt[int(0.1 * (steps - 1))], ms_median=srt[(steps - 1) // 2], ms_p90=srt[int(0.9 * (steps - 1))],
         gbs=nbytes / (step_mean * 1e-3) / 1e9,
@@ -253,18 +254,24 @@ def bench_one(name, steps, warmup, num_splits, device, scrub, warm_pass=True):
     # whole step when there is no merge kernel) against the HBM peak.
     res["roofline"] = {"bound": "hbm", "achieved": round(res["split_kernel_gbs"], 2), "peak": PEAK_HBM_GBS,
                        "unit": "GB/s", "frac": round(res["split_kernel_gbs"] / PEAK_HBM_GBS, 4),
-                       "kernel": kernel_label(w.spec, r.S, r.launches), "step_frac": round(res["gbs"] / PEAK_HBM_GBS, 4)}
+                       "kernel": kernel_label(w.spec, r.path), "step_frac": round(res["gbs"] / PEAK_HBM_GBS, 4)}
     return res, w
 
 
-def kernel_label(spec, S, launches):
-    """The partition kernel a mode runs, as the profiles name it."""
+def kernel_label(spec, path):
+    """The partition kernel a mode runs (paged_decode_path), as the profiles name it."""
+    from paged_kv_decode_amd import binding as B
     t = f"<{spec.head_dim}, {'fp8' if spec.kv_dtype != 'bf16' else 'bf16'}>"
-    if S == -1000:
-        return "balanced_kernel" + t + (" (merging in place)" if launches == 1 else " + lse_merge_kernel")
-    if S == 1:
-        return "split_kv_kernel" + t + " (direct output)"
-    return "split_kv_kernel" + t + " (partials) + lse_merge_kernel"
+    return {B.PKD_PATH_DIRECT: "split_kv_kernel" + t + " (direct output)",
+            B.PKD_PATH_DIRECT_LDS: "lds_direct_kernel" + t + " (direct output, tiles loaded into LDS)",
+            B.PKD_PATH_SPLITS: "split_kv_kernel" + t + " (partials) + lse_merge_kernel",
+            B.PKD_PATH_BALANCED: "balanced_kernel" + t + " (merging in place)",
+            B.PKD_PATH_BALANCED_MERGE: "balanced_kernel" + t + " + lse_merge_kernel"}[path]
+
+
+# Kernel-name prefixes of each path's partition kernel in rocprofv3's traces.
+PATH_TRACE_PREFIX = {1: "pkd::split_kv_kernel<", 2: "pkd::lds_direct_kernel", 3: "pkd::split_kv_kernel<",
+                     4: "pkd::balanced_kernel<", 5: "pkd::balanced_kernel<"}
 
 
 CPU_SAMPLE_S = 10.0  # length of the CPU-baseline sample
@@ -439,32 +446,73 @@ def split_sweep(w, steps, warmup, device, scrub):
     return out
 
 
-def inner_loop_ab(w, steps, warmup, device, scrub):
-    """Direct output (one workgroup per (sequence, KV head)) with the matrix-core
-    inner loop (paged_decode, num_splits = 1) against the vector-ALU inner loop
-    (pkd_decode_valu) on the same inputs, each timed like the metric."""
+def _direct_legs(r, w):
+    """Pre-marshalled calls of the three direct-output kernels on each K/V copy of
+    runner r: the register-staged grid kernel (paged_decode_ext, num_splits = 1,
+    with sink logits of -inf, which change no bit of the result but keep the call
+    off the LDS-staged kernel), the LDS-staged kernel (pkd_decode_lds) and the
+    vector-ALU kernel (pkd_decode_valu)."""
+    import ctypes
     import torch
     from paged_kv_decode_amd import binding as B
-    import ctypes
+    lib = B.lib()
+    assert B.paged_decode_path(r.dims, None, 1, 1) == B.PKD_PATH_DIRECT
+    no_sink = torch.full((w.spec.num_q_heads,), float("-inf"), dtype=torch.float32, device=r.q.device)
+    out = torch.empty_like(r.out)
+    lse = torch.empty_like(r.lse)
+    d = ctypes.byref(r.dims)
+    reg = [(d, None, r.q.data_ptr(), k.data_ptr(), v.data_ptr(), r.bt.data_ptr(), r.lens.data_ptr(), None, None,
+            no_sink.data_ptr(), float(w.scale), out.data_ptr(), lse.data_ptr(), 1, None, 0, r.handle)
+           for k, v in r.copies]
+    alt = [(d, r.q.data_ptr(), k.data_ptr(), v.data_ptr(), r.bt.data_ptr(), r.lens.data_ptr(), float(w.scale),
+            out.data_ptr(), lse.data_ptr(), r.handle) for k, v in r.copies]
+
+    def leg(fn, args):
+        def call(c):
+            st = fn(*args[c])
+            if st != 0:
+                raise B.PkdError(st)
+        return call
+    return {"register_staged": leg(lib.paged_decode_ext, reg), "lds_staged": leg(lib.pkd_decode_lds, alt),
+            "vector_alu": leg(lib.pkd_decode_valu, alt), "_keep": (no_sink, out, lse)}
+
+
+def inner_loop_ab(w, steps, warmup, device, scrub):
+    """Direct output (one workgroup per (sequence, KV head)) three ways on the same
+    inputs, each timed like the metric: matrix-core tile steps with the next
+    tile's loads held in registers (the grid kernel), the same steps with tiles
+    loaded straight into LDS stages, and a vector-ALU inner loop."""
     nbytes = algorithmic_bytes(w)
     r = _rotating_runner(w, 1, device)
     n = len(r.copies)
-    mfma = _back_to_back(r.stream, steps, warmup, n, r.step)
-    out = torch.empty_like(r.out)
-    lse = torch.empty_like(r.lse)
-    lib = B.lib()
-    args = [(ctypes.byref(r.dims), r.q.data_ptr(), k.data_ptr(), v.data_ptr(), r.bt.data_ptr(), r.lens.data_ptr(),
-             float(w.scale), out.data_ptr(), lse.data_ptr(), r.handle) for k, v in r.copies]
+    legs = _direct_legs(r, w)
+    out = {}
+    for name in ("register_staged", "lds_staged", "vector_alu"):
+        ms = _back_to_back(r.stream, steps, warmup, n, legs[name])
+        out[name + "_us"] = round(ms * 1e3, 2)
+        out[name + "_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del r, legs
+    return out
 
-    def valu(c):
-        st = lib.pkd_decode_valu(*args[c])
-        if st != 0:
-            raise B.PkdError(st)
-    vt = _back_to_back(r.stream, steps, warmup, n, valu)
-    del r
-    g = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
-    return {"matrix_core_us": round(mfma * 1e3, 2), "matrix_core_gbs": g(mfma), "vector_alu_us": round(vt * 1e3, 2),
-            "vector_alu_gbs": g(vt)}
+
+def decode_low_load(steps, warmup, device):
+    """The direct-output decode with only 8 workgroups on the chip (B = 1, 8 KV
+    heads of 8192 tokens, D = 128, S = 1), register- and LDS-staged: each
+    workgroup's streaming rate when the memory system is nearly idle, as for the
+    long items at the end of a step."""
+    from paged_kv_decode_amd import workloads as wl
+    L = 8192
+    w = wl.custom_workload(1, 32, 8, 128, 64, [L], seed=11, tail="zero", name="low_load_b1_l8192")
+    r = _rotating_runner(w, 1, device)
+    legs = _direct_legs(r, w)
+    per_wg = L * 128 * 2 * 2
+    res = {"workload": "B=1, Hq=32, Hkv=8, D=128, ps=64, L=8192, S=1 (8 workgroups)"}
+    for name in ("register_staged", "lds_staged"):
+        ms = _back_to_back(r.stream, steps, warmup, len(r.copies), legs[name])
+        res[name + "_us"] = round(ms * 1e3, 2)
+        res[name + "_gbs_per_workgroup"] = round(per_wg / (ms * 1e-3) / 1e9, 1)
+    del r, legs
+    return res
 
 
 # Launch shapes of the read-only stream kernel (pkd_stream_read) timed as the
@@ -472,9 +520,18 @@ def inner_loop_ab(w, steps, warmup, device, scrub):
 # Pattern 0 reads whole lines of each 256-byte column (one KV head's slice of
 # a 2 KiB token row: Hkv = 8, D = 128, bf16), the way the decode kernels load
 # K and V; pattern 1 reads the same bytes in the 16x16x32 matrix-core operand
-# layout (64 bytes of each of 16 rows per load), for comparison.
+# layout (64 bytes of each of 16 rows per load), for comparison; pattern 2 is
+# pattern 0 issued as direct-to-LDS loads (the load path of a pipeline staged
+# in shared memory instead of registers).
 STREAM_SHAPES = [(0, 256, 4, 8), (0, 256, 4, 16), (0, 1024, 4, 8), (0, 2048, 4, 4), (1, 256, 4, 8),
-                 (1, 1024, 4, 8)]
+                 (1, 1024, 4, 8), (2, 256, 4, 4), (2, 256, 4, 8), (2, 1024, 4, 4)]
+STREAM_PATTERNS = {0: "row order", 1: "matrix-core operand layout", 2: "row order, direct to LDS"}
+# The same streams with only 8 workgroups on the chip (one 256-byte column of
+# 8192 rows each, like one KV head of an 8192-token sequence): the rate one
+# compute unit reaches when the memory system is nearly idle, as in the tail of
+# a step whose long items outlast the rest.
+LOW_LOAD_SLICE = 16 << 20
+LOW_LOAD_SHAPES = [(0, 8, 4, 8), (2, 8, 4, 8), (0, 8, 8, 8), (2, 8, 8, 8)]
 
 
 def stream_ceiling(nbytes, steps, warmup, device, scrub):
@@ -509,15 +566,38 @@ def stream_ceiling(nbytes, steps, warmup, device, scrub):
         torch.cuda.synchronize()
         mean = e0.elapsed_time(e1) / steps
         gbs = n / (mean * 1e-3) / 1e9
-        rows.append({"pattern": "row order" if pattern == 0 else "matrix-core operand layout",
+        rows.append({"pattern": STREAM_PATTERNS[pattern],
                      "workgroups": wgs, "waves": waves, "kib_in_flight_per_batch": kb, "us": round(mean * 1e3, 2),
                      "gbs": round(gbs, 1), "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2)})
+    # Few workgroups: 16 MiB per call, cycling through every 16 MiB slice of the copies.
+    slices = [(bf, o) for bf in bufs for o in range(0, n - LOW_LOAD_SLICE + 1, LOW_LOAD_SLICE)]
+    low = []
+    for pattern, wgs, waves, kb in LOW_LOAD_SHAPES:
+        sink = torch.empty(B.pkd_stream_read_sink_bytes(wgs, waves) // 4, dtype=torch.int32, device=device)
+        args = [(bf.data_ptr() + o, LOW_LOAD_SLICE, row, chunk, pattern, wgs, waves, kb, 1, sink.data_ptr(), h)
+                for bf, o in slices]
+        for i in range(warmup):
+            if lib.pkd_stream_read(*args[i % len(args)]) != 0:
+                raise RuntimeError("pkd_stream_read refused its arguments")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            lib.pkd_stream_read(*args[i % len(args)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mean = e0.elapsed_time(e1) / steps
+        low.append({"pattern": STREAM_PATTERNS[pattern], "workgroups": wgs, "waves": waves,
+                    "kib_in_flight_per_batch": kb, "us": round(mean * 1e3, 2),
+                    "gbs_per_workgroup": round(LOW_LOAD_SLICE / wgs / (mean * 1e-3) / 1e9, 1)})
     del bufs
-    best = max((r for r in rows if r["pattern"] == "row order"), key=lambda r: r["gbs"])
-    best_mfma = max((r for r in rows if r["pattern"] != "row order"), key=lambda r: r["gbs"])
+    best = max((r for r in rows if r["pattern"] == STREAM_PATTERNS[0]), key=lambda r: r["gbs"])
+    best_mfma = max((r for r in rows if r["pattern"] == STREAM_PATTERNS[1]), key=lambda r: r["gbs"])
+    best_lds = max((r for r in rows if r["pattern"] == STREAM_PATTERNS[2]), key=lambda r: r["gbs"])
     return {"kernel": "pkd_stream_read (read-only, 16-byte non-temporal loads)", "bytes": n,
             "row_bytes": row, "column_bytes": chunk, "gbs": best["gbs"], "pct_of_peak": best["pct_of_peak"],
-            "best_shape": best, "operand_layout_best_gbs": best_mfma["gbs"], "shapes": rows}
+            "best_shape": best, "operand_layout_best_gbs": best_mfma["gbs"],
+            "direct_to_lds_best_gbs": best_lds["gbs"], "shapes": rows, "low_load": low}
 
 
 def cpu_baseline(w, nbytes):
@@ -616,7 +696,8 @@ def summarize_counters(fetch_csv, write_csv, workload, command_fetch, command_wr
 
     f_fac, f_name = calib(fetch)
     w_fac, w_name = calib(write)
-    part = [k for k in fetch if "pkd::" in k and ("balanced_kernel" in k or "split_kv_kernel" in k)]
+    part = [k for k in fetch if "pkd::" in k and ("balanced_kernel" in k or "split_kv_kernel" in k
+                                                  or "lds_direct_kernel" in k)]
     merge = [k for k in fetch if "pkd::" in k and "lse_merge_kernel" in k]
     assert part, "no partition kernel in the counter run"
     k = max(part, key=lambda x: len(fetch[x]))
@@ -775,7 +856,15 @@ def main():
     ceiling = stream_ceiling(results[PRIMARY]["algorithmic_bytes"], max(args.steps // 2, 10), 3, device, scrub)
     print(f"# stream ceiling ({ceiling['bytes']} bytes, 256 of every 2048): {ceiling['gbs']:.0f} GB/s = "
           f"{ceiling['pct_of_peak']:.1f}% of peak (shape {ceiling['best_shape']}); operand layout "
-          f"{ceiling['operand_layout_best_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+          f"{ceiling['operand_layout_best_gbs']:.0f} GB/s; direct to LDS {ceiling['direct_to_lds_best_gbs']:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    print(f"# stream with 8 workgroups (GB/s per workgroup): "
+          f"{[(r['pattern'], r['waves'], r['gbs_per_workgroup']) for r in ceiling['low_load']]}",
+          file=sys.stderr, flush=True)
+    low_decode = decode_low_load(max(args.steps // 2, 10), 10, device)
+    print(f"# decode with 8 workgroups (GB/s per workgroup): register-staged "
+          f"{low_decode['register_staged_gbs_per_workgroup']:.1f}, LDS-staged "
+          f"{low_decode['lds_staged_gbs_per_workgroup']:.1f}", file=sys.stderr, flush=True)
     app = bench_append(args.steps, args.warmup, device, scrub)
     meta = bench_metadata(primary_w, args.steps, args.warmup, device, scrub, window=1024)
     contig = bench_contiguous(primary_w, args.steps, args.warmup, device, scrub)
@@ -813,9 +902,7 @@ def main():
                      "kernel": p["roofline"]["kernel"],
                      "kernel_ms": p["split_kernel_ms"],
                      "kernel_bytes": p["split_kernel_bytes"],
-                     "trace_avg_us": trace_avg_from_profiles(
-                         PRIMARY, "pkd::balanced_kernel<128" if p["num_splits"] == -1000
-                         else "pkd::split_kv_kernel<128")},
+                     "trace_avg_us": trace_avg_from_profiles(PRIMARY, PATH_TRACE_PREFIX[p["path"]])},
         "workloads": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in results.items()},
     }
@@ -836,6 +923,7 @@ def main():
                           "window": v["window"], "sinks": v["sinks"], "num_splits": v["num_splits"]}
     line["split_sweep"] = {"steps": sweep_steps, "warmup": sweep_warmup, "gbs": sweep}
     line["stream_ceiling"] = ceiling
+    line["low_load"] = {"decode": low_decode, "stream": ceiling["low_load"]}
     line["inner_loop_ab"] = {"steps": sweep_steps, "rows": ab}
     line["roofline"]["frac_of_stream_ceiling"] = round(roof_achieved / ceiling["gbs"], 4)
     line["append"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in app.items()}

@@ -17,7 +17,10 @@
  * lane loads read 1 KB of a column in order; with pattern 1 (the operand layout
  * of a 16x16x32 matrix-core instruction, whose 16 rows sit in lanes l % 16)
  * they read 64 bytes of each of 16 consecutive rows, the next load the next
- * 64 bytes of those rows.  The 1 KB blocks of the
+ * 64 bytes of those rows; pattern 2 is pattern 0 issued as direct-to-LDS loads
+ * (global_load_lds_dwordx4), the load path of a pipeline staged in shared
+ * memory rather than registers, each wave cycling its two batches through an
+ * LDS ring of 2 * batch_kb KB.  The 1 KB blocks of the
  * column-major stream order are divided evenly among `workgroups` workgroups of
  * `waves` waves; a wave keeps two batches of batch_kb blocks (16 bytes per lane
  * per block) in flight, with nontemporal = 1 using non-temporal loads.
@@ -26,10 +29,13 @@
  *   bytes        > 0, a multiple of row_bytes and of 1024.
  *   row_bytes    a multiple of chunk_bytes.
  *   chunk_bytes  a power of two >= 16; (bytes / row_bytes) * chunk_bytes a multiple of 1024.
- *   pattern      0 or 1 (1: chunk_bytes >= 64 and bytes / row_bytes a multiple of 16).
+ *   pattern      0, 1 or 2 (1: chunk_bytes >= 64 and bytes / row_bytes a multiple of 16;
+ *                2: waves * 2 * batch_kb <= 128, the KB of LDS rings per workgroup).
  *   workgroups   1 .. 2^20;  waves 1 .. 8;  batch_kb in {4, 8, 16, 32};  nontemporal 0 or 1.
  *   sink         device uint32 array of pkd_stream_read_sink_bytes(workgroups, waves) bytes,
- *                overwritten (one word per thread).
+ *                overwritten (one word per thread: patterns 0 and 1 the XOR of every word the
+ *                thread loaded, pattern 2 the first word of the thread's 16 bytes in the
+ *                ring's first block after the last batch, 0 for a wave with no block).
  * Returns PKD_OK or a negative status of paged_kv_decode.h; argument errors enqueue nothing.
  * Enqueued on `stream` (a hipStream_t) without synchronising.
  */

@@ -39,16 +39,22 @@ PKD_SPLIT_ALIGN = 64
 PKD_SPLITS_AUTO = 0
 PKD_SPLITS_BALANCED = -1000
 PKD_BALANCED_MAX_BATCH = 1024
+PKD_PATH_DIRECT = 1
+PKD_PATH_DIRECT_LDS = 2
+PKD_PATH_SPLITS = 3
+PKD_PATH_BALANCED = 4
+PKD_PATH_BALANCED_MERGE = 5
 PKD_DTYPE_BF16 = 0
 PKD_DTYPE_FP8_E4M3 = 1
 
 EXPORTED = ("paged_decode", "paged_decode_ext", "paged_decode_partition", "paged_decode_finish",
-            "paged_decode_num_splits", "paged_decode_num_splits_ext", "paged_decode_launches",
+            "paged_decode_num_splits", "paged_decode_num_splits_ext", "paged_decode_launches", "paged_decode_path",
             "paged_decode_workspace_bytes", "paged_decode_workspace_bytes_ext", "paged_decode_partials",
             "paged_decode_merge",
             "paged_decode_check_tables", "paged_kv_append", "paged_decode_metadata", "contiguous_decode",
             "contiguous_decode_workspace_bytes", "paged_decode_status_string", "pkd_stream_read",
-            "pkd_stream_read_sink_bytes", "paged_decode_ext_noalloc", "pkd_decode_valu")
+            "pkd_stream_read_sink_bytes", "paged_decode_ext_noalloc", "pkd_decode_valu",
+            "pkd_decode_lds")
 
 
 class PkdError(RuntimeError):
@@ -139,6 +145,8 @@ _lib.paged_decode_num_splits_ext.argtypes = [_dims_p, _ext_p, _i32]
 _lib.paged_decode_num_splits_ext.restype = _i32
 _lib.paged_decode_launches.argtypes = [_dims_p, _ext_p, _i32]
 _lib.paged_decode_launches.restype = _i32
+_lib.paged_decode_path.argtypes = [_dims_p, _ext_p, _i32, _i32]
+_lib.paged_decode_path.restype = _i32
 _lib.paged_decode_workspace_bytes.argtypes = [_dims_p, _i32]
 _lib.paged_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.paged_decode_workspace_bytes_ext.argtypes = [_dims_p, _ext_p, _i32]
@@ -161,6 +169,8 @@ _lib.contiguous_decode_workspace_bytes.argtypes = [ctypes.POINTER(pkd_contig_dim
 _lib.contiguous_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.pkd_decode_valu.argtypes = [_dims_p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p]
 _lib.pkd_decode_valu.restype = _i32
+_lib.pkd_decode_lds.argtypes = [_dims_p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p]
+_lib.pkd_decode_lds.restype = _i32
 _lib.pkd_stream_read.argtypes = [_p, ctypes.c_int64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]
 _lib.pkd_stream_read.restype = _i32
 _lib.pkd_stream_read_sink_bytes.argtypes = [_i32, _i32]
@@ -235,6 +245,10 @@ def paged_decode_launches(dims, ext, num_splits: int) -> int:
     return _lib.paged_decode_launches(_dims_ref(dims), _dims_ref(ext), int(num_splits))
 
 
+def paged_decode_path(dims, ext, has_sinks: int, num_splits: int) -> int:
+    return _lib.paged_decode_path(_dims_ref(dims), _dims_ref(ext), int(has_sinks), int(num_splits))
+
+
 def paged_decode_workspace_bytes(dims, num_splits: int) -> int:
     return _lib.paged_decode_workspace_bytes(_dims_ref(dims), int(num_splits))
 
@@ -289,6 +303,11 @@ def contiguous_decode_workspace_bytes(cd, num_splits: int) -> int:
 
 def pkd_decode_valu(dims, q, k_cache, v_cache, block_table, seq_lens, scale, out, lse, stream) -> int:
     return _lib.pkd_decode_valu(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _ptr(stream))
+
+
+def pkd_decode_lds(dims, q, k_cache, v_cache, block_table, seq_lens, scale, out, lse, stream) -> int:
+    return _lib.pkd_decode_lds(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                 _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _ptr(stream))
 
 

@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpaged_kv_decode.so")
 SOURCES = ["decode_d32.hip", "decode_d64.hip", "decode_d128.hip", "decode_d256.hip", "split_kv_decode.hip",
            "lse_merge.hip", "kv_append.hip", "decode_metadata.hip", "stream_read.hip", "noalloc.hip",
-           "valu_decode.hip", "api.cpp"]
+           "valu_decode.hip", "lds_decode.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",

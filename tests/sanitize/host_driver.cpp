@@ -12,6 +12,7 @@
 
 #include "../../include/paged_kv_decode.h"
 #include "../../include/pkd_stream.h"
+#include "../../include/pkd_lds.h"
 #include "../../include/pkd_valu.h"
 
 namespace {
@@ -68,8 +69,10 @@ int main() {
                     const size_t ws = paged_decode_workspace_bytes_ext(&x, &e, S);
                     const int ns = paged_decode_num_splits_ext(&x, &e, 4096);
                     const int nl = paged_decode_launches(&x, &e, S);
+                    const int np = paged_decode_path(&x, &e, causal, S);
                     (void)ns;
                     (void)nl;
+                    (void)np;
                     const int st = paged_decode_ext(&x, &e, F, F, F, FI, FI, sc, sc, FF, 0.125f, F, FF, S, F,
                                                     ws ? ws : 256, nullptr);
                     // without a device: an argument error, or the missing device
@@ -86,6 +89,7 @@ int main() {
               paged_kv_append(&x, S, F, F, reinterpret_cast<const int64_t*>(F), nullptr, nullptr, 0, F, F, sc, sc,
                               nullptr);
               pkd_decode_valu(&x, F, F, F, FI, FI, 0.125f, F, FF, nullptr);
+              pkd_decode_lds(&x, F, F, F, FI, FI, 0.125f, F, FF, nullptr);
               paged_decode_check_tables(&x, FI, FI, reinterpret_cast<int32_t*>(F), nullptr);
               calls += 5;
             }
@@ -123,7 +127,10 @@ int main() {
     }
   for (int64_t bytes : {(int64_t)1 << 20, (int64_t)1 << 40, (int64_t)3})
     for (int wgs : {1, 256, 1 << 20, (1 << 20) + 1})
-      pkd_stream_read(F, bytes, 2048, 256, 0, wgs, 4, 8, 1, reinterpret_cast<uint32_t*>(F), nullptr);
+      for (int pattern : {0, 1, 2, 3})
+        for (int waves : {4, 8})
+          for (int kb : {4, 16, 32})
+            pkd_stream_read(F, bytes, 2048, 256, pattern, wgs, waves, kb, 1, reinterpret_cast<uint32_t*>(F), nullptr);
   size_t text = 0;
   for (int st = -20; st <= 1; ++st) text += std::strlen(paged_decode_status_string(st));
   if (text == 0) ++failures;

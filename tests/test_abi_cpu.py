@@ -445,6 +445,33 @@ def test_valu_entry_argument_checks():
         assert v(dims()) == b.PKD_ERR_DEVICE
 
 
+def test_lds_entry_argument_checks():
+    """pkd_decode_lds takes a bf16 cache, head_dim 128, G <= 16, page sizes that are
+    multiples of 16 and at most 512 pages per sequence; everything else is rejected
+    on the host."""
+    def v(d, q=FAKE, lse=None, out=FAKE):
+        return b.pkd_decode_lds(d, q, FAKE, FAKE, FAKE, FAKE, 0.125, out, lse, None)
+
+    def d128(**kw):
+        return dims(**{"head_dim": 128, **kw})
+    assert v(None) == b.PKD_ERR_NULL_POINTER
+    assert v(d128(head_dim=64)) == b.PKD_ERR_HEAD_DIM
+    assert v(d128(head_dim=256)) == b.PKD_ERR_HEAD_DIM
+    assert v(d128(kv_dtype=b.PKD_DTYPE_FP8_E4M3)) == b.PKD_ERR_DTYPE
+    assert v(d128(num_q_heads=32, num_kv_heads=1)) == b.PKD_ERR_BAD_DIMS  # G = 32
+    assert v(d128(num_q_heads=6, num_kv_heads=4)) == b.PKD_ERR_GQA
+    assert v(d128(page_size=24)) == b.PKD_ERR_BAD_DIMS
+    assert v(d128(max_pages_per_seq=513)) == b.PKD_ERR_BAD_DIMS
+    assert v(d128(), q=None) == b.PKD_ERR_NULL_POINTER
+    assert v(d128(), q=FAKE + 8) == b.PKD_ERR_ALIGNMENT
+    assert v(d128(), lse=FAKE + 2) == b.PKD_ERR_ALIGNMENT
+    assert v(d128(batch=0)) == b.PKD_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert v(d128()) == b.PKD_ERR_DEVICE
+        assert v(d128(num_q_heads=16, num_kv_heads=1, max_pages_per_seq=512)) == b.PKD_ERR_DEVICE
+
+
 def test_one_hip_runtime_in_process():
     """The library binds to PyTorch's HIP runtime instead of mapping a second one."""
     assert len(b._hip_runtimes_mapped()) <= 1
@@ -464,6 +491,30 @@ def test_launch_counts():
     assert b.paged_decode_launches(long1, None, b.PKD_SPLITS_BALANCED) == 2
     assert b.paged_decode_launches(b32, None, -5) == b.PKD_ERR_NUM_SPLITS
     assert b.paged_decode_launches(dims(head_dim=96), None, 1) == b.PKD_ERR_HEAD_DIM
+
+
+def test_paged_decode_path():
+    """The path query agrees with the launch counts; without a device the
+    LDS-staged direct kernel (which depends on the compute-unit count) is never
+    reported, and bad arguments give statuses."""
+    b32 = dims(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
+               num_pages=1500, max_pages_per_seq=64)
+    assert b.paged_decode_path(b32, None, 0, 1) == b.PKD_PATH_DIRECT
+    assert b.paged_decode_path(b32, None, 1, 1) == b.PKD_PATH_DIRECT
+    assert b.paged_decode_path(b32, None, 0, 4) == b.PKD_PATH_SPLITS
+    assert b.paged_decode_path(b32, None, 0, b.PKD_SPLITS_BALANCED) == b.PKD_PATH_BALANCED
+    long1 = dims(batch=1, num_q_heads=16, num_kv_heads=2, head_dim=64, page_size=64,
+                 num_pages=2048, max_pages_per_seq=2048)
+    assert b.paged_decode_path(long1, None, 0, b.PKD_SPLITS_BALANCED) == b.PKD_PATH_BALANCED_MERGE
+    for S in (0, 1, 3, b.PKD_SPLITS_BALANCED):
+        for d in (b32, long1):
+            path = b.paged_decode_path(d, None, 0, S)
+            want = 1 if path in (b.PKD_PATH_DIRECT, b.PKD_PATH_DIRECT_LDS, b.PKD_PATH_BALANCED) else 2
+            assert b.paged_decode_launches(d, None, S) == want
+    assert b.paged_decode_path(None, None, 0, 1) == b.PKD_ERR_NULL_POINTER
+    assert b.paged_decode_path(b32, None, 2, 1) == b.PKD_ERR_BAD_DIMS
+    assert b.paged_decode_path(b32, None, 0, -5) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_path(dims(head_dim=96), None, 0, 1) == b.PKD_ERR_HEAD_DIM
 
 
 # ---- paged_decode_metadata argument checks ----------------------------------
@@ -581,8 +632,13 @@ def test_stream_read_argument_checks():
     assert call(sink=None) == b.PKD_ERR_NULL_POINTER
     assert call(buf=FAKE + 8) == b.PKD_ERR_ALIGNMENT
     for kw in (dict(chunk_bytes=48), dict(chunk_bytes=8), dict(row_bytes=1000), dict(nbytes=2048 * 3 + 1024),
-               dict(pattern=2), dict(waves=9), dict(workgroups=0), dict(batch_kb=12), dict(nontemporal=2),
-               dict(pattern=1, chunk_bytes=32), dict(pattern=1, nbytes=2048 * 8)):
+               dict(pattern=3), dict(pattern=-1), dict(waves=9), dict(workgroups=0), dict(batch_kb=12),
+               dict(nontemporal=2), dict(pattern=1, chunk_bytes=32), dict(pattern=1, nbytes=2048 * 8),
+               dict(pattern=2, waves=8, batch_kb=16), dict(pattern=2, waves=4, batch_kb=32)):
         assert call(**kw) == b.PKD_ERR_BAD_DIMS, kw
+    # valid shapes reach the device check (no GPU here)
+    for kw in (dict(), dict(pattern=1), dict(pattern=2), dict(pattern=2, waves=8, batch_kb=8),
+               dict(pattern=2, waves=4, batch_kb=16)):
+        assert call(**kw) == b.PKD_ERR_DEVICE, kw
     assert b.pkd_stream_read_sink_bytes(256, 4) == 256 * 4 * 64 * 4
     assert b.pkd_stream_read_sink_bytes(0, 4) == 0

@@ -1278,3 +1278,104 @@ def test_valu_entry_full_size(B, name):
     w = wl.make_workload(wl.WORKLOADS[name], tail="nan")
     out, lse = run_valu(B, w, dev(w))
     check(out, lse, *oracle_full(w), what=f"valu {name}")
+
+
+# ---- tiles staged by direct-to-LDS loads (measurement entry) --------------------
+
+LDS_CASES = [
+    # (B, Hq, Hkv, D, ps, seq_lens, seed): G = 4, 1, 16, 6, 8; ragged tails, empty
+    # and one-token sequences, more tiles than waves and fewer.
+    (5, 32, 8, 128, 64, [700, 2, 0, 3000, 64], 911),
+    (4, 16, 16, 128, 16, [1, 17, 300, 33], 912),
+    (3, 16, 1, 128, 32, [5000, 31, 129], 913),
+    (6, 24, 4, 128, 48, [95, 96, 97, 1, 480, 0], 914),
+    (2, 8, 1, 128, 128, [8191, 4097], 915),
+]
+
+
+def run_lds(B, w, t):
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    out = torch.full(t["q"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(t["q"].shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    st = B.pkd_decode_lds(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale, out, lse,
+                          B.current_stream_handle(0))
+    assert st == 0, B.paged_decode_status_string(st)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("case", LDS_CASES)
+def test_lds_entry_matches_oracle_and_grid_kernel(B, case):
+    """The LDS-staged kernel against the oracle (NaN tails, -1 padding), and bit for
+    bit against paged_decode with num_splits = 1, whose arithmetic it shares."""
+    bq, hq, hkv, d, ps, lens, seed = case
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, "bf16", seed)
+    t = dev(w)
+    out, lse = run_lds(B, w, t)
+    check(out, lse, *oracle_full(w), what=f"lds {case[:5]}")
+    out1, lse1 = run(B, w, 1, t)
+    assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse1.view(torch.int32))
+
+
+def test_direct_output_path_choice(B):
+    """paged_decode runs the LDS-staged direct kernel for one round of plain
+    D = 128 items and the register-staged one otherwise; both give the same bits,
+    so the switch is invisible in the results."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    b32 = B.pkd_dims(32, 32, 8, 128, 64, 1500, 64, B.PKD_DTYPE_BF16)
+    one_round = 32 * 8 <= cus
+    want = B.PKD_PATH_DIRECT_LDS if one_round else B.PKD_PATH_DIRECT
+    assert B.paged_decode_path(b32, None, 0, 1) == want
+    assert B.paged_decode_path(b32, None, 1, 1) == B.PKD_PATH_DIRECT  # sinks
+    assert B.paged_decode_path(b32, B.pkd_ext(2, 1, 0, 0), 0, 1) == B.PKD_PATH_DIRECT  # two query tokens
+    assert B.paged_decode_path(b32, B.pkd_ext(1, 0, 512, 0), 0, 1) == B.PKD_PATH_DIRECT  # window
+    b128 = B.pkd_dims(128, 32, 8, 128, 128, 4100, 32, B.PKD_DTYPE_BF16)
+    assert B.paged_decode_path(b128, None, 0, 1) == B.PKD_PATH_DIRECT  # four rounds
+    fp8 = B.pkd_dims(32, 32, 8, 128, 64, 1500, 64, B.PKD_DTYPE_FP8_E4M3)
+    assert B.paged_decode_path(fp8, None, 0, 1) == B.PKD_PATH_DIRECT
+
+
+@pytest.mark.parametrize("name", ["llama_b32_d128_ps64", "batch128_d128_ps128"])
+def test_lds_entry_full_size(B, name):
+    """Every row of the B=32 and B=128 steps, as timed beside the register-staged kernel."""
+    w = wl.make_workload(wl.WORKLOADS[name], tail="nan")
+    t = dev(w)
+    out, lse = run_lds(B, w, t)
+    check(out, lse, *oracle_full(w), what=f"lds {name}")
+    out1, lse1 = run(B, w, 1, t)
+    assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
+
+
+# ---- the read-only stream kernel (measurement entry) ----------------------------
+
+@pytest.mark.parametrize("pattern", [0, 1])
+def test_stream_read_folds_every_word_once(B, pattern):
+    """Patterns 0 and 1 cover the buffer exactly once: the XOR of every thread's
+    sink word equals the XOR of the whole buffer (each wave's block count is a
+    multiple of the batch, so no block is folded twice)."""
+    g = torch.Generator().manual_seed(77 + pattern)
+    words = torch.randint(-2**31, 2**31 - 1, ((1 << 20) // 4,), dtype=torch.int64, generator=g).to(torch.int32)
+    buf = words.cuda()
+    wgs, waves, kb = 8, 4, 8  # 1024 blocks: 32 per wave
+    sink = torch.zeros(B.pkd_stream_read_sink_bytes(wgs, waves) // 4, dtype=torch.int32, device="cuda")
+    st = B.pkd_stream_read(buf, 1 << 20, 2048, 256, pattern, wgs, waves, kb, 1, sink, B.current_stream_handle(0))
+    assert st == 0, B.paged_decode_status_string(st)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(words.numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
+
+
+@pytest.mark.parametrize("waves,kb", [(4, 4), (4, 8), (8, 8), (4, 16)])
+def test_stream_read_direct_to_lds_lands_in_lds(B, waves, kb):
+    """Pattern 2's loads write LDS: over a buffer of one repeated word, every
+    thread of a wave with blocks reads that word back from its ring."""
+    c = 0x01020304
+    buf = torch.full(((1 << 20) // 4,), c, dtype=torch.int32, device="cuda")
+    wgs = 8  # 1024 blocks: at least 16 per wave
+    sink = torch.zeros(B.pkd_stream_read_sink_bytes(wgs, waves) // 4, dtype=torch.int32, device="cuda")
+    st = B.pkd_stream_read(buf, 1 << 20, 2048, 256, 2, wgs, waves, kb, 1, sink, B.current_stream_handle(0))
+    assert st == 0, B.paged_decode_status_string(st)
+    torch.cuda.synchronize()
+    assert bool((sink.cpu() == c).all())

@@ -52,7 +52,7 @@ def test_host_code_under_sanitizers(tmp_path):
     common = ["-O1", "-g", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
               "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     host = [(os.path.join(CSRC, "api.cpp"), []), (os.path.join(HERE, "host_driver.cpp"), [])] + \
-        [(os.path.join(CSRC, f + ".hip"), ["-x", "hip"]) for f in ("noalloc", "stream_read", "valu_decode")]
+        [(os.path.join(CSRC, f + ".hip"), ["-x", "hip"]) for f in ("noalloc", "stream_read", "valu_decode", "lds_decode")]
     built = []
     for src, lang in host:
         obj = str(tmp_path / (os.path.basename(src) + ".o"))
