@@ -15,10 +15,11 @@
 //    writes 1 KiB of LDS in lane order, so a tile is row-major with no padding.
 //    To keep the matrix-core operand reads free of bank conflicts, lane l of
 //    the instruction covering row r fetches the row's 16-byte chunk
-//    (l % 16) ^ swz(r): chunk c of row r sits in slot c ^ swz(r).  swz gives
-//    16 distinct values on 16 consecutive rows (the K operand reads 16 rows) and
-//    distinct slot pairs on each 4 consecutive rows (a transposing V read
-//    takes 32 bytes of 4 rows per 16 lanes).
+//    (l % 16) ^ swz(r): chunk c of row r sits in slot c ^ swz(r) (swz below
+//    keeps the 16-row K operand reads and the 4- and 8-row transposing V reads
+//    in distinct bank groups).  Each lane's read offsets inside a stage, and
+//    its part of every load instruction, are computed once; a load then takes
+//    the page's row address as a scalar base plus the lane's 32-bit offset.
 //  * Waits.  The compiler's own bookkeeping would wait for every outstanding
 //    direct-to-LDS load before any LDS read, which leaves one tile in flight.
 //    The loads are therefore issued from inline assembly (the LDS address
@@ -36,6 +37,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "wave_attn.hpp"
 
@@ -58,19 +60,29 @@ constexpr int kLoadsPerHalf = kTileB / 1024;  // load instructions per K (or V) 
 // The workgroup combine's staging (per-wave rows and weights) reuses the stages.
 static_assert(kLW * 16 * (2 + Cfg<kLD, false>::OW_STRIDE) * 4 + 16 * (kLW + 4) * 4 <= kBtOff, "combine staging");
 
-// Slot permutation of a tile row (see the header comment).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+// Slot permutation of tile row r (see the header comment): for s = r % 8,
+// 2s on s < 4 and 2s + 1 on s >= 4, then XOR 8 on rows 8 .. 15.  The 16 rows
+// take 16 distinct values and any 8 consecutive rows distinct values modulo 8,
+// so a K operand read (16 rows, one chunk) finds every row's chunk in another
+// bank group whether the LDS serves 8 or 16 lanes of 16 bytes per pass; and
+// slot >> 1 is distinct on any 8 consecutive rows, so the 32-byte pieces of a
+// transposing V read land in distinct bank groups for 4 and for 8 rows.
+__device__ __forceinline__ int swz(int r) {
+  const int s = r & 7;
+  return ((s << 1) + (s >> 2)) ^ (r & 8);
+}
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // LDS byte address of a pointer into this workgroup's shared memory.
 __device__ __forceinline__ uint32_t lds_address(uint8_t* p) { return (uint32_t)(uintptr_t)(lds_u8*)p; }
 
-// One direct-to-LDS load: 16 bytes from src (per lane) to LDS lds + 16 * lane.
-// The LDS address goes to M0 through the operand constraint (the compiler
-// writes M0 itself); one wait state separates that write from the load.
-__device__ __forceinline__ void load_to_lds(const uint8_t* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(lds) : "memory");
+// One direct-to-LDS load: 16 bytes from base + off (base wave-uniform, off per
+// lane) to LDS lds + 16 * lane.  The LDS address goes to M0 through the operand
+// constraint (the compiler writes M0 itself); one wait state separates that
+// write from the load.
+__device__ __forceinline__ void load_to_lds(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 // Wait until at most N direct-to-LDS loads of this wave are outstanding (they
@@ -79,7 +91,10 @@ template <int N>
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
-__global__ void __launch_bounds__(kLW * 64) lds_direct_kernel(const SplitParams p) {
+// Two waves per SIMD as the register budget (as the grid kernel): the
+// accumulators then stay in ordinary VGPRs, where the rescale reaches them.
+__global__ void __launch_bounds__(kLW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+lds_direct_kernel(const SplitParams p) {
   typedef WaveAttn<kLD, false> WA;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
@@ -101,57 +116,80 @@ __global__ void __launch_bounds__(kLW * 64) lds_direct_kernel(const SplitParams 
   A.load_q(p.q + row_n * kLD, hv);
   A.qk_scale = p.qk_scale_log2;
   A.reset();
-  const int L = p.seq_lens[b];
+  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);  // uniform: tile bookkeeping stays scalar
   __shared__ int64_t s_rows[kHeadsPerGroup];
   if (tid < kHeadsPerGroup) s_rows[tid] = (int64_t)b * p.hq + kvh * G + tid;
   __syncthreads();
 
   const int ntiles = (L + kLT - 1) / kLT;
   const int lim = L - 1;
-  // This lane's part of every load instruction: instruction i covers tile rows
-  // 4i .. 4i + 3; the lane fetches row 4i + lane / 16, chunk (lane % 16) ^ swz(row).
-  int drow[4], dchunk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    drow[i] = 4 * i + (lane >> 4);
-    dchunk[i] = ((lane & 15) ^ swz(drow[i])) * 16;
-  }
-  uint8_t* wbase = smem + wave * kWaveB;
-  const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_address(wbase));
-  const int64_t head_off = (int64_t)kvh * kRowB;
   const int ps = p.page_size;
+  const int ts = p.kv.tok_stride;
+  // This lane's part of every load instruction: instruction i covers tile rows
+  // 4i .. 4i + 3; the lane fetches row 4i + lane / 16, chunk (lane % 16) ^
+  // swz(row), at byte loff[i] of the tile's first row (32-bit: a 16-token group
+  // lies in one page).
+  int drow[kLoadsPerHalf];
+  uint32_t dchunk[kLoadsPerHalf], loff[kLoadsPerHalf];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerHalf; ++i) {
+    drow[i] = 4 * i + (lane >> 4);
+    dchunk[i] = (uint32_t)(kvh * kRowB + (((lane & 15) ^ swz(drow[i])) << 4));
+    loff[i] = (uint32_t)(drow[i] * ts) + dchunk[i];
+  }
+  // This lane's LDS read offsets inside a stage: K row n, chunk 4 kk + g; V row
+  // 4g + n / 4, chunk 2 nb + (n / 2) % 2, bytes 8 (n % 2) ..
+  const int wofs = wave * kWaveB;
+  int kofs[WA::C::KK], vofs[WA::C::NB];
+#pragma unroll
+  for (int kk = 0; kk < WA::C::KK; ++kk) kofs[kk] = wofs + A.n * kRowB + (((4 * kk + A.g) ^ swz(A.n)) << 4);
+  {
+    const int vr = 4 * A.g + (A.n >> 2);
+#pragma unroll
+    for (int nb = 0; nb < WA::C::NB; ++nb)
+      vofs[nb] = wofs + kTileB + vr * kRowB + (((2 * nb + ((A.n >> 1) & 1)) ^ swz(vr)) << 4) + ((A.n & 1) << 3);
+  }
+  const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_address(smem)) + wofs;
 
-  auto issue = [&](int t, int stage) {
+  auto issue = [&](int t, auto stage_c) {
+    constexpr int ST = decltype(stage_c)::value;
     const int tb = t * kLT;
     const int page = __builtin_amdgcn_readfirstlane(sbt[tb / ps]);
-    const int64_t base = (int64_t)page * p.kv.page_stride + (int64_t)(tb % ps) * p.kv.tok_stride + head_off;
+    const int64_t row0 = (int64_t)page * p.kv.page_stride + (int64_t)(tb % ps) * ts;
+    const uint8_t* kb = p.k + row0;
+    const uint8_t* vb = p.v + row0;
+    const uint32_t lk = wlds + ST * kStageB;
     const int rl = lim - tb;  // last row of the tile inside the sequence; later rows re-read it
-    int64_t off[4];
+    if (rl >= kLT - 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) off[i] = base + (int64_t)min(drow[i], rl) * p.kv.tok_stride + dchunk[i];
-    const uint32_t lk = wlds + stage * kStageB;
+      for (int i = 0; i < kLoadsPerHalf; ++i) load_to_lds(kb, loff[i], lk + i * 1024);
 #pragma unroll
-    for (int i = 0; i < kLoadsPerHalf; ++i) load_to_lds(p.k + off[i], lk + i * 1024);
+      for (int i = 0; i < kLoadsPerHalf; ++i) load_to_lds(vb, loff[i], lk + kTileB + i * 1024);
+    } else {
+      uint32_t o[kLoadsPerHalf];
 #pragma unroll
-    for (int i = 0; i < kLoadsPerHalf; ++i) load_to_lds(p.v + off[i], lk + kTileB + i * 1024);
+      for (int i = 0; i < kLoadsPerHalf; ++i) o[i] = (uint32_t)(min(drow[i], rl) * ts) + dchunk[i];
+#pragma unroll
+      for (int i = 0; i < kLoadsPerHalf; ++i) load_to_lds(kb, o[i], lk + i * 1024);
+#pragma unroll
+      for (int i = 0; i < kLoadsPerHalf; ++i) load_to_lds(vb, o[i], lk + kTileB + i * 1024);
+    }
   };
-  // Loads issued after a tile's K half: its V half and the later tiles.
-  constexpr int kAfterK = kLoadsPerHalf + (kLS - 1) * 2 * kLoadsPerHalf;
-  constexpr int kAfterV = (kLS - 1) * 2 * kLoadsPerHalf;
+  // Loads issued after a tile's K half: its V half and the next tile.
+  constexpr int kAfterK = 3 * kLoadsPerHalf;
+  constexpr int kAfterV = 2 * kLoadsPerHalf;
 
-  // One tile from LDS stage `stage`: QK^T, the softmax against the reference
+  // One tile from LDS stage ST: QK^T, the softmax against the reference
   // maximum, PV.  The arithmetic is the grid kernel's (WaveAttn::process) step
   // for step; only the LDS addresses differ.
-  auto compute = [&](int t, int stage) {
-    const uint8_t* kt = wbase + stage * kStageB;
-    const uint8_t* vt = kt + kTileB;
+  auto compute = [&](int t, auto stage_c) {
+    constexpr int ST = decltype(stage_c)::value;
     const int tb = t * kLT;
     wait_loads<kAfterK>();  // the tile's K has landed (its V may still be in flight)
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < WA::C::KK; ++kk) {
-      // row n, dims kk * 32 + g * 8 .. + 8: chunk 4 kk + g
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + A.n * kRowB + (((4 * kk + A.g) ^ swz(A.n)) << 4));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem + kofs[kk] + ST * kStageB);
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, A.qf[kk], s, 0, 0, 0);
     }
     float mt = -INFINITY;
@@ -193,45 +231,40 @@ __global__ void __launch_bounds__(kLW * 64) lds_direct_kernel(const SplitParams 
 #pragma unroll
     for (int i = 0; i < 4; ++i) pb[i] = (__bf16)s[i];
     const s16x4 pbs = bit_cast_dev<s16x4>(pb);
-    // lane (n, g) addresses row 4g + n/4, dims 16 nb + 4 (n % 4) .. + 3: chunk
-    // 2 nb + (n / 2) % 2, bytes 8 (n % 2) .. of it.
-    const int vr = 4 * A.g + (A.n >> 2);
-    const uint8_t* vrow = vt + vr * kRowB + ((A.n & 1) << 3);
-    const int vsw = swz(vr);
-    const int vhalf = (A.n >> 1) & 1;
     wait_loads<kAfterV>();  // and its V
 #pragma unroll
     for (int nb = 0; nb < WA::C::NB; ++nb) {
-      const s16x4 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(vrow + (((2 * nb + vhalf) ^ vsw) << 4)));
+      const s16x4 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(smem + vofs[nb] + ST * kStageB));
       A.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pbs, A.acc[nb], 0, 0, 0);
     }
     wait_lds_reads();  // this stage's reads are done before it is refilled
   };
 
-  // Tiles wave, wave + kLW, ...: kLS in flight, the oldest computed while the
-  // others load.  After the last tile the refills repeat the newest tile
-  // (rows already loaded) so that every wait sees the same count; they are
-  // never read.
+  // Tiles wave, wave + kLW, ...: two in flight, the older one computed while
+  // the newer one loads.  After the last tile the refill repeats the newer tile
+  // (rows already loaded) so that every wait sees the same count; it is never
+  // read.
   if (wave < ntiles) {
+    typedef std::integral_constant<int, 0> S0;
+    typedef std::integral_constant<int, 1> S1;
     auto nxt = [&](int t) { return t + kLW < ntiles ? t + kLW : t; };
-    int tl[kLS];  // the tiles in the stages, oldest first
-    tl[0] = wave;
-    issue(tl[0], 0);
-#pragma unroll
-    for (int i = 1; i < kLS; ++i) {
-      tl[i] = nxt(tl[i - 1]);
-      issue(tl[i], i);
-    }
-    int stage = 0;
+    int t = wave;
+    issue(t, S0());
+    int t1 = nxt(t);
+    issue(t1, S1());
     while (true) {
-      compute(tl[0], stage);
-      if (tl[1] == tl[0]) break;
-      const int tn = nxt(tl[kLS - 1]);
-      issue(tn, stage);
-#pragma unroll
-      for (int i = 0; i + 1 < kLS; ++i) tl[i] = tl[i + 1];
-      tl[kLS - 1] = tn;
-      stage = stage + 1 == kLS ? 0 : stage + 1;
+      compute(t, S0());
+      if (t1 == t) break;
+      int t2 = nxt(t1);
+      issue(t2, S0());
+      t = t1;
+      t1 = t2;
+      compute(t, S1());
+      if (t1 == t) break;
+      t2 = nxt(t1);
+      issue(t2, S1());
+      t = t1;
+      t1 = t2;
     }
   }
   wait_loads<0>();  // the combine below reuses the stages
