@@ -91,7 +91,7 @@ class Runner:
         self.ext = B.ext_for(self.q, causal=w.spec.causal, window=w.spec.window)
         self.S = num_splits if num_splits != 0 else B.paged_decode_num_splits_ext(self.dims, self.ext, 0)
         self.launches = B.paged_decode_launches(self.dims, self.ext, self.S)  # 1: the partition writes out itself
-        self.path = B.paged_decode_path(self.dims, self.ext, 0 if self.sinks is None else 1, self.S)
+        self.path = B.paged_decode_path(self.dims, self.ext, self.S)
         # plain decode in a numbered split mode goes through paged_decode itself
         self.plain = self.ext is None and self.sinks is None and 1 <= self.S <= B.PKD_MAX_SPLITS
         self.out = torch.empty(self.q.shape, dtype=torch.bfloat16, device=device)
@@ -448,33 +448,25 @@ def split_sweep(w, steps, warmup, device, scrub):
 
 def _direct_legs(r, w):
     """Pre-marshalled calls of the three direct-output kernels on each K/V copy of
-    runner r: the register-staged grid kernel (paged_decode_ext, num_splits = 1,
-    with sink logits of -inf, which change no bit of the result but keep the call
-    off the LDS-staged kernel), the LDS-staged kernel (pkd_decode_lds) and the
-    vector-ALU kernel (pkd_decode_valu)."""
+    runner r: the register-staged grid kernel (pkd_decode_registers), the
+    LDS-staged kernel (pkd_decode_lds) and the vector-ALU kernel (pkd_decode_valu)."""
     import ctypes
     import torch
     from paged_kv_decode_amd import binding as B
     lib = B.lib()
-    assert B.paged_decode_path(r.dims, None, 1, 1) == B.PKD_PATH_DIRECT
-    no_sink = torch.full((w.spec.num_q_heads,), float("-inf"), dtype=torch.float32, device=r.q.device)
     out = torch.empty_like(r.out)
     lse = torch.empty_like(r.lse)
-    d = ctypes.byref(r.dims)
-    reg = [(d, None, r.q.data_ptr(), k.data_ptr(), v.data_ptr(), r.bt.data_ptr(), r.lens.data_ptr(), None, None,
-            no_sink.data_ptr(), float(w.scale), out.data_ptr(), lse.data_ptr(), 1, None, 0, r.handle)
-           for k, v in r.copies]
-    alt = [(d, r.q.data_ptr(), k.data_ptr(), v.data_ptr(), r.bt.data_ptr(), r.lens.data_ptr(), float(w.scale),
-            out.data_ptr(), lse.data_ptr(), r.handle) for k, v in r.copies]
+    args = [(ctypes.byref(r.dims), r.q.data_ptr(), k.data_ptr(), v.data_ptr(), r.bt.data_ptr(), r.lens.data_ptr(),
+             float(w.scale), out.data_ptr(), lse.data_ptr(), r.handle) for k, v in r.copies]
 
-    def leg(fn, args):
+    def leg(fn):
         def call(c):
             st = fn(*args[c])
             if st != 0:
                 raise B.PkdError(st)
         return call
-    return {"register_staged": leg(lib.paged_decode_ext, reg), "lds_staged": leg(lib.pkd_decode_lds, alt),
-            "vector_alu": leg(lib.pkd_decode_valu, alt), "_keep": (no_sink, out, lse)}
+    return {"register_staged": leg(lib.pkd_decode_registers), "lds_staged": leg(lib.pkd_decode_lds),
+            "vector_alu": leg(lib.pkd_decode_valu), "_keep": (out, lse)}
 
 
 def inner_loop_ab(w, steps, warmup, device, scrub):

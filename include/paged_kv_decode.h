@@ -296,25 +296,25 @@ int32_t paged_decode_launches(const pkd_dims* dims, const pkd_ext* ext, int32_t 
 /*
  * paged_decode_path -- which partition kernel paged_decode_ext runs for
  * num_splits (PKD_SPLITS_AUTO: the heuristic's choice), for profilers and
- * tests that need the kernel by name.  has_sinks: whether the call passes
- * sinks (0 or 1).  Returns
+ * tests that need the kernel by name.  Returns
  *   PKD_PATH_DIRECT          direct output, the next K/V tile's loads held in registers;
  *   PKD_PATH_DIRECT_LDS      direct output, K/V tiles loaded straight into two LDS stages per
  *                            wave (the same arithmetic and the same bits), taken for a BF16
- *                            paged cache with head_dim 128, q_len 1, no window and no sinks,
- *                            G <= 16, page_size a multiple of 16, max_pages_per_seq <= 512, and
+ *                            paged cache with head_dim 128, q_len 1, no window, G <= 16,
+ *                            page_size a multiple of 16, max_pages_per_seq <= 512, and
  *                            batch * num_kv_heads at most the current device's compute units;
  *   PKD_PATH_SPLITS          split-KV partials, then the merge kernel;
  *   PKD_PATH_BALANCED        the balanced partition, merging in place;
  *   PKD_PATH_BALANCED_MERGE  the balanced partition, then the merge kernel.
- * Host only; returns a status in [-11, -1] for invalid dims or num_splits.
+ * Sinks do not change the path.  Host only; returns a status in [-11, -1] for
+ * invalid dims or num_splits.
  */
 #define PKD_PATH_DIRECT 1
 #define PKD_PATH_DIRECT_LDS 2
 #define PKD_PATH_SPLITS 3
 #define PKD_PATH_BALANCED 4
 #define PKD_PATH_BALANCED_MERGE 5
-int32_t paged_decode_path(const pkd_dims* dims, const pkd_ext* ext, int32_t has_sinks, int32_t num_splits);
+int32_t paged_decode_path(const pkd_dims* dims, const pkd_ext* ext, int32_t num_splits);
 
 /*
  * paged_decode_workspace_bytes -- workspace paged_decode needs for num_splits

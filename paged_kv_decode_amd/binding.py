@@ -54,7 +54,7 @@ EXPORTED = ("paged_decode", "paged_decode_ext", "paged_decode_partition", "paged
             "paged_decode_check_tables", "paged_kv_append", "paged_decode_metadata", "contiguous_decode",
             "contiguous_decode_workspace_bytes", "paged_decode_status_string", "pkd_stream_read",
             "pkd_stream_read_sink_bytes", "paged_decode_ext_noalloc", "pkd_decode_valu",
-            "pkd_decode_lds")
+            "pkd_decode_lds", "pkd_decode_registers")
 
 
 class PkdError(RuntimeError):
@@ -145,7 +145,7 @@ _lib.paged_decode_num_splits_ext.argtypes = [_dims_p, _ext_p, _i32]
 _lib.paged_decode_num_splits_ext.restype = _i32
 _lib.paged_decode_launches.argtypes = [_dims_p, _ext_p, _i32]
 _lib.paged_decode_launches.restype = _i32
-_lib.paged_decode_path.argtypes = [_dims_p, _ext_p, _i32, _i32]
+_lib.paged_decode_path.argtypes = [_dims_p, _ext_p, _i32]
 _lib.paged_decode_path.restype = _i32
 _lib.paged_decode_workspace_bytes.argtypes = [_dims_p, _i32]
 _lib.paged_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -171,6 +171,8 @@ _lib.pkd_decode_valu.argtypes = [_dims_p, _p, _p, _p, _p, _p, ctypes.c_float, _p
 _lib.pkd_decode_valu.restype = _i32
 _lib.pkd_decode_lds.argtypes = [_dims_p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p]
 _lib.pkd_decode_lds.restype = _i32
+_lib.pkd_decode_registers.argtypes = [_dims_p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p]
+_lib.pkd_decode_registers.restype = _i32
 _lib.pkd_stream_read.argtypes = [_p, ctypes.c_int64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]
 _lib.pkd_stream_read.restype = _i32
 _lib.pkd_stream_read_sink_bytes.argtypes = [_i32, _i32]
@@ -245,8 +247,8 @@ def paged_decode_launches(dims, ext, num_splits: int) -> int:
     return _lib.paged_decode_launches(_dims_ref(dims), _dims_ref(ext), int(num_splits))
 
 
-def paged_decode_path(dims, ext, has_sinks: int, num_splits: int) -> int:
-    return _lib.paged_decode_path(_dims_ref(dims), _dims_ref(ext), int(has_sinks), int(num_splits))
+def paged_decode_path(dims, ext, num_splits: int) -> int:
+    return _lib.paged_decode_path(_dims_ref(dims), _dims_ref(ext), int(num_splits))
 
 
 def paged_decode_workspace_bytes(dims, num_splits: int) -> int:
@@ -308,6 +310,11 @@ def pkd_decode_valu(dims, q, k_cache, v_cache, block_table, seq_lens, scale, out
 
 def pkd_decode_lds(dims, q, k_cache, v_cache, block_table, seq_lens, scale, out, lse, stream) -> int:
     return _lib.pkd_decode_lds(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _ptr(stream))
+
+
+def pkd_decode_registers(dims, q, k_cache, v_cache, block_table, seq_lens, scale, out, lse, stream) -> int:
+    return _lib.pkd_decode_registers(_dims_ref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                 _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _ptr(stream))
 
 

@@ -9,6 +9,7 @@
 #include <unistd.h>
 
 #include "../../include/paged_kv_decode.h"
+#include "../../include/pkd_lds.h"
 #include "pkd_internal.hpp"
 
 namespace {
@@ -328,11 +329,11 @@ int32_t check_out_ws(const void* out, const float* lse, const void* ws) {
 // Direct output with K/V tiles loaded straight into LDS stages, where that
 // kernel applies and the (sequence, KV head) items fit in one round of
 // workgroups.  It gives the grid kernel's bits; measured back to back it was
-// 1.2% faster at B = 32 (256 items on 256 units) and 1.2% slower at B = 128
+// 0.8-1.2% faster at B = 32 (256 items on 256 units) and 1% slower at B = 128
 // (1024 items, four rounds).
-bool use_lds_direct(const Dims& d, const Layout& lay, const float* sinks) {
+bool use_lds_direct(const Dims& d, const Layout& lay) {
   const int cus = current_cu_count();
-  return pkd::lds_direct_applies(d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, d.q_len, d.window, sinks != nullptr,
+  return pkd::lds_direct_applies(d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, d.q_len, d.window,
                                  d.num_q_heads / d.num_kv_heads, d.page_size, d.max_pages_per_seq, lay.strided) &&
          cus > 0 && (int64_t)d.batch * d.num_kv_heads <= cus;
 }
@@ -561,7 +562,7 @@ int32_t decode_checked(const Dims& d, const Layout& lay, const void* q, const vo
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
     p.sinks = sinks;
-    if (use_lds_direct(d, lay, sinks)) return pkd::launch_lds_direct(p, d.batch, s) == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
+    if (use_lds_direct(d, lay)) return pkd::launch_lds_direct(p, d.batch, s) == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
     return launch_partition(d, p, true, s);
   }
   if (pl.balanced && balanced_fused(d, pl.pair)) {
@@ -614,20 +615,34 @@ int32_t paged_decode_launches(const pkd_dims* dims, const pkd_ext* ext, int32_t 
   return 2;
 }
 
-int32_t paged_decode_path(const pkd_dims* dims, const pkd_ext* ext, int32_t has_sinks, int32_t num_splits) {
+int32_t pkd_decode_registers(const pkd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, float scale, void* out, float* lse,
+                             void* stream) {
   if (!dims) return PKD_ERR_NULL_POINTER;
-  if (has_sinks != 0 && has_sinks != 1) return PKD_ERR_BAD_DIMS;
+  const Dims d = make_dims(*dims, nullptr);
+  int32_t st = check_inputs(&d, q, k_cache, v_cache, block_table, seq_lens, nullptr, nullptr, scale);
+  if (st != PKD_OK) return st;
+  if (!out) return PKD_ERR_NULL_POINTER;
+  st = check_out_ws(out, lse, nullptr);
+  if (st != PKD_OK) return st;
+  if (d.batch == 0) return PKD_OK;
+  if (current_cu_count() < 0) return PKD_ERR_DEVICE;
+  pkd::SplitParams p =
+      make_split_params(d, paged_layout(d), q, k_cache, v_cache, block_table, seq_lens, nullptr, nullptr, scale, 1);
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  return launch_partition(d, p, true, static_cast<hipStream_t>(stream));
+}
+
+int32_t paged_decode_path(const pkd_dims* dims, const pkd_ext* ext, int32_t num_splits) {
+  if (!dims) return PKD_ERR_NULL_POINTER;
   const Dims d = make_dims(*dims, ext);
   const int32_t st = check_dims(&d);
   if (st != PKD_OK) return st;
   Plan pl;
   const int32_t pst = make_plan(d, num_splits, false, &pl);
   if (pst != PKD_OK) return pst;
-  if (pl.S == 1) {
-    static const float kAnySink = 0.f;
-    return use_lds_direct(d, paged_layout(d), has_sinks ? &kAnySink : nullptr) ? PKD_PATH_DIRECT_LDS
-                                                                              : PKD_PATH_DIRECT;
-  }
+  if (pl.S == 1) return use_lds_direct(d, paged_layout(d)) ? PKD_PATH_DIRECT_LDS : PKD_PATH_DIRECT;
   if (pl.balanced) return balanced_fused(d, pl.pair) ? PKD_PATH_BALANCED : PKD_PATH_BALANCED_MERGE;
   return PKD_PATH_SPLITS;
 }

@@ -1,9 +1,12 @@
 // Direct output (one workgroup of four waves per (KV head, sequence), out and
 // lse written directly) with the K/V tiles loaded straight into LDS stages by
 // the pipeline of lds_pipe.hpp, instead of being held in registers for one
-// tile as the grid kernel does.  paged_decode runs it for plain bf16 D = 128
-// decode whose items fit one round of workgroups; pkd_decode_lds exposes it
-// for measurement beside the grid kernel.  The arithmetic is the grid kernel's,
+// tile as the grid kernel does.  paged_decode runs it for bf16 D = 128 decode
+// of one query token per sequence without a window (sinks or not) whose items
+// fit one round of workgroups; pkd_decode_lds exposes it for measurement beside
+// the grid kernel.  It also computes several query tokens under the causal mask
+// (q_len * G <= 16 rows, bit for bit the grid kernel's), but four tokens at
+// B = 32 ran 1% slower than the grid kernel, so paged_decode does not send them.  The arithmetic is the grid kernel's,
 // so the results equal paged_decode's with num_splits = 1 bit for bit.
 #include "../../include/pkd_lds.h"
 
@@ -36,22 +39,27 @@ lds_direct_kernel(const SplitParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvh = blockIdx.x;
   const int b = blockIdx.y;
-  const int G = p.group;
   WA A;
   A.init_lane(lane);
 
   // Issued while the length is in flight: the block-table row (every entry of
-  // the sequence's row) and the query rows.
+  // the sequence's row) and the query rows (q_len * G packed rows, 16 at most).
   int32_t* sbt = reinterpret_cast<int32_t*>(smem + kBtOff);
   for (int i = tid; i < p.max_pages; i += kLW * 64) sbt[i] = p.block_table[(int64_t)b * p.max_pages + i];
-  const bool hv = A.n < G;
-  const int64_t row_n = (int64_t)b * p.hq + kvh * G + (hv ? A.n : 0);
-  A.load_q(p.q + row_n * kLpD, hv);
+  {
+    const LaneRow lq = lane_row<kLpD, false>(p, b, kvh, 0, A.n, 0, 0, 0);
+    A.load_q(p.q + lq.qoff, lq.valid);
+  }
   A.qk_scale = p.qk_scale_log2;
   A.reset();
   const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);  // uniform: tile bookkeeping stays scalar
+  const LaneRow lr = lane_row<kLpD, false>(p, b, kvh, 0, A.n, L, L, 0);
   __shared__ int64_t s_rows[kHeadsPerGroup];
-  if (tid < kHeadsPerGroup) s_rows[tid] = (int64_t)b * p.hq + kvh * G + tid;
+  __shared__ int64_t s_orow[kHeadsPerGroup];
+  if (tid < kHeadsPerGroup) {
+    s_rows[tid] = lr.row;
+    s_orow[tid] = lr.ooff;
+  }
   __syncthreads();
 
   const int ntiles = (L + kLpTT - 1) / kLpTT;
@@ -60,25 +68,28 @@ lds_direct_kernel(const SplitParams p) {
   LdsPipe P;
   P.init(smem, wave * kLpWaveB, A, lane, p.kv.tok_stride);
   // Tiles wave, wave + kLW, ...; the byte offset of token tb's row of KV head kvh.
-  P.run(A, wave, kLW, ntiles, 0, L, L, L, p.k, p.v, [&](int tb) -> int64_t {
+  P.run(A, wave, kLW, ntiles, 0, L, lr.end, lr.end_min, p.k, p.v, [&](int tb) -> int64_t {
     const int page = __builtin_amdgcn_readfirstlane(sbt[tb / ps]);
     return (int64_t)page * p.kv.page_stride + (int64_t)(tb % ps) * p.kv.tok_stride + head_off;
   });
   // every load has landed: the combine below reuses the stages
 
   auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
-    const int64_t row = s_rows[hh];
-    *reinterpret_cast<bf16x4*>(p.out + row * kLpD + d0) = to_bf16x4(o);
-    if (d0 == 0 && p.lse) p.lse[row] = lse_nat;
+    *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + d0) = to_bf16x4(o);
+    if (d0 == 0 && p.lse) p.lse[s_rows[hh]] = lse_nat;
   };
-  wg_combine<kLpD, false, kLW>(A, smem, wave, tid, G, 1.0f, store, NoSink());
+  if (p.sinks)
+    wg_combine<kLpD, false, kLW>(A, smem, wave, tid, p.rows_kv, 1.0f, store,
+                                 [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
+  else
+    wg_combine<kLpD, false, kLW>(A, smem, wave, tid, p.rows_kv, 1.0f, store, NoSink());
 }
 
 }  // namespace
 
-bool lds_direct_applies(int head_dim, bool fp8, int q_len, int window, bool sinks, int group, int page_size,
-                        int max_pages, bool strided) {
-  return head_dim == kLpD && !fp8 && q_len == 1 && window == 0 && !sinks && group >= 1 && group <= kHeadsPerGroup &&
+bool lds_direct_applies(int head_dim, bool fp8, int q_len, int window, int group, int page_size, int max_pages,
+                        bool strided) {
+  return head_dim == kLpD && !fp8 && window == 0 && q_len == 1 && group >= 1 && group <= kHeadsPerGroup &&
          page_size % 16 == 0 && max_pages >= 1 && max_pages <= kBtEntries && !strided;
 }
 
@@ -103,7 +114,7 @@ int32_t pkd_decode_lds(const pkd_dims* dims, const void* q, const void* k_cache,
   const int G = d.num_q_heads / d.num_kv_heads;
   if (d.head_dim != 128) return PKD_ERR_HEAD_DIM;
   if (d.kv_dtype != PKD_DTYPE_BF16) return PKD_ERR_DTYPE;
-  if (!pkd::lds_direct_applies(d.head_dim, false, 1, 0, false, G, d.page_size, d.max_pages_per_seq, false))
+  if (!pkd::lds_direct_applies(d.head_dim, false, 1, 0, G, d.page_size, d.max_pages_per_seq, false))
     return PKD_ERR_BAD_DIMS;
   if ((int64_t)d.num_kv_heads * 256 * d.page_size > INT32_MAX) return PKD_ERR_BAD_DIMS;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return PKD_ERR_NULL_POINTER;
@@ -126,6 +137,8 @@ int32_t pkd_decode_lds(const pkd_dims* dims, const void* q, const void* k_cache,
   p.hkv = d.num_kv_heads;
   p.group = G;
   p.q_len = 1;
+  p.rows_kv = G;
+  p.head_groups = 1;
   p.page_size = d.page_size;
   p.max_pages = d.max_pages_per_seq;
   p.kv.head_stride = 256;

@@ -179,12 +179,11 @@ hipError_t launch_check_tables(const int32_t* block_table, const int32_t* seq_le
 
 // Direct output with K/V tiles loaded straight into LDS stages (lds_decode.hip):
 // the grid kernel's arithmetic, bit for bit, for the shapes lds_direct_applies
-// accepts (paged bf16 cache, D = 128, one query token, no window or sinks,
-// G <= 16, page_size % 16 == 0, max_pages <= 512).  One workgroup per
-// (KV head, sequence); reads q, k, v, block_table, seq_lens, out, lse,
-// qk_scale_log2, hq, hkv, group, page_size, max_pages and kv of p.
-bool lds_direct_applies(int head_dim, bool fp8, int q_len, int window, bool sinks, int group, int page_size,
-                        int max_pages, bool strided);
+// accepts (paged bf16 cache, D = 128, no window, one query token, G <= 16,
+// page_size % 16 == 0, max_pages <= 512; sinks or not).  One workgroup per
+// (KV head, sequence); reads the direct-mode fields of p.
+bool lds_direct_applies(int head_dim, bool fp8, int q_len, int window, int group, int page_size, int max_pages,
+                        bool strided);
 hipError_t launch_lds_direct(const SplitParams& p, int batch, hipStream_t stream);
 
 }  // namespace pkd

@@ -69,7 +69,7 @@ int main() {
                     const size_t ws = paged_decode_workspace_bytes_ext(&x, &e, S);
                     const int ns = paged_decode_num_splits_ext(&x, &e, 4096);
                     const int nl = paged_decode_launches(&x, &e, S);
-                    const int np = paged_decode_path(&x, &e, causal, S);
+                    const int np = paged_decode_path(&x, &e, S);
                     (void)ns;
                     (void)nl;
                     (void)np;
@@ -90,6 +90,7 @@ int main() {
                               nullptr);
               pkd_decode_valu(&x, F, F, F, FI, FI, 0.125f, F, FF, nullptr);
               pkd_decode_lds(&x, F, F, F, FI, FI, 0.125f, F, FF, nullptr);
+              pkd_decode_registers(&x, F, F, F, FI, FI, 0.125f, F, FF, nullptr);
               paged_decode_check_tables(&x, FI, FI, reinterpret_cast<int32_t*>(F), nullptr);
               calls += 5;
             }

@@ -499,22 +499,38 @@ def test_paged_decode_path():
     reported, and bad arguments give statuses."""
     b32 = dims(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
                num_pages=1500, max_pages_per_seq=64)
-    assert b.paged_decode_path(b32, None, 0, 1) == b.PKD_PATH_DIRECT
-    assert b.paged_decode_path(b32, None, 1, 1) == b.PKD_PATH_DIRECT
-    assert b.paged_decode_path(b32, None, 0, 4) == b.PKD_PATH_SPLITS
-    assert b.paged_decode_path(b32, None, 0, b.PKD_SPLITS_BALANCED) == b.PKD_PATH_BALANCED
+    assert b.paged_decode_path(b32, None, 1) == b.PKD_PATH_DIRECT
+    assert b.paged_decode_path(b32, None, 4) == b.PKD_PATH_SPLITS
+    assert b.paged_decode_path(b32, None, b.PKD_SPLITS_BALANCED) == b.PKD_PATH_BALANCED
     long1 = dims(batch=1, num_q_heads=16, num_kv_heads=2, head_dim=64, page_size=64,
                  num_pages=2048, max_pages_per_seq=2048)
-    assert b.paged_decode_path(long1, None, 0, b.PKD_SPLITS_BALANCED) == b.PKD_PATH_BALANCED_MERGE
+    assert b.paged_decode_path(long1, None, b.PKD_SPLITS_BALANCED) == b.PKD_PATH_BALANCED_MERGE
     for S in (0, 1, 3, b.PKD_SPLITS_BALANCED):
         for d in (b32, long1):
-            path = b.paged_decode_path(d, None, 0, S)
+            path = b.paged_decode_path(d, None, S)
             want = 1 if path in (b.PKD_PATH_DIRECT, b.PKD_PATH_DIRECT_LDS, b.PKD_PATH_BALANCED) else 2
             assert b.paged_decode_launches(d, None, S) == want
-    assert b.paged_decode_path(None, None, 0, 1) == b.PKD_ERR_NULL_POINTER
-    assert b.paged_decode_path(b32, None, 2, 1) == b.PKD_ERR_BAD_DIMS
-    assert b.paged_decode_path(b32, None, 0, -5) == b.PKD_ERR_NUM_SPLITS
-    assert b.paged_decode_path(dims(head_dim=96), None, 0, 1) == b.PKD_ERR_HEAD_DIM
+    assert b.paged_decode_path(None, None, 1) == b.PKD_ERR_NULL_POINTER
+    assert b.paged_decode_path(b32, None, -5) == b.PKD_ERR_NUM_SPLITS
+    assert b.paged_decode_path(dims(head_dim=96), None, 1) == b.PKD_ERR_HEAD_DIM
+
+
+def test_registers_entry_argument_checks():
+    """pkd_decode_registers checks its arguments as paged_decode does (bf16 only)."""
+    def v(d, q=FAKE, lse=None, out=FAKE):
+        return b.pkd_decode_registers(d, q, FAKE, FAKE, FAKE, FAKE, 0.125, out, lse, None)
+    assert v(None) == b.PKD_ERR_NULL_POINTER
+    assert v(dims(head_dim=96)) == b.PKD_ERR_HEAD_DIM
+    assert v(dims(kv_dtype=b.PKD_DTYPE_FP8_E4M3)) == b.PKD_ERR_SCALES
+    assert v(dims(num_q_heads=6, num_kv_heads=4)) == b.PKD_ERR_GQA
+    assert v(dims(), q=None) == b.PKD_ERR_NULL_POINTER
+    assert v(dims(), out=None) == b.PKD_ERR_NULL_POINTER
+    assert v(dims(), q=FAKE + 8) == b.PKD_ERR_ALIGNMENT
+    assert v(dims(), lse=FAKE + 2) == b.PKD_ERR_ALIGNMENT
+    assert v(dims(batch=0)) == b.PKD_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert v(dims()) == b.PKD_ERR_DEVICE
 
 
 # ---- paged_decode_metadata argument checks ----------------------------------

@@ -1319,21 +1319,66 @@ def test_lds_entry_matches_oracle_and_grid_kernel(B, case):
 
 
 def test_direct_output_path_choice(B):
-    """paged_decode runs the LDS-staged direct kernel for one round of plain
-    D = 128 items and the register-staged one otherwise; both give the same bits,
-    so the switch is invisible in the results."""
+    """paged_decode runs the LDS-staged direct kernel for one round of D = 128
+    items of one query token without a window, and the register-staged one
+    otherwise; both give the same bits, so the switch is invisible in the
+    results."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     b32 = B.pkd_dims(32, 32, 8, 128, 64, 1500, 64, B.PKD_DTYPE_BF16)
-    one_round = 32 * 8 <= cus
-    want = B.PKD_PATH_DIRECT_LDS if one_round else B.PKD_PATH_DIRECT
-    assert B.paged_decode_path(b32, None, 0, 1) == want
-    assert B.paged_decode_path(b32, None, 1, 1) == B.PKD_PATH_DIRECT  # sinks
-    assert B.paged_decode_path(b32, B.pkd_ext(2, 1, 0, 0), 0, 1) == B.PKD_PATH_DIRECT  # two query tokens
-    assert B.paged_decode_path(b32, B.pkd_ext(1, 0, 512, 0), 0, 1) == B.PKD_PATH_DIRECT  # window
+    lds = B.PKD_PATH_DIRECT_LDS if 32 * 8 <= cus else B.PKD_PATH_DIRECT
+    assert B.paged_decode_path(b32, None, 1) == lds
+    assert B.paged_decode_path(b32, B.pkd_ext(1, 1, 0, 0), 1) == lds  # causal, one token: no mask
+    assert B.paged_decode_path(b32, B.pkd_ext(4, 1, 0, 0), 1) == B.PKD_PATH_DIRECT  # 4 query tokens
+    assert B.paged_decode_path(b32, B.pkd_ext(1, 0, 512, 0), 1) == B.PKD_PATH_DIRECT  # window
     b128 = B.pkd_dims(128, 32, 8, 128, 128, 4100, 32, B.PKD_DTYPE_BF16)
-    assert B.paged_decode_path(b128, None, 0, 1) == B.PKD_PATH_DIRECT  # four rounds
+    assert B.paged_decode_path(b128, None, 1) == B.PKD_PATH_DIRECT  # four rounds
     fp8 = B.pkd_dims(32, 32, 8, 128, 64, 1500, 64, B.PKD_DTYPE_FP8_E4M3)
-    assert B.paged_decode_path(fp8, None, 0, 1) == B.PKD_PATH_DIRECT
+    assert B.paged_decode_path(fp8, None, 1) == B.PKD_PATH_DIRECT
+
+
+@pytest.mark.parametrize("q_len,causal,sinks", [(1, False, True), (1, True, True), (1, False, False),
+                                                 (4, True, True)])
+def test_lds_direct_equals_grid_kernel_with_sinks(B, q_len, causal, sinks):
+    """Direct output at the B = 32 shape (LDS-staged where one round fits, for one
+    query token) against the same call with a window longer than every sequence,
+    which changes no score but runs the register-staged grid kernel: the bits
+    must agree, with and without sinks (and for four causal query tokens, which
+    both calls send to the grid kernel)."""
+    lens = [1024 + 97 * i for i in range(31)] + [3]  # a sequence shorter than q_len too
+    w = wl.custom_workload(32, 32, 8, 128, 64, lens, "bf16", 1234 + q_len, q_len=q_len, causal=causal,
+                           sinks=sinks)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    big = w.spec.max_pages_per_seq * w.spec.page_size + 64
+    assert B.paged_decode_path(dims, B.ext_for(t["q"], causal, big), 1) == B.PKD_PATH_DIRECT
+    out_w, lse_w = B.decode(t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale, num_splits=1, causal=causal,
+                            window=big, sinks=t["sinks"])
+    out, lse = run(B, w, 1, t)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_w.cpu().view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse_w.cpu().view(torch.int32))
+    check(out, lse, *oracle_full(w), what=f"lds direct q_len={q_len} causal={causal} sinks={sinks}")
+
+
+@pytest.mark.parametrize("case", LDS_CASES)
+def test_registers_entry_equals_paged_decode(B, case):
+    """pkd_decode_registers (the grid kernel whatever the shape) against the oracle
+    and bit for bit against paged_decode with num_splits = 1."""
+    bq, hq, hkv, d, ps, lens, seed = case
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, "bf16", seed)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    out = torch.full(t["q"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(t["q"].shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    st = B.pkd_decode_registers(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale, out, lse,
+                                B.current_stream_handle(0))
+    assert st == 0, B.paged_decode_status_string(st)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    check(out, lse, *oracle_full(w), what=f"registers {case[:5]}")
+    out1, lse1 = run(B, w, 1, t)
+    assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse1.view(torch.int32))
 
 
 @pytest.mark.parametrize("name", ["llama_b32_d128_ps64", "batch128_d128_ps128"])
