@@ -515,8 +515,8 @@ def decode_low_load(steps, warmup, device):
 # layout (64 bytes of each of 16 rows per load), for comparison; pattern 2 is
 # pattern 0 issued as direct-to-LDS loads (the load path of a pipeline staged
 # in shared memory instead of registers).
-STREAM_SHAPES = [(0, 256, 4, 8), (0, 256, 4, 16), (0, 1024, 4, 8), (0, 2048, 4, 4), (1, 256, 4, 8),
-                 (1, 1024, 4, 8), (2, 256, 4, 4), (2, 256, 4, 8), (2, 1024, 4, 4)]
+STREAM_SHAPES = [(0, 256, 4, 4), (0, 256, 4, 8), (0, 256, 4, 16), (0, 1024, 4, 8), (0, 2048, 4, 4),
+                 (1, 256, 4, 8), (1, 1024, 4, 8), (2, 256, 4, 4), (2, 256, 4, 8), (2, 1024, 4, 4)]
 STREAM_PATTERNS = {0: "row order", 1: "matrix-core operand layout", 2: "row order, direct to LDS"}
 # The same streams with only 8 workgroups on the chip (one 256-byte column of
 # 8192 rows each, like one KV head of an 8192-token sequence): the rate one
