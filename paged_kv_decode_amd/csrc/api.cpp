@@ -329,8 +329,8 @@ int32_t check_out_ws(const void* out, const float* lse, const void* ws) {
 // Direct output with K/V tiles loaded straight into LDS stages, where that
 // kernel applies and the (sequence, KV head) items fit in one round of
 // workgroups.  It gives the grid kernel's bits; measured back to back it was
-// 0.8-1.2% faster at B = 32 (256 items on 256 units) and 1% slower at B = 128
-// (1024 items, four rounds).
+// about 0.7% faster at B = 32 (256 items on 256 units; ahead in five of six
+// comparisons) and 1-1.5% slower at B = 128 (1024 items, four rounds).
 bool use_lds_direct(const Dims& d, const Layout& lay) {
   const int cus = current_cu_count();
   return pkd::lds_direct_applies(d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, d.q_len, d.window,
