@@ -1381,6 +1381,35 @@ def test_registers_entry_equals_paged_decode(B, case):
     assert torch.equal(lse.view(torch.int32), lse1.view(torch.int32))
 
 
+def test_lds_and_register_direct_kernels_agree_on_random_shapes(B):
+    """24 seeded random shapes (batch, G, page size, ragged and empty lengths, NaN
+    tails): the LDS-staged kernel (pkd_decode_lds) and the register-staged grid
+    kernel (pkd_decode_registers) give the same bits."""
+    rng = np.random.default_rng(20261203)
+    for case in range(24):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        bq = int(rng.integers(1, 33))
+        ps = int(rng.choice([16, 32, 48, 64, 128]))
+        lens = [int(x) for x in rng.integers(0, 2500, size=bq)]
+        lens[int(rng.integers(0, bq))] = int(rng.choice([0, 1, 15, 16, 17]))
+        w = wl.custom_workload(bq, hkv * G, hkv, 128, ps, lens, "bf16", 7000 + case)
+        t = dev(w)
+        dims = B.dims_for(t["q"], t["k"], t["bt"])
+        outs = []
+        for fn in (B.pkd_decode_lds, B.pkd_decode_registers):
+            out = torch.full(t["q"].shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+            lse = torch.full(t["q"].shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+            st = fn(dims, t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale, out, lse, B.current_stream_handle(0))
+            assert st == 0, B.paged_decode_status_string(st)
+            outs.append((out, lse))
+        torch.cuda.synchronize()
+        (o1, l1), (o2, l2) = outs
+        what = f"case {case}: B={bq} Hkv={hkv} G={G} ps={ps}"
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), what
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), what
+
+
 @pytest.mark.parametrize("name", ["llama_b32_d128_ps64", "batch128_d128_ps128"])
 def test_lds_entry_full_size(B, name):
     """Every row of the B=32 and B=128 steps, as timed beside the register-staged kernel."""
