@@ -639,8 +639,8 @@ def cpu_baseline(w, nbytes):
 # The sources the partition kernels are built from (their digest tags the counter summaries).
 # The kernels' sources and the host code that picks which kernel a workload runs.
 KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_decode_amd", "csrc", f) for f in
-               ("decode_kernels.hpp", "wave_attn.hpp", "merge_row.hpp", "pkd_internal.hpp", "decode_d128.hip",
-                "api.cpp")]
+               ("decode_kernels.hpp", "wave_attn.hpp", "lds_pipe.hpp", "merge_row.hpp", "pkd_internal.hpp",
+                "decode_d128.hip", "lds_decode.hip", "api.cpp")]
 CALIB_BYTES = 1 << 30  # the 1 GiB device-to-device copy made at start-up
 
 

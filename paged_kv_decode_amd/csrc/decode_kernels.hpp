@@ -26,7 +26,7 @@
 // wave_attn.hpp.
 #pragma once
 
-#include "wave_attn.hpp"
+#include "lds_pipe.hpp"
 
 namespace pkd {
 namespace {
@@ -206,9 +206,14 @@ split_kv_kernel(const SplitParams p) {
 // hkv and group counting wide heads), each query row zero-padded outside its
 // own head's dims, and writes only its own head's DR dims (see load_q).  Each
 // line is then read once, by one workgroup.
-template <int D, bool FP8, int NWV, bool STRIDED, bool WINDOW, bool SINKS, int VK>
-__global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4)))
+// LDSP: the tiles are loaded straight into LDS stages by the FP8 pipeline of
+// lds_pipe.hpp (LdsPipeF8) instead of being held in registers (run_tiles):
+// FP8 D = 128 in the paged layout, without a window or paired heads.  Its two
+// waves per SIMD as the register budget keep the accumulators in VGPRs.
+template <int D, bool FP8, int NWV, bool STRIDED, bool WINDOW, bool SINKS, int VK, bool LDSP = false>
+__global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(LDSP ? 2 : NWV / 4)))
 balanced_kernel(const BalancedParams p) {
+  static_assert(!LDSP || (D == kLpD && FP8 && !STRIDED && !WINDOW && VK == 1), "LDS-staged instance");
   typedef Cfg<D, FP8> C;
   constexpr int DR = D / VK;  // dims of a real head
   typedef Geometry<D, FP8, STRIDED> Geo;    // K/V rows (of wide heads when paired)
@@ -216,7 +221,7 @@ balanced_kernel(const BalancedParams p) {
   // Without a window (the instance for window = 0) nothing of it stays live.
   const int win = WINDOW ? p.window : 0;
   typedef TilePages<D, FP8, true> Pages;
-  constexpr int VT_BYTES = NWV * C::WT * 2;                         // wave-private V (and K) tiles
+  constexpr int VT_BYTES = LDSP ? NWV * kLfWaveB : NWV * C::WT * 2;  // wave-private tiles or LDS stages
   constexpr int MERGE_BYTES = NWV * 16 * (2 + C::OW_STRIDE) * 4 + 16 * (NWV + 4) * 4;  // combine staging
   constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
@@ -320,6 +325,8 @@ balanced_kernel(const BalancedParams p) {
   const int ps = p.page_size;
   const int tok_stride = Geo::tok_stride(p);
   const int64_t page_stride = Geo::page_stride(p);
+  LdsPipeF8 pipe;
+  if constexpr (LDSP) pipe.init(smem, wave * kLfWaveB, A, tid & 63, tok_stride);
 
   // Page window of a piece: lane j holds block-table entry first_page + j of
   // sequence bb (entries past the row are not read; entries past the pieces's
@@ -386,7 +393,12 @@ balanced_kernel(const BalancedParams p) {
       A.issue_paged16(p.k, p.v, s0 + tile * C::TT, lim, P.pg, ps, tok_stride, page_stride, head_off, R, idle);
     };
     const int ntiles = (s1 - s0 + C::TT - 1) / C::TT;
-    run_tiles<D, FP8, Pages>(A, wave, NWV, ntiles, s0, lr, vs, fetch, issue);
+    if constexpr (LDSP)
+      lds_pipe_run_ns<kLfStages>(pipe, A, wave, NWV, ntiles, s0, s1, lr.end, lr.end_min, p.k, p.v, [&](int t) -> int64_t {
+        return (int64_t)page_of(t / ps) * page_stride + (int64_t)(t % ps) * tok_stride + head_off;
+      });
+    else
+      run_tiles<D, FP8, Pages>(A, wave, NWV, ntiles, s0, lr, vs, fetch, issue);
 
     // This segment's pieces are those of workgroups w_first .. w_last, at
     // slots w + s (s = b * SPB + seg).
@@ -475,12 +487,13 @@ balanced_kernel(const BalancedParams p) {
           // The pieces' partials, read from the coherent copy.  Wave w merges
           // rows w, w + NWV, ...  With few pieces the loads of RC rows at a
           // time are issued before any of them is combined (RC rows of staged
-          // partials take at most 64 registers with one wave per SIMD, 32 with
-          // two); otherwise, or when only one row fits, one row at a time.
+          // partials take at most 64 registers under a one-wave-per-SIMD
+          // register budget, 32 under two); otherwise, or when only one row
+          // fits, one row at a time.
           const int64_t slot0 = w_first + sidx;
           typedef RowMerge<DR, true> RM;
           constexpr int MAXR = kHeadsPerGroup / NWV;
-          constexpr int RC_REG = (NWV > 4 ? 32 : 64) / (RM::UNROLL * RM::EPL);
+          constexpr int RC_REG = (NWV > 4 || LDSP ? 32 : 64) / (RM::UNROLL * RM::EPL);
           constexpr int RC = RC_REG < MAXR ? RC_REG : MAXR;
           const float* lp0 = p.lse_part + slot0 * p.hpg;
           const float* op0 = p.o_part + slot0 * p.hpg * DR;
@@ -555,17 +568,22 @@ hipError_t launch_d(const SplitParams& p, int batch, bool direct, bool paged16, 
 // FP8, whose tiles carry half the bytes, so that as many bytes are in flight
 // per compute unit (measured: 3% faster for FP8, 4-20% slower for bf16).
 constexpr int balanced_waves(bool fp8) { return fp8 ? 8 : 4; }
+// Waves per workgroup of the LDS-staged FP8 instance (16 KiB of stages each).
+constexpr int kBalancedLdsWaves = 8;
 
 // Instances without a window or without sinks keep none of their state live
 // (the kernel is at the edge of its scalar registers).
+// FP8 D = 128 in the paged layout without a window or pairing runs the
+// LDS-staged tile pipeline.
 template <int D, bool FP8, bool STRIDED, bool WINDOW, int VK = 1>
 void launch_bw(const BalancedParams& p, hipStream_t stream) {
-  constexpr int NWV = balanced_waves(FP8);
+  constexpr bool LDSP = D == kLpD && FP8 && !STRIDED && !WINDOW && VK == 1;
+  constexpr int NWV = LDSP ? kBalancedLdsWaves : balanced_waves(FP8);
   if (p.sinks)
-    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, true, VK>), dim3(p.num_workers),
+    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, true, VK, LDSP>), dim3(p.num_workers),
                        dim3(NWV * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, false, VK>), dim3(p.num_workers),
+    hipLaunchKernelGGL((balanced_kernel<D, FP8, NWV, STRIDED, WINDOW, false, VK, LDSP>), dim3(p.num_workers),
                        dim3(NWV * 64), 0, stream, p);
 }
 

@@ -1421,6 +1421,44 @@ def test_lds_entry_full_size(B, name):
     assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
 
 
+# ---- FP8 on the LDS-staged pipeline (balanced kernel, D = 128) -------------------
+
+FP8_LDS_CASES = [
+    # (B, Hq, Hkv, ps, seq_lens, q_len, causal, sinks, seed): G = 8, 1, 16, 4; page
+    # sizes 16..128 (32-token tiles straddling pages), ragged, empty and short
+    # sequences, causal query tokens, pieces starting on odd 16-token groups.
+    (64, 64, 8, 64, None, 1, False, False, 1601),
+    (5, 32, 4, 16, [700, 2, 0, 3001, 64], 1, False, True, 1602),
+    (4, 16, 16, 32, [1, 17, 300, 33], 1, False, False, 1603),
+    (3, 16, 1, 48, [5000, 31, 129], 3, True, False, 1604),
+    (6, 32, 8, 128, [95, 96, 97, 1, 480, 15], 2, True, True, 1605),
+    (2, 16, 4, 16, [8191, 4097], 1, False, False, 1606),
+]
+
+
+@pytest.mark.parametrize("case", FP8_LDS_CASES)
+def test_fp8_lds_pipeline_equals_register_path(B, case):
+    """FP8 K/V, D = 128, balanced mode: the tiles go through the LDS-staged pipeline.
+    The same call with a window longer than every sequence changes no score but
+    runs the register-staged tile loop; the bits must agree, and both must match
+    the oracle."""
+    bq, hq, hkv, ps, lens, q_len, causal, sinks, seed = case
+    if lens is None:
+        lens = [int(x) for x in np.random.default_rng(seed).integers(512, 8193, size=bq)]
+    w = wl.custom_workload(bq, hq, hkv, 128, ps, lens, "fp8_e4m3", seed, q_len=q_len, causal=causal,
+                           sinks=sinks)
+    t = dev(w)
+    big = w.spec.max_pages_per_seq * w.spec.page_size + 64
+    out, lse = run(B, w, B.PKD_SPLITS_BALANCED, t)
+    out_w, lse_w = B.decode(t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale, t["ks"], t["vs"],
+                            num_splits=B.PKD_SPLITS_BALANCED, causal=causal, window=big, sinks=t["sinks"])
+    torch.cuda.synchronize()
+    what = f"fp8 lds {case[:4]} q_len={q_len}"
+    assert torch.equal(out.view(torch.int16), out_w.cpu().view(torch.int16)), what
+    assert torch.equal(lse.view(torch.int32), lse_w.cpu().view(torch.int32)), what
+    check(out, lse, *oracle_full(w), what=what)
+
+
 # ---- the read-only stream kernel (measurement entry) ----------------------------
 
 @pytest.mark.parametrize("pattern", [0, 1])
