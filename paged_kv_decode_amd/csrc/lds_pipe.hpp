@@ -78,6 +78,19 @@ template <int N>
 __device__ __forceinline__ void lp_wait_loads() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
 __device__ __forceinline__ void lp_wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
+// lp_wait_loads<STEP * a + BASE>() for a runtime a in [0, MAXA] (uniform).
+template <int STEP, int BASE, int MAXA>
+__device__ __forceinline__ void lp_wait_loads_rt(int a) {
+  if constexpr (MAXA == 0) {
+    lp_wait_loads<BASE>();
+  } else {
+    if (a >= MAXA)
+      lp_wait_loads<STEP * MAXA + BASE>();
+    else
+      lp_wait_loads_rt<STEP, BASE, MAXA - 1>(a);
+  }
+}
+
 // Scores to weights, as WaveAttn::process does them, step for step: s[blk][i]
 // (the raw dot products of token tok_of(blk, i)) is scaled and, unless
 // `unmasked`, set to -inf at or past `end`; the reference maximum is raised
@@ -331,12 +344,12 @@ struct LdsPipeF8 {
   }
 
   // The tile of tokens tb .. tb + 31 from stage ST (as LdsPipe::compute).
+  // `ahead` tiles (uniform, 0 .. kLfStages - 1) were issued after it, 2
+  // kLfLoads loads each: its K codes have landed at (2 ahead + 1) kLfLoads
+  // outstanding loads, its V codes at 2 ahead kLfLoads.
   template <int ST>
-  __device__ __forceinline__ void compute(WA& A, int tb, int end, int end_min) const {
-    // With every stage's loads issued (2 kLfLoads each, oldest first), the
-    // oldest stage's K codes have landed at (2 kLfStages - 1) kLfLoads
-    // outstanding and its V codes at 2 (kLfStages - 1) kLfLoads.
-    lp_wait_loads<(2 * kLfStages - 1) * kLfLoads>();  // the tile's K codes have landed
+  __device__ __forceinline__ void compute(WA& A, int tb, int end, int end_min, int ahead) const {
+    lp_wait_loads_rt<2 * kLfLoads, kLfLoads, kLfStages - 1>(ahead);  // the tile's K codes have landed
     f32x4 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -358,7 +371,7 @@ struct LdsPipeF8 {
       pb[i] = (__bf16)s[0][i];
       pb[4 + i] = (__bf16)s[1][i];
     }
-    lp_wait_loads<2 * (kLfStages - 1) * kLfLoads>();  // and its V codes
+    lp_wait_loads_rt<2 * kLfLoads, 0, kLfStages - 1>(ahead);  // and its V codes
 #pragma unroll
     for (int nb = 0; nb < WA::C::NB; ++nb) {
       const bf16x8 a = fp8x8_to_bf16(lds_read_tr8(smem + vofs[nb] + ST * kLfStageB));
@@ -424,10 +437,11 @@ __device__ __forceinline__ bool lp_stage_round(F& f) {
   }
 }
 
-// lds_pipe_run with NS stages per wave (NS tiles in flight): the stages are
-// filled with the wave's first NS tiles; then, stage by stage, a tile is
-// computed and its stage refilled with the next tile not yet loaded (the last
-// tile again once there is none, so that every wait sees the same count).
+// lds_pipe_run with NS stages per wave (up to NS tiles in flight) and no
+// redundant loads: the stages are filled with the wave's first tiles (at most
+// NS); then, stage by stage, a tile is computed and its stage refilled with
+// the next tile not yet loaded, if there is one.  compute is told how many
+// tiles were issued after the one it computes, which sets its wait counts.
 template <int NS, typename Pipe, typename WA, typename RowOf>
 __device__ __forceinline__ void lds_pipe_run_ns(const Pipe& P, WA& A, int first, int step, int ntiles, int s0,
                                                 int s1, int end, int end_min, const uint8_t* k, const uint8_t* v,
@@ -437,9 +451,15 @@ __device__ __forceinline__ void lds_pipe_run_ns(const Pipe& P, WA& A, int first,
     const int lim = s1 - 1;
     auto nxt = [&](int t) { return t + step < ntiles ? t + step : t; };
     int newest = first;
+    int ahead = 0;  // tiles issued after cur
     auto fill = [&](auto stage_c) {
       constexpr int ST = decltype(stage_c)::value;
-      if constexpr (ST > 0) newest = nxt(newest);
+      if constexpr (ST > 0) {
+        const int n = nxt(newest);
+        if (n == newest) return false;  // fewer tiles than stages
+        newest = n;
+        ++ahead;
+      }
       P.template put<ST>(k, v, s0 + newest * TT, lim, row_of);
       return true;
     };
@@ -447,11 +467,16 @@ __device__ __forceinline__ void lds_pipe_run_ns(const Pipe& P, WA& A, int first,
     int cur = first;
     auto turn = [&](auto stage_c) {
       constexpr int ST = decltype(stage_c)::value;
-      P.template compute<ST>(A, s0 + cur * TT, end, end_min);
+      P.template compute<ST>(A, s0 + cur * TT, end, end_min, ahead);
       const int n2 = nxt(cur);
       if (n2 == cur) return false;  // that was the wave's last tile
-      newest = nxt(newest);
-      P.template put<ST>(k, v, s0 + newest * TT, lim, row_of);
+      const int n = nxt(newest);
+      if (n != newest) {
+        newest = n;
+        P.template put<ST>(k, v, s0 + newest * TT, lim, row_of);
+      } else {
+        --ahead;
+      }
       cur = n2;
       return true;
     };
