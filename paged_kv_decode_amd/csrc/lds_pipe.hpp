@@ -19,10 +19,12 @@
 //    direct-to-LDS load before any LDS read, which leaves one tile in flight.
 //    The loads are therefore issued from inline assembly (the LDS address
 //    passed in M0; they write no register), and the wave waits by count: with
-//    two tiles issued (4 + 4 instructions each), vmcnt(12) means the older
-//    tile's K has landed and vmcnt(8) its V.  Loads issued before a pipeline
-//    starts complete first (loads complete in issue order), and no other
-//    vector-memory load is issued while it runs, so the counts are exact.
+//    the next tile issued after the current one (4 + 4 instructions each),
+//    vmcnt(12) means the current tile's K has landed and vmcnt(8) its V; with
+//    none (the wave's last tile), vmcnt(4) and vmcnt(0).  Loads issued before
+//    a pipeline starts complete first (loads complete in issue order), and no
+//    other vector-memory load is issued while it runs, so the counts are
+//    exact.
 //    Before a stage is refilled the wave's LDS reads of it have completed
 //    (lgkmcnt(0)); after the last tile every load is waited for (vmcnt(0)), so
 //    the caller may reuse the stages.
@@ -197,9 +199,12 @@ struct LdsPipe {
   // The tile of tokens tb .. tb + 15 from stage ST: QK^T, the softmax against
   // the reference maximum, PV.  Tokens at or past end (this lane's row's end)
   // are masked; end_min (uniform) bounds every lane's end from below.
+  // `ahead` (uniform, 0 or 1) tiles were issued after this one: its K has
+  // landed at (2 ahead + 1) kLpLoads outstanding loads, its V at 2 ahead
+  // kLpLoads.
   template <int ST>
-  __device__ __forceinline__ void compute(WA& A, int tb, int end, int end_min) const {
-    lp_wait_loads<3 * kLpLoads>();  // the tile's K has landed (its V may still be in flight)
+  __device__ __forceinline__ void compute(WA& A, int tb, int end, int end_min, int ahead) const {
+    lp_wait_loads_rt<2 * kLpLoads, kLpLoads, 1>(ahead);  // the tile's K has landed (its V may still be in flight)
     f32x4 s[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kk = 0; kk < WA::C::KK; ++kk) {
@@ -211,7 +216,7 @@ struct LdsPipe {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pb[i] = (__bf16)s[0][i];
     const s16x4 pbs = bit_cast_dev<s16x4>(pb);
-    lp_wait_loads<2 * kLpLoads>();  // and its V
+    lp_wait_loads_rt<2 * kLpLoads, 0, 1>(ahead);  // and its V
 #pragma unroll
     for (int nb = 0; nb < WA::C::NB; ++nb) {
       const s16x4 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(smem + vofs[nb] + ST * kLpStageB));
@@ -381,50 +386,6 @@ struct LdsPipeF8 {
   }
 };
 
-// The loop of both pipelines: tiles first, first + step, ... (< ntiles) of the
-// token range [s0, s1) (s0 a multiple of 16; every 16-token group lies in one
-// page), two in flight, the older computed while the newer loads.  row_of(t)
-// gives the byte offset of token t's row (page, slot and KV head) in the
-// caches, uniform, for t a multiple of 16.  end / end_min: as for compute.
-// After the last tile the refill repeats the newer tile (rows already loaded)
-// so that every wait sees the same count; it is never read.  Returns with
-// every load complete.
-template <typename Pipe, typename WA, typename RowOf>
-__device__ __forceinline__ void lds_pipe_run(const Pipe& P, WA& A, int first, int step, int ntiles, int s0, int s1,
-                                             int end, int end_min, const uint8_t* k, const uint8_t* v,
-                                             RowOf row_of) {
-  constexpr int TT = Pipe::TT;
-  if (first < ntiles) {
-    const int lim = s1 - 1;
-    auto nxt = [&](int t) { return t + step < ntiles ? t + step : t; };
-    typedef std::integral_constant<int, 0> S0;
-    typedef std::integral_constant<int, 1> S1;
-    auto put = [&](int t, auto stage_c) {
-      constexpr int ST = decltype(stage_c)::value;
-      P.template put<ST>(k, v, s0 + t * TT, lim, row_of);
-    };
-    int t = first;
-    put(t, S0());
-    int t1 = nxt(t);
-    put(t1, S1());
-    while (true) {
-      P.template compute<0>(A, s0 + t * TT, end, end_min);
-      if (t1 == t) break;
-      int t2 = nxt(t1);
-      put(t2, S0());
-      t = t1;
-      t1 = t2;
-      P.template compute<1>(A, s0 + t * TT, end, end_min);
-      if (t1 == t) break;
-      t2 = nxt(t1);
-      put(t2, S1());
-      t = t1;
-      t1 = t2;
-    }
-  }
-  lp_wait_loads<0>();
-}
-
 // Stage S of an NS-stage round: f(stage) computes the tile in that stage and
 // refills it; false ends the rounds.
 template <int S, int NS, typename F>
@@ -437,11 +398,17 @@ __device__ __forceinline__ bool lp_stage_round(F& f) {
   }
 }
 
-// lds_pipe_run with NS stages per wave (up to NS tiles in flight) and no
-// redundant loads: the stages are filled with the wave's first tiles (at most
-// NS); then, stage by stage, a tile is computed and its stage refilled with
-// the next tile not yet loaded, if there is one.  compute is told how many
-// tiles were issued after the one it computes, which sets its wait counts.
+// The loop of both pipelines: tiles first, first + step, ... (< ntiles) of the
+// token range [s0, s1) (s0 a multiple of 16; every 16-token group lies in one
+// page), with NS stages per wave, so that up to NS tiles are in flight and the
+// oldest is computed while the newer ones load.  The stages are filled with
+// the wave's first tiles (at most NS); then, stage by stage, a tile is
+// computed and its stage refilled with the next tile not yet loaded, if there
+// is one.  compute is told how many tiles were issued after the one it
+// computes, which sets its wait counts.  row_of(t) gives the byte offset of
+// token t's row (page, slot and KV head) in the caches, uniform, for t a
+// multiple of 16.  end / end_min: as for compute.  Returns with every load
+// complete.
 template <int NS, typename Pipe, typename WA, typename RowOf>
 __device__ __forceinline__ void lds_pipe_run_ns(const Pipe& P, WA& A, int first, int step, int ntiles, int s0,
                                                 int s1, int end, int end_min, const uint8_t* k, const uint8_t* v,
@@ -489,7 +456,7 @@ __device__ __forceinline__ void lds_pipe_run_ns(const Pipe& P, WA& A, int first,
 template <typename RowOf>
 __device__ __forceinline__ void LdsPipe::run(WA& A, int first, int step, int ntiles, int s0, int s1, int end,
                                              int end_min, const uint8_t* k, const uint8_t* v, RowOf row_of) const {
-  lds_pipe_run(*this, A, first, step, ntiles, s0, s1, end, end_min, k, v, row_of);
+  lds_pipe_run_ns<2>(*this, A, first, step, ntiles, s0, s1, end, end_min, k, v, row_of);
 }
 
 }  // namespace
