@@ -266,12 +266,13 @@ def kernel_label(spec, path):
             B.PKD_PATH_DIRECT_LDS: "lds_direct_kernel" + t + " (direct output, tiles loaded into LDS)",
             B.PKD_PATH_SPLITS: "split_kv_kernel" + t + " (partials) + lse_merge_kernel",
             B.PKD_PATH_BALANCED: "balanced_kernel" + t + " (merging in place)",
-            B.PKD_PATH_BALANCED_MERGE: "balanced_kernel" + t + " + lse_merge_kernel"}[path]
+            B.PKD_PATH_BALANCED_MERGE: "balanced_kernel" + t + " + lse_merge_kernel",
+            B.PKD_PATH_PAIRED: "balanced_kernel" + t + " (whole items paired by length)"}[path]
 
 
 # Kernel-name prefixes of each path's partition kernel in rocprofv3's traces.
 PATH_TRACE_PREFIX = {1: "pkd::split_kv_kernel<", 2: "pkd::lds_direct_kernel", 3: "pkd::split_kv_kernel<",
-                     4: "pkd::balanced_kernel<", 5: "pkd::balanced_kernel<"}
+                     4: "pkd::balanced_kernel<", 5: "pkd::balanced_kernel<", 6: "pkd::balanced_kernel<"}
 
 
 CPU_SAMPLE_S = 10.0  # length of the CPU-baseline sample

@@ -123,6 +123,22 @@ extern "C" {
 #define PKD_SPLITS_BALANCED (-1000)
 #define PKD_BALANCED_MAX_BATCH 1024
 
+/* PKD_SPLITS_PAIRED selects whole items paired by length: the balanced
+ * partition's grid, in which each workgroup takes one or two whole
+ * (sequence, KV head, head group) items, so that nothing is split or merged.
+ * The device ranks the items by length (from seq_lens, with the window);
+ * with N items on W workgroups and N > W, the 2(N - W) shortest are taken in
+ * pairs, the shortest with the longest of them, and the rest one each.  When
+ * that would give some workgroup more than 1.6 times the mean work per
+ * workgroup, or N > 2W, the kernel uses the balanced partition's equal ranges
+ * instead, merging in place.  It needs what the balanced mode needs, and
+ * batch <= PKD_PAIRED_MAX_BATCH and max_pages_per_seq * page_size < 2^27; one
+ * kernel, paged_decode_ext only (the two-phase entries reject it).  This is the
+ * split-or-not choice of the AstrAI commit log's shared split-count helper
+ * (compute_num_splits), taken per item from the lengths on the device. */
+#define PKD_SPLITS_PAIRED (-1001)
+#define PKD_PAIRED_MAX_BATCH 256
+
 /* Split boundaries: with S splits, sequence b's split j covers tokens
  * [min(lo_b + j*c, L_b), min(lo_b + (j+1)*c, L_b)) where
  * c = PKD_SPLIT_ALIGN * ceil(ceil(N / S) / PKD_SPLIT_ALIGN),
@@ -204,7 +220,8 @@ int32_t paged_decode(const pkd_dims* dims, const void* q, const void* k_cache, c
  *                1: direct output; 2..PKD_MAX_SPLITS: split-KV + merge;
  *                PKD_SPLITS_BALANCED: balanced partition, which merges the pieces of each
  *                (sequence, KV head) itself when few are expected (one kernel; see
- *                paged_decode_launches), else partition + merge (two kernels).
+ *                paged_decode_launches), else partition + merge (two kernels);
+ *                PKD_SPLITS_PAIRED: whole items paired by length (one kernel; above).
  *                Any other value is PKD_ERR_NUM_SPLITS.
  *   workspace    at least paged_decode_workspace_bytes_ext(dims, ext, num_splits) bytes.
  * Other arguments as for paged_decode.  With ext NULL, sinks NULL and num_splits
@@ -305,7 +322,9 @@ int32_t paged_decode_launches(const pkd_dims* dims, const pkd_ext* ext, int32_t 
  *                            batch * num_kv_heads at most the current device's compute units;
  *   PKD_PATH_SPLITS          split-KV partials, then the merge kernel;
  *   PKD_PATH_BALANCED        the balanced partition, merging in place;
- *   PKD_PATH_BALANCED_MERGE  the balanced partition, then the merge kernel.
+ *   PKD_PATH_BALANCED_MERGE  the balanced partition, then the merge kernel;
+ *   PKD_PATH_PAIRED          the balanced kernel in paired mode (whole items, or equal
+ *                            ranges merged in place when pairing balances too poorly).
  * Sinks do not change the path.  Host only; returns a status in [-11, -1] for
  * invalid dims or num_splits.
  */
@@ -314,6 +333,7 @@ int32_t paged_decode_launches(const pkd_dims* dims, const pkd_ext* ext, int32_t 
 #define PKD_PATH_SPLITS 3
 #define PKD_PATH_BALANCED 4
 #define PKD_PATH_BALANCED_MERGE 5
+#define PKD_PATH_PAIRED 6
 int32_t paged_decode_path(const pkd_dims* dims, const pkd_ext* ext, int32_t num_splits);
 
 /*

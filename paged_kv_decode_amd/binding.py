@@ -39,11 +39,14 @@ PKD_SPLIT_ALIGN = 64
 PKD_SPLITS_AUTO = 0
 PKD_SPLITS_BALANCED = -1000
 PKD_BALANCED_MAX_BATCH = 1024
+PKD_SPLITS_PAIRED = -1001
+PKD_PAIRED_MAX_BATCH = 256
 PKD_PATH_DIRECT = 1
 PKD_PATH_DIRECT_LDS = 2
 PKD_PATH_SPLITS = 3
 PKD_PATH_BALANCED = 4
 PKD_PATH_BALANCED_MERGE = 5
+PKD_PATH_PAIRED = 6
 PKD_DTYPE_BF16 = 0
 PKD_DTYPE_FP8_E4M3 = 1
 

@@ -116,6 +116,15 @@ bool balanced_ok(const Dims& d) {
   return T < ((int64_t)1 << 46);
 }
 
+// Whether the paired mode applies: the balanced partition applies (it is the
+// paired mode's fallback), the batch fits the kernel's ranking of sequences by
+// length, and a segment's group count fits the 23 bits of its ranking key.
+static_assert(pkd::kPairedMaxBatch == PKD_PAIRED_MAX_BATCH, "paired-mode batch limit");
+bool paired_ok(const Dims& d) {
+  return balanced_ok(d) && d.batch <= pkd::kPairedMaxBatch &&
+         (int64_t)d.max_pages_per_seq * d.page_size < ((int64_t)1 << 27);
+}
+
 // KV heads the balanced kernel reads as one: 2 when adjacent heads of the paged
 // layout share 128-byte lines (head rows of fewer than 128 bytes), the pair's
 // query rows still fit one 16-row group and the pair's width has a kernel
@@ -358,6 +367,8 @@ size_t workspace_of(const Dims& d, int32_t num_splits) {
   if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size);
   if (S == PKD_SPLITS_BALANCED)
     return balanced_ok(d) ? balanced_bytes(d, pair_heads(d, false), nullptr, nullptr, nullptr) : 0;
+  if (S == PKD_SPLITS_PAIRED)
+    return paired_ok(d) ? balanced_bytes(d, pair_heads(d, false), nullptr, nullptr, nullptr) : 0;
   if (S < 1 || S > PKD_MAX_SPLITS) return 0;
   if (S == 1) return 0;
   return partial_bytes(d, S, nullptr);
@@ -438,8 +449,9 @@ namespace {
 
 // Resolved split mode of one call.
 struct Plan {
-  int S;           // 1 = direct output, 2.. = grid splits, PKD_SPLITS_BALANCED
-  bool balanced;
+  int S;           // 1 = direct output, 2.. = grid splits, PKD_SPLITS_BALANCED or _PAIRED
+  bool balanced;   // the balanced kernel runs (balanced or paired mode)
+  bool paired;     // paired mode: whole segments paired by length, merging in place if it falls back
   int pair;        // balanced: KV heads read as one (pair_heads), else 1
   size_t need;     // workspace bytes
   size_t lse_off, prefix_off, count_off;
@@ -449,8 +461,11 @@ int32_t make_plan(const Dims& d, int32_t num_splits, bool strided, Plan* pl) {
   int S = num_splits;
   if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size);
   pl->S = S;
-  pl->balanced = S == PKD_SPLITS_BALANCED;
-  if (pl->balanced ? !balanced_ok(d) : (S < 1 || S > PKD_MAX_SPLITS)) return PKD_ERR_NUM_SPLITS;
+  pl->paired = S == PKD_SPLITS_PAIRED;
+  pl->balanced = S == PKD_SPLITS_BALANCED || pl->paired;
+  if (pl->paired ? !paired_ok(d)
+                 : pl->balanced ? !balanced_ok(d) : (S < 1 || S > PKD_MAX_SPLITS))
+    return PKD_ERR_NUM_SPLITS;
   pl->pair = pl->balanced ? pair_heads(d, strided) : 1;
   pl->lse_off = pl->prefix_off = pl->count_off = 0;
   pl->need = pl->balanced ? balanced_bytes(d, pl->pair, &pl->lse_off, &pl->prefix_off, &pl->count_off)
@@ -565,10 +580,12 @@ int32_t decode_checked(const Dims& d, const Layout& lay, const void* q, const vo
     if (use_lds_direct(d, lay)) return pkd::launch_lds_direct(p, d.batch, s) == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
     return launch_partition(d, p, true, s);
   }
-  if (pl.balanced && balanced_fused(d, pl.pair)) {
-    // One kernel: the partition merges each segment's pieces itself.
+  if (pl.balanced && (pl.paired || balanced_fused(d, pl.pair))) {
+    // One kernel: the partition merges each segment's pieces itself (or, in
+    // paired mode, takes whole segments).
     pkd::BalancedParams b = make_balanced_params(d, lay, q, k, v, bt, lens, ks, vs, scale, workspace, pl);
     b.fused = 1;
+    b.paired = pl.paired ? 1 : 0;
     b.out = static_cast<uint16_t*>(out);
     b.lse = lse;
     b.sinks = sinks;
@@ -611,7 +628,7 @@ int32_t paged_decode_launches(const pkd_dims* dims, const pkd_ext* ext, int32_t 
   Plan pl;
   const int32_t pst = make_plan(d, num_splits, false, &pl);
   if (pst != PKD_OK) return pst;
-  if (pl.S == 1 || (pl.balanced && balanced_fused(d, pl.pair))) return 1;
+  if (pl.S == 1 || (pl.balanced && (pl.paired || balanced_fused(d, pl.pair)))) return 1;
   return 2;
 }
 
@@ -643,6 +660,7 @@ int32_t paged_decode_path(const pkd_dims* dims, const pkd_ext* ext, int32_t num_
   const int32_t pst = make_plan(d, num_splits, false, &pl);
   if (pst != PKD_OK) return pst;
   if (pl.S == 1) return use_lds_direct(d, paged_layout(d)) ? PKD_PATH_DIRECT_LDS : PKD_PATH_DIRECT;
+  if (pl.paired) return PKD_PATH_PAIRED;
   if (pl.balanced) return balanced_fused(d, pl.pair) ? PKD_PATH_BALANCED : PKD_PATH_BALANCED_MERGE;
   return PKD_PATH_SPLITS;
 }
@@ -676,7 +694,7 @@ int32_t paged_decode_partition(const pkd_dims* dims, const pkd_ext* ext, const v
   Plan pl;
   st = make_plan(d, num_splits, false, &pl);
   if (st != PKD_OK) return st;
-  if (pl.S == 1) return PKD_ERR_NUM_SPLITS;
+  if (pl.S == 1 || pl.paired) return PKD_ERR_NUM_SPLITS;
   if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return PKD_ERR_ALIGNMENT;
   if (d.batch == 0) return PKD_OK;
@@ -698,7 +716,7 @@ int32_t paged_decode_finish(const pkd_dims* dims, const pkd_ext* ext, int32_t nu
   Plan pl;
   st = make_plan(d, num_splits, false, &pl);
   if (st != PKD_OK) return st;
-  if (pl.S == 1) return PKD_ERR_NUM_SPLITS;
+  if (pl.S == 1 || pl.paired) return PKD_ERR_NUM_SPLITS;
   if (!workspace || workspace_bytes < pl.need) return PKD_ERR_WORKSPACE;
   if (d.batch == 0) return PKD_OK;
   if (current_cu_count() < 0) return PKD_ERR_DEVICE;

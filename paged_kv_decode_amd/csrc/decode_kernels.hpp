@@ -201,6 +201,74 @@ split_kv_kernel(const SplitParams p) {
 // merge kernel finds segment s's pieces from the same formula.  page_size
 // must be a multiple of 16.
 
+// Paired whole items (the balanced kernel's paired mode).  Items are the
+// segments of the non-empty sequences, ranked by length (groups per segment,
+// ties by sequence).  With N items on W workgroups and E = N - W: for E <= 0
+// each workgroup takes one item, for 0 < E <= W the E workgroups of the 2E
+// shortest items take two (folded: the shortest with the longest of them), the
+// others one.  The plan is taken when no workgroup then holds more than 1.6x
+// the mean work per workgroup (T / W groups): whole items need no partial, no
+// count and no merge, which measured worth that much imbalance.  Otherwise
+// (or with more than 2W items) the kernel uses its equal ranges.
+// Every thread computes the same plan; rank_b[r] is the sequence of rank r.
+struct PairPlan {
+  bool ok;
+  int items;
+};
+
+template <int NWV>
+__device__ PairPlan pair_plan(const int64_t* spre, int B, int SPB, int64_t T, int W, int tid, int64_t* red,
+                              int16_t* rank_b, uint32_t* keys) {
+  constexpr int NT = NWV * 64;
+  static_assert(NT >= kPairedMaxBatch, "one thread per sequence");
+  PairPlan r{false, 0};
+  if (B > kPairedMaxBatch) return r;
+  const int B4 = (B + 3) & ~3;
+  // Key of sequence i: groups per segment above its index (0xFFFFFFFF: empty).
+  if (tid < B4) {
+    uint32_t k = 0xFFFFFFFFu;
+    if (tid < B) {
+      const int64_t g = (spre[tid + 1] - spre[tid]) / SPB;
+      if (g > 0) k = ((uint32_t)g << 8) | (uint32_t)tid;
+    }
+    keys[tid] = k;
+  }
+  __syncthreads();
+  int nonempty = 0;
+  if (tid < B) {
+    const uint32_t mk = keys[tid];
+    if (mk != 0xFFFFFFFFu) {
+      int rank = 0;
+      for (int j = 0; j < B4; j += 4) {
+        const uint4 k4 = *reinterpret_cast<const uint4*>(keys + j);
+        rank += (int)(k4.x < mk) + (int)(k4.y < mk) + (int)(k4.z < mk) + (int)(k4.w < mk);
+      }
+      rank_b[rank] = (int16_t)tid;
+      nonempty = 1;
+    }
+  }
+  const int N = __syncthreads_count(nonempty) * SPB;
+  const int E = N - W;
+  r.items = N;
+  if (E > W) return r;
+  auto nb_of = [&](int item) -> int64_t {
+    const int bb = rank_b[item / SPB];
+    return (spre[bb + 1] - spre[bb]) / SPB;
+  };
+  int64_t m = (tid == 0 && N > 0) ? nb_of(N - 1) : 0;
+  for (int g = tid; g < E; g += NT) m = max(m, nb_of(g) + nb_of(2 * E - 1 - g));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (int64_t)__shfl_xor(m, off));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  int64_t M = 0;
+#pragma unroll
+  for (int v = 0; v < NWV; ++v) M = max(M, red[v]);
+  r.ok = 5 * M * W <= 8 * T;
+  __syncthreads();  // red and keys are reused
+  return r;
+}
+
 // VK > 1 pairs KV heads whose rows share 128-byte lines: the kernel runs on
 // "wide" heads of D = VK * DR dims (VK adjacent real heads, the parameters'
 // hkv and group counting wide heads), each query row zero-padded outside its
@@ -224,6 +292,7 @@ balanced_kernel(const BalancedParams p) {
   constexpr int VT_BYTES = LDSP ? NWV * kLfWaveB : NWV * C::WT * 2;  // wave-private tiles or LDS stages
   constexpr int MERGE_BYTES = NWV * 16 * (2 + C::OW_STRIDE) * 4 + 16 * (NWV + 4) * 4;  // combine staging
   constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
+  static_assert(SMEM >= kPairedMaxBatch * 4, "paired-mode keys");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ int64_t spre[kBalancedMaxBatch + 1];  // spre[b] = groups of all segments of sequences < b
   __shared__ int64_t stot[NWV];
@@ -231,6 +300,7 @@ balanced_kernel(const BalancedParams p) {
   __shared__ int64_t s_rows[kHeadsPerGroup];       // row indices of the current piece's packed rows
   __shared__ int64_t s_orow[kHeadsPerGroup];       // their out offsets
   __shared__ int s_slice[kHeadsPerGroup];          // paired heads: the row's head within its wide head
+  __shared__ int16_t s_rank_b[kPairedMaxBatch];    // paired mode: the non-empty sequences by length rank
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -300,14 +370,54 @@ balanced_kernel(const BalancedParams p) {
           p.lse[(int64_t)bb * rows_seq + i] = SINKS ? p.sinks[i % p.hq] : -INFINITY;
     }
   }
-  if (w >= nwe) return;  // the whole workgroup leaves together
+  // Paired whole items (p.paired): each workgroup takes one or two whole
+  // segments, chosen from the lengths, or the ranges below when that choice
+  // would leave a workgroup too much work.
+  int pi_n = 0;              // segments this workgroup takes in paired mode (0: ranges)
+  int pi_b[2] = {0, 0}, pi_s[2] = {0, 0};
+  bool paired = false;
+  if (p.paired) {
+    const PairPlan pl = pair_plan<NWV>(spre, B, SPB, T, p.num_workers, tid, stot, s_rank_b,
+                                       reinterpret_cast<uint32_t*>(smem));
+    paired = pl.ok;
+    if (paired) {
+      const int wi = blockIdx.x;
+      // Items by rank, ascending in length: with E = N - W > 0 extra items,
+      // workgroup g < E takes items g and 2E - 1 - g (the 2E shortest, folded
+      // so that each pair's lengths add up to about the same), every other
+      // workgroup one item of the N - 2E longest.
+      const int E = pl.items - p.num_workers;
+      int it0 = -1, it1 = -1;
+      if (E <= 0) {
+        if (wi < pl.items) it0 = wi;
+      } else if (wi < E) {
+        it0 = 2 * E - 1 - wi;
+        it1 = wi;
+      } else {
+        it0 = wi + E;
+      }
+      if (it0 >= 0) {
+        pi_n = it1 >= 0 ? 2 : 1;
+        pi_b[0] = s_rank_b[it0 / SPB];
+        pi_s[0] = it0 % SPB;
+        if (it1 >= 0) {
+          pi_b[1] = s_rank_b[it1 / SPB];
+          pi_s[1] = it1 % SPB;
+        }
+      }
+    }
+  }
+  if (paired ? pi_n == 0 : w >= nwe) return;  // the whole workgroup leaves together
 
-  int64_t pos = w * T / nwe;
-  const int64_t hi = (w + 1) * T / nwe;
+  int64_t pos = paired ? 0 : w * T / nwe;
+  const int64_t hi = paired ? 0 : (w + 1) * T / nwe;
+  int pi = 0;  // paired mode: index of the current item
 
   // The sequence holding group pos: spre[b] <= pos < spre[b + 1].
   int b = 0;
-  {
+  if (paired) {
+    b = pi_b[0];
+  } else {
     int lo_b = 0, hi_b = B;
     while (hi_b - lo_b > 1) {
       const int mid = (lo_b + hi_b) >> 1;
@@ -316,8 +426,8 @@ balanced_kernel(const BalancedParams p) {
     b = lo_b;
   }
   int64_t nb = (spre[b + 1] - spre[b]) / SPB;  // groups per segment of sequence b
-  int seg = (int)((pos - spre[b]) / nb);
-  int grp = (int)((pos - spre[b]) - (int64_t)seg * nb);
+  int seg = paired ? pi_s[0] : (int)((pos - spre[b]) / nb);
+  int grp = paired ? 0 : (int)((pos - spre[b]) - (int64_t)seg * nb);
 
   WaveAttn<D, FP8> A;
   A.init_lane(tid & 63);
@@ -343,8 +453,8 @@ balanced_kernel(const BalancedParams p) {
   int lo = first_of(b);
   int window = load_window(b, (lo + grp * 16) / ps);
 
-  while (pos < hi) {
-    const int gend = (int)min(nb, (int64_t)grp + (hi - pos));
+  for (;;) {
+    const int gend = paired ? (int)nb : (int)min(nb, (int64_t)grp + (hi - pos));
     const int L = p.seq_lens[b];
     const int s0 = lo + grp * 16;
     const int s1 = min(lo + gend * 16, L);
@@ -362,15 +472,24 @@ balanced_kernel(const BalancedParams p) {
     }
     const int64_t head_off = (int64_t)kvh * Geo::head_stride(p);
 
-    // The next piece: the following segment (of this or a later sequence).
+    // The next piece: the following segment (of this or a later sequence), or
+    // in paired mode this workgroup's second item.
     const int64_t npos = pos + (gend - grp);
     int nseg = seg + 1, nbq = b;
-    if (nseg == SPB) {
-      nseg = 0;
-      do { ++nbq; } while (nbq < B && spre[nbq + 1] == spre[nbq]);
+    bool more;
+    if (paired) {
+      more = pi + 1 < pi_n;
+      nbq = more ? pi_b[1] : B;
+      nseg = more ? pi_s[1] : 0;
+    } else {
+      if (nseg == SPB) {
+        nseg = 0;
+        do { ++nbq; } while (nbq < B && spre[nbq + 1] == spre[nbq]);
+      }
+      more = npos < hi;
     }
-    const int nlo = npos < hi ? (nbq == b ? lo : first_of(nbq)) : 0;
-    const int next_window = npos < hi ? load_window(nbq, nlo / ps) : 0;
+    const int nlo = more ? (nbq == b ? lo : first_of(nbq)) : 0;
+    const int next_window = more ? load_window(nbq, nlo / ps) : 0;
 
     A.template load_q<VK>(p.q + lr.qoff, lr.valid, slice);
     A.qk_scale = p.qk_scale_log2;
@@ -405,7 +524,7 @@ balanced_kernel(const BalancedParams p) {
     const int64_t sidx = (int64_t)b * SPB + seg;
     const int64_t seg_pos = spre[b] + (int64_t)seg * nb;
     const int64_t w_first = ((seg_pos + 1) * nwe - 1) / T;
-    const int npieces = (int)(((seg_pos + nb) * nwe - 1) / T - w_first + 1);
+    const int npieces = paired ? 1 : (int)(((seg_pos + nb) * nwe - 1) / T - w_first + 1);
     // Row hh's V scale, and whether dims d0.. of the wide row are its own head's
     // (always, without pairing); own_dim gives their place in the real row.
     const float vsc = FP8 ? p.v_scale[kvh * VK] : 1.0f;
@@ -534,13 +653,15 @@ balanced_kernel(const BalancedParams p) {
       }
       __syncthreads();  // the LDS is reused by the next piece
     }
+    if (!more) break;
     pos = npos;
+    ++pi;
     grp = 0;
     seg = nseg;
     if (nbq != b) {
       b = nbq;
       lo = nlo;
-      if (b < B) nb = (spre[b + 1] - spre[b]) / SPB;
+      nb = (spre[b + 1] - spre[b]) / SPB;
     }
     window = next_window;
   }

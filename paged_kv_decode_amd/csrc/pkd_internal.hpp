@@ -94,6 +94,9 @@ struct BalancedParams {
   int32_t xcd_ranges;          // give each XCD a contiguous part of the work space (heads sharing cache lines)
   int32_t pair_heads;          // 1, or 2: hkv / group / head dims count wide heads of two real KV heads
                                // (q / out rows, partials and scales stay per real head)
+  int32_t paired;              // 1 (with fused): one or two whole segments per workgroup, paired by
+                               // length rank on the device, when that balances well enough (else the
+                               // equal ranges); batch <= kPairedMaxBatch
 };
 
 // True when the balanced mode merges inside the partition kernel: when there
@@ -162,6 +165,7 @@ constexpr int kWaves = 4;            // waves per split-kernel workgroup
 constexpr int kSplitAlign = 64;      // tokens; split boundaries are multiples of this
 constexpr int kHeadsPerGroup = 16;   // query heads packed into one MFMA N dimension
 constexpr int kBalancedMaxBatch = 1024;  // largest batch the balanced kernel's prefix scan takes
+constexpr int kPairedMaxBatch = 256;     // largest batch of the balanced kernel's paired mode
 constexpr int kXcds = 8;                 // accelerator complex dies of an MI355X (gfx950), each with its own L2
 
 // Launchers (defined in the .hip files).  head_dim in {32, 64, 128, 256}.

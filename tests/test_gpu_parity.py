@@ -19,6 +19,7 @@ from paged_kv_decode_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 BAL = -1000  # PKD_SPLITS_BALANCED
+PAIR = -1001  # PKD_SPLITS_PAIRED
 OUT_ATOL = 1e-2
 OUT_RTOL = 1e-2
 LSE_ATOL = 1e-3
@@ -422,6 +423,68 @@ def test_balanced_largest_batch(B):
     check(*run(B, w, BAL), *ref, what="balanced B=1024")
 
 
+# ---- whole items paired by length (PKD_SPLITS_PAIRED) ------------------------
+
+def _paired_cases(cus):
+    """(name, batch, Hq, Hkv, D, ps, lens, dtype, extra) around one and two items
+    per compute unit: folded pairs, one item each, the equal-length and the
+    more-than-two-per-unit fallbacks to the equal ranges, empty sequences."""
+    b1 = cus // 8  # sequences with 8 KV heads that give one item per unit
+    ragged = lambda n, lo, hi, seed: [int(x) for x in
+                                      np.random.default_rng(seed).integers(lo, hi + 1, size=n)]
+    return [
+        ("pairs", b1 + 3, 32, 8, 128, 64, ragged(b1 + 3, 1, 900, 1), "bf16", {}),
+        ("pairs_all", 2 * b1, 32, 8, 128, 64, ragged(2 * b1, 1, 700, 2), "bf16", {}),
+        ("one_each", b1 - 5, 32, 8, 128, 64, ragged(b1 - 5, 1, 700, 3), "bf16", {}),
+        ("equal_fallback", b1 + 1, 32, 8, 128, 64, [320] * (b1 + 1), "bf16", {}),
+        ("over_two", 2 * b1 + 3, 16, 8, 64, 16, ragged(2 * b1 + 3, 1, 300, 4), "bf16", {}),
+        ("empties", b1 + 6, 32, 8, 128, 64, [0, 0] + ragged(b1 + 4, 1, 600, 5), "bf16", {}),
+        ("fp8", b1 + 9, 64, 8, 128, 64, ragged(b1 + 9, 1, 900, 6), "fp8_e4m3", {}),
+        ("d32_wide_heads", b1 + 2, 16, 8, 32, 64, ragged(b1 + 2, 1, 800, 7), "bf16", {}),
+        ("d256", b1 + 1, 16, 8, 256, 16, ragged(b1 + 1, 1, 300, 8), "bf16", {}),
+        ("window_sinks", b1 + 4, 32, 8, 128, 64, ragged(b1 + 4, 1, 900, 9), "bf16",
+         dict(window=200, sinks=True)),
+        ("verify_causal", b1 + 2, 16, 8, 64, 64, ragged(b1 + 2, 4, 700, 10), "bf16",
+         dict(q_len=3, causal=True)),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(11))
+def test_paired_mode(B, idx):
+    """PKD_SPLITS_PAIRED against the oracle, in every branch of the device's
+    plan (folded pairs, one item each, fallbacks to the equal ranges), with
+    empty sequences, FP8, paired KV heads, windows, sinks and several query
+    tokens; one launch, and its path query names it."""
+    name, bq, hq, hkv, d, ps, lens, dtype, extra = _paired_cases(_cu_count())[idx]
+    w = wl.custom_workload(bq, hq, hkv, d, ps, lens, dtype, seed=500 + idx, **extra)
+    ref = oracle_full(w)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    ext = B.ext_for(t["q"], w.spec.causal, w.spec.window)
+    assert B.paged_decode_path(dims, ext, PAIR) == B.PKD_PATH_PAIRED
+    assert B.paged_decode_launches(dims, ext, PAIR) == 1
+    out, lse = run(B, w, PAIR, t)
+    check(out, lse, *ref, what=f"paired {name}")
+    # a second call on the same workspace contents gives the same bits
+    out2, lse2 = run(B, w, PAIR, t)
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16)) and torch.equal(lse2, lse)
+
+
+def test_paired_mode_rejected_by_two_phases(B):
+    """The two-phase entries take no paired mode: PKD_ERR_NUM_SPLITS, nothing written."""
+    w = wl.custom_workload(4, 8, 2, 64, 16, [30, 1, 0, 90], "bf16", seed=31)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    nbytes = B.paged_decode_workspace_bytes_ext(dims, None, PAIR)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    h = B.current_stream_handle(0)
+    assert B.paged_decode_partition(dims, None, t["q"], t["k"], t["v"], t["bt"], t["lens"], None, None, w.scale,
+                                    PAIR, ws, nbytes, h) == B.PKD_ERR_NUM_SPLITS
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+
+
 # ---- full-size workloads: every output element against the oracle -----------
 
 FULL = ["llama_b32_d128_ps64", "batch128_d128_ps128", "longctx_b1_d32", "longctx_b1_d64",
@@ -432,8 +495,8 @@ FULL = ["llama_b32_d128_ps64", "batch128_d128_ps128", "longctx_b1_d32", "longctx
 def full_modes(spec):
     """The launch configurations a full-size workload is checked in: the
     library's own choice (the one the benchmark times), direct output, a fixed
-    split count, and the balanced and packed schedules where they apply."""
-    return [0, 1, 8, BAL]
+    split count, the balanced partition and whole items paired by length."""
+    return [0, 1, 8, BAL, PAIR]
 
 
 @pytest.mark.parametrize("name", FULL)
