@@ -288,6 +288,14 @@ int32_t paged_decode_finish(const pkd_dims* dims, const pkd_ext* ext, int32_t nu
  *  - else 1 when no sequence can show more than 256 tokens
  *    (max_pages_per_seq * page_size, or with a window window + q_len + 14,
  *    whichever is smaller);
+ *  - else, for more items than compute units and at most twice as many: 1 for
+ *    a BF16 paged cache with head_dim 128, q_len 1, no window, G <= 16,
+ *    page_size % 16 == 0, max_pages_per_seq <= 512, batch <= PKD_PAIRED_MAX_BATCH
+ *    and max_pages_per_seq * page_size < 2^23 (direct output, whole items paired
+ *    by length on the device: see paged_decode_path), else PKD_SPLITS_PAIRED
+ *    wherever it applies.  Whole items in pairs measured faster than the equal
+ *    cuts for ragged lengths; when every length is equal, pairs cost up to
+ *    twice an item's time on some units and PKD_SPLITS_BALANCED is faster;
  *  - else PKD_SPLITS_BALANCED wherever it applies;
  *  - else 1 when the items alone fill the device's compute units, else a split
  *    count in [2, PKD_MAX_SPLITS] bounded by the longest sequence expected,
@@ -319,7 +327,12 @@ int32_t paged_decode_launches(const pkd_dims* dims, const pkd_ext* ext, int32_t 
  *                            wave (the same arithmetic and the same bits), taken for a BF16
  *                            paged cache with head_dim 128, q_len 1, no window, G <= 16,
  *                            page_size a multiple of 16, max_pages_per_seq <= 512, and
- *                            batch * num_kv_heads at most the current device's compute units;
+ *                            batch * num_kv_heads at most the current device's compute units
+ *                            (one workgroup per item), or at most twice that with
+ *                            batch <= PKD_PAIRED_MAX_BATCH and max_pages_per_seq * page_size
+ *                            < 2^23 (one workgroup per compute unit, each taking one or two
+ *                            whole items paired by length rank on the device, as in
+ *                            PKD_SPLITS_PAIRED but never falling back);
  *   PKD_PATH_SPLITS          split-KV partials, then the merge kernel;
  *   PKD_PATH_BALANCED        the balanced partition, merging in place;
  *   PKD_PATH_BALANCED_MERGE  the balanced partition, then the merge kernel;

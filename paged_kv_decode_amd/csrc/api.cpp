@@ -218,6 +218,8 @@ int32_t split_chunk(const Dims& d, int S) {
   return (int32_t)(c < INT32_MAX ? c : INT32_MAX);
 }
 
+bool lds_direct_ok(const Dims& d, bool strided);
+
 // The split mode for PKD_SPLITS_AUTO.
 //  - Direct output (one split) when a bf16 cache whose head rows are at least
 //    128 bytes has between three quarters of one and one (sequence, KV head,
@@ -234,16 +236,26 @@ int32_t split_chunk(const Dims& d, int S) {
 //    groups, which one workgroup streams in about the time the balanced
 //    partition takes to spread it and launch its merge (the two-sequence,
 //    112-token case: 8.5 against 16.4 us).
+//  - Between one and two items per compute unit: direct output in the
+//    LDS-staged kernel's pairs form where it applies (bf16, head_dim 128, one
+//    query token, no window, paged), else the paired mode where it applies;
+//    both keep whole items, the longest alone and the shortest in pairs, which
+//    measured faster than the balanced partition's equal cuts for lengths
+//    1024-4096 (bf16, 8 KV heads, B = 33-64) and 512-8192 (FP8, B = 40-64).
 //  - Otherwise the balanced partition wherever it applies (it balances any
 //    length mix and pays each workgroup's start-up once).
 //  - Otherwise direct output when the items alone fill the device, else
 //    enough splits to fill it, bounded by the longest sequence.
-int32_t heuristic_splits(const Dims& d, int32_t max_len) {
+int32_t heuristic_splits(const Dims& d, int32_t max_len, bool strided) {
   const int cus = current_cu_count();
   const int64_t items = (int64_t)d.batch * d.num_kv_heads * head_groups(d);
   if (d.kv_dtype == PKD_DTYPE_BF16 && d.head_dim >= 64 && cus > 0 && items <= cus && 4 * items >= 3LL * cus)
     return 1;
   if (visible_span(d) <= 256) return 1;
+  if (cus > 0 && items > cus && items <= 2LL * cus) {
+    if (lds_direct_ok(d, strided)) return 1;
+    if (paired_ok(d)) return PKD_SPLITS_PAIRED;
+  }
   if (balanced_ok(d)) return PKD_SPLITS_BALANCED;
   const int64_t target = 4LL * (cus > 0 ? cus : 256);  // workgroups to keep every CU busy
   if (items <= 0 || items >= target) return 1;
@@ -337,14 +349,30 @@ int32_t check_out_ws(const void* out, const float* lse, const void* ws) {
 
 // Direct output with K/V tiles loaded straight into LDS stages, where that
 // kernel applies and the (sequence, KV head) items fit in one round of
-// workgroups.  It gives the grid kernel's bits; measured back to back it was
-// about 0.7% faster at B = 32 (256 items on 256 units; ahead in five of six
-// comparisons) and 1-1.5% slower at B = 128 (1024 items, four rounds).
-bool use_lds_direct(const Dims& d, const Layout& lay) {
+// workgroups, or in the pairs form (lds_pairs_workers) in two.  It gives the
+// grid kernel's bits; measured back to back it was about 0.7% faster at
+// B = 32 (256 items on 256 units; ahead in five of six comparisons) and
+// 1-1.5% slower at B = 128 (1024 items, four rounds).
+bool lds_direct_ok(const Dims& d, bool strided) {
   const int cus = current_cu_count();
-  return pkd::lds_direct_applies(d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, d.q_len, d.window,
-                                 d.num_q_heads / d.num_kv_heads, d.page_size, d.max_pages_per_seq, lay.strided) &&
-         cus > 0 && (int64_t)d.batch * d.num_kv_heads <= cus;
+  if (!pkd::lds_direct_applies(d.head_dim, d.kv_dtype == PKD_DTYPE_FP8_E4M3, d.q_len, d.window,
+                               d.num_q_heads / d.num_kv_heads, d.page_size, d.max_pages_per_seq, strided) ||
+      cus <= 0)
+    return false;
+  const int64_t items = (int64_t)d.batch * d.num_kv_heads;
+  if (items <= cus) return true;
+  return items <= 2LL * cus && d.batch <= pkd::kPairedMaxBatch &&
+         (int64_t)d.max_pages_per_seq * d.page_size < ((int64_t)1 << 23);
+}
+
+bool use_lds_direct(const Dims& d, const Layout& lay) { return lds_direct_ok(d, lay.strided); }
+
+// Workgroups of the LDS-staged direct kernel's pairs form (one or two whole
+// items each, paired by length on the device) when the items exceed the
+// compute units, else 0 (one workgroup per item).  Only where use_lds_direct.
+int lds_pairs_workers(const Dims& d) {
+  const int cus = current_cu_count();
+  return (int64_t)d.batch * d.num_kv_heads > cus ? cus : 0;
 }
 
 int32_t launch_partition(const Dims& d, const pkd::SplitParams& p, bool direct, hipStream_t s) {
@@ -359,12 +387,12 @@ int32_t launch_partition(const Dims& d, const pkd::SplitParams& p, bool direct, 
 // (PKD_SPLITS_AUTO: of the heuristic's choice); 0 for an unsupported mode.
 int32_t num_splits_of(const Dims& d, int32_t max_seq_len_hint) {
   const int32_t max_len = max_seq_len_hint > 0 ? max_seq_len_hint : d.max_pages_per_seq * d.page_size;
-  return heuristic_splits(d, max_len);
+  return heuristic_splits(d, max_len, false);
 }
 
 size_t workspace_of(const Dims& d, int32_t num_splits) {
   int S = num_splits;
-  if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size);
+  if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size, false);
   if (S == PKD_SPLITS_BALANCED)
     return balanced_ok(d) ? balanced_bytes(d, pair_heads(d, false), nullptr, nullptr, nullptr) : 0;
   if (S == PKD_SPLITS_PAIRED)
@@ -459,7 +487,7 @@ struct Plan {
 
 int32_t make_plan(const Dims& d, int32_t num_splits, bool strided, Plan* pl) {
   int S = num_splits;
-  if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size);
+  if (S == PKD_SPLITS_AUTO) S = heuristic_splits(d, d.max_pages_per_seq * d.page_size, strided);
   pl->S = S;
   pl->paired = S == PKD_SPLITS_PAIRED;
   pl->balanced = S == PKD_SPLITS_BALANCED || pl->paired;
@@ -577,7 +605,8 @@ int32_t decode_checked(const Dims& d, const Layout& lay, const void* q, const vo
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
     p.sinks = sinks;
-    if (use_lds_direct(d, lay)) return pkd::launch_lds_direct(p, d.batch, s) == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
+    if (use_lds_direct(d, lay))
+      return pkd::launch_lds_direct(p, d.batch, lds_pairs_workers(d), s) == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
     return launch_partition(d, p, true, s);
   }
   if (pl.balanced && (pl.paired || balanced_fused(d, pl.pair))) {

@@ -27,62 +27,123 @@ constexpr int kLdsBytes = kBtOff + kBtEntries * 4;
 // The workgroup combine's staging (per-wave rows and weights) reuses the stages.
 static_assert(kLW * 16 * (2 + Cfg<kLpD, false>::OW_STRIDE) * 4 + 16 * (kLW + 4) * 4 <= kBtOff, "combine staging");
 
+// Items (sequence, KV head) of one launch, in the pairs form: with N = B * Hkv
+// items on W workgroups (W < N <= 2W), the sequences are ranked by length
+// (ties by index), items by their sequence's rank; workgroup g < E = N - W
+// takes items 2E - 1 - g and g (the 2E shortest, folded so that the pairs'
+// lengths come out about even), every other workgroup the one item g + E.
+// The longest items thus run alone, and the pairs finish inside the time of
+// the longest item unless the shortest are nearly as long as it.  Every
+// workgroup computes the same ranking; keys are staged in LDS (kb, B + 3
+// words) and rank_b[r] receives the sequence of rank r.
+__device__ void lds_pair_items(const SplitParams& p, int batch, int tid, uint32_t* kb, int16_t* rank_b,
+                               int (&items)[2]) {
+  const int B4 = (batch + 3) & ~3;
+  if (tid < B4) {
+    // Lengths are clamped to [0, 2^23) (the host admits no larger capacity), so
+    // keys are distinct and below 2^31 and the ranks a permutation.
+    const int L = tid < batch ? min(max(p.seq_lens[tid], 0), (1 << 23) - 1) : 0;
+    kb[tid] = tid < batch ? ((uint32_t)L << 8) | (uint32_t)tid : 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  if (tid < batch) {
+    const uint32_t mk = kb[tid];
+    int rank = 0;
+    for (int j = 0; j < B4; j += 4) {
+      const uint4 k4 = *reinterpret_cast<const uint4*>(kb + j);
+      rank += (int)(k4.x < mk) + (int)(k4.y < mk) + (int)(k4.z < mk) + (int)(k4.w < mk);
+    }
+    rank_b[rank] = (int16_t)tid;
+  }
+  __syncthreads();
+  const int N = batch * p.hkv;
+  const int E = N - (int)gridDim.x;
+  const int g = blockIdx.x;
+  items[0] = g < E ? 2 * E - 1 - g : g + (E > 0 ? E : 0);
+  items[1] = g < E ? g : -1;
+  if (items[0] >= N) items[0] = -1;
+}
+
 // Two waves per SIMD as the register budget (as the grid kernel): the
 // accumulators then stay in ordinary VGPRs, where the rescale reaches them.
+// PAIRS = false: grid (Hkv, B), one item per workgroup.  PAIRS = true: a 1D
+// grid of W workgroups taking the items as lds_pair_items deals them (batch
+// <= kPairedMaxBatch).
+template <bool PAIRS>
 __global__ void __launch_bounds__(kLW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-lds_direct_kernel(const SplitParams p) {
+lds_direct_kernel(const SplitParams p, int batch) {
   typedef WaveAttn<kLpD, false> WA;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+  __shared__ int64_t s_rows[kHeadsPerGroup];
+  __shared__ int64_t s_orow[kHeadsPerGroup];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kvh = blockIdx.x;
-  const int b = blockIdx.y;
-  WA A;
-  A.init_lane(lane);
-
-  // Issued while the length is in flight: the block-table row (every entry of
-  // the sequence's row) and the query rows (q_len * G packed rows, 16 at most).
+  int items[2] = {-1, -1};
+  if constexpr (PAIRS) {
+    // Keys in the stages (unused until the first tile), ranks after them.
+    __shared__ int16_t rank_b[kPairedMaxBatch];
+    lds_pair_items(p, batch, tid, reinterpret_cast<uint32_t*>(smem), rank_b, items);
+    for (int k = 0; k < 2; ++k)
+      if (items[k] >= 0) items[k] = rank_b[items[k] / p.hkv] * p.hkv + items[k] % p.hkv;  // b * Hkv + kvh
+    __syncthreads();  // the keys' LDS is the stages'
+  } else {
+    items[0] = blockIdx.y * p.hkv + blockIdx.x;
+  }
   int32_t* sbt = reinterpret_cast<int32_t*>(smem + kBtOff);
-  for (int i = tid; i < p.max_pages; i += kLW * 64) sbt[i] = p.block_table[(int64_t)b * p.max_pages + i];
-  {
-    const LaneRow lq = lane_row<kLpD, false>(p, b, kvh, 0, A.n, 0, 0, 0);
-    A.load_q(p.q + lq.qoff, lq.valid);
-  }
-  A.qk_scale = p.qk_scale_log2;
-  A.reset();
-  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);  // uniform: tile bookkeeping stays scalar
-  const LaneRow lr = lane_row<kLpD, false>(p, b, kvh, 0, A.n, L, L, 0);
-  __shared__ int64_t s_rows[kHeadsPerGroup];
-  __shared__ int64_t s_orow[kHeadsPerGroup];
-  if (tid < kHeadsPerGroup) {
-    s_rows[tid] = lr.row;
-    s_orow[tid] = lr.ooff;
-  }
-  __syncthreads();
 
-  const int ntiles = (L + kLpTT - 1) / kLpTT;
-  const int ps = p.page_size;
-  const int64_t head_off = (int64_t)kvh * kLpRowB;
-  LdsPipe P;
-  P.init(smem, wave * kLpWaveB, A, lane, p.kv.tok_stride);
-  // Tiles wave, wave + kLW, ...; the byte offset of token tb's row of KV head kvh.
-  P.run(A, wave, kLW, ntiles, 0, L, lr.end, lr.end_min, p.k, p.v, [&](int tb) -> int64_t {
-    const int page = __builtin_amdgcn_readfirstlane(sbt[tb / ps]);
-    return (int64_t)page * p.kv.page_stride + (int64_t)(tb % ps) * p.kv.tok_stride + head_off;
-  });
-  // every load has landed: the combine below reuses the stages
+  for (int k = 0; k < 2; ++k) {
+    const int item = items[k];
+    if (item < 0) break;
+    const int b = item / p.hkv;
+    const int kvh = item - b * p.hkv;
+    WA A;
+    A.init_lane(lane);
 
-  auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
-    *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + d0) = to_bf16x4(o);
-    if (d0 == 0 && p.lse) p.lse[s_rows[hh]] = lse_nat;
-  };
-  if (p.sinks)
-    wg_combine<kLpD, false, kLW>(A, smem, wave, tid, p.rows_kv, 1.0f, store,
-                                 [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
-  else
-    wg_combine<kLpD, false, kLW>(A, smem, wave, tid, p.rows_kv, 1.0f, store, NoSink());
+    // Issued while the length is in flight: the block-table row (every entry of
+    // the sequence's row) and the query rows (q_len * G packed rows, 16 at most).
+    for (int i = tid; i < p.max_pages; i += kLW * 64) sbt[i] = p.block_table[(int64_t)b * p.max_pages + i];
+    {
+      const LaneRow lq = lane_row<kLpD, false>(p, b, kvh, 0, A.n, 0, 0, 0);
+      A.load_q(p.q + lq.qoff, lq.valid);
+    }
+    A.qk_scale = p.qk_scale_log2;
+    A.reset();
+    const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);  // uniform: tile bookkeeping stays scalar
+    const LaneRow lr = lane_row<kLpD, false>(p, b, kvh, 0, A.n, L, L, 0);
+    if (tid < kHeadsPerGroup) {
+      s_rows[tid] = lr.row;
+      s_orow[tid] = lr.ooff;
+    }
+    __syncthreads();
+
+    const int ntiles = (L + kLpTT - 1) / kLpTT;
+    const int ps = p.page_size;
+    const int64_t head_off = (int64_t)kvh * kLpRowB;
+    LdsPipe P;
+    P.init(smem, wave * kLpWaveB, A, lane, p.kv.tok_stride);
+    // Tiles wave, wave + kLW, ...; the byte offset of token tb's row of KV head
+    // kvh.  (Output stores of a previous item may still be outstanding; they
+    // only make the pipeline's load-count waits stricter.)
+    P.run(A, wave, kLW, ntiles, 0, L, lr.end, lr.end_min, p.k, p.v, [&](int tb) -> int64_t {
+      const int page = __builtin_amdgcn_readfirstlane(sbt[tb / ps]);
+      return (int64_t)page * p.kv.page_stride + (int64_t)(tb % ps) * p.kv.tok_stride + head_off;
+    });
+    // every load has landed: the combine below reuses the stages
+
+    auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
+      *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + d0) = to_bf16x4(o);
+      if (d0 == 0 && p.lse) p.lse[s_rows[hh]] = lse_nat;
+    };
+    if (p.sinks)
+      wg_combine<kLpD, false, kLW>(A, smem, wave, tid, p.rows_kv, 1.0f, store,
+                                   [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
+    else
+      wg_combine<kLpD, false, kLW>(A, smem, wave, tid, p.rows_kv, 1.0f, store, NoSink());
+    if (!PAIRS) break;
+    __syncthreads();  // the stages, the staged block table and s_rows are reused by the next item
+  }
 }
 
 }  // namespace
@@ -93,8 +154,11 @@ bool lds_direct_applies(int head_dim, bool fp8, int q_len, int window, int group
          page_size % 16 == 0 && max_pages >= 1 && max_pages <= kBtEntries && !strided;
 }
 
-hipError_t launch_lds_direct(const SplitParams& p, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL(lds_direct_kernel, dim3(p.hkv, batch), dim3(kLW * 64), 0, stream, p);
+hipError_t launch_lds_direct(const SplitParams& p, int batch, int workers, hipStream_t stream) {
+  if (workers > 0)
+    hipLaunchKernelGGL(lds_direct_kernel<true>, dim3(workers), dim3(kLW * 64), 0, stream, p, batch);
+  else
+    hipLaunchKernelGGL(lds_direct_kernel<false>, dim3(p.hkv, batch), dim3(kLW * 64), 0, stream, p, batch);
   return hipGetLastError();
 }
 
@@ -144,7 +208,7 @@ int32_t pkd_decode_lds(const pkd_dims* dims, const void* q, const void* k_cache,
   p.kv.head_stride = 256;
   p.kv.tok_stride = d.num_kv_heads * 256;
   p.kv.page_stride = (int64_t)d.page_size * p.kv.tok_stride;
-  return pkd::launch_lds_direct(p, d.batch, static_cast<hipStream_t>(stream)) == hipSuccess ? PKD_OK
+  return pkd::launch_lds_direct(p, d.batch, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? PKD_OK
                                                                                             : PKD_ERR_LAUNCH;
 }
 

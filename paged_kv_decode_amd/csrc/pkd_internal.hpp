@@ -188,6 +188,9 @@ hipError_t launch_check_tables(const int32_t* block_table, const int32_t* seq_le
 // (KV head, sequence); reads the direct-mode fields of p.
 bool lds_direct_applies(int head_dim, bool fp8, int q_len, int window, int group, int page_size, int max_pages,
                         bool strided);
-hipError_t launch_lds_direct(const SplitParams& p, int batch, hipStream_t stream);
+// workers = 0: one workgroup per (KV head, sequence); workers = W > 0: the
+// pairs form, W workgroups for B * Hkv items, W < B * Hkv <= 2W, B <= kPairedMaxBatch,
+// lengths below 2^23.
+hipError_t launch_lds_direct(const SplitParams& p, int batch, int workers, hipStream_t stream);
 
 }  // namespace pkd

@@ -546,21 +546,61 @@ def _cu_count():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-@pytest.mark.parametrize("hkv,d,dtype,expect", [(8, 128, "bf16", 1), (8, 64, "bf16", 1), (8, 32, "bf16", BAL),
-                                                 (8, 128, "fp8_e4m3", BAL)])
-def test_auto_mode_around_one_item_per_cu(B, hkv, d, dtype, expect):
+@pytest.mark.parametrize("hkv,d,dtype,expect,above", [(8, 128, "bf16", 1, 1), (8, 64, "bf16", 1, PAIR),
+                                                       (8, 32, "bf16", BAL, PAIR), (8, 128, "fp8_e4m3", BAL, PAIR)])
+def test_auto_mode_around_one_item_per_cu(B, hkv, d, dtype, expect, above):
     """PKD_SPLITS_AUTO picks direct output for a bf16 cache with head rows of at
     least 128 bytes when the (sequence, KV head, head group) items number between
     three quarters of the compute units and all of them (one whole item per unit,
-    nothing to merge), else the balanced partition."""
+    nothing to merge); above that, up to two items per unit, whole items paired
+    by length (the LDS-staged direct kernel's pairs form for bf16 D = 128, else
+    the paired mode); elsewhere the balanced partition."""
     cus = _cu_count()
     if cus % hkv:
         pytest.skip("compute units not a multiple of the KV heads")
     kvd = B.PKD_DTYPE_FP8_E4M3 if dtype == "fp8_e4m3" else B.PKD_DTYPE_BF16
     for batch, want in ((cus // hkv // 2, BAL), (3 * cus // 4 // hkv, expect), (cus // hkv - 1, expect),
-                        (cus // hkv, expect), (cus // hkv + 1, BAL)):
+                        (cus // hkv, expect), (cus // hkv + 1, above), (2 * cus // hkv, above),
+                        (2 * cus // hkv + 1, BAL)):
         dims = B.pkd_dims(batch, 4 * hkv, hkv, d, 64, 4096, 64, kvd)
         assert B.paged_decode_num_splits(dims, 0) == want, (batch, hkv, d, dtype)
+        if want == 1 and d == 128 and dtype == "bf16":
+            assert B.paged_decode_path(dims, None, 0) == B.PKD_PATH_DIRECT_LDS
+
+
+def _lds_pairs_cases(cus):
+    """(name, batch, Hq, Hkv, ps, lens, sinks) with between one and two (sequence,
+    KV head) items per compute unit, for the LDS-staged kernel's pairs form."""
+    b1 = cus // 8
+    ragged = lambda n, lo, hi, seed: [int(x) for x in
+                                      np.random.default_rng(seed).integers(lo, hi + 1, size=n)]
+    return [
+        ("ragged", b1 + 1, 32, 8, 64, ragged(b1 + 1, 1024, 4096, 11), False),
+        ("two_per_unit", 2 * b1, 32, 8, 64, ragged(2 * b1, 1, 3000, 12), False),
+        ("equal", b1 + 3, 32, 8, 64, [700] * (b1 + 3), False),
+        ("empty_and_short", b1 + 5, 32, 8, 16, [0, 1, 0, 15, 16, 17] + ragged(b1 - 1, 1, 900, 13), False),
+        ("sinks", b1 + 7, 32, 8, 64, ragged(b1 + 7, 1, 1500, 14), True),
+        ("hkv2_g16", cus // 2 + 9, 32, 2, 48, ragged(cus // 2 + 9, 1, 400, 15), False),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(6))
+def test_lds_pairs_direct(B, idx):
+    """Direct output for bf16 D = 128 with more items than compute units: the
+    LDS-staged kernel deals one or two whole items per workgroup, paired by
+    length on the device.  Against the oracle (NaN tails, -1 padding), and bit
+    for bit against the same kernel launched one workgroup per item."""
+    name, bq, hq, hkv, ps, lens, sinks = _lds_pairs_cases(_cu_count())[idx]
+    w = wl.custom_workload(bq, hq, hkv, 128, ps, lens, "bf16", seed=700 + idx, sinks=sinks)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    assert B.paged_decode_num_splits(dims, 0) == 1
+    assert B.paged_decode_path(dims, None, 1) == B.PKD_PATH_DIRECT_LDS
+    out, lse = run(B, w, 0, t)
+    check(out, lse, *oracle_full(w), what=f"lds pairs {name}")
+    if not sinks:
+        out1, lse1 = run_lds(B, w, t)
+        assert torch.equal(out.view(torch.int16), out1.view(torch.int16)) and torch.equal(lse, lse1)
 
 
 def test_two_phases_reject_auto_direct(B):
