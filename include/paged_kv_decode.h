@@ -289,7 +289,7 @@ int32_t paged_decode_finish(const pkd_dims* dims, const pkd_ext* ext, int32_t nu
  *    (max_pages_per_seq * page_size, or with a window window + q_len + 14,
  *    whichever is smaller);
  *  - else, for more items than compute units and at most twice as many: 1 for
- *    a BF16 paged cache with head_dim 128, q_len 1, no window, G <= 16,
+ *    a paged cache (BF16 or FP8) with head_dim 128, q_len 1, no window, G <= 16,
  *    page_size % 16 == 0, max_pages_per_seq <= 512, batch <= PKD_PAIRED_MAX_BATCH
  *    and max_pages_per_seq * page_size < 2^23 (direct output, whole items paired
  *    by length on the device: see paged_decode_path), else PKD_SPLITS_PAIRED
@@ -324,8 +324,10 @@ int32_t paged_decode_launches(const pkd_dims* dims, const pkd_ext* ext, int32_t 
  * tests that need the kernel by name.  Returns
  *   PKD_PATH_DIRECT          direct output, the next K/V tile's loads held in registers;
  *   PKD_PATH_DIRECT_LDS      direct output, K/V tiles loaded straight into two LDS stages per
- *                            wave (the same arithmetic and the same bits), taken for a BF16
- *                            paged cache with head_dim 128, q_len 1, no window, G <= 16,
+ *                            wave (the same arithmetic; the same bits for BF16, while FP8
+ *                            runs eight waves per workgroup whose grouping of the tiles
+ *                            rounds differently), taken for a paged cache with
+ *                            head_dim 128, q_len 1, no window, G <= 16,
  *                            page_size a multiple of 16, max_pages_per_seq <= 512, and
  *                            batch * num_kv_heads at most the current device's compute units
  *                            (one workgroup per item), or at most twice that with

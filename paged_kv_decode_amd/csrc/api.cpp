@@ -237,11 +237,13 @@ bool lds_direct_ok(const Dims& d, bool strided);
 //    partition takes to spread it and launch its merge (the two-sequence,
 //    112-token case: 8.5 against 16.4 us).
 //  - Between one and two items per compute unit: direct output in the
-//    LDS-staged kernel's pairs form where it applies (bf16, head_dim 128, one
-//    query token, no window, paged), else the paired mode where it applies;
-//    both keep whole items, the longest alone and the shortest in pairs, which
-//    measured faster than the balanced partition's equal cuts for lengths
-//    1024-4096 (bf16, 8 KV heads, B = 33-64) and 512-8192 (FP8, B = 40-64).
+//    LDS-staged kernel's pairs form where it applies (bf16 or FP8, head_dim
+//    128, one query token, no window, paged), else the paired mode where it
+//    applies; both keep whole items, the longest alone and the shortest in
+//    pairs, which measured faster than the balanced partition's equal cuts for
+//    lengths 1024-4096 (bf16, 8 KV heads, B = 33-64: 5.5-6.4 against 4.9-5.5
+//    TB/s) and 512-8192 (FP8, B = 40-64: 4.4-5.5 against 4.0-4.7 TB/s); the
+//    LDS-staged form led the paired mode by 2-7%.
 //  - Otherwise the balanced partition wherever it applies (it balances any
 //    length mix and pays each workgroup's start-up once).
 //  - Otherwise direct output when the items alone fill the device, else
@@ -349,8 +351,9 @@ int32_t check_out_ws(const void* out, const float* lse, const void* ws) {
 
 // Direct output with K/V tiles loaded straight into LDS stages, where that
 // kernel applies and the (sequence, KV head) items fit in one round of
-// workgroups, or in the pairs form (lds_pairs_workers) in two.  It gives the
-// grid kernel's bits; measured back to back it was about 0.7% faster at
+// workgroups, or in the pairs form (lds_pairs_workers) in two.  For bf16 it
+// gives the grid kernel's bits (FP8: the same arithmetic over eight waves,
+// rounding differently); measured back to back it was about 0.7% faster at
 // B = 32 (256 items on 256 units; ahead in five of six comparisons) and
 // 1-1.5% slower at B = 128 (1024 items, four rounds).
 bool lds_direct_ok(const Dims& d, bool strided) {
@@ -606,7 +609,9 @@ int32_t decode_checked(const Dims& d, const Layout& lay, const void* q, const vo
     p.lse = lse;
     p.sinks = sinks;
     if (use_lds_direct(d, lay))
-      return pkd::launch_lds_direct(p, d.batch, lds_pairs_workers(d), s) == hipSuccess ? PKD_OK : PKD_ERR_LAUNCH;
+      return pkd::launch_lds_direct(p, d.kv_dtype == PKD_DTYPE_FP8_E4M3, d.batch, lds_pairs_workers(d), s) ==
+                     hipSuccess
+                 ? PKD_OK : PKD_ERR_LAUNCH;
     return launch_partition(d, p, true, s);
   }
   if (pl.balanced && (pl.paired || balanced_fused(d, pl.pair))) {

@@ -1,13 +1,18 @@
-// Direct output (one workgroup of four waves per (KV head, sequence), out and
-// lse written directly) with the K/V tiles loaded straight into LDS stages by
-// the pipeline of lds_pipe.hpp, instead of being held in registers for one
-// tile as the grid kernel does.  paged_decode runs it for bf16 D = 128 decode
-// of one query token per sequence without a window (sinks or not) whose items
-// fit one round of workgroups; pkd_decode_lds exposes it for measurement beside
-// the grid kernel.  It also computes several query tokens under the causal mask
+// Direct output (out and lse written directly, nothing merged) with the K/V
+// tiles loaded straight into LDS stages by the pipelines of lds_pipe.hpp,
+// instead of being held in registers for one tile as the grid kernel does:
+// four waves per workgroup for a bf16 cache, eight for FP8 codes.  paged_decode
+// runs it for D = 128 decode of one query token per sequence without a window
+// (sinks or not) whose (sequence, KV head) items fit one round of workgroups
+// (one workgroup per item) or two (the pairs form: one workgroup per compute
+// unit, each taking one or two whole items paired by length on the device);
+// pkd_decode_lds exposes the bf16 one-per-item form for measurement beside the
+// grid kernel.  It also computes several query tokens under the causal mask
 // (q_len * G <= 16 rows, bit for bit the grid kernel's), but four tokens at
-// B = 32 ran 1% slower than the grid kernel, so paged_decode does not send them.  The arithmetic is the grid kernel's,
-// so the results equal paged_decode's with num_splits = 1 bit for bit.
+// B = 32 ran 1% slower than the grid kernel, so paged_decode does not send
+// them.  The arithmetic is the grid kernel's: bf16 results equal the grid
+// kernel's bit for bit; FP8 runs eight waves, whose grouping of the tiles in
+// the workgroup combine rounds differently from the grid kernel's four.
 #include "../../include/pkd_lds.h"
 
 #include <hip/hip_runtime.h>
@@ -20,12 +25,32 @@
 namespace pkd {
 namespace {
 
-constexpr int kLW = 4;                         // waves per workgroup
-constexpr int kBtOff = kLW * kLpWaveB;         // staged block-table entries after the stages
-constexpr int kBtEntries = 512;
-constexpr int kLdsBytes = kBtOff + kBtEntries * 4;
+constexpr int kBtEntries = 512;                // staged block-table entries (after the stages)
+
+// The two instances: bf16 K/V (16-token tiles, two stages of 8 KiB per wave,
+// four waves) and FP8 codes (32-token tiles, two stages of 8 KiB per wave,
+// eight waves, so that a compute unit keeps about as many bytes in flight).
+template <bool FP8>
+struct LdsDirect {
+  typedef LdsPipe Pipe;
+  static constexpr int NW = 4;          // waves per workgroup
+  static constexpr int WAVE_B = kLpWaveB;
+};
+template <>
+struct LdsDirect<true> {
+  typedef LdsPipeF8 Pipe;
+  static constexpr int NW = 8;
+  static constexpr int WAVE_B = kLfWaveB;
+};
+template <bool FP8>
+constexpr int lds_bt_offset() { return LdsDirect<FP8>::NW * LdsDirect<FP8>::WAVE_B; }
+template <bool FP8>
+constexpr int lds_bytes() { return lds_bt_offset<FP8>() + kBtEntries * 4; }
 // The workgroup combine's staging (per-wave rows and weights) reuses the stages.
-static_assert(kLW * 16 * (2 + Cfg<kLpD, false>::OW_STRIDE) * 4 + 16 * (kLW + 4) * 4 <= kBtOff, "combine staging");
+static_assert(4 * 16 * (2 + Cfg<kLpD, false>::OW_STRIDE) * 4 + 16 * (4 + 4) * 4 <= lds_bt_offset<false>(),
+              "combine staging");
+static_assert(8 * 16 * (2 + Cfg<kLpD, true>::OW_STRIDE) * 4 + 16 * (8 + 4) * 4 <= lds_bt_offset<true>(),
+              "combine staging");
 
 // Items (sequence, KV head) of one launch, in the pairs form: with N = B * Hkv
 // items on W workgroups (W < N <= 2W), the sequences are ranked by length
@@ -68,12 +93,16 @@ __device__ void lds_pair_items(const SplitParams& p, int batch, int tid, uint32_
 // accumulators then stay in ordinary VGPRs, where the rescale reaches them.
 // PAIRS = false: grid (Hkv, B), one item per workgroup.  PAIRS = true: a 1D
 // grid of W workgroups taking the items as lds_pair_items deals them (batch
-// <= kPairedMaxBatch).
-template <bool PAIRS>
-__global__ void __launch_bounds__(kLW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// <= kPairedMaxBatch).  FP8: codes dequantised with the KV head's scales.
+template <bool FP8, bool PAIRS>
+__global__ void __launch_bounds__(LdsDirect<FP8>::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 lds_direct_kernel(const SplitParams p, int batch) {
-  typedef WaveAttn<kLpD, false> WA;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+  typedef WaveAttn<kLpD, FP8> WA;
+  typedef typename LdsDirect<FP8>::Pipe Pipe;
+  constexpr int kLW = LdsDirect<FP8>::NW;
+  constexpr int kBtOff = lds_bt_offset<FP8>();
+  constexpr int TT = Pipe::TT;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[lds_bytes<FP8>()];
   __shared__ int64_t s_rows[kHeadsPerGroup];
   __shared__ int64_t s_orow[kHeadsPerGroup];
 
@@ -109,6 +138,7 @@ lds_direct_kernel(const SplitParams p, int batch) {
       A.load_q(p.q + lq.qoff, lq.valid);
     }
     A.qk_scale = p.qk_scale_log2;
+    if constexpr (FP8) A.qk_scale *= p.k_scale[kvh];
     A.reset();
     const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);  // uniform: tile bookkeeping stays scalar
     const LaneRow lr = lane_row<kLpD, false>(p, b, kvh, 0, A.n, L, L, 0);
@@ -118,29 +148,30 @@ lds_direct_kernel(const SplitParams p, int batch) {
     }
     __syncthreads();
 
-    const int ntiles = (L + kLpTT - 1) / kLpTT;
+    const int ntiles = (L + TT - 1) / TT;
     const int ps = p.page_size;
-    const int64_t head_off = (int64_t)kvh * kLpRowB;
-    LdsPipe P;
-    P.init(smem, wave * kLpWaveB, A, lane, p.kv.tok_stride);
+    const int64_t head_off = (int64_t)kvh * p.kv.head_stride;
+    Pipe P;
+    P.init(smem, wave * LdsDirect<FP8>::WAVE_B, A, lane, p.kv.tok_stride);
     // Tiles wave, wave + kLW, ...; the byte offset of token tb's row of KV head
     // kvh.  (Output stores of a previous item may still be outstanding; they
     // only make the pipeline's load-count waits stricter.)
-    P.run(A, wave, kLW, ntiles, 0, L, lr.end, lr.end_min, p.k, p.v, [&](int tb) -> int64_t {
+    lds_pipe_run_ns<2>(P, A, wave, kLW, ntiles, 0, L, lr.end, lr.end_min, p.k, p.v, [&](int tb) -> int64_t {
       const int page = __builtin_amdgcn_readfirstlane(sbt[tb / ps]);
       return (int64_t)page * p.kv.page_stride + (int64_t)(tb % ps) * p.kv.tok_stride + head_off;
     });
     // every load has landed: the combine below reuses the stages
+    const float vsc = FP8 ? p.v_scale[kvh] : 1.0f;
 
     auto store = [&](int hh, int d0, f32x4 o, float lse_nat) {
       *reinterpret_cast<bf16x4*>(p.out + s_orow[hh] + d0) = to_bf16x4(o);
       if (d0 == 0 && p.lse) p.lse[s_rows[hh]] = lse_nat;
     };
     if (p.sinks)
-      wg_combine<kLpD, false, kLW>(A, smem, wave, tid, p.rows_kv, 1.0f, store,
-                                   [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
+      wg_combine<kLpD, FP8, kLW>(A, smem, wave, tid, p.rows_kv, vsc, store,
+                                 [&](int hh) { return p.sinks[(int)(s_rows[hh] % p.hq)]; });
     else
-      wg_combine<kLpD, false, kLW>(A, smem, wave, tid, p.rows_kv, 1.0f, store, NoSink());
+      wg_combine<kLpD, FP8, kLW>(A, smem, wave, tid, p.rows_kv, vsc, store, NoSink());
     if (!PAIRS) break;
     __syncthreads();  // the stages, the staged block table and s_rows are reused by the next item
   }
@@ -150,16 +181,24 @@ lds_direct_kernel(const SplitParams p, int batch) {
 
 bool lds_direct_applies(int head_dim, bool fp8, int q_len, int window, int group, int page_size, int max_pages,
                         bool strided) {
-  return head_dim == kLpD && !fp8 && window == 0 && q_len == 1 && group >= 1 && group <= kHeadsPerGroup &&
+  (void)fp8;  // both caches have an instance
+  return head_dim == kLpD && window == 0 && q_len == 1 && group >= 1 && group <= kHeadsPerGroup &&
          page_size % 16 == 0 && max_pages >= 1 && max_pages <= kBtEntries && !strided;
 }
 
-hipError_t launch_lds_direct(const SplitParams& p, int batch, int workers, hipStream_t stream) {
+template <bool FP8>
+hipError_t launch_lds_direct_t(const SplitParams& p, int batch, int workers, hipStream_t stream) {
+  const dim3 block(LdsDirect<FP8>::NW * 64);
   if (workers > 0)
-    hipLaunchKernelGGL(lds_direct_kernel<true>, dim3(workers), dim3(kLW * 64), 0, stream, p, batch);
+    hipLaunchKernelGGL((lds_direct_kernel<FP8, true>), dim3(workers), block, 0, stream, p, batch);
   else
-    hipLaunchKernelGGL(lds_direct_kernel<false>, dim3(p.hkv, batch), dim3(kLW * 64), 0, stream, p, batch);
+    hipLaunchKernelGGL((lds_direct_kernel<FP8, false>), dim3(p.hkv, batch), block, 0, stream, p, batch);
   return hipGetLastError();
+}
+
+hipError_t launch_lds_direct(const SplitParams& p, bool fp8, int batch, int workers, hipStream_t stream) {
+  return fp8 ? launch_lds_direct_t<true>(p, batch, workers, stream)
+             : launch_lds_direct_t<false>(p, batch, workers, stream);
 }
 
 }  // namespace pkd
@@ -208,7 +247,7 @@ int32_t pkd_decode_lds(const pkd_dims* dims, const void* q, const void* k_cache,
   p.kv.head_stride = 256;
   p.kv.tok_stride = d.num_kv_heads * 256;
   p.kv.page_stride = (int64_t)d.page_size * p.kv.tok_stride;
-  return pkd::launch_lds_direct(p, d.batch, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? PKD_OK
+  return pkd::launch_lds_direct(p, false, d.batch, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? PKD_OK
                                                                                             : PKD_ERR_LAUNCH;
 }
 

@@ -191,6 +191,6 @@ bool lds_direct_applies(int head_dim, bool fp8, int q_len, int window, int group
 // workers = 0: one workgroup per (KV head, sequence); workers = W > 0: the
 // pairs form, W workgroups for B * Hkv items, W < B * Hkv <= 2W, B <= kPairedMaxBatch,
 // lengths below 2^23.
-hipError_t launch_lds_direct(const SplitParams& p, int batch, int workers, hipStream_t stream);
+hipError_t launch_lds_direct(const SplitParams& p, bool fp8, int batch, int workers, hipStream_t stream);
 
 }  // namespace pkd

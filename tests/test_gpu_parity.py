@@ -547,14 +547,15 @@ def _cu_count():
 
 
 @pytest.mark.parametrize("hkv,d,dtype,expect,above", [(8, 128, "bf16", 1, 1), (8, 64, "bf16", 1, PAIR),
-                                                       (8, 32, "bf16", BAL, PAIR), (8, 128, "fp8_e4m3", BAL, PAIR)])
+                                                       (8, 32, "bf16", BAL, PAIR), (8, 128, "fp8_e4m3", BAL, 1),
+                                                       (8, 64, "fp8_e4m3", BAL, PAIR)])
 def test_auto_mode_around_one_item_per_cu(B, hkv, d, dtype, expect, above):
     """PKD_SPLITS_AUTO picks direct output for a bf16 cache with head rows of at
     least 128 bytes when the (sequence, KV head, head group) items number between
     three quarters of the compute units and all of them (one whole item per unit,
     nothing to merge); above that, up to two items per unit, whole items paired
-    by length (the LDS-staged direct kernel's pairs form for bf16 D = 128, else
-    the paired mode); elsewhere the balanced partition."""
+    by length (the LDS-staged direct kernel's pairs form for D = 128, else the
+    paired mode); elsewhere the balanced partition."""
     cus = _cu_count()
     if cus % hkv:
         pytest.skip("compute units not a multiple of the KV heads")
@@ -564,7 +565,7 @@ def test_auto_mode_around_one_item_per_cu(B, hkv, d, dtype, expect, above):
                         (2 * cus // hkv + 1, BAL)):
         dims = B.pkd_dims(batch, 4 * hkv, hkv, d, 64, 4096, 64, kvd)
         assert B.paged_decode_num_splits(dims, 0) == want, (batch, hkv, d, dtype)
-        if want == 1 and d == 128 and dtype == "bf16":
+        if want == 1 and d == 128:
             assert B.paged_decode_path(dims, None, 0) == B.PKD_PATH_DIRECT_LDS
 
 
@@ -1422,21 +1423,54 @@ def test_lds_entry_matches_oracle_and_grid_kernel(B, case):
 
 
 def test_direct_output_path_choice(B):
-    """paged_decode runs the LDS-staged direct kernel for one round of D = 128
-    items of one query token without a window, and the register-staged one
-    otherwise; both give the same bits, so the switch is invisible in the
-    results."""
+    """paged_decode runs the LDS-staged direct kernel (bf16 or FP8) for up to two
+    rounds of D = 128 items of one query token without a window (two in its
+    pairs form), and the register-staged one otherwise; for bf16 both give the
+    same bits, so the switch is invisible in the results."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     b32 = B.pkd_dims(32, 32, 8, 128, 64, 1500, 64, B.PKD_DTYPE_BF16)
-    lds = B.PKD_PATH_DIRECT_LDS if 32 * 8 <= cus else B.PKD_PATH_DIRECT
+    lds = B.PKD_PATH_DIRECT_LDS if 32 * 8 <= 2 * cus else B.PKD_PATH_DIRECT
     assert B.paged_decode_path(b32, None, 1) == lds
     assert B.paged_decode_path(b32, B.pkd_ext(1, 1, 0, 0), 1) == lds  # causal, one token: no mask
     assert B.paged_decode_path(b32, B.pkd_ext(4, 1, 0, 0), 1) == B.PKD_PATH_DIRECT  # 4 query tokens
     assert B.paged_decode_path(b32, B.pkd_ext(1, 0, 512, 0), 1) == B.PKD_PATH_DIRECT  # window
+    b64 = B.pkd_dims(64, 32, 8, 128, 64, 1500, 64, B.PKD_DTYPE_BF16)
+    assert B.paged_decode_path(b64, None, 1) == (B.PKD_PATH_DIRECT_LDS if 64 * 8 <= 2 * cus else B.PKD_PATH_DIRECT)
     b128 = B.pkd_dims(128, 32, 8, 128, 128, 4100, 32, B.PKD_DTYPE_BF16)
     assert B.paged_decode_path(b128, None, 1) == B.PKD_PATH_DIRECT  # four rounds
     fp8 = B.pkd_dims(32, 32, 8, 128, 64, 1500, 64, B.PKD_DTYPE_FP8_E4M3)
-    assert B.paged_decode_path(fp8, None, 1) == B.PKD_PATH_DIRECT
+    assert B.paged_decode_path(fp8, None, 1) == lds
+    fp8_d64 = B.pkd_dims(32, 32, 8, 64, 64, 1500, 64, B.PKD_DTYPE_FP8_E4M3)
+    assert B.paged_decode_path(fp8_d64, None, 1) == B.PKD_PATH_DIRECT
+
+
+@pytest.mark.parametrize("bq,hq,lens_seed,sinks", [(20, 64, 1, False), (33, 64, 2, True), (64, 64, 3, False),
+                                                   (40, 8, 4, True)])
+def test_fp8_lds_direct_matches_oracle(B, bq, hq, lens_seed, sinks):
+    """FP8 direct output on the LDS-staged kernel (one workgroup per item, or the
+    pairs form above one item per compute unit) against the oracle, and against
+    the same call with a window longer than every sequence, which changes no
+    score but runs the register-staged grid kernel.  Its eight waves group the
+    tiles differently from the grid kernel's four, so the two agree to rounding
+    (a few bf16 ulps), not bit for bit; a repeated call gives the same bits."""
+    lens = [int(x) for x in np.random.default_rng(lens_seed).integers(0, 2500, size=bq)]
+    w = wl.custom_workload(bq, hq, 8, 128, 64, lens, "fp8_e4m3", 4100 + lens_seed, sinks=sinks)
+    t = dev(w)
+    dims = B.dims_for(t["q"], t["k"], t["bt"])
+    assert B.paged_decode_path(dims, None, 1) == B.PKD_PATH_DIRECT_LDS
+    big = w.spec.max_pages_per_seq * w.spec.page_size + 64
+    assert B.paged_decode_path(dims, B.ext_for(t["q"], False, big), 1) == B.PKD_PATH_DIRECT
+    out_w, lse_w = B.decode(t["q"], t["k"], t["v"], t["bt"], t["lens"], w.scale, t["ks"], t["vs"], num_splits=1,
+                            window=big, sinks=t["sinks"])
+    out, lse = run(B, w, 1, t)
+    torch.cuda.synchronize()
+    ref = oracle_full(w)
+    check(out, lse, *ref, what=f"fp8 lds direct B={bq}")
+    check(out_w.cpu(), lse_w.cpu(), *ref, what=f"fp8 grid direct B={bq}")
+    d = (out.float() - out_w.cpu().float()).abs()
+    assert float(d.max()) <= 4 * 2.0 ** -8 * float(out.float().abs().max()) + 1e-6
+    out2, lse2 = run(B, w, 1, t)
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16)) and torch.equal(lse2, lse)
 
 
 @pytest.mark.parametrize("q_len,causal,sinks", [(1, False, True), (1, True, True), (1, False, False),
