@@ -447,6 +447,30 @@ def split_sweep(w, steps, warmup, device, scrub):
     return out
 
 
+BATCH_SWEEP = (31, 32, 33, 40, 48, 64)
+
+
+def batch_sweep(steps, warmup, device):
+    """GB/s of the B=32 step's shape at neighbouring batch sizes (the same length
+    recipe and seed, so B=31 and B=33 share the B=32 lengths but for one), each in
+    the library's own mode, timed like the metric.  Across one and two items per
+    compute unit the mode keeps whole items (one per workgroup, then paired by
+    length), so the rate should not step at B=33."""
+    import dataclasses
+    from paged_kv_decode_amd import workloads as wl
+    base = wl.WORKLOADS[PRIMARY]
+    out = {}
+    for bq in BATCH_SWEEP:
+        spec = dataclasses.replace(base, name=f"{base.name}_b{bq}", batch=bq)
+        w = wl.make_workload(spec, tail="zero")
+        r = _rotating_runner(w, 0, device)
+        ms = _back_to_back(r.stream, steps, warmup, len(r.copies), r.step)
+        out[f"B={bq}"] = {"gbs": round(algorithmic_bytes(w) / (ms * 1e-3) / 1e9, 1), "us": round(ms * 1e3, 2),
+                          "num_splits": r.S, "path": r.path}
+        del r, w
+    return out
+
+
 def _direct_legs(r, w):
     """Pre-marshalled calls of the three direct-output kernels on each K/V copy of
     runner r: the register-staged grid kernel (pkd_decode_registers), the
@@ -843,6 +867,9 @@ def main():
     sweep = {name: split_sweep(w, sweep_steps, sweep_warmup, device, scrub) for name, w in sweep_w.items()}
     for name, row in sweep.items():
         print(f"# num_splits sweep {name} (GB/s): {row}", file=sys.stderr, flush=True)
+    bsweep = batch_sweep(max(args.steps // 2, 10), 20, device)
+    print(f"# batch sweep of {PRIMARY} (GB/s): "
+          f"{ {k: v['gbs'] for k, v in bsweep.items()} }", file=sys.stderr, flush=True)
     ab = {name: inner_loop_ab(w, sweep_steps, sweep_warmup, device, scrub) for name, w in sweep_w.items()}
     for name, row in ab.items():
         print(f"# inner loop A/B {name} (direct output): {row}", file=sys.stderr, flush=True)
@@ -915,6 +942,7 @@ def main():
                           "queries_per_s": round(v["queries_per_s"], 1), "ms_per_step": v["ms_per_step"],
                           "window": v["window"], "sinks": v["sinks"], "num_splits": v["num_splits"]}
     line["split_sweep"] = {"steps": sweep_steps, "warmup": sweep_warmup, "gbs": sweep}
+    line["batch_sweep"] = {"steps": max(args.steps // 2, 10), "warmup": 20, "rows": bsweep}
     line["stream_ceiling"] = ceiling
     line["low_load"] = {"decode": low_decode, "stream": ceiling["low_load"]}
     line["inner_loop_ab"] = {"steps": sweep_steps, "rows": ab}
