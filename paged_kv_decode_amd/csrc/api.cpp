@@ -186,8 +186,7 @@ uint64_t next_epoch() {
     uint64_t expect = 0;
     g_epoch.compare_exchange_strong(expect, (seed & ((1ull << 40) - 1)) | 1);
   }
-  uint64_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) & ((1ull << 40) - 1);
-  return e != 0 ? e : 1;
+  return pkd::call_tag(g_epoch.fetch_add(1, std::memory_order_relaxed));
 }
 
 size_t partial_bytes(const Dims& d, int S, size_t* lse_offset) {

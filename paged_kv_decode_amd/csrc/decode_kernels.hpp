@@ -386,16 +386,8 @@ balanced_kernel(const BalancedParams p) {
       // workgroup g < E takes items g and 2E - 1 - g (the 2E shortest, folded
       // so that each pair's lengths add up to about the same), every other
       // workgroup one item of the N - 2E longest.
-      const int E = pl.items - p.num_workers;
-      int it0 = -1, it1 = -1;
-      if (E <= 0) {
-        if (wi < pl.items) it0 = wi;
-      } else if (wi < E) {
-        it0 = 2 * E - 1 - wi;
-        it1 = wi;
-      } else {
-        it0 = wi + E;
-      }
+      int it0, it1;
+      paired_items(wi, pl.items, p.num_workers, &it0, &it1);
       if (it0 >= 0) {
         pi_n = it1 >= 0 ? 2 : 1;
         pi_b[0] = s_rank_b[it0 / SPB];
@@ -523,8 +515,10 @@ balanced_kernel(const BalancedParams p) {
     // slots w + s (s = b * SPB + seg).
     const int64_t sidx = (int64_t)b * SPB + seg;
     const int64_t seg_pos = spre[b] + (int64_t)seg * nb;
-    const int64_t w_first = ((seg_pos + 1) * nwe - 1) / T;
-    const int npieces = paired ? 1 : (int)(((seg_pos + nb) * nwe - 1) / T - w_first + 1);
+    int64_t w_first;
+    int npieces;
+    segment_pieces(seg_pos, nb, nwe, T, &w_first, &npieces);
+    if (paired) npieces = 1;
     // Row hh's V scale, and whether dims d0.. of the wide row are its own head's
     // (always, without pairing); own_dim gives their place in the real row.
     const float vsc = FP8 ? p.v_scale[kvh * VK] : 1.0f;
@@ -587,16 +581,16 @@ balanced_kernel(const BalancedParams p) {
           uint64_t old = __hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           uint64_t nv;
           do {
-            nv = ((old >> 24) == E ? old : (E << 24)) + 1;
+            nv = count_word_add(old, E);
           } while (!__hip_atomic_compare_exchange_weak(cw, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT));
-          const bool last = (int)(nv & 0xFFFFFF) == npieces;
+          const bool last = count_word_pieces(nv) == npieces;
           if (last) {
             // Acquire at agent scope: the other pieces' partials, which their
             // counts made visible before this count saw them, are read after it.
             // Only a merging piece pays for it (one per multi-piece segment).
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            __hip_atomic_store(cw, E << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(cw, count_word_reset(E), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
           s_last = last;
         }

@@ -81,12 +81,7 @@ __device__ void lds_pair_items(const SplitParams& p, int batch, int tid, uint32_
     rank_b[rank] = (int16_t)tid;
   }
   __syncthreads();
-  const int N = batch * p.hkv;
-  const int E = N - (int)gridDim.x;
-  const int g = blockIdx.x;
-  items[0] = g < E ? 2 * E - 1 - g : g + (E > 0 ? E : 0);
-  items[1] = g < E ? g : -1;
-  if (items[0] >= N) items[0] = -1;
+  paired_items(blockIdx.x, batch * p.hkv, gridDim.x, &items[0], &items[1]);
 }
 
 // Two waves per SIMD as the register budget (as the grid kernel): the

@@ -77,9 +77,8 @@ __global__ void __launch_bounds__(64 * (WPR == 1 ? 4 : WPR)) lse_merge_kernel(co
     if (nb > 0) {
       const int64_t ps_ = p.prefix[b] + seg * nb;
       const int64_t nwe = min((int64_t)p.num_workers, T);
-      const int64_t w_first = ((ps_ + 1) * nwe - 1) / T;
-      const int64_t w_last = ((ps_ + nb) * nwe - 1) / T;
-      S = (int)(w_last - w_first + 1);
+      int64_t w_first;
+      segment_pieces(ps_, nb, nwe, T, &w_first, &S);
       slot0 = w_first + (int64_t)b * spb + seg;
     }
     lp = p.lse_part + slot0 * p.hpg + nh;

@@ -99,6 +99,54 @@ struct BalancedParams {
                                // equal ranges); batch <= kPairedMaxBatch
 };
 
+// ---- Arithmetic shared by the kernels and the host, in one place so that a
+// host-only test can check it (the in-place merge's counter words, the
+// balanced partition's pieces, the paired deal of whole items). ----
+
+// An in-place merge counter word is (tag << 24) | pieces counted.  A word
+// carrying another tag counts as zero, so a workspace left by any earlier call
+// (or never initialised) needs no clearing; the piece that completes the count
+// writes count_word_reset, which any later tag, the same one included, again
+// reads as zero.  Tags are 40 bits and never 0.
+__host__ __device__ inline uint64_t count_word_add(uint64_t old, uint64_t tag) {
+  return ((old >> 24) == tag ? old : (tag << 24)) + 1;
+}
+__host__ __device__ inline int count_word_pieces(uint64_t word) { return (int)(word & 0xFFFFFF); }
+__host__ __device__ inline uint64_t count_word_reset(uint64_t tag) { return tag << 24; }
+// The tag of the call numbered n (a process-wide counter): its low 40 bits, 0
+// read as 1.
+__host__ __device__ inline uint64_t call_tag(uint64_t n) {
+  const uint64_t e = n & ((1ull << 40) - 1);
+  return e != 0 ? e : 1;
+}
+
+// The balanced partition: T groups on nwe workgroups, workgroup w taking
+// groups [w T / nwe, (w + 1) T / nwe).  A segment holding groups
+// [seg_pos, seg_pos + nb) (nb >= 1) is split among the workgroups w_first ..
+// w_first + npieces - 1, one piece each.
+__host__ __device__ inline void segment_pieces(int64_t seg_pos, int64_t nb, int64_t nwe, int64_t T,
+                                               int64_t* w_first, int* npieces) {
+  const int64_t f = ((seg_pos + 1) * nwe - 1) / T;
+  *w_first = f;
+  *npieces = (int)(((seg_pos + nb) * nwe - 1) / T - f + 1);
+}
+
+// The paired deal of N whole items, ranked by length ascending, on W
+// workgroups: with E = N - W > 0, workgroup g < E takes items 2E - 1 - g
+// (first) and g, every other workgroup g < W item g + E; with E <= 0
+// workgroup g < N takes item g.  -1: none.  Each item goes to exactly one
+// workgroup when N <= 2W.
+__host__ __device__ inline void paired_items(int g, int N, int W, int* first, int* second) {
+  const int E = N - W;
+  if (E > 0) {
+    *first = g < E ? 2 * E - 1 - g : (g + E < N ? g + E : -1);
+    *second = g < E ? g : -1;
+  } else {
+    *first = g < N ? g : -1;
+    *second = -1;
+  }
+}
+
 // True when the balanced mode merges inside the partition kernel: when there
 // are at least as many segments as workgroups, so a segment spans one or two
 // pieces and a multi-piece merge is short.  (Measured: the same or faster
