@@ -773,6 +773,24 @@ def trace_avg_from_profiles(name, kernel_prefix):
     return None
 
 
+def rdreq_bytes_from_profiles(name):
+    """Bytes the partition kernel read from memory per launch by the L2's own
+    count: TCC_EA0_RDREQ_sum per dispatch in the committed counter summary of
+    workload name times 128 (the request size; each summary shows that the
+    calibrated FETCH_SIZE divides into 128-byte requests), or None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{name}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path, encoding="utf-8"):
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) > 3 and cells[1] == "`TCC_EA0_RDREQ_sum`":
+            try:
+                return float(cells[2].replace(",", "")) * 128.0
+            except ValueError:
+                return None
+    return None
+
+
 def traffic_from_profiles(name):
     """Measured HBM bytes per launch of the partition kernel, if a counter summary
     for this workload and the current kernel source is committed under profiles/
@@ -922,7 +940,8 @@ def main():
                      "kernel": p["roofline"]["kernel"],
                      "kernel_ms": p["split_kernel_ms"],
                      "kernel_bytes": p["split_kernel_bytes"],
-                     "trace_avg_us": trace_avg_from_profiles(PRIMARY, PATH_TRACE_PREFIX[p["path"]])},
+                     "trace_avg_us": trace_avg_from_profiles(PRIMARY, PATH_TRACE_PREFIX[p["path"]]),
+                     "read_bytes_rdreq": rdreq_bytes_from_profiles(PRIMARY)},
         "workloads": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in results.items()},
     }
@@ -947,6 +966,11 @@ def main():
     line["low_load"] = {"decode": low_decode, "stream": ceiling["low_load"]}
     line["inner_loop_ab"] = {"steps": sweep_steps, "rows": ab}
     line["roofline"]["frac_of_stream_ceiling"] = round(roof_achieved / ceiling["gbs"], 4)
+    # The same fraction from the committed kernel trace's average duration (the
+    # event-timed frac above includes the dispatch gap between back-to-back steps).
+    tr = line["roofline"]["trace_avg_us"]
+    line["roofline"]["frac_trace"] = (round(p["split_kernel_bytes"] / (tr * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                                      if tr else None)
     line["append"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in app.items()}
     line["metadata"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in meta.items()}
     line["contiguous"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in contig.items()}

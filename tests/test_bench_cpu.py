@@ -45,6 +45,22 @@ def test_trace_average_is_read_from_the_committed_summary():
     assert bench.trace_avg_from_profiles("no_such_workload", "pkd::") is None
 
 
+def test_read_requests_give_the_read_bytes():
+    """The L2's own read-request count in the committed B = 32 counter summary,
+    times the 128-byte request size, is the step's algorithmic bytes to within
+    1% (the step reads each K/V byte once; q, the block table and the lengths are
+    a few hundred KB), and agrees with the calibrated FETCH_SIZE figure."""
+    from paged_kv_decode_amd import workloads as wl
+    rd = bench.rdreq_bytes_from_profiles("llama_b32_d128_ps64")
+    assert rd is not None
+    alg = bench.algorithmic_bytes(wl.make_workload(wl.WORKLOADS["llama_b32_d128_ps64"], tail="zero"))
+    assert abs(rd / alg - 1) < 0.01, (rd, alg)
+    rec = __import__("json").load(open(os.path.join(ROOT, "profiles", "traffic_llama_b32_d128_ps64.json")))
+    fetch = rec["fetch_kib_per_dispatch"] * 1024 * rec["fetch_scale"]
+    assert abs(rd / fetch - 1) < 0.01, (rd, fetch)
+    assert bench.rdreq_bytes_from_profiles("no_such_workload") is None
+
+
 def test_traffic_is_dropped_when_the_kernel_sources_change(tmp_path, monkeypatch):
     """A traffic figure under profiles/ is used only while the digest of the
     kernels' sources matches the one it was taken with."""
