@@ -296,6 +296,10 @@ int32_t paged_decode_finish(const pkd_dims* dims, const pkd_ext* ext, int32_t nu
  *    wherever it applies.  Whole items in pairs measured faster than the equal
  *    cuts for ragged lengths; when every length is equal, pairs cost up to
  *    twice an item's time on some units and PKD_SPLITS_BALANCED is faster;
+ *  - else, with at most one item per 64 compute units (a few long sequences),
+ *    S = units / items split by the grid kernel (one workgroup per unit),
+ *    capped by the longest sequence expected (at least 256 tokens per split)
+ *    and by PKD_MAX_SPLITS, when that gives S >= 2;
  *  - else PKD_SPLITS_BALANCED wherever it applies;
  *  - else 1 when the items alone fill the device's compute units, else a split
  *    count in [2, PKD_MAX_SPLITS] bounded by the longest sequence expected,

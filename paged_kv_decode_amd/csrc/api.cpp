@@ -243,6 +243,13 @@ bool lds_direct_ok(const Dims& d, bool strided);
 //    lengths 1024-4096 (bf16, 8 KV heads, B = 33-64: 5.5-6.4 against 4.9-5.5
 //    TB/s) and 512-8192 (FP8, B = 40-64: 4.4-5.5 against 4.0-4.7 TB/s); the
 //    LDS-staged form led the paired mode by 2-7%.
+//  - At most one item per 64 compute units (a few long sequences): grid
+//    splits, about one workgroup per unit (S = units / items, at least 256
+//    tokens per split).  The grid kernel's start-up (length, q and block table
+//    loaded together) is shorter than the balanced partition's (lengths, prefix
+//    sums, page window, q in turn), which weighs at these sizes: B = 1 with
+//    131072 tokens and 2 KV heads ran 15.5 / 18.7 / 51.9 us against 18.6 /
+//    22.3 / 55.4 balanced at D = 32 / 64 / 256.
 //  - Otherwise the balanced partition wherever it applies (it balances any
 //    length mix and pays each workgroup's start-up once).
 //  - Otherwise direct output when the items alone fill the device, else
@@ -256,6 +263,15 @@ int32_t heuristic_splits(const Dims& d, int32_t max_len, bool strided) {
   if (cus > 0 && items > cus && items <= 2LL * cus) {
     if (lds_direct_ok(d, strided)) return 1;
     if (paired_ok(d)) return PKD_SPLITS_PAIRED;
+  }
+  if (cus > 0 && items > 0 && items * 64 <= cus) {
+    // A few long items: grid splits, about one workgroup per unit.
+    const int64_t span = max_len < visible_span(d) ? max_len : visible_span(d);
+    int64_t s = cus / items;
+    const int64_t by_len = (span + 255) / 256;  // at least ~256 tokens per split
+    if (s > by_len) s = by_len;
+    if (s > PKD_MAX_SPLITS) s = PKD_MAX_SPLITS;
+    if (s >= 2) return (int32_t)s;
   }
   if (balanced_ok(d)) return PKD_SPLITS_BALANCED;
   const int64_t target = 4LL * (cus > 0 ? cus : 256);  // workgroups to keep every CU busy
