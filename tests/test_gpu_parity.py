@@ -656,12 +656,16 @@ def test_plain_entry_heuristic(B, case):
     check(ref_out, ref_lse, *oracle_full(w), what=f"plain entry heuristic {case}")
 
 
-@pytest.mark.parametrize("S", [BAL, 4, 1])
-def test_graph_replays(B, S):
+@pytest.mark.parametrize("S,nseq", [(BAL, 32), (4, 32), (1, 32), (PAIR, 32), (PAIR, 40), (0, 40)])
+def test_graph_replays(B, S, nseq):
     """A captured decode replays correctly several times, with eager work and
-    synchronisations between the replays, and matches the eager call bitwise."""
-    lens = [(i * 1543) % 6000 + 100 for i in range(32)]
-    w = wl.custom_workload(32, 32, 8, 128, 64, lens, "bf16", seed=21)
+    synchronisations between the replays, and matches the eager call bitwise.
+    The call tag of the in-place merge's counters is fixed at capture, so every
+    replay reuses it (the paired mode's fallback at 32 sequences merges in
+    place; at 40 sequences it deals pairs, and AUTO runs the LDS-staged pairs
+    form)."""
+    lens = [(i * 1543) % 6000 + 100 for i in range(nseq)]
+    w = wl.custom_workload(nseq, 32, 8, 128, 64, lens, "bf16", seed=21)
     t = dev(w)
     dims = B.dims_for(t["q"], t["k"], t["bt"])
     nbytes = B.paged_decode_workspace_bytes_ext(dims, None, S)
