@@ -13,6 +13,7 @@ from paged_kv_decode_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 BAL = -1000  # PKD_SPLITS_BALANCED
+PAIR = -1001  # PKD_SPLITS_PAIRED
 
 
 @pytest.fixture(scope="module")
@@ -73,6 +74,12 @@ CASES = [
      _lens(9, 1500, 8)),
     ("verify, window, sinks", BAL, 10, 16, 2, 128, 64, "bf16", 4, True, 500, True, _lens(10, 3000, 9),
      _lens(4, 800, 10)),
+    # whole items paired by length (40 and 36 sequences of 8 KV heads: between one and two
+    # items per compute unit), and the same mode falling back to the equal ranges with the
+    # in-place merge (equal lengths)
+    ("paired mode", PAIR, 40, 32, 8, 64, 64, "bf16", 1, False, 0, False, _lens(40, 3000, 11),
+     _lens(36, 2000, 12)),
+    ("paired mode, fallback", PAIR, 33, 32, 8, 64, 64, "bf16", 1, False, 0, False, [900] * 33, [700] * 34),
 ]
 
 
