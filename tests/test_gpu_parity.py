@@ -569,6 +569,28 @@ def test_auto_mode_around_one_item_per_cu(B, hkv, d, dtype, expect, above):
             assert B.paged_decode_path(dims, None, 0) == B.PKD_PATH_DIRECT_LDS
 
 
+def test_auto_few_long_items(B):
+    """PKD_SPLITS_AUTO for at most one item per 64 compute units (a few long
+    sequences): grid splits, about one workgroup per unit (units / items), capped
+    by the longest sequence at 256 tokens per split; with more items, or short
+    sequences, the other rules."""
+    cus = _cu_count()
+    if cus < 128:
+        pytest.skip("fewer than 128 compute units")
+    for hkv, mp in ((2, 2048), (1, 2048), (2, 40)):
+        dims = B.pkd_dims(1, 16, hkv, 64, 64, 4096, mp, B.PKD_DTYPE_BF16)
+        want = min(cus // hkv, -(-(mp * 64) // 256), B.PKD_MAX_SPLITS)  # hkv items
+        assert B.paged_decode_num_splits(dims, 0) == want, (hkv, mp, want)
+        assert B.paged_decode_path(dims, None, 0) == B.PKD_PATH_SPLITS
+    # no sequence longer than 256 tokens: direct output comes first
+    dims = B.pkd_dims(1, 16, 2, 64, 64, 4096, 4, B.PKD_DTYPE_BF16)
+    assert B.paged_decode_num_splits(dims, 0) == 1
+    # 16 sequences of 2 KV heads: 32 items, above one per 64 units -> balanced
+    dims = B.pkd_dims(16, 16, 2, 64, 64, 8192, 512, B.PKD_DTYPE_BF16)
+    if 32 * 64 > cus:
+        assert B.paged_decode_num_splits(dims, 0) == BAL
+
+
 def _lds_pairs_cases(cus):
     """(name, batch, Hq, Hkv, ps, lens, sinks) with between one and two (sequence,
     KV head) items per compute unit, for the LDS-staged kernel's pairs form."""
